@@ -1,0 +1,268 @@
+"""fp8_weight_only_amd — FP8 (OCP e4m3fn) weight-only linear layer for MI355X.
+
+A thin ctypes binding over ``libfp8w.so`` (declared in ``include/fp8w.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensors, hands their device pointers and torch's current HIP stream
+to the C ABI, and allocates outputs with torch (torch is plumbing here: device
+memory and streams).
+
+The raw entry points keep the C names (``fp8w_quantize``, ``fp8w_linear``,
+``fp8w_linear_with_path``, ``fp8w_dequantize_fallback``, ``fp8w_linear_path``,
+``fp8w_linear_workspace_bytes``, ``fp8w_status_string``) and take integers
+(pointers, sizes, the stream handle). The tensor-level helpers ``quantize``,
+``linear``, ``dequantize`` and the ``QuantizedLinear`` holder sit on top.
+
+The method ("FP8 weight-only (precision: fp8_weights)", section "The
+contract"): quantise once at build time with one scale per output channel,
+scale = amax(|row|) / 448 and codes rounded to nearest even in e4m3 (clamped
+to +-448), keep no higher-precision copy, and per call compute
+y = scale[n] * sum_k x[m,k] q[n,k] + bias[n] with fp32 accumulation and one
+rounding to the activation dtype.
+
+If ``libfp8w.so`` has not been built, importing the package still works but
+every call raises: there is no CPU or PyTorch fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "Fp8wError", "lib_path", "load", "fp8w_quantize", "fp8w_linear", "fp8w_linear_with_path",
+    "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes",
+    "fp8w_status_string", "fp8w_abi_version", "quantize", "linear", "dequantize",
+    "linear_path", "workspace_bytes", "QuantizedLinear",
+    "BF16", "FP16", "FP32", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_FALLBACK", "EXPORTS",
+]
+
+BF16, FP16, FP32 = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_FALLBACK = -1, 0, 1, 2
+SUCCESS, ERR_INVALID_VALUE, ERR_MISALIGNED, ERR_NONFINITE, ERR_WORKSPACE, ERR_HIP = range(6)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_I = ctypes.c_int
+
+# name -> (restype, argtypes), mirroring include/fp8w.h
+EXPORTS = {
+    "fp8w_quantize": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
+    "fp8w_linear": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "fp8w_linear_with_path": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _I, _P]),
+    "fp8w_dequantize_fallback": (_I, [_P, _P, _I64, _I64, _P, _I, _P]),
+    "fp8w_linear_path": (_I, [_I64, _I64, _I64, _I, _P, _P, _P]),
+    "fp8w_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _P, _P, _P]),
+    "fp8w_status_string": (ctypes.c_char_p, [_I]),
+    "fp8w_last_hip_error": (_I, []),
+    "fp8w_abi_version": (_I, []),
+}
+
+
+class Fp8wError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = fp8w_status_string(status)
+        if status == ERR_HIP:
+            msg += f" (hipError {load().fp8w_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfp8w.so")
+
+
+def load():
+    """Load libfp8w.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        p = lib_path()
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()'); "
+                               "there is no non-HIP implementation")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+# ------------------------------------------------------------------ raw C entry points
+def fp8w_quantize(w, w_dtype, n, k, q, scale, stream) -> int:
+    return load().fp8w_quantize(w, w_dtype, n, k, q, scale, stream)
+
+
+def fp8w_linear(x, act_dtype, m, k, q, scale, bias, n, y, workspace, workspace_bytes, stream) -> int:
+    return load().fp8w_linear(x, act_dtype, m, k, q, scale, bias, n, y, workspace, workspace_bytes, stream)
+
+
+def fp8w_linear_with_path(x, act_dtype, m, k, q, scale, bias, n, y, workspace, workspace_bytes, path,
+                          stream) -> int:
+    return load().fp8w_linear_with_path(x, act_dtype, m, k, q, scale, bias, n, y, workspace, workspace_bytes,
+                                        path, stream)
+
+
+def fp8w_dequantize_fallback(q, scale, n, k, out, out_dtype, stream) -> int:
+    return load().fp8w_dequantize_fallback(q, scale, n, k, out, out_dtype, stream)
+
+
+def fp8w_linear_path(m, n, k, act_dtype, x, q, y) -> int:
+    return load().fp8w_linear_path(m, n, k, act_dtype, x, q, y)
+
+
+def fp8w_linear_workspace_bytes(m, n, k, act_dtype, x, q, y) -> int:
+    return load().fp8w_linear_workspace_bytes(m, n, k, act_dtype, x, q, y)
+
+
+def fp8w_status_string(status) -> str:
+    return load().fp8w_status_string(status).decode()
+
+
+def fp8w_abi_version() -> int:
+    return load().fp8w_abi_version()
+
+
+# ------------------------------------------------------------------ tensor helpers
+_DT = {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}")
+    return _DT[t]
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(st: int, where: str) -> None:
+    if st != SUCCESS:
+        raise Fp8wError(st, where)
+
+
+def quantize(w: torch.Tensor):
+    """Per-output-channel e4m3 quantization of a [n, k] weight (fp32, bf16 or fp16).
+
+    Returns (q uint8 [n, k], scale fp32 [n]). Raises Fp8wError (status
+    ERR_NONFINITE) on NaN / inf weights."""
+    if w.dim() != 2:
+        raise ValueError("w must be [n, k]")
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n,), dtype=torch.float32, device=w.device)
+    st = fp8w_quantize(_dev(w, "w") if w.numel() else 0, _dtype_code(w.dtype), n, k,
+                       q.data_ptr() if q.numel() else 0, scale.data_ptr() if n else 0, _stream(w.device))
+    _check(st, "fp8w_quantize")
+    return q, scale
+
+
+def linear_path(x: torch.Tensor, q: torch.Tensor, y: torch.Tensor = None) -> int:
+    m, k = x.shape
+    return fp8w_linear_path(m, q.shape[0], k, _dtype_code(x.dtype), x.data_ptr(), q.data_ptr(),
+                            0 if y is None else y.data_ptr())
+
+
+def workspace_bytes(x: torch.Tensor, q: torch.Tensor, y: torch.Tensor = None) -> int:
+    m, k = x.shape
+    return fp8w_linear_workspace_bytes(m, q.shape[0], k, _dtype_code(x.dtype), x.data_ptr(), q.data_ptr(),
+                                       0 if y is None else y.data_ptr())
+
+
+def linear(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor = None,
+           out: torch.Tensor = None, workspace: torch.Tensor = None, path: int = PATH_AUTO) -> torch.Tensor:
+    """y = scale[n] * sum_k x[m,k] value(q[n,k]) + bias[n], rounded once to x.dtype.
+
+    x: [m, k] bf16 / fp16; q: [n, k] uint8 codes; scale: [n] fp32; bias: [n]
+    of x.dtype or None. ``workspace`` (uint8, any device tensor) is only needed
+    on the fallback path; when it is None and the path needs one, one is
+    allocated here with torch."""
+    if x.dim() != 2 or q.dim() != 2 or q.dtype != torch.uint8 or scale.dtype != torch.float32:
+        raise ValueError("expected x [m,k], q uint8 [n,k], scale fp32 [n]")
+    m, k = x.shape
+    n = q.shape[0]
+    if q.shape[1] != k or scale.shape != (n,):
+        raise ValueError("shape mismatch between x, q and scale")
+    if bias is not None and (bias.shape != (n,) or bias.dtype != x.dtype):
+        raise ValueError("bias must be [n] in the activation dtype")
+    act = _dtype_code(x.dtype)
+    if act == FP32:
+        raise TypeError("activations must be bf16 or fp16")
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    elif out.shape != (m, n) or out.dtype != x.dtype:
+        raise ValueError("out must be [m, n] in the activation dtype")
+    xp = _dev(x, "x") if x.numel() else 0
+    qp = _dev(q, "q") if q.numel() else 0
+    sp = _dev(scale, "scale") if n else 0
+    bp = _dev(bias, "bias") if bias is not None and n else 0
+    yp = _dev(out, "out") if out.numel() else 0
+    if path == PATH_FALLBACK or (path == PATH_AUTO and fp8w_linear_path(m, n, k, act, xp, qp, yp) == PATH_FALLBACK):
+        need = n * k * 2
+    else:
+        need = 0
+    if need and workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    wp = _dev(workspace, "workspace") if workspace is not None and workspace.numel() else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = fp8w_linear_with_path(xp, act, m, k, qp, sp, bp, n, yp, wp, wb, path, _stream(x.device))
+    _check(st, "fp8w_linear")
+    return out
+
+
+def dequantize(q: torch.Tensor, scale: torch.Tensor = None, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """value(q) * scale[:, None] in ``dtype`` (fp32: exactly q.float() * scale[:, None]),
+    or the exact unscaled values when scale is None."""
+    n, k = q.shape
+    out = torch.empty((n, k), dtype=dtype, device=q.device)
+    st = fp8w_dequantize_fallback(_dev(q, "q") if q.numel() else 0,
+                                  _dev(scale, "scale") if scale is not None and n else 0,
+                                  n, k, out.data_ptr() if out.numel() else 0, _dtype_code(dtype),
+                                  _stream(q.device))
+    _check(st, "fp8w_dequantize_fallback")
+    return out
+
+
+class QuantizedLinear:
+    """An nn.Linear-shaped layer whose weight is held only as e4m3 codes + scales.
+
+    ``QuantizedLinear.build(weight, bias)`` quantises once; ``__call__(x)``
+    runs the fp8w linear. The original weight is not kept."""
+
+    def __init__(self, q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor = None):
+        self.q, self.scale, self.bias = q, scale, bias
+        self._ws = None
+
+    @classmethod
+    def build(cls, weight: torch.Tensor, bias: torch.Tensor = None) -> "QuantizedLinear":
+        q, scale = quantize(weight)
+        return cls(q, scale, bias)
+
+    @property
+    def out_features(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def in_features(self) -> int:
+        return self.q.shape[1]
+
+    def __call__(self, x: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        need = workspace_bytes(x2, self.q)
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.empty((need,), dtype=torch.uint8, device=x.device)
+        y = linear(x2, self.q, self.scale, self.bias, out=out, workspace=self._ws if need else None)
+        return y.reshape(*lead, self.out_features)

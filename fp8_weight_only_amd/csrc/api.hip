@@ -1,0 +1,275 @@
+// C ABI of libfp8w.so: argument validation, path selection and kernel
+// dispatch. Declarations and the contract of each call are in include/fp8w.h.
+#include <math.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/fp8w.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxNK = (int64_t)0x7fffffff;  // grid dimension and row-count limit
+constexpr int64_t kMaxM = (int64_t)65535 * 16;     // fallback token tiles on grid.y
+constexpr int64_t kMaxElems = (int64_t)1 << 62;
+
+fp8w_status_t hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return FP8W_SUCCESS;
+    g_last_hip_error = (int)e;
+    return FP8W_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a)
+{
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+int elem_bytes(fp8w_dtype_t t)
+{
+    return t == FP8W_FP32 ? 4 : 2;
+}
+
+bool valid_dtype(fp8w_dtype_t t)
+{
+    return t == FP8W_BF16 || t == FP8W_FP16 || t == FP8W_FP32;
+}
+
+bool valid_act(fp8w_dtype_t t)
+{
+    return t == FP8W_BF16 || t == FP8W_FP16;
+}
+
+fp8w::Act act_of(fp8w_dtype_t t)
+{
+    return t == FP8W_BF16 ? fp8w::Act::BF16 : (t == FP8W_FP16 ? fp8w::Act::FP16 : fp8w::Act::FP32);
+}
+
+bool sizes_ok(int64_t m, int64_t n, int64_t k)
+{
+    if (m < 0 || n < 0 || k < 0 || m > kMaxM || n > kMaxNK || k > kMaxNK)
+        return false;
+    return n == 0 || k <= kMaxElems / n;
+}
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap (empty ranges never do).
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0)
+        return false;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+// The fast kernels' coverage: see fp8w_linear in include/fp8w.h.
+bool fast_shape(int64_t m, int64_t k)
+{
+    return m >= 1 && m <= 32 && k >= 256 && k % 256 == 0;
+}
+
+bool fast_pointers(const void* x, const uint8_t* q)
+{
+    return aligned(x, 16) && aligned(q, 16);
+}
+
+int auto_path(int64_t m, int64_t k, const void* x, const uint8_t* q)
+{
+    if (fast_shape(m, k) && fast_pointers(x, q))
+        return m == 1 ? FP8W_PATH_GEMV : FP8W_PATH_SKINNY;
+    return FP8W_PATH_FALLBACK;
+}
+
+size_t fallback_workspace(int64_t n, int64_t k, fp8w_dtype_t act)
+{
+    return (size_t)n * (size_t)k * (size_t)elem_bytes(act);
+}
+
+fp8w_status_t check_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, const uint8_t* q,
+                           const float* scale, const void* bias, int64_t n, const void* y)
+{
+    if (!valid_act(act) || !sizes_ok(m, n, k))
+        return FP8W_ERR_INVALID_VALUE;
+    if (m == 0 || n == 0)
+        return FP8W_SUCCESS;
+    if (!y || !scale || (k > 0 && (!x || !q)))
+        return FP8W_ERR_INVALID_VALUE;
+    if (!aligned(x, 2) || !aligned(y, 2) || !aligned(bias, 2) || !aligned(scale, 4))
+        return FP8W_ERR_MISALIGNED;
+    const size_t eb = 2;
+    const size_t ybytes = (size_t)m * (size_t)n * eb;
+    if (overlap(y, ybytes, x, (size_t)m * (size_t)k * eb) || overlap(y, ybytes, q, (size_t)n * (size_t)k) ||
+        overlap(y, ybytes, scale, (size_t)n * 4) || overlap(y, ybytes, bias, bias ? (size_t)n * eb : 0))
+        return FP8W_ERR_INVALID_VALUE;
+    return FP8W_SUCCESS;
+}
+
+fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, const uint8_t* q,
+                         const float* scale, const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes,
+                         int path, hipStream_t stream)
+{
+    fp8w_status_t st = check_linear(x, act, m, k, q, scale, bias, n, y);
+    if (st != FP8W_SUCCESS)
+        return st;
+    if (path == FP8W_PATH_AUTO)
+        path = auto_path(m, k, x, q);
+    if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
+        if (path == FP8W_PATH_GEMV && m != 1 && m != 0)
+            return FP8W_ERR_INVALID_VALUE;
+        if (m > 32 || k % 256 != 0 || k == 0)
+            return FP8W_ERR_INVALID_VALUE;
+        if (!fast_pointers(x, q))
+            return FP8W_ERR_MISALIGNED;
+    } else if (path != FP8W_PATH_FALLBACK) {
+        return FP8W_ERR_INVALID_VALUE;
+    }
+    if (m == 0 || n == 0)
+        return FP8W_SUCCESS;
+
+    const fp8w::Act a = act_of(act);
+    if (path == FP8W_PATH_GEMV)
+        return hip_status(fp8w::launch_gemv(x, a, k, q, scale, bias, n, y, stream));
+    if (path == FP8W_PATH_SKINNY)
+        return hip_status(fp8w::launch_skinny(x, a, m, k, q, scale, bias, n, y, stream));
+
+    const size_t need = fallback_workspace(n, k, act);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return FP8W_ERR_WORKSPACE;
+        if (!aligned(ws, 2))
+            return FP8W_ERR_MISALIGNED;
+        const size_t ybytes = (size_t)m * (size_t)n * 2;
+        if (overlap(ws, need, y, ybytes) || overlap(ws, need, x, (size_t)m * (size_t)k * 2) ||
+            overlap(ws, need, q, (size_t)n * (size_t)k) || overlap(ws, need, scale, (size_t)n * 4) ||
+            overlap(ws, need, bias, bias ? (size_t)n * 2 : 0))
+            return FP8W_ERR_INVALID_VALUE;
+        st = hip_status(fp8w::launch_dequantize(q, nullptr, n, k, ws, a, stream));
+        if (st != FP8W_SUCCESS)
+            return st;
+    }
+    return hip_status(fp8w::launch_fallback_gemm(x, a, m, k, ws, scale, bias, n, y, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8w_status_t fp8w_quantize(const void* w, fp8w_dtype_t w_dtype, int64_t n, int64_t k, uint8_t* q, float* scale,
+                            hipStream_t stream)
+{
+    if (!valid_dtype(w_dtype) || !sizes_ok(0, n, k))
+        return FP8W_ERR_INVALID_VALUE;
+    if (n == 0)
+        return FP8W_SUCCESS;
+    if (!scale || (k > 0 && (!w || !q)))
+        return FP8W_ERR_INVALID_VALUE;
+    const size_t eb = (size_t)elem_bytes(w_dtype);
+    if (!aligned(w, eb) || !aligned(scale, 4))
+        return FP8W_ERR_MISALIGNED;
+    const size_t wbytes = (size_t)n * (size_t)k * eb;
+    if (overlap(q, (size_t)n * (size_t)k, w, wbytes) || overlap(scale, (size_t)n * 4, w, wbytes) ||
+        overlap(scale, (size_t)n * 4, q, (size_t)n * (size_t)k))
+        return FP8W_ERR_INVALID_VALUE;
+
+    fp8w_status_t st = hip_status(fp8w::launch_quantize(w, act_of(w_dtype), n, k, q, scale, stream));
+    if (st != FP8W_SUCCESS)
+        return st;
+    std::vector<float> host((size_t)n);
+    st = hip_status(hipMemcpyAsync(host.data(), scale, (size_t)n * 4, hipMemcpyDeviceToHost, stream));
+    if (st != FP8W_SUCCESS)
+        return st;
+    st = hip_status(hipStreamSynchronize(stream));
+    if (st != FP8W_SUCCESS)
+        return st;
+    for (float s : host)
+        if (!isfinite(s))
+            return FP8W_ERR_NONFINITE;
+    return FP8W_SUCCESS;
+}
+
+fp8w_status_t fp8w_linear(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k, const uint8_t* q,
+                          const float* scale, const void* bias, int64_t n, void* y, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    return run_linear(x, act_dtype, m, k, q, scale, bias, n, y, workspace, workspace_bytes, FP8W_PATH_AUTO,
+                      stream);
+}
+
+fp8w_status_t fp8w_linear_with_path(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                    const uint8_t* q, const float* scale, const void* bias, int64_t n, void* y,
+                                    void* workspace, size_t workspace_bytes, int path, hipStream_t stream)
+{
+    if (path < FP8W_PATH_AUTO || path > FP8W_PATH_FALLBACK)
+        return FP8W_ERR_INVALID_VALUE;
+    return run_linear(x, act_dtype, m, k, q, scale, bias, n, y, workspace, workspace_bytes, path, stream);
+}
+
+fp8w_status_t fp8w_dequantize_fallback(const uint8_t* q, const float* scale, int64_t n, int64_t k, void* out,
+                                       fp8w_dtype_t out_dtype, hipStream_t stream)
+{
+    if (!valid_dtype(out_dtype) || !sizes_ok(0, n, k))
+        return FP8W_ERR_INVALID_VALUE;
+    if (n == 0 || k == 0)
+        return FP8W_SUCCESS;
+    if (!q || !out)
+        return FP8W_ERR_INVALID_VALUE;
+    const size_t eb = (size_t)elem_bytes(out_dtype);
+    if (!aligned(out, eb) || !aligned(scale, 4))
+        return FP8W_ERR_MISALIGNED;
+    const size_t obytes = (size_t)n * (size_t)k * eb;
+    if (overlap(out, obytes, q, (size_t)n * (size_t)k) || overlap(out, obytes, scale, scale ? (size_t)n * 4 : 0))
+        return FP8W_ERR_INVALID_VALUE;
+    return hip_status(fp8w::launch_dequantize(q, scale, n, k, out, act_of(out_dtype), stream));
+}
+
+int fp8w_linear_path(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x, const uint8_t* q,
+                     const void* y)
+{
+    (void)y;
+    if (!valid_act(act_dtype) || !sizes_ok(m, n, k))
+        return -1;
+    return auto_path(m, k, x, q);
+}
+
+size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x,
+                                   const uint8_t* q, const void* y)
+{
+    const int p = fp8w_linear_path(m, n, k, act_dtype, x, q, y);
+    if (p != FP8W_PATH_FALLBACK)
+        return 0;
+    return fallback_workspace(n, k, act_dtype);
+}
+
+const char* fp8w_status_string(fp8w_status_t status)
+{
+    switch (status) {
+    case FP8W_SUCCESS:
+        return "success";
+    case FP8W_ERR_INVALID_VALUE:
+        return "invalid value (size, dtype, NULL pointer, overlapping buffers or path request)";
+    case FP8W_ERR_MISALIGNED:
+        return "misaligned pointer";
+    case FP8W_ERR_NONFINITE:
+        return "non-finite weight (NaN or infinity)";
+    case FP8W_ERR_WORKSPACE:
+        return "workspace missing or too small for the fallback path";
+    case FP8W_ERR_HIP:
+        return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int fp8w_last_hip_error(void)
+{
+    return g_last_hip_error;
+}
+
+int fp8w_abi_version(void)
+{
+    return 1;
+}
+
+}  // extern "C"

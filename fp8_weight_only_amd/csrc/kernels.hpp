@@ -1,0 +1,39 @@
+// Host-side launchers of the fp8w HIP kernels. Internal to the library: the
+// public interface is the C ABI in include/fp8w.h. Every launcher enqueues on
+// the given stream, returns the launch status, and assumes the C-ABI layer has
+// already validated sizes, pointers and alignment.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8w {
+
+enum class Act { BF16 = 0, FP16 = 1, FP32 = 2 };
+
+// Build-time quantizer: one workgroup per row; scale[r] = NaN marks a row with
+// a non-finite weight.
+hipError_t launch_quantize(const void* w, Act w_type, int64_t n, int64_t k, uint8_t* q, float* scale,
+                           hipStream_t stream);
+
+// M = 1 streaming GEMV; k % 256 == 0, x and q 16-byte aligned.
+hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,
+                       const void* bias, int64_t n, void* y, hipStream_t stream);
+
+// M = 1..32 MFMA skinny GEMM; k % 256 == 0, x and q 16-byte aligned.
+hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
+                         const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream);
+
+// Dequantize codes to out_type: value(q) * scale[r] (scale != nullptr) or the
+// exact unscaled value (scale == nullptr).
+hipError_t launch_dequantize(const uint8_t* q, const float* scale, int64_t n, int64_t k, void* out,
+                             Act out_type, hipStream_t stream);
+
+// Guarded GEMM over an activation-dtype weight wd [n, k] (any m, n, k, any
+// 2-byte alignment) followed by the scale/bias epilogue.
+hipError_t launch_fallback_gemm(const void* x, Act act, int64_t m, int64_t k, const void* wd,
+                                const float* scale, const void* bias, int64_t n, void* y,
+                                hipStream_t stream);
+
+}  // namespace fp8w

@@ -1,0 +1,168 @@
+/*
+ * fp8w — FP8 (OCP e4m3fn) weight-only linear layer for AMD MI355X (gfx950).
+ *
+ * C ABI of libfp8w.so. The method, from "FP8 weight-only (precision:
+ * fp8_weights)", section "The contract":
+ *   - at build time, once: one symmetric scale per output channel,
+ *       scale[n] = amax_k |W[n,k]| / 448   (fp32),
+ *       q[n,k]   = e4m3 code of W[n,k] / scale[n], rounded to nearest even and
+ *                  clamped to +-448; no higher-precision copy of W is kept;
+ *   - per call: y[m,n] = scale[n] * sum_k x[m,k] * value(q[n,k]) + bias[n],
+ *     activations stay bf16 / fp16, accumulation and the scale/bias epilogue
+ *     are fp32, and the result is rounded to the activation dtype once;
+ *   - shapes the fast kernels do not cover go through the dequantised weight
+ *     with the same numerics (section "The contract", item "Fallback").
+ * The e4m3 format is the OCP one (bias 7, largest finite 448, 0x7F / 0xFF NaN,
+ * 0x80 = -0): "B04 - Precision & Quantization", section "The numbers, derived
+ * rather than tabulated", and section "Hardware support, and where the vendors
+ * diverge" (not the FNUZ variant, whose maximum is 240).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense and row-major: W, q and a dequantised weight are
+ *     [n, k] (n output channels, k input features), x is [m, k], y is [m, n].
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates device memory and keeps no state between calls.
+ *   - Work is enqueued on `stream` (0 = the null stream) in stream order.
+ *     Only fp8w_quantize synchronizes (on `stream`), to report non-finite
+ *     weights. The other calls are asynchronous.
+ *   - Arguments are validated before anything is enqueued. An invalid call
+ *     returns an error and enqueues nothing.
+ *   - Sizes: 0 <= n, k <= 2^31 - 1; 0 <= m <= 1048560; n*k <= 2^62.
+ *     A zero-sized call is valid and enqueues nothing, except that k == 0
+ *     writes y = bias (or zeros).
+ *   - Thread-safe: there is no global mutable state.
+ */
+#ifndef FP8W_H
+#define FP8W_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FP8W_API __attribute__((visibility("default")))
+#else
+#define FP8W_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8W_BF16 = 0, /* bfloat16, 2 bytes */
+    FP8W_FP16 = 1, /* IEEE binary16, 2 bytes */
+    FP8W_FP32 = 2  /* IEEE binary32, 4 bytes */
+} fp8w_dtype_t;
+
+typedef enum {
+    FP8W_SUCCESS = 0,
+    FP8W_ERR_INVALID_VALUE = 1, /* bad size, dtype, NULL pointer, aliasing or path request */
+    FP8W_ERR_MISALIGNED = 2,    /* a pointer is not aligned to its element size, or a forced fast
+                                   path was asked for with pointers it cannot take */
+    FP8W_ERR_NONFINITE = 3,     /* fp8w_quantize: some weight is NaN or +-inf */
+    FP8W_ERR_WORKSPACE = 4,     /* fallback path needs a larger workspace */
+    FP8W_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+} fp8w_status_t;
+
+/* Dispatch paths (fp8w_linear_path, fp8w_linear_with_path). */
+#define FP8W_PATH_AUTO (-1)
+#define FP8W_PATH_GEMV 0     /* m == 1 streaming GEMV (fp32 FMA) */
+#define FP8W_PATH_SKINNY 1   /* 1 <= m <= 32, matrix-core (MFMA) skinny GEMM */
+#define FP8W_PATH_FALLBACK 2 /* unscaled dequantise to the activation dtype + guarded MFMA GEMM */
+
+/*
+ * Build-time quantizer ("The contract": scale = amax(|row|) / 448, codes
+ * round(w / scale) in e4m3, nearest even, clamped to +-448; "Skill: Write an
+ * FP8 Kernel", "Required reasoning process" steps 2 and 4).
+ *   w       [n, k] weights, element type w_dtype (FP32, or BF16 / FP16 widened
+ *           exactly to fp32), aligned to its element size.
+ *   q       [n, k] output codes (uint8, OCP e4m3fn).
+ *   scale   [n] output scales (fp32): fl32(amax / 448); 0 for an all-zero row,
+ *           whose codes are then all 0x00 (no division takes place).
+ *   Each code is the round-to-nearest-even e4m3 encoding of the fp32 quotient
+ *   fl32(w / scale), clamped to +-448; -0 and negative values that round to
+ *   zero give 0x80.
+ * Enqueues one kernel on `stream`, copies the scales back and synchronizes the
+ * stream. Returns FP8W_ERR_NONFINITE if any weight is NaN or infinite: the
+ * scale of every such row is then NaN and its codes are unspecified.
+ * q and scale must not overlap w.
+ */
+FP8W_API fp8w_status_t fp8w_quantize(const void* w, fp8w_dtype_t w_dtype, int64_t n, int64_t k, uint8_t* q,
+                            float* scale, hipStream_t stream);
+
+/*
+ * The linear layer, y[m,n] = scale[n] * sum_k x[m,k] * value(q[n,k]) + bias[n]
+ * ("The contract"), with fp32 accumulation and one rounding to act_dtype.
+ *   x         [m, k] activations, act_dtype = FP8W_BF16 or FP8W_FP16.
+ *   q, scale  as written by fp8w_quantize for an [n, k] weight.
+ *   bias      [n] in act_dtype, or NULL for none.
+ *   y         [m, n] output in act_dtype; must not overlap x, q, scale or bias.
+ *   workspace device scratch for the fallback path, at least
+ *             fp8w_linear_workspace_bytes(...) bytes (NULL / 0 when that is 0),
+ *             16-byte aligned for full speed; it must not overlap anything else.
+ * Dispatch (fp8w_linear_path): the fast kernels take 1 <= m <= 32 with
+ * k % 256 == 0 and x, q 16-byte aligned (m == 1: GEMV, else skinny MFMA);
+ * everything else takes the fallback. Results of different paths agree to
+ * within fp32 summation-order rounding. Asynchronous; a failed launch returns
+ * FP8W_ERR_HIP.
+ */
+FP8W_API fp8w_status_t fp8w_linear(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k, const uint8_t* q,
+                          const float* scale, const void* bias, int64_t n, void* y, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fp8w_linear with an explicit path (FP8W_PATH_*), for cross-checking the
+ * kernels against one another. FP8W_PATH_GEMV needs m == 1 and
+ * FP8W_PATH_SKINNY needs m <= 32, both with k % 256 == 0
+ * (FP8W_ERR_INVALID_VALUE otherwise) and 16-byte aligned x and q
+ * (FP8W_ERR_MISALIGNED otherwise). FP8W_PATH_FALLBACK takes any shape and needs
+ * n * k * element_size(act_dtype) bytes of workspace.
+ */
+FP8W_API fp8w_status_t fp8w_linear_with_path(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                    const uint8_t* q, const float* scale, const void* bias, int64_t n,
+                                    void* y, void* workspace, size_t workspace_bytes, int path,
+                                    hipStream_t stream);
+
+/*
+ * The dequantised weight ("The contract", item "Fallback": q.float() * scale[:, None]).
+ *   out[r, j] = out_dtype(fl32(value(q[r,j]) * scale[r]))  when scale != NULL
+ *               (FP32 is exactly q.float() * scale; BF16 / FP16 round that
+ *               fp32 product to nearest even),
+ *   out[r, j] = value(q[r,j])                              when scale == NULL
+ *               (exact in every out_dtype; this is what the fallback GEMM uses).
+ *   q [n, k] codes; scale [n] fp32 or NULL; out [n, k] of out_dtype
+ *   (FP8W_BF16, FP8W_FP16 or FP8W_FP32), not overlapping q or scale.
+ * Asynchronous.
+ */
+FP8W_API fp8w_status_t fp8w_dequantize_fallback(const uint8_t* q, const float* scale, int64_t n, int64_t k, void* out,
+                                       fp8w_dtype_t out_dtype, hipStream_t stream);
+
+/*
+ * Which path fp8w_linear takes for these sizes and pointers: FP8W_PATH_GEMV,
+ * FP8W_PATH_SKINNY or FP8W_PATH_FALLBACK; -1 when the arguments are invalid.
+ * NULL pointers are treated as 256-byte aligned.
+ */
+FP8W_API int fp8w_linear_path(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x, const uint8_t* q,
+                     const void* y);
+
+/* Workspace bytes fp8w_linear needs for these sizes and pointers (0 on the
+   fast paths, n * k * element_size(act_dtype) on the fallback; 0 when invalid). */
+FP8W_API size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x,
+                                   const uint8_t* q, const void* y);
+
+/* Static, NUL-terminated description of a status code. */
+FP8W_API const char* fp8w_status_string(fp8w_status_t status);
+
+/* The hipError_t of the most recent FP8W_ERR_HIP returned on this thread (0 if none). */
+FP8W_API int fp8w_last_hip_error(void);
+
+/* ABI version of this header: 1. */
+FP8W_API int fp8w_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8W_H */

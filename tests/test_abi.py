@@ -1,0 +1,180 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/fp8w.h declares, and rejects invalid arguments before it
+enqueues anything (so no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_weight_only_amd as fw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8w.h")
+
+# fake but aligned device addresses: validation must fail before they are used
+X = 0x10000000
+Q = 0x20000000
+S = 0x30000000
+B = 0x40000000
+Y = 0x50000000
+WS = 0x60000000
+
+
+def declared_symbols():
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"FP8W_API\s+[\w\s\*]+?\b(fp8w_\w+)\s*\(", text)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = fw.load()
+    names = declared_symbols()
+    assert len(names) == 9
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in fw.EXPORTS, name
+    assert fw.fp8w_abi_version() == 1
+
+
+def test_dynamic_symbol_table_has_only_the_abi():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", fw.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    ours = sorted(l.split()[-1] for l in out.splitlines() if " T " in l and "fp8w" in l)
+    assert ours == sorted(declared_symbols())
+
+
+def test_status_strings():
+    for st in range(6):
+        s = fw.fp8w_status_string(st)
+        assert isinstance(s, str) and s
+    assert fw.fp8w_status_string(0) == "success"
+    assert "unknown" in fw.fp8w_status_string(99)
+
+
+def test_path_selection():
+    p = fw.fp8w_linear_path
+    assert p(1, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_GEMV
+    assert p(2, 4096, 4096, fw.FP16, X, Q, Y) == fw.PATH_SKINNY
+    assert p(32, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_SKINNY
+    assert p(33, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK
+    assert p(1, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK      # k % 256 != 0
+    assert p(1, 100, 128, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # k < 256
+    assert p(1, 100, 0, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK           # k == 0
+    assert p(1, 4096, 4096, fw.BF16, X + 2, Q, Y) == fw.PATH_FALLBACK   # x not 16-B aligned
+    assert p(4, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_FALLBACK   # q not 16-B aligned
+    assert p(1, 4096, 4096, fw.BF16, 0, 0, 0) == fw.PATH_GEMV           # NULL = aligned
+    assert p(1, 4096, 4096, fw.FP32, X, Q, Y) == -1                     # fp32 activations
+    assert p(-1, 4096, 4096, fw.BF16, X, Q, Y) == -1
+    assert p(1, -5, 4096, fw.BF16, X, Q, Y) == -1
+    assert p(1, 1 << 31, 4096, fw.BF16, X, Q, Y) == -1
+
+
+def test_workspace_bytes():
+    wb = fw.fp8w_linear_workspace_bytes
+    assert wb(1, 4096, 4096, fw.BF16, X, Q, Y) == 0
+    assert wb(16, 4096, 4096, fw.BF16, X, Q, Y) == 0
+    assert wb(4, 28672, 8200, fw.BF16, X, Q, Y) == 28672 * 8200 * 2
+    assert wb(64, 100, 512, fw.FP16, X, Q, Y) == 100 * 512 * 2
+    assert wb(1, 10, 0, fw.BF16, X, Q, Y) == 0
+    assert wb(1, 4096, 4096, fw.FP32, X, Q, Y) == 0
+
+
+def _lin(x=X, act=fw.BF16, m=4, k=4096, q=Q, s=S, b=B, n=4096, y=Y, ws=0, wsb=0, path=fw.PATH_AUTO):
+    return fw.fp8w_linear_with_path(x, act, m, k, q, s, b, n, y, ws, wsb, path, 0)
+
+
+def test_linear_rejects_invalid_arguments():
+    assert _lin(act=fw.FP32) == fw.ERR_INVALID_VALUE
+    assert _lin(act=7) == fw.ERR_INVALID_VALUE
+    assert _lin(m=-1) == fw.ERR_INVALID_VALUE
+    assert _lin(n=-1) == fw.ERR_INVALID_VALUE
+    assert _lin(k=-256) == fw.ERR_INVALID_VALUE
+    assert _lin(m=2_000_000) == fw.ERR_INVALID_VALUE
+    assert _lin(x=0) == fw.ERR_INVALID_VALUE
+    assert _lin(q=0) == fw.ERR_INVALID_VALUE
+    assert _lin(s=0) == fw.ERR_INVALID_VALUE
+    assert _lin(y=0) == fw.ERR_INVALID_VALUE
+    assert _lin(s=S + 2) == fw.ERR_MISALIGNED
+    assert _lin(b=B + 1) == fw.ERR_MISALIGNED
+    assert _lin(y=Y + 1) == fw.ERR_MISALIGNED
+    assert _lin(path=3) == fw.ERR_INVALID_VALUE
+    assert _lin(path=-2) == fw.ERR_INVALID_VALUE
+    # forced paths the shape cannot take
+    assert _lin(m=2, path=fw.PATH_GEMV) == fw.ERR_INVALID_VALUE
+    assert _lin(m=33, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
+    assert _lin(k=4000, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
+    assert _lin(m=1, x=X + 2, path=fw.PATH_GEMV) == fw.ERR_MISALIGNED
+    # y overlapping an input
+    assert _lin(y=X + 64) == fw.ERR_INVALID_VALUE
+    assert _lin(y=Q) == fw.ERR_INVALID_VALUE
+    assert _lin(y=S - 16) == fw.ERR_INVALID_VALUE
+    assert _lin(y=B) == fw.ERR_INVALID_VALUE
+
+
+def test_linear_fallback_needs_workspace():
+    assert _lin(k=8200) == fw.ERR_WORKSPACE
+    assert _lin(k=8200, ws=WS, wsb=4096 * 8200 * 2 - 1) == fw.ERR_WORKSPACE
+    assert _lin(k=8200, ws=WS + 1, wsb=4096 * 8200 * 2) == fw.ERR_MISALIGNED
+    assert _lin(k=8200, ws=X, wsb=4096 * 8200 * 2) == fw.ERR_INVALID_VALUE  # overlaps x
+    assert _lin(m=64, path=fw.PATH_FALLBACK) == fw.ERR_WORKSPACE
+
+
+def test_zero_sized_calls_succeed_without_a_device():
+    assert _lin(m=0) == fw.SUCCESS
+    assert _lin(n=0) == fw.SUCCESS
+    assert _lin(m=0, x=0, y=0) == fw.SUCCESS
+    assert fw.fp8w_quantize(0, fw.FP32, 0, 100, 0, 0, 0) == fw.SUCCESS
+    assert fw.fp8w_dequantize_fallback(0, 0, 0, 100, 0, fw.BF16, 0) == fw.SUCCESS
+    assert fw.fp8w_dequantize_fallback(Q, S, 100, 0, 0, fw.BF16, 0) == fw.SUCCESS
+
+
+def test_quantize_rejects_invalid_arguments():
+    qz = fw.fp8w_quantize
+    assert qz(X, 9, 10, 10, Q, S, 0) == fw.ERR_INVALID_VALUE
+    assert qz(X, fw.FP32, -1, 10, Q, S, 0) == fw.ERR_INVALID_VALUE
+    assert qz(X, fw.FP32, 10, -1, Q, S, 0) == fw.ERR_INVALID_VALUE
+    assert qz(0, fw.FP32, 10, 10, Q, S, 0) == fw.ERR_INVALID_VALUE
+    assert qz(X, fw.FP32, 10, 10, 0, S, 0) == fw.ERR_INVALID_VALUE
+    assert qz(X, fw.FP32, 10, 10, Q, 0, 0) == fw.ERR_INVALID_VALUE
+    assert qz(X + 2, fw.FP32, 10, 10, Q, S, 0) == fw.ERR_MISALIGNED
+    assert qz(X, fw.FP32, 10, 10, Q, S + 1, 0) == fw.ERR_MISALIGNED
+    assert qz(X, fw.FP32, 10, 10, X + 16, S, 0) == fw.ERR_INVALID_VALUE  # q overlaps w
+    assert qz(X, fw.FP32, 10, 10, Q, X, 0) == fw.ERR_INVALID_VALUE       # scale overlaps w
+    assert qz(X, fw.FP32, 1 << 31, 10, Q, S, 0) == fw.ERR_INVALID_VALUE
+
+
+def test_dequantize_rejects_invalid_arguments():
+    dq = fw.fp8w_dequantize_fallback
+    assert dq(Q, S, 10, 10, Y, 5, 0) == fw.ERR_INVALID_VALUE
+    assert dq(0, S, 10, 10, Y, fw.BF16, 0) == fw.ERR_INVALID_VALUE
+    assert dq(Q, S, 10, 10, 0, fw.BF16, 0) == fw.ERR_INVALID_VALUE
+    assert dq(Q, S, 10, 10, Y + 2, fw.FP32, 0) == fw.ERR_MISALIGNED
+    assert dq(Q, S + 2, 10, 10, Y, fw.FP32, 0) == fw.ERR_MISALIGNED
+    assert dq(Q, S, 10, 10, Q + 4, fw.BF16, 0) == fw.ERR_INVALID_VALUE  # out overlaps q
+
+
+def test_product_path_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    """With libfp8w.so absent there is no fallback: every entry point raises."""
+    monkeypatch.setattr(fw, "_LIB", None)
+    monkeypatch.setattr(fw, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fw.fp8w_abi_version()
+    with pytest.raises(RuntimeError, match="missing"):
+        fw.fp8w_linear_path(1, 1, 256, fw.BF16, 0, 0, 0)
+
+
+def test_package_never_imports_the_oracle():
+    import subprocess
+    import sys
+    code = ("import sys; import fp8_weight_only_amd; "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), 'oracle imported'")
+    subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True)
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "fp8_weight_only_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                with open(os.path.join(dirpath, f)) as fh:
+                    text = fh.read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "fp8w_oracle" not in text and "liboracle" not in text, f

@@ -1,0 +1,237 @@
+"""GPU parity of the linear layer (fp8w_linear and its three paths) and of the
+exported dequantize, at sizes the oracle finishes in seconds that still span
+several tiles and ragged tails.
+
+Sources: "FP8 weight-only (precision: fp8_weights)", sections "The contract"
+and "Dequantise in registers"; "Inference with NVFP4/MXFP8" (cuTile-rs), the
+all-ones check; "Skill: Write an FP8 Kernel", step 7 (scale = 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_weight_only_amd as fw
+import oracle
+import workloads
+from parity_util import assert_gate, assert_same_bits, nan_like, oracle_case
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+PATHS = {fw.PATH_GEMV: "gemv", fw.PATH_SKINNY: "skinny", fw.PATH_FALLBACK: "fallback"}
+
+
+def _prepare(case):
+    w = torch.from_numpy(case.layer.w).to(DEV)
+    q, s = fw.quantize(w)
+    x = case.x.to(DEV)
+    b = None if case.layer.bias is None else case.layer.bias.to(DEV)
+    return q, s, x, b
+
+
+def _check(case, path=fw.PATH_AUTO, expect_path=None):
+    q, s, x, b = _prepare(case)
+    m, k = case.x.shape
+    n = case.layer.w.shape[0]
+    q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
+    assert_same_bits(q.cpu().numpy(), q_ref, "codes")
+    if expect_path is not None:
+        assert fw.linear_path(x, q) == expect_path
+    y = nan_like((m, n), case.x.dtype, DEV)
+    fw.linear(x, q, s, b, out=y, path=path)
+    torch.cuda.synchronize()
+    assert_gate(y.double().cpu().numpy(), y_ref, x64, amax, f"{case.layer.name} m={m} path={path}")
+    return y
+
+
+SMALL = [
+    # (m, n, k, dtype, bias, expected auto path)
+    (1, 1024, 1024, torch.bfloat16, True, fw.PATH_GEMV),
+    (1, 17, 256, torch.bfloat16, True, fw.PATH_GEMV),
+    (1, 300, 4352, torch.float16, False, fw.PATH_GEMV),
+    (1, 64, 14336, torch.bfloat16, True, fw.PATH_GEMV),
+    (2, 272, 512, torch.float16, True, fw.PATH_SKINNY),
+    (4, 100, 768, torch.bfloat16, False, fw.PATH_SKINNY),
+    (8, 33, 4096, torch.bfloat16, True, fw.PATH_SKINNY),
+    (16, 512, 1024, torch.float16, True, fw.PATH_SKINNY),
+    (17, 48, 2048, torch.bfloat16, True, fw.PATH_SKINNY),
+    (22, 130, 1280, torch.float16, True, fw.PATH_SKINNY),
+    (32, 256, 4096, torch.bfloat16, False, fw.PATH_SKINNY),
+    (33, 64, 512, torch.bfloat16, True, fw.PATH_FALLBACK),
+    (70, 40, 300, torch.float16, True, fw.PATH_FALLBACK),
+    (1, 77, 8200, torch.bfloat16, True, fw.PATH_FALLBACK),
+    (3, 50, 1, torch.bfloat16, True, fw.PATH_FALLBACK),
+    (5, 31, 37, torch.float16, False, fw.PATH_FALLBACK),
+    (4, 128, 200, torch.bfloat16, True, fw.PATH_FALLBACK),
+]
+
+
+@pytest.mark.parametrize("m,n,k,dtype,bias,path", SMALL)
+def test_linear_small_parity(m, n, k, dtype, bias, path):
+    print(f"linear m={m} n={n} k={k} {dtype} bias={bias} path={PATHS[path]}", flush=True)
+    case = workloads.random_case(m * 1000 + n, m, n, k, dtype, with_bias=bias)
+    _check(case, expect_path=path)
+
+
+@pytest.mark.parametrize("m,k", [(1, 256), (1, 4096), (2, 1024), (16, 768), (17, 512), (32, 2048)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_every_path_matches_the_oracle(m, k, dtype):
+    """Forced paths on covered shapes: the GEMV (m == 1), the skinny MFMA kernel
+    and the fallback each pass the gate on the same inputs."""
+    n = 200
+    case = workloads.random_case(7 + m + k, m, n, k, dtype)
+    paths = [fw.PATH_SKINNY, fw.PATH_FALLBACK] + ([fw.PATH_GEMV] if m == 1 else [])
+    outs = {}
+    for p in paths:
+        print(f"forced path {PATHS[p]} m={m} k={k} {dtype}", flush=True)
+        outs[p] = _check(case, path=p).double().cpu().numpy()
+    # the paths differ only in fp32 summation order
+    a = outs[fw.PATH_SKINNY]
+    for p, o in outs.items():
+        assert np.allclose(o, a, rtol=2e-2, atol=1e-2), PATHS[p]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK])
+def test_all_256_codes_decode_exactly_on_each_path(dtype, path):
+    """q[n, :] = n for every code n, unit scales and a one-hot x: y[n] is the
+    exact value of code n (0x7F / 0xFF give NaN). Pins each path's hardware
+    conversion (fp32 for the GEMV, bf16/f16 for the MFMA operands)."""
+    print(f"256 codes {dtype} path={PATHS[path]}", flush=True)
+    n, k = 256, 512
+    q = torch.arange(256, dtype=torch.int32).to(torch.uint8)[:, None].repeat(1, k).contiguous().to(DEV)
+    s = torch.ones(n, dtype=torch.float32, device=DEV)
+    m = 1 if path == fw.PATH_GEMV else 2
+    x = torch.zeros((m, k), dtype=dtype)
+    x[0, 5] = 1.0
+    if m == 2:
+        x[1, k - 1] = -2.0
+    y = nan_like((m, n), dtype, DEV)
+    fw.linear(x.to(DEV), q, s, None, out=y, path=path)
+    torch.cuda.synchronize()
+    yv = y.double().cpu().numpy()
+    ref = oracle.decode(np.arange(256))
+    fin = np.isfinite(ref)
+    assert np.array_equal(yv[0][fin], ref[fin])
+    assert np.all(np.isnan(yv[0][~fin]))
+    if m == 2:
+        assert np.array_equal(yv[1][fin], -2.0 * ref[fin])
+
+
+@pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK])
+def test_all_ones_closed_form(path):
+    """x = 1 and rows W[n,:] = c_n: all codes are 0x7E, so y = fl32(c_n/448)*448*K + b."""
+    k = 2048
+    n = 96
+    c = np.linspace(0.001, 2.0, n).astype(np.float32)
+    w = np.repeat(c[:, None], k, axis=1)
+    m = 1 if path == fw.PATH_GEMV else 3
+    b = torch.linspace(-1, 1, n).to(torch.bfloat16)
+    q, s = fw.quantize(torch.from_numpy(w).to(DEV))
+    assert torch.all(q == 0x7E)
+    y = nan_like((m, n), torch.bfloat16, DEV)
+    fw.linear(torch.ones((m, k), dtype=torch.bfloat16, device=DEV), q, s, b.to(DEV), out=y, path=path)
+    torch.cuda.synchronize()
+    expect = (c / np.float32(448.0)).astype(np.float64) * 448.0 * k + b.double().numpy()
+    got = y.double().cpu().numpy()
+    # fp32 accumulation of 448 * K is exact here; one bf16 rounding of the epilogue remains
+    assert np.all(np.abs(got - expect[None, :]) <= np.abs(expect)[None, :] * 2.0 ** -8)
+
+
+@pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK])
+def test_zero_rows_give_bias_exactly(path):
+    lay = workloads.block_layer(0)
+    w = lay.w[:512].copy()
+    zero_rows = np.flatnonzero(np.all(w == 0, axis=1))
+    w[[5, 77]] = 0.0
+    zero_rows = np.union1d(zero_rows, [5, 77])
+    m = 1 if path == fw.PATH_GEMV else 5
+    case = workloads.Case(workloads.Linear("zero_rows", w, torch.linspace(-3, 3, 512).to(torch.bfloat16)),
+                          workloads.activations(41, 0, m, 4096, torch.bfloat16))
+    y = _check(case, path=path)
+    yz = y[:, zero_rows].cpu()
+    assert torch.equal(yz, case.layer.bias[zero_rows][None, :].repeat(m, 1))
+
+
+@pytest.mark.parametrize("m", [1, 4, 32])
+def test_deterministic(m):
+    case = workloads.random_case(55, m, 700, 4096, torch.bfloat16)
+    q, s, x, b = _prepare(case)
+    first = fw.linear(x, q, s, b).clone()
+    for _ in range(5):
+        again = fw.linear(x, q, s, b)
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+def test_unaligned_activations_take_the_fallback():
+    case = workloads.random_case(61, 4, 96, 1024, torch.bfloat16)
+    q, s, _, b = _prepare(case)
+    buf = torch.zeros(4 * 1024 + 1, dtype=torch.bfloat16, device=DEV)
+    buf[1:] = case.x.reshape(-1).to(DEV)
+    x_view = buf[1:].view(4, 1024)
+    assert x_view.data_ptr() % 16 != 0
+    assert fw.linear_path(x_view, q) == fw.PATH_FALLBACK
+    y = nan_like((4, 96), torch.bfloat16, DEV)
+    fw.linear(x_view, q, s, b, out=y)
+    torch.cuda.synchronize()
+    q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
+    assert_gate(y.double().cpu().numpy(), y_ref, x64, amax, "unaligned x")
+
+
+def test_k_zero_gives_bias_and_empty_calls_write_nothing():
+    n = 40
+    b = torch.linspace(-2, 2, n).to(torch.bfloat16).to(DEV)
+    q = torch.empty((n, 0), dtype=torch.uint8, device=DEV)
+    s = torch.ones(n, dtype=torch.float32, device=DEV)
+    y = nan_like((3, n), torch.bfloat16, DEV)
+    fw.linear(torch.empty((3, 0), dtype=torch.bfloat16, device=DEV), q, s, b, out=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu(), b.cpu()[None, :].repeat(3, 1))
+    y2 = nan_like((3, n), torch.bfloat16, DEV)
+    fw.linear(torch.empty((3, 0), dtype=torch.bfloat16, device=DEV), q, s, None, out=y2)
+    torch.cuda.synchronize()
+    assert torch.all(y2 == 0)
+    # m == 0 and n == 0: nothing to do
+    q2 = torch.zeros((n, 256), dtype=torch.uint8, device=DEV)
+    out = fw.linear(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV), q2, s, b)
+    assert out.shape == (0, n)
+    q3 = torch.zeros((0, 256), dtype=torch.uint8, device=DEV)
+    out = fw.linear(torch.ones((2, 256), dtype=torch.bfloat16, device=DEV), q3,
+                    torch.empty(0, dtype=torch.float32, device=DEV))
+    assert out.shape == (2, 0)
+
+
+def test_runs_on_the_callers_stream():
+    case = workloads.random_case(71, 8, 333, 2048, torch.float16)
+    q, s, x, b = _prepare(case)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        y = fw.linear(x, q, s, b)
+    side.synchronize()
+    q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
+    assert_gate(y.double().cpu().numpy(), y_ref, x64, amax, "side stream")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape", [(64, 512), (33, 8200), (7, 13)])
+def test_dequantize_matches_oracle(out_dtype, shape):
+    """fp8w_dequantize_fallback: fp32 out is exactly q.float() * scale; bf16 / fp16
+    round that product to nearest even; without a scale the value is exact."""
+    g = np.random.default_rng(shape[1])
+    w = (g.standard_normal(shape) * 0.03).astype(np.float32)
+    q, s = fw.quantize(torch.from_numpy(w).to(DEV))
+    q_np, s_np = q.cpu().numpy(), s.cpu().numpy()
+    exact = oracle.dequantize_f64(q_np, s_np)
+    f32 = exact.astype(np.float32)  # one rounding of the exact product = the fp32 product
+    if out_dtype == torch.float32:
+        ref_bits = f32
+    elif out_dtype == torch.bfloat16:
+        ref_bits = oracle.round_bf16_bits(f32)
+    else:
+        ref_bits = f32.astype(np.float16)
+    got = fw.dequantize(q, s, out_dtype)
+    torch.cuda.synchronize()
+    got_np = got.cpu().view(torch.int32 if out_dtype == torch.float32 else torch.int16).numpy()
+    assert_same_bits(got_np.view(ref_bits.dtype), ref_bits, f"dequantize {out_dtype}")
+    unscaled = fw.dequantize(q, None, out_dtype).double().cpu().numpy()
+    assert np.array_equal(unscaled, oracle.dequantize_f64(q_np))

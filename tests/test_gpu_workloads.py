@@ -1,0 +1,118 @@
+"""GPU parity at the full sizes of the five synthetic workloads, through the
+same auto-dispatched fp8w_linear calls the benchmark times: scales and codes
+bit-identical to the oracle, every output within the gate.
+
+Workloads (seeded, see workloads.py): tiny GEMV 1024x1024; decode GEMV M=1 at
+4096x4096, 14336x4096, 4096x14336; skinny sweep 14336x4096 (Student-t
+weights, fp16) at M = 2..32; one decoder block's seven linears at M=16 with
+outlier and zero rows; large 28672x8192 / 8192x28672 / 28672x8200 (fallback)
+at M = 1, 4, 8, 32 with outlier activations.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_weight_only_amd as fw
+import oracle
+import workloads
+from parity_util import assert_gate, assert_same_bits, gate_sampled, nan_like
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _quantize_checked(layer):
+    q, s = fw.quantize(torch.from_numpy(layer.w).to(DEV))
+    q_ref, s_ref, st = oracle.quantize_rows(layer.w)
+    assert st == 0
+    assert_same_bits(s.cpu().numpy(), s_ref, f"{layer.name} scale")
+    assert_same_bits(q.cpu().numpy(), q_ref, f"{layer.name} codes")
+    return q, s, q_ref, s_ref
+
+
+def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path, full=True):
+    m, k = x.shape
+    n = layer.w.shape[0]
+    xd = x.to(DEV)
+    bd = None if layer.bias is None else layer.bias.to(DEV)
+    assert fw.linear_path(xd, q) == expect_path, (layer.name, m)
+    y = nan_like((m, n), x.dtype, DEV)
+    fw.linear(xd, q, s, bd, out=y)
+    torch.cuda.synchronize()
+    yv = y.double().cpu().numpy()
+    x64 = x.double().numpy()
+    b64 = None if layer.bias is None else layer.bias.double().numpy()
+    if full:
+        y_ref = oracle.linear_f64(x64, q_ref, s_ref, b64)
+        assert_gate(yv, y_ref, x64, amax, f"{layer.name} m={m}")
+        return yv, y_ref
+    # sampled: every row, 4096 seeded channels (including the first and last)
+    g = np.random.default_rng(m * 7 + n)
+    cols = np.unique(np.concatenate([[0, n - 1], g.choice(n, size=min(n, 4096), replace=False)]))
+    rows = np.repeat(np.arange(m), cols.size)
+    cc = np.tile(cols, m)
+    y_ref = oracle.linear_f64_sampled(x64, q_ref, s_ref, b64, rows, cc)
+    ok = gate_sampled(yv[rows, cc], y_ref, np.linalg.norm(x64, axis=1)[rows], amax[cc])
+    assert ok.all(), f"{layer.name} m={m}: {np.count_nonzero(~ok)} sampled outputs outside the gate"
+    assert np.all(np.isfinite(yv)), f"{layer.name} m={m}: non-finite outputs"
+    return yv, None
+
+
+def test_tiny_gemv():
+    case = workloads.tiny_gemv()
+    print("tiny gemv 1024x1024", flush=True)
+    q, s, q_ref, s_ref = _quantize_checked(case.layer)
+    amax = oracle.row_amax(case.layer.w)
+    yv, y_ref = _linear_checked(case.layer, q, s, q_ref, s_ref, case.x, amax, fw.PATH_GEMV)
+    rep = oracle.weight_error(case.layer.w, q_ref, s_ref)
+    print(f"  rel_l2={rep['rel_l2']:.4f} worst={rep['worst_channel_rel_l2']:.4f} "
+          f"underflow={rep['underflow']:.2e} {oracle.output_metrics(yv, y_ref)}", flush=True)
+
+
+@pytest.mark.parametrize("i", [0, 1, 2])
+def test_decode_gemv(i):
+    lay = workloads.decode_layer(i)
+    print(f"decode {lay.name}", flush=True)
+    q, s, q_ref, s_ref = _quantize_checked(lay)
+    amax = oracle.row_amax(lay.w)
+    _linear_checked(lay, q, s, q_ref, s_ref, workloads.decode_x(i), amax, fw.PATH_GEMV)
+
+
+def test_skinny_sweep():
+    lay = workloads.skinny_layer()
+    print(f"skinny {lay.name}", flush=True)
+    q, s, q_ref, s_ref = _quantize_checked(lay)
+    amax = oracle.row_amax(lay.w)
+    rep = oracle.weight_error(lay.w, q_ref, s_ref)
+    print(f"  student-t weights: rel_l2={rep['rel_l2']:.4f} worst={rep['worst_channel_rel_l2']:.4f} "
+          f"underflow={rep['underflow']:.2e} crest_max={rep['crest_max']:.1f}", flush=True)
+    for m in workloads.SKINNY_MS:
+        print(f"  m={m}", flush=True)
+        _linear_checked(lay, q, s, q_ref, s_ref, workloads.skinny_x(m), amax, fw.PATH_SKINNY)
+
+
+def test_decoder_block():
+    for i, (name, n, k) in enumerate(workloads.DECODER_BLOCK):
+        lay = workloads.block_layer(i)
+        print(f"block {name} [{n},{k}]", flush=True)
+        q, s, q_ref, s_ref = _quantize_checked(lay)
+        amax = oracle.row_amax(lay.w)
+        yv, _ = _linear_checked(lay, q, s, q_ref, s_ref, workloads.block_x(i), amax, fw.PATH_SKINNY)
+        zero = s_ref == 0
+        assert zero.sum() == int(round(0.005 * n))
+        assert np.all(yv[:, zero] == 0.0)  # no bias: zero rows give exact zeros
+
+
+@pytest.mark.parametrize("shape", workloads.LARGE_SHAPES + [workloads.LARGE_FALLBACK_SHAPE])
+def test_large(shape):
+    lay = workloads.large_layer(shape)
+    print(f"large {lay.name}", flush=True)
+    q, s, q_ref, s_ref = _quantize_checked(lay)
+    amax = oracle.row_amax(lay.w)
+    for m in workloads.LARGE_MS:
+        print(f"  m={m}", flush=True)
+        if shape == workloads.LARGE_FALLBACK_SHAPE:
+            path = fw.PATH_FALLBACK
+        else:
+            path = fw.PATH_GEMV if m == 1 else fw.PATH_SKINNY
+        _linear_checked(lay, q, s, q_ref, s_ref, workloads.large_x(shape, m), amax, path, full=(m <= 8))
