@@ -12,6 +12,9 @@
 
 namespace fp8w {
 
+// Note: __builtin_bit_cast is only ever applied to whole values here, never to
+// a vector element expression such as v.y (clang lowers that form to a read of
+// element 0).
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -29,11 +29,9 @@ struct OutF32 {
     // 8 values to a 32-byte aligned address
     __device__ __forceinline__ static void store8(void* p, int64_t i, const float* v)
     {
-        u32x4* d = reinterpret_cast<u32x4*>(static_cast<float*>(p) + i);
-        d[0] = u32x4{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
-                     __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
-        d[1] = u32x4{__builtin_bit_cast(uint32_t, v[4]), __builtin_bit_cast(uint32_t, v[5]),
-                     __builtin_bit_cast(uint32_t, v[6]), __builtin_bit_cast(uint32_t, v[7])};
+        f32x4* d = reinterpret_cast<f32x4*>(static_cast<float*>(p) + i);
+        d[0] = f32x4{v[0], v[1], v[2], v[3]};
+        d[1] = f32x4{v[4], v[5], v[6], v[7]};
     }
 };
 template <typename A>

@@ -33,14 +33,14 @@ struct WF32 {
     // 16 consecutive elements from a 16-byte aligned address
     __device__ __forceinline__ static void load16(const void* p, int64_t i, float* o)
     {
-        const u32x4* v = reinterpret_cast<const u32x4*>(static_cast<const float*>(p) + i);
+        const f32x4* v = reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const u32x4 d = v[j];
-            o[4 * j + 0] = __builtin_bit_cast(float, d.x);
-            o[4 * j + 1] = __builtin_bit_cast(float, d.y);
-            o[4 * j + 2] = __builtin_bit_cast(float, d.z);
-            o[4 * j + 3] = __builtin_bit_cast(float, d.w);
+            const f32x4 d = v[j];
+            o[4 * j + 0] = d.x;
+            o[4 * j + 1] = d.y;
+            o[4 * j + 2] = d.z;
+            o[4 * j + 3] = d.w;
         }
     }
 };
