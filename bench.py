@@ -2,25 +2,35 @@
 
 One step = one pass of the per-call hot path over the decode GEMV workload:
 three fp8w_linear calls at M = 1 (bf16 activations) on the weight shapes
-[4096, 4096], [14336, 4096] and [4096, 14336], each weight quantized once at
-build time (that build-time quantize is timed separately). Inputs are already
-resident in HBM when the timed region starts. Every step reads a different
-copy of the weight codes and scales (rotating through >= 1 GiB) so the 256 MB
-Infinity Cache cannot serve repeats: the kernels stream from HBM.
+[4096, 4096], [14336, 4096] and [4096, 14336]; each weight was quantized once
+at build time (that quantize is timed separately). Inputs are resident in HBM
+when the timed region starts, and every step reads a different copy of the
+weight codes and scales (rotating through >= 1 GiB) so the 256 MB Infinity
+Cache cannot serve repeats: the kernels stream from HBM.
 
-value = algorithmic bytes of the timed steps / timed wall time, in GB/s.
-Algorithmic bytes per call = N*K (codes) + 4N (scales) + 2N (bias) + 2MK (x)
-+ 2MN (y).
+Each step's three calls are captured once per weight copy into a HIP graph
+(torch.cuda.CUDAGraph around the ctypes calls, which launch on torch's current
+stream) and the timed region replays one graph per step, so host launch cost
+does not hide the kernels; the same loop launched eagerly is reported in
+"eager".
 
-The roofline entry is for the dominant kernel (the M=1 GEMV): achieved =
-algorithmic bytes of its launches / the sum of their durations, each launch
-timed with HIP events recorded on the stream it runs on (torch's current
-stream, which is the stream handed to fp8w_linear).
+value = algorithmic bytes of the timed steps / the timed region's duration
+(HIP events on the launch stream, around exactly --steps steps, with
+synchronizes on both sides). Algorithmic bytes per call = N*K (codes) + 4N
+(scales) + 2N (bias) + 2MK (x) + 2MN (y).
 
-Also reported (in "extra"): the build-time quantize, the skinny sweep
-(M = 2..32), one decoder block at M=16, the large shapes and their fallback,
-each with the same MALL rotation, and the oracle on the host cores
-("cpu_baseline").
+roofline: the dominant kernel is the M = 1 GEMV (it is every launch of the
+step): achieved = algorithmic bytes per launch / average launch duration, the
+duration being the timed region divided by its launches. Per-shape microseconds
+per call come from bursts of back-to-back launches of one shape between two
+events (the GPU overlaps consecutive dispatches, so a burst's average matches
+the profiler's kernel durations).
+
+Also reported ("extra"): the skinny sweep (M = 2..32, fp16), one decoder block
+at M = 16, the large shapes and their K = 8200 fallback, each with the same
+cache rotation; the build-time quantize; a plain streaming-read reference
+("read_ceiling": torch's int32 sum over buffers of each decode weight's size,
+rotated the same way); and the CPU oracle ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -59,8 +69,9 @@ def alg_bytes(m, n, k, bias=True):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "fp8_weight_only_amd", "csrc"))):
-        with open(os.path.join(ROOT, "fp8_weight_only_amd", "csrc", f), "rb") as fh:
+    d = os.path.join(ROOT, "fp8_weight_only_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -68,99 +79,135 @@ def kernel_source_hash():
 class Layer:
     """One quantized layer on the GPU with `copies` rotated copies of (q, scale)."""
 
-    def __init__(self, lw, copies, dev, dtype=torch.bfloat16):
+    def __init__(self, lw, copies, dev):
         w = torch.from_numpy(lw.w).to(dev)
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         q, s = fw.quantize(w)
-        t1.record()
+        e1.record()
         torch.cuda.synchronize()
-        self.quantize_ms = t0.elapsed_time(t1)
+        self.quantize_ms = e0.elapsed_time(e1)
         self.n, self.k = lw.w.shape
         self.name = lw.name
         del w
         self.qs = [(q, s)] + [(q.clone(), s.clone()) for _ in range(copies - 1)]
         self.bias = None if lw.bias is None else lw.bias.to(dev)
-        self.dtype = dtype
 
 
-def run_calls(calls, steps, stream, events=None):
-    """calls: list of (fn_args) for fw raw linear; each step issues every call once
-    with the copy index rotating. events: optional list to receive (start, end, idx)."""
-    lib = fw.load()
-    f = lib.fp8w_linear
-    for st in range(steps):
-        for ci, c in enumerate(calls):
-            args = c[st % len(c)]
-            if events is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                r = f(*args, stream)
-                e1.record()
-                events.append((e0, e1, ci))
-            else:
-                r = f(*args, stream)
-            if r != 0:
-                raise fw.Fp8wError(r, "fp8w_linear")
+class Call:
+    """Argument tuples of one fp8w_linear call for every weight copy."""
+
+    def __init__(self, layer, x, dev, ws=None):
+        self.layer, self.x = layer, x
+        self.m = x.shape[0]
+        self.y = torch.empty((self.m, layer.n), dtype=x.dtype, device=dev)
+        self.ws = ws
+        act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
+        self.path = ["gemv", "skinny", "fallback"][fw.linear_path(x, layer.qs[0][0])]
+        self.args = [(x.data_ptr(), act, self.m, layer.k, q.data_ptr(), s.data_ptr(),
+                      0 if layer.bias is None else layer.bias.data_ptr(), layer.n, self.y.data_ptr(),
+                      0 if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel())
+                     for q, s in layer.qs]
+        self.bytes = alg_bytes(self.m, layer.n, layer.k, layer.bias is not None)
+
+    def launch(self, copy, stream):
+        r = fw.load().fp8w_linear(*self.args[copy % len(self.args)], stream)
+        if r != 0:
+            raise fw.Fp8wError(r, "fp8w_linear")
 
 
-def build_calls(layer, x, y, ws=None):
-    act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
-    m, k = x.shape
+def burst_us(call, reps, warmup, stream, warm=False):
+    """Average microseconds per launch over `reps` back-to-back launches of one call
+    (rotating weight copies unless warm), between two events on the launch stream."""
+    for i in range(warmup):
+        call.launch(0 if warm else i, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        call.launch(0 if warm else i, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def call_report(call, us):
+    gbps = call.bytes / (us * 1e-6) / 1e9
+    return {"layer": call.layer.name, "m": call.m, "n": call.layer.n, "k": call.layer.k, "path": call.path,
+            "us_per_call": round(us, 3), "alg_bytes": call.bytes, "gbps": round(gbps, 1),
+            "pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+            "tflops": round(2.0 * call.m * call.layer.n * call.layer.k / (us * 1e-6) / 1e12, 3)}
+
+
+def capture_graphs(calls, copies, stream_obj):
+    """One HIP graph per weight copy, each holding one step (every call once)."""
+    graphs = []
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream_obj):
+            st = torch.cuda.current_stream().cuda_stream
+            for call in calls:
+                call.launch(c, st)
+        graphs.append(g)
+    return graphs
+
+
+def timed_steps(calls, steps, warmup, copies, use_graph, dev):
+    """Duration (ms) of exactly `steps` steps, events around them and synchronizes on both sides."""
+    stream = torch.cuda.current_stream(dev)
+    graphs = None
+    if use_graph:
+        side = torch.cuda.Stream(device=dev)
+        graphs = capture_graphs(calls, copies, side)
+    torch.cuda.synchronize()
+
+    def step(i):
+        if graphs is not None:
+            graphs[i % copies].replay()
+        else:
+            for call in calls:
+                call.launch(i, stream.cuda_stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def read_ceiling(dev, sizes, reps=100):
+    """A plain streaming read of the same byte counts (torch int32 sum), rotating
+    through 1 GiB: the reference the GEMV's achieved bandwidth is read against."""
+    big = torch.ones(ROTATE_BYTES // 4, dtype=torch.int32, device=dev)
     out = []
-    for q, s in layer.qs:
-        out.append((x.data_ptr(), act, m, k, q.data_ptr(), s.data_ptr(),
-                    0 if layer.bias is None else layer.bias.data_ptr(), layer.n, y.data_ptr(),
-                    0 if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel()))
+    for nbytes in sizes:
+        cnt = nbytes // 4
+        copies = max(1, big.numel() // cnt)
+        views = [big[i * cnt:(i + 1) * cnt] for i in range(copies)]
+        for i in range(10):
+            views[i % copies].sum()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            views[i % copies].sum()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out.append({"bytes": nbytes, "us": round(us, 3), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    del big
+    torch.cuda.empty_cache()
     return out
-
-
-def time_calls(calls, steps, warmup, stream):
-    """Whole-step wall time (events around the timed region) and per-launch event durations."""
-    run_calls(calls, warmup, stream)
-    torch.cuda.synchronize()
-    ev = []
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    g0.record()
-    run_calls(calls, steps, stream, events=ev)
-    g1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    total_ms = g0.elapsed_time(g1)
-    per = [[] for _ in calls]
-    for e0, e1, ci in ev:
-        per[ci].append(e0.elapsed_time(e1) * 1e3)  # us
-    return total_ms, wall, per
-
-
-def summarize_us(v):
-    a = np.asarray(v)
-    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
-            "p90": float(np.percentile(a, 90)), "mean": float(a.mean())}
-
-
-def bench_shapes(name, layers, xs, steps, warmup, dev, stream, ws_bytes=0):
-    ys = [torch.empty((x.shape[0], L.n), dtype=x.dtype, device=dev) for L, x in zip(layers, xs)]
-    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
-    calls = [build_calls(L, x, y, ws) for L, x, y in zip(layers, xs, ys)]
-    total_ms, wall, per = time_calls(calls, steps, warmup, stream)
-    rows = []
-    for L, x, p in zip(layers, xs, per):
-        m = x.shape[0]
-        b = alg_bytes(m, L.n, L.k, L.bias is not None)
-        s = summarize_us(p)
-        rows.append({"layer": L.name, "m": m, "n": L.n, "k": L.k,
-                     "path": ["gemv", "skinny", "fallback"][fw.linear_path(x, L.qs[0][0])],
-                     "us_per_call": s, "alg_bytes": b,
-                     "gbps_median": b / (s["median"] * 1e-6) / 1e9,
-                     "pct_peak_median": 100.0 * b / (s["median"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-                     "tflops_median": 2.0 * m * L.n * L.k / (s["median"] * 1e-6) / 1e12})
-    return {"name": name, "steps": steps, "timed_ms": total_ms, "wall_s": wall, "calls": rows}
 
 
 def cpu_info():
@@ -170,24 +217,23 @@ def cpu_info():
         for line in out.splitlines():
             if line.startswith("Model name"):
                 model = line.split(":", 1)[1].strip()
-    except Exception:
+    except Exception:  # noqa: BLE001
         pass
     return os.cpu_count(), model
 
 
-def cpu_baseline(layers_np, xs, budget_s=10.0):
-    """The oracle (fp64 C, OpenMP over rows) on the host cores, on the same decode
-    calls, repeated until ~budget_s of CPU work: GB/s of algorithmic bytes."""
+def cpu_baseline(layers_np, xs, budget_s):
+    """The oracle (fp64 C, OpenMP over output channels) on the host cores, on the
+    same three decode calls, repeated until ~budget_s of CPU work."""
     import oracle
     prepared = []
     for lw, x in zip(layers_np, xs):
-        q, s, st = oracle.quantize_rows(lw.w)
+        q, s, _ = oracle.quantize_rows(lw.w)
         prepared.append((x.double().numpy(), q, s, None if lw.bias is None else lw.bias.double().numpy()))
-    reps = 0
-    byts = 0
+    reps, byts = 0, 0
     t0 = time.perf_counter()
     while True:
-        for (x64, q, s, b), lw in zip(prepared, layers_np):
+        for (x64, q, s, b) in prepared:
             oracle.linear_f64(x64, q, s, b)
             byts += alg_bytes(x64.shape[0], q.shape[0], q.shape[1], b is not None)
         reps += 1
@@ -195,15 +241,15 @@ def cpu_baseline(layers_np, xs, budget_s=10.0):
         if el >= budget_s:
             break
     nproc, model = cpu_info()
-    return {"value": byts / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} passes over the 3 decode GEMV calls (M=1; 4096x4096, 14336x4096, 4096x14336), "
-                      f"fp64 oracle, {el:.1f} s",
+    return {"value": round(byts / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} passes over the 3 decode GEMV calls (M=1; 4096x4096, 14336x4096, 4096x14336) "
+                      f"through the fp64 oracle, {el:.1f} s",
             "host_cpus": nproc, "host_model": model}
 
 
-def traffic_entry(bytes_per_launch):
-    """HBM traffic of the GEMV from the committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel sources; else None."""
+def traffic_entry():
+    """HBM traffic per GEMV launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -214,19 +260,37 @@ def traffic_entry(bytes_per_launch):
     return t.get("bytes_per_launch")
 
 
+def parity_check(layers, lws, xs_cpu, xs):
+    import oracle
+    ok = True
+    for L, lw, xc, x in zip(layers, lws, xs_cpu, xs):
+        q_ref, s_ref, _ = oracle.quantize_rows(lw.w)
+        ok &= bool(np.array_equal(L.qs[0][0].cpu().numpy(), q_ref))
+        ok &= bool(np.array_equal(L.qs[0][1].cpu().numpy().view(np.uint32), s_ref.view(np.uint32)))
+        y = fw.linear(x, L.qs[0][0], L.qs[0][1], L.bias)
+        x64 = xc.double().numpy()
+        b64 = None if lw.bias is None else lw.bias.double().numpy()
+        y_ref = oracle.linear_f64(x64, q_ref, s_ref, b64)
+        tol = 1e-2 * np.abs(y_ref) + 1e-3 * np.linalg.norm(x64, axis=1)[:, None] * oracle.row_amax(lw.w)[None, :]
+        yv = y.double().cpu().numpy()
+        ok &= bool(np.all(np.isfinite(yv)) and np.all(np.abs(yv - y_ref) <= tol))
+    return ok
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--quick", action="store_true", help="decode workload only (no extra sections)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time the eager launch loop instead of graphs")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the per-GPU shard is the "
-              "measured unit; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (each GPU would hold its own "
+              "shard of the weight; the per-GPU kernel is what is measured here)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -241,76 +305,81 @@ def main():
     # ---------------------------------------------------------------- decode workload (the metric)
     per_step = sum(alg_bytes(1, n, k) for n, k in workloads.DECODE_SHAPES)
     copies = max(1, math.ceil(ROTATE_BYTES / per_step))
-    log(f"decode workload: {per_step / 1e6:.2f} MB per step, {copies} rotated copies")
+    log(f"decode workload: {per_step / 1e6:.2f} MB per step, {copies} rotated weight copies")
     lws = [workloads.decode_layer(i) for i in range(3)]
     layers = [Layer(lw, copies, dev) for lw in lws]
     xs_cpu = [workloads.decode_x(i) for i in range(3)]
     xs = [x.to(dev) for x in xs_cpu]
-    quant = [{"layer": L.name, "ms": L.quantize_ms, "gbps": 5.0 * L.n * L.k / (L.quantize_ms * 1e-3) / 1e9}
-             for L in layers]
+    calls = [Call(L, x, dev) for L, x in zip(layers, xs)]
+    quant = [{"layer": L.name, "ms": round(L.quantize_ms, 4),
+              "gbps": round(5.0 * L.n * L.k / (L.quantize_ms * 1e-3) / 1e9, 1)} for L in layers]
 
-    # parity of what is timed (the oracle is test infrastructure; checked once, before timing)
-    parity = True
     try:
-        import oracle
-        for L, lw, xc, x in zip(layers, lws, xs_cpu, xs):
-            q_ref, s_ref, _ = oracle.quantize_rows(lw.w)
-            if not np.array_equal(L.qs[0][0].cpu().numpy(), q_ref):
-                parity = False
-            y = fw.linear(x, L.qs[0][0], L.qs[0][1], L.bias)
-            x64 = xc.double().numpy()
-            y_ref = oracle.linear_f64(x64, q_ref, s_ref, lw.bias.double().numpy())
-            tol = 1e-2 * np.abs(y_ref) + 1e-3 * np.linalg.norm(x64) * oracle.row_amax(lw.w)[None, :]
-            yv = y.double().cpu().numpy()
-            parity &= bool(np.all(np.isfinite(yv)) and np.all(np.abs(yv - y_ref) <= tol))
-    except Exception as e:  # noqa: BLE001
+        parity = parity_check(layers, lws, xs_cpu, xs)
+    except ImportError as e:
         log(f"parity check skipped: {e}")
         parity = None
     log(f"parity vs oracle: {parity}")
 
-    res = bench_shapes("decode", layers, xs, args.steps, args.warmup, dev, stream)
-    step_bytes = per_step
-    value = step_bytes * args.steps / (res["timed_ms"] * 1e-3) / 1e9
-    ms_per_step = res["timed_ms"] / args.steps
-    # roofline: the GEMV launches, timed one by one with events on their stream
-    gemv_bytes = sum(c["alg_bytes"] for c in res["calls"])
-    gemv_us = sum(c["us_per_call"]["mean"] for c in res["calls"])
-    achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
-    for c in res["calls"]:
-        log(f"  {c['layer']}: median {c['us_per_call']['median']:.2f} us  {c['gbps_median']:.0f} GB/s "
-            f"({c['pct_peak_median']:.1f}% of 8 TB/s)")
-    log(f"step: {ms_per_step * 1e3:.2f} us, {value:.0f} GB/s whole-step")
+    per_call = []
+    for c in calls:
+        us = burst_us(c, 200, 20, stream)
+        per_call.append(call_report(c, us))
+        r = per_call[-1]
+        log(f"  {r['layer']}: {r['us_per_call']:.2f} us/call  {r['gbps']:.0f} GB/s ({r['pct_peak']:.1f}% of 8 TB/s)")
+    warm = [call_report(c, burst_us(c, 200, 20, stream, warm=True)) for c in calls]
+    ceiling = read_ceiling(dev, [c.layer.n * c.layer.k for c in calls])
 
-    traffic = traffic_entry(gemv_bytes / len(res["calls"]))
+    use_graph = not args.no_graph
+    try:
+        ms = timed_steps(calls, args.steps, args.warmup, copies, use_graph, dev)
+    except Exception as e:  # noqa: BLE001
+        if not use_graph:
+            raise
+        log(f"graph capture failed ({e}); timing the eager loop")
+        use_graph = False
+        ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
+    eager_ms = timed_steps(calls, max(200, args.steps // 10), 20, copies, False, dev) if use_graph else ms
+    eager_steps = max(200, args.steps // 10) if use_graph else args.steps
+    value = per_step * args.steps / (ms * 1e-3) / 1e9
+    ms_per_step = ms / args.steps
+    launches = args.steps * len(calls)
+    mean_launch_us = ms * 1e3 / launches
+    achieved = (per_step / len(calls)) / (mean_launch_us * 1e-6) / 1e9
+    log(f"timed region ({'graph' if use_graph else 'eager'}): {ms_per_step * 1e3:.2f} us/step, {value:.0f} GB/s; "
+        f"eager {eager_ms * 1e3 / eager_steps:.2f} us/step")
+
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "decode GEMV, M=1: three fp8w_linear calls per step on W e4m3 [4096,4096], "
-                               "[14336,4096], [4096,14336] (N(0,0.02^2) weights, per-channel scales), "
-                               "x bf16 N(0,1), zero bf16 bias, weights rotated through >= 1 GiB",
+        "config": {"workload": "decode GEMV, M=1: three fp8w_linear calls per step on e4m3 weights [4096,4096], "
+                               "[14336,4096], [4096,14336] (N(0,0.02^2) fp32 -> per-channel scales), x bf16 N(0,1), "
+                               "zero bf16 bias; weight copies rotated through >= 1 GiB",
                    "m": 1, "shapes_nk": workloads.DECODE_SHAPES, "act_dtype": "bf16", "weight_dtype": "e4m3fn",
-                   "accumulate": "f32", "rotated_copies": copies, "bytes_per_step": step_bytes},
+                   "accumulate": "f32", "rotated_copies": copies, "bytes_per_step": per_step,
+                   "launch": "hipGraph replay, one graph per weight copy" if use_graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "kernel": "gemv_kernel (M=1 GEMV)",
-                     "alg_bytes_per_launch": gemv_bytes / len(res["calls"]),
-                     "mean_launch_us": gemv_us / len(res["calls"])},
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_entry(),
+                     "kernel": "gemv_kernel (M=1 GEMV, every launch of the step)",
+                     "alg_bytes_per_launch": per_step / len(calls), "mean_launch_us": round(mean_launch_us, 3)},
         "parity": parity,
-        "per_call": res["calls"],
+        "per_call": per_call,
+        "warm_per_call": warm,
+        "eager": {"us_per_step": round(eager_ms * 1e3 / eager_steps, 3),
+                  "gbps": round(per_step * eager_steps / (eager_ms * 1e-3) / 1e9, 1)},
         "quantize": quant,
+        "read_ceiling": ceiling,
     }
 
     if not args.quick:
-        out["extra"] = extra_sections(dev, stream, max(50, args.steps // 5), max(10, args.warmup // 5))
+        out["extra"] = extra_sections(dev, stream)
 
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(lws, xs_cpu, args.cpu_budget)
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)...")
-        out["cpu_baseline"] = cpu_baseline(lws, xs_cpu, args.cpu_budget)
-    else:
-        out["cpu_baseline"] = None
+        log(f"cpu baseline: {out['cpu_baseline']['value']} GB/s on {out['cpu_baseline']['cores']} threads")
 
-    # a plain 256 MiB device copy: the calibration point for --pmc FETCH_SIZE / WRITE_SIZE
+    # a plain 256 MiB device copy: the calibration point for --pmc FETCH_SIZE / WRITE_SIZE runs
     a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     b.copy_(a)
@@ -318,55 +387,54 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def extra_sections(dev, stream, steps, warmup):
+def extra_sections(dev, stream, reps=100):
     ex = {}
-    # skinny sweep, fp16
-    lw = workloads.skinny_layer()
+    # skinny sweep, fp16 activations
     per = alg_bytes(32, 14336, 4096)
-    L = Layer(lw, max(1, math.ceil(ROTATE_BYTES / per)), dev, torch.float16)
+    L = Layer(workloads.skinny_layer(), max(1, math.ceil(ROTATE_BYTES / per)), dev)
     sk = []
     for m in workloads.SKINNY_MS:
-        x = workloads.skinny_x(m).to(dev)
-        r = bench_shapes(f"skinny_m{m}", [L], [x], steps, warmup, dev, stream)
-        c = r["calls"][0]
-        log(f"  skinny m={m}: {c['us_per_call']['median']:.2f} us {c['pct_peak_median']:.1f}% of peak")
-        sk.append(c)
+        c = Call(L, workloads.skinny_x(m).to(dev), dev)
+        sk.append(call_report(c, burst_us(c, reps, 10, stream)))
+        log(f"  skinny m={m}: {sk[-1]['us_per_call']:.2f} us {sk[-1]['pct_peak']:.1f}% of peak [{c.path}]")
     ex["skinny_sweep"] = sk
-    ex["skinny_quantize_ms"] = L.quantize_ms
+    ex["skinny_quantize_ms"] = round(L.quantize_ms, 3)
     del L
     torch.cuda.empty_cache()
 
-    # decoder block at M=16 (seven calls per step)
+    # one decoder block at M = 16: seven calls per step, per-call bursts and graph-timed steps
     blk_bytes = sum(alg_bytes(16, n, k, False) for _, n, k in workloads.DECODER_BLOCK)
     copies = max(1, math.ceil(ROTATE_BYTES / blk_bytes))
     Ls = [Layer(workloads.block_layer(i), copies, dev) for i in range(len(workloads.DECODER_BLOCK))]
-    xs = [workloads.block_x(i).to(dev) for i in range(len(workloads.DECODER_BLOCK))]
-    r = bench_shapes("decoder_block_m16", Ls, xs, steps, warmup, dev, stream)
-    tot_us = sum(c["us_per_call"]["median"] for c in r["calls"])
-    r["block_us_sum_of_medians"] = tot_us
-    r["block_gbps"] = blk_bytes / (tot_us * 1e-6) / 1e9
-    r["block_step_us"] = r["timed_ms"] * 1e3 / steps
-    log(f"  decoder block m=16: {tot_us:.1f} us (sum of medians), {r['block_gbps']:.0f} GB/s")
-    ex["decoder_block"] = r
-    del Ls
+    calls = [Call(Li, workloads.block_x(i).to(dev), dev) for i, Li in enumerate(Ls)]
+    blk = [call_report(c, burst_us(c, reps, 10, stream)) for c in calls]
+    try:
+        ms = timed_steps(calls, 200, 10, copies, True, dev)
+        mode = "graph"
+    except Exception:  # noqa: BLE001
+        ms = timed_steps(calls, 200, 10, copies, False, dev)
+        mode = "eager"
+    ex["decoder_block"] = {"calls": blk, "us_sum_of_calls": round(sum(b["us_per_call"] for b in blk), 2),
+                           "step_us": round(ms * 1e3 / 200, 2), "step_mode": mode,
+                           "step_gbps": round(blk_bytes / (ms * 1e-3 / 200) / 1e9, 1), "bytes": blk_bytes}
+    log(f"  decoder block m=16: {ex['decoder_block']['step_us']:.1f} us/step ({mode}), "
+        f"{ex['decoder_block']['step_gbps']:.0f} GB/s")
+    del Ls, calls
     torch.cuda.empty_cache()
 
-    # large shapes (+ the K=8200 fallback)
+    # large shapes and the k = 8200 fallback
     lg = []
     for shape in workloads.LARGE_SHAPES + [workloads.LARGE_FALLBACK_SHAPE]:
-        lw = workloads.large_layer(shape)
         per = alg_bytes(32, *shape, False)
-        L = Layer(lw, max(1, math.ceil(ROTATE_BYTES / per)), dev)
-        del lw
+        L = Layer(workloads.large_layer(shape), max(1, math.ceil(ROTATE_BYTES / per)), dev)
         for m in workloads.LARGE_MS:
             x = workloads.large_x(shape, m).to(dev)
-            ws = fw.workspace_bytes(x, L.qs[0][0])
-            r = bench_shapes(f"large_{shape}_m{m}", [L], [x], max(20, steps // 2), warmup, dev, stream, ws)
-            c = r["calls"][0]
-            log(f"  large {shape} m={m} [{c['path']}]: {c['us_per_call']['median']:.2f} us "
-                f"{c['pct_peak_median']:.1f}% of peak")
-            lg.append(c)
-        lg.append({"layer": L.name, "quantize_ms": L.quantize_ms})
+            wsb = fw.workspace_bytes(x, L.qs[0][0])
+            ws = torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None
+            c = Call(L, x, dev, ws)
+            lg.append(call_report(c, burst_us(c, max(20, reps // 2), 5, stream)))
+            log(f"  large {shape} m={m} [{c.path}]: {lg[-1]['us_per_call']:.2f} us {lg[-1]['pct_peak']:.1f}% of peak")
+        lg.append({"layer": L.name, "quantize_ms": round(L.quantize_ms, 3)})
         del L
         torch.cuda.empty_cache()
     ex["large"] = lg

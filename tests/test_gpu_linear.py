@@ -56,6 +56,10 @@ SMALL = [
     (17, 48, 2048, torch.bfloat16, True, fw.PATH_SKINNY),
     (22, 130, 1280, torch.float16, True, fw.PATH_SKINNY),
     (32, 256, 4096, torch.bfloat16, False, fw.PATH_SKINNY),
+    (6, 8200, 256, torch.bfloat16, True, fw.PATH_SKINNY),
+    (12, 40, 768, torch.float16, False, fw.PATH_SKINNY),
+    (20, 8192, 512, torch.float16, True, fw.PATH_SKINNY),
+    (3, 8192, 1024, torch.bfloat16, True, fw.PATH_SKINNY),
     (33, 64, 512, torch.bfloat16, True, fw.PATH_FALLBACK),
     (70, 40, 300, torch.float16, True, fw.PATH_FALLBACK),
     (1, 77, 8200, torch.bfloat16, True, fw.PATH_FALLBACK),
@@ -91,20 +95,21 @@ def test_every_path_matches_the_oracle(m, k, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK])
-def test_all_256_codes_decode_exactly_on_each_path(dtype, path):
+@pytest.mark.parametrize("path,m", [(fw.PATH_GEMV, 1), (fw.PATH_SKINNY, 2), (fw.PATH_SKINNY, 6),
+                                    (fw.PATH_SKINNY, 12), (fw.PATH_SKINNY, 20), (fw.PATH_FALLBACK, 2)])
+def test_all_256_codes_decode_exactly_on_each_path(dtype, path, m):
     """q[n, :] = n for every code n, unit scales and a one-hot x: y[n] is the
-    exact value of code n (0x7F / 0xFF give NaN). Pins each path's hardware
-    conversion (fp32 for the GEMV, bf16/f16 for the MFMA operands)."""
-    print(f"256 codes {dtype} path={PATHS[path]}", flush=True)
+    exact value of code n (0x7F / 0xFF give NaN). Pins each kernel's hardware
+    conversion (fp32 for the GEMV, bf16/f16 for the MFMA operands) and its
+    operand layout."""
+    print(f"256 codes {dtype} path={PATHS[path]} m={m}", flush=True)
     n, k = 256, 512
     q = torch.arange(256, dtype=torch.int32).to(torch.uint8)[:, None].repeat(1, k).contiguous().to(DEV)
     s = torch.ones(n, dtype=torch.float32, device=DEV)
-    m = 1 if path == fw.PATH_GEMV else 2
     x = torch.zeros((m, k), dtype=dtype)
     x[0, 5] = 1.0
-    if m == 2:
-        x[1, k - 1] = -2.0
+    if m >= 2:
+        x[m - 1, k - 1] = -2.0
     y = nan_like((m, n), dtype, DEV)
     fw.linear(x.to(DEV), q, s, None, out=y, path=path)
     torch.cuda.synchronize()
@@ -113,8 +118,10 @@ def test_all_256_codes_decode_exactly_on_each_path(dtype, path):
     fin = np.isfinite(ref)
     assert np.array_equal(yv[0][fin], ref[fin])
     assert np.all(np.isnan(yv[0][~fin]))
-    if m == 2:
-        assert np.array_equal(yv[1][fin], -2.0 * ref[fin])
+    if m >= 2:
+        assert np.array_equal(yv[m - 1][fin], -2.0 * ref[fin])
+        for r in range(1, m - 1):  # all-zero activation rows give +-0 (NaN codes give NaN)
+            assert np.all(yv[r][fin] == 0.0)
 
 
 @pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK])
