@@ -8,11 +8,11 @@ when the timed region starts, and every step reads a different copy of the
 weight codes and scales (rotating through >= 1 GiB) so the 256 MB Infinity
 Cache cannot serve repeats: the kernels stream from HBM.
 
-Each step's three calls are captured once per weight copy into a HIP graph
-(torch.cuda.CUDAGraph around the ctypes calls, which launch on torch's current
-stream) and the timed region replays one graph per step, so host launch cost
-does not hide the kernels; the same loop launched eagerly is reported in
-"eager".
+The timed region launches the calls eagerly through the C ABI (ctypes) on
+torch's current stream; host enqueue is faster than the kernels, so the GPU
+stays busy. The same steps replayed from HIP graphs (one graph per weight
+copy) are reported in "graph": on this ROCm, replay adds a few microseconds
+per step, so graphs are not used for the headline number.
 
 value = algorithmic bytes of the timed steps / the timed region's duration
 (HIP events on the launch stream, around exactly --steps steps, with
@@ -81,14 +81,11 @@ class Layer:
 
     def __init__(self, lw, copies, dev):
         w = torch.from_numpy(lw.w).to(dev)
+        fw.quantize(w)  # first call also loads the code object
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        q, s = fw.quantize(w)
-        e1.record()
-        torch.cuda.synchronize()
-        self.quantize_ms = e0.elapsed_time(e1)
+        t0 = time.perf_counter()
+        q, s = fw.quantize(w)  # kernel + scale read-back + stream sync
+        self.quantize_ms = (time.perf_counter() - t0) * 1e3
         self.n, self.k = lw.w.shape
         self.name = lw.name
         del w
@@ -185,26 +182,32 @@ def timed_steps(calls, steps, warmup, copies, use_graph, dev):
 
 
 def read_ceiling(dev, sizes, reps=100):
-    """A plain streaming read of the same byte counts (torch int32 sum), rotating
-    through 1 GiB: the reference the GEMV's achieved bandwidth is read against."""
-    big = torch.ones(ROTATE_BYTES // 4, dtype=torch.int32, device=dev)
+    """The library's plain streaming-read kernel over the same byte counts,
+    rotating through 1 GiB: the reference the GEMV's bandwidth is read against."""
+    big = torch.empty(ROTATE_BYTES, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
     out = []
     for nbytes in sizes:
-        cnt = nbytes // 4
-        copies = max(1, big.numel() // cnt)
-        views = [big[i * cnt:(i + 1) * cnt] for i in range(copies)]
+        copies = max(1, big.numel() // nbytes)
+
+        def go(i):
+            st = fw.fp8w_stream_read_probe(big.data_ptr() + (i % copies) * nbytes, nbytes, sink.data_ptr(), stream)
+            if st != 0:
+                raise fw.Fp8wError(st, "fp8w_stream_read_probe")
         for i in range(10):
-            views[i % copies].sum()
+            go(i)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
-            views[i % copies].sum()
+            go(i)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        out.append({"bytes": nbytes, "us": round(us, 3), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        out.append({"bytes": nbytes, "us": round(us, 3), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "pct_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2)})
     del big
     torch.cuda.empty_cache()
     return out
@@ -284,9 +287,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--quick", action="store_true", help="decode workload only (no extra sections)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time the eager launch loop instead of graphs")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--only-timed", action="store_true",
+                    help="run only the timed region (for profiler runs: every GEMV launch is then a timed one)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/gemv_decode_traffic.json from two rocprofv3 --pmc runs, then exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_FILE)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (each GPU would hold its own "
@@ -321,6 +330,15 @@ def main():
         parity = None
     log(f"parity vs oracle: {parity}")
 
+    if args.only_timed:
+        ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
+        launches = args.steps * len(calls)
+        calibration_copy(dev)
+        print(json.dumps({"steps": args.steps, "ms": ms, "us_per_step": ms * 1e3 / args.steps,
+                          "mean_launch_us": ms * 1e3 / launches,
+                          "gbps": per_step * args.steps / (ms * 1e-3) / 1e9}), flush=True)
+        return
+
     per_call = []
     for c in calls:
         us = burst_us(c, 200, 20, stream)
@@ -330,24 +348,20 @@ def main():
     warm = [call_report(c, burst_us(c, 200, 20, stream, warm=True)) for c in calls]
     ceiling = read_ceiling(dev, [c.layer.n * c.layer.k for c in calls])
 
-    use_graph = not args.no_graph
+    ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
+    graph_steps = max(200, args.steps // 10)
     try:
-        ms = timed_steps(calls, args.steps, args.warmup, copies, use_graph, dev)
+        graph_ms = timed_steps(calls, graph_steps, 20, copies, True, dev)
     except Exception as e:  # noqa: BLE001
-        if not use_graph:
-            raise
-        log(f"graph capture failed ({e}); timing the eager loop")
-        use_graph = False
-        ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
-    eager_ms = timed_steps(calls, max(200, args.steps // 10), 20, copies, False, dev) if use_graph else ms
-    eager_steps = max(200, args.steps // 10) if use_graph else args.steps
+        log(f"graph capture failed: {e}")
+        graph_ms = None
     value = per_step * args.steps / (ms * 1e-3) / 1e9
     ms_per_step = ms / args.steps
     launches = args.steps * len(calls)
     mean_launch_us = ms * 1e3 / launches
     achieved = (per_step / len(calls)) / (mean_launch_us * 1e-6) / 1e9
-    log(f"timed region ({'graph' if use_graph else 'eager'}): {ms_per_step * 1e3:.2f} us/step, {value:.0f} GB/s; "
-        f"eager {eager_ms * 1e3 / eager_steps:.2f} us/step")
+    log(f"timed region (eager): {ms_per_step * 1e3:.2f} us/step, {value:.0f} GB/s"
+        + (f"; graph replay {graph_ms * 1e3 / graph_steps:.2f} us/step" if graph_ms else ""))
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -358,7 +372,7 @@ def main():
                                "zero bf16 bias; weight copies rotated through >= 1 GiB",
                    "m": 1, "shapes_nk": workloads.DECODE_SHAPES, "act_dtype": "bf16", "weight_dtype": "e4m3fn",
                    "accumulate": "f32", "rotated_copies": copies, "bytes_per_step": per_step,
-                   "launch": "hipGraph replay, one graph per weight copy" if use_graph else "eager"},
+                   "launch": "eager, C ABI on torch's current stream"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_entry(),
                      "kernel": "gemv_kernel (M=1 GEMV, every launch of the step)",
@@ -366,8 +380,9 @@ def main():
         "parity": parity,
         "per_call": per_call,
         "warm_per_call": warm,
-        "eager": {"us_per_step": round(eager_ms * 1e3 / eager_steps, 3),
-                  "gbps": round(per_step * eager_steps / (eager_ms * 1e-3) / 1e9, 1)},
+        "graph": None if graph_ms is None else {
+            "steps": graph_steps, "us_per_step": round(graph_ms * 1e3 / graph_steps, 3),
+            "gbps": round(per_step * graph_steps / (graph_ms * 1e-3) / 1e9, 1)},
         "quantize": quant,
         "read_ceiling": ceiling,
     }
@@ -379,12 +394,54 @@ def main():
     if not args.no_cpu_baseline:
         log(f"cpu baseline: {out['cpu_baseline']['value']} GB/s on {out['cpu_baseline']['cores']} threads")
 
-    # a plain 256 MiB device copy: the calibration point for --pmc FETCH_SIZE / WRITE_SIZE runs
-    a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    calibration_copy(dev)
+    print(json.dumps(out), flush=True)
+
+
+COPY_BYTES = 256 << 20
+
+
+def calibration_copy(dev):
+    """A plain 256 MiB device-to-device copy (torch): the known-size point that
+    scales the profiler's FETCH_SIZE / WRITE_SIZE readings to bytes."""
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps(out), flush=True)
+
+
+def _pmc_rows(path, counter):
+    import csv
+    with open(path) as f:
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+
+def pmc_summary(fetch_csv, write_csv, out_path):
+    """Turn two rocprofv3 --pmc runs of `bench.py --only-timed` (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) into HBM bytes per GEMV launch, each counter
+    scaled by what it reads for the 256 MiB calibration copy."""
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path, name)
+        gemv = [float(r["Counter_Value"]) for r in rows if "gemv_kernel" in r["Kernel_Name"]]
+        # the calibration copy is the run's last and largest device copy (a blit
+        # kernel or an elementwise copy, depending on how torch lowers it)
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"] or "direct_copy" in r["Kernel_Name"]]
+        copy = float(max(copies, key=lambda r: int(r["Dispatch_Id"]))["Counter_Value"]) if copies else None
+        factor = (COPY_BYTES / 1024.0) / copy if copy else None
+        res[name] = {"gemv_kib_mean": sum(gemv) / len(gemv), "gemv_dispatches": len(gemv),
+                     "copy_kib": copy, "scale": factor}
+    fetch = res["FETCH_SIZE"]["gemv_kib_mean"] * 1024 * res["FETCH_SIZE"]["scale"]
+    write = res["WRITE_SIZE"]["gemv_kib_mean"] * 1024 * res["WRITE_SIZE"]["scale"]
+    per_step = sum(alg_bytes(1, n, k) for n, k in workloads.DECODE_SHAPES)
+    out = {"kernel": "gemv_kernel (decode GEMV launches of bench.py --only-timed)",
+           "kernel_source_hash": kernel_source_hash(), "counters": res,
+           "bytes_per_launch": round(fetch + write, 1), "fetch_bytes_per_launch": round(fetch, 1),
+           "write_bytes_per_launch": round(write, 1),
+           "alg_bytes_per_launch": per_step / len(workloads.DECODE_SHAPES)}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def extra_sections(dev, stream, reps=100):
@@ -408,16 +465,11 @@ def extra_sections(dev, stream, reps=100):
     Ls = [Layer(workloads.block_layer(i), copies, dev) for i in range(len(workloads.DECODER_BLOCK))]
     calls = [Call(Li, workloads.block_x(i).to(dev), dev) for i, Li in enumerate(Ls)]
     blk = [call_report(c, burst_us(c, reps, 10, stream)) for c in calls]
-    try:
-        ms = timed_steps(calls, 200, 10, copies, True, dev)
-        mode = "graph"
-    except Exception:  # noqa: BLE001
-        ms = timed_steps(calls, 200, 10, copies, False, dev)
-        mode = "eager"
+    ms = timed_steps(calls, 200, 10, copies, False, dev)
     ex["decoder_block"] = {"calls": blk, "us_sum_of_calls": round(sum(b["us_per_call"] for b in blk), 2),
-                           "step_us": round(ms * 1e3 / 200, 2), "step_mode": mode,
+                           "step_us": round(ms * 1e3 / 200, 2), "step_mode": "eager",
                            "step_gbps": round(blk_bytes / (ms * 1e-3 / 200) / 1e9, 1), "bytes": blk_bytes}
-    log(f"  decoder block m=16: {ex['decoder_block']['step_us']:.1f} us/step ({mode}), "
+    log(f"  decoder block m=16: {ex['decoder_block']['step_us']:.1f} us/step (eager), "
         f"{ex['decoder_block']['step_gbps']:.0f} GB/s")
     del Ls, calls
     torch.cuda.empty_cache()

@@ -262,6 +262,17 @@ const char* fp8w_status_string(fp8w_status_t status)
     return "unknown status";
 }
 
+fp8w_status_t fp8w_stream_read_probe(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream)
+{
+    if (bytes == 0)
+        return FP8W_SUCCESS;
+    if (!p || !sink || bytes % 16 != 0 || bytes / 16 > (size_t)1 << 40)
+        return FP8W_ERR_INVALID_VALUE;
+    if (!aligned(p, 16) || !aligned(sink, 4))
+        return FP8W_ERR_MISALIGNED;
+    return hip_status(fp8w::launch_read_probe(p, bytes, sink, stream));
+}
+
 int fp8w_last_hip_error(void)
 {
     return g_last_hip_error;

@@ -90,6 +90,9 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
             xv[u][0] = load16(xp + off);
             xv[u][1] = load16(xp + off + 8);
         }
+        // keep every load of this group ahead of the first use: without this the
+        // scheduler trades loads in flight for registers
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u)
             accum_chunk<A, R>(code[u], xv[u][0], xv[u][1], acc);

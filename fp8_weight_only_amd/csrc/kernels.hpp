@@ -36,4 +36,8 @@ hipError_t launch_fallback_gemm(const void* x, Act act, int64_t m, int64_t k, co
                                 const float* scale, const void* bias, int64_t n, void* y,
                                 hipStream_t stream);
 
+// Plain streaming read of `bytes` bytes (16-byte aligned, multiple of 16): the
+// bandwidth reference the linear kernels are read against.
+hipError_t launch_read_probe(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace fp8w

@@ -152,6 +152,16 @@ FP8W_API int fp8w_linear_path(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_
 FP8W_API size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x,
                                    const uint8_t* q, const void* y);
 
+/*
+ * Measurement aid, not part of the method: read `bytes` bytes at `p` once
+ * with the 128-bit streaming loads the linear kernels use, folding them into a
+ * word that is written to `sink` (one uint32, device) only for one specific
+ * value. Its duration is the streaming-read reference for a weight of that
+ * size on this GPU. bytes must be a multiple of 16, p 16-byte aligned.
+ * Asynchronous.
+ */
+FP8W_API fp8w_status_t fp8w_stream_read_probe(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 FP8W_API const char* fp8w_status_string(fp8w_status_t status);
 

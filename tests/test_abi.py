@@ -30,7 +30,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fw.load()
     names = declared_symbols()
-    assert len(names) == 9
+    assert len(names) == 10
     for name in names:
         assert hasattr(lib, name), name
         assert name in fw.EXPORTS, name
@@ -143,6 +143,15 @@ def test_quantize_rejects_invalid_arguments():
     assert qz(X, fw.FP32, 10, 10, X + 16, S, 0) == fw.ERR_INVALID_VALUE  # q overlaps w
     assert qz(X, fw.FP32, 10, 10, Q, X, 0) == fw.ERR_INVALID_VALUE       # scale overlaps w
     assert qz(X, fw.FP32, 1 << 31, 10, Q, S, 0) == fw.ERR_INVALID_VALUE
+
+
+def test_read_probe_rejects_invalid_arguments():
+    rp = fw.fp8w_stream_read_probe
+    assert rp(X, 0, S, 0) == fw.SUCCESS
+    assert rp(0, 4096, S, 0) == fw.ERR_INVALID_VALUE
+    assert rp(X, 4096, 0, 0) == fw.ERR_INVALID_VALUE
+    assert rp(X, 4095, S, 0) == fw.ERR_INVALID_VALUE
+    assert rp(X + 8, 4096, S, 0) == fw.ERR_MISALIGNED
 
 
 def test_dequantize_rejects_invalid_arguments():

@@ -242,3 +242,13 @@ def test_dequantize_matches_oracle(out_dtype, shape):
     assert_same_bits(got_np.view(ref_bits.dtype), ref_bits, f"dequantize {out_dtype}")
     unscaled = fw.dequantize(q, None, out_dtype).double().cpu().numpy()
     assert np.array_equal(unscaled, oracle.dequantize_f64(q_np))
+
+
+def test_stream_read_probe_runs_and_writes_nothing_for_zeros():
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    st = fw.fp8w_stream_read_probe(buf.data_ptr(), buf.numel(), sink.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+    assert st == fw.SUCCESS
+    torch.cuda.synchronize()
+    assert sink.item() == 7
