@@ -29,7 +29,8 @@ import torch
 
 __all__ = [
     "Fp8wError", "lib_path", "load", "fp8w_quantize", "fp8w_linear", "fp8w_linear_with_path",
-    "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes", "fp8w_stream_read_probe",
+    "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes", "fp8w_linear_kernel",
+    "fp8w_stream_read_probe",
     "fp8w_status_string", "fp8w_abi_version", "quantize", "linear", "dequantize",
     "linear_path", "workspace_bytes", "QuantizedLinear",
     "BF16", "FP16", "FP32", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_FALLBACK", "EXPORTS",
@@ -55,6 +56,7 @@ EXPORTS = {
     "fp8w_dequantize_fallback": (_I, [_P, _P, _I64, _I64, _P, _I, _P]),
     "fp8w_linear_path": (_I, [_I64, _I64, _I64, _I, _P, _P, _P]),
     "fp8w_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _P, _P, _P]),
+    "fp8w_linear_kernel": (ctypes.c_char_p, [_I, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_stream_read_probe": (_I, [_P, _SZ, _P, _P]),
     "fp8w_status_string": (ctypes.c_char_p, [_I]),
     "fp8w_last_hip_error": (_I, []),
@@ -117,6 +119,12 @@ def fp8w_linear_path(m, n, k, act_dtype, x, q, y) -> int:
 
 def fp8w_linear_workspace_bytes(m, n, k, act_dtype, x, q, y) -> int:
     return load().fp8w_linear_workspace_bytes(m, n, k, act_dtype, x, q, y)
+
+
+def fp8w_linear_kernel(path, m, n, k, act_dtype, x, q):
+    """Name of the kernel `path` launches for these sizes (None if invalid)."""
+    r = load().fp8w_linear_kernel(path, m, n, k, act_dtype, x, q)
+    return r.decode() if r is not None else None
 
 
 def fp8w_stream_read_probe(p, nbytes, sink, stream) -> int:

@@ -243,6 +243,23 @@ size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t
     return fallback_workspace(n, k, act_dtype);
 }
 
+const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x,
+                               const uint8_t* q)
+{
+    if (!valid_act(act_dtype) || !sizes_ok(m, n, k))
+        return nullptr;
+    if (path == FP8W_PATH_AUTO)
+        path = auto_path(m, k, x, q);
+    if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
+        if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || k % 256 != 0 || k == 0)
+            return nullptr;
+        return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(k) : fp8w::skinny_kernel_name(m, n, k);
+    }
+    if (path == FP8W_PATH_FALLBACK)
+        return "dequantize_kernel+fallback_gemm_kernel";
+    return nullptr;
+}
+
 const char* fp8w_status_string(fp8w_status_t status)
 {
     switch (status) {

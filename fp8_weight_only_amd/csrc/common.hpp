@@ -152,4 +152,25 @@ __device__ __forceinline__ uint16_t epilogue(float acc, float scale, const uint1
     return Act::from_f32(__builtin_fmaf(scale, acc, b));
 }
 
+// The same with scale and bias already in registers: the streaming kernels
+// fetch them when they start, so that the end of every workgroup does not
+// wait for one more memory round trip.
+template <typename Act>
+__device__ __forceinline__ uint16_t epilogue(float acc, float scale, uint16_t bias_bits)
+{
+    return Act::from_f32(__builtin_fmaf(scale, acc, Act::to_f32(bias_bits)));
+}
+
+// Raw bias bits of channel ch (+0.0 without a bias), widened only where the
+// epilogue uses them so that the load is not waited for early. The load is
+// unconditional (a pointer select, no branch): without a bias it reads a zero
+// held in device memory.
+static __device__ uint16_t kNoBias = 0;  // never written; global address space
+
+__device__ __forceinline__ uint16_t bias_bits(const uint16_t* bias, int64_t ch)
+{
+    const uint16_t* p = bias ? bias + ch : &kNoBias;
+    return *p;
+}
+
 }  // namespace fp8w

@@ -72,6 +72,12 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
         qr[r] = q + (row0 + r < n ? row0 + r : n - 1) * k + (int64_t)t * 16;
     const uint16_t* xp = x + (int64_t)t * 16;
 
+    // epilogue operands of this workgroup's rows, fetched up front (threads
+    // t < R use them; the others read a valid row and discard it)
+    const int64_t er = row0 + (t % R) < n ? row0 + (t % R) : n - 1;
+    const float sc = scale[er];
+    const uint16_t bi = bias_bits(bias, er);
+
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
 #pragma unroll
         for (int w = 1; w < NW; ++w)
             s += red[w][t];
-        y[row0 + t] = epilogue<A>(s, scale[row0 + t], bias, row0 + t);
+        y[row0 + t] = epilogue<A>(s, sc, bi);
     }
 }
 
@@ -147,6 +153,11 @@ hipError_t launch_typed(const void* x, int64_t k, const uint8_t* q, const float*
 }
 
 }  // namespace
+
+const char* gemv_kernel_name(int64_t k)
+{
+    return k <= 4096 ? "gemv_kernel<R=2,U=1,NT=256>" : "gemv_kernel<R=4,U=2,NT=128>";
+}
 
 hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,
                        const void* bias, int64_t n, void* y, hipStream_t stream)

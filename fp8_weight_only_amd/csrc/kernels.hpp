@@ -21,9 +21,16 @@ hipError_t launch_quantize(const void* w, Act w_type, int64_t n, int64_t k, uint
 hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,
                        const void* bias, int64_t n, void* y, hipStream_t stream);
 
+// Name of the GEMV instance launch_gemv picks for this k.
+const char* gemv_kernel_name(int64_t k);
+
 // M = 1..32 MFMA skinny GEMM; k % 256 == 0, x and q 16-byte aligned.
 hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
                          const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream);
+
+// Name of the kernel and tile launch_skinny picks for this shape (a
+// thread-local string; for tests and measurement reports).
+const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k);
 
 // Dequantize codes to out_type: value(q) * scale[r] (scale != nullptr) or the
 // exact unscaled value (scale == nullptr).

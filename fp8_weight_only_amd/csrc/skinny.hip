@@ -16,20 +16,28 @@
 // quarter-wave would touch 16 different rows, and the vector memory unit's
 // per-cache-line work, not HBM, would set the speed. Two layouts avoid that:
 //
-// * seg_kernel (M <= 8, and 17..32 on wide layers): one MFMA covers MP = 16/SEG
+// * seg_kernel (M <= 8 on layers under 8192 channels, and shapes the pipe
+//   ring cannot tile): one MFMA covers MP = 16/SEG
 //   channels x MP tokens x SEG k-segments. A row i = MP*s + c and B column
 //   j = MP*s + t; only the D blocks with matching segment (s == s') are kept and
 //   summed over s at the end. Lane (i, g) reads the 16 codes of channel c at
 //   kb + 16*SEG*g + 16*s, so a quarter-wave reads 16*SEG contiguous bytes per
 //   channel (64 B for M <= 4). T channel groups per wave share the activation
 //   fragments; W waves split k.
-// * lds_kernel (M = 9..32): codes and activations are read with fully
-//   coalesced loads (a quarter-wave reads 256 contiguous bytes of one row),
-//   written to a per-wave LDS tile and read back in the MFMA layout.
+// * pipe_kernel (M = 2..32 on layers of 4096 channels and more): codes and
+//   activations travel from HBM/L2 straight into LDS with gfx950's direct
+//   global-to-LDS loads (no register staging), through a ring of NS stage
+//   buffers, so NS - 1 stages of every workgroup are in flight while the
+//   matrix cores work on the oldest one. Each load instruction moves 1 KB: a
+//   quarter-wave fetches 256 contiguous bytes of one code row (or half a row of
+//   activations), and the lane-to-address mapping rotates every row's 16-byte
+//   chunks so that the MFMA-layout reads from LDS hit 16 distinct banks.
 //
 // One workgroup owns a block of output channels over the whole of k (no
 // cross-workgroup reduction: on MI355X the eight XCDs have separate L2s and a
 // device-scope handoff between workgroups costs more than it saves).
+#include <stdio.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -167,115 +175,262 @@ __global__ __launch_bounds__(W* kWave) void seg_kernel(
     }
 }
 
-// ---------------------------------------------------------------- lds_kernel
-constexpr int kCodeRow = 256 + 16;  // LDS code tile row stride (bytes): 256 codes + pad
-constexpr int kActRow = 512 + 16;   // LDS activation tile row stride (bytes): 256 values + pad
+// ---------------------------------------------------------------- pipe_kernel
+#define FP8W_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <typename A, int MT, int W>
-__global__ __launch_bounds__(W* kWave) void lds_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k)
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's vector-memory loads
+// (the direct-to-LDS ones included) still outstanding, all LDS reads returned.
+template <int N>
+__device__ __forceinline__ void wait_loads_at_most()
 {
-    __shared__ __attribute__((aligned(16))) uint8_t ctile_all[W][16 * kCodeRow];
-    __shared__ __attribute__((aligned(16))) uint8_t xtile_all[W][MT * 16 * kActRow];
-    __shared__ f32x4 part[W][MT][kWave];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
-    const int i = lane & 15, g = lane >> 4;
-    uint8_t* ctile = ctile_all[wave];
-    uint8_t* xtile = xtile_all[wave];
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
-    // coalesced roles: code row 4j + (lane >> 4) at byte (lane & 15) * 16;
-    // activation row 2j + (lane >> 5) at element (lane & 31) * 8
-    const int cr0 = lane >> 4, co = (lane & 15) * 16;
-    const uint8_t* qrow[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t r = n0 + 4 * j + cr0;
-        qrow[j] = q + (r < n ? r : n - 1) * k + co;
-    }
-    const int xt0 = lane >> 5, xo = (lane & 31) * 8;
-    constexpr int XJ = MT * 8;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < XJ; ++j)  // rows of tokens >= m stay zero
-        *reinterpret_cast<u32x4*>(xtile + (2 * j + xt0) * kActRow + xo * 2) = zero;
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would drain every outstanding load, including the stages still being
+// prefetched. LDS visibility comes from the explicit wait before it; the empty
+// asm keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier()
+{
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
-    const int64_t steps = k >> 8;  // 256-k super-steps
-    const int64_t per = (steps + W - 1) / W;
-    const int64_t s0 = (int64_t)wave * per;
-    const int64_t s1 = (s0 + per < steps) ? s0 + per : steps;
+// XR activation rows are fetched (m <= XR; MFMA columns past XR read row XR - 1
+// and are discarded); CT channel tiles of 16 and KP k-parts make the
+// workgroup's CT * KP waves; NS stage buffers; one stage is 256 k per wave.
+template <int XR, int CT, int KP, int NS>
+struct PipeCfg {
+    static_assert(XR % 2 == 0 && XR >= 2 && XR <= 32, "activation rows");
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    static constexpr int MT = XR > 16 ? 2 : 1;      // 16-token MFMA tiles
+    static constexpr int W = CT * KP;               // waves
+    static constexpr int CODE = 16 * 256;           // code bytes per wave and stage
+    static constexpr int XPART = XR * 512;          // activation bytes per k-part and stage
+    static constexpr int STAGE = W * CODE + KP * XPART;
+    static constexpr int XLOADS = (XR / 2) * KP;    // 1 KB activation loads per stage
+    static constexpr int XPW = (XLOADS + W - 1) / W;  // per wave; duplicates fill the last round
+    static constexpr int LOADS = 4 + XPW;           // load instructions per wave and stage
+    static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
+};
 
-    f32x4 acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-        acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+template <typename A, int XR, int CT, int KP, int NS>
+struct Pipe {
+    using C = PipeCfg<XR, CT, KP, NS>;
+    static constexpr int MT = C::MT;
 
-    for (int64_t st = s0; st < s1; ++st) {
-        const int64_t kb = st * 256;
-        u32x4 cv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            cv[j] = load_stream16(qrow[j] + kb);
-        u32x4 xv[XJ];
-#pragma unroll
-        for (int j = 0; j < XJ; ++j) {
-            const int tok = 2 * j + xt0;
-            xv[j] = tok < m ? load16(x + (int64_t)tok * k + kb + xo) : zero;
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4*>(ctile + (4 * j + cr0) * kCodeRow + co) = cv[j];
-#pragma unroll
-        for (int j = 0; j < XJ; ++j) {
-            const int tok = 2 * j + xt0;
-            if (tok < m)
-                *reinterpret_cast<u32x4*>(xtile + tok * kActRow + xo * 2) = xv[j];
-        }
-        __builtin_amdgcn_wave_barrier();
+    const uint16_t* x;
+    const uint8_t* q;
+    int m;
+    int64_t n, k, n0;
+    int64_t S, rot;  // stages; this workgroup's first stage
+    int lane, wave, ct, kp;
+
+    // Stage s into buf. Workgroups start at different stages (rot) and wrap
+    // around, so that the workgroups resident on one XCD at a time read all
+    // the k offsets of their rows rather than the same one: measured on MI355X,
+    // the unstaggered order ran 10-30 % slower on the large layers, by an amount
+    // that depended on where the weight happened to be allocated. Wave (ct, kp) loads
+    // its 16 code rows of k-part kp: instruction j puts rows 4j..4j+3 at
+    // buf + wave * CODE + 1024 j, lane l landing at 16 l, i.e. row r = 4j + l / 16
+    // at slot l % 16 holds chunk (slot - r) mod 16 of that row. Activation
+    // instruction p puts rows 2p', 2p'+1 of k-part p / (XR / 2) (p' = p mod XR / 2)
+    // in the same rotated way, 32 chunks per row. Rows past n or m are clamped
+    // to real rows; their results are never stored.
+    __device__ __forceinline__ void issue(int64_t s, uint8_t* buf) const
+    {
+        int64_t sr = s + rot;  // s < S and rot < S
+        sr = sr < S ? sr : sr - S;
+        const int64_t kb = sr * (KP * 256);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            // codes kb + 64g + 16j .. +15 of channel i: MFMA pair (j, 0/1)
-            const u32x4 c16 = *reinterpret_cast<const u32x4*>(ctile + i * kCodeRow + 64 * g + 16 * j);
+            const int r = 4 * j + (lane >> 4);
+            const int chunk = ((lane & 15) - r) & 15;
+            int64_t row = n0 + 16 * ct + r;
+            row = row < n ? row : n - 1;
+            const uint8_t* src = q + row * k + kb + kp * 256 + chunk * 16;
+            __builtin_amdgcn_global_load_lds((const void*)src, FP8W_LDS(buf + wave * C::CODE + j * 1024), 16, 0,
+                                             2 /* non-temporal */);
+        }
+#pragma unroll
+        for (int u = 0; u < C::XPW; ++u) {
+            const int p = (wave * C::XPW + u) % C::XLOADS;
+            const int kpx = p / (XR / 2);
+            const int pair = p % (XR / 2);
+            const int t = 2 * pair + (lane >> 5);
+            const int chunk = ((lane & 31) - t) & 31;
+            const int tc = t < m ? t : m - 1;
+            const uint16_t* src = x + (int64_t)tc * k + kb + kpx * 256 + chunk * 8;
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             FP8W_LDS(buf + C::W * C::CODE + kpx * C::XPART + pair * 1024), 16, 0, 0);
+        }
+    }
+
+    // MFMA pair j of this wave's 256 k: lane (i, g) takes codes 64g + 16j .. +15 of
+    // channel i (16 contiguous k, two MFMAs) and the matching activations of
+    // token i (+ 16 mt).
+    __device__ __forceinline__ void compute(const uint8_t* buf, f32x4* acc) const
+    {
+        const int i = lane & 15, g = lane >> 4;
+        const uint8_t* cb = buf + wave * C::CODE;
+        const uint8_t* xb = buf + C::W * C::CODE + kp * C::XPART;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 c16 = *reinterpret_cast<const u32x4*>(cb + 16 * (16 * i + ((4 * g + j + i) & 15)));
             const u32x2 d0 = A::decode4(c16.x), d1 = A::decode4(c16.y);
             const u32x2 d2 = A::decode4(c16.z), d3 = A::decode4(c16.w);
             const u32x4 a0 = {d0.x, d0.y, d1.x, d1.y};
             const u32x4 a1 = {d2.x, d2.y, d3.x, d3.y};
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const uint8_t* xpp = xtile + (i + 16 * t) * kActRow + (64 * g + 16 * j) * 2;
-                const u32x4 b0 = *reinterpret_cast<const u32x4*>(xpp);
-                const u32x4 b1 = *reinterpret_cast<const u32x4*>(xpp + 16);
-                acc[t] = A::mfma(a0, b0, acc[t]);
-                acc[t] = A::mfma(a1, b1, acc[t]);
+            for (int mt = 0; mt < MT; ++mt) {
+                const int t = (i + 16 * mt) < XR ? (i + 16 * mt) : XR - 1;
+                const uint8_t* xr = xb + 16 * (32 * t);
+                const u32x4 b0 = *reinterpret_cast<const u32x4*>(xr + 16 * ((8 * g + 2 * j + t) & 31));
+                const u32x4 b1 = *reinterpret_cast<const u32x4*>(xr + 16 * ((8 * g + 2 * j + 1 + t) & 31));
+                acc[mt] = A::mfma(a0, b0, acc[mt]);
+                acc[mt] = A::mfma(a1, b1, acc[mt]);
             }
         }
-        __builtin_amdgcn_wave_barrier();
     }
 
+    // One pipeline step: stage s is complete for every wave, then stage
+    // s + NS - 1 is issued into the buffer stage s - 1 used, then s is consumed.
+    __device__ __forceinline__ void step(int64_t s, const uint8_t* cur, uint8_t* nxt, f32x4* acc) const
+    {
+        wait_loads_at_most<C::LOADS*(NS - 2)>();
+        stage_barrier();
+        issue(s + NS - 1, nxt);
+        compute(cur, acc);
+    }
+};
+
+// Requires k % (KP * 256 * NS) == 0. The stage buffers are distinct arrays and
+// the ring is unrolled NS-fold, with every load and wait unconditional, so the
+// compiler can tell the buffers apart and adds no drain of its own inside the
+// loop; the last group of NS stages issues only its first load and then drains.
+template <typename A, int XR, int CT, int KP, int NS>
+__global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k)
+{
+    using P = Pipe<A, XR, CT, KP, NS>;
+    using C = typename P::C;
+    constexpr int MT = C::MT;
+    __shared__ __attribute__((aligned(1024))) uint8_t b0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t b1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t b2[NS > 2 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t b3[NS > 3 ? C::STAGE : 16];
+
+    P p;
+    p.x = x;
+    p.q = q;
+    p.m = m;
+    p.n = n;
+    p.k = k;
+    p.lane = threadIdx.x & (kWave - 1);
+    p.wave = threadIdx.x / kWave;
+    p.ct = p.wave % CT;
+    p.kp = p.wave / CT;
+    p.n0 = (int64_t)blockIdx.x * (16 * CT);
+
+    f32x4 acc[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-        part[wave][t][lane] = acc[t];
+    for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // epilogue operands of this lane's four channels, fetched before the ring
+    // starts (extra loads ahead of the ring only make its waits stricter)
+    float sc[4];
+    uint16_t bi[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        int64_t ch = p.n0 + 16 * p.ct + 4 * (p.lane >> 4) + r;
+        ch = ch < n ? ch : n - 1;
+        sc[r] = scale[ch];
+        bi[r] = bias_bits(bias, ch);
+    }
+
+    const int64_t S = k / (KP * 256);
+    p.S = S;
+    // workgroups are dealt to the eight XCDs in turn: consecutive workgroups of
+    // one XCD get consecutive start stages
+    p.rot = (int64_t)(blockIdx.x / 8) % S;
+    p.issue(0, b0);
+    if constexpr (NS > 2)
+        p.issue(1, b1);
+    if constexpr (NS > 3)
+        p.issue(2, b2);
+    int64_t s = 0;
+    for (; s < S - NS; s += NS) {
+        if constexpr (NS == 2) {
+            p.step(s, b0, b1, acc);
+            p.step(s + 1, b1, b0, acc);
+        } else if constexpr (NS == 3) {
+            p.step(s, b0, b2, acc);
+            p.step(s + 1, b1, b0, acc);
+            p.step(s + 2, b2, b1, acc);
+        } else {
+            p.step(s, b0, b3, acc);
+            p.step(s + 1, b1, b0, acc);
+            p.step(s + 2, b2, b1, acc);
+            p.step(s + 3, b3, b2, acc);
+        }
+    }
+    // last group: stage S - 1 is issued by its first step, then the ring drains
+    if constexpr (NS == 2) {
+        p.step(s, b0, b1, acc);
+        wait_loads_at_most<0>();
+        stage_barrier();
+        p.compute(b1, acc);
+    } else if constexpr (NS == 3) {
+        p.step(s, b0, b2, acc);
+        wait_loads_at_most<C::LOADS>();
+        stage_barrier();
+        p.compute(b1, acc);
+        wait_loads_at_most<0>();
+        stage_barrier();
+        p.compute(b2, acc);
+    } else {
+        p.step(s, b0, b3, acc);
+        wait_loads_at_most<2 * C::LOADS>();
+        stage_barrier();
+        p.compute(b1, acc);
+        wait_loads_at_most<C::LOADS>();
+        stage_barrier();
+        p.compute(b2, acc);
+        wait_loads_at_most<0>();
+        stage_barrier();
+        p.compute(b3, acc);
+    }
+
+    // k-part partial sums meet in stage buffer 0, then wave (ct, 0) adds them in
+    // k order and applies the epilogue; D[4g + r][i] is channel 4g + r, token i.
+    static_assert(C::STAGE >= C::W * MT * kWave * 16, "reduction fits in a stage buffer");
+    f32x4(*part)[MT][kWave] = reinterpret_cast<f32x4(*)[MT][kWave]>(b0);
     __syncthreads();
-    if (wave != 0)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        part[p.wave][mt][p.lane] = acc[mt];
+    __syncthreads();
+    if (p.kp != 0)
         return;
+    const int i = p.lane & 15, g = p.lane >> 4;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        f32x4 sum = part[0][t][lane];
+    for (int mt = 0; mt < MT; ++mt) {
+        f32x4 sum = part[p.ct][mt][p.lane];
 #pragma unroll
-        for (int w = 1; w < W; ++w)
-            sum += part[w][t][lane];
-        const int tok = i + 16 * t;
+        for (int kp = 1; kp < KP; ++kp)
+            sum += part[kp * CT + p.ct][mt][p.lane];
+        const int tok = i + 16 * mt;
         if (tok >= m)
             continue;
         const float v[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t ch = n0 + 4 * g + r;
+            const int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
             if (ch < n)
-                y[(int64_t)tok * n + ch] = epilogue<A>(v[r], scale[ch], bias, ch);
+                y[(int64_t)tok * n + ch] = epilogue<A>(v[r], sc[r], bi[r]);
         }
     }
 }
@@ -293,36 +448,106 @@ hipError_t launch_seg(const void* x, int m, int64_t k, const uint8_t* q, const f
     return hipGetLastError();
 }
 
-template <typename A, int MT, int W>
-hipError_t launch_lds(const void* x, int m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
-                      int64_t n, void* y, hipStream_t stream)
+template <typename A, int XR, int CT, int KP, int NS>
+hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
+                       int64_t n, void* y, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((n + 15) / 16)), block(W * kWave);
-    hipLaunchKernelGGL((lds_kernel<A, MT, W>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q, scale,
-                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
+    const dim3 grid((unsigned)((n + 16 * CT - 1) / (16 * CT))), block(CT * KP * kWave);
+    hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
+                       q, scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
     return hipGetLastError();
 }
 
-// Tile choice per batch size, from sweeps on MI355X (k % 256 == 0 here). A
-// workgroup always covers the whole of k, so layers with few channels
-// (n < 8192) keep 16 channels per workgroup to give every CU work.
+// Kernel choice per shape, from sweeps on MI355X (k % 256 == 0 here).
+// pipe_kernel: a workgroup owns 16 * CT channels over the whole of k, so CT is
+// the largest that still gives about one workgroup per CU (224-448 workgroups
+// on the decode and sweep layers), and NS the deepest ring whose LDS lets every
+// workgroup be resident at once. seg_kernel covers small batches on narrow
+// layers, where it measured faster, and the shapes the ring cannot tile.
+struct SkinnyPlan {
+    bool pipe;
+    int xr, ct, kp, ns;         // pipe_kernel
+    int seg, t, w, u, mt;       // seg_kernel
+};
+
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k)
+{
+    SkinnyPlan p{};
+    int ct = 0, kp = 1, ns = 4;
+    if (m >= 2) {
+        if (n >= 16384) {
+            ct = 4;
+            ns = 2;
+        } else if (n >= 12288) {
+            ct = 4;
+        } else if (n >= 8192) {
+            ct = 2;
+        } else if (m > 8) {
+            ct = 1;
+            kp = 2;
+        }
+    }
+    if (ct != 0) {
+        if (k % (kp * 256 * ns) != 0)
+            ns = 2;
+        if (k % (kp * 256 * ns) == 0) {
+            p.pipe = true;
+            p.xr = m <= 4 ? 4 : m <= 8 ? 8 : m <= 16 ? 16 : m <= 24 ? 24 : 32;
+            p.ct = ct;
+            p.kp = kp;
+            p.ns = ns;
+            return p;
+        }
+    }
+    if (m <= 4)
+        p.seg = 4, p.t = 4, p.w = 4, p.u = 2, p.mt = 1;
+    else if (m <= 8 && n >= 8192)
+        p.seg = 2, p.t = 4, p.w = 4, p.u = 1, p.mt = 1;
+    else if (m <= 8)
+        p.seg = 2, p.t = 2, p.w = 8, p.u = 2, p.mt = 1;
+    else
+        p.seg = 1, p.t = 2, p.w = 4, p.u = 1, p.mt = 2;
+    return p;
+}
+
+template <typename A, int XR>
+hipError_t launch_pipe_xr(const SkinnyPlan& p, const void* x, int m, int64_t k, const uint8_t* q,
+                          const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    const int key = p.ct * 100 + p.kp * 10 + p.ns;
+    switch (key) {
+    case 412: return launch_pipe<A, XR, 4, 1, 2>(x, m, k, q, scale, bias, n, y, stream);
+    case 414: return launch_pipe<A, XR, 4, 1, 4>(x, m, k, q, scale, bias, n, y, stream);
+    case 212: return launch_pipe<A, XR, 2, 1, 2>(x, m, k, q, scale, bias, n, y, stream);
+    case 214: return launch_pipe<A, XR, 2, 1, 4>(x, m, k, q, scale, bias, n, y, stream);
+    case 122: return launch_pipe<A, XR, 1, 2, 2>(x, m, k, q, scale, bias, n, y, stream);
+    case 124: return launch_pipe<A, XR, 1, 2, 4>(x, m, k, q, scale, bias, n, y, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename A>
 hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale,
                         const void* bias, int64_t n, void* y, hipStream_t stream)
 {
     const int mi = (int)m;
-    if (m <= 4)
-        return launch_seg<A, 4, 4, 4, 2, 1>(x, mi, k, q, scale, bias, n, y, stream);
-    if (m <= 8) {
-        if (n >= 8192)
-            return launch_seg<A, 2, 4, 4, 1, 1>(x, mi, k, q, scale, bias, n, y, stream);
-        return launch_seg<A, 2, 2, 8, 2, 1>(x, mi, k, q, scale, bias, n, y, stream);
+    const SkinnyPlan p = plan_skinny(m, n, k);
+    if (p.pipe) {
+        switch (p.xr) {
+        case 4: return launch_pipe_xr<A, 4>(p, x, mi, k, q, scale, bias, n, y, stream);
+        case 8: return launch_pipe_xr<A, 8>(p, x, mi, k, q, scale, bias, n, y, stream);
+        case 16: return launch_pipe_xr<A, 16>(p, x, mi, k, q, scale, bias, n, y, stream);
+        case 24: return launch_pipe_xr<A, 24>(p, x, mi, k, q, scale, bias, n, y, stream);
+        default: return launch_pipe_xr<A, 32>(p, x, mi, k, q, scale, bias, n, y, stream);
+        }
     }
-    if (m <= 16)
-        return launch_lds<A, 1, 4>(x, mi, k, q, scale, bias, n, y, stream);
-    if (n >= 8192)
-        return launch_seg<A, 1, 2, 4, 1, 2>(x, mi, k, q, scale, bias, n, y, stream);
-    return launch_lds<A, 2, 4>(x, mi, k, q, scale, bias, n, y, stream);
+    if (p.seg == 4)
+        return launch_seg<A, 4, 4, 4, 2, 1>(x, mi, k, q, scale, bias, n, y, stream);
+    if (p.seg == 2 && p.t == 4)
+        return launch_seg<A, 2, 4, 4, 1, 1>(x, mi, k, q, scale, bias, n, y, stream);
+    if (p.seg == 2)
+        return launch_seg<A, 2, 2, 8, 2, 1>(x, mi, k, q, scale, bias, n, y, stream);
+    return launch_seg<A, 1, 2, 4, 1, 2>(x, mi, k, q, scale, bias, n, y, stream);
 }
 
 }  // namespace
@@ -339,6 +564,17 @@ hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uin
     if (act == Act::FP16)
         return launch_typed<F16>(x, m, k, q, scale, bias, n, y, stream);
     return hipErrorInvalidValue;
+}
+
+const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k)
+{
+    thread_local char name[64];
+    const SkinnyPlan p = plan_skinny(m, n, k);
+    if (p.pipe)
+        snprintf(name, sizeof name, "pipe_kernel<XR=%d,CT=%d,KP=%d,NS=%d>", p.xr, p.ct, p.kp, p.ns);
+    else
+        snprintf(name, sizeof name, "seg_kernel<SEG=%d,T=%d,W=%d,U=%d,MT=%d>", p.seg, p.t, p.w, p.u, p.mt);
+    return name;
 }
 
 }  // namespace fp8w

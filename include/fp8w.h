@@ -153,6 +153,16 @@ FP8W_API size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8
                                    const uint8_t* q, const void* y);
 
 /*
+ * Name of the kernel (and its tile parameters) that `path` (FP8W_PATH_AUTO or
+ * a forced path) launches for these sizes and pointers, e.g.
+ * "pipe_kernel<XR=16,CT=4,KP=1,NS=4>". A static or thread-local string, valid
+ * until the next call on this thread; NULL when the arguments or the forced
+ * path are invalid. For tests and measurement reports.
+ */
+FP8W_API const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype,
+                                        const void* x, const uint8_t* q);
+
+/*
  * Measurement aid, not part of the method: read `bytes` bytes at `p` once
  * with the 128-bit streaming loads the linear kernels use, folding them into a
  * word that is written to `sink` (one uint32, device) only for one specific

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fw.load()
     names = declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     for name in names:
         assert hasattr(lib, name), name
         assert name in fw.EXPORTS, name
@@ -69,6 +69,29 @@ def test_path_selection():
     assert p(-1, 4096, 4096, fw.BF16, X, Q, Y) == -1
     assert p(1, -5, 4096, fw.BF16, X, Q, Y) == -1
     assert p(1, 1 << 31, 4096, fw.BF16, X, Q, Y) == -1
+
+
+def test_kernel_names():
+    kn = fw.fp8w_linear_kernel
+    A = fw.PATH_AUTO
+    assert kn(A, 1, 4096, 4096, fw.BF16, X, Q) == "gemv_kernel<R=2,U=1,NT=256>"
+    assert kn(A, 1, 4096, 14336, fw.BF16, X, Q) == "gemv_kernel<R=4,U=2,NT=128>"
+    assert kn(A, 16, 14336, 4096, fw.FP16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4>"
+    assert kn(A, 32, 28672, 8192, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>"
+    assert kn(A, 22, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=2,KP=1,NS=4>"
+    assert kn(A, 16, 4096, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"
+    assert kn(A, 3, 14336, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=4>"
+    assert kn(A, 8, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=2,T=2,W=8,U=2,MT=1>"
+    assert kn(A, 4, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"
+    assert kn(A, 12, 40, 768, fw.BF16, X, Q) == "seg_kernel<SEG=1,T=2,W=4,U=1,MT=2>"      # k % 1024 != 0
+    assert kn(A, 12, 40, 1024, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=2>"
+    assert kn(A, 20, 12300, 512, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=2>"
+    assert kn(fw.PATH_SKINNY, 1, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"
+    assert kn(A, 4, 28672, 8200, fw.BF16, X, Q) == "dequantize_kernel+fallback_gemm_kernel"
+    assert kn(fw.PATH_GEMV, 2, 4096, 4096, fw.BF16, X, Q) is None
+    assert kn(fw.PATH_SKINNY, 33, 4096, 4096, fw.BF16, X, Q) is None
+    assert kn(A, 1, 4096, 4096, fw.FP32, X, Q) is None
+    assert kn(7, 1, 4096, 4096, fw.BF16, X, Q) is None
 
 
 def test_workspace_bytes():

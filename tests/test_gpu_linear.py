@@ -76,6 +76,31 @@ def test_linear_small_parity(m, n, k, dtype, bias, path):
     _check(case, expect_path=path)
 
 
+PIPE = [
+    # (m, n, k, dtype, kernel the dispatcher must pick): every ring shape and
+    # activation-row count of the direct-to-LDS kernel, ragged channel tails
+    (2, 12300, 1024, torch.bfloat16, "pipe_kernel<XR=4,CT=4,KP=1,NS=4>"),
+    (5, 8200, 1024, torch.float16, "pipe_kernel<XR=8,CT=2,KP=1,NS=4>"),
+    (7, 8250, 512, torch.bfloat16, "pipe_kernel<XR=8,CT=2,KP=1,NS=2>"),
+    (9, 200, 2048, torch.bfloat16, "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"),
+    (16, 4100, 1024, torch.float16, "pipe_kernel<XR=16,CT=1,KP=2,NS=2>"),
+    (19, 16400, 512, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>"),
+    (24, 12288, 2048, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>"),
+    (32, 8192, 3072, torch.float16, "pipe_kernel<XR=32,CT=2,KP=1,NS=4>"),
+    (32, 300, 4096, torch.bfloat16, "pipe_kernel<XR=32,CT=1,KP=2,NS=4>"),
+    (3, 16500, 1536, torch.bfloat16, "pipe_kernel<XR=4,CT=4,KP=1,NS=2>"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,dtype,kernel", PIPE)
+def test_pipe_kernel_parity(m, n, k, dtype, kernel):
+    print(f"pipe m={m} n={n} k={k} {dtype} {kernel}", flush=True)
+    assert fw.fp8w_linear_kernel(fw.PATH_AUTO, m, n, k, fw.BF16 if dtype == torch.bfloat16 else fw.FP16,
+                                 0, 0) == kernel
+    case = workloads.random_case(31 * m + n + k, m, n, k, dtype, with_bias=(m % 2 == 1))
+    _check(case, expect_path=fw.PATH_SKINNY)
+
+
 @pytest.mark.parametrize("m,k", [(1, 256), (1, 4096), (2, 1024), (16, 768), (17, 512), (32, 2048)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 def test_every_path_matches_the_oracle(m, k, dtype):
@@ -95,16 +120,20 @@ def test_every_path_matches_the_oracle(m, k, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("path,m", [(fw.PATH_GEMV, 1), (fw.PATH_SKINNY, 2), (fw.PATH_SKINNY, 6),
-                                    (fw.PATH_SKINNY, 12), (fw.PATH_SKINNY, 20), (fw.PATH_FALLBACK, 2)])
-def test_all_256_codes_decode_exactly_on_each_path(dtype, path, m):
-    """q[n, :] = n for every code n, unit scales and a one-hot x: y[n] is the
-    exact value of code n (0x7F / 0xFF give NaN). Pins each kernel's hardware
-    conversion (fp32 for the GEMV, bf16/f16 for the MFMA operands) and its
-    operand layout."""
-    print(f"256 codes {dtype} path={PATHS[path]} m={m}", flush=True)
-    n, k = 256, 512
-    q = torch.arange(256, dtype=torch.int32).to(torch.uint8)[:, None].repeat(1, k).contiguous().to(DEV)
+@pytest.mark.parametrize("path,m,n,k", [(fw.PATH_GEMV, 1, 256, 512), (fw.PATH_SKINNY, 2, 256, 512),
+                                        (fw.PATH_SKINNY, 6, 256, 512), (fw.PATH_SKINNY, 12, 256, 512),
+                                        (fw.PATH_SKINNY, 20, 256, 512), (fw.PATH_FALLBACK, 2, 256, 512),
+                                        (fw.PATH_SKINNY, 2, 12288, 1024), (fw.PATH_SKINNY, 12, 256, 2048),
+                                        (fw.PATH_SKINNY, 20, 8192, 1024), (fw.PATH_SKINNY, 32, 16384, 512)])
+def test_all_256_codes_decode_exactly_on_each_path(dtype, path, m, n, k):
+    """q[n, :] = n mod 256 for every code, unit scales and a one-hot x: y[n] is
+    the exact value of its code (0x7F / 0xFF give NaN). Pins each kernel's
+    hardware conversion (fp32 for the GEMV, bf16/f16 for the MFMA operands)
+    and its operand layout; the wide shapes take the direct-to-LDS kernel."""
+    act = fw.BF16 if dtype == torch.bfloat16 else fw.FP16
+    print(f"256 codes {dtype} path={PATHS[path]} m={m} n={n} k={k} "
+          f"{fw.fp8w_linear_kernel(path, m, n, k, act, 0, 0)}", flush=True)
+    q = (torch.arange(n, dtype=torch.int32) % 256).to(torch.uint8)[:, None].repeat(1, k).contiguous().to(DEV)
     s = torch.ones(n, dtype=torch.float32, device=DEV)
     x = torch.zeros((m, k), dtype=dtype)
     x[0, 5] = 1.0
@@ -114,7 +143,7 @@ def test_all_256_codes_decode_exactly_on_each_path(dtype, path, m):
     fw.linear(x.to(DEV), q, s, None, out=y, path=path)
     torch.cuda.synchronize()
     yv = y.double().cpu().numpy()
-    ref = oracle.decode(np.arange(256))
+    ref = oracle.decode(np.arange(n) % 256)
     fin = np.isfinite(ref)
     assert np.array_equal(yv[0][fin], ref[fin])
     assert np.all(np.isnan(yv[0][~fin]))
