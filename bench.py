@@ -315,12 +315,19 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--only-timed", action="store_true",
                     help="run only the timed region (for profiler runs: every GEMV launch is then a timed one)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print a markdown table of the library's kernels in a rocprofv3 kernel trace, then exit")
+    ap.add_argument("--last", type=int, default=None,
+                    help="with --trace-summary: only the last N library dispatches")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/gemv_decode_traffic.json from two rocprofv3 --pmc runs, then exit")
     args = ap.parse_args()
     SPIN_MS = args.spin_ms
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_FILE)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.last)
         return
 
     if args.gpus != 1:
@@ -468,6 +475,32 @@ def pmc_summary(fetch_csv, write_csv, out_path):
     with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def trace_summary(csv_path, last=None):
+    """Markdown table of the library's kernels in a rocprofv3 --kernel-trace CSV:
+    one row per kernel instance and grid (the grid identifies the shape), with
+    launch count and duration statistics in microseconds. `last` keeps only the
+    last `last` library dispatches (the timed region of bench.py --only-timed)."""
+    import csv
+    import re
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Dispatch_Id"]))
+    ours = [r for r in rows if "fp8w::" in r["Kernel_Name"]]
+    if last:
+        ours = ours[-last:]
+    groups = {}
+    for r in ours:
+        m = re.search(r"(\w+_kernel)(<[^()]*>)?\(", r["Kernel_Name"].replace("(anonymous namespace)::", ""))
+        name = (m.group(1) + (m.group(2) or "")).replace("fp8w::", "") if m else r["Kernel_Name"][:60]
+        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        key = (name, wgs, int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = ["| Kernel | Workgroups x threads | Launches | Mean (us) | Median (us) | Min (us) |",
+             "|---|---|---|---|---|---|"]
+    for (name, wgs, wg), d in groups.items():
+        d = np.array(d)
+        lines.append(f"| `{name}` | {wgs} x {wg} | {len(d)} | {d.mean():.3f} | {np.median(d):.3f} | {d.min():.3f} |")
+    print("\n".join(lines))
 
 
 def extra_sections(dev, stream, reps=100):
