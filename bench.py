@@ -106,6 +106,9 @@ class Call:
         self.layer, self.x = layer, x
         self.m = x.shape[0]
         self.y = torch.empty((self.m, layer.n), dtype=x.dtype, device=dev)
+        if ws is None:  # the workspace the library asks for (fallback, or a k split), allocated once
+            wsb = fw.workspace_bytes(x, layer.qs[0][0])
+            ws = torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None
         self.ws = ws
         act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
         self.path = ["gemv", "skinny", "fallback"][fw.linear_path(x, layer.qs[0][0])]
@@ -156,7 +159,13 @@ def burst_us(call, reps, warmup, stream, warm=False, spin_ms=None):
 
 def call_report(call, us):
     gbps = call.bytes / (us * 1e-6) / 1e9
+    act = fw.BF16 if call.x.dtype == torch.bfloat16 else fw.FP16
+    kernel = fw.fp8w_linear_kernel(fw.PATH_AUTO, call.m, call.layer.n, call.layer.k, act, call.x.data_ptr(),
+                                   call.layer.qs[0][0].data_ptr())
+    if call.path == "skinny" and call.ws is None and "splitk" in kernel:
+        kernel = "single pass (no workspace)"
     return {"layer": call.layer.name, "m": call.m, "n": call.layer.n, "k": call.layer.k, "path": call.path,
+            "kernel": kernel,
             "us_per_call": round(us, 3), "alg_bytes": call.bytes, "gbps": round(gbps, 1),
             "pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
             "tflops": round(2.0 * call.m * call.layer.n * call.layer.k / (us * 1e-6) / 1e12, 3)}
@@ -512,7 +521,7 @@ def extra_sections(dev, stream, reps=100):
     for m in workloads.SKINNY_MS:
         c = Call(L, workloads.skinny_x(m).to(dev), dev)
         sk.append(call_report(c, burst_us(c, reps, 10, stream)))
-        log(f"  skinny m={m}: {sk[-1]['us_per_call']:.2f} us {sk[-1]['pct_peak']:.1f}% of peak [{c.path}]")
+        log(f"  skinny m={m}: {sk[-1]['us_per_call']:.2f} us {sk[-1]['pct_peak']:.1f}% of peak [{sk[-1]['kernel']}]")
     ex["skinny_sweep"] = sk
     ex["skinny_quantize_ms"] = round(L.quantize_ms, 3)
     del L
@@ -540,11 +549,10 @@ def extra_sections(dev, stream, reps=100):
         L = Layer(workloads.large_layer(shape), max(1, math.ceil(ROTATE_BYTES / per)), dev)
         for m in workloads.LARGE_MS:
             x = workloads.large_x(shape, m).to(dev)
-            wsb = fw.workspace_bytes(x, L.qs[0][0])
-            ws = torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None
-            c = Call(L, x, dev, ws)
+            c = Call(L, x, dev)
             lg.append(call_report(c, burst_us(c, max(20, reps // 2), 5, stream)))
-            log(f"  large {shape} m={m} [{c.path}]: {lg[-1]['us_per_call']:.2f} us {lg[-1]['pct_peak']:.1f}% of peak")
+            log(f"  large {shape} m={m} [{lg[-1]['kernel']}]: {lg[-1]['us_per_call']:.2f} us "
+                f"{lg[-1]['pct_peak']:.1f}% of peak")
         lg.append({"layer": L.name, "quantize_ms": round(L.quantize_ms, 3)})
         del L
         torch.cuda.empty_cache()

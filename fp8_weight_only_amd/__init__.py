@@ -199,9 +199,11 @@ def linear(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Te
     """y = scale[n] * sum_k x[m,k] value(q[n,k]) + bias[n], rounded once to x.dtype.
 
     x: [m, k] bf16 / fp16; q: [n, k] uint8 codes; scale: [n] fp32; bias: [n]
-    of x.dtype or None. ``workspace`` (uint8, any device tensor) is only needed
-    on the fallback path; when it is None and the path needs one, one is
-    allocated here with torch."""
+    of x.dtype or None. ``workspace`` (any device tensor) is what the C ABI
+    calls workspace: needed on the fallback path, used for a k split on a few
+    skinny shapes. When it is None and the call uses one, one of
+    fp8w_linear_workspace_bytes is allocated here with torch; an empty tensor
+    makes such skinny shapes take their single-pass plan."""
     if x.dim() != 2 or q.dim() != 2 or q.dtype != torch.uint8 or scale.dtype != torch.float32:
         raise ValueError("expected x [m,k], q uint8 [n,k], scale fp32 [n]")
     m, k = x.shape
@@ -222,8 +224,11 @@ def linear(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Te
     sp = _dev(scale, "scale") if n else 0
     bp = _dev(bias, "bias") if bias is not None and n else 0
     yp = _dev(out, "out") if out.numel() else 0
-    if path == PATH_FALLBACK or (path == PATH_AUTO and fp8w_linear_path(m, n, k, act, xp, qp, yp) == PATH_FALLBACK):
+    auto = fp8w_linear_path(m, n, k, act, xp, qp, yp)
+    if path == PATH_FALLBACK or (path == PATH_AUTO and auto == PATH_FALLBACK):
         need = n * k * 2
+    elif path in (PATH_AUTO, PATH_SKINNY) and auto == PATH_SKINNY:
+        need = fp8w_linear_workspace_bytes(m, n, k, act, xp, qp, yp)
     else:
         need = 0
     if need and workspace is None:

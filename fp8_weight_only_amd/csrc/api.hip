@@ -107,6 +107,15 @@ fp8w_status_t check_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k
     return FP8W_SUCCESS;
 }
 
+// Whether `need` bytes of workspace at ws overlap any operand of the call.
+bool ws_overlaps(const void* ws, size_t need, const void* x, int64_t m, int64_t k, const uint8_t* q,
+                 const float* scale, const void* bias, int64_t n, const void* y)
+{
+    return overlap(ws, need, y, (size_t)m * (size_t)n * 2) || overlap(ws, need, x, (size_t)m * (size_t)k * 2) ||
+           overlap(ws, need, q, (size_t)n * (size_t)k) || overlap(ws, need, scale, (size_t)n * 4) ||
+           overlap(ws, need, bias, bias ? (size_t)n * 2 : 0);
+}
+
 fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, const uint8_t* q,
                          const float* scale, const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes,
                          int path, hipStream_t stream)
@@ -132,8 +141,19 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
     const fp8w::Act a = act_of(act);
     if (path == FP8W_PATH_GEMV)
         return hip_status(fp8w::launch_gemv(x, a, k, q, scale, bias, n, y, stream));
-    if (path == FP8W_PATH_SKINNY)
-        return hip_status(fp8w::launch_skinny(x, a, m, k, q, scale, bias, n, y, stream));
+    if (path == FP8W_PATH_SKINNY) {
+        // split k on shapes that use it, when the caller's workspace is large enough
+        const size_t need = fp8w::skinny_workspace_bytes(m, n, k);
+        const bool use_ws = need > 0 && ws && ws_bytes >= need;
+        if (use_ws) {
+            if (!aligned(ws, 16))
+                return FP8W_ERR_MISALIGNED;
+            if (ws_overlaps(ws, need, x, m, k, q, scale, bias, n, y))
+                return FP8W_ERR_INVALID_VALUE;
+        }
+        return hip_status(fp8w::launch_skinny(x, a, m, k, q, scale, bias, n, y, use_ws ? ws : nullptr,
+                                              use_ws ? ws_bytes : 0, stream));
+    }
 
     const size_t need = fallback_workspace(n, k, act);
     if (need > 0) {
@@ -141,10 +161,7 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
             return FP8W_ERR_WORKSPACE;
         if (!aligned(ws, 2))
             return FP8W_ERR_MISALIGNED;
-        const size_t ybytes = (size_t)m * (size_t)n * 2;
-        if (overlap(ws, need, y, ybytes) || overlap(ws, need, x, (size_t)m * (size_t)k * 2) ||
-            overlap(ws, need, q, (size_t)n * (size_t)k) || overlap(ws, need, scale, (size_t)n * 4) ||
-            overlap(ws, need, bias, bias ? (size_t)n * 2 : 0))
+        if (ws_overlaps(ws, need, x, m, k, q, scale, bias, n, y))
             return FP8W_ERR_INVALID_VALUE;
         st = hip_status(fp8w::launch_dequantize(q, nullptr, n, k, ws, a, stream));
         if (st != FP8W_SUCCESS)
@@ -238,6 +255,8 @@ size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t
                                    const uint8_t* q, const void* y)
 {
     const int p = fp8w_linear_path(m, n, k, act_dtype, x, q, y);
+    if (p == FP8W_PATH_SKINNY)
+        return fp8w::skinny_workspace_bytes(m, n, k);
     if (p != FP8W_PATH_FALLBACK)
         return 0;
     return fallback_workspace(n, k, act_dtype);
@@ -253,7 +272,7 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || k % 256 != 0 || k == 0)
             return nullptr;
-        return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(k) : fp8w::skinny_kernel_name(m, n, k);
+        return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(k) : fp8w::skinny_kernel_name(m, n, k, true);
     }
     if (path == FP8W_PATH_FALLBACK)
         return "dequantize_kernel+fallback_gemm_kernel";

@@ -24,13 +24,19 @@ hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, cons
 // Name of the GEMV instance launch_gemv picks for this k.
 const char* gemv_kernel_name(int64_t k);
 
-// M = 1..32 MFMA skinny GEMM; k % 256 == 0, x and q 16-byte aligned.
-hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
-                         const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream);
+// M = 1..32 MFMA skinny GEMM; k % 256 == 0, x and q 16-byte aligned. Shapes
+// that split k use ws (fp32 partial sums, 16-byte aligned, not overlapping any
+// operand) when ws_bytes >= skinny_workspace_bytes(m, n, k); otherwise they take
+// the single-pass plan.
+hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
+                         const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Workspace bytes the skinny path uses for split k on this shape (0: none).
+size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 // Name of the kernel and tile launch_skinny picks for this shape (a
 // thread-local string; for tests and measurement reports).
-const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k);
+const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace);
 
 // Dequantize codes to out_type: value(q) * scale[r] (scale != nullptr) or the
 // exact unscaled value (scale == nullptr).

@@ -312,7 +312,8 @@ struct Pipe {
 template <typename A, int XR, int CT, int KP, int NS>
 __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k)
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k,
+    float* __restrict__ part_out)
 {
     using P = Pipe<A, XR, CT, KP, NS>;
     using C = typename P::C;
@@ -322,9 +323,11 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t b2[NS > 2 ? C::STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t b3[NS > 3 ? C::STAGE : 16];
 
+    // split k: workgroup row blockIdx.y owns k range [y * kc, (y + 1) * kc)
+    const int64_t kc = k / gridDim.y;
     P p;
-    p.x = x;
-    p.q = q;
+    p.x = x + (int64_t)blockIdx.y * kc;
+    p.q = q + (int64_t)blockIdx.y * kc;
     p.m = m;
     p.n = n;
     p.k = k;
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
         bi[r] = bias_bits(bias, ch);
     }
 
-    const int64_t S = k / (KP * 256);
+    const int64_t S = kc / (KP * 256);
     p.S = S;
     // workgroups are dealt to the eight XCDs in turn: consecutive workgroups of
     // one XCD get consecutive start stages
@@ -426,6 +429,16 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
         if (tok >= m)
             continue;
         const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+        if (part_out) {  // split k: fp32 partial sums, reduced by splitk_reduce_kernel
+            float* o = part_out + ((int64_t)blockIdx.y * m + tok) * n;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
+                if (ch < n)
+                    o[ch] = v[r];
+            }
+            continue;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
@@ -433,6 +446,24 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
                 y[(int64_t)tok * n + ch] = epilogue<A>(v[r], sc[r], bi[r]);
         }
     }
+}
+
+// Sum of the split-k partial sums in split order, then the epilogue: one
+// output per thread.
+template <typename A>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int m,
+                                                            int64_t n, const float* __restrict__ scale,
+                                                            const uint16_t* __restrict__ bias,
+                                                            uint16_t* __restrict__ y)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)m * n)
+        return;
+    const int64_t ch = e % n;
+    float sum = part[e];
+    for (int s = 1; s < splits; ++s)
+        sum += part[(int64_t)s * m * n + e];
+    y[e] = epilogue<A>(sum, scale[ch], bias_bits(bias, ch));
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -448,32 +479,45 @@ hipError_t launch_seg(const void* x, int m, int64_t k, const uint8_t* q, const f
     return hipGetLastError();
 }
 
+// splits > 1: k is split over `splits` workgroup rows whose fp32 partial sums
+// go to part (splits * m * n floats), then a second kernel reduces them.
 template <typename A, int XR, int CT, int KP, int NS>
 hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
-                       int64_t n, void* y, hipStream_t stream)
+                       int64_t n, void* y, hipStream_t stream, int splits = 1, float* part = nullptr)
 {
-    const dim3 grid((unsigned)((n + 16 * CT - 1) / (16 * CT))), block(CT * KP * kWave);
+    const dim3 grid((unsigned)((n + 16 * CT - 1) / (16 * CT)), (unsigned)splits), block(CT * KP * kWave);
     hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
-                       q, scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
+                       q, scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k,
+                       splits > 1 ? part : nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits <= 1)
+        return e;
+    const int64_t total = (int64_t)m * n;
+    hipLaunchKernelGGL((splitk_reduce_kernel<A>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, part,
+                       splits, m, n, scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y));
     return hipGetLastError();
 }
 
 // Kernel choice per shape, from sweeps on MI355X (k % 256 == 0 here).
-// pipe_kernel: a workgroup owns 16 * CT channels over the whole of k, so CT is
-// the largest that still gives about one workgroup per CU (224-448 workgroups
-// on the decode and sweep layers), and NS the deepest ring whose LDS lets every
-// workgroup be resident at once. seg_kernel covers small batches on narrow
-// layers, where it measured faster, and the shapes the ring cannot tile.
+// pipe_kernel: a workgroup owns 16 * CT channels, so CT is the largest that
+// still gives about one workgroup per CU (224-448 workgroups on the decode and
+// sweep layers), KP > 1 adds waves on narrower layers, and NS is the deepest
+// ring whose LDS lets every workgroup be resident at once. Layers of 8192
+// channels with long k split k over two workgroup rows when the batch is
+// above 16 (fp32 partial sums in the caller's workspace, one more kernel to
+// reduce them); without workspace they take the single-pass plan. seg_kernel
+// covers small batches on narrow layers, where it measured faster, and the
+// shapes the ring cannot tile.
 struct SkinnyPlan {
     bool pipe;
-    int xr, ct, kp, ns;         // pipe_kernel
-    int seg, t, w, u, mt;       // seg_kernel
+    int xr, ct, kp, ns, splits;  // pipe_kernel
+    int seg, t, w, u, mt;        // seg_kernel
 };
 
-SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k)
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
 {
     SkinnyPlan p{};
-    int ct = 0, kp = 1, ns = 4;
+    int ct = 0, kp = 1, ns = 4, splits = 1;
     if (m >= 2) {
         if (n >= 16384) {
             ct = 4;
@@ -481,24 +525,35 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k)
         } else if (n >= 12288) {
             ct = 4;
         } else if (n >= 8192) {
-            ct = 2;
+            if (m > 16 && allow_split && k % (2 * 1024) == 0) {
+                ct = 4;
+                splits = 2;
+            } else if (m <= 16 && k % 2048 == 0) {
+                ct = 2;
+                kp = 2;
+            } else {
+                ct = 2;
+            }
         } else if (m > 8) {
             ct = 1;
             kp = 2;
         }
     }
     if (ct != 0) {
-        if (k % (kp * 256 * ns) != 0)
+        const int64_t kc = k / splits;
+        if (kc % (kp * 256 * ns) != 0)
             ns = 2;
-        if (k % (kp * 256 * ns) == 0) {
+        if (kc % (kp * 256 * ns) == 0) {
             p.pipe = true;
             p.xr = m <= 4 ? 4 : m <= 8 ? 8 : m <= 16 ? 16 : m <= 24 ? 24 : 32;
             p.ct = ct;
             p.kp = kp;
             p.ns = ns;
+            p.splits = splits;
             return p;
         }
     }
+    p.splits = 1;
     if (m <= 4)
         p.seg = 4, p.t = 4, p.w = 4, p.u = 2, p.mt = 1;
     else if (m <= 8 && n >= 8192)
@@ -512,33 +567,44 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k)
 
 template <typename A, int XR>
 hipError_t launch_pipe_xr(const SkinnyPlan& p, const void* x, int m, int64_t k, const uint8_t* q,
-                          const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
+                          const float* scale, const void* bias, int64_t n, void* y, float* part,
+                          hipStream_t stream)
 {
     const int key = p.ct * 100 + p.kp * 10 + p.ns;
+    const int sp = p.splits;
     switch (key) {
-    case 412: return launch_pipe<A, XR, 4, 1, 2>(x, m, k, q, scale, bias, n, y, stream);
-    case 414: return launch_pipe<A, XR, 4, 1, 4>(x, m, k, q, scale, bias, n, y, stream);
-    case 212: return launch_pipe<A, XR, 2, 1, 2>(x, m, k, q, scale, bias, n, y, stream);
-    case 214: return launch_pipe<A, XR, 2, 1, 4>(x, m, k, q, scale, bias, n, y, stream);
-    case 122: return launch_pipe<A, XR, 1, 2, 2>(x, m, k, q, scale, bias, n, y, stream);
-    case 124: return launch_pipe<A, XR, 1, 2, 4>(x, m, k, q, scale, bias, n, y, stream);
+    case 412: return launch_pipe<A, XR, 4, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 414: return launch_pipe<A, XR, 4, 1, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 212: return launch_pipe<A, XR, 2, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 214: return launch_pipe<A, XR, 2, 1, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 122: return launch_pipe<A, XR, 1, 2, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 124: return launch_pipe<A, XR, 1, 2, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 222:
+    case 224:
+        if constexpr (XR <= 16) {  // the plan uses two k-parts of 32 channels only up to 16 tokens
+            if (key == 222)
+                return launch_pipe<A, XR, 2, 2, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+            return launch_pipe<A, XR, 2, 2, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+        }
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
 
 template <typename A>
 hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale,
-                        const void* bias, int64_t n, void* y, hipStream_t stream)
+                        const void* bias, int64_t n, void* y, float* part, size_t part_bytes, hipStream_t stream)
 {
     const int mi = (int)m;
-    const SkinnyPlan p = plan_skinny(m, n, k);
+    const size_t need = skinny_workspace_bytes(m, n, k);
+    const SkinnyPlan p = plan_skinny(m, n, k, part != nullptr && need > 0 && part_bytes >= need);
     if (p.pipe) {
         switch (p.xr) {
-        case 4: return launch_pipe_xr<A, 4>(p, x, mi, k, q, scale, bias, n, y, stream);
-        case 8: return launch_pipe_xr<A, 8>(p, x, mi, k, q, scale, bias, n, y, stream);
-        case 16: return launch_pipe_xr<A, 16>(p, x, mi, k, q, scale, bias, n, y, stream);
-        case 24: return launch_pipe_xr<A, 24>(p, x, mi, k, q, scale, bias, n, y, stream);
-        default: return launch_pipe_xr<A, 32>(p, x, mi, k, q, scale, bias, n, y, stream);
+        case 4: return launch_pipe_xr<A, 4>(p, x, mi, k, q, scale, bias, n, y, part, stream);
+        case 8: return launch_pipe_xr<A, 8>(p, x, mi, k, q, scale, bias, n, y, part, stream);
+        case 16: return launch_pipe_xr<A, 16>(p, x, mi, k, q, scale, bias, n, y, part, stream);
+        case 24: return launch_pipe_xr<A, 24>(p, x, mi, k, q, scale, bias, n, y, part, stream);
+        default: return launch_pipe_xr<A, 32>(p, x, mi, k, q, scale, bias, n, y, part, stream);
         }
     }
     if (p.seg == 4)
@@ -552,25 +618,37 @@ hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, c
 
 }  // namespace
 
-hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
-                         const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
+size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k)
+{
+    if (m < 1 || m > 32 || n < 1 || k < 256 || k % 256 != 0)
+        return 0;
+    const SkinnyPlan p = plan_skinny(m, n, k, true);
+    return p.pipe && p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
+hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
+                         const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     if (n == 0 || m == 0)
         return hipSuccess;
     if (m > 32 || k % 256 != 0)
         return hipErrorInvalidValue;
+    float* part = static_cast<float*>(ws);
     if (act == Act::BF16)
-        return launch_typed<Bf16>(x, m, k, q, scale, bias, n, y, stream);
+        return launch_typed<Bf16>(x, m, k, q, scale, bias, n, y, part, ws_bytes, stream);
     if (act == Act::FP16)
-        return launch_typed<F16>(x, m, k, q, scale, bias, n, y, stream);
+        return launch_typed<F16>(x, m, k, q, scale, bias, n, y, part, ws_bytes, stream);
     return hipErrorInvalidValue;
 }
 
-const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k)
+const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace)
 {
-    thread_local char name[64];
-    const SkinnyPlan p = plan_skinny(m, n, k);
-    if (p.pipe)
+    thread_local char name[96];
+    const SkinnyPlan p = plan_skinny(m, n, k, with_workspace);
+    if (p.pipe && p.splits > 1)
+        snprintf(name, sizeof name, "pipe_kernel<XR=%d,CT=%d,KP=%d,NS=%d>x%d+splitk_reduce_kernel", p.xr, p.ct,
+                 p.kp, p.ns, p.splits);
+    else if (p.pipe)
         snprintf(name, sizeof name, "pipe_kernel<XR=%d,CT=%d,KP=%d,NS=%d>", p.xr, p.ct, p.kp, p.ns);
     else
         snprintf(name, sizeof name, "seg_kernel<SEG=%d,T=%d,W=%d,U=%d,MT=%d>", p.seg, p.t, p.w, p.u, p.mt);

@@ -99,14 +99,17 @@ FP8W_API fp8w_status_t fp8w_quantize(const void* w, fp8w_dtype_t w_dtype, int64_
  *   q, scale  as written by fp8w_quantize for an [n, k] weight.
  *   bias      [n] in act_dtype, or NULL for none.
  *   y         [m, n] output in act_dtype; must not overlap x, q, scale or bias.
- *   workspace device scratch for the fallback path, at least
- *             fp8w_linear_workspace_bytes(...) bytes (NULL / 0 when that is 0),
- *             16-byte aligned for full speed; it must not overlap anything else.
+ *   workspace device scratch of fp8w_linear_workspace_bytes(...) bytes (NULL / 0
+ *             when that is 0); it must not overlap anything else. The fallback
+ *             path needs it (2-byte aligned, FP8W_ERR_WORKSPACE when missing or
+ *             short). A few skinny shapes (8192-channel layers, m > 16) use it
+ *             for fp32 partial sums of a k split (16-byte aligned); given less,
+ *             they take a slower single-pass plan instead, with no error.
  * Dispatch (fp8w_linear_path): the fast kernels take 1 <= m <= 32 with
  * k % 256 == 0 and x, q 16-byte aligned (m == 1: GEMV, else skinny MFMA);
- * everything else takes the fallback. Results of different paths agree to
- * within fp32 summation-order rounding. Asynchronous; a failed launch returns
- * FP8W_ERR_HIP.
+ * everything else takes the fallback. Results of different paths and plans
+ * agree to within fp32 summation-order rounding; a given call is
+ * deterministic. Asynchronous; a failed launch returns FP8W_ERR_HIP.
  */
 FP8W_API fp8w_status_t fp8w_linear(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k, const uint8_t* q,
                           const float* scale, const void* bias, int64_t n, void* y, void* workspace,
@@ -147,15 +150,17 @@ FP8W_API fp8w_status_t fp8w_dequantize_fallback(const uint8_t* q, const float* s
 FP8W_API int fp8w_linear_path(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x, const uint8_t* q,
                      const void* y);
 
-/* Workspace bytes fp8w_linear needs for these sizes and pointers (0 on the
-   fast paths, n * k * element_size(act_dtype) on the fallback; 0 when invalid). */
+/* Workspace bytes fp8w_linear uses for these sizes and pointers: 0 on the GEMV
+   and most skinny shapes, splits * m * n * 4 on skinny shapes that split k,
+   n * k * element_size(act_dtype) on the fallback; 0 when invalid. */
 FP8W_API size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x,
                                    const uint8_t* q, const void* y);
 
 /*
  * Name of the kernel (and its tile parameters) that `path` (FP8W_PATH_AUTO or
  * a forced path) launches for these sizes and pointers, e.g.
- * "pipe_kernel<XR=16,CT=4,KP=1,NS=4>". A static or thread-local string, valid
+ * "pipe_kernel<XR=16,CT=4,KP=1,NS=4>", given the workspace
+ * fp8w_linear_workspace_bytes reports. A static or thread-local string, valid
  * until the next call on this thread; NULL when the arguments or the forced
  * path are invalid. For tests and measurement reports.
  */

@@ -78,7 +78,9 @@ def test_kernel_names():
     assert kn(A, 1, 4096, 14336, fw.BF16, X, Q) == "gemv_kernel<R=4,U=2,NT=128>"
     assert kn(A, 16, 14336, 4096, fw.FP16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4>"
     assert kn(A, 32, 28672, 8192, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>"
-    assert kn(A, 22, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=2,KP=1,NS=4>"
+    assert kn(A, 22, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"
+    assert kn(A, 8, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=8,CT=2,KP=2,NS=4>"
+    assert kn(A, 16, 8192, 3072, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"       # k % 2048 != 0
     assert kn(A, 16, 4096, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"
     assert kn(A, 3, 14336, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=4>"
     assert kn(A, 8, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=2,T=2,W=8,U=2,MT=1>"
@@ -102,6 +104,10 @@ def test_workspace_bytes():
     assert wb(64, 100, 512, fw.FP16, X, Q, Y) == 100 * 512 * 2
     assert wb(1, 10, 0, fw.BF16, X, Q, Y) == 0
     assert wb(1, 4096, 4096, fw.FP32, X, Q, Y) == 0
+    assert wb(32, 8192, 28672, fw.BF16, X, Q, Y) == 2 * 32 * 8192 * 4     # split k
+    assert wb(17, 11000, 4096, fw.FP16, X, Q, Y) == 2 * 17 * 11000 * 4
+    assert wb(16, 8192, 28672, fw.BF16, X, Q, Y) == 0
+    assert wb(32, 8192, 1024, fw.BF16, X, Q, Y) == 0                      # k % 2048 != 0
 
 
 def _lin(x=X, act=fw.BF16, m=4, k=4096, q=Q, s=S, b=B, n=4096, y=Y, ws=0, wsb=0, path=fw.PATH_AUTO):
@@ -134,6 +140,14 @@ def test_linear_rejects_invalid_arguments():
     assert _lin(y=Q) == fw.ERR_INVALID_VALUE
     assert _lin(y=S - 16) == fw.ERR_INVALID_VALUE
     assert _lin(y=B) == fw.ERR_INVALID_VALUE
+
+
+def test_split_k_workspace_is_validated():
+    need = 2 * 32 * 8192 * 4
+    big = dict(m=32, n=8192, k=28672)
+    assert _lin(ws=WS + 8, wsb=need, **big) == fw.ERR_MISALIGNED
+    assert _lin(ws=X, wsb=need, **big) == fw.ERR_INVALID_VALUE      # overlaps x
+    assert _lin(ws=Y - 64, wsb=need, **big) == fw.ERR_INVALID_VALUE  # overlaps y
 
 
 def test_linear_fallback_needs_workspace():

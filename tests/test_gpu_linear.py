@@ -89,6 +89,11 @@ PIPE = [
     (32, 8192, 3072, torch.float16, "pipe_kernel<XR=32,CT=2,KP=1,NS=4>"),
     (32, 300, 4096, torch.bfloat16, "pipe_kernel<XR=32,CT=1,KP=2,NS=4>"),
     (3, 16500, 1536, torch.bfloat16, "pipe_kernel<XR=4,CT=4,KP=1,NS=2>"),
+    (6, 8192, 2048, torch.bfloat16, "pipe_kernel<XR=8,CT=2,KP=2,NS=4>"),
+    (12, 9000, 4096, torch.float16, "pipe_kernel<XR=16,CT=2,KP=2,NS=4>"),
+    (10, 8300, 1024, torch.bfloat16, "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"),
+    (20, 8200, 2048, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
+    (32, 8192, 4096, torch.float16, "pipe_kernel<XR=32,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
 ]
 
 
@@ -99,6 +104,35 @@ def test_pipe_kernel_parity(m, n, k, dtype, kernel):
                                  0, 0) == kernel
     case = workloads.random_case(31 * m + n + k, m, n, k, dtype, with_bias=(m % 2 == 1))
     _check(case, expect_path=fw.PATH_SKINNY)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_split_k_matches_single_pass(dtype):
+    """A shape that splits k when given workspace: with it (two workgroup rows of
+    fp32 partial sums, then the reduce kernel) and without it (single pass) both
+    pass the gate, and agree to fp32 summation-order rounding."""
+    m, n, k = 24, 8256, 4096
+    act = fw.BF16 if dtype == torch.bfloat16 else fw.FP16
+    assert fw.fp8w_linear_workspace_bytes(m, n, k, act, 0, 0, 0) == 2 * m * n * 4
+    case = workloads.random_case(4242, m, n, k, dtype, with_bias=True)
+    q, s, x, b = _prepare(case)
+    q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
+    outs = []
+    for ws in (None, torch.empty(0, dtype=torch.uint8, device=DEV)):
+        y = nan_like((m, n), dtype, DEV)
+        fw.linear(x, q, s, b, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        yv = y.double().cpu().numpy()
+        assert_gate(yv, y_ref, x64, amax, f"split={ws is None}")
+        outs.append(yv)
+    assert np.allclose(outs[0], outs[1], rtol=2e-2, atol=1e-2)
+    # a second call reuses the workspace contents without clearing: same bits
+    y2 = nan_like((m, n), dtype, DEV)
+    ws = torch.full((2 * m * n * 4,), 0x7F, dtype=torch.uint8, device=DEV)
+    fw.linear(x, q, s, b, out=y2, workspace=ws)
+    fw.linear(x, q, s, b, out=y2, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.double().cpu().numpy(), outs[0])
 
 
 @pytest.mark.parametrize("m,k", [(1, 256), (1, 4096), (2, 1024), (16, 768), (17, 512), (32, 2048)])
