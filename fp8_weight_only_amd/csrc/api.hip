@@ -272,7 +272,7 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || k % 256 != 0 || k == 0)
             return nullptr;
-        return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(k) : fp8w::skinny_kernel_name(m, n, k, true);
+        return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(n, k) : fp8w::skinny_kernel_name(m, n, k, true);
     }
     if (path == FP8W_PATH_FALLBACK)
         return "dequantize_kernel+fallback_gemm_kernel";

@@ -140,23 +140,28 @@ hipError_t launch_cfg(const void* x, int64_t k, const uint8_t* q, const float* s
     return hipGetLastError();
 }
 
-// Tile choice, from sweeps on MI355X over the decode and large shapes: two
-// rows per 256-thread workgroup up to k = 4096 (one pass per row), four rows
-// per 128-thread workgroup with two passes in flight beyond that.
+// Tile choice, from sweeps on MI355X: two passes in flight per 128-thread
+// workgroup; two rows per workgroup for weights under 96 MB, four above. Per
+// shape, other tiles came within a few percent; a single instance for all the
+// decode-sized layers also means consecutive layers of different shapes run
+// the same code: in a decode step, switching to a second kernel binary cost
+// about 1 us, the refill of each CU's instruction cache.
+constexpr int64_t kLargeWeight = (int64_t)96 << 20;
+
 template <typename A>
 hipError_t launch_typed(const void* x, int64_t k, const uint8_t* q, const float* scale, const void* bias,
                         int64_t n, void* y, hipStream_t stream)
 {
-    if (k <= 4096)
-        return launch_cfg<A, 2, 1, 256>(x, k, q, scale, bias, n, y, stream);
-    return launch_cfg<A, 4, 2, 128>(x, k, q, scale, bias, n, y, stream);
+    if (n * k >= kLargeWeight)
+        return launch_cfg<A, 4, 2, 128>(x, k, q, scale, bias, n, y, stream);
+    return launch_cfg<A, 2, 2, 128>(x, k, q, scale, bias, n, y, stream);
 }
 
 }  // namespace
 
-const char* gemv_kernel_name(int64_t k)
+const char* gemv_kernel_name(int64_t n, int64_t k)
 {
-    return k <= 4096 ? "gemv_kernel<R=2,U=1,NT=256>" : "gemv_kernel<R=4,U=2,NT=128>";
+    return n * k >= kLargeWeight ? "gemv_kernel<R=4,U=2,NT=128>" : "gemv_kernel<R=2,U=2,NT=128>";
 }
 
 hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,

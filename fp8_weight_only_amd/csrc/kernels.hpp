@@ -21,8 +21,8 @@ hipError_t launch_quantize(const void* w, Act w_type, int64_t n, int64_t k, uint
 hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,
                        const void* bias, int64_t n, void* y, hipStream_t stream);
 
-// Name of the GEMV instance launch_gemv picks for this k.
-const char* gemv_kernel_name(int64_t k);
+// Name of the GEMV instance launch_gemv picks for this shape.
+const char* gemv_kernel_name(int64_t n, int64_t k);
 
 // M = 1..32 MFMA skinny GEMM; k % 256 == 0, x and q 16-byte aligned. Shapes
 // that split k use ws (fp32 partial sums, 16-byte aligned, not overlapping any
