@@ -275,7 +275,7 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
         return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(n, k) : fp8w::skinny_kernel_name(m, n, k, true);
     }
     if (path == FP8W_PATH_FALLBACK)
-        return "dequantize_kernel+fallback_gemm_kernel";
+        return fp8w::fallback_kernel_name(m, n, k, x);
     return nullptr;
 }
 

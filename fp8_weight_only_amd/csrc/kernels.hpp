@@ -43,6 +43,10 @@ const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_worksp
 hipError_t launch_dequantize(const uint8_t* q, const float* scale, int64_t n, int64_t k, void* out,
                              Act out_type, hipStream_t stream);
 
+// Name of the fallback's GEMM for this shape (assuming a 16-byte aligned
+// workspace).
+const char* fallback_kernel_name(int64_t m, int64_t n, int64_t k, const void* x);
+
 // Guarded GEMM over an activation-dtype weight wd [n, k] (any m, n, k, any
 // 2-byte alignment) followed by the scale/bias epilogue.
 hipError_t launch_fallback_gemm(const void* x, Act act, int64_t m, int64_t k, const void* wd,

@@ -1,0 +1,109 @@
+// Direct-to-LDS load ring shared by the streaming MFMA kernels (gfx950).
+//
+// A workgroup keeps NS stage buffers in LDS. Stage s is loaded with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at the instruction's LDS
+// base + 16 * lane; no registers hold data in flight), NS - 1 stages are in
+// flight while the matrix cores consume the oldest one.
+//
+// How the waits stay exact: every stage issues the same number of load
+// instructions per wave (LOADS), all unconditionally, and the stage buffers
+// are distinct __shared__ arrays addressed only through statically unrolled
+// steps. The compiler's own wait-count pass can then tell the buffers apart
+// and inserts no drain of its own inside the loop, and the explicit
+// s_waitcnt vmcnt(LOADS * (NS - 2)) before each step's barrier is exactly
+// "this stage has landed" (loads complete in order). The barrier is a bare
+// s_barrier: __syncthreads() would add release/acquire fences that drain
+// every outstanding load, the prefetched stages included.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+#define FP8W_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+namespace fp8w {
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's vector-memory loads
+// (the direct-to-LDS ones included) still outstanding, all LDS reads returned.
+template <int N>
+__device__ __forceinline__ void wait_loads_at_most()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads();
+// LDS visibility comes from the explicit wait before it, and the empty asm
+// keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier()
+{
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Runs stages 0 .. S-1 through the ring (S % NS == 0, S >= NS). P provides
+// issue(s, buf) (exactly LOADS load instructions per wave) and compute(buf, acc).
+// The last group of NS stages issues only its first load, then drains.
+template <int NS, int LOADS, typename P, typename Acc>
+__device__ __forceinline__ void run_ring(const P& p, int64_t S, uint8_t* b0, uint8_t* b1, uint8_t* b2, uint8_t* b3,
+                                         Acc* acc)
+{
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
+    auto step = [&](int64_t s, const uint8_t* cur, uint8_t* nxt) {
+        wait_loads_at_most<LOADS*(NS - 2)>();
+        stage_barrier();
+        p.issue(s + NS - 1, nxt);
+        p.compute(cur, acc);
+    };
+    p.issue(0, b0);
+    if constexpr (NS > 2)
+        p.issue(1, b1);
+    if constexpr (NS > 3)
+        p.issue(2, b2);
+    int64_t s = 0;
+    for (; s < S - NS; s += NS) {
+        if constexpr (NS == 2) {
+            step(s, b0, b1);
+            step(s + 1, b1, b0);
+        } else if constexpr (NS == 3) {
+            step(s, b0, b2);
+            step(s + 1, b1, b0);
+            step(s + 2, b2, b1);
+        } else {
+            step(s, b0, b3);
+            step(s + 1, b1, b0);
+            step(s + 2, b2, b1);
+            step(s + 3, b3, b2);
+        }
+    }
+    if constexpr (NS == 2) {
+        step(s, b0, b1);
+        wait_loads_at_most<0>();
+        stage_barrier();
+        p.compute(b1, acc);
+    } else if constexpr (NS == 3) {
+        step(s, b0, b2);
+        wait_loads_at_most<LOADS>();
+        stage_barrier();
+        p.compute(b1, acc);
+        wait_loads_at_most<0>();
+        stage_barrier();
+        p.compute(b2, acc);
+    } else {
+        step(s, b0, b3);
+        wait_loads_at_most<2 * LOADS>();
+        stage_barrier();
+        p.compute(b1, acc);
+        wait_loads_at_most<LOADS>();
+        stage_barrier();
+        p.compute(b2, acc);
+        wait_loads_at_most<0>();
+        stage_barrier();
+        p.compute(b3, acc);
+    }
+}
+
+}  // namespace fp8w

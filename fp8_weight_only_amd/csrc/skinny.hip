@@ -40,6 +40,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "ring.hpp"
 
 namespace fp8w {
 namespace {
@@ -176,27 +177,6 @@ __global__ __launch_bounds__(W* kWave) void seg_kernel(
 }
 
 // ---------------------------------------------------------------- pipe_kernel
-#define FP8W_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's vector-memory loads
-// (the direct-to-LDS ones included) still outstanding, all LDS reads returned.
-template <int N>
-__device__ __forceinline__ void wait_loads_at_most()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-// Workgroup barrier without the release/acquire fences of __syncthreads():
-// those would drain every outstanding load, including the stages still being
-// prefetched. LDS visibility comes from the explicit wait before it; the empty
-// asm keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void stage_barrier()
-{
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // XR activation rows are fetched (m <= XR; MFMA columns past XR read row XR - 1
 // and are discarded); CT channel tiles of 16 and KP k-parts make the
 // workgroup's CT * KP waves; NS stage buffers; one stage is 256 k per wave.
@@ -294,21 +274,9 @@ struct Pipe {
         }
     }
 
-    // One pipeline step: stage s is complete for every wave, then stage
-    // s + NS - 1 is issued into the buffer stage s - 1 used, then s is consumed.
-    __device__ __forceinline__ void step(int64_t s, const uint8_t* cur, uint8_t* nxt, f32x4* acc) const
-    {
-        wait_loads_at_most<C::LOADS*(NS - 2)>();
-        stage_barrier();
-        issue(s + NS - 1, nxt);
-        compute(cur, acc);
-    }
 };
 
-// Requires k % (KP * 256 * NS) == 0. The stage buffers are distinct arrays and
-// the ring is unrolled NS-fold, with every load and wait unconditional, so the
-// compiler can tell the buffers apart and adds no drain of its own inside the
-// loop; the last group of NS stages issues only its first load and then drains.
+// Requires (k / splits) % (KP * 256 * NS) == 0; the ring is run_ring's.
 template <typename A, int XR, int CT, int KP, int NS>
 __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
@@ -359,53 +327,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     // workgroups are dealt to the eight XCDs in turn: consecutive workgroups of
     // one XCD get consecutive start stages
     p.rot = (int64_t)(blockIdx.x / 8) % S;
-    p.issue(0, b0);
-    if constexpr (NS > 2)
-        p.issue(1, b1);
-    if constexpr (NS > 3)
-        p.issue(2, b2);
-    int64_t s = 0;
-    for (; s < S - NS; s += NS) {
-        if constexpr (NS == 2) {
-            p.step(s, b0, b1, acc);
-            p.step(s + 1, b1, b0, acc);
-        } else if constexpr (NS == 3) {
-            p.step(s, b0, b2, acc);
-            p.step(s + 1, b1, b0, acc);
-            p.step(s + 2, b2, b1, acc);
-        } else {
-            p.step(s, b0, b3, acc);
-            p.step(s + 1, b1, b0, acc);
-            p.step(s + 2, b2, b1, acc);
-            p.step(s + 3, b3, b2, acc);
-        }
-    }
-    // last group: stage S - 1 is issued by its first step, then the ring drains
-    if constexpr (NS == 2) {
-        p.step(s, b0, b1, acc);
-        wait_loads_at_most<0>();
-        stage_barrier();
-        p.compute(b1, acc);
-    } else if constexpr (NS == 3) {
-        p.step(s, b0, b2, acc);
-        wait_loads_at_most<C::LOADS>();
-        stage_barrier();
-        p.compute(b1, acc);
-        wait_loads_at_most<0>();
-        stage_barrier();
-        p.compute(b2, acc);
-    } else {
-        p.step(s, b0, b3, acc);
-        wait_loads_at_most<2 * C::LOADS>();
-        stage_barrier();
-        p.compute(b1, acc);
-        wait_loads_at_most<C::LOADS>();
-        stage_barrier();
-        p.compute(b2, acc);
-        wait_loads_at_most<0>();
-        stage_barrier();
-        p.compute(b3, acc);
-    }
+    run_ring<NS, C::LOADS>(p, S, b0, b1, b2, b3, acc);
 
     // k-part partial sums meet in stage buffer 0, then wave (ct, 0) adds them in
     // k order and applies the epilogue; D[4g + r][i] is channel 4g + r, token i.

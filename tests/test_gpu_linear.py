@@ -66,6 +66,9 @@ SMALL = [
     (3, 50, 1, torch.bfloat16, True, fw.PATH_FALLBACK),
     (5, 31, 37, torch.float16, False, fw.PATH_FALLBACK),
     (4, 128, 200, torch.bfloat16, True, fw.PATH_FALLBACK),
+    (40, 300, 1000, torch.float16, True, fw.PATH_FALLBACK),    # 2 token tiles, 488-value k tail
+    (7, 16500, 776, torch.bfloat16, False, fw.PATH_FALLBACK),  # wide layer, 264-value tail
+    (12, 70, 264, torch.bfloat16, True, fw.PATH_FALLBACK),     # shortest ring (2 stages), 8-value tail
 ]
 
 
