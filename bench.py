@@ -73,10 +73,15 @@ def alg_bytes(m, n, k, bias=True):
     return n * k + 4 * n + (2 * n if bias else 0) + 2 * m * k + 2 * m * n
 
 
+# the sources that define the dominant kernel (the decode GEMV) and its dispatch;
+# a change to any of them voids the recorded traffic counters
+GEMV_SOURCES = ("api.hip", "common.hpp", "gemv.hip", "kernels.hpp")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     d = os.path.join(ROOT, "fp8_weight_only_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in GEMV_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

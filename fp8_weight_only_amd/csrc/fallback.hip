@@ -49,14 +49,18 @@ struct Out16 {
     {
         static_cast<uint16_t*>(p)[i] = A::from_f32(v);
     }
-    // 8 values to a 16-byte aligned address
+    // 8 values to a 16-byte aligned address, as a streaming (non-temporal)
+    // store: the dequantised weight is read back once, right away, by the
+    // fallback GEMM, which measured faster when these writes had drained to HBM
+    // instead of lingering dirty in the memory-side cache
     __device__ __forceinline__ static void store8(void* p, int64_t i, const float* v)
     {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             w[e] = (uint32_t)A::from_f32(v[2 * e]) | ((uint32_t)A::from_f32(v[2 * e + 1]) << 16);
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p) + i) = u32x4{w[0], w[1], w[2], w[3]};
+        __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
+                                    reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p) + i));
     }
 };
 
