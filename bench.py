@@ -30,14 +30,27 @@ Every timed region (the steps and each burst) is preceded by --spin-ms of the
 same work: the GPU raises its clocks only under sustained load, and the first
 ~10 ms run up to 15 % slower than the steady state measured here.
 
-Also reported ("extra"): the skinny sweep (M = 2..32, fp16), one decoder block
-at M = 16, the large shapes and their K = 8200 fallback, each with the same
-cache rotation; the build-time quantize; a plain streaming-read reference
-("read_ceiling": the library's fp8w_stream_read_probe over buffers of each
-decode weight's size, rotated the same way); and the CPU oracle
-("cpu_baseline").
+Per-call lines give the burst mean and p10 / median / p90 over ten groups of
+the burst, warm (one cache-resident copy) numbers, and the host wall time of a
+single call ("host_latency": the ctypes enqueue, and enqueue plus a stream
+synchronize). Skinny lines also give the matrix-core work: padded M, issued and
+useful FLOPs as a share of the 2.5 PFLOP/s dense bf16/fp16 peak.
+
+Also reported ("extra"): latency-bound calls (the 1024 x 1024 GEMV and the
+x [22,1024] x [1024,4096] shape the pages time), the skinny sweep (M = 2..32,
+fp16), one decoder block at M = 16 (seven calls, and four with q/k/v and
+gate/up merged; eager and graph-replayed steps), the large shapes and their
+K = 8200 fallback, each with the same cache rotation; the build-time quantize;
+a plain streaming-read reference ("read_ceiling": the library's
+fp8w_stream_read_probe over buffers of each decode weight's size, rotated the
+same way); and the CPU oracle ("cpu_baseline", all host threads and one),
+whose leg also checks this run's GPU results against the oracle results it
+produced.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--spin-ms MS] [--quick]
+                       [--only tiny|skinny|block|large ...] [--reps R]
+Profile helpers: --trace-summary CSV [--last N], --mfma-summary CSV N K,
+--pmc-summary FETCH_CSV WRITE_CSV.
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -145,35 +158,109 @@ def spin_up(launch, ms):
             return i
 
 
-def burst_us(call, reps, warmup, stream, warm=False, spin_ms=None):
-    """Average microseconds per launch over `reps` back-to-back launches of one call
-    (rotating weight copies unless warm), between two events on the launch stream."""
+def burst(call, reps, warmup, stream, warm=False, spin_ms=None, groups=10):
+    """Microseconds per launch over `reps` back-to-back launches of one call
+    (rotating weight copies unless warm), between events on the launch stream.
+    The launches are split into `groups` equal groups, each between two events:
+    "mean" is the whole burst's average, "p10" / "median" / "p90" are taken over
+    the groups' averages."""
     spin_up(lambda i: call.launch(0 if warm else i, stream), SPIN_MS if spin_ms is None else spin_ms)
     for i in range(warmup):
         call.launch(0 if warm else i, stream)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(reps):
-        call.launch(0 if warm else i, stream)
-    e1.record()
+    groups = max(1, min(groups, reps))
+    per = reps // groups
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    ev[0].record()
+    i = 0
+    for g in range(groups):
+        for _ in range(per):
+            call.launch(0 if warm else i, stream)
+            i += 1
+        ev[g + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+    gus = np.array([ev[g].elapsed_time(ev[g + 1]) * 1e3 / per for g in range(groups)])
+    return {"mean": ev[0].elapsed_time(ev[groups]) * 1e3 / (per * groups),
+            "p10": float(np.percentile(gus, 10)), "median": float(np.median(gus)),
+            "p90": float(np.percentile(gus, 90))}
+
+
+def burst_us(call, reps, warmup, stream, warm=False, spin_ms=None):
+    return burst(call, reps, warmup, stream, warm, spin_ms)["mean"]
+
+
+def host_latency(call, stream, reps=200):
+    """Host wall time of one warm call (same weight copy every time): the ctypes
+    call into fp8w_linear alone (enqueue), and the call followed by a stream
+    synchronize (the latency a caller that waits for the result sees), medians
+    over `reps` calls."""
+    call.launch(0, stream)
+    torch.cuda.synchronize()
+    enq, full = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        call.launch(0, stream)
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        enq.append(t1 - t0)
+        full.append(t2 - t0)
+    return {"enqueue_us": round(float(np.median(enq)) * 1e6, 2),
+            "call_and_sync_us": round(float(np.median(full)) * 1e6, 2), "calls": reps}
+
+
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix-core peak of MI355X
+
+
+def mfma_issued_flops(kernel, m, n, k):
+    """Matrix-core FLOPs a skinny launch issues, from its tile parameters (the
+    kernel name fp8w_linear_kernel reports): every v_mfma_f32_16x16x32 is
+    2*16*16*32 FLOPs whether its token columns are real or padding.
+    pipe_kernel: 16*CT-channel blocks, tokens padded to 16*MT (MT = 2 above 16
+    rows); seg_kernel: MP = 16/SEG channels x MP tokens per segment, SEG
+    segments per instruction of which one is kept, so tokens count as
+    MP*MT*SEG. None for other kernels."""
+    import re
+    mm = re.match(r"pipe_kernel<XR=(\d+),CT=(\d+),KP=\d+,NS=\d+>", kernel or "")
+    if mm:
+        xr, ct = int(mm.group(1)), int(mm.group(2))
+        mt = 2 if xr > 16 else 1
+        chans = 16 * ct * math.ceil(n / (16 * ct))
+        return 2.0 * k * chans * 16 * mt, 16 * mt
+    mm = re.match(r"seg_kernel<SEG=(\d+),T=(\d+),W=\d+,U=\d+,MT=(\d+)>", kernel or "")
+    if mm:
+        seg, t, mt = int(mm.group(1)), int(mm.group(2)), int(mm.group(3))
+        mp = 16 // seg
+        chans = mp * t * math.ceil(n / (mp * t))
+        return 2.0 * k * chans * mp * mt * seg, mp * mt * seg
+    return None, None
 
 
 def call_report(call, us):
+    """Per-call line: `us` is a burst() result (or a plain mean in microseconds)."""
+    st = us if isinstance(us, dict) else None
+    us = st["mean"] if st else us
     gbps = call.bytes / (us * 1e-6) / 1e9
     act = fw.BF16 if call.x.dtype == torch.bfloat16 else fw.FP16
     kernel = fw.fp8w_linear_kernel(fw.PATH_AUTO, call.m, call.layer.n, call.layer.k, act, call.x.data_ptr(),
                                    call.layer.qs[0][0].data_ptr())
     if call.path == "skinny" and call.ws is None and "splitk" in kernel:
         kernel = "single pass (no workspace)"
-    return {"layer": call.layer.name, "m": call.m, "n": call.layer.n, "k": call.layer.k, "path": call.path,
-            "kernel": kernel,
-            "us_per_call": round(us, 3), "alg_bytes": call.bytes, "gbps": round(gbps, 1),
-            "pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
-            "tflops": round(2.0 * call.m * call.layer.n * call.layer.k / (us * 1e-6) / 1e12, 3)}
+    useful = 2.0 * call.m * call.layer.n * call.layer.k
+    r = {"layer": call.layer.name, "m": call.m, "n": call.layer.n, "k": call.layer.k, "path": call.path,
+         "kernel": kernel,
+         "us_per_call": round(us, 3), "alg_bytes": call.bytes, "gbps": round(gbps, 1),
+         "pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+         "tflops": round(useful / (us * 1e-6) / 1e12, 3)}
+    if st:
+        r["us_p10"], r["us_median"], r["us_p90"] = (round(st[q], 3) for q in ("p10", "median", "p90"))
+    if call.path == "skinny":
+        issued, mpad = mfma_issued_flops(kernel, call.m, call.layer.n, call.layer.k)
+        if issued:
+            r["mfma"] = {"padded_m": mpad, "issued_tflops": round(issued / (us * 1e-6) / 1e12, 2),
+                         "useful_pct_of_peak": round(100.0 * useful / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 3),
+                         "issued_pct_of_peak": round(100.0 * issued / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 3)}
+    return r
 
 
 def capture_graphs(calls, copies, stream_obj):
@@ -261,28 +348,59 @@ def cpu_info():
     return os.cpu_count(), model
 
 
-def cpu_baseline(layers_np, xs, budget_s):
+def cpu_baseline(layers, lws, xs_cpu, calls, budget_s):
     """The oracle (fp64 C, OpenMP over output channels) on the host cores, on the
-    same three decode calls, repeated until ~budget_s of CPU work."""
+    same three decode calls, repeated until ~budget_s of CPU work; then once more
+    on one core. The oracle's results of this leg are also compared with the
+    GPU's: codes and scales bit for bit, and the GPU outputs of the same calls
+    against the output gate."""
     import oracle
     prepared = []
-    for lw, x in zip(layers_np, xs):
+    for lw, x in zip(lws, xs_cpu):
         q, s, _ = oracle.quantize_rows(lw.w)
-        prepared.append((x.double().numpy(), q, s, None if lw.bias is None else lw.bias.double().numpy()))
-    reps, byts = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        for (x64, q, s, b) in prepared:
-            oracle.linear_f64(x64, q, s, b)
-            byts += alg_bytes(x64.shape[0], q.shape[0], q.shape[1], b is not None)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+        prepared.append((x.double().numpy(), q, s, None if lw.bias is None else lw.bias.double().numpy(),
+                         oracle.row_amax(lw.w)))
+
+    def run(budget):
+        reps, byts, outs = 0, 0, []
+        t0 = time.perf_counter()
+        while True:
+            outs = []
+            for (x64, q, s, b, _) in prepared:
+                outs.append(oracle.linear_f64(x64, q, s, b))
+                byts += alg_bytes(x64.shape[0], q.shape[0], q.shape[1], b is not None)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, byts, el, outs
+
+    threads = oracle.num_threads()
+    reps, byts, el, outs = run(budget_s)
+    oracle.set_num_threads(1)
+    try:
+        reps1, byts1, el1, _ = run(min(budget_s, 3.0))
+    finally:
+        oracle.set_num_threads(threads)
+
+    # parity of this run's GPU results against the oracle's
+    ok = True
+    for L, c, (x64, q, s, b, amax), y_ref in zip(layers, calls, prepared, outs):
+        ok &= bool(np.array_equal(L.qs[0][0].cpu().numpy(), q))
+        ok &= bool(np.array_equal(L.qs[0][1].cpu().numpy().view(np.uint32), s.view(np.uint32)))
+        c.y.fill_(float("nan"))
+        c.launch(0, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        yv = c.y.double().cpu().numpy()
+        tol = 1e-2 * np.abs(y_ref) + 1e-3 * np.linalg.norm(x64, axis=1)[:, None] * amax[None, :]
+        ok &= bool(np.all(np.isfinite(yv)) and np.all(np.abs(yv - y_ref) <= tol))
+
     nproc, model = cpu_info()
-    return {"value": round(byts / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": round(byts / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} passes over the 3 decode GEMV calls (M=1; 4096x4096, 14336x4096, 4096x14336) "
                       f"through the fp64 oracle, {el:.1f} s",
+            "one_core": {"value": round(byts1 / el1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                         "sample": f"{reps1} passes, {el1:.1f} s"},
+            "gpu_parity_vs_this_oracle_run": ok,
             "host_cpus": nproc, "host_model": model}
 
 
@@ -299,23 +417,6 @@ def traffic_entry():
     return t.get("bytes_per_launch")
 
 
-def parity_check(layers, lws, xs_cpu, xs):
-    import oracle
-    ok = True
-    for L, lw, xc, x in zip(layers, lws, xs_cpu, xs):
-        q_ref, s_ref, _ = oracle.quantize_rows(lw.w)
-        ok &= bool(np.array_equal(L.qs[0][0].cpu().numpy(), q_ref))
-        ok &= bool(np.array_equal(L.qs[0][1].cpu().numpy().view(np.uint32), s_ref.view(np.uint32)))
-        y = fw.linear(x, L.qs[0][0], L.qs[0][1], L.bias)
-        x64 = xc.double().numpy()
-        b64 = None if lw.bias is None else lw.bias.double().numpy()
-        y_ref = oracle.linear_f64(x64, q_ref, s_ref, b64)
-        tol = 1e-2 * np.abs(y_ref) + 1e-3 * np.linalg.norm(x64, axis=1)[:, None] * oracle.row_amax(lw.w)[None, :]
-        yv = y.double().cpu().numpy()
-        ok &= bool(np.all(np.isfinite(yv)) and np.all(np.abs(yv - y_ref) <= tol))
-    return ok
-
-
 def main():
     global SPIN_MS
     ap = argparse.ArgumentParser()
@@ -329,16 +430,24 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--only-timed", action="store_true",
                     help="run only the timed region (for profiler runs: every GEMV launch is then a timed one)")
+    ap.add_argument("--only", choices=SECTIONS, nargs="+",
+                    help="run only these extra sections (no decode workload) and print their JSON")
+    ap.add_argument("--reps", type=int, default=100, help="launches per burst in the extra sections")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="print a markdown table of the library's kernels in a rocprofv3 kernel trace, then exit")
     ap.add_argument("--last", type=int, default=None,
                     help="with --trace-summary: only the last N library dispatches")
+    ap.add_argument("--mfma-summary", nargs=3, metavar=("PMC_CSV", "N", "K"),
+                    help="print a markdown table of the skinny kernels' matrix-core counters, then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/gemv_decode_traffic.json from two rocprofv3 --pmc runs, then exit")
     args = ap.parse_args()
     SPIN_MS = args.spin_ms
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_FILE)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary[0], int(args.mfma_summary[1]), int(args.mfma_summary[2]))
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.last)
@@ -358,6 +467,12 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name} CUs={props.multi_processor_count} mem={props.total_memory / 2**30:.0f} GiB")
 
+    if args.only:
+        out = extra_sections(dev, stream, args.reps, args.only)
+        calibration_copy(dev)
+        print(json.dumps(out), flush=True)
+        return
+
     # ---------------------------------------------------------------- decode workload (the metric)
     per_step = sum(alg_bytes(1, n, k) for n, k in workloads.DECODE_SHAPES)
     copies = max(1, math.ceil(ROTATE_BYTES / per_step))
@@ -370,13 +485,6 @@ def main():
     quant = [{"layer": L.name, "ms": round(L.quantize_ms, 4),
               "gbps": round(5.0 * L.n * L.k / (L.quantize_ms * 1e-3) / 1e9, 1)} for L in layers]
 
-    try:
-        parity = parity_check(layers, lws, xs_cpu, xs)
-    except ImportError as e:
-        log(f"parity check skipped: {e}")
-        parity = None
-    log(f"parity vs oracle: {parity}")
-
     if args.only_timed:
         ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
         launches = args.steps * len(calls)
@@ -388,11 +496,12 @@ def main():
 
     per_call = []
     for c in calls:
-        us = burst_us(c, 200, 20, stream)
+        us = burst(c, 200, 20, stream)
         per_call.append(call_report(c, us))
         r = per_call[-1]
         log(f"  {r['layer']}: {r['us_per_call']:.2f} us/call  {r['gbps']:.0f} GB/s ({r['pct_peak']:.1f}% of 8 TB/s)")
-    warm = [call_report(c, burst_us(c, 200, 20, stream, warm=True)) for c in calls]
+    warm = [call_report(c, burst(c, 200, 20, stream, warm=True)) for c in calls]
+    host = [dict(layer=c.layer.name, **host_latency(c, stream)) for c in calls]
     ceiling = read_ceiling(dev, [c.layer.n * c.layer.k for c in calls])
 
     ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
@@ -424,9 +533,9 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_entry(),
                      "kernel": "gemv_kernel (M=1 GEMV, every launch of the step)",
                      "alg_bytes_per_launch": per_step / len(calls), "mean_launch_us": round(mean_launch_us, 3)},
-        "parity": parity,
         "per_call": per_call,
         "warm_per_call": warm,
+        "host_latency": host,
         "graph": None if graph_ms is None else {
             "steps": graph_steps, "us_per_step": round(graph_ms * 1e3 / graph_steps, 3),
             "gbps": round(per_step * graph_steps / (graph_ms * 1e-3) / 1e9, 1)},
@@ -435,11 +544,14 @@ def main():
     }
 
     if not args.quick:
-        out["extra"] = extra_sections(dev, stream)
+        out["extra"] = extra_sections(dev, stream, args.reps)
 
-    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(lws, xs_cpu, args.cpu_budget)
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(layers, lws, xs_cpu, calls,
+                                                                          args.cpu_budget)
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: {out['cpu_baseline']['value']} GB/s on {out['cpu_baseline']['cores']} threads")
+        cb = out["cpu_baseline"]
+        log(f"cpu baseline: {cb['value']} GB/s on {cb['cores']} threads, {cb['one_core']['value']} GB/s on one; "
+            f"GPU results vs this oracle run: {'pass' if cb['gpu_parity_vs_this_oracle_run'] else 'FAIL'}")
 
     calibration_copy(dev)
     print(json.dumps(out), flush=True)
@@ -491,77 +603,180 @@ def pmc_summary(fetch_csv, write_csv, out_path):
     print(json.dumps(out, indent=1))
 
 
+def _short_kernel_name(full):
+    """'pipe_kernel<XR=16,CT=4,KP=1,NS=4>'-style name from a demangled trace name."""
+    import re
+    full = full.replace("(anonymous namespace)::", "").replace("fp8w::", "")
+    m = re.search(r"(\w+_kernel)(<[^()]*>)?\(", full)
+    if not m:
+        return full[:60]
+    name, targs = m.group(1), (m.group(2) or "")
+    args = [a.strip() for a in targs[1:-1].split(",")] if targs else []
+    keys = {"pipe_kernel": ("XR", "CT", "KP", "NS"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
+            "gemv_kernel": ("R", "U", "NT"), "wpipe_kernel": ("XR", "CT", "NS")}.get(name)
+    if keys and len(args) == len(keys) + 1:  # first argument is the activation type
+        return f"{name}<" + ",".join(f"{kk}={v}" for kk, v in zip(keys, args[1:])) + ">"
+    return name + targs
+
+
 def trace_summary(csv_path, last=None):
     """Markdown table of the library's kernels in a rocprofv3 --kernel-trace CSV:
     one row per kernel instance and grid (the grid identifies the shape), with
     launch count and duration statistics in microseconds. `last` keeps only the
     last `last` library dispatches (the timed region of bench.py --only-timed)."""
     import csv
-    import re
     rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Dispatch_Id"]))
     ours = [r for r in rows if "fp8w::" in r["Kernel_Name"]]
     if last:
         ours = ours[-last:]
     groups = {}
     for r in ours:
-        m = re.search(r"(\w+_kernel)(<[^()]*>)?\(", r["Kernel_Name"].replace("(anonymous namespace)::", ""))
-        name = (m.group(1) + (m.group(2) or "")).replace("fp8w::", "") if m else r["Kernel_Name"][:60]
+        name = _short_kernel_name(r["Kernel_Name"])
         wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
         key = (name, wgs, int(r["Workgroup_Size_X"]))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
-    lines = ["| Kernel | Workgroups x threads | Launches | Mean (us) | Median (us) | Min (us) |",
-             "|---|---|---|---|---|---|"]
+    lines = ["| Kernel | Workgroups x threads | Launches | Mean (us) | p10 (us) | Median (us) | p90 (us) | Min (us) |",
+             "|---|---|---|---|---|---|---|---|"]
     for (name, wgs, wg), d in groups.items():
         d = np.array(d)
-        lines.append(f"| `{name}` | {wgs} x {wg} | {len(d)} | {d.mean():.3f} | {np.median(d):.3f} | {d.min():.3f} |")
+        lines.append(f"| `{name}` | {wgs} x {wg} | {len(d)} | {d.mean():.3f} | {np.percentile(d, 10):.3f} | "
+                     f"{np.median(d):.3f} | {np.percentile(d, 90):.3f} | {d.min():.3f} |")
     print("\n".join(lines))
 
 
-def extra_sections(dev, stream, reps=100):
+def mfma_summary(csv_path, n, k):
+    """Markdown table from a rocprofv3 --pmc run with the derived counters
+    MfmaFlopsF16, MfmaFlopsBF16 and MfmaUtil over the skinny kernels of an
+    [n, k] weight: matrix-core FLOPs each launch issued (counted) next to the
+    tile formula's figure, and the share of the run's SIMD cycles the matrix
+    cores were busy."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if not any(t in r["Kernel_Name"] for t in ("pipe_kernel", "seg_kernel")):
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": _short_kernel_name(r["Kernel_Name"]),
+                                                   "wgs": int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])),
+                                                   "wg": int(r["Workgroup_Size"]), "vgpr": r["VGPR_Count"],
+                                                   "lds": r["LDS_Block_Size"]})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    groups = {}
+    for d in per.values():
+        groups.setdefault((d["name"], d["wgs"], d["wg"], d["vgpr"], d["lds"]), []).append(d)
+    lines = ["| Kernel | Workgroups x threads | VGPRs | LDS (B) | Launches | Issued GFLOP / launch (counted) | "
+             "Issued GFLOP (tile formula) | Padded M | MFMA busy (% of SIMD cycles) |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for (name, wgs, wg, vgpr, lds), ds in groups.items():
+        fl = np.mean([d.get("MfmaFlopsF16", 0.0) + d.get("MfmaFlopsBF16", 0.0) for d in ds]) / 1e9
+        util = np.mean([d.get("MfmaUtil", float("nan")) for d in ds])
+        issued, mpad = mfma_issued_flops(name, 0, n, k)
+        exp = f"{issued / 1e9:.3f}" if issued else "-"
+        lines.append(f"| `{name}` | {wgs} x {wg} | {vgpr} | {lds} | {len(ds)} | {fl:.3f} | {exp} | {mpad or '-'} | "
+                     f"{util:.2f} |")
+    print("\n".join(lines))
+
+
+SECTIONS = ("tiny", "skinny", "block", "large")
+
+
+def extra_sections(dev, stream, reps=100, only=None):
     ex = {}
-    # skinny sweep, fp16 activations
-    per = alg_bytes(32, 14336, 4096)
-    L = Layer(workloads.skinny_layer(), max(1, math.ceil(ROTATE_BYTES / per)), dev)
-    sk = []
-    for m in workloads.SKINNY_MS:
-        c = Call(L, workloads.skinny_x(m).to(dev), dev)
-        sk.append(call_report(c, burst_us(c, reps, 10, stream)))
-        log(f"  skinny m={m}: {sk[-1]['us_per_call']:.2f} us {sk[-1]['pct_peak']:.1f}% of peak [{sk[-1]['kernel']}]")
-    ex["skinny_sweep"] = sk
-    ex["skinny_quantize_ms"] = round(L.quantize_ms, 3)
-    del L
-    torch.cuda.empty_cache()
+    want = set(only or SECTIONS)
 
-    # one decoder block at M = 16: seven calls per step, per-call bursts and graph-timed steps
-    blk_bytes = sum(alg_bytes(16, n, k, False) for _, n, k in workloads.DECODER_BLOCK)
-    copies = max(1, math.ceil(ROTATE_BYTES / blk_bytes))
-    Ls = [Layer(workloads.block_layer(i), copies, dev) for i in range(len(workloads.DECODER_BLOCK))]
-    calls = [Call(Li, workloads.block_x(i).to(dev), dev) for i, Li in enumerate(Ls)]
-    blk = [call_report(c, burst_us(c, reps, 10, stream)) for c in calls]
-    ms = timed_steps(calls, 200, 10, copies, False, dev)
-    ex["decoder_block"] = {"calls": blk, "us_sum_of_calls": round(sum(b["us_per_call"] for b in blk), 2),
-                           "step_us": round(ms * 1e3 / 200, 2), "step_mode": "eager",
-                           "step_gbps": round(blk_bytes / (ms * 1e-3 / 200) / 1e9, 1), "bytes": blk_bytes}
-    log(f"  decoder block m=16: {ex['decoder_block']['step_us']:.1f} us/step (eager), "
-        f"{ex['decoder_block']['step_gbps']:.0f} GB/s")
-    del Ls, calls
-    torch.cuda.empty_cache()
+    if "tiny" in want:
+        # latency-bound calls: the 1024x1024 GEMV and the pages' example shape
+        # ([22,1024] x [1024,4096]), cold (rotated) and warm, plus host wall time
+        tiny = []
+        for case in (workloads.tiny_gemv(), workloads.pages_example()):
+            n, k = case.layer.w.shape
+            per = alg_bytes(case.x.shape[0], n, k, case.layer.bias is not None)
+            L = Layer(case.layer, max(1, math.ceil(ROTATE_BYTES / per)), dev)
+            c = Call(L, case.x.to(dev), dev)
+            r = call_report(c, burst(c, 400, 20, stream))
+            r["warm"] = call_report(c, burst(c, 400, 20, stream, warm=True))
+            r["host"] = host_latency(c, stream)
+            tiny.append(r)
+            log(f"  {r['layer']} m={r['m']}: {r['us_per_call']:.2f} us cold, {r['warm']['us_per_call']:.2f} us warm, "
+                f"{r['host']['call_and_sync_us']:.1f} us call+sync [{r['kernel']}]")
+            del L, c
+            torch.cuda.empty_cache()
+        ex["tiny"] = tiny
 
-    # large shapes and the k = 8200 fallback
-    lg = []
-    for shape in workloads.LARGE_SHAPES + [workloads.LARGE_FALLBACK_SHAPE]:
-        per = alg_bytes(32, *shape, False)
-        L = Layer(workloads.large_layer(shape), max(1, math.ceil(ROTATE_BYTES / per)), dev)
-        for m in workloads.LARGE_MS:
-            x = workloads.large_x(shape, m).to(dev)
-            c = Call(L, x, dev)
-            lg.append(call_report(c, burst_us(c, max(20, reps // 2), 5, stream)))
-            log(f"  large {shape} m={m} [{lg[-1]['kernel']}]: {lg[-1]['us_per_call']:.2f} us "
-                f"{lg[-1]['pct_peak']:.1f}% of peak")
-        lg.append({"layer": L.name, "quantize_ms": round(L.quantize_ms, 3)})
+    if "skinny" in want:
+        # skinny sweep, fp16 activations
+        per = alg_bytes(32, 14336, 4096)
+        L = Layer(workloads.skinny_layer(), max(1, math.ceil(ROTATE_BYTES / per)), dev)
+        sk = []
+        for m in workloads.SKINNY_MS:
+            c = Call(L, workloads.skinny_x(m).to(dev), dev)
+            sk.append(call_report(c, burst(c, reps, 10, stream)))
+            r = sk[-1]
+            log(f"  skinny m={m}: {r['us_per_call']:.2f} us {r['pct_peak']:.1f}% of peak, MFMA useful "
+                f"{r['mfma']['useful_pct_of_peak']:.2f}% / issued {r['mfma']['issued_pct_of_peak']:.2f}% "
+                f"[{r['kernel']}]")
+        ex["skinny_sweep"] = sk
+        ex["skinny_quantize_ms"] = round(L.quantize_ms, 3)
         del L
         torch.cuda.empty_cache()
-    ex["large"] = lg
+
+    if "block" in want:
+        # one decoder block at M = 16: seven calls per step, per-call bursts, eager
+        # and graph-replayed steps; then the same block with q/k/v and gate/up
+        # merged into one call each (their weights concatenated along n before
+        # quantization: per-row scales make the codes identical), four calls
+        blk_bytes = sum(alg_bytes(16, n, k, False) for _, n, k in workloads.DECODER_BLOCK)
+        copies = max(1, math.ceil(ROTATE_BYTES / blk_bytes))
+        lws = [workloads.block_layer(i) for i in range(len(workloads.DECODER_BLOCK))]
+        Ls = [Layer(lw, copies, dev) for lw in lws]
+        calls = [Call(Li, workloads.block_x(i).to(dev), dev) for i, Li in enumerate(Ls)]
+        blk = [call_report(c, burst(c, reps, 10, stream)) for c in calls]
+        ms = timed_steps(calls, 200, 10, copies, False, dev)
+        gms = timed_steps(calls, 200, 10, copies, True, dev)
+        ex["decoder_block"] = {"calls": blk, "us_sum_of_calls": round(sum(b["us_per_call"] for b in blk), 2),
+                               "step_us": round(ms * 1e3 / 200, 2), "step_mode": "eager",
+                               "step_gbps": round(blk_bytes / (ms * 1e-3 / 200) / 1e9, 1),
+                               "graph_step_us": round(gms * 1e3 / 200, 2), "bytes": blk_bytes}
+        log(f"  decoder block m=16: {ex['decoder_block']['step_us']:.1f} us/step (eager), "
+            f"{ex['decoder_block']['graph_step_us']:.1f} (graph), {ex['decoder_block']['step_gbps']:.0f} GB/s")
+        del Ls, calls
+        torch.cuda.empty_cache()
+
+        groups = workloads.MERGED_BLOCK
+        mlws = [workloads.Linear("+".join(lws[i].name for i in g), np.concatenate([lws[i].w for i in g]), None)
+                for g in groups]
+        mbytes = sum(alg_bytes(16, lw.w.shape[0], lw.w.shape[1], False) for lw in mlws)
+        Ms = [Layer(lw, copies, dev) for lw in mlws]
+        mcalls = [Call(Mi, workloads.block_x(g[0]).to(dev), dev) for Mi, g in zip(Ms, groups)]
+        mblk = [call_report(c, burst(c, reps, 10, stream)) for c in mcalls]
+        ms = timed_steps(mcalls, 200, 10, copies, False, dev)
+        gms = timed_steps(mcalls, 200, 10, copies, True, dev)
+        ex["decoder_block_merged"] = {
+            "calls": mblk, "us_sum_of_calls": round(sum(b["us_per_call"] for b in mblk), 2),
+            "step_us": round(ms * 1e3 / 200, 2), "step_mode": "eager",
+            "step_gbps": round(mbytes / (ms * 1e-3 / 200) / 1e9, 1), "graph_step_us": round(gms * 1e3 / 200, 2),
+            "bytes": mbytes}
+        log(f"  decoder block m=16, merged q/k/v and gate/up: {ex['decoder_block_merged']['step_us']:.1f} us/step "
+            f"(eager), {ex['decoder_block_merged']['graph_step_us']:.1f} (graph), "
+            f"{ex['decoder_block_merged']['step_gbps']:.0f} GB/s")
+        del Ms, mcalls
+        torch.cuda.empty_cache()
+
+    if "large" in want:
+        # large shapes and the k = 8200 fallback
+        lg = []
+        for shape in workloads.LARGE_SHAPES + [workloads.LARGE_FALLBACK_SHAPE]:
+            per = alg_bytes(32, *shape, False)
+            L = Layer(workloads.large_layer(shape), max(1, math.ceil(ROTATE_BYTES / per)), dev)
+            for m in workloads.LARGE_MS:
+                x = workloads.large_x(shape, m).to(dev)
+                c = Call(L, x, dev)
+                lg.append(call_report(c, burst(c, max(20, reps // 2), 5, stream)))
+                log(f"  large {shape} m={m} [{lg[-1]['kernel']}]: {lg[-1]['us_per_call']:.2f} us "
+                    f"{lg[-1]['pct_peak']:.1f}% of peak")
+            lg.append({"layer": L.name, "quantize_ms": round(L.quantize_ms, 3)})
+            del L
+            torch.cuda.empty_cache()
+        ex["large"] = lg
     return ex
 
 

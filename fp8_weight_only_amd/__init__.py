@@ -261,12 +261,29 @@ class QuantizedLinear:
 
     def __init__(self, q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor = None):
         self.q, self.scale, self.bias = q, scale, bias
+        self.split_sizes = [int(q.shape[0])]
         self._ws = None
 
     @classmethod
     def build(cls, weight: torch.Tensor, bias: torch.Tensor = None) -> "QuantizedLinear":
         q, scale = quantize(weight)
         return cls(q, scale, bias)
+
+    @classmethod
+    def build_merged(cls, weights, biases=None) -> "QuantizedLinear":
+        """One layer for several that read the same input (q/k/v, gate/up): the
+        weights are stacked along the output dimension and quantised once. The
+        scales are per output row, so each row's codes and scale are exactly
+        those of its own layer; the output's columns are the layers' outputs
+        side by side (``split_sizes`` gives their widths). Biases: all or none."""
+        weights = list(weights)
+        if biases is not None and any(b is None for b in biases):
+            raise ValueError("build_merged: give a bias for every layer or for none")
+        w = torch.cat([wi.reshape(wi.shape[0], -1) for wi in weights], dim=0)
+        b = None if biases is None else torch.cat(list(biases))
+        layer = cls.build(w, b)
+        layer.split_sizes = [int(wi.shape[0]) for wi in weights]
+        return layer
 
     @property
     def out_features(self) -> int:

@@ -424,12 +424,16 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
 // pipe_kernel: a workgroup owns 16 * CT channels, so CT is the largest that
 // still gives about one workgroup per CU (224-448 workgroups on the decode and
 // sweep layers), KP > 1 adds waves on narrower layers, and NS is the deepest
-// ring whose LDS lets every workgroup be resident at once. Layers of 8192
-// channels with long k split k over two workgroup rows when the batch is
-// above 16 (fp32 partial sums in the caller's workspace, one more kernel to
-// reduce them); without workspace they take the single-pass plan. seg_kernel
-// covers small batches on narrow layers, where it measured faster, and the
-// shapes the ring cannot tile.
+// ring whose LDS lets every workgroup be resident at once. Every workgroup
+// streams all XR activation rows of its k range, so on narrow layers above 16
+// tokens the activations outweigh the codes; there k is split over workgroup
+// rows instead (four on layers of 4096-8191 channels, two on 8192-channel
+// layers), each with 64 channels, and a second kernel reduces the fp32
+// partial sums from the caller's workspace. Measured on MI355X this pays only
+// above 16 tokens, where it cut [4096 x 14336] at 32 tokens from 28.8 to
+// 19.7 us; without workspace these shapes take the single-pass plan.
+// seg_kernel covers small batches on narrow layers, where it measured
+// faster, and the shapes the ring cannot tile.
 struct SkinnyPlan {
     bool pipe;
     int xr, ct, kp, ns, splits;  // pipe_kernel
@@ -456,6 +460,9 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
             } else {
                 ct = 2;
             }
+        } else if (m > 16 && n >= 4096 && allow_split && k % (4 * 512) == 0) {
+            ct = 4;
+            splits = 4;
         } else if (m > 8) {
             ct = 1;
             kp = 2;

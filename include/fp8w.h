@@ -102,9 +102,10 @@ FP8W_API fp8w_status_t fp8w_quantize(const void* w, fp8w_dtype_t w_dtype, int64_
  *   workspace device scratch of fp8w_linear_workspace_bytes(...) bytes (NULL / 0
  *             when that is 0); it must not overlap anything else. The fallback
  *             path needs it (2-byte aligned, FP8W_ERR_WORKSPACE when missing or
- *             short). A few skinny shapes (8192-channel layers, m > 16) use it
- *             for fp32 partial sums of a k split (16-byte aligned); given less,
- *             they take a slower single-pass plan instead, with no error.
+ *             short). Some skinny shapes (m > 16 on layers of 4096 to 8192
+ *             channels) use it for fp32 partial sums of a k split (16-byte
+ *             aligned); given less, they take a slower single-pass plan
+ *             instead, with no error.
  * Dispatch (fp8w_linear_path): the fast kernels take 1 <= m <= 32 with
  * k % 256 == 0 and x, q 16-byte aligned (m == 1: GEMV, else skinny MFMA);
  * everything else takes the fallback. Results of different paths and plans

@@ -83,6 +83,12 @@ def test_kernel_names():
     assert kn(A, 8, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=8,CT=2,KP=2,NS=4>"
     assert kn(A, 16, 8192, 3072, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"       # k % 2048 != 0
     assert kn(A, 16, 4096, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"
+    assert kn(A, 16, 4096, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"
+    assert kn(A, 32, 4096, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"
+    assert kn(A, 22, 4096, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"
+    assert kn(A, 17, 6000, 2048, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"
+    assert kn(A, 32, 2048, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=1,KP=2,NS=4>"      # n < 4096
+    assert kn(A, 32, 4096, 4608, fw.BF16, X, Q) == "seg_kernel<SEG=1,T=2,W=4,U=1,MT=2>"     # k % 2048 != 0
     assert kn(A, 3, 14336, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=4>"
     assert kn(A, 8, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=2,T=2,W=8,U=2,MT=1>"
     assert kn(A, 4, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"
@@ -112,6 +118,8 @@ def test_workspace_bytes():
     assert wb(32, 8192, 28672, fw.BF16, X, Q, Y) == 2 * 32 * 8192 * 4     # split k
     assert wb(17, 11000, 4096, fw.FP16, X, Q, Y) == 2 * 17 * 11000 * 4
     assert wb(16, 8192, 28672, fw.BF16, X, Q, Y) == 0
+    assert wb(32, 4096, 14336, fw.BF16, X, Q, Y) == 4 * 32 * 4096 * 4    # split k in four
+    assert wb(16, 4096, 14336, fw.BF16, X, Q, Y) == 0
     assert wb(32, 8192, 1024, fw.BF16, X, Q, Y) == 0                      # k % 2048 != 0
 
 

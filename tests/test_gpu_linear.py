@@ -97,6 +97,9 @@ PIPE = [
     (10, 8300, 1024, torch.bfloat16, "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"),
     (20, 8200, 2048, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
     (32, 8192, 4096, torch.float16, "pipe_kernel<XR=32,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
+    (17, 4100, 2048, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    (24, 5000, 4096, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"),
+    (32, 4096, 6144, torch.bfloat16, "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
 ]
 
 
@@ -109,14 +112,14 @@ def test_pipe_kernel_parity(m, n, k, dtype, kernel):
     _check(case, expect_path=fw.PATH_SKINNY)
 
 
+@pytest.mark.parametrize("m,n,k,splits", [(24, 8256, 4096, 2), (20, 4160, 8192, 4)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_split_k_matches_single_pass(dtype):
-    """A shape that splits k when given workspace: with it (two workgroup rows of
+def test_split_k_matches_single_pass(m, n, k, splits, dtype):
+    """A shape that splits k when given workspace: with it (workgroup rows of
     fp32 partial sums, then the reduce kernel) and without it (single pass) both
     pass the gate, and agree to fp32 summation-order rounding."""
-    m, n, k = 24, 8256, 4096
     act = fw.BF16 if dtype == torch.bfloat16 else fw.FP16
-    assert fw.fp8w_linear_workspace_bytes(m, n, k, act, 0, 0, 0) == 2 * m * n * 4
+    assert fw.fp8w_linear_workspace_bytes(m, n, k, act, 0, 0, 0) == splits * m * n * 4
     case = workloads.random_case(4242, m, n, k, dtype, with_bias=True)
     q, s, x, b = _prepare(case)
     q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
@@ -131,7 +134,7 @@ def test_split_k_matches_single_pass(dtype):
     assert np.allclose(outs[0], outs[1], rtol=2e-2, atol=1e-2)
     # a second call reuses the workspace contents without clearing: same bits
     y2 = nan_like((m, n), dtype, DEV)
-    ws = torch.full((2 * m * n * 4,), 0x7F, dtype=torch.uint8, device=DEV)
+    ws = torch.full((splits * m * n * 4,), 0x7F, dtype=torch.uint8, device=DEV)
     fw.linear(x, q, s, b, out=y2, workspace=ws)
     fw.linear(x, q, s, b, out=y2, workspace=ws)
     torch.cuda.synchronize()

@@ -7,7 +7,18 @@ Workloads (seeded, see workloads.py): tiny GEMV 1024x1024; decode GEMV M=1 at
 weights, fp16) at M = 2..32; one decoder block's seven linears at M=16 with
 outlier and zero rows; large 28672x8192 / 8192x28672 / 28672x8200 (fallback)
 at M = 1, 4, 8, 32 with outlier activations.
+
+Each test also records the error report the method asks for ("FP8 weight-only
+(precision: fp8_weights)", section "The contract": the weight's rel_l2,
+worst-channel rel_l2, underflow fraction and crest, and per call the minimum
+cosine and maximum relative l2 of the outputs), both against the oracle
+(parity) and against x W^T + b with the original fp32 weight (what the
+quantization costs). With FP8W_QUALITY_REPORT set to a file path, the module
+writes the report there as JSON when it finishes.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,6 +30,44 @@ from parity_util import assert_gate, assert_same_bits, gate_sampled, nan_like
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
+REPORT = {}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def quality_report():
+    yield
+    path = os.environ.get("FP8W_QUALITY_REPORT")
+    if path and REPORT:
+        with open(path, "w") as f:
+            json.dump(REPORT, f, indent=1)
+
+
+def _weight_report(layer, q_ref, s_ref):
+    rep = oracle.weight_error(layer.w, q_ref, s_ref)
+    rep.pop("channel_rel_l2")
+    REPORT.setdefault(layer.name, {})["weight"] = rep
+    return rep
+
+
+def _exact_product(x64, w, b64):
+    """x W^T (+ b) in fp64 with the original fp32 weight, in row blocks."""
+    out = np.empty((x64.shape[0], w.shape[0]), dtype=np.float64)
+    for r0 in range(0, w.shape[0], 4096):
+        out[:, r0:r0 + 4096] = x64 @ w[r0:r0 + 4096].astype(np.float64).T
+    return out if b64 is None else out + b64[None, :]
+
+
+def _call_report(layer, m, yv, y_ref, x64, amax):
+    b64 = None if layer.bias is None else layer.bias.double().numpy()
+    rec = {"vs_fp32_weight": oracle.output_metrics(yv, _exact_product(x64, layer.w, b64))}
+    if y_ref is not None:
+        tol = 1e-2 * np.abs(y_ref) + 1e-3 * np.linalg.norm(x64, axis=1)[:, None] * amax[None, :]
+        rec["vs_oracle"] = oracle.output_metrics(yv, y_ref)
+        err = np.abs(yv - y_ref)
+        with np.errstate(divide="ignore", invalid="ignore"):  # tol == 0 (a zero row, no bias): err must be 0
+            use = np.where(tol > 0, err / tol, np.where(err == 0, 0.0, np.inf))
+        rec["vs_oracle"]["max_error_over_gate"] = float(use.max())
+    REPORT.setdefault(layer.name, {}).setdefault("calls", {})[f"m={m}"] = rec
 
 
 def _quantize_checked(layer):
@@ -45,6 +94,7 @@ def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path, full=True):
     if full:
         y_ref = oracle.linear_f64(x64, q_ref, s_ref, b64)
         assert_gate(yv, y_ref, x64, amax, f"{layer.name} m={m}")
+        _call_report(layer, m, yv, y_ref, x64, amax)
         return yv, y_ref
     # sampled: every row, 4096 seeded channels (including the first and last)
     g = np.random.default_rng(m * 7 + n)
@@ -55,6 +105,7 @@ def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path, full=True):
     ok = gate_sampled(yv[rows, cc], y_ref, np.linalg.norm(x64, axis=1)[rows], amax[cc])
     assert ok.all(), f"{layer.name} m={m}: {np.count_nonzero(~ok)} sampled outputs outside the gate"
     assert np.all(np.isfinite(yv)), f"{layer.name} m={m}: non-finite outputs"
+    _call_report(layer, m, yv, None, x64, amax)
     return yv, None
 
 
@@ -64,7 +115,7 @@ def test_tiny_gemv():
     q, s, q_ref, s_ref = _quantize_checked(case.layer)
     amax = oracle.row_amax(case.layer.w)
     yv, y_ref = _linear_checked(case.layer, q, s, q_ref, s_ref, case.x, amax, fw.PATH_GEMV)
-    rep = oracle.weight_error(case.layer.w, q_ref, s_ref)
+    rep = _weight_report(case.layer, q_ref, s_ref)
     print(f"  rel_l2={rep['rel_l2']:.4f} worst={rep['worst_channel_rel_l2']:.4f} "
           f"underflow={rep['underflow']:.2e} {oracle.output_metrics(yv, y_ref)}", flush=True)
 
@@ -75,6 +126,7 @@ def test_decode_gemv(i):
     print(f"decode {lay.name}", flush=True)
     q, s, q_ref, s_ref = _quantize_checked(lay)
     amax = oracle.row_amax(lay.w)
+    _weight_report(lay, q_ref, s_ref)
     _linear_checked(lay, q, s, q_ref, s_ref, workloads.decode_x(i), amax, fw.PATH_GEMV)
 
 
@@ -83,7 +135,7 @@ def test_skinny_sweep():
     print(f"skinny {lay.name}", flush=True)
     q, s, q_ref, s_ref = _quantize_checked(lay)
     amax = oracle.row_amax(lay.w)
-    rep = oracle.weight_error(lay.w, q_ref, s_ref)
+    rep = _weight_report(lay, q_ref, s_ref)
     print(f"  student-t weights: rel_l2={rep['rel_l2']:.4f} worst={rep['worst_channel_rel_l2']:.4f} "
           f"underflow={rep['underflow']:.2e} crest_max={rep['crest_max']:.1f}", flush=True)
     for m in workloads.SKINNY_MS:
@@ -97,6 +149,7 @@ def test_decoder_block():
         print(f"block {name} [{n},{k}]", flush=True)
         q, s, q_ref, s_ref = _quantize_checked(lay)
         amax = oracle.row_amax(lay.w)
+        _weight_report(lay, q_ref, s_ref)
         yv, _ = _linear_checked(lay, q, s, q_ref, s_ref, workloads.block_x(i), amax, fw.PATH_SKINNY)
         zero = s_ref == 0
         assert zero.sum() == int(round(0.005 * n))
@@ -109,6 +162,7 @@ def test_large(shape):
     print(f"large {lay.name}", flush=True)
     q, s, q_ref, s_ref = _quantize_checked(lay)
     amax = oracle.row_amax(lay.w)
+    _weight_report(lay, q_ref, s_ref)
     for m in workloads.LARGE_MS:
         print(f"  m={m}", flush=True)
         if shape == workloads.LARGE_FALLBACK_SHAPE:

@@ -26,6 +26,12 @@ quantization; activations are [M, K]):
 5. large sweep: W [28672,8192], [8192,28672] and [28672,8200] ~ N(0, 0.015^2);
    x [M,K] bf16 ~ N(0,1) with 0.1 % of entries (seeded) multiplied by 20;
    no bias; M in 1,4,8,32.
+
+Context shape (workload id 6): the one timing of this method the pages print is
+for x [22,1024] times a [1024,4096] weight ("FP8 weight-only (precision:
+fp8_weights)", the Triton variant in "Dequantise in registers"); it is drawn
+like the decode workload: W [4096,1024] ~ N(0, 0.02^2), x [22,1024] bf16 ~
+N(0,1), no bias.
 """
 from dataclasses import dataclass
 from typing import List, Optional
@@ -43,6 +49,10 @@ SKINNY_MS = [2, 4, 8, 16, 22, 32]
 LARGE_SHAPES = [(28672, 8192), (8192, 28672)]
 LARGE_FALLBACK_SHAPE = (28672, 8200)
 LARGE_MS = [1, 4, 8, 32]
+PAGES_EXAMPLE = (22, 4096, 1024)  # m, n, k
+# the decoder block with the layers that share an input merged into one call:
+# q/k/v, o, gate/up, down (indices into DECODER_BLOCK)
+MERGED_BLOCK = [(0, 1, 2), (3,), (4, 5), (6,)]
 
 
 def rng(workload: int, tensor: int, sub: int = 0) -> np.random.Generator:
@@ -144,6 +154,12 @@ def large_x(shape, m: int) -> torch.Tensor:
     n, k = shape
     sub = {(28672, 8192): 0, (8192, 28672): 1, (28672, 8200): 2}[(n, k)]
     return activations(5, 100 * sub + m, m, k, torch.bfloat16, outlier_frac=0.001)
+
+
+def pages_example():
+    m, n, k = PAGES_EXAMPLE
+    return Case(Linear(f"example_{n}x{k}", weight_normal(6, 0, n, k, 0.02), None),
+                activations(6, 0, m, k, torch.bfloat16))
 
 
 # ------------------------------------------------------------------ small parity cases
