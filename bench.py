@@ -348,7 +348,7 @@ def cpu_info():
     return os.cpu_count(), model
 
 
-def cpu_baseline(layers, lws, xs_cpu, calls, budget_s):
+def cpu_baseline(layers, lws, xs_cpu, calls, budget_s, with_configs=True):
     """The oracle (fp64 C, OpenMP over output channels) on the host cores, on the
     same three decode calls, repeated until ~budget_s of CPU work; then once more
     on one core. The oracle's results of this leg are also compared with the
@@ -394,6 +394,7 @@ def cpu_baseline(layers, lws, xs_cpu, calls, budget_s):
         tol = 1e-2 * np.abs(y_ref) + 1e-3 * np.linalg.norm(x64, axis=1)[:, None] * amax[None, :]
         ok &= bool(np.all(np.isfinite(yv)) and np.all(np.abs(yv - y_ref) <= tol))
 
+    per_config = oracle_per_config() if with_configs else None
     nproc, model = cpu_info()
     return {"value": round(byts / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} passes over the 3 decode GEMV calls (M=1; 4096x4096, 14336x4096, 4096x14336) "
@@ -401,7 +402,66 @@ def cpu_baseline(layers, lws, xs_cpu, calls, budget_s):
             "one_core": {"value": round(byts1 / el1 / 1e9, 3), "unit": "GB/s", "cores": 1,
                          "sample": f"{reps1} passes, {el1:.1f} s"},
             "gpu_parity_vs_this_oracle_run": ok,
+            "per_workload": per_config,
             "host_cpus": nproc, "host_model": model}
+
+
+def oracle_per_config():
+    """The oracle's quantizer and fp64 linear timed on every workload (part of the
+    cpu_baseline leg): median wall time of `reps` runs on all host threads, and
+    for the smaller workloads again on one thread. GB/s use the same algorithmic
+    bytes as the GPU lines (the quantizer: 4 B read + 1 B written per weight)."""
+    import oracle
+    threads = oracle.num_threads()
+
+    def med(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    def one(name, lw, xs, reps, one_core):
+        n, k = lw.w.shape
+        q, s, _ = oracle.quantize_rows(lw.w)
+        b = None if lw.bias is None else lw.bias.double().numpy()
+        r = {"workload": name, "n": n, "k": k, "runs": reps}
+        tq = med(lambda: oracle.quantize_rows(lw.w), reps)
+        r["quantize_us"] = round(tq * 1e6, 1)
+        r["quantize_gbps"] = round(5.0 * n * k / tq / 1e9, 3)
+        r["linear"] = []
+        for x in xs:
+            x64 = x.double().numpy()
+            m = x64.shape[0]
+            byts = alg_bytes(m, n, k, b is not None)
+            t = med(lambda: oracle.linear_f64(x64, q, s, b), reps)
+            e = {"m": m, "us": round(t * 1e6, 1), "gbps": round(byts / t / 1e9, 3)}
+            if one_core:
+                oracle.set_num_threads(1)
+                try:
+                    t1 = med(lambda: oracle.linear_f64(x64, q, s, b), 1)
+                finally:
+                    oracle.set_num_threads(threads)
+                e["one_core_us"] = round(t1 * 1e6, 1)
+                e["one_core_gbps"] = round(byts / t1 / 1e9, 3)
+            r["linear"].append(e)
+        return r
+
+    out = []
+    t0 = time.perf_counter()
+    case = workloads.tiny_gemv()
+    out.append(one("tiny", case.layer, [case.x], 10, True))
+    for i in range(3):
+        out.append(one("decode", workloads.decode_layer(i), [workloads.decode_x(i)], 3, True))
+    out.append(one("skinny", workloads.skinny_layer(), [workloads.skinny_x(2), workloads.skinny_x(32)], 3, True))
+    for i, (nm, _, _) in enumerate(workloads.DECODER_BLOCK):
+        out.append(one(f"block_{nm}", workloads.block_layer(i), [workloads.block_x(i)], 1, False))
+    shape = workloads.LARGE_SHAPES[0]
+    out.append(one("large", workloads.large_layer(shape), [workloads.large_x(shape, 1), workloads.large_x(shape, 32)],
+                   1, False))
+    log(f"  oracle per workload: {time.perf_counter() - t0:.1f} s")
+    return {"threads": threads, "configs": out}
 
 
 def traffic_entry():
@@ -428,6 +488,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="decode workload only (no extra sections)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-oracle-workloads", action="store_true",
+                    help="skip timing the oracle on every workload (part of the cpu_baseline leg)")
     ap.add_argument("--only-timed", action="store_true",
                     help="run only the timed region (for profiler runs: every GEMV launch is then a timed one)")
     ap.add_argument("--only", choices=SECTIONS, nargs="+",
@@ -547,7 +609,8 @@ def main():
         out["extra"] = extra_sections(dev, stream, args.reps)
 
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(layers, lws, xs_cpu, calls,
-                                                                          args.cpu_budget)
+                                                                          args.cpu_budget,
+                                                                          not args.no_oracle_workloads)
     if not args.no_cpu_baseline:
         cb = out["cpu_baseline"]
         log(f"cpu baseline: {cb['value']} GB/s on {cb['cores']} threads, {cb['one_core']['value']} GB/s on one; "
