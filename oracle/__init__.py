@@ -22,6 +22,12 @@ reporting. Sources, by page title and section:
 * "Skill: Write an FP8 Kernel", "Required reasoning process" step 2 (amax,
   scale = amax / fp8_max, cast of x / scale) and step 7 (~1 % relative error
   against a wide reference; scale = 0 handled without a division).
+* Group scales along k: "B04 - Precision & Quantization", sections
+  "Post-training quantization versus quantization-aware training" (one scale
+  per run of g = 32 / 64 / 128 weights of a row) and "The one that matters:
+  quantization is a quality decision" (per-channel -> per-group); the Day-98
+  lab page's storage census ("one scale per 32": the block's max |w| / 448).
+  Each group is quantized as the contract quantizes a row.
 
 Pinned by ``tests/test_oracle_*.py`` against the values and closed forms the
 pages fix (no function here is "parity unpinned").
@@ -66,6 +72,16 @@ def _lib():
         lib.o_dequantize_f64.argtypes = [P, P, I64, I64, P]
         lib.o_weight_error.restype = None
         lib.o_weight_error.argtypes = [P, P, P, I64, I64, P, P, P]
+        lib.o_quantize_groups.restype = ctypes.c_int
+        lib.o_quantize_groups.argtypes = [P, I64, I64, I64, P, P]
+        lib.o_linear_f64_groups.restype = None
+        lib.o_linear_f64_groups.argtypes = [P, I64, I64, P, P, I64, P, I64, P]
+        lib.o_linear_f64_groups_sampled.restype = None
+        lib.o_linear_f64_groups_sampled.argtypes = [P, I64, P, P, I64, P, P, P, I64, P]
+        lib.o_dequantize_groups_f64.restype = None
+        lib.o_dequantize_groups_f64.argtypes = [P, P, I64, I64, I64, P]
+        lib.o_weight_error_groups.restype = None
+        lib.o_weight_error_groups.argtypes = [P, P, P, I64, I64, I64, P, P, P]
         lib.o_num_threads.restype = ctypes.c_int
         lib.o_num_threads.argtypes = []
         lib.o_set_num_threads.restype = None
@@ -235,6 +251,81 @@ def output_metrics(y, y_ref) -> dict:
         rel = np.where(nr > 0, np.linalg.norm(y - y_ref, axis=1) / nr,
                        np.where(ny == 0, 0.0, np.inf))
     return {"min_cosine": float(cos.min()), "max_rel_l2": float(rel.max())}
+
+
+# ----------------------------------------------------------------- group scales along k
+def _check_group(k: int, g: int) -> None:
+    if g <= 0 or k % g != 0:
+        raise ValueError(f"group size {g} must divide k = {k}")
+
+
+def quantize_groups(w, g: int):
+    """One scale per run of g weights of a row: (q uint8 [n,k], scale fp32 [n, k/g], status)."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    _check_group(k, g)
+    q = np.empty((n, k), dtype=np.uint8)
+    scale = np.empty((n, k // g), dtype=np.float32)
+    st = _lib().o_quantize_groups(_p(w), n, k, g, _p(q), _p(scale))
+    return q, scale, int(st)
+
+
+def linear_f64_groups(x, q, scale, g: int, bias=None) -> np.ndarray:
+    """y[m,n] = sum_j scale[n,j] * sum_{i<g} x[m,jg+i] value(q[n,jg+i]) + bias[n], in fp64."""
+    x = _c(x, np.float64)
+    q = _c(q, np.uint8)
+    scale = _c(scale, np.float32)
+    m, k = x.shape
+    n = q.shape[0]
+    _check_group(k, g)
+    assert q.shape == (n, k) and scale.shape == (n, k // g)
+    b = None if bias is None else _c(bias, np.float64)
+    y = np.empty((m, n), dtype=np.float64)
+    _lib().o_linear_f64_groups(_p(x), m, k, _p(q), _p(scale), g, _p(b), n, _p(y))
+    return y
+
+
+def linear_f64_groups_sampled(x, q, scale, g: int, bias, rows, cols) -> np.ndarray:
+    """The same formula for the listed (row, channel) pairs only."""
+    x = _c(x, np.float64)
+    q = _c(q, np.uint8)
+    scale = _c(scale, np.float32)
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int64)
+    b = None if bias is None else _c(bias, np.float64)
+    k = x.shape[1]
+    _check_group(k, g)
+    y = np.empty(rows.shape, dtype=np.float64)
+    _lib().o_linear_f64_groups_sampled(_p(x), k, _p(q), _p(scale), g, _p(b), _p(rows), _p(cols), rows.size, _p(y))
+    return y
+
+
+def dequantize_groups_f64(q, scale, g: int) -> np.ndarray:
+    """value(q[n,k]) * scale[n, k/g], fp64."""
+    q = _c(q, np.uint8)
+    scale = _c(scale, np.float32)
+    n, k = q.shape
+    _check_group(k, g)
+    out = np.empty((n, k), dtype=np.float64)
+    _lib().o_dequantize_groups_f64(_p(q), _p(scale), g, n, k, _p(out))
+    return out
+
+
+def weight_error_groups(w, q, scale, g: int) -> dict:
+    """rel_l2, worst_channel_rel_l2, underflow and crest with group scales."""
+    w = _c(w, np.float32)
+    q = _c(q, np.uint8)
+    scale = _c(scale, np.float32)
+    n, k = w.shape
+    _check_group(k, g)
+    out = np.zeros(3, dtype=np.float64)
+    ch = np.empty(n, dtype=np.float64)
+    crest = np.empty(n, dtype=np.float64)
+    _lib().o_weight_error_groups(_p(w), _p(q), _p(scale), g, n, k, _p(out), _p(ch), _p(crest))
+    return {"rel_l2": float(out[0]), "worst_channel_rel_l2": float(out[1]),
+            "underflow": float(out[2]), "crest_max": float(crest.max()) if n else 0.0,
+            "crest_median": float(np.median(crest)) if n else 0.0,
+            "channel_rel_l2": ch}
 
 
 def num_threads() -> int:

@@ -348,6 +348,154 @@ void o_weight_error(const float *w, const uint8_t *q, const float *scale, int64_
     out[2] = (nz > 0) ? (double)under / (double)nz : 0.0;
 }
 
+/* ========================================================================= */
+/* Group-wise scales along k.                                                 */
+/*   [B04] "Post-training quantization versus quantization-aware training"   */
+/*   (granularity table: one scale per run of g weights in a row, g = 32, 64 */
+/*   or 128) and "The one that matters: quantization is a quality decision"  */
+/*   (raise the granularity from per-channel to per-group); the Day-98 lab   */
+/*   page's storage census ("FP8 e4m3, one scale per 32": the block's max    */
+/*   |w| / 448 as an fp32 scale, the cast of w / scale as the code).          */
+/* Each run of g weights of a row is quantized exactly as [FP8W]'s contract   */
+/* quantizes a whole row:                                                     */
+/*   scale[n, j] = fl32(max_{i < g} |W[n, j*g + i]| / 448)                    */
+/*   q[n, k]     = E(fl32(W[n, k] / scale[n, k / g]))   (0x00 if scale is 0) */
+/* scale is [n, k / g] row-major; k % g == 0.                                 */
+/* ========================================================================= */
+int o_quantize_groups(const float *w, int64_t n, int64_t k, int64_t g, uint8_t *q, float *scale)
+{
+    const int64_t ng = k / g;
+    int nonfinite = 0;
+#pragma omp parallel for reduction(| : nonfinite) schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t j = 0; j < ng; ++j) {
+            const float *grp = w + r * k + j * g;
+            float amax = 0.0f;
+            for (int64_t i = 0; i < g; ++i) {
+                const float a = fabsf(grp[i]);
+                if (!isfinite(a))
+                    nonfinite = 1;
+                else if (a > amax)
+                    amax = a;
+            }
+            const float s = amax / 448.0f;
+            scale[r * ng + j] = s;
+            for (int64_t i = 0; i < g; ++i)
+                q[r * k + j * g + i] = (s == 0.0f) ? 0x00 : o_e4m3_encode(grp[i] / s);
+        }
+    }
+    return nonfinite ? 3 : 0;
+}
+
+/* The linear layer with group scales, in fp64:                              */
+/*   y[m,n] = sum_j scale[n,j] * (sum_{i<g} x[m,jg+i] * value(q[n,jg+i]))     */
+/*            + bias[n]                                                       */
+/* Each product x * value(q) is exact in fp64; the group sums, their scaling */
+/* and the sum over groups round in fp64 only.                                */
+void o_linear_f64_groups(const double *x, int64_t m, int64_t k, const uint8_t *q, const float *scale,
+                         int64_t g, const double *bias, int64_t n, double *y)
+{
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = o_e4m3_decode((uint8_t)c);
+    const int64_t ng = k / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < n; ++c) {
+        const uint8_t *qr = q + c * k;
+        for (int64_t r = 0; r < m; ++r) {
+            const double *xr = x + r * k;
+            double acc = 0.0;
+            for (int64_t j = 0; j < ng; ++j) {
+                double part = 0.0;
+                for (int64_t i = 0; i < g; ++i)
+                    part += xr[j * g + i] * lut[qr[j * g + i]];
+                acc += (double)scale[c * ng + j] * part;
+            }
+            y[r * n + c] = acc + (bias ? bias[c] : 0.0);
+        }
+    }
+}
+
+/* The same for the listed (row, channel) pairs only. */
+void o_linear_f64_groups_sampled(const double *x, int64_t k, const uint8_t *q, const float *scale, int64_t g,
+                                 const double *bias, const int64_t *rows, const int64_t *cols, int64_t count,
+                                 double *y)
+{
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = o_e4m3_decode((uint8_t)c);
+    const int64_t ng = k / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < count; ++t) {
+        const double *xr = x + rows[t] * k;
+        const uint8_t *qr = q + cols[t] * k;
+        double acc = 0.0;
+        for (int64_t j = 0; j < ng; ++j) {
+            double part = 0.0;
+            for (int64_t i = 0; i < g; ++i)
+                part += xr[j * g + i] * lut[qr[j * g + i]];
+            acc += (double)scale[cols[t] * ng + j] * part;
+        }
+        y[t] = acc + (bias ? bias[cols[t]] : 0.0);
+    }
+}
+
+/* Dequantised weight with group scales: value(q[n,k]) * scale[n, k / g]. */
+void o_dequantize_groups_f64(const uint8_t *q, const float *scale, int64_t g, int64_t n, int64_t k, double *out)
+{
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = o_e4m3_decode((uint8_t)c);
+    const int64_t ng = k / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t j = 0; j < k; ++j)
+            out[r * k + j] = lut[q[r * k + j]] * (double)scale[r * ng + j / g];
+}
+
+/* The error report of o_weight_error with group scales: What[n,k] =        */
+/* value(q[n,k]) * scale[n, k / g]. The figures are defined as there.         */
+void o_weight_error_groups(const float *w, const uint8_t *q, const float *scale, int64_t g, int64_t n,
+                           int64_t k, double *out, double *channel_rel_l2, double *crest)
+{
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = o_e4m3_decode((uint8_t)c);
+    const int64_t ng = k / g;
+    double err2 = 0.0, ref2 = 0.0, worst = 0.0;
+    int64_t nz = 0, under = 0;
+#pragma omp parallel for reduction(+ : err2, ref2, nz, under) reduction(max : worst) schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        double e2 = 0.0, w2 = 0.0, amax = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            const double wv = (double)w[r * k + j];
+            const double v = lut[q[r * k + j]];
+            const double d = v * (double)scale[r * ng + j / g] - wv;
+            e2 += d * d;
+            w2 += wv * wv;
+            if (fabs(wv) > amax)
+                amax = fabs(wv);
+            if (wv != 0.0) {
+                nz += 1;
+                if (v == 0.0)
+                    under += 1;
+            }
+        }
+        err2 += e2;
+        ref2 += w2;
+        const double ch = (w2 > 0.0) ? sqrt(e2 / w2) : 0.0;
+        if (channel_rel_l2)
+            channel_rel_l2[r] = ch;
+        if (crest)
+            crest[r] = (w2 > 0.0) ? amax / sqrt(w2 / (double)k) : 0.0;
+        if (ch > worst)
+            worst = ch;
+    }
+    out[0] = (ref2 > 0.0) ? sqrt(err2 / ref2) : 0.0;
+    out[1] = worst;
+    out[2] = (nz > 0) ? (double)under / (double)nz : 0.0;
+}
+
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 int o_num_threads(void)
 {
