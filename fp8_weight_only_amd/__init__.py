@@ -30,7 +30,9 @@ import torch
 __all__ = [
     "Fp8wError", "lib_path", "load", "fp8w_quantize", "fp8w_linear", "fp8w_linear_with_path",
     "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes", "fp8w_linear_kernel",
-    "fp8w_stream_read_probe",
+    "fp8w_stream_read_probe", "fp8w_quantize_grouped", "fp8w_linear_grouped", "fp8w_linear_grouped_with_path",
+    "fp8w_linear_grouped_path", "fp8w_linear_grouped_kernel", "fp8w_dequantize_grouped",
+    "quantize_grouped", "linear_grouped", "dequantize_grouped",
     "fp8w_status_string", "fp8w_abi_version", "quantize", "linear", "dequantize",
     "linear_path", "workspace_bytes", "QuantizedLinear",
     "BF16", "FP16", "FP32", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_FALLBACK", "EXPORTS",
@@ -58,6 +60,12 @@ EXPORTS = {
     "fp8w_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _P, _P, _P]),
     "fp8w_linear_kernel": (ctypes.c_char_p, [_I, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_stream_read_probe": (_I, [_P, _SZ, _P, _P]),
+    "fp8w_quantize_grouped": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P]),
+    "fp8w_linear_grouped": (_I, [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P]),
+    "fp8w_linear_grouped_with_path": (_I, [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _I, _P]),
+    "fp8w_linear_grouped_path": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P]),
+    "fp8w_linear_grouped_kernel": (ctypes.c_char_p, [_I, _I64, _I64, _I64, _I64, _I, _P, _P]),
+    "fp8w_dequantize_grouped": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "fp8w_status_string": (ctypes.c_char_p, [_I]),
     "fp8w_last_hip_error": (_I, []),
     "fp8w_abi_version": (_I, []),
@@ -129,6 +137,31 @@ def fp8w_linear_kernel(path, m, n, k, act_dtype, x, q):
 
 def fp8w_stream_read_probe(p, nbytes, sink, stream) -> int:
     return load().fp8w_stream_read_probe(p, nbytes, sink, stream)
+
+
+def fp8w_quantize_grouped(w, w_dtype, n, k, group, q, scale, stream) -> int:
+    return load().fp8w_quantize_grouped(w, w_dtype, n, k, group, q, scale, stream)
+
+
+def fp8w_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, stream) -> int:
+    return load().fp8w_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, stream)
+
+
+def fp8w_linear_grouped_with_path(x, act_dtype, m, k, q, scale, group, bias, n, y, path, stream) -> int:
+    return load().fp8w_linear_grouped_with_path(x, act_dtype, m, k, q, scale, group, bias, n, y, path, stream)
+
+
+def fp8w_linear_grouped_path(m, n, k, group, act_dtype, x, q) -> int:
+    return load().fp8w_linear_grouped_path(m, n, k, group, act_dtype, x, q)
+
+
+def fp8w_linear_grouped_kernel(path, m, n, k, group, act_dtype, x, q):
+    r = load().fp8w_linear_grouped_kernel(path, m, n, k, group, act_dtype, x, q)
+    return r.decode() if r is not None else None
+
+
+def fp8w_dequantize_grouped(q, scale, group, n, k, out, out_dtype, stream) -> int:
+    return load().fp8w_dequantize_grouped(q, scale, group, n, k, out, out_dtype, stream)
 
 
 def fp8w_status_string(status) -> str:
@@ -250,6 +283,61 @@ def dequantize(q: torch.Tensor, scale: torch.Tensor = None, dtype: torch.dtype =
                                   n, k, out.data_ptr() if out.numel() else 0, _dtype_code(dtype),
                                   _stream(q.device))
     _check(st, "fp8w_dequantize_fallback")
+    return out
+
+
+def quantize_grouped(w: torch.Tensor, group: int):
+    """e4m3 quantization with one scale per run of ``group`` (32, 64 or 128)
+    weights of each row of a [n, k] weight. Returns (q uint8 [n, k], scale fp32
+    [n, k // group])."""
+    if w.dim() != 2:
+        raise ValueError("w must be [n, k]")
+    n, k = w.shape
+    if group <= 0 or k % group:
+        raise ValueError("group must divide k")
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n, k // group), dtype=torch.float32, device=w.device)
+    st = fp8w_quantize_grouped(_dev(w, "w") if w.numel() else 0, _dtype_code(w.dtype), n, k, group,
+                               q.data_ptr() if q.numel() else 0, scale.data_ptr() if scale.numel() else 0,
+                               _stream(w.device))
+    _check(st, "fp8w_quantize_grouped")
+    return q, scale
+
+
+def linear_grouped(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor = None,
+                   out: torch.Tensor = None, path: int = PATH_AUTO) -> torch.Tensor:
+    """y = sum_j scale[n, j] * sum_{k in group j} x[m,k] value(q[n,k]) + bias[n],
+    rounded once to x.dtype; scale is [n, k // group] (the group size follows)."""
+    if x.dim() != 2 or q.dim() != 2 or q.dtype != torch.uint8 or scale.dtype != torch.float32 or scale.dim() != 2:
+        raise ValueError("expected x [m,k], q uint8 [n,k], scale fp32 [n, k // group]")
+    m, k = x.shape
+    n = q.shape[0]
+    if q.shape[1] != k or scale.shape[0] != n or scale.shape[1] == 0 or k % scale.shape[1]:
+        raise ValueError("shape mismatch between x, q and scale")
+    group = k // scale.shape[1]
+    if bias is not None and (bias.shape != (n,) or bias.dtype != x.dtype):
+        raise ValueError("bias must be [n] in the activation dtype")
+    act = _dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    elif out.shape != (m, n) or out.dtype != x.dtype:
+        raise ValueError("out must be [m, n] in the activation dtype")
+    st = fp8w_linear_grouped_with_path(_dev(x, "x") if x.numel() else 0, act, m, k,
+                                       _dev(q, "q") if q.numel() else 0, _dev(scale, "scale"), group,
+                                       _dev(bias, "bias") if bias is not None and n else 0, n,
+                                       _dev(out, "out") if out.numel() else 0, path, _stream(x.device))
+    _check(st, "fp8w_linear_grouped")
+    return out
+
+
+def dequantize_grouped(q: torch.Tensor, scale: torch.Tensor, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """value(q[n,k]) * scale[n, k // group] in ``dtype`` (fp32: exactly the fp32 product)."""
+    n, k = q.shape
+    group = k // scale.shape[1]
+    out = torch.empty((n, k), dtype=dtype, device=q.device)
+    st = fp8w_dequantize_grouped(_dev(q, "q"), _dev(scale, "scale"), group, n, k, out.data_ptr(),
+                                 _dtype_code(dtype), _stream(q.device))
+    _check(st, "fp8w_dequantize_grouped")
     return out
 
 

@@ -170,9 +170,143 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
     return hip_status(fp8w::launch_fallback_gemm(x, a, m, k, ws, scale, bias, n, y, stream));
 }
 
+// ---- group-wise scales
+bool valid_group(int64_t k, int64_t group)
+{
+    return (group == 32 || group == 64 || group == 128) && k % group == 0;
+}
+
+size_t group_scale_bytes(int64_t n, int64_t k, int64_t group)
+{
+    return (size_t)n * (size_t)(k / group) * 4;
+}
+
+fp8w_status_t run_linear_grouped(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, const uint8_t* q,
+                                 const float* scale, int64_t group, const void* bias, int64_t n, void* y, int path,
+                                 hipStream_t stream)
+{
+    if (!valid_act(act) || !sizes_ok(m, n, k) || !valid_group(k, group))
+        return FP8W_ERR_INVALID_VALUE;
+    if (path < FP8W_PATH_AUTO || path > FP8W_PATH_FALLBACK)
+        return FP8W_ERR_INVALID_VALUE;
+    if (path == FP8W_PATH_AUTO)
+        path = auto_path(m, k, x, q);
+    if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
+        if (path == FP8W_PATH_GEMV && m != 1 && m != 0)
+            return FP8W_ERR_INVALID_VALUE;
+        if (m > 32 || k % 256 != 0 || k == 0)
+            return FP8W_ERR_INVALID_VALUE;
+    }
+    if (m == 0 || n == 0)
+        return FP8W_SUCCESS;
+    if (!y || (k > 0 && (!x || !q || !scale)))
+        return FP8W_ERR_INVALID_VALUE;
+    if (!aligned(x, 2) || !aligned(y, 2) || !aligned(bias, 2) || !aligned(scale, 4))
+        return FP8W_ERR_MISALIGNED;
+    if ((path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) && !fast_pointers(x, q))
+        return FP8W_ERR_MISALIGNED;
+    const size_t ybytes = (size_t)m * (size_t)n * 2;
+    if (overlap(y, ybytes, x, (size_t)m * (size_t)k * 2) || overlap(y, ybytes, q, (size_t)n * (size_t)k) ||
+        overlap(y, ybytes, scale, group_scale_bytes(n, k, group)) ||
+        overlap(y, ybytes, bias, bias ? (size_t)n * 2 : 0))
+        return FP8W_ERR_INVALID_VALUE;
+    return hip_status(fp8w::launch_linear_grouped(path, x, act_of(act), m, k, q, scale, group, bias, n, y, stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+fp8w_status_t fp8w_quantize_grouped(const void* w, fp8w_dtype_t w_dtype, int64_t n, int64_t k, int64_t group,
+                                    uint8_t* q, float* scale, hipStream_t stream)
+{
+    if (!valid_dtype(w_dtype) || !sizes_ok(0, n, k) || !valid_group(k, group))
+        return FP8W_ERR_INVALID_VALUE;
+    if (n == 0 || k == 0)
+        return FP8W_SUCCESS;
+    if (!w || !q || !scale)
+        return FP8W_ERR_INVALID_VALUE;
+    const size_t eb = (size_t)elem_bytes(w_dtype);
+    if (!aligned(w, eb) || !aligned(scale, 4))
+        return FP8W_ERR_MISALIGNED;
+    const size_t wbytes = (size_t)n * (size_t)k * eb, qbytes = (size_t)n * (size_t)k;
+    const size_t sbytes = group_scale_bytes(n, k, group);
+    if (overlap(q, qbytes, w, wbytes) || overlap(scale, sbytes, w, wbytes) || overlap(scale, sbytes, q, qbytes))
+        return FP8W_ERR_INVALID_VALUE;
+
+    fp8w_status_t st =
+        hip_status(fp8w::launch_quantize_groups(w, act_of(w_dtype), n, k, group, q, scale, stream));
+    if (st != FP8W_SUCCESS)
+        return st;
+    std::vector<float> host(sbytes / 4);
+    st = hip_status(hipMemcpyAsync(host.data(), scale, sbytes, hipMemcpyDeviceToHost, stream));
+    if (st != FP8W_SUCCESS)
+        return st;
+    st = hip_status(hipStreamSynchronize(stream));
+    if (st != FP8W_SUCCESS)
+        return st;
+    for (float s : host)
+        if (!isfinite(s))
+            return FP8W_ERR_NONFINITE;
+    return FP8W_SUCCESS;
+}
+
+fp8w_status_t fp8w_linear_grouped(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k, const uint8_t* q,
+                                  const float* scale, int64_t group, const void* bias, int64_t n, void* y,
+                                  hipStream_t stream)
+{
+    return run_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, FP8W_PATH_AUTO, stream);
+}
+
+fp8w_status_t fp8w_linear_grouped_with_path(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                            const uint8_t* q, const float* scale, int64_t group, const void* bias,
+                                            int64_t n, void* y, int path, hipStream_t stream)
+{
+    return run_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, path, stream);
+}
+
+int fp8w_linear_grouped_path(int64_t m, int64_t n, int64_t k, int64_t group, fp8w_dtype_t act_dtype,
+                             const void* x, const uint8_t* q)
+{
+    if (!valid_act(act_dtype) || !sizes_ok(m, n, k) || !valid_group(k, group))
+        return -1;
+    return auto_path(m, k, x, q);
+}
+
+const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k, int64_t group,
+                                       fp8w_dtype_t act_dtype, const void* x, const uint8_t* q)
+{
+    if (!valid_act(act_dtype) || !sizes_ok(m, n, k) || !valid_group(k, group))
+        return nullptr;
+    if (path == FP8W_PATH_AUTO)
+        path = auto_path(m, k, x, q);
+    if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
+        if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || k % 256 != 0 || k == 0)
+            return nullptr;
+        return fp8w::grouped_kernel_name(path, m, n, k);
+    }
+    if (path == FP8W_PATH_FALLBACK)
+        return fp8w::grouped_kernel_name(2, m, n, k);
+    return nullptr;
+}
+
+fp8w_status_t fp8w_dequantize_grouped(const uint8_t* q, const float* scale, int64_t group, int64_t n, int64_t k,
+                                      void* out, fp8w_dtype_t out_dtype, hipStream_t stream)
+{
+    if (!valid_dtype(out_dtype) || !sizes_ok(0, n, k) || !valid_group(k, group))
+        return FP8W_ERR_INVALID_VALUE;
+    if (n == 0 || k == 0)
+        return FP8W_SUCCESS;
+    if (!q || !scale || !out)
+        return FP8W_ERR_INVALID_VALUE;
+    const size_t eb = (size_t)elem_bytes(out_dtype);
+    if (!aligned(out, eb) || !aligned(scale, 4))
+        return FP8W_ERR_MISALIGNED;
+    const size_t obytes = (size_t)n * (size_t)k * eb;
+    if (overlap(out, obytes, q, (size_t)n * (size_t)k) || overlap(out, obytes, scale, group_scale_bytes(n, k, group)))
+        return FP8W_ERR_INVALID_VALUE;
+    return hip_status(fp8w::launch_dequantize_grouped(q, scale, group, n, k, out, act_of(out_dtype), stream));
+}
 
 fp8w_status_t fp8w_quantize(const void* w, fp8w_dtype_t w_dtype, int64_t n, int64_t k, uint8_t* q, float* scale,
                             hipStream_t stream)

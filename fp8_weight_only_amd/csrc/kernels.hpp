@@ -53,6 +53,28 @@ hipError_t launch_fallback_gemm(const void* x, Act act, int64_t m, int64_t k, co
                                 const float* scale, const void* bias, int64_t n, void* y,
                                 hipStream_t stream);
 
+// ---- group-wise scales along k (scale [n, k / group], group 32, 64 or 128)
+
+// Build-time quantizer with one scale per run of `group` weights of a row; a
+// group with a non-finite weight gets a NaN scale.
+hipError_t launch_quantize_groups(const void* w, Act w_type, int64_t n, int64_t k, int64_t group, uint8_t* q,
+                                  float* scale, hipStream_t stream);
+
+// The grouped linear. path 0: M = 1 GEMV (k % 256 == 0, x and q 16-byte
+// aligned); path 1: M <= 32 skinny ring where k allows it, else the generic
+// kernel; path 2: the generic kernel (any m, n, k % group == 0, x 2-byte and q
+// 1-byte aligned).
+hipError_t launch_linear_grouped(int path, const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
+                                 const float* scale, int64_t group, const void* bias, int64_t n, void* y,
+                                 hipStream_t stream);
+
+// Name of the kernel launch_linear_grouped runs for this path and shape.
+const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k);
+
+// value(q) * scale[r, j / group] rounded to out_type.
+hipError_t launch_dequantize_grouped(const uint8_t* q, const float* scale, int64_t group, int64_t n, int64_t k,
+                                     void* out, Act out_type, hipStream_t stream);
+
 // Plain streaming read of `bytes` bytes (16-byte aligned, multiple of 16): the
 // bandwidth reference the linear kernels are read against.
 hipError_t launch_read_probe(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -26,9 +26,19 @@ constexpr int kThreads = 256;
 
 // Weight element readers: fp32 as is, bf16/fp16 widened exactly.
 struct WF32 {
+    static constexpr int kBytes = 4;
     __device__ __forceinline__ static float at(const void* p, int64_t i)
     {
         return static_cast<const float*>(p)[i];
+    }
+    // 4 consecutive elements from a 16-byte aligned address
+    __device__ __forceinline__ static void load4(const void* p, int64_t i, float* o)
+    {
+        const f32x4 d = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+        o[0] = d.x;
+        o[1] = d.y;
+        o[2] = d.z;
+        o[3] = d.w;
     }
     // 16 consecutive elements from a 16-byte aligned address
     __device__ __forceinline__ static void load16(const void* p, int64_t i, float* o)
@@ -47,9 +57,19 @@ struct WF32 {
 
 template <typename A>
 struct W16 {
+    static constexpr int kBytes = 2;
     __device__ __forceinline__ static float at(const void* p, int64_t i)
     {
         return A::to_f32(static_cast<const uint16_t*>(p)[i]);
+    }
+    // 4 consecutive elements from an 8-byte aligned address
+    __device__ __forceinline__ static void load4(const void* p, int64_t i, float* o)
+    {
+        const u32x2 d = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+        o[0] = A::lo_f32(d.x);
+        o[1] = A::hi_f32(d.x);
+        o[2] = A::lo_f32(d.y);
+        o[3] = A::hi_f32(d.y);
     }
     __device__ __forceinline__ static void load16(const void* p, int64_t i, float* o)
     {
@@ -165,7 +185,123 @@ hipError_t launch_typed(const void* w, int elem_bytes, int64_t n, int64_t k, uin
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- group scales
+// One scale per run of G weights of a row (G = 32, 64 or 128; k % G == 0):
+// "B04 - Precision & Quantization", section "Post-training quantization versus
+// quantization-aware training" (per-group granularity), and the Day-98 lab
+// page's "one scale per 32" census. Each group is quantized as the contract
+// quantizes a row: scale = fl32(amax / 448), codes the RNE e4m3 of the IEEE
+// quotient clamped to +-448, an all-zero group gets scale 0 and codes 0x00. A
+// group with a NaN or infinite weight gets a NaN scale (codes unspecified).
+//
+// VEC: each thread takes 4 consecutive weights, so a group is G / 4 adjacent
+// lanes of one wave and its amax is a butterfly over those lanes. Every lane
+// runs every shuffle (lanes past the row's end carry zeros): k % G == 0, so a
+// lane group is either wholly inside the row or wholly past it.
+template <typename W, int G, bool VEC>
+__global__ __launch_bounds__(kThreads) void quantize_groups_kernel(const void* __restrict__ w, int64_t k,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ scale)
+{
+    static_assert(G == 32 || G == 64 || G == 128, "group size");
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const int64_t base = r * k;
+    const int64_t ng = k / G;
+    if (VEC) {
+        constexpr int LG = G / 4;  // lanes per group
+        for (int64_t j0 = 0; j0 < k; j0 += kThreads * 4) {
+            const int64_t j = j0 + (int64_t)tid * 4;
+            const bool in = j < k;
+            float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (in)
+                W::load4(w, base + j, v);
+            float amax = 0.0f;
+            int bad = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = fabsf(v[e]);
+                bad |= !(a <= 3.402823466e38f);
+                amax = fmaxf(amax, a);
+            }
+#pragma unroll
+            for (int off = 1; off < LG; off <<= 1) {
+                amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+                bad |= __shfl_xor(bad, off, kWave);
+            }
+            if (!in)
+                continue;
+            const float s = amax / 448.0f;
+            if ((tid & (LG - 1)) == 0)
+                scale[r * ng + j / G] = bad ? __builtin_nanf("") : s;
+            if (bad)
+                continue;
+            const uint32_t out = (s != 0.0f) ? encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s) : 0u;
+            *reinterpret_cast<uint32_t*>(q + base + j) = out;
+        }
+    } else {
+        // any alignment: one thread per group
+        for (int64_t g = tid; g < ng; g += kThreads) {
+            const int64_t g0 = base + g * G;
+            float amax = 0.0f;
+            int bad = 0;
+            for (int e = 0; e < G; ++e) {
+                const float a = fabsf(W::at(w, g0 + e));
+                bad |= !(a <= 3.402823466e38f);
+                amax = fmaxf(amax, a);
+            }
+            const float s = amax / 448.0f;
+            scale[r * ng + g] = bad ? __builtin_nanf("") : s;
+            if (bad)
+                continue;
+            for (int e = 0; e < G; ++e)
+                q[g0 + e] = (s != 0.0f) ? encode1(W::at(w, g0 + e) / s) : (uint8_t)0;
+        }
+    }
+}
+
+template <typename W, int G>
+hipError_t launch_groups_g(const void* w, int64_t n, int64_t k, uint8_t* q, float* scale, hipStream_t stream)
+{
+    const bool vec = ((reinterpret_cast<uintptr_t>(w) & (4 * W::kBytes - 1)) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(q) & 3) == 0);
+    const dim3 grid((unsigned)n), block(kThreads);
+    if (vec)
+        hipLaunchKernelGGL((quantize_groups_kernel<W, G, true>), grid, block, 0, stream, w, k, q, scale);
+    else
+        hipLaunchKernelGGL((quantize_groups_kernel<W, G, false>), grid, block, 0, stream, w, k, q, scale);
+    return hipGetLastError();
+}
+
+template <typename W>
+hipError_t launch_groups_typed(const void* w, int64_t n, int64_t k, int64_t group, uint8_t* q, float* scale,
+                               hipStream_t stream)
+{
+    switch (group) {
+    case 32: return launch_groups_g<W, 32>(w, n, k, q, scale, stream);
+    case 64: return launch_groups_g<W, 64>(w, n, k, q, scale, stream);
+    case 128: return launch_groups_g<W, 128>(w, n, k, q, scale, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_groups(const void* w, Act w_type, int64_t n, int64_t k, int64_t group, uint8_t* q,
+                                  float* scale, hipStream_t stream)
+{
+    if (n == 0 || k == 0)
+        return hipSuccess;
+    switch (w_type) {
+    case Act::FP32:
+        return launch_groups_typed<WF32>(w, n, k, group, q, scale, stream);
+    case Act::BF16:
+        return launch_groups_typed<W16<Bf16>>(w, n, k, group, q, scale, stream);
+    case Act::FP16:
+        return launch_groups_typed<W16<F16>>(w, n, k, group, q, scale, stream);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_quantize(const void* w, Act w_type, int64_t n, int64_t k, uint8_t* q, float* scale,
                            hipStream_t stream)

@@ -169,6 +169,59 @@ FP8W_API const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t 
                                         const void* x, const uint8_t* q);
 
 /*
+ * Group-wise weight scales along k: one fp32 scale per run of `group`
+ * consecutive weights of a row, group = 32, 64 or 128 ("B04 - Precision &
+ * Quantization", section "Post-training quantization versus
+ * quantization-aware training": per-group granularity, g = 32/64/128; section
+ * "The one that matters: quantization is a quality decision": per-channel ->
+ * per-group when an outlier inside a row costs accuracy; the Day-98 lab page's
+ * "one scale per 32" census). Each group is quantized exactly as
+ * fp8w_quantize quantizes a row. Scales are [n, k / group] fp32, row-major;
+ * k % group == 0 is required (FP8W_ERR_INVALID_VALUE otherwise).
+ */
+
+/* Build-time quantizer with group scales: scale[r, j] = fl32(amax_j / 448) over
+   w[r, j*group .. (j+1)*group), codes as in fp8w_quantize (0 for an all-zero
+   group). Synchronizes `stream`; FP8W_ERR_NONFINITE if any weight is NaN or
+   infinite (that group's scale is then NaN). q and scale must not overlap w. */
+FP8W_API fp8w_status_t fp8w_quantize_grouped(const void* w, fp8w_dtype_t w_dtype, int64_t n, int64_t k,
+                                             int64_t group, uint8_t* q, float* scale, hipStream_t stream);
+
+/* y[m,n] = sum_j scale[n,j] * sum_{i<group} x[m, j*group+i] * value(q[n, j*group+i]) + bias[n],
+   fp32 accumulation (each partial sum of exact products lies inside one
+   group and is scaled before it is added), one rounding to act_dtype.
+   Arguments as for fp8w_linear; no workspace. Dispatch as fp8w_linear_path
+   (m == 1: GEMV; m <= 32: skinny MFMA kernel; k % 256 == 0 and 16-byte
+   aligned x and q for both); everything else, and skinny shapes whose k the
+   ring cannot tile, runs a generic kernel (any m, n; x 2-byte aligned).
+   Asynchronous. */
+FP8W_API fp8w_status_t fp8w_linear_grouped(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                           const uint8_t* q, const float* scale, int64_t group, const void* bias,
+                                           int64_t n, void* y, hipStream_t stream);
+
+/* fp8w_linear_grouped with an explicit FP8W_PATH_* (same requirements as
+   fp8w_linear_with_path; FP8W_PATH_FALLBACK is the generic kernel). */
+FP8W_API fp8w_status_t fp8w_linear_grouped_with_path(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                                     const uint8_t* q, const float* scale, int64_t group,
+                                                     const void* bias, int64_t n, void* y, int path,
+                                                     hipStream_t stream);
+
+/* Path fp8w_linear_grouped takes (FP8W_PATH_*), -1 when the arguments are invalid. */
+FP8W_API int fp8w_linear_grouped_path(int64_t m, int64_t n, int64_t k, int64_t group, fp8w_dtype_t act_dtype,
+                                      const void* x, const uint8_t* q);
+
+/* Name of the kernel a grouped call takes (as fp8w_linear_kernel); NULL when invalid. */
+FP8W_API const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k, int64_t group,
+                                                fp8w_dtype_t act_dtype, const void* x, const uint8_t* q);
+
+/* The dequantised weight with group scales: out[r, j] = out_dtype(fl32(value(q[r,j])
+   * scale[r, j / group])); out_dtype FP8W_FP32 (exactly q.float() * scale),
+   FP8W_BF16 or FP8W_FP16 (round to nearest even). out must not overlap q or
+   scale. Asynchronous. */
+FP8W_API fp8w_status_t fp8w_dequantize_grouped(const uint8_t* q, const float* scale, int64_t group, int64_t n,
+                                               int64_t k, void* out, fp8w_dtype_t out_dtype, hipStream_t stream);
+
+/*
  * Measurement aid, not part of the method: read `bytes` bytes at `p` once
  * with the 128-bit streaming loads the linear kernels use, folding them into a
  * word that is written to `sink` (one uint32, device) only for one specific

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fw.load()
     names = declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 17
     for name in names:
         assert hasattr(lib, name), name
         assert name in fw.EXPORTS, name
@@ -237,3 +237,56 @@ def test_package_never_imports_the_oracle():
                     text = fh.read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "fp8w_oracle" not in text and "liboracle" not in text, f
+
+
+# ---------------------------------------------------------------- group scales
+def _glin(x=X, act=fw.BF16, m=4, k=4096, q=Q, s=S, g=32, b=B, n=4096, y=Y, path=fw.PATH_AUTO):
+    return fw.fp8w_linear_grouped_with_path(x, act, m, k, q, s, g, b, n, y, path, 0)
+
+
+def test_grouped_paths_and_kernel_names():
+    gp, gk, A = fw.fp8w_linear_grouped_path, fw.fp8w_linear_grouped_kernel, fw.PATH_AUTO
+    assert gp(1, 4096, 4096, 32, fw.BF16, X, Q) == fw.PATH_GEMV
+    assert gp(16, 4096, 4096, 64, fw.BF16, X, Q) == fw.PATH_SKINNY
+    assert gp(33, 4096, 4096, 128, fw.BF16, X, Q) == fw.PATH_FALLBACK
+    assert gp(1, 4096, 4160, 32, fw.BF16, X, Q) == fw.PATH_FALLBACK      # k % 256 != 0
+    assert gp(1, 4096, 4096, 48, fw.BF16, X, Q) == -1                    # group not 32/64/128
+    assert gp(1, 4096, 4000, 64, fw.BF16, X, Q) == -1                    # group does not divide k
+    assert gk(A, 1, 4096, 4096, 32, fw.BF16, X, Q) == "gemv_grouped_kernel<R=2,U=2,NT=128>"
+    assert gk(A, 1, 28672, 8192, 128, fw.BF16, X, Q) == "gemv_grouped_kernel<R=4,U=2,NT=128>"
+    assert gk(A, 16, 14336, 4096, 32, fw.FP16, X, Q) == "pipe_grouped_kernel<XR=16,CT=4,KP=1,NS=4>"
+    assert gk(A, 32, 28672, 4096, 32, fw.BF16, X, Q) == "pipe_grouped_kernel<XR=32,CT=4,KP=1,NS=2>"
+    assert gk(A, 8, 4096, 4096, 64, fw.BF16, X, Q) == "pipe_grouped_kernel<XR=8,CT=1,KP=2,NS=4>"
+    assert gk(A, 32, 4096, 4096, 64, fw.BF16, X, Q) == "pipe_grouped_kernel<XR=32,CT=1,KP=2,NS=2>"
+    assert gk(A, 2, 4096, 768, 128, fw.BF16, X, Q) == "grouped_generic_kernel"      # ring cannot tile k
+    assert gk(A, 64, 4096, 4096, 32, fw.BF16, X, Q) == "grouped_generic_kernel"
+    assert gk(fw.PATH_FALLBACK, 1, 4096, 4096, 32, fw.BF16, X, Q) == "grouped_generic_kernel"
+    assert gk(fw.PATH_GEMV, 2, 4096, 4096, 32, fw.BF16, X, Q) is None
+
+
+def test_grouped_rejects_invalid_arguments():
+    assert _glin(g=16) == fw.ERR_INVALID_VALUE
+    assert _glin(g=256) == fw.ERR_INVALID_VALUE
+    assert _glin(k=4000, g=64) == fw.ERR_INVALID_VALUE
+    assert _glin(act=fw.FP32) == fw.ERR_INVALID_VALUE
+    assert _glin(s=S + 2) == fw.ERR_MISALIGNED
+    assert _glin(x=X + 2, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED
+    assert _glin(m=2, path=fw.PATH_GEMV) == fw.ERR_INVALID_VALUE
+    assert _glin(k=4160, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
+    assert _glin(y=Q) == fw.ERR_INVALID_VALUE                            # y overlaps q
+    assert _glin(path=5) == fw.ERR_INVALID_VALUE
+    assert _glin(m=0) == fw.SUCCESS
+    assert _glin(n=0) == fw.SUCCESS
+
+
+def test_grouped_quantize_and_dequantize_validation():
+    qg, dg = fw.fp8w_quantize_grouped, fw.fp8w_dequantize_grouped
+    assert qg(0, fw.FP32, 0, 64, 32, 0, 0, 0) == fw.SUCCESS
+    assert qg(X, fw.FP32, 4, 64, 48, Q, S, 0) == fw.ERR_INVALID_VALUE
+    assert qg(X, fw.FP32, 4, 96, 64, Q, S, 0) == fw.ERR_INVALID_VALUE
+    assert qg(X + 2, fw.FP32, 4, 64, 32, Q, S, 0) == fw.ERR_MISALIGNED
+    assert qg(X, fw.FP32, 4, 64, 32, Q, 0, 0) == fw.ERR_INVALID_VALUE
+    assert dg(Q, S, 32, 0, 64, Y, fw.BF16, 0) == fw.SUCCESS
+    assert dg(Q, 0, 32, 4, 64, Y, fw.BF16, 0) == fw.ERR_INVALID_VALUE
+    assert dg(Q, S, 32, 4, 64, Y + 1, fw.BF16, 0) == fw.ERR_MISALIGNED
+    assert dg(Q, S, 32, 4, 64, Q, fw.BF16, 0) == fw.ERR_INVALID_VALUE    # out overlaps q
