@@ -117,6 +117,65 @@ class Layer:
         self.bias = None if lw.bias is None else lw.bias.to(dev)
 
 
+class GroupedLayer:
+    """A layer quantized with group scales along k, `copies` rotated copies."""
+
+    def __init__(self, lw, group, copies, dev):
+        w = torch.from_numpy(lw.w).to(dev)
+        fw.quantize_grouped(w, group)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        q, s = fw.quantize_grouped(w, group)
+        self.quantize_ms = (time.perf_counter() - t0) * 1e3
+        self.n, self.k = lw.w.shape
+        self.group = group
+        self.name = f"{lw.name}_g{group}"
+        del w
+        self.qs = [(q, s)] + [(q.clone(), s.clone()) for _ in range(copies - 1)]
+        self.bias = None if lw.bias is None else lw.bias.to(dev)
+
+
+def grouped_bytes(m, n, k, g, bias):
+    return n * k + 4 * n * (k // g) + (2 * n if bias else 0) + 2 * m * k + 2 * m * n
+
+
+class GroupedCall:
+    def __init__(self, layer, x, dev):
+        self.layer, self.x = layer, x
+        self.m = x.shape[0]
+        self.y = torch.empty((self.m, layer.n), dtype=x.dtype, device=dev)
+        act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
+        self.act = act
+        self.args = [(x.data_ptr(), act, self.m, layer.k, q.data_ptr(), s.data_ptr(), layer.group,
+                      0 if layer.bias is None else layer.bias.data_ptr(), layer.n, self.y.data_ptr())
+                     for q, s in layer.qs]
+        self.bytes = grouped_bytes(self.m, layer.n, layer.k, layer.group, layer.bias is not None)
+        self.kernel = fw.fp8w_linear_grouped_kernel(fw.PATH_AUTO, self.m, layer.n, layer.k, layer.group, act,
+                                                    x.data_ptr(), layer.qs[0][0].data_ptr())
+
+    def launch(self, copy, stream):
+        r = fw.load().fp8w_linear_grouped(*self.args[copy % len(self.args)], stream)
+        if r != 0:
+            raise fw.Fp8wError(r, "fp8w_linear_grouped")
+
+
+def grouped_report(call, st):
+    us = st["mean"]
+    gbps = call.bytes / (us * 1e-6) / 1e9
+    useful = 2.0 * call.m * call.layer.n * call.layer.k
+    r = {"layer": call.layer.name, "group": call.layer.group, "m": call.m, "n": call.layer.n, "k": call.layer.k,
+         "kernel": call.kernel, "us_per_call": round(us, 3), "us_p10": round(st["p10"], 3),
+         "us_p90": round(st["p90"], 3), "alg_bytes": call.bytes, "gbps": round(gbps, 1),
+         "pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+         "tflops": round(useful / (us * 1e-6) / 1e12, 3)}
+    issued, mpad = mfma_issued_flops(call.kernel, call.m, call.layer.n, call.layer.k)
+    if issued:
+        r["mfma"] = {"padded_m": mpad, "issued_pct_of_peak": round(100.0 * issued / (us * 1e-6) / 1e12 /
+                                                                   MFMA_PEAK_TFLOPS, 3),
+                     "useful_pct_of_peak": round(100.0 * useful / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 3)}
+    return r
+
+
 class Call:
     """Argument tuples of one fp8w_linear call for every weight copy."""
 
@@ -221,7 +280,7 @@ def mfma_issued_flops(kernel, m, n, k):
     segments per instruction of which one is kept, so tokens count as
     MP*MT*SEG. None for other kernels."""
     import re
-    mm = re.match(r"pipe_kernel<XR=(\d+),CT=(\d+),KP=\d+,NS=\d+>", kernel or "")
+    mm = re.match(r"pipe(?:_grouped)?_kernel<XR=(\d+),CT=(\d+),KP=\d+,NS=\d+>", kernel or "")
     if mm:
         xr, ct = int(mm.group(1)), int(mm.group(2))
         mt = 2 if xr > 16 else 1
@@ -739,7 +798,7 @@ def mfma_summary(csv_path, n, k):
     print("\n".join(lines))
 
 
-SECTIONS = ("tiny", "skinny", "block", "large")
+SECTIONS = ("tiny", "skinny", "block", "large", "grouped")
 
 
 def extra_sections(dev, stream, reps=100, only=None):
@@ -823,6 +882,33 @@ def extra_sections(dev, stream, reps=100, only=None):
             f"{ex['decoder_block_merged']['step_gbps']:.0f} GB/s")
         del Ms, mcalls
         torch.cuda.empty_cache()
+
+    if "grouped" in want:
+        # group scales along k: the decode layers at M = 1 (bf16) and the skinny
+        # layer at M = 2, 16, 32 (fp16), with g = 32 and g = 128
+        gr = []
+        for g in (32, 128):
+            for i in range(3):
+                lw = workloads.decode_layer(i)
+                n, k = lw.w.shape
+                L = GroupedLayer(lw, g, max(1, math.ceil(ROTATE_BYTES / grouped_bytes(1, n, k, g, True))), dev)
+                c = GroupedCall(L, workloads.decode_x(i).to(dev), dev)
+                gr.append(grouped_report(c, burst(c, 200, 20, stream)))
+                gr[-1]["quantize_ms"] = round(L.quantize_ms, 3)
+                log(f"  grouped g={g} {L.name} m=1: {gr[-1]['us_per_call']:.2f} us {gr[-1]['pct_peak']:.1f}% "
+                    f"[{c.kernel}]")
+                del L, c
+                torch.cuda.empty_cache()
+            L = GroupedLayer(workloads.skinny_layer(), g,
+                             max(1, math.ceil(ROTATE_BYTES / grouped_bytes(32, 14336, 4096, g, True))), dev)
+            for m in (2, 16, 32):
+                c = GroupedCall(L, workloads.skinny_x(m).to(dev), dev)
+                gr.append(grouped_report(c, burst(c, reps, 10, stream)))
+                log(f"  grouped g={g} skinny m={m}: {gr[-1]['us_per_call']:.2f} us {gr[-1]['pct_peak']:.1f}% "
+                    f"[{c.kernel}]")
+            del L
+            torch.cuda.empty_cache()
+        ex["grouped"] = gr
 
     if "large" in want:
         # large shapes and the k = 8200 fallback

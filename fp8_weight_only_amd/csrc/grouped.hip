@@ -154,30 +154,34 @@ __global__ __launch_bounds__(NT) void gemv_grouped_kernel(const uint16_t* __rest
 // The direct-to-LDS ring of the per-channel skinny kernel (same code and
 // activation staging: rotated 16-byte chunks, XR activation rows, KP k-parts,
 // NS stages, k-staggered start), plus each wave's group scales for the stage:
-// 16 channels x (256 / G) groups, 4 bytes per lane, two load instructions
-// (lane l of instruction p brings scale[channel (64p + l) % 16][group
-// ((64p + l) / 16) mod (256 / G)], landing at 4 (64p + l), so the LDS holds
-// them as [group][channel]; for G > 32 the surplus lanes write copies that are
-// never read).
-template <int XR, int CT, int KP, int NS>
+// 16 channels x (256 / G) groups, 4 bytes per lane (lane l of instruction p
+// brings scale[channel (64p + l) % 16][group ((64p + l) / 16) mod (256 / G)],
+// landing at 4 (64p + l), so the LDS holds them as [group][channel]; for
+// G = 128 the surplus lanes write copies that are never read).
+template <int XR, int CT, int KP, int NS, int G>
 struct PipeGCfg {
     static_assert(XR % 2 == 0 && XR >= 2 && XR <= 32, "activation rows");
+    static_assert(G == 32 || G == 64 || G == 128, "group size");
     static constexpr int MT = XR > 16 ? 2 : 1;
     static constexpr int W = CT * KP;
     static constexpr int CODE = 16 * 256;
     static constexpr int XPART = XR * 512;
-    static constexpr int SCB = 512;  // scale bytes per wave and stage
+    static constexpr int NGS = 256 / G;                  // groups per wave and stage
+    static constexpr int SLW = NGS * 16 * 4 > 256 ? 2 : 1;  // scale load instructions per wave
+    static constexpr int SCB = 256 * SLW;                // scale bytes per wave and stage
     static constexpr int STAGE = W * CODE + KP * XPART + W * SCB;
     static constexpr int XLOADS = (XR / 2) * KP;
     static constexpr int XPW = (XLOADS + W - 1) / W;
-    static constexpr int LOADS = 4 + XPW + 2;
+    static constexpr int LOADS = 4 + XPW + SLW;
     static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
 };
 
-template <typename A, int XR, int CT, int KP, int NS>
+template <typename A, int XR, int CT, int KP, int NS, int G>
 struct PipeG {
-    using C = PipeGCfg<XR, CT, KP, NS>;
+    using C = PipeGCfg<XR, CT, KP, NS, G>;
     static constexpr int MT = C::MT;
+    static constexpr int NGS = C::NGS;
+    static constexpr int TPG = G / 32;  // MFMAs per group
 
     const uint16_t* x;
     const uint8_t* q;
@@ -185,7 +189,7 @@ struct PipeG {
     int m;
     int64_t n, k, n0, ng;
     int64_t S, rot;
-    int lane, wave, ct, kp, lg;  // lg = log2(G)
+    int lane, wave, ct, kp;
 
     __device__ __forceinline__ void issue(int64_t s, uint8_t* buf) const
     {
@@ -214,14 +218,13 @@ struct PipeG {
             __builtin_amdgcn_global_load_lds((const void*)src,
                                              FP8W_LDS(buf + C::W * C::CODE + kpx * C::XPART + pair * 1024), 16, 0, 0);
         }
-        const int ngs = 256 >> lg;  // groups per wave and stage
-        const int64_t g0 = (kb + kp * 256) >> lg;
+        const int64_t g0 = (kb + kp * 256) / G;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        for (int p = 0; p < C::SLW; ++p) {
             const int idx = 64 * p + lane;
             int64_t row = n0 + 16 * ct + (idx & 15);
             row = row < n ? row : n - 1;
-            const float* src = scale + row * ng + g0 + ((idx >> 4) & (ngs - 1));
+            const float* src = scale + row * ng + g0 + ((idx >> 4) % NGS);
             __builtin_amdgcn_global_load_lds((const void*)src,
                                              FP8W_LDS(buf + C::W * C::CODE + KP * C::XPART + wave * C::SCB + 256 * p),
                                              4, 0, 0);
@@ -229,7 +232,12 @@ struct PipeG {
     }
 
     // MFMA t of this wave's 256 k covers k = 32t .. 32t + 31: lane (i, g)
-    // takes codes 32t + 8g .. +7 of channel i and the same k of token i.
+    // takes codes 32t + 8g .. +7 of channel i and the same k of token i. The
+    // G / 32 MFMAs of one group chain into one partial sum, which is scaled and
+    // added once. The stage runs in three phases, fenced so the scheduler
+    // cannot interleave them back into a chain: every LDS read; every decode
+    // and MFMA; then the scaled adds, by which time the products are done.
+    // Interleaved, each step waited for its own LDS read and MFMA result.
     __device__ __forceinline__ void compute(const uint8_t* buf, f32x4* acc) const
     {
         const int i = lane & 15, g = lane >> 4;
@@ -237,34 +245,57 @@ struct PipeG {
         const uint8_t* xb = buf + C::W * C::CODE + kp * C::XPART;
         const uint8_t* sb = buf + C::W * C::CODE + KP * C::XPART + wave * C::SCB;
         const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        u32x2 c8[8];
+        u32x4 b[8][MT];
+        f32x4 s4[NGS];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int c = 2 * t + (g >> 1);
-            const u32x2 c8 = *reinterpret_cast<const u32x2*>(cb + 16 * (16 * i + ((c + i) & 15)) + 8 * (g & 1));
-            const u32x2 d0 = A::decode4(c8.x), d1 = A::decode4(c8.y);
-            const u32x4 a = {d0.x, d0.y, d1.x, d1.y};
-            const f32x4 s4 = *reinterpret_cast<const f32x4*>(sb + 4 * (16 * ((32 * t) >> lg) + 4 * g));
+            c8[t] = *reinterpret_cast<const u32x2*>(cb + 16 * (16 * i + ((c + i) & 15)) + 8 * (g & 1));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int tok = (i + 16 * mt) < XR ? (i + 16 * mt) : XR - 1;
-                const u32x4 b = *reinterpret_cast<const u32x4*>(xb + 16 * (32 * tok + ((4 * t + g + tok) & 31)));
-                const f32x4 part = A::mfma(a, b, zero);
-                acc[mt].x = __builtin_fmaf(s4.x, part.x, acc[mt].x);
-                acc[mt].y = __builtin_fmaf(s4.y, part.y, acc[mt].y);
-                acc[mt].z = __builtin_fmaf(s4.z, part.z, acc[mt].z);
-                acc[mt].w = __builtin_fmaf(s4.w, part.w, acc[mt].w);
+                b[t][mt] = *reinterpret_cast<const u32x4*>(xb + 16 * (32 * tok + ((4 * t + g + tok) & 31)));
             }
         }
+#pragma unroll
+        for (int j = 0; j < NGS; ++j)
+            s4[j] = *reinterpret_cast<const f32x4*>(sb + 4 * (16 * j + 4 * g));
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 part[NGS][MT];
+#pragma unroll
+        for (int j = 0; j < NGS; ++j)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                part[j][mt] = zero;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const u32x2 d0 = A::decode4(c8[t].x), d1 = A::decode4(c8[t].y);
+            const u32x4 a = {d0.x, d0.y, d1.x, d1.y};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                part[t / TPG][mt] = A::mfma(a, b[t][mt], part[t / TPG][mt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NGS; ++j)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[mt].x = __builtin_fmaf(s4[j].x, part[j][mt].x, acc[mt].x);
+                acc[mt].y = __builtin_fmaf(s4[j].y, part[j][mt].y, acc[mt].y);
+                acc[mt].z = __builtin_fmaf(s4[j].z, part[j][mt].z, acc[mt].z);
+                acc[mt].w = __builtin_fmaf(s4[j].w, part[j][mt].w, acc[mt].w);
+            }
     }
 };
 
 // Requires k % (KP * 256 * NS) == 0 and scale 4-byte aligned.
-template <typename A, int XR, int CT, int KP, int NS>
+template <typename A, int XR, int CT, int KP, int NS, int G>
 __global__ __launch_bounds__(CT* KP * kWave) void pipe_grouped_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k, int lg)
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k)
 {
-    using P = PipeG<A, XR, CT, KP, NS>;
+    using P = PipeG<A, XR, CT, KP, NS, G>;
     using C = typename P::C;
     constexpr int MT = C::MT;
     __shared__ __attribute__((aligned(1024))) uint8_t b0[C::STAGE];
@@ -279,8 +310,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_grouped_kernel(
     p.m = m;
     p.n = n;
     p.k = k;
-    p.lg = lg;
-    p.ng = k >> lg;
+    p.ng = k / G;
     p.lane = threadIdx.x & (kWave - 1);
     p.wave = threadIdx.x / kWave;
     p.ct = p.wave % CT;
@@ -459,31 +489,43 @@ GroupedPlan plan_grouped(int64_t m, int64_t n, int64_t k)
     return p;
 }
 
-template <typename A, int XR, int CT, int KP, int NS>
+template <typename A, int XR, int CT, int KP, int NS, int G>
 hipError_t launch_pipe_g(const void* x, int m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
-                         int64_t n, void* y, int lg, hipStream_t stream)
+                         int64_t n, void* y, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + 16 * CT - 1) / (16 * CT))), block(CT * KP * kWave);
-    hipLaunchKernelGGL((pipe_grouped_kernel<A, XR, CT, KP, NS>), grid, block, 0, stream,
+    hipLaunchKernelGGL((pipe_grouped_kernel<A, XR, CT, KP, NS, G>), grid, block, 0, stream,
                        static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias),
-                       static_cast<uint16_t*>(y), m, n, k, lg);
+                       static_cast<uint16_t*>(y), m, n, k);
     return hipGetLastError();
 }
 
-template <typename A, int XR>
+template <typename A, int XR, int G>
 hipError_t launch_pipe_g_xr(const GroupedPlan& p, const void* x, int m, int64_t k, const uint8_t* q,
-                            const float* scale, const void* bias, int64_t n, void* y, int lg, hipStream_t stream)
+                            const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
 {
     const int key = p.ct * 100 + p.kp * 10 + p.ns;
     switch (key) {
-    case 412: return launch_pipe_g<A, XR, 4, 1, 2>(x, m, k, q, scale, bias, n, y, lg, stream);
-    case 414: return launch_pipe_g<A, XR, 4, 1, 4>(x, m, k, q, scale, bias, n, y, lg, stream);
-    case 122: return launch_pipe_g<A, XR, 1, 2, 2>(x, m, k, q, scale, bias, n, y, lg, stream);
+    case 412: return launch_pipe_g<A, XR, 4, 1, 2, G>(x, m, k, q, scale, bias, n, y, stream);
+    case 414: return launch_pipe_g<A, XR, 4, 1, 4, G>(x, m, k, q, scale, bias, n, y, stream);
+    case 122: return launch_pipe_g<A, XR, 1, 2, 2, G>(x, m, k, q, scale, bias, n, y, stream);
     case 124:
         if constexpr (XR <= 16)
-            return launch_pipe_g<A, XR, 1, 2, 4>(x, m, k, q, scale, bias, n, y, lg, stream);
+            return launch_pipe_g<A, XR, 1, 2, 4, G>(x, m, k, q, scale, bias, n, y, stream);
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename A, int G>
+hipError_t launch_pipe_g_plan(const GroupedPlan& p, const void* x, int m, int64_t k, const uint8_t* q,
+                              const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    switch (p.xr) {
+    case 4: return launch_pipe_g_xr<A, 4, G>(p, x, m, k, q, scale, bias, n, y, stream);
+    case 8: return launch_pipe_g_xr<A, 8, G>(p, x, m, k, q, scale, bias, n, y, stream);
+    case 16: return launch_pipe_g_xr<A, 16, G>(p, x, m, k, q, scale, bias, n, y, stream);
+    default: return launch_pipe_g_xr<A, 32, G>(p, x, m, k, q, scale, bias, n, y, stream);
     }
 }
 
@@ -509,12 +551,11 @@ hipError_t launch_grouped_typed(int path, const void* x, int64_t m, int64_t k, c
         const GroupedPlan p = plan_grouped(m, n, k);
         if (p.pipe) {
             const int mi = (int)m;
-            switch (p.xr) {
-            case 4: return launch_pipe_g_xr<A, 4>(p, x, mi, k, q, scale, bias, n, y, lg, stream);
-            case 8: return launch_pipe_g_xr<A, 8>(p, x, mi, k, q, scale, bias, n, y, lg, stream);
-            case 16: return launch_pipe_g_xr<A, 16>(p, x, mi, k, q, scale, bias, n, y, lg, stream);
-            default: return launch_pipe_g_xr<A, 32>(p, x, mi, k, q, scale, bias, n, y, lg, stream);
-            }
+            if (lg == 5)
+                return launch_pipe_g_plan<A, 32>(p, x, mi, k, q, scale, bias, n, y, stream);
+            if (lg == 6)
+                return launch_pipe_g_plan<A, 64>(p, x, mi, k, q, scale, bias, n, y, stream);
+            return launch_pipe_g_plan<A, 128>(p, x, mi, k, q, scale, bias, n, y, stream);
         }
     }
     const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 15) / 16)), block(256);
