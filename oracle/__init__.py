@@ -22,6 +22,10 @@ reporting. Sources, by page title and section:
 * "Skill: Write an FP8 Kernel", "Required reasoning process" step 2 (amax,
   scale = amax / fp8_max, cast of x / scale) and step 7 (~1 % relative error
   against a wide reference; scale = 0 handled without a division).
+* E4M3FNUZ: "B04 - Precision & Quantization", the format table's FNUZ row and
+  the sections "Hardware support, and where the vendors diverge" (bias 8,
+  maximum 240, 0x80 NaN, no negative zero) and the trap list (the same bits
+  decode a factor of two apart; tag the format).
 * Group scales along k: "B04 - Precision & Quantization", sections
   "Post-training quantization versus quantization-aware training" (one scale
   per run of g = 32 / 64 / 128 weights of a row) and "The one that matters:
@@ -82,6 +86,10 @@ def _lib():
         lib.o_dequantize_groups_f64.argtypes = [P, P, I64, I64, I64, P]
         lib.o_weight_error_groups.restype = None
         lib.o_weight_error_groups.argtypes = [P, P, P, I64, I64, I64, P, P, P]
+        lib.o_fnuz_decode.restype = ctypes.c_double
+        lib.o_fnuz_decode.argtypes = [ctypes.c_uint8]
+        lib.o_fnuz_to_ocp.restype = None
+        lib.o_fnuz_to_ocp.argtypes = [P, I64, P]
         lib.o_num_threads.restype = ctypes.c_int
         lib.o_num_threads.argtypes = []
         lib.o_set_num_threads.restype = None
@@ -326,6 +334,22 @@ def weight_error_groups(w, q, scale, g: int) -> dict:
             "underflow": float(out[2]), "crest_max": float(crest.max()) if n else 0.0,
             "crest_median": float(np.median(crest)) if n else 0.0,
             "channel_rel_l2": ch}
+
+
+# ----------------------------------------------------------------- E4M3FNUZ interop
+def fnuz_decode(codes) -> np.ndarray:
+    """E4M3FNUZ values (bias 8, 0x80 NaN, no negative zero) of uint8 codes, fp64."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lib = _lib()
+    return np.vectorize(lambda v: lib.o_fnuz_decode(int(v)), otypes=[np.float64])(c)
+
+
+def fnuz_to_ocp(codes) -> np.ndarray:
+    """OCP e4m3fn codes of the same values as the given E4M3FNUZ codes (RNE; NaN -> 0x7F)."""
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, dtype=np.uint8)
+    _lib().o_fnuz_to_ocp(_p(c), c.size, _p(out))
+    return out
 
 
 def num_threads() -> int:

@@ -496,6 +496,44 @@ void o_weight_error_groups(const float *w, const uint8_t *q, const float *scale,
     out[2] = (nz > 0) ? (double)under / (double)nz : 0.0;
 }
 
+/* ========================================================================= */
+/* The other e4m3: E4M3FNUZ ([B04] "The numbers, derived rather than         */
+/* tabulated", its table row and footnote; "Hardware support, and where the   */
+/* vendors diverge"; the "values 2x off" trap). Fields as OCP e4m3 but bias 8, */
+/* no infinities, no negative zero, and one NaN: 0x80. Every other pattern is */
+/* finite, the top exponent included (maximum 1.875 * 2^7 = 240).            */
+/* ========================================================================= */
+double o_fnuz_decode(uint8_t c)
+{
+    if (c == 0x80)
+        return NAN;
+    const int s = (c >> 7) & 1;
+    const int e = (c >> 3) & 15;
+    const int m = c & 7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, 1 - 8 - 3);            /* subnormal: m * 2^-10 */
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 8);    /* normal: 1.m * 2^(e-8) */
+    return s ? -v : v;
+}
+
+/* An FNUZ-coded weight carried over to OCP codes with its scales unchanged:  */
+/* each code becomes the OCP code of the same value, by the encoder above     */
+/* (round to nearest even; every FNUZ value is within the OCP range). NaN     */
+/* stays NaN (0x7F).                                                           */
+void o_fnuz_to_ocp(const uint8_t *src, int64_t count, uint8_t *dst)
+{
+    uint8_t table[256];
+    for (int c = 0; c < 256; ++c) {
+        const double v = o_fnuz_decode((uint8_t)c);
+        table[c] = isnan(v) ? 0x7F : o_e4m3_encode((float)v);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        dst[i] = table[src[i]];
+}
+
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 int o_num_threads(void)
 {
