@@ -32,7 +32,7 @@ __all__ = [
     "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes", "fp8w_linear_kernel",
     "fp8w_stream_read_probe", "fp8w_quantize_grouped", "fp8w_linear_grouped", "fp8w_linear_grouped_with_path",
     "fp8w_linear_grouped_path", "fp8w_linear_grouped_kernel", "fp8w_dequantize_grouped",
-    "quantize_grouped", "linear_grouped", "dequantize_grouped",
+    "quantize_grouped", "linear_grouped", "dequantize_grouped", "fp8w_fnuz_to_ocp", "fnuz_to_ocp", "ocp_codes",
     "fp8w_status_string", "fp8w_abi_version", "quantize", "linear", "dequantize",
     "linear_path", "workspace_bytes", "QuantizedLinear",
     "BF16", "FP16", "FP32", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_FALLBACK", "EXPORTS",
@@ -66,6 +66,7 @@ EXPORTS = {
     "fp8w_linear_grouped_path": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_linear_grouped_kernel": (ctypes.c_char_p, [_I, _I64, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_dequantize_grouped": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P]),
+    "fp8w_fnuz_to_ocp": (_I, [_P, _I64, _P, _P]),
     "fp8w_status_string": (ctypes.c_char_p, [_I]),
     "fp8w_last_hip_error": (_I, []),
     "fp8w_abi_version": (_I, []),
@@ -162,6 +163,10 @@ def fp8w_linear_grouped_kernel(path, m, n, k, group, act_dtype, x, q):
 
 def fp8w_dequantize_grouped(q, scale, group, n, k, out, out_dtype, stream) -> int:
     return load().fp8w_dequantize_grouped(q, scale, group, n, k, out, out_dtype, stream)
+
+
+def fp8w_fnuz_to_ocp(src, count, dst, stream) -> int:
+    return load().fp8w_fnuz_to_ocp(src, count, dst, stream)
 
 
 def fp8w_status_string(status) -> str:
@@ -339,6 +344,32 @@ def dequantize_grouped(q: torch.Tensor, scale: torch.Tensor, dtype: torch.dtype 
                                  _dtype_code(dtype), _stream(q.device))
     _check(st, "fp8w_dequantize_grouped")
     return out
+
+
+def fnuz_to_ocp(codes: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """OCP e4m3fn codes (uint8) of the same values as E4M3FNUZ codes (uint8 or
+    torch.float8_e4m3fnuz); ``out`` may be ``codes`` itself (in place)."""
+    src = codes.view(torch.uint8) if codes.dtype != torch.uint8 else codes
+    if out is None:
+        out = torch.empty_like(src)
+    n = src.numel()
+    st = fp8w_fnuz_to_ocp(_dev(src, "codes") if n else 0, n, _dev(out, "out") if n else 0, _stream(src.device))
+    _check(st, "fp8w_fnuz_to_ocp")
+    return out
+
+
+def ocp_codes(codes: torch.Tensor) -> torch.Tensor:
+    """The weight codes this library takes (OCP e4m3fn bytes), from a tensor
+    whose dtype is its format tag: torch.float8_e4m3fn is viewed as bytes,
+    torch.float8_e4m3fnuz is translated value for value (fnuz_to_ocp), and
+    plain uint8 is taken as OCP already."""
+    if codes.dtype == torch.float8_e4m3fn:
+        return codes.view(torch.uint8)
+    if codes.dtype == torch.float8_e4m3fnuz:
+        return fnuz_to_ocp(codes)
+    if codes.dtype == torch.uint8:
+        return codes
+    raise TypeError(f"not an e4m3 code tensor: {codes.dtype}")
 
 
 class QuantizedLinear:

@@ -290,6 +290,19 @@ const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k
     return nullptr;
 }
 
+fp8w_status_t fp8w_fnuz_to_ocp(const uint8_t* src, int64_t count, uint8_t* dst, hipStream_t stream)
+{
+    if (count < 0 || count > kMaxElems)
+        return FP8W_ERR_INVALID_VALUE;
+    if (count == 0)
+        return FP8W_SUCCESS;
+    if (!src || !dst)
+        return FP8W_ERR_INVALID_VALUE;
+    if (src != dst && overlap(src, (size_t)count, dst, (size_t)count))
+        return FP8W_ERR_INVALID_VALUE;
+    return hip_status(fp8w::launch_fnuz_to_ocp(src, count, dst, stream));
+}
+
 fp8w_status_t fp8w_dequantize_grouped(const uint8_t* q, const float* scale, int64_t group, int64_t n, int64_t k,
                                       void* out, fp8w_dtype_t out_dtype, hipStream_t stream)
 {

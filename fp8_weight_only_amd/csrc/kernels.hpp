@@ -75,6 +75,9 @@ const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k);
 hipError_t launch_dequantize_grouped(const uint8_t* q, const float* scale, int64_t group, int64_t n, int64_t k,
                                      void* out, Act out_type, hipStream_t stream);
 
+// E4M3FNUZ codes -> OCP e4m3fn codes of the same values (dst may equal src).
+hipError_t launch_fnuz_to_ocp(const uint8_t* src, int64_t count, uint8_t* dst, hipStream_t stream);
+
 // Plain streaming read of `bytes` bytes (16-byte aligned, multiple of 16): the
 // bandwidth reference the linear kernels are read against.
 hipError_t launch_read_probe(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);

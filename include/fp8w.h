@@ -222,6 +222,21 @@ FP8W_API fp8w_status_t fp8w_dequantize_grouped(const uint8_t* q, const float* sc
                                                int64_t k, void* out, fp8w_dtype_t out_dtype, hipStream_t stream);
 
 /*
+ * Format interop ("B04 - Precision & Quantization", the format table's
+ * E4M3FNUZ row, section "Hardware support, and where the vendors diverge", and
+ * its trap list: the same bits decode a factor of two apart on gfx942's FNUZ
+ * e4m3 (bias 8, maximum 240, 0x80 NaN, no negative zero) and the OCP e4m3fn
+ * this library computes in; tag the format). Translates `count` FNUZ codes
+ * into the OCP codes of the same values, round to nearest even, so a
+ * checkpoint quantized for gfx942 keeps its scales. All values are kept
+ * except the 16 patterns below 2^-6 with an odd mantissa, which lie halfway
+ * between OCP subnormals and move 2^-10 to the even one; NaN (0x80) becomes
+ * 0x7F. src and dst are device pointers; dst may equal src (in place) but may
+ * not otherwise overlap it. Asynchronous.
+ */
+FP8W_API fp8w_status_t fp8w_fnuz_to_ocp(const uint8_t* src, int64_t count, uint8_t* dst, hipStream_t stream);
+
+/*
  * Measurement aid, not part of the method: read `bytes` bytes at `p` once
  * with the 128-bit streaming loads the linear kernels use, folding them into a
  * word that is written to `sink` (one uint32, device) only for one specific

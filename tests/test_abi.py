@@ -30,7 +30,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fw.load()
     names = declared_symbols()
-    assert len(names) == 17
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
         assert name in fw.EXPORTS, name
@@ -290,3 +290,11 @@ def test_grouped_quantize_and_dequantize_validation():
     assert dg(Q, 0, 32, 4, 64, Y, fw.BF16, 0) == fw.ERR_INVALID_VALUE
     assert dg(Q, S, 32, 4, 64, Y + 1, fw.BF16, 0) == fw.ERR_MISALIGNED
     assert dg(Q, S, 32, 4, 64, Q, fw.BF16, 0) == fw.ERR_INVALID_VALUE    # out overlaps q
+
+
+def test_fnuz_to_ocp_validation():
+    f = fw.fp8w_fnuz_to_ocp
+    assert f(0, 0, 0, 0) == fw.SUCCESS
+    assert f(Q, -1, Y, 0) == fw.ERR_INVALID_VALUE
+    assert f(0, 16, Y, 0) == fw.ERR_INVALID_VALUE
+    assert f(Q, 64, Q + 8, 0) == fw.ERR_INVALID_VALUE     # partial overlap
