@@ -86,9 +86,9 @@ def alg_bytes(m, n, k, bias=True):
     return n * k + 4 * n + (2 * n if bias else 0) + 2 * m * k + 2 * m * n
 
 
-# the sources that define the dominant kernel (the decode GEMV) and its dispatch;
-# a change to any of them voids the recorded traffic counters
-GEMV_SOURCES = ("api.hip", "common.hpp", "gemv.hip", "kernels.hpp")
+# the sources that define the dominant kernel (the decode GEMV: its code and its
+# tile choice); a change to either voids the recorded traffic counters
+GEMV_SOURCES = ("common.hpp", "gemv.hip")
 
 
 def kernel_source_hash():
@@ -735,7 +735,8 @@ def _short_kernel_name(full):
     name, targs = m.group(1), (m.group(2) or "")
     args = [a.strip() for a in targs[1:-1].split(",")] if targs else []
     keys = {"pipe_kernel": ("XR", "CT", "KP", "NS"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
-            "gemv_kernel": ("R", "U", "NT"), "wpipe_kernel": ("XR", "CT", "NS")}.get(name)
+            "gemv_kernel": ("R", "U", "NT"), "wpipe_kernel": ("XR", "CT", "NS"),
+            "gemv_grouped_kernel": ("R", "U", "NT"), "pipe_grouped_kernel": ("XR", "CT", "KP", "NS", "G")}.get(name)
     if keys and len(args) == len(keys) + 1:  # first argument is the activation type
         return f"{name}<" + ",".join(f"{kk}={v}" for kk, v in zip(keys, args[1:])) + ">"
     return name + targs
