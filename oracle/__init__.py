@@ -22,6 +22,9 @@ reporting. Sources, by page title and section:
 * "Skill: Write an FP8 Kernel", "Required reasoning process" step 2 (amax,
   scale = amax / fp8_max, cast of x / scale) and step 7 (~1 % relative error
   against a wide reference; scale = 0 handled without a division).
+* W8A8: "Skill: Write an FP8 Kernel", "Required reasoning process" steps 2, 4
+  and 5 and "Correctness requirements" (per-token activation scales, fp32
+  accumulation, acc * scale_x[m] * scale_w[n] in the epilogue).
 * E4M3FNUZ: "B04 - Precision & Quantization", the format table's FNUZ row and
   the sections "Hardware support, and where the vendors diverge" (bias 8,
   maximum 240, 0x80 NaN, no negative zero) and the trap list (the same bits
@@ -86,6 +89,8 @@ def _lib():
         lib.o_dequantize_groups_f64.argtypes = [P, P, I64, I64, I64, P]
         lib.o_weight_error_groups.restype = None
         lib.o_weight_error_groups.argtypes = [P, P, P, I64, I64, I64, P, P, P]
+        lib.o_linear_w8a8_f64.restype = None
+        lib.o_linear_w8a8_f64.argtypes = [P, P, I64, I64, P, P, P, I64, P]
         lib.o_fnuz_decode.restype = ctypes.c_double
         lib.o_fnuz_decode.argtypes = [ctypes.c_uint8]
         lib.o_fnuz_to_ocp.restype = None
@@ -334,6 +339,28 @@ def weight_error_groups(w, q, scale, g: int) -> dict:
             "underflow": float(out[2]), "crest_max": float(crest.max()) if n else 0.0,
             "crest_median": float(np.median(crest)) if n else 0.0,
             "channel_rel_l2": ch}
+
+
+# ----------------------------------------------------------------- W8A8
+def quantize_activations(x):
+    """Per-token e4m3 quantization of activations x [m, k] (their exact values):
+    the row quantizer applied to the rows of x. Returns (qx, scale_x, status)."""
+    return quantize_rows(np.asarray(x, dtype=np.float64).astype(np.float32))
+
+
+def linear_w8a8_f64(qx, sx, qw, sw, bias=None) -> np.ndarray:
+    """y[m,n] = (sum_k value(qx[m,k]) value(qw[n,k])) * sx[m] * sw[n] + bias[n], fp64."""
+    qx = _c(qx, np.uint8)
+    qw = _c(qw, np.uint8)
+    sx = _c(sx, np.float32)
+    sw = _c(sw, np.float32)
+    m, k = qx.shape
+    n = qw.shape[0]
+    assert qw.shape == (n, k) and sx.shape == (m,) and sw.shape == (n,)
+    b = None if bias is None else _c(bias, np.float64)
+    y = np.empty((m, n), dtype=np.float64)
+    _lib().o_linear_w8a8_f64(_p(qx), _p(sx), m, k, _p(qw), _p(sw), _p(b), n, _p(y))
+    return y
 
 
 # ----------------------------------------------------------------- E4M3FNUZ interop

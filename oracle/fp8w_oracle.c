@@ -19,7 +19,8 @@
  *           footnote) and "Hardware support, and where the vendors diverge"
  *           (OCP versus FNUZ encodings).
  *   [WFK]   "Skill: Write an FP8 Kernel", sections "Required reasoning process"
- *           step 2 (amax -> scale -> cast of x/scale) and step 7 (scale = 0).
+ *           step 2 (amax -> scale -> cast of x/scale) and step 7 (scale = 0);
+ *           steps 4-5 and "Correctness requirements" for W8A8.
  */
 #include <math.h>
 #include <stdint.h>
@@ -494,6 +495,34 @@ void o_weight_error_groups(const float *w, const uint8_t *q, const float *scale,
     out[0] = (ref2 > 0.0) ? sqrt(err2 / ref2) : 0.0;
     out[1] = worst;
     out[2] = (nz > 0) ? (double)under / (double)nz : 0.0;
+}
+
+/* ========================================================================= */
+/* W8A8 (both operands e4m3), [WFK] "Required reasoning process" steps 2, 4   */
+/* and 5 and its correctness requirements: activations quantized per token   */
+/* (row of x) exactly as weights are per channel (o_quantize_rows on x),      */
+/* fp32 accumulation of the e4m3 x e4m3 products, and the epilogue           */
+/*   y[m,n] = acc[m,n] * scale_x[m] * scale_w[n] + bias[n],                  */
+/* with scale_x indexed by the row, scale_w by the column. In fp64 here:     */
+/* every product of two e4m3 values is exact, so only the sum rounds.         */
+/* ========================================================================= */
+void o_linear_w8a8_f64(const uint8_t *qx, const float *sx, int64_t m, int64_t k, const uint8_t *qw,
+                       const float *sw, const double *bias, int64_t n, double *y)
+{
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = o_e4m3_decode((uint8_t)c);
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < n; ++c) {
+        const uint8_t *wr = qw + c * k;
+        for (int64_t r = 0; r < m; ++r) {
+            const uint8_t *xr = qx + r * k;
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                acc += lut[xr[j]] * lut[wr[j]];
+            y[r * n + c] = acc * (double)sx[r] * (double)sw[c] + (bias ? bias[c] : 0.0);
+        }
+    }
 }
 
 /* ========================================================================= */
