@@ -33,6 +33,8 @@ __all__ = [
     "fp8w_stream_read_probe", "fp8w_quantize_grouped", "fp8w_linear_grouped", "fp8w_linear_grouped_with_path",
     "fp8w_linear_grouped_path", "fp8w_linear_grouped_kernel", "fp8w_dequantize_grouped",
     "quantize_grouped", "linear_grouped", "dequantize_grouped", "fp8w_fnuz_to_ocp", "fnuz_to_ocp", "ocp_codes",
+    "fp8w_quantize_activations", "fp8w_gemm_w8a8", "fp8w_linear_w8a8", "fp8w_linear_w8a8_workspace_bytes",
+    "fp8w_linear_w8a8_kernel", "quantize_activations", "gemm_w8a8", "linear_w8a8",
     "fp8w_status_string", "fp8w_abi_version", "quantize", "linear", "dequantize",
     "linear_path", "workspace_bytes", "QuantizedLinear",
     "BF16", "FP16", "FP32", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_FALLBACK", "EXPORTS",
@@ -67,6 +69,11 @@ EXPORTS = {
     "fp8w_linear_grouped_kernel": (ctypes.c_char_p, [_I, _I64, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_dequantize_grouped": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "fp8w_fnuz_to_ocp": (_I, [_P, _I64, _P, _P]),
+    "fp8w_quantize_activations": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
+    "fp8w_gemm_w8a8": (_I, [_P, _P, _I64, _I64, _P, _P, _P, _I64, _P, _I, _P]),
+    "fp8w_linear_w8a8_workspace_bytes": (_SZ, [_I64, _I64]),
+    "fp8w_linear_w8a8": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "fp8w_linear_w8a8_kernel": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "fp8w_status_string": (ctypes.c_char_p, [_I]),
     "fp8w_last_hip_error": (_I, []),
     "fp8w_abi_version": (_I, []),
@@ -167,6 +174,27 @@ def fp8w_dequantize_grouped(q, scale, group, n, k, out, out_dtype, stream) -> in
 
 def fp8w_fnuz_to_ocp(src, count, dst, stream) -> int:
     return load().fp8w_fnuz_to_ocp(src, count, dst, stream)
+
+
+def fp8w_quantize_activations(x, act_dtype, m, k, qx, sx, stream) -> int:
+    return load().fp8w_quantize_activations(x, act_dtype, m, k, qx, sx, stream)
+
+
+def fp8w_gemm_w8a8(qx, sx, m, k, qw, sw, bias, n, y, out_dtype, stream) -> int:
+    return load().fp8w_gemm_w8a8(qx, sx, m, k, qw, sw, bias, n, y, out_dtype, stream)
+
+
+def fp8w_linear_w8a8_workspace_bytes(m, k) -> int:
+    return load().fp8w_linear_w8a8_workspace_bytes(m, k)
+
+
+def fp8w_linear_w8a8(x, act_dtype, m, k, qw, sw, bias, n, y, workspace, workspace_bytes, stream) -> int:
+    return load().fp8w_linear_w8a8(x, act_dtype, m, k, qw, sw, bias, n, y, workspace, workspace_bytes, stream)
+
+
+def fp8w_linear_w8a8_kernel(m, n, k):
+    r = load().fp8w_linear_w8a8_kernel(m, n, k)
+    return r.decode() if r is not None else None
 
 
 def fp8w_status_string(status) -> str:
@@ -343,6 +371,51 @@ def dequantize_grouped(q: torch.Tensor, scale: torch.Tensor, dtype: torch.dtype 
     st = fp8w_dequantize_grouped(_dev(q, "q"), _dev(scale, "scale"), group, n, k, out.data_ptr(),
                                  _dtype_code(dtype), _stream(q.device))
     _check(st, "fp8w_dequantize_grouped")
+    return out
+
+
+def quantize_activations(x: torch.Tensor):
+    """Per-token e4m3 quantization of activations x [m, k] (bf16 / fp16):
+    (qx uint8 [m, k], sx fp32 [m]). Asynchronous; non-finite rows get NaN scales."""
+    m, k = x.shape
+    qx = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    sx = torch.empty((m,), dtype=torch.float32, device=x.device)
+    st = fp8w_quantize_activations(_dev(x, "x") if x.numel() else 0, _dtype_code(x.dtype), m, k,
+                                   qx.data_ptr() if qx.numel() else 0, sx.data_ptr() if m else 0, _stream(x.device))
+    _check(st, "fp8w_quantize_activations")
+    return qx, sx
+
+
+def gemm_w8a8(qx: torch.Tensor, sx: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor = None,
+              out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor = None) -> torch.Tensor:
+    """y = (sum_k value(qx) value(q)) * sx[:, None] * scale[None, :] + bias, rounded once to out_dtype."""
+    m, k = qx.shape
+    n = q.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=qx.device)
+    st = fp8w_gemm_w8a8(_dev(qx, "qx"), _dev(sx, "sx"), m, k, _dev(q, "q"), _dev(scale, "scale"),
+                        _dev(bias, "bias") if bias is not None else 0, n, _dev(out, "out"),
+                        _dtype_code(out.dtype), _stream(qx.device))
+    _check(st, "fp8w_gemm_w8a8")
+    return out
+
+
+def linear_w8a8(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor = None,
+                out: torch.Tensor = None, workspace: torch.Tensor = None) -> torch.Tensor:
+    """The W8A8 layer on bf16 / fp16 activations: per-token quantization of x
+    into the workspace, then the fp8 x fp8 GEMM (see gemm_w8a8)."""
+    m, k = x.shape
+    n = q.shape[0]
+    need = fp8w_linear_w8a8_workspace_bytes(m, k)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    st = fp8w_linear_w8a8(_dev(x, "x"), _dtype_code(x.dtype), m, k, _dev(q, "q"), _dev(scale, "scale"),
+                          _dev(bias, "bias") if bias is not None else 0, n, _dev(out, "out"),
+                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                          _stream(x.device))
+    _check(st, "fp8w_linear_w8a8")
     return out
 
 

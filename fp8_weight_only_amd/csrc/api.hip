@@ -290,6 +290,87 @@ const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k
     return nullptr;
 }
 
+fp8w_status_t fp8w_quantize_activations(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k, uint8_t* qx,
+                                        float* sx, hipStream_t stream)
+{
+    if (!valid_act(act_dtype) || !sizes_ok(m, 0, k))
+        return FP8W_ERR_INVALID_VALUE;
+    if (m == 0)
+        return FP8W_SUCCESS;
+    if (!sx || (k > 0 && (!x || !qx)))
+        return FP8W_ERR_INVALID_VALUE;
+    if (!aligned(x, 2) || !aligned(sx, 4))
+        return FP8W_ERR_MISALIGNED;
+    const size_t xbytes = (size_t)m * (size_t)k * 2, qbytes = (size_t)m * (size_t)k;
+    if (overlap(qx, qbytes, x, xbytes) || overlap(sx, (size_t)m * 4, x, xbytes) ||
+        overlap(sx, (size_t)m * 4, qx, qbytes))
+        return FP8W_ERR_INVALID_VALUE;
+    return hip_status(fp8w::launch_quantize(x, act_of(act_dtype), m, k, qx, sx, stream));
+}
+
+fp8w_status_t fp8w_gemm_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw,
+                             const float* sw, const void* bias, int64_t n, void* y, fp8w_dtype_t out_dtype,
+                             hipStream_t stream)
+{
+    if (!valid_act(out_dtype) || !sizes_ok(m, n, k) || k == 0 || k % 256 != 0)
+        return FP8W_ERR_INVALID_VALUE;
+    if (m == 0 || n == 0)
+        return FP8W_SUCCESS;
+    if (!qx || !sx || !qw || !sw || !y)
+        return FP8W_ERR_INVALID_VALUE;
+    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 2) ||
+        !aligned(bias, 2))
+        return FP8W_ERR_MISALIGNED;
+    const size_t ybytes = (size_t)m * (size_t)n * 2;
+    if (overlap(y, ybytes, qx, (size_t)m * (size_t)k) || overlap(y, ybytes, qw, (size_t)n * (size_t)k) ||
+        overlap(y, ybytes, sx, (size_t)m * 4) || overlap(y, ybytes, sw, (size_t)n * 4) ||
+        overlap(y, ybytes, bias, bias ? (size_t)n * 2 : 0))
+        return FP8W_ERR_INVALID_VALUE;
+    return hip_status(fp8w::launch_w8a8(qx, sx, m, k, qw, sw, bias, n, y, act_of(out_dtype), stream));
+}
+
+size_t fp8w_linear_w8a8_workspace_bytes(int64_t m, int64_t k)
+{
+    if (!sizes_ok(m, 0, k))
+        return 0;
+    return (((size_t)m * (size_t)k + 255) & ~(size_t)255) + (size_t)m * 4;
+}
+
+fp8w_status_t fp8w_linear_w8a8(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k, const uint8_t* qw,
+                               const float* sw, const void* bias, int64_t n, void* y, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream)
+{
+    if (!valid_act(act_dtype) || !sizes_ok(m, n, k) || k == 0 || k % 256 != 0)
+        return FP8W_ERR_INVALID_VALUE;
+    if (m == 0 || n == 0)
+        return FP8W_SUCCESS;
+    const size_t need = fp8w_linear_w8a8_workspace_bytes(m, k);
+    if (!workspace || workspace_bytes < need)
+        return FP8W_ERR_WORKSPACE;
+    if (!aligned(workspace, 16))
+        return FP8W_ERR_MISALIGNED;
+    if (!x || !y || !aligned(x, 2) || !aligned(y, 2))
+        return x && y ? FP8W_ERR_MISALIGNED : FP8W_ERR_INVALID_VALUE;
+    if (overlap(workspace, need, x, (size_t)m * (size_t)k * 2) || overlap(workspace, need, y, (size_t)m * (size_t)n * 2) ||
+        overlap(workspace, need, qw, (size_t)n * (size_t)k) || overlap(workspace, need, sw, (size_t)n * 4) ||
+        overlap(workspace, need, bias, bias ? (size_t)n * 2 : 0) ||
+        overlap(y, (size_t)m * (size_t)n * 2, x, (size_t)m * (size_t)k * 2))
+        return FP8W_ERR_INVALID_VALUE;
+    uint8_t* qx = static_cast<uint8_t*>(workspace);
+    float* sx = reinterpret_cast<float*>(qx + (need - (size_t)m * 4));
+    fp8w_status_t st = fp8w_quantize_activations(x, act_dtype, m, k, qx, sx, stream);
+    if (st != FP8W_SUCCESS)
+        return st;
+    return fp8w_gemm_w8a8(qx, sx, m, k, qw, sw, bias, n, y, act_dtype, stream);
+}
+
+const char* fp8w_linear_w8a8_kernel(int64_t m, int64_t n, int64_t k)
+{
+    if (!sizes_ok(m, n, k) || m < 1 || n < 1 || k == 0 || k % 256 != 0)
+        return nullptr;
+    return fp8w::w8a8_kernel_name(m, n);
+}
+
 fp8w_status_t fp8w_fnuz_to_ocp(const uint8_t* src, int64_t count, uint8_t* dst, hipStream_t stream)
 {
     if (count < 0 || count > kMaxElems)

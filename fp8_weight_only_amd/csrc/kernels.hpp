@@ -75,6 +75,15 @@ const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k);
 hipError_t launch_dequantize_grouped(const uint8_t* q, const float* scale, int64_t group, int64_t n, int64_t k,
                                      void* out, Act out_type, hipStream_t stream);
 
+// W8A8 GEMM: y[t, c] = out(acc * sx[t] * sw[c] + bias[c]) with acc the fp32 sum
+// of e4m3 x e4m3 products of qx [m, k] and qw [n, k]; k % 256 == 0, qx and qw
+// 16-byte aligned.
+hipError_t launch_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw, const float* sw,
+                       const void* bias, int64_t n, void* y, Act out, hipStream_t stream);
+
+// Name of the W8A8 kernel instance for this shape.
+const char* w8a8_kernel_name(int64_t m, int64_t n);
+
 // E4M3FNUZ codes -> OCP e4m3fn codes of the same values (dst may equal src).
 hipError_t launch_fnuz_to_ocp(const uint8_t* src, int64_t count, uint8_t* dst, hipStream_t stream);
 

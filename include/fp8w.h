@@ -222,6 +222,47 @@ FP8W_API fp8w_status_t fp8w_dequantize_grouped(const uint8_t* q, const float* sc
                                                int64_t k, void* out, fp8w_dtype_t out_dtype, hipStream_t stream);
 
 /*
+ * W8A8: activations quantized too, for batches far above 32 tokens (prefill),
+ * where the matrix cores, not the weight stream, bound the layer ("Skill:
+ * Write an FP8 Kernel", "Required reasoning process" steps 2, 4 and 5, and
+ * "Correctness requirements"; the weight-only contract reserves this for
+ * compute-bound GEMMs). Weights are the codes and scales of fp8w_quantize.
+ */
+
+/* Per-token activation quantizer: each row of x [m, k] (act_dtype BF16 / FP16)
+   quantized exactly as fp8w_quantize quantizes a weight row: sx[t] =
+   fl32(amax_t / 448), qx[t, :] the RNE e4m3 codes of x / sx[t], clamped to
+   +-448 (0 for an all-zero row). Asynchronous: a row with a NaN or infinite
+   value gets a NaN scale (its outputs are then NaN); nothing is reported. */
+FP8W_API fp8w_status_t fp8w_quantize_activations(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                                 uint8_t* qx, float* sx, hipStream_t stream);
+
+/* The W8A8 GEMM: y[t, c] = out_dtype(fl32(fl32(acc * sx[t]) * sw[c]) + bias[c]),
+   acc = fp32 sum over k of value(qx[t,k]) * value(qw[c,k]) on the fp8 matrix
+   cores (their internal sum is not exactly fp32: measured within ~1e-5 of
+   the sum of |terms|). qx [m, k], qw [n, k] (16-byte aligned), k a positive
+   multiple of 256 (FP8W_ERR_INVALID_VALUE otherwise); bias [n] in out_dtype or
+   NULL; y [m, n] in out_dtype (BF16 / FP16), not overlapping any input.
+   Asynchronous. */
+FP8W_API fp8w_status_t fp8w_gemm_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw,
+                                      const float* sw, const void* bias, int64_t n, void* y, fp8w_dtype_t out_dtype,
+                                      hipStream_t stream);
+
+/* Workspace of fp8w_linear_w8a8: the quantized activations (m*k bytes,
+   rounded up to 256) followed by their m fp32 scales. */
+FP8W_API size_t fp8w_linear_w8a8_workspace_bytes(int64_t m, int64_t k);
+
+/* fp8w_quantize_activations into the workspace (16-byte aligned, at least
+   fp8w_linear_w8a8_workspace_bytes; FP8W_ERR_WORKSPACE otherwise), then
+   fp8w_gemm_w8a8 with out_dtype = act_dtype. Asynchronous. */
+FP8W_API fp8w_status_t fp8w_linear_w8a8(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                        const uint8_t* qw, const float* sw, const void* bias, int64_t n, void* y,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Name of the W8A8 GEMM instance for these sizes; NULL when unsupported. */
+FP8W_API const char* fp8w_linear_w8a8_kernel(int64_t m, int64_t n, int64_t k);
+
+/*
  * Format interop ("B04 - Precision & Quantization", the format table's
  * E4M3FNUZ row, section "Hardware support, and where the vendors diverge", and
  * its trap list: the same bits decode a factor of two apart on gfx942's FNUZ

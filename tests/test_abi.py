@@ -30,7 +30,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fw.load()
     names = declared_symbols()
-    assert len(names) == 18
+    assert len(names) == 23
     for name in names:
         assert hasattr(lib, name), name
         assert name in fw.EXPORTS, name
@@ -298,3 +298,23 @@ def test_fnuz_to_ocp_validation():
     assert f(Q, -1, Y, 0) == fw.ERR_INVALID_VALUE
     assert f(0, 16, Y, 0) == fw.ERR_INVALID_VALUE
     assert f(Q, 64, Q + 8, 0) == fw.ERR_INVALID_VALUE     # partial overlap
+
+
+def test_w8a8_validation():
+    g = fw.fp8w_gemm_w8a8
+    assert g(X, S, 0, 4096, Q, S, 0, 4096, Y, fw.BF16, 0) == fw.SUCCESS
+    assert g(X, S, 64, 4000, Q, S, 0, 4096, Y, fw.BF16, 0) == fw.ERR_INVALID_VALUE    # k % 256 != 0
+    assert g(X, S, 64, 4096, Q, S, 0, 4096, Y, fw.FP32, 0) == fw.ERR_INVALID_VALUE
+    assert g(X + 8, S, 64, 4096, Q, S, 0, 4096, Y, fw.BF16, 0) == fw.ERR_MISALIGNED
+    assert g(X, S, 64, 4096, Q, S, 0, 4096, Q, fw.BF16, 0) == fw.ERR_INVALID_VALUE    # y overlaps q
+    assert fw.fp8w_linear_w8a8_workspace_bytes(100, 256) == 25600 + 400
+    assert fw.fp8w_linear_w8a8_workspace_bytes(3, 256) == 768 + 12
+    lw = fw.fp8w_linear_w8a8
+    assert lw(X, fw.BF16, 64, 4096, Q, S, 0, 4096, Y, 0, 0, 0) == fw.ERR_WORKSPACE
+    assert lw(X, fw.BF16, 64, 4096, Q, S, 0, 4096, Y, WS + 8, 1 << 22, 0) == fw.ERR_MISALIGNED
+    assert lw(X, fw.BF16, 64, 4096, Q, S, 0, 4096, Y, X, 1 << 22, 0) == fw.ERR_INVALID_VALUE  # overlaps x
+    assert fw.fp8w_quantize_activations(X, fw.BF16, 0, 64, Q, S, 0) == fw.SUCCESS
+    assert fw.fp8w_quantize_activations(X, fw.FP32, 4, 64, Q, S, 0) == fw.ERR_INVALID_VALUE
+    assert fw.fp8w_linear_w8a8_kernel(4096, 4096, 4096) == "w8a8_kernel<BN=256,BM=256,NS=4>"
+    assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4096) == "w8a8_kernel<BN=128,BM=128,NS=4>"
+    assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4000) is None

@@ -1,0 +1,89 @@
+"""GPU parity of the W8A8 path (per-token activation quantizer and the e4m3 x
+e4m3 GEMM) against the oracle.
+
+Source: "Skill: Write an FP8 Kernel", "Required reasoning process" steps 2,
+4, 5 and "Correctness requirements". The activation codes and scales must
+equal the oracle's bit for bit (the row quantizer on the rows of x); outputs
+must pass the gate against the oracle's fp64 W8A8 layer on the same codes,
+with the dequantized activations' norm in the gate's second term.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_weight_only_amd as fw
+import oracle
+import workloads
+from parity_util import assert_gate, assert_same_bits, nan_like
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _check(m, n, k, dtype, bias, seed, expect_kernel=None, sampled=False):
+    case = workloads.random_case(seed, m, n, k, dtype, with_bias=bias)
+    q, s = fw.quantize(torch.from_numpy(case.layer.w).to(DEV))
+    x = case.x.to(DEV)
+    qx, sx = fw.quantize_activations(x)
+    qx_ref, sx_ref, st = oracle.quantize_activations(case.x.float().numpy())
+    assert st == 0
+    assert_same_bits(sx.cpu().numpy(), sx_ref, "activation scales")
+    assert_same_bits(qx.cpu().numpy(), qx_ref, "activation codes")
+    if expect_kernel:
+        assert fw.fp8w_linear_w8a8_kernel(m, n, k) == expect_kernel
+    b = None if case.layer.bias is None else case.layer.bias.to(DEV)
+    y = nan_like((m, n), dtype, DEV)
+    fw.linear_w8a8(x, q, s, b, out=y)
+    torch.cuda.synchronize()
+    q_ref, s_ref, _ = oracle.quantize_rows(case.layer.w)
+    b64 = None if case.layer.bias is None else case.layer.bias.double().numpy()
+    xd = oracle.decode(qx_ref) * sx_ref.astype(np.float64)[:, None]
+    amax = oracle.row_amax(case.layer.w)
+    yv = y.double().cpu().numpy()
+    if not sampled:
+        y_ref = oracle.linear_w8a8_f64(qx_ref, sx_ref, q_ref, s_ref, b64)
+        assert_gate(yv, y_ref, xd, amax, f"w8a8 m={m} n={n} k={k}")
+        return yv
+    rows = np.random.default_rng(seed).choice(m, size=min(m, 48), replace=False)
+    y_ref = oracle.linear_w8a8_f64(qx_ref[rows], sx_ref[rows], q_ref, s_ref, b64)
+    assert_gate(yv[rows], y_ref, xd[rows], amax, f"w8a8 m={m} n={n} k={k} (sampled rows)")
+    assert np.all(np.isfinite(yv))
+    return yv
+
+
+CASES = [
+    # (m, n, k, dtype, bias)
+    (64, 128, 256, torch.bfloat16, True),
+    (100, 200, 512, torch.float16, False),      # ragged tiles
+    (130, 300, 1024, torch.bfloat16, True),
+    (33, 1000, 768, torch.float16, True),
+    (1, 64, 256, torch.bfloat16, False),
+    (257, 257, 2048, torch.bfloat16, True),
+]
+
+
+@pytest.mark.parametrize("m,n,k,dtype,bias", CASES)
+def test_w8a8_small(m, n, k, dtype, bias):
+    print(f"w8a8 m={m} n={n} k={k}", flush=True)
+    _check(m, n, k, dtype, bias, m + n + k, "w8a8_kernel<BN=128,BM=128,NS=4>")
+
+
+def test_w8a8_large_tile():
+    print("w8a8 large tile 4096 x 4096 x 1024", flush=True)
+    _check(4096, 4096, 1024, torch.bfloat16, True, 5, "w8a8_kernel<BN=256,BM=256,NS=4>", sampled=True)
+
+
+def test_w8a8_zero_rows_and_scale_zero():
+    """An all-zero token gets scale 0 and codes 0 (no division), so its outputs are the bias."""
+    m, n, k = 40, 96, 512
+    case = workloads.random_case(9, m, n, k, torch.bfloat16)
+    xh = case.x.clone()
+    xh[7] = 0
+    q, s = fw.quantize(torch.from_numpy(case.layer.w).to(DEV))
+    b = case.layer.bias.to(DEV)
+    qx, sx = fw.quantize_activations(xh.to(DEV))
+    assert sx[7].item() == 0.0
+    assert int(qx[7].sum()) == 0
+    y = fw.gemm_w8a8(qx, sx, q, s, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y[7], b)
