@@ -40,7 +40,10 @@ Also reported ("extra"): latency-bound calls (the 1024 x 1024 GEMV and the
 x [22,1024] x [1024,4096] shape the pages time), the skinny sweep (M = 2..32,
 fp16), one decoder block at M = 16 (seven calls, and four with q/k/v and
 gate/up merged; eager and graph-replayed steps), the large shapes and their
-K = 8200 fallback, each with the same cache rotation; the build-time quantize;
+K = 8200 fallback, each with the same cache rotation; the W8A8 layer at
+prefill batches ("w8a8": M = 512 / 2048 / 4096 on the block's three distinct
+shapes, in TFLOP/s against the 5.0 PFLOP/s dense e4m3 matrix-core peak; the
+whole layer, its GEMM and its activation quantizer); the build-time quantize;
 a plain streaming-read reference ("read_ceiling": the library's
 fp8w_stream_read_probe over buffers of each decode weight's size, rotated the
 same way); and the CPU oracle ("cpu_baseline", all host threads and one),
@@ -48,7 +51,7 @@ whose leg also checks this run's GPU results against the oracle results it
 produced.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--spin-ms MS] [--quick]
-                       [--only tiny|skinny|block|large ...] [--reps R]
+                       [--only tiny|skinny|block|large|grouped|w8a8 ...] [--reps R]
 Profile helpers: --trace-summary CSV [--last N], --mfma-summary CSV N K,
 --pmc-summary FETCH_CSV WRITE_CSV.
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -199,6 +202,58 @@ class Call:
         r = fw.load().fp8w_linear(*self.args[copy % len(self.args)], stream)
         if r != 0:
             raise fw.Fp8wError(r, "fp8w_linear")
+
+
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense e4m3 matrix-core peak
+
+
+class W8Call:
+    """One W8A8 call over rotated weight copies: the whole layer
+    (fp8w_linear_w8a8: per-token quantize of x, then the fp8 GEMM), the GEMM
+    alone on x quantized once (fp8w_gemm_w8a8), or the activation quantizer
+    alone (fp8w_quantize_activations)."""
+
+    def __init__(self, layer, x, dev, mode):
+        self.layer, self.x, self.mode = layer, x, mode
+        self.m = x.shape[0]
+        m, n, k = self.m, layer.n, layer.k
+        self.y = torch.empty((m, n), dtype=x.dtype, device=dev)
+        self.ws = torch.empty((fw.fp8w_linear_w8a8_workspace_bytes(m, k),), dtype=torch.uint8, device=dev)
+        self.qx, self.sx = fw.quantize_activations(x)
+        act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
+        lib = fw.load()
+        if mode == "layer":
+            self.fn = lib.fp8w_linear_w8a8
+            self.args = [(x.data_ptr(), act, m, k, q.data_ptr(), s.data_ptr(), 0, n, self.y.data_ptr(),
+                          self.ws.data_ptr(), self.ws.numel()) for q, s in layer.qs]
+        elif mode == "gemm":
+            self.fn = lib.fp8w_gemm_w8a8
+            self.args = [(self.qx.data_ptr(), self.sx.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), 0, n,
+                          self.y.data_ptr(), act) for q, s in layer.qs]
+        else:
+            self.fn = lib.fp8w_quantize_activations
+            self.args = [(x.data_ptr(), act, m, k, self.qx.data_ptr(), self.sx.data_ptr())]
+        self.kernel = fw.fp8w_linear_w8a8_kernel(m, n, k)
+
+    def launch(self, copy, stream):
+        r = self.fn(*self.args[copy % len(self.args)], stream)
+        if r != 0:
+            raise fw.Fp8wError(r, self.fn.__name__)
+
+
+def w8a8_report(call, st):
+    us = st["mean"]
+    m, n, k = call.m, call.layer.n, call.layer.k
+    r = {"layer": call.layer.name, "mode": call.mode, "m": m, "n": n, "k": k, "us_per_call": round(us, 3),
+         "us_p10": round(st["p10"], 3), "us_p90": round(st["p90"], 3)}
+    if call.mode == "quantize_x":
+        moved = 2 * m * k + m * k + 4 * m
+        r.update(gbps=round(moved / (us * 1e-6) / 1e9, 1),
+                 pct_peak=round(100.0 * moved / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2))
+    else:
+        tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+        r.update(kernel=call.kernel, tflops=round(tf, 1), pct_fp8_peak=round(100.0 * tf / FP8_MFMA_PEAK_TFLOPS, 2))
+    return r
 
 
 def spin_up(launch, ms):
@@ -735,7 +790,7 @@ def _short_kernel_name(full):
     name, targs = m.group(1), (m.group(2) or "")
     args = [a.strip() for a in targs[1:-1].split(",")] if targs else []
     keys = {"pipe_kernel": ("XR", "CT", "KP", "NS"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
-            "gemv_kernel": ("R", "U", "NT"), "wpipe_kernel": ("XR", "CT", "NS"),
+            "gemv_kernel": ("R", "U", "NT", "DB"), "wpipe_kernel": ("XR", "CT", "NS"), "w8a8_kernel": ("BN", "BM", "NS"),
             "gemv_grouped_kernel": ("R", "U", "NT"), "pipe_grouped_kernel": ("XR", "CT", "KP", "NS", "G")}.get(name)
     if keys and len(args) == len(keys) + 1:  # first argument is the activation type
         return f"{name}<" + ",".join(f"{kk}={v}" for kk, v in zip(keys, args[1:])) + ">"
@@ -755,7 +810,7 @@ def trace_summary(csv_path, last=None):
     groups = {}
     for r in ours:
         name = _short_kernel_name(r["Kernel_Name"])
-        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])) * int(r.get("Grid_Size_Y") or 1)
         key = (name, wgs, int(r["Workgroup_Size_X"]))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     lines = ["| Kernel | Workgroups x threads | Launches | Mean (us) | p10 (us) | Median (us) | p90 (us) | Min (us) |",
@@ -799,7 +854,7 @@ def mfma_summary(csv_path, n, k):
     print("\n".join(lines))
 
 
-SECTIONS = ("tiny", "skinny", "block", "large", "grouped")
+SECTIONS = ("tiny", "skinny", "block", "large", "grouped", "w8a8")
 
 
 def extra_sections(dev, stream, reps=100, only=None):
@@ -927,6 +982,31 @@ def extra_sections(dev, stream, reps=100, only=None):
             del L
             torch.cuda.empty_cache()
         ex["large"] = lg
+
+    if "w8a8" in want:
+        # prefill: the W8A8 layer on the decoder block's three distinct shapes
+        # at M = 512, 2048, 4096 (bf16), matrix-core bound; weights rotated as
+        # elsewhere; the whole layer, the GEMM alone and the activation quantizer
+        pf = []
+        for i in range(len(workloads.PREFILL_SHAPES)):
+            lw = workloads.prefill_layer(i)
+            n, k = lw.w.shape
+            L = Layer(lw, max(1, math.ceil(ROTATE_BYTES / (n * k))), dev)
+            for m in workloads.PREFILL_MS:
+                x = workloads.prefill_x(i, m).to(dev)
+                for mode in ("layer", "gemm", "quantize_x"):
+                    c = W8Call(L, x, dev, mode)
+                    pf.append(w8a8_report(c, burst(c, max(20, reps // 2), 5, stream, spin_ms=min(SPIN_MS, 50.0))))
+                    r = pf[-1]
+                    if mode == "quantize_x":
+                        log(f"  w8a8 {L.name} m={m} quantize x: {r['us_per_call']:.2f} us {r['gbps']:.0f} GB/s")
+                    else:
+                        log(f"  w8a8 {L.name} m={m} {mode}: {r['us_per_call']:.2f} us {r['tflops']:.0f} TFLOP/s "
+                            f"({r['pct_fp8_peak']:.1f}% of 5.0 PF) [{r['kernel']}]")
+                    del c
+            del L
+            torch.cuda.empty_cache()
+        ex["w8a8"] = pf
     return ex
 
 

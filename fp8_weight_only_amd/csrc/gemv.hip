@@ -13,8 +13,10 @@
 // t of every one of its rows, so a quarter-wave reads 256 contiguous bytes of
 // one row and each load instruction touches the fewest cache lines. The
 // activation chunk a thread needs is the same for its R rows and is read once
-// per pass. U passes are issued back to back before any is consumed; a
-// predicated tail pass handles k that is not a multiple of 16*NT*U. Per-thread
+// per pass. U passes are issued back to back before any is consumed (one
+// group); the decode-sized instance keeps the next group in flight while it
+// consumes the current one (double buffering in registers); a predicated tail
+// pass handles k that is not a multiple of 16*NT*U. Per-thread
 // sums are reduced with cross-lane shuffles, then across the workgroup's
 // waves through LDS in a fixed order (deterministic).
 //
@@ -52,7 +54,36 @@ __device__ __forceinline__ void accum_chunk(const u32x4* code, u32x4 x0, u32x4 x
     }
 }
 
-template <typename A, int R, int U, int NT>
+// U passes of a thread's chunks for R rows, and the activation chunks they
+// share. load() issues every load of the group back to back (the scheduling
+// barrier keeps the compiler from trading loads in flight for registers).
+template <int R, int U>
+struct Group {
+    u32x4 code[U][R];
+    u32x4 xv[U][2];
+    __device__ __forceinline__ void load(const uint8_t* const* qr, const uint16_t* xp, int64_t c0, int nt)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t off = (c0 + (int64_t)nt * u) * 16;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                code[u][r] = load_stream16(qr[r] + off);
+            xv[u][0] = load16(xp + off);
+            xv[u][1] = load16(xp + off + 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    template <typename A>
+    __device__ __forceinline__ void use(float* acc) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            accum_chunk<A, R>(code[u], xv[u][0], xv[u][1], acc);
+    }
+};
+
+template <typename A, int R, int U, int NT, bool DB>
 __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
                                                   const float* __restrict__ scale,
                                                   const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -83,26 +114,37 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
     for (int r = 0; r < R; ++r)
         acc[r] = 0.0f;
 
-    int64_t c0 = 0;
-    for (; c0 + (int64_t)NT * U <= nch; c0 += (int64_t)NT * U) {
-        u32x4 code[U][R];
-        u32x4 xv[U][2];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t off = (c0 + (int64_t)NT * u) * 16;
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                code[u][r] = load_stream16(qr[r] + off);
-            xv[u][0] = load16(xp + off);
-            xv[u][1] = load16(xp + off + 8);
+    // groups of U passes; with DB the next group's loads are issued before the
+    // current group is consumed, so each wave keeps a continuous stream of
+    // requests in flight instead of draining it at every group
+    constexpr int64_t GS = (int64_t)NT * U;
+    const int64_t G = nch / GS;
+    Group<R, U> ga, gb;
+    if constexpr (DB) {
+        int64_t g = 0;
+        if (G > 0) {
+            ga.load(qr, xp, 0, NT);
+            for (; g + 2 < G; g += 2) {
+                gb.load(qr, xp, (g + 1) * GS, NT);
+                ga.template use<A>(acc);
+                ga.load(qr, xp, (g + 2) * GS, NT);
+                gb.template use<A>(acc);
+            }
+            if (g + 1 < G) {
+                gb.load(qr, xp, (g + 1) * GS, NT);
+                ga.template use<A>(acc);
+                gb.template use<A>(acc);
+            } else {
+                ga.template use<A>(acc);
+            }
         }
-        // keep every load of this group ahead of the first use: without this the
-        // scheduler trades loads in flight for registers
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            accum_chunk<A, R>(code[u], xv[u][0], xv[u][1], acc);
+    } else {
+        for (int64_t g = 0; g < G; ++g) {
+            ga.load(qr, xp, g * GS, NT);
+            ga.template use<A>(acc);
+        }
     }
+    int64_t c0 = G * GS;
     for (; c0 < nch; c0 += NT) {  // tail passes: only threads whose chunk exists
         if (c0 + t < nch) {
             const int64_t off = c0 * 16;
@@ -130,22 +172,28 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
     }
 }
 
-template <typename A, int R, int U, int NT>
+template <typename A, int R, int U, int NT, bool DB>
 hipError_t launch_cfg(const void* x, int64_t k, const uint8_t* q, const float* scale, const void* bias, int64_t n,
                       void* y, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + R - 1) / R)), block(NT);
-    hipLaunchKernelGGL((gemv_kernel<A, R, U, NT>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
+    hipLaunchKernelGGL((gemv_kernel<A, R, U, NT, DB>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
                        scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), n, k);
     return hipGetLastError();
 }
 
-// Tile choice, from sweeps on MI355X: two passes in flight per 128-thread
-// workgroup; two rows per workgroup for weights under 96 MB, four above. Per
-// shape, other tiles came within a few percent; a single instance for all the
-// decode-sized layers also means consecutive layers of different shapes run
-// the same code: in a decode step, switching to a second kernel binary cost
-// about 1 us, the refill of each CU's instruction cache.
+// Tile choice, from sweeps on MI355X (kernel durations, weights rotated
+// through 1 GiB). Weights under 96 MB: one-wave workgroups of two rows,
+// two-pass groups, double-buffered; four-row, 128-thread workgroups with
+// single-buffered two-pass groups above. On the long rows of the
+// [4096, 14336] down projection the double-buffered one-wave tile took 11.1-11.5
+// us against 12.3 for the single-buffered 128-thread one (a plain read of the
+// same bytes: 10.1-10.3); on [4096, 4096] and [14336, 4096] the two were
+// within 0.3 us of each other. Double buffering did not help the large
+// weights' four-row tile. A single instance for all the decode-sized layers
+// also means consecutive layers of different shapes run the same code: in a
+// decode step, switching to a second kernel binary cost about 1 us, the refill
+// of each CU's instruction cache.
 constexpr int64_t kLargeWeight = (int64_t)96 << 20;
 
 template <typename A>
@@ -153,15 +201,15 @@ hipError_t launch_typed(const void* x, int64_t k, const uint8_t* q, const float*
                         int64_t n, void* y, hipStream_t stream)
 {
     if (n * k >= kLargeWeight)
-        return launch_cfg<A, 4, 2, 128>(x, k, q, scale, bias, n, y, stream);
-    return launch_cfg<A, 2, 2, 128>(x, k, q, scale, bias, n, y, stream);
+        return launch_cfg<A, 4, 2, 128, false>(x, k, q, scale, bias, n, y, stream);
+    return launch_cfg<A, 2, 2, 64, true>(x, k, q, scale, bias, n, y, stream);
 }
 
 }  // namespace
 
 const char* gemv_kernel_name(int64_t n, int64_t k)
 {
-    return n * k >= kLargeWeight ? "gemv_kernel<R=4,U=2,NT=128>" : "gemv_kernel<R=2,U=2,NT=128>";
+    return n * k >= kLargeWeight ? "gemv_kernel<R=4,U=2,NT=128>" : "gemv_kernel<R=2,U=2,NT=64,DB>";
 }
 
 hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,

@@ -74,8 +74,8 @@ def test_path_selection():
 def test_kernel_names():
     kn = fw.fp8w_linear_kernel
     A = fw.PATH_AUTO
-    assert kn(A, 1, 4096, 4096, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=128>"
-    assert kn(A, 1, 4096, 14336, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=128>"
+    assert kn(A, 1, 4096, 4096, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"
+    assert kn(A, 1, 4096, 14336, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"
     assert kn(A, 1, 28672, 8192, fw.BF16, X, Q) == "gemv_kernel<R=4,U=2,NT=128>"
     assert kn(A, 16, 14336, 4096, fw.FP16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4>"
     assert kn(A, 32, 28672, 8192, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>"

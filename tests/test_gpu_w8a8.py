@@ -87,3 +87,32 @@ def test_w8a8_zero_rows_and_scale_zero():
     y = fw.gemm_w8a8(qx, sx, q, s, b)
     torch.cuda.synchronize()
     assert torch.equal(y[7], b)
+
+
+@pytest.mark.parametrize("i", range(len(workloads.PREFILL_SHAPES)))
+def test_w8a8_prefill_workload(i):
+    """The prefill workload at full size (M = 2048): activation codes and scales
+    bit-exact on every row; outputs of 48 seeded rows against the oracle."""
+    m = 2048
+    lw = workloads.prefill_layer(i)
+    n, k = lw.w.shape
+    print(f"w8a8 prefill {lw.name} m={m}", flush=True)
+    xc = workloads.prefill_x(i, m)
+    q, s = fw.quantize(torch.from_numpy(lw.w).to(DEV))
+    x = xc.to(DEV)
+    qx, sx = fw.quantize_activations(x)
+    qx_ref, sx_ref, st = oracle.quantize_activations(xc.float().numpy())
+    assert st == 0
+    assert_same_bits(sx.cpu().numpy(), sx_ref, "activation scales")
+    assert_same_bits(qx.cpu().numpy(), qx_ref, "activation codes")
+    assert fw.fp8w_linear_w8a8_kernel(m, n, k) is not None
+    y = nan_like((m, n), torch.bfloat16, DEV)
+    fw.linear_w8a8(x, q, s, None, out=y)
+    torch.cuda.synchronize()
+    yv = y.double().cpu().numpy()
+    assert np.all(np.isfinite(yv))
+    q_ref, s_ref, _ = oracle.quantize_rows(lw.w)
+    rows = np.random.default_rng(700 + i).choice(m, size=48, replace=False)
+    y_ref = oracle.linear_w8a8_f64(qx_ref[rows], sx_ref[rows], q_ref, s_ref, None)
+    xd = oracle.decode(qx_ref[rows]) * sx_ref[rows].astype(np.float64)[:, None]
+    assert_gate(yv[rows], y_ref, xd, oracle.row_amax(lw.w), f"w8a8 prefill {lw.name} (sampled rows)")

@@ -27,6 +27,11 @@ quantization; activations are [M, K]):
    x [M,K] bf16 ~ N(0,1) with 0.1 % of entries (seeded) multiplied by 20;
    no bias; M in 1,4,8,32.
 
+Prefill, W8A8 (workload id 7): the decoder block's three distinct shapes q
+[4096,4096], gate [14336,4096] and down [4096,14336], W ~ N(0, 0.02^2), no bias;
+x [M,K] bf16 ~ N(0,1) with 0.1 % of entries (seeded) multiplied by 20, for M
+in 512, 2048, 4096 (batches far above the weight-only kernels' 32 tokens).
+
 Context shape (workload id 6): the one timing of this method the pages print is
 for x [22,1024] times a [1024,4096] weight ("FP8 weight-only (precision:
 fp8_weights)", the Triton variant in "Dequantise in registers"); it is drawn
@@ -50,6 +55,8 @@ LARGE_SHAPES = [(28672, 8192), (8192, 28672)]
 LARGE_FALLBACK_SHAPE = (28672, 8200)
 LARGE_MS = [1, 4, 8, 32]
 PAGES_EXAMPLE = (22, 4096, 1024)  # m, n, k
+PREFILL_SHAPES = [(4096, 4096), (14336, 4096), (4096, 14336)]
+PREFILL_MS = [512, 2048, 4096]
 # the decoder block with the layers that share an input merged into one call:
 # q/k/v, o, gate/up, down (indices into DECODER_BLOCK)
 MERGED_BLOCK = [(0, 1, 2), (3,), (4, 5), (6,)]
@@ -156,6 +163,16 @@ def large_x(shape, m: int) -> torch.Tensor:
     return activations(5, 100 * sub + m, m, k, torch.bfloat16, outlier_frac=0.001)
 
 
+def prefill_layer(i: int) -> Linear:
+    n, k = PREFILL_SHAPES[i]
+    return Linear(f"prefill_{n}x{k}", weight_normal(7, i, n, k, 0.02), None)
+
+
+def prefill_x(i: int, m: int) -> torch.Tensor:
+    n, k = PREFILL_SHAPES[i]
+    return activations(7, 10000 * i + m, m, k, torch.bfloat16, outlier_frac=0.001)
+
+
 def pages_example():
     m, n, k = PAGES_EXAMPLE
     return Case(Linear(f"example_{n}x{k}", weight_normal(6, 0, n, k, 0.02), None),
@@ -173,4 +190,4 @@ def random_case(seed: int, m: int, n: int, k: int, dtype: torch.dtype, with_bias
 
 
 def all_workload_names() -> List[str]:
-    return ["tiny_gemv", "decode", "skinny", "decoder_block", "large"]
+    return ["tiny_gemv", "decode", "skinny", "decoder_block", "large", "prefill"]
