@@ -18,10 +18,21 @@
 // consecutive D rows are four consecutive channels of one token: one 8-byte
 // store per fragment row. A workgroup of four waves owns BN channels x BM
 // tokens; stages of 64 k of both tiles travel HBM/L2 -> LDS by direct
-// global-to-LDS loads through the same NS-stage ring as the weight-only
-// kernels (csrc/ring.hpp). In LDS every 64-byte row keeps its four 16-byte
+// global-to-LDS loads through a four-stage ring (the waits and barrier of
+// csrc/ring.hpp). In LDS every 64-byte row keeps its four 16-byte
 // chunks rotated by row / 4, so the 16 lanes of each ds_read_b128 phase
 // (rows i .. i+15, same chunk) hit 16 distinct bank groups.
+//
+// With one wave per SIMD there is no other wave to hide LDS latency behind, so
+// the ring prefetches fragments: the fragments of stage s + 1 are read into a
+// second register set while the MFMAs of stage s run, one read issued after
+// each MFMA (scheduling-group barriers hold that order). The epilogue's
+// operands (the workgroup's channel scales and biases and its token scales)
+// are fetched once when the workgroup starts and pass through LDS, so the end
+// of a tile waits for no global load. Tiles are dealt so that the workgroups
+// resident on one XCD at a time cover a compact block of the output (rows of
+// four tiles along the tokens), and share more of their operand rows in that
+// XCD's L2.
 #include <stdio.h>
 
 #include "common.hpp"
@@ -98,16 +109,20 @@ struct W8Pipe {
         return v;
     }
 
-    __device__ __forceinline__ void compute(const uint8_t* buf, f32x16* acc) const
+    // fragments of this wave's channel (a) and token (b) tiles from a stage buffer
+    __device__ __forceinline__ void read(const uint8_t* buf, i32x8* a, i32x8* b) const
     {
         const int i = lane & 31;
-        i32x8 a[C::FN], b[C::FM];
 #pragma unroll
         for (int f = 0; f < C::FN; ++f)
             a[f] = frag(buf, wn * (BN / 2) + 32 * f + i);
 #pragma unroll
         for (int f = 0; f < C::FM; ++f)
             b[f] = frag(buf + C::ABYTES, wm * (BM / 2) + 32 * f + i);
+    }
+
+    __device__ __forceinline__ void mma(const i32x8* a, const i32x8* b, f32x16* acc) const
+    {
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
@@ -115,64 +130,176 @@ struct W8Pipe {
                 acc[fn * C::FM + fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     a[fn], b[fm], acc[fn * C::FM + fm], 0, 0, 0, 0, 0, 0);
     }
+
+    // MFMAs on (a, b) while the next stage's fragments are read from nbuf into
+    // (na, nb): one MFMA, then one ds_read_b128, in turn
+    __device__ __forceinline__ void step(const uint8_t* nbuf, const i32x8* a, const i32x8* b, i32x8* na, i32x8* nb,
+                                         f32x16* acc) const
+    {
+        read(nbuf, na, nb);
+        mma(a, b, acc);
+        constexpr int NR = 2 * (C::FN + C::FM);  // ds_read_b128 per stage
+        constexpr int NM = C::FN * C::FM;
+        constexpr int PER = NR / NM > 0 ? NR / NM : 1;
+#pragma unroll
+        for (int j = 0; j < NM; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (j * PER < NR)
+                __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);  // then LDS reads
+        }
+    }
 };
 
+// Tile (tn, tm) of workgroup (blockIdx.x, blockIdx.y). Workgroups are dealt
+// to the 8 XCDs in turn by linear id L: XCD x = L % 8 is given the contiguous
+// range of tile ids that starts at x * (T / 8) + min(x, T % 8), walked in the
+// order that fills groups of GM tile rows (GM token tiles x all channel
+// tiles) column by column, so the tiles one XCD holds at a time form a
+// GM x (32 / GM) block. A bijection of [0, T).
+template <int GM>
+__device__ __forceinline__ void tile_of(int64_t& tn, int64_t& tm)
+{
+    const int64_t TN = gridDim.x, TM = gridDim.y, T = TN * TM;
+    const int64_t L = blockIdx.x + TN * blockIdx.y;
+    const int64_t xcd = L % 8, loc = L / 8, q = T / 8, r = T % 8;
+    const int64_t id = xcd * q + (xcd < r ? xcd : r) + loc;
+    const int64_t grp = id / (GM * TN), first = grp * GM;
+    const int64_t gs = TM - first < GM ? TM - first : GM;
+    const int64_t w = id - grp * GM * TN;
+    tm = first + w % gs;
+    tn = w / gs;
+}
+
 // y[t, c] = out(fl32(fl32(acc * scale_x[t]) * scale_w[c]) + bias[c]).
-// Requires k % (64 * NS) == 0; qw, qx 16-byte aligned.
-template <typename A, int BN, int BM, int NS>
+// Requires k % 256 == 0 (k / 64 stages, a multiple of the 4-stage ring);
+// qw, qx 16-byte aligned.
+template <typename A, int BN, int BM>
 __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ qx, const float* __restrict__ sx,
                                                   const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                                   const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
                                                   int64_t m, int64_t n, int64_t k)
 {
+    constexpr int NS = 4;
     using P = W8Pipe<BN, BM, NS>;
     using C = typename P::C;
+    constexpr int L = C::LOADS;
+    static_assert(BN <= 256 && BM <= 256, "one epilogue operand per thread");
     __shared__ __attribute__((aligned(1024))) uint8_t b0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t b1[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t b2[NS > 2 ? C::STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t b3[NS > 3 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t b2[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t b3[C::STAGE];
+    __shared__ __attribute__((aligned(16))) float e_sw[BN];
+    __shared__ __attribute__((aligned(16))) uint16_t e_bias[BN];
+    __shared__ __attribute__((aligned(16))) float e_sx[BM];
 
+    int64_t tn, tm;
+    tile_of<4>(tn, tm);
     P p;
     p.qw = qw;
     p.qx = qx;
     p.n = n;
     p.m = m;
     p.k = k;
-    p.n0 = (int64_t)blockIdx.x * BN;
-    p.m0 = (int64_t)blockIdx.y * BM;
+    p.n0 = tn * BN;
+    p.m0 = tm * BM;
     p.lane = threadIdx.x & (kWave - 1);
     p.wave = threadIdx.x / kWave;
     p.wn = p.wave & 1;
     p.wm = p.wave >> 1;
+
+    // epilogue operands, one per thread, fetched before the ring starts and
+    // stored to LDS once the ring's first wait (which covers them: loads
+    // complete in order) has passed
+    const int tt = threadIdx.x;
+    float r_sw = 0.0f, r_sx = 0.0f;
+    uint16_t r_bias = 0;
+    if (tt < BN) {
+        const int64_t c = p.n0 + tt < n ? p.n0 + tt : n - 1;
+        r_sw = sw[c];
+        r_bias = bias_bits(bias, c);
+    }
+    if (tt < BM)
+        r_sx = sx[p.m0 + tt < m ? p.m0 + tt : m - 1];
 
     f32x16 acc[C::FN * C::FM];
 #pragma unroll
     for (int f = 0; f < C::FN * C::FM; ++f)
         acc[f] = f32x16{0.0f};
 
-    run_ring<NS, C::LOADS>(p, k / 64, b0, b1, b2, b3, acc);
+    // The ring: stage s + 3 is issued at step s into the buffer of stage s - 1,
+    // whose fragments were read during step s - 2; step s waits for stage
+    // s + 1 (the stages in flight are then s + 2 and the one just issued),
+    // runs stage s's MFMAs and reads stage s + 1's fragments.
+    i32x8 a0[C::FN], x0[C::FM], a1[C::FN], x1[C::FM];
+    const int64_t S = k / 64;
+    p.issue(0, b0);
+    p.issue(1, b1);
+    p.issue(2, b2);
+    wait_loads_at_most<2 * L>();
+    stage_barrier();
+    if (tt < BN) {
+        e_sw[tt] = r_sw;
+        e_bias[tt] = r_bias;
+    }
+    if (tt < BM)
+        e_sx[tt] = r_sx;
+    p.read(b0, a0, x0);
+    int64_t s = 0;
+    for (; s < S - 4; s += 4) {
+        wait_loads_at_most<L>();
+        stage_barrier();
+        p.issue(s + 3, b3);
+        p.step(b1, a0, x0, a1, x1, acc);
+        wait_loads_at_most<L>();
+        stage_barrier();
+        p.issue(s + 4, b0);
+        p.step(b2, a1, x1, a0, x0, acc);
+        wait_loads_at_most<L>();
+        stage_barrier();
+        p.issue(s + 5, b1);
+        p.step(b3, a0, x0, a1, x1, acc);
+        wait_loads_at_most<L>();
+        stage_barrier();
+        p.issue(s + 6, b2);
+        p.step(b0, a1, x1, a0, x0, acc);
+    }
+    // the last four stages: S - 1 is the last one issued
+    wait_loads_at_most<L>();
+    stage_barrier();
+    p.issue(s + 3, b3);
+    p.step(b1, a0, x0, a1, x1, acc);
+    wait_loads_at_most<L>();
+    stage_barrier();
+    p.step(b2, a1, x1, a0, x0, acc);
+    wait_loads_at_most<0>();
+    stage_barrier();
+    p.step(b3, a0, x0, a1, x1, acc);
+    p.mma(a1, x1, acc);
+    __syncthreads();
 
-    // epilogue: lane (i, h) holds channels c0 + 8j + 4h + r (r = 0..3) of token t
+    // lane (i, h) holds channels c0 + 8j + 4h + r (r = 0..3) of token t
     const int i = p.lane & 31, h = p.lane >> 5;
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
-        const int64_t t = p.m0 + p.wm * (BM / 2) + 32 * fm + i;
+        const int tl = p.wm * (BM / 2) + 32 * fm + i;
+        const int64_t t = p.m0 + tl;
         if (t >= m)
             continue;
-        const float st = sx[t];
+        const float st = e_sx[tl];
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
             const f32x16 d = acc[fn * C::FM + fm];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t c0 = p.n0 + p.wn * (BN / 2) + 32 * fn + 8 * j + 4 * h;
+                const int cl = p.wn * (BN / 2) + 32 * fn + 8 * j + 4 * h;
+                const int64_t c0 = p.n0 + cl;
+                const f32x4 s4 = *reinterpret_cast<const f32x4*>(&e_sw[cl]);
+                const u32x2 b4 = *reinterpret_cast<const u32x2*>(&e_bias[cl]);
+                const float bf[4] = {A::lo_f32(b4.x), A::hi_f32(b4.x), A::lo_f32(b4.y), A::hi_f32(b4.y)};
                 uint16_t o[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t c = c0 + r < n ? c0 + r : n - 1;
-                    const float v = (d[4 * j + r] * st) * sw[c];
-                    o[r] = A::from_f32(v + A::to_f32(bias_bits(bias, c)));
-                }
+                for (int r = 0; r < 4; ++r)
+                    o[r] = A::from_f32((d[4 * j + r] * st) * s4[r] + bf[r]);
                 uint16_t* dst = y + t * n + c0;
                 if (c0 + 3 < n && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
                     u32x2 pk;
@@ -190,12 +317,12 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ q
     }
 }
 
-template <typename A, int BN, int BM, int NS>
+template <typename A, int BN, int BM>
 hipError_t launch_w8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw, const float* sw,
                      const void* bias, int64_t n, void* y, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(256);
-    hipLaunchKernelGGL((w8a8_kernel<A, BN, BM, NS>), grid, block, 0, stream, qx, sx, qw, sw,
+    hipLaunchKernelGGL((w8a8_kernel<A, BN, BM>), grid, block, 0, stream, qx, sx, qw, sw,
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
     return hipGetLastError();
 }
@@ -215,17 +342,17 @@ hipError_t launch_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k,
         return hipSuccess;
     const bool large = w8a8_large_tile(m, n);
     if (out == Act::BF16)
-        return large ? launch_w8<Bf16, 256, 256, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream)
-                     : launch_w8<Bf16, 128, 128, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return large ? launch_w8<Bf16, 256, 256>(qx, sx, m, k, qw, sw, bias, n, y, stream)
+                     : launch_w8<Bf16, 128, 128>(qx, sx, m, k, qw, sw, bias, n, y, stream);
     if (out == Act::FP16)
-        return large ? launch_w8<F16, 256, 256, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream)
-                     : launch_w8<F16, 128, 128, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return large ? launch_w8<F16, 256, 256>(qx, sx, m, k, qw, sw, bias, n, y, stream)
+                     : launch_w8<F16, 128, 128>(qx, sx, m, k, qw, sw, bias, n, y, stream);
     return hipErrorInvalidValue;
 }
 
 const char* w8a8_kernel_name(int64_t m, int64_t n)
 {
-    return w8a8_large_tile(m, n) ? "w8a8_kernel<BN=256,BM=256,NS=4>" : "w8a8_kernel<BN=128,BM=128,NS=4>";
+    return w8a8_large_tile(m, n) ? "w8a8_kernel<BN=256,BM=256>" : "w8a8_kernel<BN=128,BM=128>";
 }
 
 }  // namespace fp8w
