@@ -308,9 +308,12 @@ fp8w_status_t fp8w_quantize_activations(const void* x, fp8w_dtype_t act_dtype, i
     return hip_status(fp8w::launch_quantize(x, act_of(act_dtype), m, k, qx, sx, stream));
 }
 
-fp8w_status_t fp8w_gemm_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw,
-                             const float* sw, const void* bias, int64_t n, void* y, fp8w_dtype_t out_dtype,
-                             hipStream_t stream)
+// Every check of the W8A8 GEMM's arguments, run before anything is enqueued
+// (fp8w_linear_w8a8 runs it on its workspace pointers before it launches the
+// activation quantizer).
+static fp8w_status_t check_gemm_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw,
+                                     const float* sw, const void* bias, int64_t n, const void* y,
+                                     fp8w_dtype_t out_dtype)
 {
     if (!valid_act(out_dtype) || !sizes_ok(m, n, k) || k == 0 || k % 256 != 0)
         return FP8W_ERR_INVALID_VALUE;
@@ -326,6 +329,16 @@ fp8w_status_t fp8w_gemm_w8a8(const uint8_t* qx, const float* sx, int64_t m, int6
         overlap(y, ybytes, sx, (size_t)m * 4) || overlap(y, ybytes, sw, (size_t)n * 4) ||
         overlap(y, ybytes, bias, bias ? (size_t)n * 2 : 0))
         return FP8W_ERR_INVALID_VALUE;
+    return FP8W_SUCCESS;
+}
+
+fp8w_status_t fp8w_gemm_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw,
+                             const float* sw, const void* bias, int64_t n, void* y, fp8w_dtype_t out_dtype,
+                             hipStream_t stream)
+{
+    const fp8w_status_t st = check_gemm_w8a8(qx, sx, m, k, qw, sw, bias, n, y, out_dtype);
+    if (st != FP8W_SUCCESS || m == 0 || n == 0)
+        return st;
     return hip_status(fp8w::launch_w8a8(qx, sx, m, k, qw, sw, bias, n, y, act_of(out_dtype), stream));
 }
 
@@ -358,7 +371,10 @@ fp8w_status_t fp8w_linear_w8a8(const void* x, fp8w_dtype_t act_dtype, int64_t m,
         return FP8W_ERR_INVALID_VALUE;
     uint8_t* qx = static_cast<uint8_t*>(workspace);
     float* sx = reinterpret_cast<float*>(qx + (need - (size_t)m * 4));
-    fp8w_status_t st = fp8w_quantize_activations(x, act_dtype, m, k, qx, sx, stream);
+    fp8w_status_t st = check_gemm_w8a8(qx, sx, m, k, qw, sw, bias, n, y, act_dtype);
+    if (st != FP8W_SUCCESS)
+        return st;
+    st = fp8w_quantize_activations(x, act_dtype, m, k, qx, sx, stream);
     if (st != FP8W_SUCCESS)
         return st;
     return fp8w_gemm_w8a8(qx, sx, m, k, qw, sw, bias, n, y, act_dtype, stream);

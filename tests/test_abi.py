@@ -313,6 +313,12 @@ def test_w8a8_validation():
     assert lw(X, fw.BF16, 64, 4096, Q, S, 0, 4096, Y, 0, 0, 0) == fw.ERR_WORKSPACE
     assert lw(X, fw.BF16, 64, 4096, Q, S, 0, 4096, Y, WS + 8, 1 << 22, 0) == fw.ERR_MISALIGNED
     assert lw(X, fw.BF16, 64, 4096, Q, S, 0, 4096, Y, X, 1 << 22, 0) == fw.ERR_INVALID_VALUE  # overlaps x
+    # the GEMM's arguments are checked before the activation quantizer is enqueued
+    assert lw(X, fw.BF16, 64, 4096, 0, S, 0, 4096, Y, WS, 1 << 22, 0) == fw.ERR_INVALID_VALUE     # no weight codes
+    assert lw(X, fw.BF16, 64, 4096, Q, 0, 0, 4096, Y, WS, 1 << 22, 0) == fw.ERR_INVALID_VALUE     # no weight scales
+    assert lw(X, fw.BF16, 64, 4096, Q + 8, S, 0, 4096, Y, WS, 1 << 22, 0) == fw.ERR_MISALIGNED
+    assert lw(X, fw.BF16, 64, 4096, Q, S + 2, 0, 4096, Y, WS, 1 << 22, 0) == fw.ERR_MISALIGNED
+    assert lw(X, fw.BF16, 64, 4096, Q, S, 0, 4096, Q, WS, 1 << 22, 0) == fw.ERR_INVALID_VALUE     # y overlaps q
     assert fw.fp8w_quantize_activations(X, fw.BF16, 0, 64, Q, S, 0) == fw.SUCCESS
     assert fw.fp8w_quantize_activations(X, fw.FP32, 4, 64, Q, S, 0) == fw.ERR_INVALID_VALUE
     assert fw.fp8w_linear_w8a8_kernel(4096, 4096, 4096) == "w8a8_kernel<BN=256,BM=256>"
