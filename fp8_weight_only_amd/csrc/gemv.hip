@@ -17,8 +17,8 @@
 // group); the decode-sized instance keeps the next group in flight while it
 // consumes the current one (double buffering in registers); a predicated tail
 // pass handles k that is not a multiple of 16*NT*U. Per-thread
-// sums are reduced with cross-lane shuffles, then across the workgroup's
-// waves through LDS in a fixed order (deterministic).
+// sums are reduced with cross-lane shuffles, then (workgroups of several
+// waves) across the waves through LDS in a fixed order (deterministic).
 //
 // Many small workgroups (R rows each) keep every CU streaming until the end
 // of the matrix; measured on MI355X, this shape runs within a few percent of a
@@ -156,6 +156,20 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
         }
     }
 
+    if constexpr (NW == 1) {
+        // one wave: after the butterfly every lane holds every row's sum, and
+        // lane r stores row r (no LDS, no barrier)
+        float tot = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float s = wave_sum(acc[r]);
+            if (t == r)
+                tot = s;
+        }
+        if (t < R && row0 + t < n)
+            y[row0 + t] = epilogue<A>(tot, sc, bi);
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const float s = wave_sum(acc[r]);
