@@ -35,9 +35,71 @@ namespace {
 
 // ---------------------------------------------------------------- M = 1
 // The per-channel GEMV's layout (R rows per NT-thread workgroup, thread t reads
-// chunk t of each row, U passes in flight), with a per-chunk partial sum and
-// the chunk's group scale loaded beside its codes.
-template <typename A, int R, int U, int NT>
+// chunk t of each row, groups of U passes in flight, double-buffered with DB),
+// with a per-chunk partial sum and the chunk's group scale loaded beside its
+// codes.
+template <typename A, int R>
+__device__ __forceinline__ void grouped_chunk(const u32x4* code, const float* sc, u32x4 x0, u32x4 x1, float* acc)
+{
+    float xf[16];
+    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        xf[2 * e + 0] = A::lo_f32(xw[e]);
+        xf[2 * e + 1] = A::hi_f32(xw[e]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t cw[4] = {code[r].x, code[r].y, code[r].z, code[r].w};
+        float dot = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            float w0, w1, w2, w3;
+            decode4_f32(cw[d], w0, w1, w2, w3);
+            dot = __builtin_fmaf(xf[4 * d + 0], w0, dot);
+            dot = __builtin_fmaf(xf[4 * d + 1], w1, dot);
+            dot = __builtin_fmaf(xf[4 * d + 2], w2, dot);
+            dot = __builtin_fmaf(xf[4 * d + 3], w3, dot);
+        }
+        acc[r] = __builtin_fmaf(sc[r], dot, acc[r]);
+    }
+}
+
+// U passes of a thread's chunks for R rows, their group scales and the
+// activation chunks they share; load() issues all of it back to back.
+template <int R, int U>
+struct GGroup {
+    u32x4 code[U][R];
+    u32x4 xv[U][2];
+    float sc[U][R];
+    __device__ __forceinline__ void load(const uint8_t* const* qr, const float* const* sr, const uint16_t* xp,
+                                         int64_t c0, int t, int nt, int lg_chunks)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + (int64_t)nt * u;
+            const int64_t off = c * 16;
+            const int64_t gi = (c + t) >> lg_chunks;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                code[u][r] = load_stream16(qr[r] + off);
+                sc[u][r] = sr[r][gi];
+            }
+            xv[u][0] = load16(xp + off);
+            xv[u][1] = load16(xp + off + 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    template <typename A>
+    __device__ __forceinline__ void use(float* acc) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            grouped_chunk<A, R>(code[u], sc[u], xv[u][0], xv[u][1], acc);
+    }
+};
+
+template <typename A, int R, int U, int NT, bool DB>
 __global__ __launch_bounds__(NT) void gemv_grouped_kernel(const uint16_t* __restrict__ x,
                                                           const uint8_t* __restrict__ q,
                                                           const float* __restrict__ scale,
@@ -71,55 +133,34 @@ __global__ __launch_bounds__(NT) void gemv_grouped_kernel(const uint16_t* __rest
     for (int r = 0; r < R; ++r)
         acc[r] = 0.0f;
 
-    auto chunk = [&](const u32x4* code, const float* sc, u32x4 x0, u32x4 x1) {
-        float xf[16];
-        const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            xf[2 * e + 0] = A::lo_f32(xw[e]);
-            xf[2 * e + 1] = A::hi_f32(xw[e]);
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t cw[4] = {code[r].x, code[r].y, code[r].z, code[r].w};
-            float dot = 0.0f;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                float w0, w1, w2, w3;
-                decode4_f32(cw[d], w0, w1, w2, w3);
-                dot = __builtin_fmaf(xf[4 * d + 0], w0, dot);
-                dot = __builtin_fmaf(xf[4 * d + 1], w1, dot);
-                dot = __builtin_fmaf(xf[4 * d + 2], w2, dot);
-                dot = __builtin_fmaf(xf[4 * d + 3], w3, dot);
+    constexpr int64_t GS = (int64_t)NT * U;
+    const int64_t G = nch / GS;
+    GGroup<R, U> ga, gb;
+    if constexpr (DB) {
+        int64_t g = 0;
+        if (G > 0) {
+            ga.load(qr, sr, xp, 0, t, NT, lg_chunks);
+            for (; g + 2 < G; g += 2) {
+                gb.load(qr, sr, xp, (g + 1) * GS, t, NT, lg_chunks);
+                ga.template use<A>(acc);
+                ga.load(qr, sr, xp, (g + 2) * GS, t, NT, lg_chunks);
+                gb.template use<A>(acc);
             }
-            acc[r] = __builtin_fmaf(sc[r], dot, acc[r]);
-        }
-    };
-
-    int64_t c0 = 0;
-    for (; c0 + (int64_t)NT * U <= nch; c0 += (int64_t)NT * U) {
-        u32x4 code[U][R];
-        u32x4 xv[U][2];
-        float sc[U][R];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c = c0 + (int64_t)NT * u;
-            const int64_t off = c * 16;
-            const int64_t gi = (c + t) >> lg_chunks;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                code[u][r] = load_stream16(qr[r] + off);
-                sc[u][r] = sr[r][gi];
+            if (g + 1 < G) {
+                gb.load(qr, sr, xp, (g + 1) * GS, t, NT, lg_chunks);
+                ga.template use<A>(acc);
+                gb.template use<A>(acc);
+            } else {
+                ga.template use<A>(acc);
             }
-            xv[u][0] = load16(xp + off);
-            xv[u][1] = load16(xp + off + 8);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            chunk(code[u], sc[u], xv[u][0], xv[u][1]);
+    } else {
+        for (int64_t g = 0; g < G; ++g) {
+            ga.load(qr, sr, xp, g * GS, t, NT, lg_chunks);
+            ga.template use<A>(acc);
+        }
     }
-    for (; c0 < nch; c0 += NT) {
+    for (int64_t c0 = G * GS; c0 < nch; c0 += NT) {  // tail passes
         if (c0 + t < nch) {
             const int64_t off = c0 * 16;
             const int64_t gi = (c0 + t) >> lg_chunks;
@@ -130,10 +171,23 @@ __global__ __launch_bounds__(NT) void gemv_grouped_kernel(const uint16_t* __rest
                 code[r] = load_stream16(qr[r] + off);
                 sc[r] = sr[r][gi];
             }
-            chunk(code, sc, load16(xp + off), load16(xp + off + 8));
+            grouped_chunk<A, R>(code, sc, load16(xp + off), load16(xp + off + 8), acc);
         }
     }
 
+    if constexpr (NW == 1) {
+        // one wave: every lane holds every row's sum after the butterfly
+        float tot = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float s = wave_sum(acc[r]);
+            if (t == r)
+                tot = s;
+        }
+        if (t < R && row0 + t < n)
+            y[row0 + t] = epilogue<A>(tot, 1.0f, bi);
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const float s = wave_sum(acc[r]);
@@ -534,14 +588,13 @@ hipError_t launch_grouped_typed(int path, const void* x, int64_t m, int64_t k, c
                                 const float* scale, int lg, const void* bias, int64_t n, void* y,
                                 hipStream_t stream)
 {
-    if (path == 0) {
-        const dim3 block(128);
+    if (path == 0) {  // the per-channel GEMV's tiles (one-wave double-buffered below 96 MB)
         if (n * k >= ((int64_t)96 << 20)) {
-            hipLaunchKernelGGL((gemv_grouped_kernel<A, 4, 2, 128>), dim3((unsigned)((n + 3) / 4)), block, 0,
+            hipLaunchKernelGGL((gemv_grouped_kernel<A, 4, 2, 128, false>), dim3((unsigned)((n + 3) / 4)), dim3(128), 0,
                                stream, static_cast<const uint16_t*>(x), q, scale,
                                static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), n, k, lg - 4);
         } else {
-            hipLaunchKernelGGL((gemv_grouped_kernel<A, 2, 2, 128>), dim3((unsigned)((n + 1) / 2)), block, 0,
+            hipLaunchKernelGGL((gemv_grouped_kernel<A, 2, 2, 64, true>), dim3((unsigned)((n + 1) / 2)), dim3(64), 0,
                                stream, static_cast<const uint16_t*>(x), q, scale,
                                static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), n, k, lg - 4);
         }
@@ -587,7 +640,7 @@ const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k)
     static thread_local char name[96];
     if (path == 0)
         return n * k >= ((int64_t)96 << 20) ? "gemv_grouped_kernel<R=4,U=2,NT=128>"
-                                            : "gemv_grouped_kernel<R=2,U=2,NT=128>";
+                                            : "gemv_grouped_kernel<R=2,U=2,NT=64,DB>";
     if (path == 1) {
         const GroupedPlan p = plan_grouped(m, n, k);
         if (p.pipe) {

@@ -252,7 +252,7 @@ def test_grouped_paths_and_kernel_names():
     assert gp(1, 4096, 4160, 32, fw.BF16, X, Q) == fw.PATH_FALLBACK      # k % 256 != 0
     assert gp(1, 4096, 4096, 48, fw.BF16, X, Q) == -1                    # group not 32/64/128
     assert gp(1, 4096, 4000, 64, fw.BF16, X, Q) == -1                    # group does not divide k
-    assert gk(A, 1, 4096, 4096, 32, fw.BF16, X, Q) == "gemv_grouped_kernel<R=2,U=2,NT=128>"
+    assert gk(A, 1, 4096, 4096, 32, fw.BF16, X, Q) == "gemv_grouped_kernel<R=2,U=2,NT=64,DB>"
     assert gk(A, 1, 28672, 8192, 128, fw.BF16, X, Q) == "gemv_grouped_kernel<R=4,U=2,NT=128>"
     assert gk(A, 16, 14336, 4096, 32, fw.FP16, X, Q) == "pipe_grouped_kernel<XR=16,CT=4,KP=1,NS=4>"
     assert gk(A, 32, 28672, 4096, 32, fw.BF16, X, Q) == "pipe_grouped_kernel<XR=32,CT=4,KP=1,NS=2>"

@@ -119,7 +119,7 @@ GEMV = [
 def test_grouped_gemv(n, k, g, dtype, bias):
     print(f"grouped gemv n={n} k={k} g={g}", flush=True)
     w, x, b = _case(n + k, 1, n, k, g, dtype, bias)
-    _run_and_check(w, x, b, g, fw.PATH_AUTO, "gemv_grouped_kernel<R=2,U=2,NT=128>")
+    _run_and_check(w, x, b, g, fw.PATH_AUTO, "gemv_grouped_kernel<R=2,U=2,NT=64,DB>")
 
 
 SKINNY = [
