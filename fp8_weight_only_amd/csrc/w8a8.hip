@@ -17,9 +17,9 @@
 // A operand (channels) and the token rows the B operand, so a lane's four
 // consecutive D rows are four consecutive channels of one token: one 8-byte
 // store per fragment row. A workgroup of four waves owns BN channels x BM
-// tokens; stages of 64 k of both tiles travel HBM/L2 -> LDS by direct
-// global-to-LDS loads through a four-stage ring (the waits and barrier of
-// csrc/ring.hpp). In LDS every 64-byte row keeps its four 16-byte
+// tokens (256 x 256 down to 128 x 64, by the shape); stages of 64 k of both
+// tiles travel HBM/L2 -> LDS by direct global-to-LDS loads through a
+// four-stage ring (the waits and barrier of csrc/ring.hpp). In LDS every 64-byte row keeps its four 16-byte
 // chunks rotated by row / 4, so the 16 lanes of each ds_read_b128 phase
 // (rows i .. i+15, same chunk) hit 16 distinct bank groups.
 //
@@ -327,10 +327,40 @@ hipError_t launch_w8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, c
     return hipGetLastError();
 }
 
-// 256 x 256 tiles when they still give a workgroup per CU, 128 x 128 otherwise.
-bool w8a8_large_tile(int64_t m, int64_t n)
+// Tile choice, from a sweep of four tile shapes on the prefill shapes
+// (M = 512 / 2048 / 4096 on [4096, 4096], [14336, 4096], [4096, 14336]): the
+// largest tile that still gives at least 224 workgroups (7/8 of the CUs, one
+// workgroup per CU), in the order 256 x 256, 256 x 128, 128 x 128, 128 x 64
+// (channels x tokens); the smallest below that. It picked the fastest or
+// within 1 % of the fastest shape in all nine cases.
+struct W8Tile {
+    int bn, bm;
+};
+
+W8Tile w8a8_tile(int64_t m, int64_t n)
 {
-    return ((n + 255) / 256) * ((m + 255) / 256) >= 256;
+    auto tiles = [&](int64_t bn, int64_t bm) { return ((n + bn - 1) / bn) * ((m + bm - 1) / bm); };
+    if (tiles(256, 256) >= 224)
+        return {256, 256};
+    if (tiles(256, 128) >= 224)
+        return {256, 128};
+    if (tiles(128, 128) >= 224)
+        return {128, 128};
+    return {128, 64};
+}
+
+template <typename A>
+hipError_t launch_w8_typed(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw,
+                           const float* sw, const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    const W8Tile t = w8a8_tile(m, n);
+    if (t.bn == 256 && t.bm == 256)
+        return launch_w8<A, 256, 256>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+    if (t.bn == 256)
+        return launch_w8<A, 256, 128>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+    if (t.bm == 128)
+        return launch_w8<A, 128, 128>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+    return launch_w8<A, 128, 64>(qx, sx, m, k, qw, sw, bias, n, y, stream);
 }
 
 }  // namespace
@@ -340,19 +370,23 @@ hipError_t launch_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k,
 {
     if (m == 0 || n == 0)
         return hipSuccess;
-    const bool large = w8a8_large_tile(m, n);
     if (out == Act::BF16)
-        return large ? launch_w8<Bf16, 256, 256>(qx, sx, m, k, qw, sw, bias, n, y, stream)
-                     : launch_w8<Bf16, 128, 128>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return launch_w8_typed<Bf16>(qx, sx, m, k, qw, sw, bias, n, y, stream);
     if (out == Act::FP16)
-        return large ? launch_w8<F16, 256, 256>(qx, sx, m, k, qw, sw, bias, n, y, stream)
-                     : launch_w8<F16, 128, 128>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return launch_w8_typed<F16>(qx, sx, m, k, qw, sw, bias, n, y, stream);
     return hipErrorInvalidValue;
 }
 
 const char* w8a8_kernel_name(int64_t m, int64_t n)
 {
-    return w8a8_large_tile(m, n) ? "w8a8_kernel<BN=256,BM=256>" : "w8a8_kernel<BN=128,BM=128>";
+    const W8Tile t = w8a8_tile(m, n);
+    if (t.bn == 256 && t.bm == 256)
+        return "w8a8_kernel<BN=256,BM=256>";
+    if (t.bn == 256)
+        return "w8a8_kernel<BN=256,BM=128>";
+    if (t.bm == 128)
+        return "w8a8_kernel<BN=128,BM=128>";
+    return "w8a8_kernel<BN=128,BM=64>";
 }
 
 }  // namespace fp8w

@@ -322,5 +322,8 @@ def test_w8a8_validation():
     assert fw.fp8w_quantize_activations(X, fw.BF16, 0, 64, Q, S, 0) == fw.SUCCESS
     assert fw.fp8w_quantize_activations(X, fw.FP32, 4, 64, Q, S, 0) == fw.ERR_INVALID_VALUE
     assert fw.fp8w_linear_w8a8_kernel(4096, 4096, 4096) == "w8a8_kernel<BN=256,BM=256>"
-    assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4096) == "w8a8_kernel<BN=128,BM=128>"
+    assert fw.fp8w_linear_w8a8_kernel(2048, 4096, 4096) == "w8a8_kernel<BN=256,BM=128>"
+    assert fw.fp8w_linear_w8a8_kernel(1024, 4096, 4096) == "w8a8_kernel<BN=128,BM=128>"
+    assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4096) == "w8a8_kernel<BN=128,BM=64>"
+    assert fw.fp8w_linear_w8a8_kernel(512, 14336, 4096) == "w8a8_kernel<BN=256,BM=128>"
     assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4000) is None

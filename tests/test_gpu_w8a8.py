@@ -65,7 +65,17 @@ CASES = [
 @pytest.mark.parametrize("m,n,k,dtype,bias", CASES)
 def test_w8a8_small(m, n, k, dtype, bias):
     print(f"w8a8 m={m} n={n} k={k}", flush=True)
-    _check(m, n, k, dtype, bias, m + n + k, "w8a8_kernel<BN=128,BM=128>")
+    _check(m, n, k, dtype, bias, m + n + k, "w8a8_kernel<BN=128,BM=64>")
+
+
+@pytest.mark.parametrize("m,n,k,dtype,tile", [
+    (2048, 4096, 512, torch.bfloat16, "w8a8_kernel<BN=256,BM=128>"),
+    (1000, 4000, 768, torch.float16, "w8a8_kernel<BN=128,BM=128>"),     # ragged edges of the 128 x 128 tile
+    (2000, 4100, 256, torch.float16, "w8a8_kernel<BN=256,BM=128>"),     # ragged edges of the 256 x 128 tile
+])
+def test_w8a8_mid_tiles(m, n, k, dtype, tile):
+    print(f"w8a8 m={m} n={n} k={k} {tile}", flush=True)
+    _check(m, n, k, dtype, True, m + n + k, tile, sampled=True)
 
 
 def test_w8a8_large_tile():
