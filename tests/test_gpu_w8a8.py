@@ -126,3 +126,50 @@ def test_w8a8_prefill_workload(i):
     y_ref = oracle.linear_w8a8_f64(qx_ref[rows], sx_ref[rows], q_ref, s_ref, None)
     xd = oracle.decode(qx_ref[rows]) * sx_ref[rows].astype(np.float64)[:, None]
     assert_gate(yv[rows], y_ref, xd, oracle.row_amax(lw.w), f"w8a8 prefill {lw.name} (sampled rows)")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_w8a8_every_code_pair_exact(out_dtype):
+    """One-hot codes and unit scales: y[a, b] = value(a) * value(b) from a single
+    product, for every pair of finite codes (254 x 254). Each product has at most
+    8 significant bits and lies in [2^-18, 448^2], so it is exact in bf16 (and in
+    fp16 where it is in range), and the GPU must match it exactly."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    m = n = len(codes)
+    k = 256
+    qx = np.zeros((m, k), dtype=np.uint8)
+    qw = np.zeros((n, k), dtype=np.uint8)
+    qx[:, 0] = codes
+    qw[:, 0] = codes
+    ones_m = torch.ones(m, dtype=torch.float32, device=DEV)
+    ones_n = torch.ones(n, dtype=torch.float32, device=DEV)
+    y = fw.gemm_w8a8(torch.from_numpy(qx).to(DEV), ones_m, torch.from_numpy(qw).to(DEV), ones_n,
+                     out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    v = oracle.decode(codes)
+    expect = np.outer(v, v)
+    exp_t = torch.from_numpy(expect).to(out_dtype).double().numpy()
+    if out_dtype == torch.bfloat16:
+        assert np.array_equal(exp_t, expect)  # every product is a bf16 value
+    got = y.double().cpu().numpy()
+    bad = np.argwhere(got != exp_t)
+    assert len(bad) == 0, f"{len(bad)} products differ; first {bad[0]}: got {got[tuple(bad[0])]} want {exp_t[tuple(bad[0])]}"
+
+
+def test_w8a8_empty_calls_write_nothing_and_results_are_deterministic():
+    case = workloads.random_case(31, 300, 520, 512, torch.bfloat16)
+    q, s = fw.quantize(torch.from_numpy(case.layer.w).to(DEV))
+    x = case.x.to(DEV)
+    y = nan_like((300, 520), torch.bfloat16, DEV)
+    st = fw.fp8w_linear_w8a8(x.data_ptr(), fw.BF16, 0, 512, q.data_ptr(), s.data_ptr(), 0, 520, y.data_ptr(),
+                             0, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == fw.SUCCESS
+    st = fw.fp8w_gemm_w8a8(0, 0, 300, 512, q.data_ptr(), s.data_ptr(), 0, 0, y.data_ptr(), fw.BF16,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == fw.SUCCESS
+    torch.cuda.synchronize()
+    assert torch.isnan(y.float()).all()
+    y1 = fw.linear_w8a8(x, q, s)
+    y2 = fw.linear_w8a8(x, q, s)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
