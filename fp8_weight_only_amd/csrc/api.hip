@@ -384,7 +384,7 @@ const char* fp8w_linear_w8a8_kernel(int64_t m, int64_t n, int64_t k)
 {
     if (!sizes_ok(m, n, k) || m < 1 || n < 1 || k == 0 || k % 256 != 0)
         return nullptr;
-    return fp8w::w8a8_kernel_name(m, n);
+    return fp8w::w8a8_kernel_name(m, n, k);
 }
 
 fp8w_status_t fp8w_fnuz_to_ocp(const uint8_t* src, int64_t count, uint8_t* dst, hipStream_t stream)

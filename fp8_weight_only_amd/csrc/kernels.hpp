@@ -82,7 +82,7 @@ hipError_t launch_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k,
                        const void* bias, int64_t n, void* y, Act out, hipStream_t stream);
 
 // Name of the W8A8 kernel instance for this shape.
-const char* w8a8_kernel_name(int64_t m, int64_t n);
+const char* w8a8_kernel_name(int64_t m, int64_t n, int64_t k);
 
 // E4M3FNUZ codes -> OCP e4m3fn codes of the same values (dst may equal src).
 hipError_t launch_fnuz_to_ocp(const uint8_t* src, int64_t count, uint8_t* dst, hipStream_t stream);

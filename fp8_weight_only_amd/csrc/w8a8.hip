@@ -35,6 +35,9 @@
 // XCD's L2.
 #include <stdio.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "ring.hpp"
@@ -170,30 +173,69 @@ __device__ __forceinline__ void tile_of(int64_t& tn, int64_t& tm)
     tn = w / gs;
 }
 
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // y[t, c] = out(fl32(fl32(acc * scale_x[t]) * scale_w[c]) + bias[c]).
-// Requires k % 256 == 0 (k / 64 stages, a multiple of the 4-stage ring);
-// qw, qx 16-byte aligned.
-template <typename A, int BN, int BM>
+// Requires k % (64 * NS) == 0 (k / 64 stages, a multiple of the NS-stage
+// ring); qw, qx 16-byte aligned.
+template <typename A, int BN, int BM, int NS, int GM = 4>
 __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ qx, const float* __restrict__ sx,
                                                   const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                                   const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
                                                   int64_t m, int64_t n, int64_t k)
 {
-    constexpr int NS = 4;
+    static_assert(NS == 4 || NS == 6 || NS == 8, "an even number of stages, 4 to 8");
     using P = W8Pipe<BN, BM, NS>;
     using C = typename P::C;
     constexpr int L = C::LOADS;
     static_assert(BN <= 256 && BM <= 256, "one epilogue operand per thread");
+    // one array per stage buffer: the compiler can then tell the buffer being
+    // read from the ones the direct-to-LDS loads are writing, and inserts no
+    // waits of its own
     __shared__ __attribute__((aligned(1024))) uint8_t b0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t b1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t b2[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t b3[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t b4[NS > 4 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t b5[NS > 5 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t b6[NS > 6 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t b7[NS > 7 ? C::STAGE : 16];
     __shared__ __attribute__((aligned(16))) float e_sw[BN];
     __shared__ __attribute__((aligned(16))) uint16_t e_bias[BN];
     __shared__ __attribute__((aligned(16))) float e_sx[BM];
+    auto buf = [&](auto I) -> uint8_t* {
+        constexpr int i = decltype(I)::value % NS;
+        if constexpr (i == 0)
+            return b0;
+        else if constexpr (i == 1)
+            return b1;
+        else if constexpr (i == 2)
+            return b2;
+        else if constexpr (i == 3)
+            return b3;
+        else if constexpr (i == 4)
+            return b4;
+        else if constexpr (i == 5)
+            return b5;
+        else if constexpr (i == 6)
+            return b6;
+        else
+            return b7;
+    };
 
     int64_t tn, tm;
-    tile_of<4>(tn, tm);
+    tile_of<GM>(tn, tm);
     P p;
     p.qw = qw;
     p.qx = qx;
@@ -226,16 +268,15 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ q
     for (int f = 0; f < C::FN * C::FM; ++f)
         acc[f] = f32x16{0.0f};
 
-    // The ring: stage s + 3 is issued at step s into the buffer of stage s - 1,
-    // whose fragments were read during step s - 2; step s waits for stage
-    // s + 1 (the stages in flight are then s + 2 and the one just issued),
-    // runs stage s's MFMAs and reads stage s + 1's fragments.
+    // The ring: stage s + NS - 1 is issued at step s into the buffer of stage
+    // s - 1, whose fragments were read during step s - 2; step s waits for
+    // stage s + 1 (NS - 3 later stages may still be in flight), runs stage s's
+    // MFMAs and reads stage s + 1's fragments into the other register set
+    // (even steps compute set 0, odd steps set 1).
     i32x8 a0[C::FN], x0[C::FM], a1[C::FN], x1[C::FM];
     const int64_t S = k / 64;
-    p.issue(0, b0);
-    p.issue(1, b1);
-    p.issue(2, b2);
-    wait_loads_at_most<2 * L>();
+    static_for<NS - 1>([&](auto I) { p.issue(decltype(I)::value, buf(I)); });
+    wait_loads_at_most<(NS - 2) * L>();
     stage_barrier();
     if (tt < BN) {
         e_sw[tt] = r_sw;
@@ -244,37 +285,35 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ q
     if (tt < BM)
         e_sx[tt] = r_sx;
     p.read(b0, a0, x0);
+    auto step = [&](auto U) {
+        constexpr int u = decltype(U)::value;
+        if constexpr (u % 2 == 0)
+            p.step(buf(std::integral_constant<int, u + 1>{}), a0, x0, a1, x1, acc);
+        else
+            p.step(buf(std::integral_constant<int, u + 1>{}), a1, x1, a0, x0, acc);
+    };
     int64_t s = 0;
-    for (; s < S - 4; s += 4) {
-        wait_loads_at_most<L>();
-        stage_barrier();
-        p.issue(s + 3, b3);
-        p.step(b1, a0, x0, a1, x1, acc);
-        wait_loads_at_most<L>();
-        stage_barrier();
-        p.issue(s + 4, b0);
-        p.step(b2, a1, x1, a0, x0, acc);
-        wait_loads_at_most<L>();
-        stage_barrier();
-        p.issue(s + 5, b1);
-        p.step(b3, a0, x0, a1, x1, acc);
-        wait_loads_at_most<L>();
-        stage_barrier();
-        p.issue(s + 6, b2);
-        p.step(b0, a1, x1, a0, x0, acc);
+    for (; s < S - NS; s += NS) {
+        static_for<NS>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            wait_loads_at_most<(NS - 3) * L>();
+            stage_barrier();
+            p.issue(s + u + NS - 1, buf(std::integral_constant<int, u + NS - 1>{}));
+            step(U);
+        });
     }
-    // the last four stages: S - 1 is the last one issued
-    wait_loads_at_most<L>();
+    // the last NS stages: S - 1 is issued at the first step, then the ring drains
+    wait_loads_at_most<(NS - 3) * L>();
     stage_barrier();
-    p.issue(s + 3, b3);
-    p.step(b1, a0, x0, a1, x1, acc);
-    wait_loads_at_most<L>();
-    stage_barrier();
-    p.step(b2, a1, x1, a0, x0, acc);
-    wait_loads_at_most<0>();
-    stage_barrier();
-    p.step(b3, a0, x0, a1, x1, acc);
-    p.mma(a1, x1, acc);
+    p.issue(s + NS - 1, buf(std::integral_constant<int, NS - 1>{}));
+    step(std::integral_constant<int, 0>{});
+    static_for<NS - 2>([&](auto J) {
+        constexpr int j = decltype(J)::value + 1;
+        wait_loads_at_most<(NS - 2 - j) * L>();
+        stage_barrier();
+        step(std::integral_constant<int, j>{});
+    });
+    p.mma(a1, x1, acc);  // NS is even: the last step computes set 1
     __syncthreads();
 
     // lane (i, h) holds channels c0 + 8j + 4h + r (r = 0..3) of token t
@@ -317,12 +356,12 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ q
     }
 }
 
-template <typename A, int BN, int BM>
+template <typename A, int BN, int BM, int NS>
 hipError_t launch_w8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw, const float* sw,
                      const void* bias, int64_t n, void* y, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(256);
-    hipLaunchKernelGGL((w8a8_kernel<A, BN, BM>), grid, block, 0, stream, qx, sx, qw, sw,
+    hipLaunchKernelGGL((w8a8_kernel<A, BN, BM, NS>), grid, block, 0, stream, qx, sx, qw, sw,
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
     return hipGetLastError();
 }
@@ -333,34 +372,48 @@ hipError_t launch_w8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, c
 // workgroup per CU), in the order 256 x 256, 256 x 128, 128 x 128, 128 x 64
 // (channels x tokens); the smallest below that. It picked the fastest or
 // within 1 % of the fastest shape in all nine cases.
+//
+// Ring depth: the 128-wide tiles do few MFMAs per stage, so four stages keep
+// too little in flight to cover the weights' trip from HBM. Where such a tile
+// gives at most 256 workgroups (one per CU either way) eight stages are used
+// (k % 512 == 0): measured 12-14 % faster at M = 512 on the 4096-channel
+// layers. With more workgroups, the four-stage ring's smaller LDS footprint
+// lets two or three share a CU, which measured faster.
 struct W8Tile {
-    int bn, bm;
+    int bn, bm, ns;
 };
 
-W8Tile w8a8_tile(int64_t m, int64_t n)
+W8Tile w8a8_tile(int64_t m, int64_t n, int64_t k)
 {
     auto tiles = [&](int64_t bn, int64_t bm) { return ((n + bn - 1) / bn) * ((m + bm - 1) / bm); };
+    W8Tile t;
     if (tiles(256, 256) >= 224)
-        return {256, 256};
-    if (tiles(256, 128) >= 224)
-        return {256, 128};
-    if (tiles(128, 128) >= 224)
-        return {128, 128};
-    return {128, 64};
+        t = {256, 256, 4};
+    else if (tiles(256, 128) >= 224)
+        t = {256, 128, 4};
+    else if (tiles(128, 128) >= 224)
+        t = {128, 128, 4};
+    else
+        t = {128, 64, 4};
+    if (t.bn == 128 && tiles(t.bn, t.bm) <= 256 && k % 512 == 0)
+        t.ns = 8;
+    return t;
 }
 
 template <typename A>
 hipError_t launch_w8_typed(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw,
                            const float* sw, const void* bias, int64_t n, void* y, hipStream_t stream)
 {
-    const W8Tile t = w8a8_tile(m, n);
+    const W8Tile t = w8a8_tile(m, n, k);
     if (t.bn == 256 && t.bm == 256)
-        return launch_w8<A, 256, 256>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return launch_w8<A, 256, 256, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
     if (t.bn == 256)
-        return launch_w8<A, 256, 128>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return launch_w8<A, 256, 128, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
     if (t.bm == 128)
-        return launch_w8<A, 128, 128>(qx, sx, m, k, qw, sw, bias, n, y, stream);
-    return launch_w8<A, 128, 64>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return t.ns == 8 ? launch_w8<A, 128, 128, 8>(qx, sx, m, k, qw, sw, bias, n, y, stream)
+                         : launch_w8<A, 128, 128, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+    return t.ns == 8 ? launch_w8<A, 128, 64, 8>(qx, sx, m, k, qw, sw, bias, n, y, stream)
+                     : launch_w8<A, 128, 64, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
 }
 
 }  // namespace
@@ -377,16 +430,16 @@ hipError_t launch_w8a8(const uint8_t* qx, const float* sx, int64_t m, int64_t k,
     return hipErrorInvalidValue;
 }
 
-const char* w8a8_kernel_name(int64_t m, int64_t n)
+const char* w8a8_kernel_name(int64_t m, int64_t n, int64_t k)
 {
-    const W8Tile t = w8a8_tile(m, n);
+    const W8Tile t = w8a8_tile(m, n, k);
     if (t.bn == 256 && t.bm == 256)
-        return "w8a8_kernel<BN=256,BM=256>";
+        return "w8a8_kernel<BN=256,BM=256,NS=4>";
     if (t.bn == 256)
-        return "w8a8_kernel<BN=256,BM=128>";
+        return "w8a8_kernel<BN=256,BM=128,NS=4>";
     if (t.bm == 128)
-        return "w8a8_kernel<BN=128,BM=128>";
-    return "w8a8_kernel<BN=128,BM=64>";
+        return t.ns == 8 ? "w8a8_kernel<BN=128,BM=128,NS=8>" : "w8a8_kernel<BN=128,BM=128,NS=4>";
+    return t.ns == 8 ? "w8a8_kernel<BN=128,BM=64,NS=8>" : "w8a8_kernel<BN=128,BM=64,NS=4>";
 }
 
 }  // namespace fp8w
