@@ -16,23 +16,27 @@
 // D[8j + 4(l / 32) + r][l % 32] at accumulator 4j + r). The weight rows are the
 // A operand (channels) and the token rows the B operand, so a lane's four
 // consecutive D rows are four consecutive channels of one token: one 8-byte
-// store per fragment row. A workgroup of four waves owns BN channels x BM
-// tokens (256 x 256 down to 128 x 64, by the shape); stages of 64 k of both
-// tiles travel HBM/L2 -> LDS by direct global-to-LDS loads through a
-// four-stage ring (the waits and barrier of csrc/ring.hpp). In LDS every 64-byte row keeps its four 16-byte
-// chunks rotated by row / 4, so the 16 lanes of each ds_read_b128 phase
-// (rows i .. i+15, same chunk) hit 16 distinct bank groups.
+// store per fragment row.
 //
-// With one wave per SIMD there is no other wave to hide LDS latency behind, so
-// the ring prefetches fragments: the fragments of stage s + 1 are read into a
-// second register set while the MFMAs of stage s run, one read issued after
-// each MFMA (scheduling-group barriers hold that order). The epilogue's
-// operands (the workgroup's channel scales and biases and its token scales)
-// are fetched once when the workgroup starts and pass through LDS, so the end
-// of a tile waits for no global load. Tiles are dealt so that the workgroups
-// resident on one XCD at a time cover a compact block of the output (rows of
-// four tiles along the tokens), and share more of their operand rows in that
-// XCD's L2.
+// A workgroup of WN x WM waves owns BN channels x BM tokens (256 x 256 down to
+// 128 x 64, by the shape); each wave owns BN / WN channels x BM / WM tokens.
+// Stages of 64 k of both tiles travel HBM/L2 -> LDS by direct global-to-LDS
+// loads through a ring of NS stage buffers (the waits and barrier of
+// csrc/ring.hpp). In LDS every 64-byte row keeps its four 16-byte chunks
+// rotated by row / 4, so the 16 lanes of each ds_read_b128 phase (rows
+// i .. i+15, same chunk) hit 16 distinct bank groups.
+//
+// Latency hiding: with eight waves (two per SIMD) one wave's MFMAs run while
+// the other waits for LDS or the barrier. With four waves (one per SIMD, the
+// 128 x 64 tile) the ring prefetches fragments instead: the fragments of
+// stage s + 1 are read into a second register set while the MFMAs of stage s
+// run, one read issued after each MFMA (scheduling-group barriers hold that
+// order). The epilogue's operands (the workgroup's channel scales and biases
+// and its token scales) are fetched once when the workgroup starts and pass
+// through LDS, so the end of a tile waits for no global load. Tiles are dealt
+// so that the workgroups resident on one XCD at a time cover a compact block
+// of the output (rows of four tiles along the tokens), and share more of
+// their operand rows in that XCD's L2.
 #include <stdio.h>
 
 #include <type_traits>
@@ -48,21 +52,23 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BN, int BM, int NS>
+template <int BN, int BM, int NS, int WN, int WM>
 struct W8Cfg {
-    static constexpr int FN = BN / 64;  // 32-channel fragments per wave (two waves along n)
-    static constexpr int FM = BM / 64;  // 32-token fragments per wave (two waves along m)
+    static constexpr int W = WN * WM;            // waves
+    static constexpr int FN = BN / WN / 32;      // 32-channel fragments per wave
+    static constexpr int FM = BM / WM / 32;      // 32-token fragments per wave
     static constexpr int ABYTES = BN * 64;
     static constexpr int STAGE = (BN + BM) * 64;
     static constexpr int BLOCKS = (BN + BM) / 16;  // 1 KB load instructions per stage
-    static constexpr int LOADS = BLOCKS / 4;       // per wave
-    static_assert(BLOCKS % 4 == 0, "blocks split over four waves");
+    static constexpr int LOADS = BLOCKS / W;       // per wave
+    static_assert(FN >= 1 && FM >= 1, "at least one fragment each way per wave");
+    static_assert(BLOCKS % W == 0, "blocks split evenly over the waves");
     static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
 };
 
-template <int BN, int BM, int NS>
+template <int BN, int BM, int NS, int WN, int WM>
 struct W8Pipe {
-    using C = W8Cfg<BN, BM, NS>;
+    using C = W8Cfg<BN, BM, NS, WN, WM>;
     const uint8_t* qw;  // [n, k]
     const uint8_t* qx;  // [m, k]
     int64_t n, m, k, n0, m0;
@@ -118,10 +124,10 @@ struct W8Pipe {
         const int i = lane & 31;
 #pragma unroll
         for (int f = 0; f < C::FN; ++f)
-            a[f] = frag(buf, wn * (BN / 2) + 32 * f + i);
+            a[f] = frag(buf, wn * (BN / WN) + 32 * f + i);
 #pragma unroll
         for (int f = 0; f < C::FM; ++f)
-            b[f] = frag(buf + C::ABYTES, wm * (BM / 2) + 32 * f + i);
+            b[f] = frag(buf + C::ABYTES, wm * (BM / WM) + 32 * f + i);
     }
 
     __device__ __forceinline__ void mma(const i32x8* a, const i32x8* b, f32x16* acc) const
@@ -134,8 +140,16 @@ struct W8Pipe {
                     a[fn], b[fm], acc[fn * C::FM + fm], 0, 0, 0, 0, 0, 0);
     }
 
+    // one stage with no prefetch (run_ring's step; eight-wave tiles)
+    __device__ __forceinline__ void compute(const uint8_t* buf, f32x16* acc) const
+    {
+        i32x8 a[C::FN], b[C::FM];
+        read(buf, a, b);
+        mma(a, b, acc);
+    }
+
     // MFMAs on (a, b) while the next stage's fragments are read from nbuf into
-    // (na, nb): one MFMA, then one ds_read_b128, in turn
+    // (na, nb): one MFMA, then one ds_read_b128, in turn (four-wave tiles)
     __device__ __forceinline__ void step(const uint8_t* nbuf, const i32x8* a, const i32x8* b, i32x8* na, i32x8* nb,
                                          f32x16* acc) const
     {
@@ -189,17 +203,22 @@ __device__ __forceinline__ void static_for(F&& f)
 // y[t, c] = out(fl32(fl32(acc * scale_x[t]) * scale_w[c]) + bias[c]).
 // Requires k % (64 * NS) == 0 (k / 64 stages, a multiple of the NS-stage
 // ring); qw, qx 16-byte aligned.
-template <typename A, int BN, int BM, int NS, int GM = 4>
-__global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ qx, const float* __restrict__ sx,
-                                                  const uint8_t* __restrict__ qw, const float* __restrict__ sw,
-                                                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-                                                  int64_t m, int64_t n, int64_t k)
+template <typename A, int BN, int BM, int NS, int WN, int WM, int GM = 4>
+__global__ __launch_bounds__(WN* WM * kWave) void w8a8_kernel(const uint8_t* __restrict__ qx,
+                                                             const float* __restrict__ sx,
+                                                             const uint8_t* __restrict__ qw,
+                                                             const float* __restrict__ sw,
+                                                             const uint16_t* __restrict__ bias,
+                                                             uint16_t* __restrict__ y, int64_t m, int64_t n,
+                                                             int64_t k)
 {
     static_assert(NS == 4 || NS == 6 || NS == 8, "an even number of stages, 4 to 8");
-    using P = W8Pipe<BN, BM, NS>;
+    using P = W8Pipe<BN, BM, NS, WN, WM>;
     using C = typename P::C;
     constexpr int L = C::LOADS;
-    static_assert(BN <= 256 && BM <= 256, "one epilogue operand per thread");
+    constexpr int NT = C::W * kWave;
+    static_assert(C::W == 4 || (C::W == 8 && NS == 4), "eight-wave tiles run the four-stage ring");
+    static_assert(BN <= NT && BM <= NT, "one epilogue operand per thread");
     // one array per stage buffer: the compiler can then tell the buffer being
     // read from the ones the direct-to-LDS loads are writing, and inserts no
     // waits of its own
@@ -246,8 +265,8 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ q
     p.m0 = tm * BM;
     p.lane = threadIdx.x & (kWave - 1);
     p.wave = threadIdx.x / kWave;
-    p.wn = p.wave & 1;
-    p.wm = p.wave >> 1;
+    p.wn = p.wave % WN;
+    p.wm = p.wave / WN;
 
     // epilogue operands, one per thread, fetched before the ring starts and
     // stored to LDS once the ring's first wait (which covers them: loads
@@ -262,65 +281,74 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ q
     }
     if (tt < BM)
         r_sx = sx[p.m0 + tt < m ? p.m0 + tt : m - 1];
+    auto store_epilogue_operands = [&]() {
+        if (tt < BN) {
+            e_sw[tt] = r_sw;
+            e_bias[tt] = r_bias;
+        }
+        if (tt < BM)
+            e_sx[tt] = r_sx;
+    };
 
     f32x16 acc[C::FN * C::FM];
 #pragma unroll
     for (int f = 0; f < C::FN * C::FM; ++f)
         acc[f] = f32x16{0.0f};
-
-    // The ring: stage s + NS - 1 is issued at step s into the buffer of stage
-    // s - 1, whose fragments were read during step s - 2; step s waits for
-    // stage s + 1 (NS - 3 later stages may still be in flight), runs stage s's
-    // MFMAs and reads stage s + 1's fragments into the other register set
-    // (even steps compute set 0, odd steps set 1).
-    i32x8 a0[C::FN], x0[C::FM], a1[C::FN], x1[C::FM];
     const int64_t S = k / 64;
-    static_for<NS - 1>([&](auto I) { p.issue(decltype(I)::value, buf(I)); });
-    wait_loads_at_most<(NS - 2) * L>();
-    stage_barrier();
-    if (tt < BN) {
-        e_sw[tt] = r_sw;
-        e_bias[tt] = r_bias;
-    }
-    if (tt < BM)
-        e_sx[tt] = r_sx;
-    p.read(b0, a0, x0);
-    auto step = [&](auto U) {
-        constexpr int u = decltype(U)::value;
-        if constexpr (u % 2 == 0)
-            p.step(buf(std::integral_constant<int, u + 1>{}), a0, x0, a1, x1, acc);
-        else
-            p.step(buf(std::integral_constant<int, u + 1>{}), a1, x1, a0, x0, acc);
-    };
-    int64_t s = 0;
-    for (; s < S - NS; s += NS) {
-        static_for<NS>([&](auto U) {
-            constexpr int u = decltype(U)::value;
-            wait_loads_at_most<(NS - 3) * L>();
-            stage_barrier();
-            p.issue(s + u + NS - 1, buf(std::integral_constant<int, u + NS - 1>{}));
-            step(U);
-        });
-    }
-    // the last NS stages: S - 1 is issued at the first step, then the ring drains
-    wait_loads_at_most<(NS - 3) * L>();
-    stage_barrier();
-    p.issue(s + NS - 1, buf(std::integral_constant<int, NS - 1>{}));
-    step(std::integral_constant<int, 0>{});
-    static_for<NS - 2>([&](auto J) {
-        constexpr int j = decltype(J)::value + 1;
-        wait_loads_at_most<(NS - 2 - j) * L>();
+
+    if constexpr (C::W == 8) {
+        // two waves per SIMD: the plain ring (csrc/ring.hpp)
+        store_epilogue_operands();
+        run_ring<NS, L>(p, S, b0, b1, b2, b3, acc);
+    } else {
+        // The prefetching ring: stage s + NS - 1 is issued at step s into the
+        // buffer of stage s - 1, whose fragments were read during step s - 2;
+        // step s waits for stage s + 1 (NS - 3 later stages may still be in
+        // flight), runs stage s's MFMAs and reads stage s + 1's fragments into
+        // the other register set (even steps compute set 0, odd steps set 1).
+        i32x8 a0[C::FN], x0[C::FM], a1[C::FN], x1[C::FM];
+        static_for<NS - 1>([&](auto I) { p.issue(decltype(I)::value, buf(I)); });
+        wait_loads_at_most<(NS - 2) * L>();
         stage_barrier();
-        step(std::integral_constant<int, j>{});
-    });
-    p.mma(a1, x1, acc);  // NS is even: the last step computes set 1
+        store_epilogue_operands();
+        p.read(b0, a0, x0);
+        auto step = [&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if constexpr (u % 2 == 0)
+                p.step(buf(std::integral_constant<int, u + 1>{}), a0, x0, a1, x1, acc);
+            else
+                p.step(buf(std::integral_constant<int, u + 1>{}), a1, x1, a0, x0, acc);
+        };
+        int64_t s = 0;
+        for (; s < S - NS; s += NS) {
+            static_for<NS>([&](auto U) {
+                constexpr int u = decltype(U)::value;
+                wait_loads_at_most<(NS - 3) * L>();
+                stage_barrier();
+                p.issue(s + u + NS - 1, buf(std::integral_constant<int, u + NS - 1>{}));
+                step(U);
+            });
+        }
+        // the last NS stages: S - 1 is issued at the first step, then the ring drains
+        wait_loads_at_most<(NS - 3) * L>();
+        stage_barrier();
+        p.issue(s + NS - 1, buf(std::integral_constant<int, NS - 1>{}));
+        step(std::integral_constant<int, 0>{});
+        static_for<NS - 2>([&](auto J) {
+            constexpr int j = decltype(J)::value + 1;
+            wait_loads_at_most<(NS - 2 - j) * L>();
+            stage_barrier();
+            step(std::integral_constant<int, j>{});
+        });
+        p.mma(a1, x1, acc);  // NS is even: the last step computes set 1
+    }
     __syncthreads();
 
     // lane (i, h) holds channels c0 + 8j + 4h + r (r = 0..3) of token t
     const int i = p.lane & 31, h = p.lane >> 5;
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
-        const int tl = p.wm * (BM / 2) + 32 * fm + i;
+        const int tl = p.wm * (BM / WM) + 32 * fm + i;
         const int64_t t = p.m0 + tl;
         if (t >= m)
             continue;
@@ -330,7 +358,7 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ q
             const f32x16 d = acc[fn * C::FM + fm];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int cl = p.wn * (BN / 2) + 32 * fn + 8 * j + 4 * h;
+                const int cl = p.wn * (BN / WN) + 32 * fn + 8 * j + 4 * h;
                 const int64_t c0 = p.n0 + cl;
                 const f32x4 s4 = *reinterpret_cast<const f32x4*>(&e_sw[cl]);
                 const u32x2 b4 = *reinterpret_cast<const u32x2*>(&e_bias[cl]);
@@ -356,12 +384,12 @@ __global__ __launch_bounds__(256) void w8a8_kernel(const uint8_t* __restrict__ q
     }
 }
 
-template <typename A, int BN, int BM, int NS>
+template <typename A, int BN, int BM, int NS, int WN, int WM>
 hipError_t launch_w8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, const uint8_t* qw, const float* sw,
                      const void* bias, int64_t n, void* y, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(256);
-    hipLaunchKernelGGL((w8a8_kernel<A, BN, BM, NS>), grid, block, 0, stream, qx, sx, qw, sw,
+    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(WN * WM * kWave);
+    hipLaunchKernelGGL((w8a8_kernel<A, BN, BM, NS, WN, WM>), grid, block, 0, stream, qx, sx, qw, sw,
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
     return hipGetLastError();
 }
@@ -373,31 +401,31 @@ hipError_t launch_w8(const uint8_t* qx, const float* sx, int64_t m, int64_t k, c
 // (channels x tokens); the smallest below that. It picked the fastest or
 // within 1 % of the fastest shape in all nine cases.
 //
-// Ring depth: the 128-wide tiles do few MFMAs per stage, so four stages keep
-// too little in flight to cover the weights' trip from HBM. Where such a tile
-// gives at most 256 workgroups (one per CU either way) eight stages are used
-// (k % 512 == 0): measured 12-14 % faster at M = 512 on the 4096-channel
-// layers. With more workgroups, the four-stage ring's smaller LDS footprint
-// lets two or three share a CU, which measured faster.
+// Waves: eight (2 x 4, two per SIMD) on the three larger tiles, which measured
+// 15-25 % faster than four at 256 x 256, 3-8 % at 256 x 128 and 128 x 128;
+// four (2 x 2) at 128 x 64, whose 12 load instructions per stage do not split
+// over eight waves.
+//
+// Ring depth (four-wave tile): with two MFMAs per wave per stage, four stages
+// cover too little of the weights' trip from HBM. Where the tile gives at most
+// 256 workgroups (one per CU either way) eight stages are used (k % 512 == 0):
+// measured 12-14 % faster at M = 512 on the 4096-channel layers. With more
+// workgroups, the four-stage ring's smaller LDS footprint lets two or three
+// share a CU, which measured faster.
 struct W8Tile {
-    int bn, bm, ns;
+    int bn, bm, ns, waves;
 };
 
 W8Tile w8a8_tile(int64_t m, int64_t n, int64_t k)
 {
     auto tiles = [&](int64_t bn, int64_t bm) { return ((n + bn - 1) / bn) * ((m + bm - 1) / bm); };
-    W8Tile t;
     if (tiles(256, 256) >= 224)
-        t = {256, 256, 4};
-    else if (tiles(256, 128) >= 224)
-        t = {256, 128, 4};
-    else if (tiles(128, 128) >= 224)
-        t = {128, 128, 4};
-    else
-        t = {128, 64, 4};
-    if (t.bn == 128 && tiles(t.bn, t.bm) <= 256 && k % 512 == 0)
-        t.ns = 8;
-    return t;
+        return {256, 256, 4, 8};
+    if (tiles(256, 128) >= 224)
+        return {256, 128, 4, 8};
+    if (tiles(128, 128) >= 224)
+        return {128, 128, 4, 8};
+    return {128, 64, tiles(128, 64) <= 256 && k % 512 == 0 ? 8 : 4, 4};
 }
 
 template <typename A>
@@ -406,14 +434,13 @@ hipError_t launch_w8_typed(const uint8_t* qx, const float* sx, int64_t m, int64_
 {
     const W8Tile t = w8a8_tile(m, n, k);
     if (t.bn == 256 && t.bm == 256)
-        return launch_w8<A, 256, 256, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return launch_w8<A, 256, 256, 4, 2, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
     if (t.bn == 256)
-        return launch_w8<A, 256, 128, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return launch_w8<A, 256, 128, 4, 2, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
     if (t.bm == 128)
-        return t.ns == 8 ? launch_w8<A, 128, 128, 8>(qx, sx, m, k, qw, sw, bias, n, y, stream)
-                         : launch_w8<A, 128, 128, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
-    return t.ns == 8 ? launch_w8<A, 128, 64, 8>(qx, sx, m, k, qw, sw, bias, n, y, stream)
-                     : launch_w8<A, 128, 64, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+        return launch_w8<A, 128, 128, 4, 2, 4>(qx, sx, m, k, qw, sw, bias, n, y, stream);
+    return t.ns == 8 ? launch_w8<A, 128, 64, 8, 2, 2>(qx, sx, m, k, qw, sw, bias, n, y, stream)
+                     : launch_w8<A, 128, 64, 4, 2, 2>(qx, sx, m, k, qw, sw, bias, n, y, stream);
 }
 
 }  // namespace
@@ -434,12 +461,12 @@ const char* w8a8_kernel_name(int64_t m, int64_t n, int64_t k)
 {
     const W8Tile t = w8a8_tile(m, n, k);
     if (t.bn == 256 && t.bm == 256)
-        return "w8a8_kernel<BN=256,BM=256,NS=4>";
+        return "w8a8_kernel<BN=256,BM=256,NS=4,W=8>";
     if (t.bn == 256)
-        return "w8a8_kernel<BN=256,BM=128,NS=4>";
+        return "w8a8_kernel<BN=256,BM=128,NS=4,W=8>";
     if (t.bm == 128)
-        return t.ns == 8 ? "w8a8_kernel<BN=128,BM=128,NS=8>" : "w8a8_kernel<BN=128,BM=128,NS=4>";
-    return t.ns == 8 ? "w8a8_kernel<BN=128,BM=64,NS=8>" : "w8a8_kernel<BN=128,BM=64,NS=4>";
+        return "w8a8_kernel<BN=128,BM=128,NS=4,W=8>";
+    return t.ns == 8 ? "w8a8_kernel<BN=128,BM=64,NS=8,W=4>" : "w8a8_kernel<BN=128,BM=64,NS=4,W=4>";
 }
 
 }  // namespace fp8w

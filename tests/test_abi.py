@@ -321,12 +321,13 @@ def test_w8a8_validation():
     assert lw(X, fw.BF16, 64, 4096, Q, S, 0, 4096, Q, WS, 1 << 22, 0) == fw.ERR_INVALID_VALUE     # y overlaps q
     assert fw.fp8w_quantize_activations(X, fw.BF16, 0, 64, Q, S, 0) == fw.SUCCESS
     assert fw.fp8w_quantize_activations(X, fw.FP32, 4, 64, Q, S, 0) == fw.ERR_INVALID_VALUE
-    assert fw.fp8w_linear_w8a8_kernel(4096, 4096, 4096) == "w8a8_kernel<BN=256,BM=256,NS=4>"
-    assert fw.fp8w_linear_w8a8_kernel(2048, 4096, 4096) == "w8a8_kernel<BN=256,BM=128,NS=4>"
-    assert fw.fp8w_linear_w8a8_kernel(1024, 4096, 4096) == "w8a8_kernel<BN=128,BM=128,NS=8>"    # 256 tiles
-    assert fw.fp8w_linear_w8a8_kernel(1024, 4096, 768) == "w8a8_kernel<BN=128,BM=128,NS=4>"     # k % 512 != 0
-    assert fw.fp8w_linear_w8a8_kernel(1536, 4096, 4096) == "w8a8_kernel<BN=128,BM=128,NS=4>"    # 384 tiles
-    assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4096) == "w8a8_kernel<BN=128,BM=64,NS=8>"
-    assert fw.fp8w_linear_w8a8_kernel(100, 200, 256) == "w8a8_kernel<BN=128,BM=64,NS=4>"
-    assert fw.fp8w_linear_w8a8_kernel(512, 14336, 4096) == "w8a8_kernel<BN=256,BM=128,NS=4>"
+    assert fw.fp8w_linear_w8a8_kernel(4096, 4096, 4096) == "w8a8_kernel<BN=256,BM=256,NS=4,W=8>"
+    assert fw.fp8w_linear_w8a8_kernel(2048, 4096, 4096) == "w8a8_kernel<BN=256,BM=128,NS=4,W=8>"
+    assert fw.fp8w_linear_w8a8_kernel(1024, 4096, 4096) == "w8a8_kernel<BN=128,BM=128,NS=4,W=8>"
+    assert fw.fp8w_linear_w8a8_kernel(500, 4000, 1536) == "w8a8_kernel<BN=128,BM=64,NS=8,W=4>"     # 256 tiles
+    assert fw.fp8w_linear_w8a8_kernel(500, 4000, 768) == "w8a8_kernel<BN=128,BM=64,NS=4,W=4>"      # k % 512 != 0
+    assert fw.fp8w_linear_w8a8_kernel(700, 4000, 1536) == "w8a8_kernel<BN=128,BM=64,NS=4,W=4>"     # 352 tiles
+    assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4096) == "w8a8_kernel<BN=128,BM=64,NS=8,W=4>"
+    assert fw.fp8w_linear_w8a8_kernel(100, 200, 256) == "w8a8_kernel<BN=128,BM=64,NS=4,W=4>"
+    assert fw.fp8w_linear_w8a8_kernel(512, 14336, 4096) == "w8a8_kernel<BN=256,BM=128,NS=4,W=8>"
     assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4000) is None

@@ -66,15 +66,15 @@ CASES = [
 def test_w8a8_small(m, n, k, dtype, bias):
     print(f"w8a8 m={m} n={n} k={k}", flush=True)
     ns = 8 if k % 512 == 0 else 4
-    _check(m, n, k, dtype, bias, m + n + k, f"w8a8_kernel<BN=128,BM=64,NS={ns}>")
+    _check(m, n, k, dtype, bias, m + n + k, f"w8a8_kernel<BN=128,BM=64,NS={ns},W=4>")
 
 
 @pytest.mark.parametrize("m,n,k,dtype,tile", [
-    (2048, 4096, 512, torch.bfloat16, "w8a8_kernel<BN=256,BM=128,NS=4>"),
-    (1000, 4000, 768, torch.float16, "w8a8_kernel<BN=128,BM=128,NS=4>"),     # ragged edges of the 128 x 128 tile
-    (1000, 4000, 1024, torch.bfloat16, "w8a8_kernel<BN=128,BM=128,NS=8>"),   # the same with the 8-stage ring
-    (500, 4000, 1536, torch.float16, "w8a8_kernel<BN=128,BM=64,NS=8>"),      # 128 x 64, 8 stages, ragged
-    (2000, 4100, 256, torch.float16, "w8a8_kernel<BN=256,BM=128,NS=4>"),     # ragged edges of the 256 x 128 tile
+    (2048, 4096, 512, torch.bfloat16, "w8a8_kernel<BN=256,BM=128,NS=4,W=8>"),
+    (1000, 4000, 768, torch.float16, "w8a8_kernel<BN=128,BM=128,NS=4,W=8>"),     # ragged edges of the 128 x 128 tile
+    (700, 4000, 1536, torch.bfloat16, "w8a8_kernel<BN=128,BM=64,NS=4,W=4>"),     # 128 x 64 past 256 workgroups
+    (500, 4000, 1536, torch.float16, "w8a8_kernel<BN=128,BM=64,NS=8,W=4>"),      # 128 x 64, 8 stages, ragged
+    (2000, 4100, 256, torch.float16, "w8a8_kernel<BN=256,BM=128,NS=4,W=8>"),     # ragged edges of the 256 x 128 tile
 ])
 def test_w8a8_mid_tiles(m, n, k, dtype, tile):
     print(f"w8a8 m={m} n={n} k={k} {tile}", flush=True)
@@ -83,7 +83,7 @@ def test_w8a8_mid_tiles(m, n, k, dtype, tile):
 
 def test_w8a8_large_tile():
     print("w8a8 large tile 4096 x 4096 x 1024", flush=True)
-    _check(4096, 4096, 1024, torch.bfloat16, True, 5, "w8a8_kernel<BN=256,BM=256,NS=4>", sampled=True)
+    _check(4096, 4096, 1024, torch.bfloat16, True, 5, "w8a8_kernel<BN=256,BM=256,NS=4,W=8>", sampled=True)
 
 
 def test_w8a8_zero_rows_and_scale_zero():
