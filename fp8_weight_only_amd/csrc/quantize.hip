@@ -9,7 +9,9 @@
 // an all-zero row (scale 0) needs no division (its codes are all 0x00).
 //
 // One workgroup of 256 threads per row. Pass 1 reduces |w| to the row's amax
-// (and flags NaN/inf); pass 2 re-reads the row (mostly from L2) and encodes.
+// (and flags NaN/inf); pass 2 encodes, from registers when the row fits (k up
+// to 16384 with 16-byte alignment, the activation rows of the W8A8 path
+// included), otherwise re-reading the row (mostly from L2).
 // The quotient w / scale is an IEEE fp32 division (the compiler's correctly
 // rounded sequence; no fast-math) and the result is clamped to +-448 in fp32
 // before the hardware RNE conversion, so the conversion never sees an
@@ -107,11 +109,15 @@ __device__ __forceinline__ uint8_t encode1(float a)
 
 // VEC: k % 16 == 0 and w, q 16-byte aligned, so every thread moves 16 elements
 // per iteration (four or two 128-bit loads in, one 128-bit store out).
-template <typename W, bool VEC>
+// U > 0 (VEC only, k <= U * 16 * kThreads): the row is read once and held in
+// registers (U chunks of 16 elements per thread) between the amax and the
+// encode, instead of a second read of the row; the arithmetic is the same.
+template <typename W, bool VEC, int U = 0>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const void* __restrict__ w, int64_t k,
                                                                  uint8_t* __restrict__ q,
                                                                  float* __restrict__ scale)
 {
+    static_assert(U == 0 || VEC, "the register-resident row needs the vector path");
     __shared__ float wave_amax[kThreads / kWave];
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
@@ -120,7 +126,22 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const void* __r
     // pass 1: amax and the non-finite flag
     float amax = 0.0f;
     int bad = 0;
-    if (VEC) {
+    float held[U > 0 ? U : 1][16];
+    if constexpr (U > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = ((int64_t)u * kThreads + tid) * 16;
+            if (j < k) {
+                W::load16(w, base + j, held[u]);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float a = fabsf(held[u][e]);
+                    bad |= !(a <= 3.402823466e38f);
+                    amax = fmaxf(amax, a);
+                }
+            }
+        }
+    } else if (VEC) {
         for (int64_t j = (int64_t)tid * 16; j < k; j += kThreads * 16) {
             float v[16];
             W::load16(w, base + j, v);
@@ -152,18 +173,29 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const void* __r
         return;  // uniform over the workgroup; the host reports the error
 
     // pass 2: codes
-    if (VEC) {
+    auto encode16 = [&](const float* v) {
+        u32x4 out = {0u, 0u, 0u, 0u};
+        if (s != 0.0f) {
+            out.x = encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+            out.y = encode4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
+            out.z = encode4(v[8] / s, v[9] / s, v[10] / s, v[11] / s);
+            out.w = encode4(v[12] / s, v[13] / s, v[14] / s, v[15] / s);
+        }
+        return out;
+    };
+    if constexpr (U > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = ((int64_t)u * kThreads + tid) * 16;
+            if (j < k)
+                *reinterpret_cast<u32x4*>(q + base + j) = encode16(held[u]);
+        }
+    } else if (VEC) {
         for (int64_t j = (int64_t)tid * 16; j < k; j += kThreads * 16) {
-            u32x4 out = {0u, 0u, 0u, 0u};
-            if (s != 0.0f) {
-                float v[16];
+            float v[16];
+            if (s != 0.0f)
                 W::load16(w, base + j, v);
-                out.x = encode4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
-                out.y = encode4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
-                out.z = encode4(v[8] / s, v[9] / s, v[10] / s, v[11] / s);
-                out.w = encode4(v[12] / s, v[13] / s, v[14] / s, v[15] / s);
-            }
-            *reinterpret_cast<u32x4*>(q + base + j) = out;
+            *reinterpret_cast<u32x4*>(q + base + j) = encode16(v);
         }
     } else {
         for (int64_t j = tid; j < k; j += kThreads)
@@ -178,7 +210,14 @@ hipError_t launch_typed(const void* w, int elem_bytes, int64_t n, int64_t k, uin
     const bool vec = (k % 16 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
                      ((reinterpret_cast<uintptr_t>(q) & 15) == 0) && ((k * elem_bytes) % 16 == 0);
     const dim3 grid((unsigned)n), block(kThreads);
-    if (vec)
+    constexpr int64_t kChunk = 16 * kThreads;  // elements per register-resident chunk
+    if (vec && k <= kChunk)
+        hipLaunchKernelGGL((quantize_rows_kernel<W, true, 1>), grid, block, 0, stream, w, k, q, scale);
+    else if (vec && k <= 2 * kChunk)
+        hipLaunchKernelGGL((quantize_rows_kernel<W, true, 2>), grid, block, 0, stream, w, k, q, scale);
+    else if (vec && k <= 4 * kChunk)
+        hipLaunchKernelGGL((quantize_rows_kernel<W, true, 4>), grid, block, 0, stream, w, k, q, scale);
+    else if (vec)
         hipLaunchKernelGGL((quantize_rows_kernel<W, true>), grid, block, 0, stream, w, k, q, scale);
     else
         hipLaunchKernelGGL((quantize_rows_kernel<W, false>), grid, block, 0, stream, w, k, q, scale);
