@@ -432,8 +432,11 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
 // partial sums from the caller's workspace. Measured on MI355X this pays only
 // above 16 tokens, where it cut [4096 x 14336] at 32 tokens from 28.8 to
 // 19.7 us; without workspace these shapes take the single-pass plan.
-// seg_kernel covers small batches on narrow layers, where it measured
-// faster, and the shapes the ring cannot tile.
+// A layer of exactly 256 * 48 = 12288 channels (merged q/k/v) takes three
+// channel tiles: 256 workgroups, one per CU, where four tiles leave a quarter of
+// the CUs idle (10.9 against 11.7 us at 16 tokens on [12288 x 4096], 14.7
+// against 15.3 at 32). seg_kernel covers small batches on narrow layers, where
+// it measured faster, and the shapes the ring cannot tile.
 struct SkinnyPlan {
     bool pipe;
     int xr, ct, kp, ns, splits;  // pipe_kernel
@@ -449,7 +452,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
             ct = 4;
             ns = 2;
         } else if (n >= 12288) {
-            ct = 4;
+            ct = n <= 256 * 48 ? 3 : 4;
         } else if (n >= 8192) {
             if (m > 16 && allow_split && k % (2 * 1024) == 0) {
                 ct = 4;
@@ -504,6 +507,8 @@ hipError_t launch_pipe_xr(const SkinnyPlan& p, const void* x, int m, int64_t k, 
     switch (key) {
     case 412: return launch_pipe<A, XR, 4, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
     case 414: return launch_pipe<A, XR, 4, 1, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 312: return launch_pipe<A, XR, 3, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 314: return launch_pipe<A, XR, 3, 1, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
     case 212: return launch_pipe<A, XR, 2, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
     case 214: return launch_pipe<A, XR, 2, 1, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
     case 122: return launch_pipe<A, XR, 1, 2, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);

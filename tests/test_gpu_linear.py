@@ -88,7 +88,9 @@ PIPE = [
     (9, 200, 2048, torch.bfloat16, "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"),
     (16, 4100, 1024, torch.float16, "pipe_kernel<XR=16,CT=1,KP=2,NS=2>"),
     (19, 16400, 512, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>"),
-    (24, 12288, 2048, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>"),
+    (24, 12288, 2048, torch.float16, "pipe_kernel<XR=24,CT=3,KP=1,NS=4>"),
+    (3, 12288, 512, torch.bfloat16, "pipe_kernel<XR=4,CT=3,KP=1,NS=2>"),
+    (16, 12288, 4096, torch.bfloat16, "pipe_kernel<XR=16,CT=3,KP=1,NS=4>"),
     (32, 8192, 3072, torch.float16, "pipe_kernel<XR=32,CT=2,KP=1,NS=4>"),
     (32, 300, 4096, torch.bfloat16, "pipe_kernel<XR=32,CT=1,KP=2,NS=4>"),
     (3, 16500, 1536, torch.bfloat16, "pipe_kernel<XR=4,CT=4,KP=1,NS=2>"),
