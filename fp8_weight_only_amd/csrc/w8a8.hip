@@ -36,7 +36,8 @@
 // through LDS, so the end of a tile waits for no global load. Tiles are dealt
 // so that the workgroups resident on one XCD at a time cover a compact block
 // of the output (rows of four tiles along the tokens), and share more of
-// their operand rows in that XCD's L2.
+// their operand rows in that XCD's L2; each XCD's workgroups start at their
+// own eighth of k.
 #include <stdio.h>
 
 #include <type_traits>
@@ -72,14 +73,18 @@ struct W8Pipe {
     const uint8_t* qw;  // [n, k]
     const uint8_t* qx;  // [m, k]
     int64_t n, m, k, n0, m0;
+    int64_t S, rot;  // stages; the k stage this workgroup starts at
     int lane, wave, wn, wm;
 
-    // Block b of the stage holds rows 16b .. 16b + 15 of the weight tile (b <
-    // BN / 16) or of the token tile; lane l brings 16 bytes of row 16b + l / 4,
-    // the chunk that belongs at slot l % 4 (chunk (slot - row / 4) mod 4).
+    // Stage s covers k stage (s + rot) mod S. Block b of the stage holds rows
+    // 16b .. 16b + 15 of the weight tile (b < BN / 16) or of the token tile;
+    // lane l brings 16 bytes of row 16b + l / 4, the chunk that belongs at
+    // slot l % 4 (chunk (slot - row / 4) mod 4).
     __device__ __forceinline__ void issue(int64_t s, uint8_t* buf) const
     {
-        const int64_t kb = s * 64;
+        int64_t sr = s + rot;  // s < S and rot < S
+        sr = sr < S ? sr : sr - S;
+        const int64_t kb = sr * 64;
 #pragma unroll
         for (int u = 0; u < C::LOADS; ++u) {
             const int b = wave * C::LOADS + u;
@@ -295,6 +300,14 @@ __global__ __launch_bounds__(WN* WM * kWave) void w8a8_kernel(const uint8_t* __r
     for (int f = 0; f < C::FN * C::FM; ++f)
         acc[f] = f32x16{0.0f};
     const int64_t S = k / 64;
+    // k stagger per XCD: the workgroups one XCD holds (linear id L, XCD L % 8)
+    // walk k in step and share operand rows in its L2; the eight XCDs start
+    // an eighth of k apart, so their weight reads spread over more of HBM.
+    // Measured on MI355X: 5-11 % faster on the 4096-channel prefill layers at
+    // M = 512 and 2048, within run-to-run noise elsewhere; a stagger per
+    // workgroup was slower.
+    p.S = S;
+    p.rot = ((blockIdx.x + (int64_t)gridDim.x * blockIdx.y) % 8) * (S / 8);
 
     if constexpr (C::W == 8) {
         // two waves per SIMD: the plain ring (csrc/ring.hpp)
