@@ -10,9 +10,11 @@ Cache cannot serve repeats: the kernels stream from HBM.
 
 The timed region launches the calls eagerly through the C ABI (ctypes) on
 torch's current stream; host enqueue is faster than the kernels, so the GPU
-stays busy. The same steps replayed from HIP graphs (one graph per weight
-copy) are reported in "graph": on this ROCm, replay adds a few microseconds
-per step, so graphs are not used for the headline number.
+stays busy. The same steps replayed from a HIP graph are reported in "graph".
+The graph holds one pass over the rotated weight copies (one step per copy):
+on this ROCm each graph launch costs about 4.5 us, so a graph of a single step
+ran that much slower than eager launches, while a graph of eight steps runs
+within 1 % of them.
 
 value = algorithmic bytes of the timed steps / the timed region's duration
 (HIP events on the launch stream, around exactly --steps steps, with
@@ -377,44 +379,50 @@ def call_report(call, us):
     return r
 
 
-def capture_graphs(calls, copies, stream_obj):
-    """One HIP graph per weight copy, each holding one step (every call once)."""
-    graphs = []
-    for c in range(copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream_obj):
-            st = torch.cuda.current_stream().cuda_stream
+def capture_pass(calls, copies, stream_obj):
+    """One HIP graph holding `copies` steps, step c on weight copy c (every call
+    once per step): one replay is one pass over the rotated copies."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream_obj):
+        st = torch.cuda.current_stream().cuda_stream
+        for c in range(copies):
             for call in calls:
                 call.launch(c, st)
-        graphs.append(g)
-    return graphs
+    return g
 
 
 def timed_steps(calls, steps, warmup, copies, use_graph, dev):
-    """Duration (ms) of exactly `steps` steps, events around them and synchronizes on both sides."""
+    """Duration (ms) of exactly `steps` steps, events around them and synchronizes
+    on both sides. With use_graph the steps are replays of one pass graph, so
+    `steps` must be a multiple of `copies`."""
     stream = torch.cuda.current_stream(dev)
-    graphs = None
+    graph = None
     if use_graph:
-        side = torch.cuda.Stream(device=dev)
-        graphs = capture_graphs(calls, copies, side)
+        if steps % copies:
+            raise ValueError("graph steps must be a whole number of passes over the weight copies")
+        graph = capture_pass(calls, copies, torch.cuda.Stream(device=dev))
     torch.cuda.synchronize()
 
     def step(i):
-        if graphs is not None:
-            graphs[i % copies].replay()
-        else:
-            for call in calls:
-                call.launch(i, stream.cuda_stream)
+        for call in calls:
+            call.launch(i, stream.cuda_stream)
 
-    spin_up(step, SPIN_MS)
-    for i in range(warmup):
-        step(i)
+    def unit(i):  # one eager step, or one replayed pass of `copies` steps
+        if graph is not None:
+            graph.replay()
+        else:
+            step(i)
+
+    per_unit = copies if graph is not None else 1
+    spin_up(unit, SPIN_MS)
+    for i in range(-(-warmup // per_unit)):
+        unit(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        step(i)
+    for i in range(steps // per_unit):
+        unit(i)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1)
@@ -681,7 +689,7 @@ def main():
     ceiling = read_ceiling(dev, [c.layer.n * c.layer.k for c in calls])
 
     ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
-    graph_steps = max(200, args.steps // 10)
+    graph_steps = copies * -(-max(200, args.steps // 10) // copies)
     try:
         graph_ms = timed_steps(calls, graph_steps, 20, copies, True, dev)
     except Exception as e:  # noqa: BLE001
@@ -908,12 +916,13 @@ def extra_sections(dev, stream, reps=100, only=None):
         Ls = [Layer(lw, copies, dev) for lw in lws]
         calls = [Call(Li, workloads.block_x(i).to(dev), dev) for i, Li in enumerate(Ls)]
         blk = [call_report(c, burst(c, reps, 10, stream)) for c in calls]
+        gsteps = copies * -(-200 // copies)  # whole passes over the weight copies
         ms = timed_steps(calls, 200, 10, copies, False, dev)
-        gms = timed_steps(calls, 200, 10, copies, True, dev)
+        gms = timed_steps(calls, gsteps, 10, copies, True, dev)
         ex["decoder_block"] = {"calls": blk, "us_sum_of_calls": round(sum(b["us_per_call"] for b in blk), 2),
                                "step_us": round(ms * 1e3 / 200, 2), "step_mode": "eager",
                                "step_gbps": round(blk_bytes / (ms * 1e-3 / 200) / 1e9, 1),
-                               "graph_step_us": round(gms * 1e3 / 200, 2), "bytes": blk_bytes}
+                               "graph_step_us": round(gms * 1e3 / gsteps, 2), "bytes": blk_bytes}
         log(f"  decoder block m=16: {ex['decoder_block']['step_us']:.1f} us/step (eager), "
             f"{ex['decoder_block']['graph_step_us']:.1f} (graph), {ex['decoder_block']['step_gbps']:.0f} GB/s")
         del Ls, calls
@@ -927,11 +936,11 @@ def extra_sections(dev, stream, reps=100, only=None):
         mcalls = [Call(Mi, workloads.block_x(g[0]).to(dev), dev) for Mi, g in zip(Ms, groups)]
         mblk = [call_report(c, burst(c, reps, 10, stream)) for c in mcalls]
         ms = timed_steps(mcalls, 200, 10, copies, False, dev)
-        gms = timed_steps(mcalls, 200, 10, copies, True, dev)
+        gms = timed_steps(mcalls, gsteps, 10, copies, True, dev)
         ex["decoder_block_merged"] = {
             "calls": mblk, "us_sum_of_calls": round(sum(b["us_per_call"] for b in mblk), 2),
             "step_us": round(ms * 1e3 / 200, 2), "step_mode": "eager",
-            "step_gbps": round(mbytes / (ms * 1e-3 / 200) / 1e9, 1), "graph_step_us": round(gms * 1e3 / 200, 2),
+            "step_gbps": round(mbytes / (ms * 1e-3 / 200) / 1e9, 1), "graph_step_us": round(gms * 1e3 / gsteps, 2),
             "bytes": mbytes}
         log(f"  decoder block m=16, merged q/k/v and gate/up: {ex['decoder_block_merged']['step_us']:.1f} us/step "
             f"(eager), {ex['decoder_block_merged']['graph_step_us']:.1f} (graph), "
