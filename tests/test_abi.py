@@ -93,7 +93,8 @@ def test_kernel_names():
     assert kn(A, 8, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=2,T=2,W=8,U=2,MT=1>"
     assert kn(A, 4, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"
     assert kn(A, 12, 40, 768, fw.BF16, X, Q) == "seg_kernel<SEG=1,T=2,W=4,U=1,MT=2>"      # k % 1024 != 0
-    assert kn(A, 12, 40, 1024, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=2>"
+    assert kn(A, 12, 40, 1024, fw.BF16, X, Q) == "pipe_kernel<XR=12,CT=1,KP=2,NS=2>"
+    assert kn(A, 13, 40, 1024, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=2>"
     assert kn(A, 20, 12300, 512, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=2>"
     assert kn(A, 16, 12288, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=3,KP=1,NS=4>"
     assert kn(fw.PATH_SKINNY, 1, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"

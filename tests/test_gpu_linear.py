@@ -85,7 +85,7 @@ PIPE = [
     (2, 12300, 1024, torch.bfloat16, "pipe_kernel<XR=4,CT=4,KP=1,NS=4>"),
     (5, 8200, 1024, torch.float16, "pipe_kernel<XR=8,CT=2,KP=1,NS=4>"),
     (7, 8250, 512, torch.bfloat16, "pipe_kernel<XR=8,CT=2,KP=1,NS=2>"),
-    (9, 200, 2048, torch.bfloat16, "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"),
+    (9, 200, 2048, torch.bfloat16, "pipe_kernel<XR=12,CT=1,KP=2,NS=4>"),
     (16, 4100, 1024, torch.float16, "pipe_kernel<XR=16,CT=1,KP=2,NS=2>"),
     (19, 16400, 512, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>"),
     (24, 12288, 2048, torch.float16, "pipe_kernel<XR=24,CT=3,KP=1,NS=4>"),
@@ -95,8 +95,11 @@ PIPE = [
     (32, 300, 4096, torch.bfloat16, "pipe_kernel<XR=32,CT=1,KP=2,NS=4>"),
     (3, 16500, 1536, torch.bfloat16, "pipe_kernel<XR=4,CT=4,KP=1,NS=2>"),
     (6, 8192, 2048, torch.bfloat16, "pipe_kernel<XR=8,CT=2,KP=2,NS=4>"),
-    (12, 9000, 4096, torch.float16, "pipe_kernel<XR=16,CT=2,KP=2,NS=4>"),
-    (10, 8300, 1024, torch.bfloat16, "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"),
+    (12, 9000, 4096, torch.float16, "pipe_kernel<XR=12,CT=2,KP=2,NS=4>"),
+    (10, 8300, 1024, torch.bfloat16, "pipe_kernel<XR=12,CT=2,KP=1,NS=4>"),
+    (13, 4100, 2048, torch.float16, "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"),
+    (11, 12288, 1024, torch.bfloat16, "pipe_kernel<XR=12,CT=3,KP=1,NS=4>"),
+    (12, 14400, 1024, torch.float16, "pipe_kernel<XR=12,CT=4,KP=1,NS=4>"),
     (20, 8200, 2048, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
     (32, 8192, 4096, torch.float16, "pipe_kernel<XR=32,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
     (17, 4100, 2048, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
