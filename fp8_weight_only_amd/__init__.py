@@ -37,11 +37,11 @@ __all__ = [
     "fp8w_linear_w8a8_kernel", "quantize_activations", "gemm_w8a8", "linear_w8a8",
     "fp8w_status_string", "fp8w_abi_version", "quantize", "linear", "dequantize",
     "linear_path", "workspace_bytes", "QuantizedLinear",
-    "BF16", "FP16", "FP32", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_FALLBACK", "EXPORTS",
+    "BF16", "FP16", "FP32", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_FALLBACK", "PATH_BATCH", "EXPORTS",
 ]
 
 BF16, FP16, FP32 = 0, 1, 2
-PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_FALLBACK = -1, 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_FALLBACK, PATH_BATCH = -1, 0, 1, 2, 3
 SUCCESS, ERR_INVALID_VALUE, ERR_MISALIGNED, ERR_NONFINITE, ERR_WORKSPACE, ERR_HIP = range(6)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -66,9 +66,14 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb)
 }
 
 // The fast kernels' coverage: see fp8w_linear in include/fp8w.h.
+bool fast_k(int64_t k)
+{
+    return k >= 256 && k % 256 == 0;
+}
+
 bool fast_shape(int64_t m, int64_t k)
 {
-    return m >= 1 && m <= 32 && k >= 256 && k % 256 == 0;
+    return m >= 1 && m <= 32 && fast_k(k);
 }
 
 bool fast_pointers(const void* x, const uint8_t* q)
@@ -76,7 +81,17 @@ bool fast_pointers(const void* x, const uint8_t* q)
     return aligned(x, 16) && aligned(q, 16);
 }
 
+// The per-channel linear: GEMV, skinny MFMA, the batch GEMM above 32 tokens,
+// or the fallback.
 int auto_path(int64_t m, int64_t k, const void* x, const uint8_t* q)
+{
+    if (!fast_k(k) || !fast_pointers(x, q) || m < 1)
+        return FP8W_PATH_FALLBACK;
+    return m == 1 ? FP8W_PATH_GEMV : m <= 32 ? FP8W_PATH_SKINNY : FP8W_PATH_BATCH;
+}
+
+// The grouped linear has no batch kernel: above 32 tokens it takes its generic one.
+int auto_path_grouped(int64_t m, int64_t k, const void* x, const uint8_t* q)
 {
     if (fast_shape(m, k) && fast_pointers(x, q))
         return m == 1 ? FP8W_PATH_GEMV : FP8W_PATH_SKINNY;
@@ -128,7 +143,12 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if (path == FP8W_PATH_GEMV && m != 1 && m != 0)
             return FP8W_ERR_INVALID_VALUE;
-        if (m > 32 || k % 256 != 0 || k == 0)
+        if (m > 32 || !fast_k(k))
+            return FP8W_ERR_INVALID_VALUE;
+        if (!fast_pointers(x, q))
+            return FP8W_ERR_MISALIGNED;
+    } else if (path == FP8W_PATH_BATCH) {
+        if (!fast_k(k))
             return FP8W_ERR_INVALID_VALUE;
         if (!fast_pointers(x, q))
             return FP8W_ERR_MISALIGNED;
@@ -141,6 +161,8 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
     const fp8w::Act a = act_of(act);
     if (path == FP8W_PATH_GEMV)
         return hip_status(fp8w::launch_gemv(x, a, k, q, scale, bias, n, y, stream));
+    if (path == FP8W_PATH_BATCH)
+        return hip_status(fp8w::launch_batch(x, a, m, k, q, scale, bias, n, y, stream));
     if (path == FP8W_PATH_SKINNY) {
         // split k on shapes that use it, when the caller's workspace is large enough
         const size_t need = fp8w::skinny_workspace_bytes(m, n, k);
@@ -190,7 +212,7 @@ fp8w_status_t run_linear_grouped(const void* x, fp8w_dtype_t act, int64_t m, int
     if (path < FP8W_PATH_AUTO || path > FP8W_PATH_FALLBACK)
         return FP8W_ERR_INVALID_VALUE;
     if (path == FP8W_PATH_AUTO)
-        path = auto_path(m, k, x, q);
+        path = auto_path_grouped(m, k, x, q);
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if (path == FP8W_PATH_GEMV && m != 1 && m != 0)
             return FP8W_ERR_INVALID_VALUE;
@@ -270,7 +292,7 @@ int fp8w_linear_grouped_path(int64_t m, int64_t n, int64_t k, int64_t group, fp8
 {
     if (!valid_act(act_dtype) || !sizes_ok(m, n, k) || !valid_group(k, group))
         return -1;
-    return auto_path(m, k, x, q);
+    return auto_path_grouped(m, k, x, q);
 }
 
 const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k, int64_t group,
@@ -279,7 +301,7 @@ const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k
     if (!valid_act(act_dtype) || !sizes_ok(m, n, k) || !valid_group(k, group))
         return nullptr;
     if (path == FP8W_PATH_AUTO)
-        path = auto_path(m, k, x, q);
+        path = auto_path_grouped(m, k, x, q);
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || k % 256 != 0 || k == 0)
             return nullptr;
@@ -463,7 +485,7 @@ fp8w_status_t fp8w_linear_with_path(const void* x, fp8w_dtype_t act_dtype, int64
                                     const uint8_t* q, const float* scale, const void* bias, int64_t n, void* y,
                                     void* workspace, size_t workspace_bytes, int path, hipStream_t stream)
 {
-    if (path < FP8W_PATH_AUTO || path > FP8W_PATH_FALLBACK)
+    if (path < FP8W_PATH_AUTO || path > FP8W_PATH_BATCH)
         return FP8W_ERR_INVALID_VALUE;
     return run_linear(x, act_dtype, m, k, q, scale, bias, n, y, workspace, workspace_bytes, path, stream);
 }
@@ -514,10 +536,12 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
     if (path == FP8W_PATH_AUTO)
         path = auto_path(m, k, x, q);
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
-        if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || k % 256 != 0 || k == 0)
+        if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || !fast_k(k))
             return nullptr;
         return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(n, k) : fp8w::skinny_kernel_name(m, n, k, true);
     }
+    if (path == FP8W_PATH_BATCH)
+        return m >= 1 && fast_k(k) ? fp8w::batch_kernel_name(m, n) : nullptr;
     if (path == FP8W_PATH_FALLBACK)
         return fp8w::fallback_kernel_name(m, n, k, x);
     return nullptr;

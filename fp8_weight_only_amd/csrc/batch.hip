@@ -1,0 +1,318 @@
+// The weight-only linear for batches above the skinny kernels' 32 tokens
+// (batched decode): y[m, n] = scale[n] * sum_k x[m, k] * value(q[n, k]) + bias[n],
+// the same contract as the other paths ("FP8 weight-only (precision:
+// fp8_weights)", section "The contract": e4m3 weights, activations kept in
+// bf16 / fp16, fp32 accumulation, the scale and bias in an fp32 epilogue, one
+// rounding to the activation dtype). Unlike the fallback it never writes a
+// dequantised weight: the codes are decoded in the GEMM itself, exactly, into
+// the activation dtype ("Dequantise in registers": every e4m3 value is a bf16
+// and an fp16 value), so the layer reads one byte per weight per tile row.
+//
+// A workgroup of WN x WM waves owns BN channels x BM tokens. Stages of 64 k of
+// both tiles (BN rows of 64 codes, BM rows of 64 activations) go HBM/L2 -> LDS
+// by direct global-to-LDS loads through the four-stage ring of csrc/ring.hpp.
+// The matrix cores run v_mfma_f32_32x32x16_{bf16,f16}: channels are the A
+// operand, tokens the B operand, so a lane's four consecutive accumulators are
+// four consecutive channels of one token (one 8-byte store).
+//
+// Which k a lane feeds: in MFMA step j (0..3) of a stage, lane half h feeds k
+// = 32h + 8j .. 32h + 8j + 7 of the stage to both operands. Each MFMA then
+// sums 16 of the stage's products, every product exactly once over the four
+// steps; only the summation order differs from a plain k loop, which the
+// contract leaves open. A lane thus reads its 32 codes of a weight row as two
+// 16-byte LDS reads and decodes them per step.
+//
+// LDS layout: each 64-byte weight row keeps its four 16-byte chunks rotated by
+// row / 4, each 128-byte activation row its eight chunks rotated by row / 2,
+// so the 16 lanes of a ds_read_b128 phase (16 consecutive rows, one chunk)
+// hit distinct bank groups. Tiles are dealt XCD-aware and each XCD starts an
+// eighth of k later, as in the W8A8 kernel.
+#include <stdio.h>
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "ring.hpp"
+
+namespace fp8w {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename A>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (std::is_same<A, Bf16>::value)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+}
+
+template <int BN, int BM, int WN, int WM>
+struct BatchCfg {
+    static constexpr int W = WN * WM;                  // waves
+    static constexpr int FN = BN / WN / 32;            // 32-channel fragments per wave
+    static constexpr int FM = BM / WM / 32;            // 32-token fragments per wave
+    static constexpr int ABLK = BN / 16;               // 1 KB load blocks of weight rows (16 rows x 64 codes)
+    static constexpr int BBLK = BM / 8;                // 1 KB load blocks of activation rows (8 rows x 64 values)
+    static constexpr int BLOCKS = ABLK + BBLK;
+    static constexpr int LOADS = (BLOCKS + W - 1) / W;  // per wave; the last round repeats blocks
+    static constexpr int ABYTES = BN * 64;
+    static constexpr int STAGE = ABYTES + BM * 128;
+    static_assert(FN >= 1 && FM >= 1 && BN == FN * WN * 32 && BM == FM * WM * 32, "tile and wave layout");
+    static_assert(LOADS * 2 < 64, "vmcnt range of the four-stage ring");
+};
+
+template <typename A, int BN, int BM, int WN, int WM>
+struct BatchPipe {
+    using C = BatchCfg<BN, BM, WN, WM>;
+    const uint8_t* q;   // [n, k]
+    const uint16_t* x;  // [m, k]
+    int64_t n, m, k, n0, m0;
+    int64_t S, rot;  // stages; the k stage this workgroup starts at
+    int lane, wave, wn, wm;
+
+    // Stage s covers k stage (s + rot) mod S. Block b < ABLK holds weight rows
+    // 16b .. 16b + 15 (lane l: row 16b + l / 4, slot l % 4, chunk (slot - row
+    // / 4) mod 4); block ABLK + b holds activation rows 8b .. 8b + 7 (lane l:
+    // row 8b + l / 8, slot l % 8, chunk (slot - row / 2) mod 8). Blocks are
+    // dealt to the waves in turn; when they do not divide evenly, waves repeat
+    // blocks of the first round (identical bytes to the same LDS address).
+    // Rows past n or m read the last real row; their results are not stored.
+    __device__ __forceinline__ void issue(int64_t s, uint8_t* buf) const
+    {
+        int64_t sr = s + rot;  // s < S and rot < S
+        sr = sr < S ? sr : sr - S;
+        const int64_t kb = sr * 64;
+#pragma unroll
+        for (int u = 0; u < C::LOADS; ++u) {
+            const int b = (wave * C::LOADS + u) % C::BLOCKS;
+            const void* src;
+            if (b < C::ABLK) {
+                const int r = 16 * b + (lane >> 2);
+                const int chunk = ((lane & 3) - (r >> 2)) & 3;
+                int64_t row = n0 + r;
+                row = row < n ? row : n - 1;
+                src = q + row * k + kb + 16 * chunk;
+            } else {
+                const int r = 8 * (b - C::ABLK) + (lane >> 3);
+                const int chunk = ((lane & 7) - (r >> 1)) & 7;
+                int64_t row = m0 + r;
+                row = row < m ? row : m - 1;
+                src = x + row * k + kb + 8 * chunk;
+            }
+            __builtin_amdgcn_global_load_lds(src, FP8W_LDS(buf + 1024 * b), 16, 0, 0);
+        }
+    }
+
+    // one stage: FN weight and FM token fragments, four MFMA steps each pair
+    __device__ __forceinline__ void compute(const uint8_t* buf, f32x16* acc) const
+    {
+        const int i = lane & 31, h = lane >> 5;
+        u32x4 wc[C::FN][2];  // 32 codes of the lane's weight row: k 32h .. 32h + 31
+#pragma unroll
+        for (int f = 0; f < C::FN; ++f) {
+            const int r = wn * (BN / WN) + 32 * f + i;
+            const uint8_t* p = buf + 64 * r;
+            wc[f][0] = *reinterpret_cast<const u32x4*>(p + 16 * ((2 * h + (r >> 2)) & 3));
+            wc[f][1] = *reinterpret_cast<const u32x4*>(p + 16 * ((2 * h + 1 + (r >> 2)) & 3));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x4 a[C::FN], b[C::FM];
+#pragma unroll
+            for (int f = 0; f < C::FN; ++f) {
+                const u32x4& c = wc[f][j >> 1];
+                const u32x2 d0 = A::decode4((j & 1) ? c.z : c.x);
+                const u32x2 d1 = A::decode4((j & 1) ? c.w : c.y);
+                a[f] = u32x4{d0.x, d0.y, d1.x, d1.y};
+            }
+#pragma unroll
+            for (int f = 0; f < C::FM; ++f) {
+                const int r = wm * (BM / WM) + 32 * f + i;
+                b[f] = *reinterpret_cast<const u32x4*>(buf + C::ABYTES + 128 * r + 16 * ((4 * h + j + (r >> 1)) & 7));
+            }
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < C::FM; ++fm)
+                    acc[fn * C::FM + fm] = mfma32<A>(a[fn], b[fm], acc[fn * C::FM + fm]);
+        }
+    }
+};
+
+// Requires k % 256 == 0 (k / 64 stages, a multiple of the four-stage ring); x
+// and q 16-byte aligned.
+template <typename A, int BN, int BM, int WN, int WM, int GM = 4>
+__global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* __restrict__ x,
+                                                              const uint8_t* __restrict__ q,
+                                                              const float* __restrict__ scale,
+                                                              const uint16_t* __restrict__ bias,
+                                                              uint16_t* __restrict__ y, int64_t m, int64_t n,
+                                                              int64_t k)
+{
+    using P = BatchPipe<A, BN, BM, WN, WM>;
+    using C = typename P::C;
+    static_assert(BN <= C::W * kWave, "one epilogue operand per thread");
+    __shared__ __attribute__((aligned(1024))) uint8_t b0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t b1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t b2[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t b3[C::STAGE];
+    __shared__ __attribute__((aligned(16))) float e_scale[BN];
+    __shared__ __attribute__((aligned(16))) uint16_t e_bias[BN];
+
+    int64_t tn, tm;
+    xcd_tile_of<GM>(tn, tm);
+    P p;
+    p.q = q;
+    p.x = x;
+    p.n = n;
+    p.m = m;
+    p.k = k;
+    p.n0 = tn * BN;
+    p.m0 = tm * BM;
+    p.lane = threadIdx.x & (kWave - 1);
+    p.wave = threadIdx.x / kWave;
+    p.wn = p.wave % WN;
+    p.wm = p.wave / WN;
+    p.S = k / 64;
+    // the workgroups one XCD holds walk k in step; the XCDs start an eighth of k apart
+    p.rot = ((blockIdx.x + (int64_t)gridDim.x * blockIdx.y) % 8) * (p.S / 8);
+
+    // epilogue operands of the tile's channels, one per thread: loaded before
+    // the ring, held in registers through it (their latency overlaps the
+    // ring's), then passed through LDS
+    const int tt = threadIdx.x;
+    float r_scale = 0.0f;
+    uint16_t r_bias = 0;
+    if (tt < BN) {
+        const int64_t c = p.n0 + tt < n ? p.n0 + tt : n - 1;
+        r_scale = scale[c];
+        r_bias = bias_bits(bias, c);
+    }
+
+    f32x16 acc[C::FN * C::FM];
+#pragma unroll
+    for (int f = 0; f < C::FN * C::FM; ++f)
+        acc[f] = f32x16{0.0f};
+    run_ring<4, C::LOADS>(p, p.S, b0, b1, b2, b3, acc);
+    if (tt < BN) {
+        e_scale[tt] = r_scale;
+        e_bias[tt] = r_bias;
+    }
+    __syncthreads();
+
+    // lane (i, h) holds channels 8j + 4h + r (r = 0..3) of token i in
+    // accumulators 4j + r of each fragment
+    const int i = p.lane & 31, h = p.lane >> 5;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+        const int64_t t = p.m0 + p.wm * (BM / WM) + 32 * fm + i;
+        if (t >= m)
+            continue;
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+            const f32x16 d = acc[fn * C::FM + fm];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int cl = p.wn * (BN / WN) + 32 * fn + 8 * j + 4 * h;
+                const int64_t c0 = p.n0 + cl;
+                const f32x4 s4 = *reinterpret_cast<const f32x4*>(&e_scale[cl]);
+                const u32x2 b4 = *reinterpret_cast<const u32x2*>(&e_bias[cl]);
+                const uint16_t bb[4] = {(uint16_t)(b4.x & 0xffffu), (uint16_t)(b4.x >> 16), (uint16_t)(b4.y & 0xffffu),
+                                        (uint16_t)(b4.y >> 16)};
+                uint16_t o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[r] = epilogue<A>(d[4 * j + r], s4[r], bb[r]);
+                uint16_t* dst = y + t * n + c0;
+                if (c0 + 3 < n && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+                    u32x2 pk;
+                    pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+                    pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+                    *reinterpret_cast<u32x2*>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (c0 + r < n)
+                            dst[r] = o[r];
+                }
+            }
+        }
+    }
+}
+
+template <typename A, int BN, int BM, int WN, int WM>
+hipError_t launch_b(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
+                    int64_t n, void* y, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(WN * WM * kWave);
+    hipLaunchKernelGGL((batch_kernel<A, BN, BM, WN, WM>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
+                       scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
+    return hipGetLastError();
+}
+
+// Tile choice: the largest tile that still gives at least 224 workgroups (7/8
+// of the CUs), in the order 256 x 128, 128 x 128, 128 x 64, 64 x 64, 64 x 32,
+// 32 x 32 (channels x tokens); the smallest below that.
+struct BatchTile {
+    int bn, bm, wn, wm;
+};
+
+constexpr BatchTile kBatchTiles[] = {{256, 128, 2, 4}, {128, 128, 2, 4}, {128, 64, 4, 2},
+                                     {64, 64, 2, 2},   {64, 32, 2, 1},   {32, 32, 1, 1}};
+
+BatchTile batch_tile(int64_t m, int64_t n)
+{
+    for (const BatchTile& t : kBatchTiles)
+        if (((n + t.bn - 1) / t.bn) * ((m + t.bm - 1) / t.bm) >= 224)
+            return t;
+    return kBatchTiles[sizeof(kBatchTiles) / sizeof(kBatchTiles[0]) - 1];
+}
+
+template <typename A>
+hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
+                        int64_t n, void* y, hipStream_t stream)
+{
+    const BatchTile t = batch_tile(m, n);
+    if (t.bn == 256)
+        return launch_b<A, 256, 128, 2, 4>(x, m, k, q, scale, bias, n, y, stream);
+    if (t.bn == 128 && t.bm == 128)
+        return launch_b<A, 128, 128, 2, 4>(x, m, k, q, scale, bias, n, y, stream);
+    if (t.bn == 128)
+        return launch_b<A, 128, 64, 4, 2>(x, m, k, q, scale, bias, n, y, stream);
+    if (t.bm == 64)
+        return launch_b<A, 64, 64, 2, 2>(x, m, k, q, scale, bias, n, y, stream);
+    if (t.bn == 64)
+        return launch_b<A, 64, 32, 2, 1>(x, m, k, q, scale, bias, n, y, stream);
+    return launch_b<A, 32, 32, 1, 1>(x, m, k, q, scale, bias, n, y, stream);
+}
+
+}  // namespace
+
+hipError_t launch_batch(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
+                        const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    if (m == 0 || n == 0)
+        return hipSuccess;
+    if (k % 256 != 0 || k == 0)
+        return hipErrorInvalidValue;
+    if (act == Act::BF16)
+        return launch_typed<Bf16>(x, m, k, q, scale, bias, n, y, stream);
+    if (act == Act::FP16)
+        return launch_typed<F16>(x, m, k, q, scale, bias, n, y, stream);
+    return hipErrorInvalidValue;
+}
+
+const char* batch_kernel_name(int64_t m, int64_t n)
+{
+    thread_local char name[64];
+    const BatchTile t = batch_tile(m, n);
+    snprintf(name, sizeof name, "batch_kernel<BN=%d,BM=%d,W=%d>", t.bn, t.bm, t.wn * t.wm);
+    return name;
+}
+
+}  // namespace fp8w

@@ -38,6 +38,14 @@ size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 // thread-local string; for tests and measurement reports).
 const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace);
 
+// The linear for m > 32 (any m >= 1): a GEMM over BN x BM tiles that decodes the
+// codes in its main loop; k % 256 == 0, x and q 16-byte aligned.
+hipError_t launch_batch(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
+                        const void* bias, int64_t n, void* y, hipStream_t stream);
+
+// Name of the batch kernel tile launch_batch picks for this shape.
+const char* batch_kernel_name(int64_t m, int64_t n);
+
 // Dequantize codes to out_type: value(q) * scale[r] (scale != nullptr) or the
 // exact unscaled value (scale == nullptr).
 hipError_t launch_dequantize(const uint8_t* q, const float* scale, int64_t n, int64_t k, void* out,

@@ -106,4 +106,24 @@ __device__ __forceinline__ void run_ring(const P& p, int64_t S, uint8_t* b0, uin
     }
 }
 
+// Tile (tn, tm) of workgroup (blockIdx.x, blockIdx.y). Workgroups are dealt
+// to the 8 XCDs in turn by linear id L: XCD x = L % 8 is given the contiguous
+// range of tile ids that starts at x * (T / 8) + min(x, T % 8), walked in the
+// order that fills groups of GM tile rows (GM token tiles x all channel
+// tiles) column by column, so the tiles one XCD holds at a time form a
+// GM x (32 / GM) block. A bijection of [0, T).
+template <int GM>
+__device__ __forceinline__ void xcd_tile_of(int64_t& tn, int64_t& tm)
+{
+    const int64_t TN = gridDim.x, TM = gridDim.y, T = TN * TM;
+    const int64_t L = blockIdx.x + TN * blockIdx.y;
+    const int64_t xcd = L % 8, loc = L / 8, q = T / 8, r = T % 8;
+    const int64_t id = xcd * q + (xcd < r ? xcd : r) + loc;
+    const int64_t grp = id / (GM * TN), first = grp * GM;
+    const int64_t gs = TM - first < GM ? TM - first : GM;
+    const int64_t w = id - grp * GM * TN;
+    tm = first + w % gs;
+    tn = w / gs;
+}
+
 }  // namespace fp8w

@@ -172,26 +172,6 @@ struct W8Pipe {
     }
 };
 
-// Tile (tn, tm) of workgroup (blockIdx.x, blockIdx.y). Workgroups are dealt
-// to the 8 XCDs in turn by linear id L: XCD x = L % 8 is given the contiguous
-// range of tile ids that starts at x * (T / 8) + min(x, T % 8), walked in the
-// order that fills groups of GM tile rows (GM token tiles x all channel
-// tiles) column by column, so the tiles one XCD holds at a time form a
-// GM x (32 / GM) block. A bijection of [0, T).
-template <int GM>
-__device__ __forceinline__ void tile_of(int64_t& tn, int64_t& tm)
-{
-    const int64_t TN = gridDim.x, TM = gridDim.y, T = TN * TM;
-    const int64_t L = blockIdx.x + TN * blockIdx.y;
-    const int64_t xcd = L % 8, loc = L / 8, q = T / 8, r = T % 8;
-    const int64_t id = xcd * q + (xcd < r ? xcd : r) + loc;
-    const int64_t grp = id / (GM * TN), first = grp * GM;
-    const int64_t gs = TM - first < GM ? TM - first : GM;
-    const int64_t w = id - grp * GM * TN;
-    tm = first + w % gs;
-    tn = w / gs;
-}
-
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>)
@@ -259,7 +239,7 @@ __global__ __launch_bounds__(WN* WM * kWave) void w8a8_kernel(const uint8_t* __r
     };
 
     int64_t tn, tm;
-    tile_of<GM>(tn, tm);
+    xcd_tile_of<GM>(tn, tm);
     P p;
     p.qw = qw;
     p.qx = qx;

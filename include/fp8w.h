@@ -71,6 +71,7 @@ typedef enum {
 #define FP8W_PATH_GEMV 0     /* m == 1 streaming GEMV (fp32 FMA) */
 #define FP8W_PATH_SKINNY 1   /* 1 <= m <= 32, matrix-core (MFMA) skinny GEMM */
 #define FP8W_PATH_FALLBACK 2 /* unscaled dequantise to the activation dtype + guarded MFMA GEMM */
+#define FP8W_PATH_BATCH 3    /* m > 32: tiled MFMA GEMM that decodes the codes in its main loop */
 
 /*
  * Build-time quantizer ("The contract": scale = amax(|row|) / 448, codes
@@ -106,8 +107,9 @@ FP8W_API fp8w_status_t fp8w_quantize(const void* w, fp8w_dtype_t w_dtype, int64_
  *             channels) use it for fp32 partial sums of a k split (16-byte
  *             aligned); given less, they take a slower single-pass plan
  *             instead, with no error.
- * Dispatch (fp8w_linear_path): the fast kernels take 1 <= m <= 32 with
- * k % 256 == 0 and x, q 16-byte aligned (m == 1: GEMV, else skinny MFMA);
+ * Dispatch (fp8w_linear_path): the fast kernels take k % 256 == 0 with x, q
+ * 16-byte aligned: m == 1 the GEMV, 2 <= m <= 32 the skinny MFMA kernel, m > 32
+ * the batch GEMM (which decodes the codes in its main loop, no workspace);
  * everything else takes the fallback. Results of different paths and plans
  * agree to within fp32 summation-order rounding; a given call is
  * deterministic. Asynchronous; a failed launch returns FP8W_ERR_HIP.
@@ -118,9 +120,9 @@ FP8W_API fp8w_status_t fp8w_linear(const void* x, fp8w_dtype_t act_dtype, int64_
 
 /*
  * fp8w_linear with an explicit path (FP8W_PATH_*), for cross-checking the
- * kernels against one another. FP8W_PATH_GEMV needs m == 1 and
- * FP8W_PATH_SKINNY needs m <= 32, both with k % 256 == 0
- * (FP8W_ERR_INVALID_VALUE otherwise) and 16-byte aligned x and q
+ * kernels against one another. FP8W_PATH_GEMV needs m == 1,
+ * FP8W_PATH_SKINNY needs m <= 32 and FP8W_PATH_BATCH takes any m, all with
+ * k % 256 == 0 (FP8W_ERR_INVALID_VALUE otherwise) and 16-byte aligned x and q
  * (FP8W_ERR_MISALIGNED otherwise). FP8W_PATH_FALLBACK takes any shape and needs
  * n * k * element_size(act_dtype) bytes of workspace.
  */
@@ -145,8 +147,8 @@ FP8W_API fp8w_status_t fp8w_dequantize_fallback(const uint8_t* q, const float* s
 
 /*
  * Which path fp8w_linear takes for these sizes and pointers: FP8W_PATH_GEMV,
- * FP8W_PATH_SKINNY or FP8W_PATH_FALLBACK; -1 when the arguments are invalid.
- * NULL pointers are treated as 256-byte aligned.
+ * FP8W_PATH_SKINNY, FP8W_PATH_BATCH or FP8W_PATH_FALLBACK; -1 when the
+ * arguments are invalid. NULL pointers are treated as 256-byte aligned.
  */
 FP8W_API int fp8w_linear_path(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x, const uint8_t* q,
                      const void* y);
@@ -206,7 +208,8 @@ FP8W_API fp8w_status_t fp8w_linear_grouped_with_path(const void* x, fp8w_dtype_t
                                                      const void* bias, int64_t n, void* y, int path,
                                                      hipStream_t stream);
 
-/* Path fp8w_linear_grouped takes (FP8W_PATH_*), -1 when the arguments are invalid. */
+/* Path fp8w_linear_grouped takes (FP8W_PATH_GEMV, _SKINNY or _FALLBACK; grouped
+   calls above 32 tokens take the generic kernel), -1 when the arguments are invalid. */
 FP8W_API int fp8w_linear_grouped_path(int64_t m, int64_t n, int64_t k, int64_t group, fp8w_dtype_t act_dtype,
                                       const void* x, const uint8_t* q);
 

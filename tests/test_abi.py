@@ -58,7 +58,10 @@ def test_path_selection():
     assert p(1, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_GEMV
     assert p(2, 4096, 4096, fw.FP16, X, Q, Y) == fw.PATH_SKINNY
     assert p(32, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_SKINNY
-    assert p(33, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK
+    assert p(33, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_BATCH
+    assert p(4096, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_BATCH
+    assert p(64, 4096, 4100, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK      # k % 256 != 0
+    assert p(64, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_FALLBACK  # q not 16-B aligned
     assert p(1, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK      # k % 256 != 0
     assert p(1, 100, 128, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # k < 256
     assert p(1, 100, 0, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK           # k == 0
@@ -105,6 +108,15 @@ def test_kernel_names():
     assert kn(A, 3, 100, 4096, fw.BF16, X + 2, Q) == "dequantize_kernel+fallback_gemm_kernel"  # x unaligned
     assert kn(fw.PATH_GEMV, 2, 4096, 4096, fw.BF16, X, Q) is None
     assert kn(fw.PATH_SKINNY, 33, 4096, 4096, fw.BF16, X, Q) is None
+    assert kn(A, 33, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=32,BM=32,W=1>"
+    assert kn(A, 64, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=64,BM=64,W=4>"
+    assert kn(A, 256, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=128,BM=128,W=8>"
+    assert kn(A, 128, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=128,BM=64,W=8>"
+    assert kn(A, 128, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=64,BM=32,W=2>"
+    assert kn(A, 512, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=256,BM=128,W=8>"
+    assert kn(A, 2048, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=256,BM=128,W=8>"
+    assert kn(fw.PATH_BATCH, 1, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=32,BM=32,W=1>"
+    assert kn(fw.PATH_BATCH, 64, 4096, 4100, fw.BF16, X, Q) is None     # k % 256 != 0
     assert kn(A, 1, 4096, 4096, fw.FP32, X, Q) is None
     assert kn(7, 1, 4096, 4096, fw.BF16, X, Q) is None
 
@@ -114,7 +126,8 @@ def test_workspace_bytes():
     assert wb(1, 4096, 4096, fw.BF16, X, Q, Y) == 0
     assert wb(16, 4096, 4096, fw.BF16, X, Q, Y) == 0
     assert wb(4, 28672, 8200, fw.BF16, X, Q, Y) == 28672 * 8200 * 2
-    assert wb(64, 100, 512, fw.FP16, X, Q, Y) == 100 * 512 * 2
+    assert wb(64, 100, 500, fw.FP16, X, Q, Y) == 100 * 500 * 2           # k % 256 != 0: fallback
+    assert wb(64, 100, 512, fw.FP16, X, Q, Y) == 0                       # batch kernel
     assert wb(1, 10, 0, fw.BF16, X, Q, Y) == 0
     assert wb(1, 4096, 4096, fw.FP32, X, Q, Y) == 0
     assert wb(32, 8192, 28672, fw.BF16, X, Q, Y) == 2 * 32 * 8192 * 4     # split k
@@ -143,13 +156,18 @@ def test_linear_rejects_invalid_arguments():
     assert _lin(s=S + 2) == fw.ERR_MISALIGNED
     assert _lin(b=B + 1) == fw.ERR_MISALIGNED
     assert _lin(y=Y + 1) == fw.ERR_MISALIGNED
-    assert _lin(path=3) == fw.ERR_INVALID_VALUE
+    assert _lin(path=4) == fw.ERR_INVALID_VALUE
     assert _lin(path=-2) == fw.ERR_INVALID_VALUE
     # forced paths the shape cannot take
     assert _lin(m=2, path=fw.PATH_GEMV) == fw.ERR_INVALID_VALUE
     assert _lin(m=33, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
     assert _lin(k=4000, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
     assert _lin(m=1, x=X + 2, path=fw.PATH_GEMV) == fw.ERR_MISALIGNED
+    assert _lin(m=64, k=4000, path=fw.PATH_BATCH) == fw.ERR_INVALID_VALUE
+    assert _lin(m=64, k=128, path=fw.PATH_BATCH) == fw.ERR_INVALID_VALUE
+    assert _lin(m=64, q=Q + 8, path=fw.PATH_BATCH) == fw.ERR_MISALIGNED
+    assert _lin(m=64, x=X + 2, path=fw.PATH_BATCH) == fw.ERR_MISALIGNED
+    assert _lin(m=64, y=X + 64, path=fw.PATH_BATCH) == fw.ERR_INVALID_VALUE
     # y overlapping an input
     assert _lin(y=X + 64) == fw.ERR_INVALID_VALUE
     assert _lin(y=Q) == fw.ERR_INVALID_VALUE
@@ -177,6 +195,8 @@ def test_zero_sized_calls_succeed_without_a_device():
     assert _lin(m=0) == fw.SUCCESS
     assert _lin(n=0) == fw.SUCCESS
     assert _lin(m=0, x=0, y=0) == fw.SUCCESS
+    assert _lin(m=0, path=fw.PATH_BATCH) == fw.SUCCESS
+    assert _lin(m=64, n=0, path=fw.PATH_BATCH) == fw.SUCCESS
     assert fw.fp8w_quantize(0, fw.FP32, 0, 100, 0, 0, 0) == fw.SUCCESS
     assert fw.fp8w_dequantize_fallback(0, 0, 0, 100, 0, fw.BF16, 0) == fw.SUCCESS
     assert fw.fp8w_dequantize_fallback(Q, S, 100, 0, 0, fw.BF16, 0) == fw.SUCCESS

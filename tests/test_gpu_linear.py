@@ -17,7 +17,7 @@ from parity_util import assert_gate, assert_same_bits, nan_like, oracle_case
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-PATHS = {fw.PATH_GEMV: "gemv", fw.PATH_SKINNY: "skinny", fw.PATH_FALLBACK: "fallback"}
+PATHS = {fw.PATH_GEMV: "gemv", fw.PATH_SKINNY: "skinny", fw.PATH_FALLBACK: "fallback", fw.PATH_BATCH: "batch"}
 
 
 def _prepare(case):
@@ -60,7 +60,8 @@ SMALL = [
     (12, 40, 768, torch.float16, False, fw.PATH_SKINNY),
     (20, 8192, 512, torch.float16, True, fw.PATH_SKINNY),
     (3, 8192, 1024, torch.bfloat16, True, fw.PATH_SKINNY),
-    (33, 64, 512, torch.bfloat16, True, fw.PATH_FALLBACK),
+    (33, 64, 512, torch.bfloat16, True, fw.PATH_BATCH),
+    (300, 200, 768, torch.float16, False, fw.PATH_BATCH),
     (70, 40, 300, torch.float16, True, fw.PATH_FALLBACK),
     (1, 77, 8200, torch.bfloat16, True, fw.PATH_FALLBACK),
     (3, 50, 1, torch.bfloat16, True, fw.PATH_FALLBACK),
@@ -149,11 +150,11 @@ def test_split_k_matches_single_pass(m, n, k, splits, dtype):
 @pytest.mark.parametrize("m,k", [(1, 256), (1, 4096), (2, 1024), (16, 768), (17, 512), (32, 2048)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 def test_every_path_matches_the_oracle(m, k, dtype):
-    """Forced paths on covered shapes: the GEMV (m == 1), the skinny MFMA kernel
-    and the fallback each pass the gate on the same inputs."""
+    """Forced paths on covered shapes: the GEMV (m == 1), the skinny MFMA kernel,
+    the batch GEMM and the fallback each pass the gate on the same inputs."""
     n = 200
     case = workloads.random_case(7 + m + k, m, n, k, dtype)
-    paths = [fw.PATH_SKINNY, fw.PATH_FALLBACK] + ([fw.PATH_GEMV] if m == 1 else [])
+    paths = [fw.PATH_SKINNY, fw.PATH_FALLBACK, fw.PATH_BATCH] + ([fw.PATH_GEMV] if m == 1 else [])
     outs = {}
     for p in paths:
         print(f"forced path {PATHS[p]} m={m} k={k} {dtype}", flush=True)
@@ -169,7 +170,9 @@ def test_every_path_matches_the_oracle(m, k, dtype):
                                         (fw.PATH_SKINNY, 6, 256, 512), (fw.PATH_SKINNY, 12, 256, 512),
                                         (fw.PATH_SKINNY, 20, 256, 512), (fw.PATH_FALLBACK, 2, 256, 512),
                                         (fw.PATH_SKINNY, 2, 12288, 1024), (fw.PATH_SKINNY, 12, 256, 2048),
-                                        (fw.PATH_SKINNY, 20, 8192, 1024), (fw.PATH_SKINNY, 32, 16384, 512)])
+                                        (fw.PATH_SKINNY, 20, 8192, 1024), (fw.PATH_SKINNY, 32, 16384, 512),
+                                        (fw.PATH_BATCH, 2, 256, 512), (fw.PATH_BATCH, 40, 300, 256),
+                                        (fw.PATH_BATCH, 130, 7168, 256), (fw.PATH_BATCH, 300, 14336, 256)])
 def test_all_256_codes_decode_exactly_on_each_path(dtype, path, m, n, k):
     """q[n, :] = n mod 256 for every code, unit scales and a one-hot x: y[n] is
     the exact value of its code (0x7F / 0xFF give NaN). Pins each kernel's
@@ -198,7 +201,7 @@ def test_all_256_codes_decode_exactly_on_each_path(dtype, path, m, n, k):
             assert np.all(yv[r][fin] == 0.0)
 
 
-@pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK])
+@pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK, fw.PATH_BATCH])
 def test_all_ones_closed_form(path):
     """x = 1 and rows W[n,:] = c_n: all codes are 0x7E, so y = fl32(c_n/448)*448*K + b."""
     k = 2048
@@ -218,7 +221,7 @@ def test_all_ones_closed_form(path):
     assert np.all(np.abs(got - expect[None, :]) <= np.abs(expect)[None, :] * 2.0 ** -8)
 
 
-@pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK])
+@pytest.mark.parametrize("path", [fw.PATH_GEMV, fw.PATH_SKINNY, fw.PATH_FALLBACK, fw.PATH_BATCH])
 def test_zero_rows_give_bias_exactly(path):
     lay = workloads.block_layer(0)
     w = lay.w[:512].copy()
