@@ -42,7 +42,9 @@ Also reported ("extra"): latency-bound calls (the 1024 x 1024 GEMV and the
 x [22,1024] x [1024,4096] shape the pages time), the skinny sweep (M = 2..32,
 fp16), one decoder block at M = 16 (seven calls, and four with q/k/v and
 gate/up merged; eager and graph-replayed steps), the large shapes and their
-K = 8200 fallback, each with the same cache rotation; the W8A8 layer at
+K = 8200 fallback, each with the same cache rotation; batched decode
+("batch": the decode weights at M = 64 / 128 / 256, the weight-only batch GEMM,
+against HBM and against the 2.5 PFLOP/s bf16 matrix-core peak); the W8A8 layer at
 prefill batches ("w8a8": M = 512 / 2048 / 4096 on the block's three distinct
 shapes, in TFLOP/s against the 5.0 PFLOP/s dense e4m3 matrix-core peak; the
 whole layer, its GEMM and its activation quantizer); the build-time quantize;
@@ -53,7 +55,7 @@ whose leg also checks this run's GPU results against the oracle results it
 produced.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--spin-ms MS] [--quick]
-                       [--only tiny|skinny|block|large|grouped|w8a8 ...] [--reps R]
+                       [--only tiny|skinny|block|large|batch|grouped|w8a8 ...] [--reps R]
 Profile helpers: --trace-summary CSV [--last N], --mfma-summary CSV N K,
 --pmc-summary FETCH_CSV WRITE_CSV.
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -193,7 +195,7 @@ class Call:
             ws = torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None
         self.ws = ws
         act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
-        self.path = ["gemv", "skinny", "fallback"][fw.linear_path(x, layer.qs[0][0])]
+        self.path = ["gemv", "skinny", "fallback", "batch"][fw.linear_path(x, layer.qs[0][0])]
         self.args = [(x.data_ptr(), act, self.m, layer.k, q.data_ptr(), s.data_ptr(),
                       0 if layer.bias is None else layer.bias.data_ptr(), layer.n, self.y.data_ptr(),
                       0 if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel())
@@ -360,7 +362,7 @@ def call_report(call, us):
     act = fw.BF16 if call.x.dtype == torch.bfloat16 else fw.FP16
     kernel = fw.fp8w_linear_kernel(fw.PATH_AUTO, call.m, call.layer.n, call.layer.k, act, call.x.data_ptr(),
                                    call.layer.qs[0][0].data_ptr())
-    if call.path == "skinny" and call.ws is None and "splitk" in kernel:
+    if call.path in ("skinny", "batch") and call.ws is None and "splitk" in kernel:
         kernel = "single pass (no workspace)"
     useful = 2.0 * call.m * call.layer.n * call.layer.k
     r = {"layer": call.layer.name, "m": call.m, "n": call.layer.n, "k": call.layer.k, "path": call.path,
@@ -862,7 +864,7 @@ def mfma_summary(csv_path, n, k):
     print("\n".join(lines))
 
 
-SECTIONS = ("tiny", "skinny", "block", "large", "grouped", "w8a8")
+SECTIONS = ("tiny", "skinny", "block", "large", "batch", "grouped", "w8a8")
 
 
 def extra_sections(dev, stream, reps=100, only=None):
@@ -991,6 +993,27 @@ def extra_sections(dev, stream, reps=100, only=None):
             del L
             torch.cuda.empty_cache()
         ex["large"] = lg
+
+    if "batch" in want:
+        # batched decode: the decode weights at M = 64, 128, 256 (bf16), the
+        # weight-only batch GEMM (k split over workgroups where its plan asks,
+        # workspace given); bytes against HBM and FLOPs against the bf16 matrix cores
+        bt = []
+        for i in range(len(workloads.DECODE_SHAPES)):
+            lw = workloads.decode_layer(i)
+            n, k = lw.w.shape
+            L = Layer(lw, max(1, math.ceil(ROTATE_BYTES / (n * k))), dev)
+            for m in workloads.BATCH_MS:
+                c = Call(L, workloads.batch_x(i, m).to(dev), dev)
+                r = call_report(c, burst(c, max(20, reps // 2), 5, stream))
+                r["pct_bf16_mfma_peak"] = round(100.0 * r["tflops"] / MFMA_PEAK_TFLOPS, 2)
+                bt.append(r)
+                log(f"  batch {L.name} m={m}: {r['us_per_call']:.2f} us {r['gbps']:.0f} GB/s ({r['pct_peak']:.1f}% "
+                    f"of 8 TB/s), {r['tflops']:.0f} TFLOP/s ({r['pct_bf16_mfma_peak']:.1f}% of 2.5 PF) [{r['kernel']}]")
+                del c
+            del L
+            torch.cuda.empty_cache()
+        ex["batch"] = bt
 
     if "w8a8" in want:
         # prefill: the W8A8 layer on the decoder block's three distinct shapes

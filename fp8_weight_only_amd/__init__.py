@@ -266,10 +266,10 @@ def linear(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Te
 
     x: [m, k] bf16 / fp16; q: [n, k] uint8 codes; scale: [n] fp32; bias: [n]
     of x.dtype or None. ``workspace`` (any device tensor) is what the C ABI
-    calls workspace: needed on the fallback path, used for a k split on a few
-    skinny shapes. When it is None and the call uses one, one of
+    calls workspace: needed on the fallback path, used for a k split on some
+    skinny and batch shapes. When it is None and the call uses one, one of
     fp8w_linear_workspace_bytes is allocated here with torch; an empty tensor
-    makes such skinny shapes take their single-pass plan."""
+    makes such shapes take their single-pass plan."""
     if x.dim() != 2 or q.dim() != 2 or q.dtype != torch.uint8 or scale.dtype != torch.float32:
         raise ValueError("expected x [m,k], q uint8 [n,k], scale fp32 [n]")
     m, k = x.shape
@@ -291,9 +291,10 @@ def linear(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Te
     bp = _dev(bias, "bias") if bias is not None and n else 0
     yp = _dev(out, "out") if out.numel() else 0
     auto = fp8w_linear_path(m, n, k, act, xp, qp, yp)
-    if path == PATH_FALLBACK or (path == PATH_AUTO and auto == PATH_FALLBACK):
+    eff = auto if path == PATH_AUTO else path
+    if eff == PATH_FALLBACK:
         need = n * k * 2
-    elif path in (PATH_AUTO, PATH_SKINNY) and auto == PATH_SKINNY:
+    elif eff in (PATH_SKINNY, PATH_BATCH) and eff == auto:
         need = fp8w_linear_workspace_bytes(m, n, k, act, xp, qp, yp)
     else:
         need = 0

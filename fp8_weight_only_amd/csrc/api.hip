@@ -161,8 +161,19 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
     const fp8w::Act a = act_of(act);
     if (path == FP8W_PATH_GEMV)
         return hip_status(fp8w::launch_gemv(x, a, k, q, scale, bias, n, y, stream));
-    if (path == FP8W_PATH_BATCH)
-        return hip_status(fp8w::launch_batch(x, a, m, k, q, scale, bias, n, y, stream));
+    if (path == FP8W_PATH_BATCH) {
+        // split k on plans that use it, when the caller's workspace is large enough
+        const size_t need = fp8w::batch_workspace_bytes(m, n, k);
+        const bool use_ws = need > 0 && ws && ws_bytes >= need;
+        if (use_ws) {
+            if (!aligned(ws, 16))
+                return FP8W_ERR_MISALIGNED;
+            if (ws_overlaps(ws, need, x, m, k, q, scale, bias, n, y))
+                return FP8W_ERR_INVALID_VALUE;
+        }
+        return hip_status(fp8w::launch_batch(x, a, m, k, q, scale, bias, n, y, use_ws ? ws : nullptr,
+                                             use_ws ? ws_bytes : 0, stream));
+    }
     if (path == FP8W_PATH_SKINNY) {
         // split k on shapes that use it, when the caller's workspace is large enough
         const size_t need = fp8w::skinny_workspace_bytes(m, n, k);
@@ -523,6 +534,8 @@ size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t
     const int p = fp8w_linear_path(m, n, k, act_dtype, x, q, y);
     if (p == FP8W_PATH_SKINNY)
         return fp8w::skinny_workspace_bytes(m, n, k);
+    if (p == FP8W_PATH_BATCH)
+        return fp8w::batch_workspace_bytes(m, n, k);
     if (p != FP8W_PATH_FALLBACK)
         return 0;
     return fallback_workspace(n, k, act_dtype);
@@ -540,8 +553,9 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
             return nullptr;
         return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(n, k) : fp8w::skinny_kernel_name(m, n, k, true);
     }
-    if (path == FP8W_PATH_BATCH)
-        return m >= 1 && fast_k(k) ? fp8w::batch_kernel_name(m, n) : nullptr;
+    if (path == FP8W_PATH_BATCH)  // the workspace fp8w_linear_workspace_bytes reports exists only on the batch path
+        return m >= 1 && fast_k(k) ? fp8w::batch_kernel_name(m, n, k, auto_path(m, k, x, q) == FP8W_PATH_BATCH)
+                                   : nullptr;
     if (path == FP8W_PATH_FALLBACK)
         return fp8w::fallback_kernel_name(m, n, k, x);
     return nullptr;

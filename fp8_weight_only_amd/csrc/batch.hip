@@ -22,6 +22,12 @@
 // contract leaves open. A lane thus reads its 32 codes of a weight row as two
 // 16-byte LDS reads and decodes them per step.
 //
+// Split k: with too few tiles to fill the chip (few tokens, or few channels),
+// k is split over grid.z; each workgroup writes the fp32 sums of its k range to
+// the caller's workspace and the skinny path's reduce kernel adds them in split
+// order and applies the epilogue (deterministic). The plan (tile and split
+// count) comes from a cost model fitted to measured plans (batch_plan).
+//
 // LDS layout: each 64-byte weight row keeps its four 16-byte chunks rotated by
 // row / 4, each 128-byte activation row its eight chunks rotated by row / 2,
 // so the 16 lanes of a ds_read_b128 phase (16 consecutive rows, one chunk)
@@ -146,13 +152,16 @@ struct BatchPipe {
 
 // Requires k % 256 == 0 (k / 64 stages, a multiple of the four-stage ring); x
 // and q 16-byte aligned.
+// grid.z > 1 splits k: workgroup row z owns k range [z * kc, (z + 1) * kc),
+// kc = k / gridDim.z (a multiple of 256), and writes fp32 sums to part
+// ([gridDim.z, m, n]) instead of y.
 template <typename A, int BN, int BM, int WN, int WM, int GM = 4>
 __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* __restrict__ x,
                                                               const uint8_t* __restrict__ q,
                                                               const float* __restrict__ scale,
                                                               const uint16_t* __restrict__ bias,
                                                               uint16_t* __restrict__ y, int64_t m, int64_t n,
-                                                              int64_t k)
+                                                              int64_t k, float* __restrict__ part)
 {
     using P = BatchPipe<A, BN, BM, WN, WM>;
     using C = typename P::C;
@@ -166,19 +175,20 @@ __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* _
 
     int64_t tn, tm;
     xcd_tile_of<GM>(tn, tm);
+    const int64_t kc = k / gridDim.z;
     P p;
-    p.q = q;
-    p.x = x;
+    p.q = q + (int64_t)blockIdx.z * kc;
+    p.x = x + (int64_t)blockIdx.z * kc;
     p.n = n;
     p.m = m;
-    p.k = k;
+    p.k = k;  // row stride
     p.n0 = tn * BN;
     p.m0 = tm * BM;
     p.lane = threadIdx.x & (kWave - 1);
     p.wave = threadIdx.x / kWave;
     p.wn = p.wave % WN;
     p.wm = p.wave / WN;
-    p.S = k / 64;
+    p.S = kc / 64;
     // the workgroups one XCD holds walk k in step; the XCDs start an eighth of k apart
     p.rot = ((blockIdx.x + (int64_t)gridDim.x * blockIdx.y) % 8) * (p.S / 8);
 
@@ -220,6 +230,18 @@ __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* _
             for (int j = 0; j < 4; ++j) {
                 const int cl = p.wn * (BN / WN) + 32 * fn + 8 * j + 4 * h;
                 const int64_t c0 = p.n0 + cl;
+                if (part) {  // split k: fp32 sums of this k range
+                    float* dst = part + ((int64_t)blockIdx.z * m + t) * n + c0;
+                    if (c0 + 3 < n && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+                        *reinterpret_cast<f32x4*>(dst) = f32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (c0 + r < n)
+                                dst[r] = d[4 * j + r];
+                    }
+                    continue;
+                }
                 const f32x4 s4 = *reinterpret_cast<const f32x4*>(&e_scale[cl]);
                 const u32x2 b4 = *reinterpret_cast<const u32x2*>(&e_bias[cl]);
                 const uint16_t bb[4] = {(uint16_t)(b4.x & 0xffffu), (uint16_t)(b4.x >> 16), (uint16_t)(b4.y & 0xffffu),
@@ -247,71 +269,137 @@ __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* _
 
 template <typename A, int BN, int BM, int WN, int WM>
 hipError_t launch_b(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
-                    int64_t n, void* y, hipStream_t stream)
+                    int64_t n, void* y, int splits, float* part, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM)), block(WN * WM * kWave);
+    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM), (unsigned)splits);
+    const dim3 block(WN * WM * kWave);
     hipLaunchKernelGGL((batch_kernel<A, BN, BM, WN, WM>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
-                       scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
+                       scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k,
+                       splits > 1 ? part : nullptr);
     return hipGetLastError();
 }
 
-// Tile choice: the largest tile that still gives at least 224 workgroups (7/8
-// of the CUs), in the order 256 x 128, 128 x 128, 128 x 64, 64 x 64, 64 x 32,
-// 32 x 32 (channels x tokens); the smallest below that.
 struct BatchTile {
     int bn, bm, wn, wm;
 };
 
-constexpr BatchTile kBatchTiles[] = {{256, 128, 2, 4}, {128, 128, 2, 4}, {128, 64, 4, 2},
-                                     {64, 64, 2, 2},   {64, 32, 2, 1},   {32, 32, 1, 1}};
+constexpr BatchTile kBatchTiles[] = {{256, 128, 2, 4}, {256, 64, 4, 2}, {128, 128, 2, 4}, {128, 64, 4, 2},
+                                     {64, 64, 2, 2},   {64, 32, 2, 1},  {32, 32, 1, 1}};
 
-BatchTile batch_tile(int64_t m, int64_t n)
+struct BatchPlan {
+    BatchTile tile;
+    int splits;
+};
+
+// Plan choice: the plan with the lowest modelled time, a model fitted to a
+// sweep of every tile and split count over 40 shapes on MI355X (n = 4096,
+// 14336, 28672; k = 4096, 14336; m = 48..512), where it picked a plan within
+// 4 % of the fastest measured one on every shape (0.3 % on average):
+//   - the operand stream (weight tiles read once per token tile, activation
+//     tiles once per channel tile, padded to whole tiles) at 8 bytes per ns,
+//     80 % of that for the 256-channel tiles, scaled by the share of the CUs
+//     the grid fills (224 workgroups count as full; an eight-wave tile takes a
+//     whole CU, so a grid past 256 of them pays for a partly empty round);
+//   - or, when larger, the padded MFMA work at 1 PFLOP/s;
+//   - plus, for a split, the fp32 partial sums written and read back at 2
+//     bytes per ns.
+// Split counts divide k / 256 and leave at least 512 k per workgroup; without
+// workspace (allow_split false) every plan is single-pass. Ties go to the
+// larger tile.
+double batch_cost_us(const BatchTile& t, int64_t s, int64_t m, int64_t n, int64_t k)
 {
-    for (const BatchTile& t : kBatchTiles)
-        if (((n + t.bn - 1) / t.bn) * ((m + t.bm - 1) / t.bm) >= 224)
-            return t;
-    return kBatchTiles[sizeof(kBatchTiles) / sizeof(kBatchTiles[0]) - 1];
+    const int64_t tn = (n + t.bn - 1) / t.bn, tm = (m + t.bm - 1) / t.bm, wgs = tn * tm * s;
+    const double mbytes = ((double)(tm * tn * t.bn) * (double)k + (double)(tn * tm * t.bm) * (double)k * 2.0) * 1e-6;
+    const double gflop = 2.0 * (double)(tm * t.bm) * (double)(tn * t.bn) * (double)k * 1e-9;
+    double fill = wgs < 224 ? (double)wgs / 224.0 : 1.0;
+    if (t.wn * t.wm == 8 && wgs > 256)
+        fill = (double)wgs / (256.0 * (double)((wgs + 255) / 256));
+    const double t_mem = mbytes / (8.0 * (t.bn == 256 ? 0.8 : 1.0) * fill);
+    const double t_mfma = gflop / (wgs < 256 ? (double)wgs / 256.0 : 1.0);
+    const double t_split = s > 1 ? 8.0 * (double)s * (double)m * (double)n * 1e-6 / 2.0 : 0.0;
+    return (t_mem > t_mfma ? t_mem : t_mfma) + t_split;
+}
+
+BatchPlan batch_plan(int64_t m, int64_t n, int64_t k, bool allow_split)
+{
+    BatchPlan best{kBatchTiles[0], 1};
+    double best_cost = -1.0;
+    const int64_t k256 = k / 256;
+    for (const BatchTile& t : kBatchTiles) {
+        for (int64_t s = 1; s <= (allow_split ? k256 : 1); ++s) {
+            if (k256 % s != 0 || (s > 1 && k / s < 512))
+                continue;
+            const double c = batch_cost_us(t, s, m, n, k);
+            if (best_cost < 0.0 || c < best_cost) {  // tiles are listed largest first: ties keep the larger
+                best_cost = c;
+                best = BatchPlan{t, (int)s};
+            }
+        }
+    }
+    return best;
 }
 
 template <typename A>
-hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
-                        int64_t n, void* y, hipStream_t stream)
+hipError_t launch_typed(const BatchPlan& p, const void* x, int64_t m, int64_t k, const uint8_t* q,
+                        const float* scale, const void* bias, int64_t n, void* y, float* part, hipStream_t stream)
 {
-    const BatchTile t = batch_tile(m, n);
+    const BatchTile& t = p.tile;
+    const int s = p.splits;
+    if (t.bn == 256 && t.bm == 128)
+        return launch_b<A, 256, 128, 2, 4>(x, m, k, q, scale, bias, n, y, s, part, stream);
     if (t.bn == 256)
-        return launch_b<A, 256, 128, 2, 4>(x, m, k, q, scale, bias, n, y, stream);
+        return launch_b<A, 256, 64, 4, 2>(x, m, k, q, scale, bias, n, y, s, part, stream);
     if (t.bn == 128 && t.bm == 128)
-        return launch_b<A, 128, 128, 2, 4>(x, m, k, q, scale, bias, n, y, stream);
+        return launch_b<A, 128, 128, 2, 4>(x, m, k, q, scale, bias, n, y, s, part, stream);
     if (t.bn == 128)
-        return launch_b<A, 128, 64, 4, 2>(x, m, k, q, scale, bias, n, y, stream);
+        return launch_b<A, 128, 64, 4, 2>(x, m, k, q, scale, bias, n, y, s, part, stream);
     if (t.bm == 64)
-        return launch_b<A, 64, 64, 2, 2>(x, m, k, q, scale, bias, n, y, stream);
+        return launch_b<A, 64, 64, 2, 2>(x, m, k, q, scale, bias, n, y, s, part, stream);
     if (t.bn == 64)
-        return launch_b<A, 64, 32, 2, 1>(x, m, k, q, scale, bias, n, y, stream);
-    return launch_b<A, 32, 32, 1, 1>(x, m, k, q, scale, bias, n, y, stream);
+        return launch_b<A, 64, 32, 2, 1>(x, m, k, q, scale, bias, n, y, s, part, stream);
+    return launch_b<A, 32, 32, 1, 1>(x, m, k, q, scale, bias, n, y, s, part, stream);
 }
 
 }  // namespace
 
+size_t batch_workspace_bytes(int64_t m, int64_t n, int64_t k)
+{
+    if (m < 1 || n < 1 || k < 256 || k % 256 != 0)
+        return 0;
+    const BatchPlan p = batch_plan(m, n, k, true);
+    return p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
 hipError_t launch_batch(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
-                        const void* bias, int64_t n, void* y, hipStream_t stream)
+                        const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     if (m == 0 || n == 0)
         return hipSuccess;
     if (k % 256 != 0 || k == 0)
         return hipErrorInvalidValue;
+    const size_t need = batch_workspace_bytes(m, n, k);
+    const BatchPlan p = batch_plan(m, n, k, ws != nullptr && need > 0 && ws_bytes >= need);
+    float* part = static_cast<float*>(ws);
+    hipError_t e = hipErrorInvalidValue;
     if (act == Act::BF16)
-        return launch_typed<Bf16>(x, m, k, q, scale, bias, n, y, stream);
-    if (act == Act::FP16)
-        return launch_typed<F16>(x, m, k, q, scale, bias, n, y, stream);
-    return hipErrorInvalidValue;
+        e = launch_typed<Bf16>(p, x, m, k, q, scale, bias, n, y, part, stream);
+    else if (act == Act::FP16)
+        e = launch_typed<F16>(p, x, m, k, q, scale, bias, n, y, part, stream);
+    if (e != hipSuccess || p.splits <= 1)
+        return e;
+    return launch_splitk_reduce(part, p.splits, m, n, scale, bias, y, act, stream);
 }
 
-const char* batch_kernel_name(int64_t m, int64_t n)
+const char* batch_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace)
 {
-    thread_local char name[64];
-    const BatchTile t = batch_tile(m, n);
-    snprintf(name, sizeof name, "batch_kernel<BN=%d,BM=%d,W=%d>", t.bn, t.bm, t.wn * t.wm);
+    thread_local char name[96];
+    const BatchPlan p = batch_plan(m, n, k, with_workspace);
+    const BatchTile& t = p.tile;
+    if (p.splits > 1)
+        snprintf(name, sizeof name, "batch_kernel<BN=%d,BM=%d,W=%d>x%d+splitk_reduce_kernel", t.bn, t.bm, t.wn * t.wm,
+                 p.splits);
+    else
+        snprintf(name, sizeof name, "batch_kernel<BN=%d,BM=%d,W=%d>", t.bn, t.bm, t.wn * t.wm);
     return name;
 }
 

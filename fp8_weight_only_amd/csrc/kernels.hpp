@@ -38,13 +38,24 @@ size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 // thread-local string; for tests and measurement reports).
 const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace);
 
-// The linear for m > 32 (any m >= 1): a GEMM over BN x BM tiles that decodes the
-// codes in its main loop; k % 256 == 0, x and q 16-byte aligned.
-hipError_t launch_batch(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
-                        const void* bias, int64_t n, void* y, hipStream_t stream);
+// Sum of fp32 partial sums part[splits, m, n] in split order, then the
+// scale/bias epilogue into y (act_type).
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t m, int64_t n, const float* scale,
+                                const void* bias, void* y, Act act, hipStream_t stream);
 
-// Name of the batch kernel tile launch_batch picks for this shape.
-const char* batch_kernel_name(int64_t m, int64_t n);
+// The linear for m > 32 (any m >= 1): a GEMM over BN x BM tiles that decodes the
+// codes in its main loop; k % 256 == 0, x and q 16-byte aligned. Plans that
+// split k use ws (fp32 partial sums, 16-byte aligned, not overlapping any
+// operand) when ws_bytes >= batch_workspace_bytes(m, n, k); otherwise the
+// single-pass plan runs.
+hipError_t launch_batch(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
+                        const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Workspace bytes the batch path uses for split k on this shape (0: none).
+size_t batch_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+// Name of the batch kernel plan launch_batch picks for this shape.
+const char* batch_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace);
 
 // Dequantize codes to out_type: value(q) * scale[r] (scale != nullptr) or the
 // exact unscaled value (scale == nullptr).

@@ -38,6 +38,8 @@
 // device-scope handoff between workgroups costs more than it saves).
 #include <stdio.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "ring.hpp"
@@ -414,10 +416,8 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits <= 1)
         return e;
-    const int64_t total = (int64_t)m * n;
-    hipLaunchKernelGGL((splitk_reduce_kernel<A>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, part,
-                       splits, m, n, scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y));
-    return hipGetLastError();
+    return launch_splitk_reduce(part, splits, m, n, scale, bias, y, std::is_same<A, Bf16>::value ? Act::BF16 : Act::FP16,
+                                stream);
 }
 
 // Kernel choice per shape, from sweeps on MI355X (k % 256 == 0 here).
@@ -562,6 +562,26 @@ size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k)
         return 0;
     const SkinnyPlan p = plan_skinny(m, n, k, true);
     return p.pipe && p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t m, int64_t n, const float* scale,
+                                const void* bias, void* y, Act act, hipStream_t stream)
+{
+    const int64_t total = m * n;
+    if (total == 0)
+        return hipSuccess;
+    if ((total + 255) / 256 > INT32_MAX || m > INT32_MAX)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    const uint16_t* b = static_cast<const uint16_t*>(bias);
+    uint16_t* yy = static_cast<uint16_t*>(y);
+    if (act == Act::BF16)
+        hipLaunchKernelGGL((splitk_reduce_kernel<Bf16>), grid, block, 0, stream, part, splits, (int)m, n, scale, b, yy);
+    else if (act == Act::FP16)
+        hipLaunchKernelGGL((splitk_reduce_kernel<F16>), grid, block, 0, stream, part, splits, (int)m, n, scale, b, yy);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,

@@ -103,10 +103,11 @@ FP8W_API fp8w_status_t fp8w_quantize(const void* w, fp8w_dtype_t w_dtype, int64_
  *   workspace device scratch of fp8w_linear_workspace_bytes(...) bytes (NULL / 0
  *             when that is 0); it must not overlap anything else. The fallback
  *             path needs it (2-byte aligned, FP8W_ERR_WORKSPACE when missing or
- *             short). Some skinny shapes (m > 16 on layers of 4096 to 8192
- *             channels) use it for fp32 partial sums of a k split (16-byte
- *             aligned); given less, they take a slower single-pass plan
- *             instead, with no error.
+ *             short). Skinny and batch shapes whose tiles alone would leave
+ *             CUs idle (skinny: m > 16 on layers of 4096 to 8192 channels;
+ *             batch: few tiles) use it for fp32 partial sums of a k split
+ *             (16-byte aligned); given less, they take a slower single-pass
+ *             plan instead, with no error.
  * Dispatch (fp8w_linear_path): the fast kernels take k % 256 == 0 with x, q
  * 16-byte aligned: m == 1 the GEMV, 2 <= m <= 32 the skinny MFMA kernel, m > 32
  * the batch GEMM (which decodes the codes in its main loop, no workspace);
@@ -154,8 +155,9 @@ FP8W_API int fp8w_linear_path(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_
                      const void* y);
 
 /* Workspace bytes fp8w_linear uses for these sizes and pointers: 0 on the GEMV
-   and most skinny shapes, splits * m * n * 4 on skinny shapes that split k,
-   n * k * element_size(act_dtype) on the fallback; 0 when invalid. */
+   and on skinny and batch shapes that do not split k, splits * m * n * 4 on
+   those that do, n * k * element_size(act_dtype) on the fallback; 0 when
+   invalid. */
 FP8W_API size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x,
                                    const uint8_t* q, const void* y);
 

@@ -108,14 +108,14 @@ def test_kernel_names():
     assert kn(A, 3, 100, 4096, fw.BF16, X + 2, Q) == "dequantize_kernel+fallback_gemm_kernel"  # x unaligned
     assert kn(fw.PATH_GEMV, 2, 4096, 4096, fw.BF16, X, Q) is None
     assert kn(fw.PATH_SKINNY, 33, 4096, 4096, fw.BF16, X, Q) is None
-    assert kn(A, 33, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=32,BM=32,W=1>"
-    assert kn(A, 64, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=64,BM=64,W=4>"
-    assert kn(A, 256, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=128,BM=128,W=8>"
+    assert kn(A, 33, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=64,BM=64,W=4>x4+splitk_reduce_kernel"
+    assert kn(A, 64, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=128,BM=64,W=8>x2+splitk_reduce_kernel"
     assert kn(A, 128, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=128,BM=64,W=8>"
-    assert kn(A, 128, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=64,BM=32,W=2>"
+    assert kn(A, 128, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=128,BM=64,W=8>x4+splitk_reduce_kernel"
     assert kn(A, 512, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=256,BM=128,W=8>"
     assert kn(A, 2048, 14336, 4096, fw.BF16, X, Q) == "batch_kernel<BN=256,BM=128,W=8>"
-    assert kn(fw.PATH_BATCH, 1, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=32,BM=32,W=1>"
+    assert kn(A, 33, 64, 256, fw.BF16, X, Q) == "batch_kernel<BN=32,BM=32,W=1>"
+    assert kn(fw.PATH_BATCH, 1, 4096, 4096, fw.BF16, X, Q) == "batch_kernel<BN=32,BM=32,W=1>"  # no workspace
     assert kn(fw.PATH_BATCH, 64, 4096, 4100, fw.BF16, X, Q) is None     # k % 256 != 0
     assert kn(A, 1, 4096, 4096, fw.FP32, X, Q) is None
     assert kn(7, 1, 4096, 4096, fw.BF16, X, Q) is None
@@ -127,7 +127,9 @@ def test_workspace_bytes():
     assert wb(16, 4096, 4096, fw.BF16, X, Q, Y) == 0
     assert wb(4, 28672, 8200, fw.BF16, X, Q, Y) == 28672 * 8200 * 2
     assert wb(64, 100, 500, fw.FP16, X, Q, Y) == 100 * 500 * 2           # k % 256 != 0: fallback
-    assert wb(64, 100, 512, fw.FP16, X, Q, Y) == 0                       # batch kernel
+    assert wb(64, 100, 512, fw.FP16, X, Q, Y) == 0                       # batch kernel, single pass
+    assert wb(64, 14336, 4096, fw.BF16, X, Q, Y) == 2 * 64 * 14336 * 4    # batch kernel, k in two
+    assert wb(512, 14336, 4096, fw.BF16, X, Q, Y) == 0
     assert wb(1, 10, 0, fw.BF16, X, Q, Y) == 0
     assert wb(1, 4096, 4096, fw.FP32, X, Q, Y) == 0
     assert wb(32, 8192, 28672, fw.BF16, X, Q, Y) == 2 * 32 * 8192 * 4     # split k
@@ -178,6 +180,14 @@ def test_linear_rejects_invalid_arguments():
 def test_split_k_workspace_is_validated():
     need = 2 * 32 * 8192 * 4
     big = dict(m=32, n=8192, k=28672)
+    assert _lin(ws=WS + 8, wsb=need, **big) == fw.ERR_MISALIGNED
+    assert _lin(ws=X, wsb=need, **big) == fw.ERR_INVALID_VALUE      # overlaps x
+    assert _lin(ws=Y - 64, wsb=need, **big) == fw.ERR_INVALID_VALUE  # overlaps y
+
+
+def test_batch_split_workspace_is_validated():
+    need = 2 * 64 * 14336 * 4
+    big = dict(m=64, n=14336, k=4096)
     assert _lin(ws=WS + 8, wsb=need, **big) == fw.ERR_MISALIGNED
     assert _lin(ws=X, wsb=need, **big) == fw.ERR_INVALID_VALUE      # overlaps x
     assert _lin(ws=Y - 64, wsb=need, **big) == fw.ERR_INVALID_VALUE  # overlaps y

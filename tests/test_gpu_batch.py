@@ -27,16 +27,23 @@ def _act(dtype):
 
 
 TILES = [
-    # (m, n, k, dtype, bias, kernel the dispatcher must pick)
-    (1000, 7000, 256, torch.bfloat16, True, "batch_kernel<BN=256,BM=128,W=8>"),
-    (1024, 7168, 512, torch.float16, False, "batch_kernel<BN=256,BM=128,W=8>"),
-    (290, 14300, 256, torch.float16, True, "batch_kernel<BN=128,BM=128,W=8>"),
-    (100, 14300, 512, torch.bfloat16, False, "batch_kernel<BN=128,BM=64,W=8>"),
-    (60, 14300, 768, torch.bfloat16, True, "batch_kernel<BN=64,BM=64,W=4>"),
-    (120, 4000, 1024, torch.float16, False, "batch_kernel<BN=64,BM=32,W=2>"),
-    (50, 1000, 256, torch.bfloat16, True, "batch_kernel<BN=32,BM=32,W=1>"),
-    (33, 100, 4096, torch.float16, True, "batch_kernel<BN=32,BM=32,W=1>"),
-    (64, 4096, 2048, torch.bfloat16, False, "batch_kernel<BN=32,BM=32,W=1>"),
+    # (m, n, k, dtype, bias, plan the dispatcher must pick): every tile shape,
+    # single pass and with k split over workgroups, ragged channel and token tails
+    (33, 64, 256, torch.bfloat16, True, "batch_kernel<BN=32,BM=32,W=1>"),
+    (33, 64, 1024, torch.float16, False, "batch_kernel<BN=32,BM=32,W=1>x2+splitk_reduce_kernel"),
+    (33, 5000, 256, torch.bfloat16, True, "batch_kernel<BN=64,BM=32,W=2>"),
+    (33, 1000, 3072, torch.float16, True, "batch_kernel<BN=64,BM=32,W=2>x6+splitk_reduce_kernel"),
+    (33, 14300, 256, torch.bfloat16, False, "batch_kernel<BN=64,BM=64,W=4>"),
+    (33, 3000, 2048, torch.float16, True, "batch_kernel<BN=64,BM=64,W=4>x4+splitk_reduce_kernel"),
+    (70, 10000, 256, torch.bfloat16, True, "batch_kernel<BN=128,BM=64,W=8>"),
+    (33, 5000, 2048, torch.float16, False, "batch_kernel<BN=128,BM=64,W=8>x4+splitk_reduce_kernel"),
+    (200, 10000, 256, torch.bfloat16, True, "batch_kernel<BN=128,BM=128,W=8>"),
+    (70, 10000, 3072, torch.float16, True, "batch_kernel<BN=128,BM=128,W=8>x3+splitk_reduce_kernel"),
+    (257, 11264, 1024, torch.bfloat16, False, "batch_kernel<BN=256,BM=64,W=8>"),
+    (33, 9216, 5120, torch.float16, True, "batch_kernel<BN=256,BM=64,W=8>x5+splitk_reduce_kernel"),
+    (400, 10000, 256, torch.bfloat16, True, "batch_kernel<BN=256,BM=128,W=8>"),
+    (65, 8704, 5120, torch.float16, False, "batch_kernel<BN=256,BM=128,W=8>x5+splitk_reduce_kernel"),
+    (1000, 7000, 768, torch.bfloat16, True, "batch_kernel<BN=256,BM=128,W=8>"),
 ]
 
 
@@ -50,13 +57,24 @@ def test_batch_tiles_parity(m, n, k, dtype, bias, kernel):
     x = case.x.to(DEV)
     b = None if case.layer.bias is None else case.layer.bias.to(DEV)
     assert fw.linear_path(x, q) == fw.PATH_BATCH
-    assert fw.workspace_bytes(x, q) == 0
+    split = "splitk" in kernel
+    assert (fw.workspace_bytes(x, q) > 0) == split
     q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
     assert_same_bits(q.cpu().numpy(), q_ref, "codes")
     y = nan_like((m, n), dtype, DEV)
-    fw.linear(x, q, s, b, out=y)
+    fw.linear(x, q, s, b, out=y)  # allocates the workspace a split plan asks for
     torch.cuda.synchronize()
-    assert_gate(y.double().cpu().numpy(), y_ref, x64, amax, kernel)
+    yv = y.double().cpu().numpy()
+    assert_gate(yv, y_ref, x64, amax, kernel)
+    if split:
+        # no workspace: the single-pass plan, also within the gate and within
+        # fp32 summation-order rounding of the split result
+        y1 = nan_like((m, n), dtype, DEV)
+        fw.linear(x, q, s, b, out=y1, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+        torch.cuda.synchronize()
+        y1v = y1.double().cpu().numpy()
+        assert_gate(y1v, y_ref, x64, amax, kernel + " single pass")
+        assert np.allclose(y1v, yv, rtol=2e-2, atol=1e-2)
 
 
 @pytest.mark.parametrize("m", [64, 128, 256])
@@ -113,17 +131,19 @@ def test_batch_matches_the_other_paths(dtype):
 
 
 def test_batch_is_deterministic_and_writes_only_y():
-    m, n, k = 200, 3000, 1024
+    m, n, k = 128, 4096, 4096  # a split plan: one workspace, reused without clearing
     case = workloads.random_case(78, m, n, k, torch.bfloat16, with_bias=True)
     q, s = fw.quantize(torch.from_numpy(case.layer.w).to(DEV))
     x, b = case.x.to(DEV), case.layer.bias.to(DEV)
+    assert "splitk" in fw.fp8w_linear_kernel(fw.PATH_AUTO, m, n, k, fw.BF16, 0, 0)
+    ws = torch.empty((fw.workspace_bytes(x, q),), dtype=torch.uint8, device=DEV)
     # y inside a larger buffer: the guard bands on both sides must stay untouched
     buf = torch.full((m * n + 2 * 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
     y = buf[4096:4096 + m * n].view(m, n)
-    fw.linear(x, q, s, b, out=y)
+    fw.linear(x, q, s, b, out=y, workspace=ws)
     first = y.clone()
     for _ in range(3):
-        fw.linear(x, q, s, b, out=y)
+        fw.linear(x, q, s, b, out=y, workspace=ws)
         assert torch.equal(y.view(torch.int16), first.view(torch.int16))
     torch.cuda.synchronize()
     assert torch.all(buf[:4096] == 7.0) and torch.all(buf[4096 + m * n:] == 7.0)

@@ -32,6 +32,10 @@ Prefill, W8A8 (workload id 7): the decoder block's three distinct shapes q
 x [M,K] bf16 ~ N(0,1) with 0.1 % of entries (seeded) multiplied by 20, for M
 in 512, 2048, 4096 (batches far above the weight-only kernels' 32 tokens).
 
+Batched decode (workload id 8): the decode workload's three weights (workload 2)
+at M = 64, 128, 256 tokens; x [M,K] bf16 ~ N(0,1); bias all zeros (bf16), as
+in decode. Above the skinny kernels' 32 tokens and below prefill sizes.
+
 Context shape (workload id 6): the one timing of this method the pages print is
 for x [22,1024] times a [1024,4096] weight ("FP8 weight-only (precision:
 fp8_weights)", the Triton variant in "Dequantise in registers"); it is drawn
@@ -57,6 +61,7 @@ LARGE_MS = [1, 4, 8, 32]
 PAGES_EXAMPLE = (22, 4096, 1024)  # m, n, k
 PREFILL_SHAPES = [(4096, 4096), (14336, 4096), (4096, 14336)]
 PREFILL_MS = [512, 2048, 4096]
+BATCH_MS = [64, 128, 256]
 # the decoder block with the layers that share an input merged into one call:
 # q/k/v, o, gate/up, down (indices into DECODER_BLOCK)
 MERGED_BLOCK = [(0, 1, 2), (3,), (4, 5), (6,)]
@@ -161,6 +166,11 @@ def large_x(shape, m: int) -> torch.Tensor:
     n, k = shape
     sub = {(28672, 8192): 0, (8192, 28672): 1, (28672, 8200): 2}[(n, k)]
     return activations(5, 100 * sub + m, m, k, torch.bfloat16, outlier_frac=0.001)
+
+
+def batch_x(i: int, m: int) -> torch.Tensor:
+    n, k = DECODE_SHAPES[i]
+    return activations(8, 1000 * i + m, m, k, torch.bfloat16)
 
 
 def prefill_layer(i: int) -> Linear:
