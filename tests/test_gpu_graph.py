@@ -3,8 +3,8 @@
 Every path enqueues only kernel launches with the caller's buffers (no
 allocation, no memset, no host copy), so a captured sequence must replay to
 the eager results, bit for bit: each call is deterministic. The graph holds a
-GEMV, a single-pass and a split-k skinny call, a fallback call, grouped calls
-and a W8A8 layer. Between replays the outputs are overwritten with NaN and
+GEMV, a single-pass and a split-k skinny call, a split and a single-pass call
+of the batch GEMM, a fallback call, grouped calls and a W8A8 layer. Between replays the outputs are overwritten with NaN and
 unrelated eager calls run on the same stream, so a replay that skipped a
 launch or read a stale buffer would show.
 """
@@ -23,6 +23,8 @@ CALLS = [
     ("linear", 8, 2048, 1024, torch.float16, None),
     ("linear", 20, 4100, 2048, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
     ("linear", 3, 300, 1000, torch.bfloat16, None),  # k % 256 != 0: fallback through the workspace
+    ("linear", 70, 640, 1024, torch.float16, "batch_kernel<BN=32,BM=32,W=1>x2+splitk_reduce_kernel"),
+    ("linear", 300, 2048, 512, torch.bfloat16, "batch_kernel<BN=64,BM=32,W=2>"),
     ("grouped32", 1, 512, 1024, torch.bfloat16, None),
     ("grouped128", 16, 1024, 2048, torch.float16, None),
     ("w8a8", 300, 512, 512, torch.bfloat16, None),
