@@ -801,7 +801,8 @@ def _short_kernel_name(full):
     args = [a.strip() for a in targs[1:-1].split(",")] if targs else []
     keys = {"pipe_kernel": ("XR", "CT", "KP", "NS"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
             "gemv_kernel": ("R", "U", "NT", "DB"), "wpipe_kernel": ("XR", "CT", "NS"), "w8a8_kernel": ("BN", "BM", "NS", "WN", "WM", "GM"),
-            "gemv_grouped_kernel": ("R", "U", "NT", "DB"), "pipe_grouped_kernel": ("XR", "CT", "KP", "NS", "G")}.get(name)
+            "gemv_grouped_kernel": ("R", "U", "NT", "DB"), "pipe_grouped_kernel": ("XR", "CT", "KP", "NS", "G"),
+            "batch_kernel": ("BN", "BM", "WN", "WM", "GM")}.get(name)
     if keys and len(args) == len(keys) + 1:  # first argument is the activation type
         return f"{name}<" + ",".join(f"{kk}={v}" for kk, v in zip(keys, args[1:])) + ">"
     return name + targs

@@ -189,7 +189,10 @@ __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* _
     p.wn = p.wave % WN;
     p.wm = p.wave / WN;
     p.S = kc / 64;
-    // the workgroups one XCD holds walk k in step; the XCDs start an eighth of k apart
+    // the workgroups one XCD holds walk k in step; the XCDs start an eighth of k
+    // apart (with a k split the XCD is taken within each slice of grid.z: the
+    // tile order and the stagger are placement heuristics, the results do not
+    // depend on them)
     p.rot = ((blockIdx.x + (int64_t)gridDim.x * blockIdx.y) % 8) * (p.S / 8);
 
     // epilogue operands of the tile's channels, one per thread: loaded before
