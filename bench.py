@@ -821,7 +821,8 @@ def trace_summary(csv_path, last=None):
     groups = {}
     for r in ours:
         name = _short_kernel_name(r["Kernel_Name"])
-        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])) * int(r.get("Grid_Size_Y") or 1)
+        wgs = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])) * int(r.get("Grid_Size_Y") or 1)
+               * int(r.get("Grid_Size_Z") or 1))
         key = (name, wgs, int(r["Workgroup_Size_X"]))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     lines = ["| Kernel | Workgroups x threads | Launches | Mean (us) | p10 (us) | Median (us) | p90 (us) | Min (us) |",
