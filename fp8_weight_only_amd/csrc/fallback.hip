@@ -1,7 +1,7 @@
-// Fallback for shapes the fast kernels do not cover (k % 256 != 0, m > 32,
-// unaligned pointers): "FP8 weight-only (precision: fp8_weights)", section
-// "The contract", item "Fallback": take the dequantised weight through a plain
-// GEMM with the same numerics.
+// Fallback for shapes the fast kernels do not cover (k % 256 != 0 or k < 256,
+// unaligned pointers) at any m, and for calls that force it: "FP8 weight-only
+// (precision: fp8_weights)", section "The contract", item "Fallback": take the
+// dequantised weight through a plain GEMM with the same numerics.
 //
 // Same numerics here means: the codes are decoded *unscaled* into the
 // activation dtype (exact, since every e4m3 value is a bf16 and an fp16
