@@ -90,12 +90,10 @@ int auto_path(int64_t m, int64_t k, const void* x, const uint8_t* q)
     return m == 1 ? FP8W_PATH_GEMV : m <= 32 ? FP8W_PATH_SKINNY : FP8W_PATH_BATCH;
 }
 
-// The grouped linear has no batch kernel: above 32 tokens it takes its generic one.
+// The grouped linear: the same split by tokens as the per-channel one.
 int auto_path_grouped(int64_t m, int64_t k, const void* x, const uint8_t* q)
 {
-    if (fast_shape(m, k) && fast_pointers(x, q))
-        return m == 1 ? FP8W_PATH_GEMV : FP8W_PATH_SKINNY;
-    return FP8W_PATH_FALLBACK;
+    return auto_path(m, k, x, q);
 }
 
 size_t fallback_workspace(int64_t n, int64_t k, fp8w_dtype_t act)
@@ -220,7 +218,7 @@ fp8w_status_t run_linear_grouped(const void* x, fp8w_dtype_t act, int64_t m, int
 {
     if (!valid_act(act) || !sizes_ok(m, n, k) || !valid_group(k, group))
         return FP8W_ERR_INVALID_VALUE;
-    if (path < FP8W_PATH_AUTO || path > FP8W_PATH_FALLBACK)
+    if (path < FP8W_PATH_AUTO || path > FP8W_PATH_BATCH)
         return FP8W_ERR_INVALID_VALUE;
     if (path == FP8W_PATH_AUTO)
         path = auto_path_grouped(m, k, x, q);
@@ -229,6 +227,8 @@ fp8w_status_t run_linear_grouped(const void* x, fp8w_dtype_t act, int64_t m, int
             return FP8W_ERR_INVALID_VALUE;
         if (m > 32 || k % 256 != 0 || k == 0)
             return FP8W_ERR_INVALID_VALUE;
+    } else if (path == FP8W_PATH_BATCH && !fast_k(k)) {
+        return FP8W_ERR_INVALID_VALUE;
     }
     if (m == 0 || n == 0)
         return FP8W_SUCCESS;
@@ -236,7 +236,7 @@ fp8w_status_t run_linear_grouped(const void* x, fp8w_dtype_t act, int64_t m, int
         return FP8W_ERR_INVALID_VALUE;
     if (!aligned(x, 2) || !aligned(y, 2) || !aligned(bias, 2) || !aligned(scale, 4))
         return FP8W_ERR_MISALIGNED;
-    if ((path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) && !fast_pointers(x, q))
+    if (path != FP8W_PATH_FALLBACK && !fast_pointers(x, q))
         return FP8W_ERR_MISALIGNED;
     const size_t ybytes = (size_t)m * (size_t)n * 2;
     if (overlap(y, ybytes, x, (size_t)m * (size_t)k * 2) || overlap(y, ybytes, q, (size_t)n * (size_t)k) ||
@@ -316,10 +316,12 @@ const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || k % 256 != 0 || k == 0)
             return nullptr;
-        return fp8w::grouped_kernel_name(path, m, n, k);
+        return fp8w::grouped_kernel_name(path, m, n, k, group);
     }
+    if (path == FP8W_PATH_BATCH)
+        return m >= 1 && fast_k(k) ? fp8w::grouped_kernel_name(3, m, n, k, group) : nullptr;
     if (path == FP8W_PATH_FALLBACK)
-        return fp8w::grouped_kernel_name(2, m, n, k);
+        return fp8w::grouped_kernel_name(2, m, n, k, group);
     return nullptr;
 }
 

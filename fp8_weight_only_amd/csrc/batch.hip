@@ -57,7 +57,9 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
                                                       0, 0, 0);
 }
 
-template <int BN, int BM, int WN, int WM>
+// G = 0: per-channel scales (applied in the epilogue). G = 32, 64, 128: group
+// scales along k ([n, k / G] fp32), staged per stage next to the operands.
+template <int BN, int BM, int WN, int WM, int G = 0>
 struct BatchCfg {
     static constexpr int W = WN * WM;                  // waves
     static constexpr int FN = BN / WN / 32;            // 32-channel fragments per wave
@@ -65,19 +67,26 @@ struct BatchCfg {
     static constexpr int ABLK = BN / 16;               // 1 KB load blocks of weight rows (16 rows x 64 codes)
     static constexpr int BBLK = BM / 8;                // 1 KB load blocks of activation rows (8 rows x 64 values)
     static constexpr int BLOCKS = ABLK + BBLK;
-    static constexpr int LOADS = (BLOCKS + W - 1) / W;  // per wave; the last round repeats blocks
+    static constexpr int OPS = (BLOCKS + W - 1) / W;   // operand loads per wave; the last round repeats blocks
+    static constexpr int SPANS = G == 0 ? 0 : (G >= 64 ? 1 : 64 / G);  // spans of one group in a 64-k stage
+    static constexpr int SBLK = SPANS * (BN / 64);     // 256-byte scale loads per stage (64 channels each)
+    static constexpr int SLW = (SBLK + W - 1) / W;     // per wave; repeats fill the last round
+    static constexpr int LOADS = OPS + SLW;            // load instructions per wave and stage
     static constexpr int ABYTES = BN * 64;
-    static constexpr int STAGE = ABYTES + BM * 128;
+    static constexpr int SOFF = ABYTES + BM * 128;     // the stage's group scales, [span][channel] fp32
+    static constexpr int STAGE = SOFF + SPANS * BN * 4;
     static_assert(FN >= 1 && FM >= 1 && BN == FN * WN * 32 && BM == FM * WM * 32, "tile and wave layout");
+    static_assert(G == 0 || ((G == 32 || G == 64 || G == 128) && BN % 64 == 0), "group size and tile");
     static_assert(LOADS * 2 < 64, "vmcnt range of the four-stage ring");
 };
 
-template <typename A, int BN, int BM, int WN, int WM>
+template <typename A, int BN, int BM, int WN, int WM, int G = 0>
 struct BatchPipe {
-    using C = BatchCfg<BN, BM, WN, WM>;
+    using C = BatchCfg<BN, BM, WN, WM, G>;
     const uint8_t* q;   // [n, k]
     const uint16_t* x;  // [m, k]
-    int64_t n, m, k, n0, m0;
+    const float* gs;    // G > 0: group scales [n, ng]
+    int64_t n, m, k, n0, m0, ng, kz0;  // kz0: the k this workgroup's split slice starts at
     int64_t S, rot;  // stages; the k stage this workgroup starts at
     int lane, wave, wn, wm;
 
@@ -94,8 +103,8 @@ struct BatchPipe {
         sr = sr < S ? sr : sr - S;
         const int64_t kb = sr * 64;
 #pragma unroll
-        for (int u = 0; u < C::LOADS; ++u) {
-            const int b = (wave * C::LOADS + u) % C::BLOCKS;
+        for (int u = 0; u < C::OPS; ++u) {
+            const int b = (wave * C::OPS + u) % C::BLOCKS;
             const void* src;
             if (b < C::ABLK) {
                 const int r = 16 * b + (lane >> 2);
@@ -112,11 +121,29 @@ struct BatchPipe {
             }
             __builtin_amdgcn_global_load_lds(src, FP8W_LDS(buf + 1024 * b), 16, 0, 0);
         }
+        if constexpr (G > 0) {
+            // scale load u: span sp, channels 64c .. 64c + 63 (lane l: channel
+            // 64c + l), the group that holds the span's k
+#pragma unroll
+            for (int u = 0; u < C::SLW; ++u) {
+                const int idx = (wave * C::SLW + u) % C::SBLK;
+                const int sp = idx / (BN / 64), c = idx % (BN / 64);
+                int64_t row = n0 + 64 * c + lane;
+                row = row < n ? row : n - 1;
+                const int64_t gidx = (kz0 + kb) / G + (C::SPANS > 1 ? sp : 0);
+                __builtin_amdgcn_global_load_lds(gs + row * ng + gidx,
+                                                 FP8W_LDS(buf + C::SOFF + 4 * (sp * BN + 64 * c)), 4, 0, 0);
+            }
+        }
     }
 
     // one stage: FN weight and FM token fragments, four MFMA steps each pair
     __device__ __forceinline__ void compute(const uint8_t* buf, f32x16* acc) const
     {
+        if constexpr (G > 0) {
+            compute_grouped(buf, acc);
+            return;
+        }
         const int i = lane & 31, h = lane >> 5;
         u32x4 wc[C::FN][2];  // 32 codes of the lane's weight row: k 32h .. 32h + 31
 #pragma unroll
@@ -148,6 +175,58 @@ struct BatchPipe {
                     acc[fn * C::FM + fm] = mfma32<A>(a[fn], b[fm], acc[fn * C::FM + fm]);
         }
     }
+
+    // Group scales: MFMA step j sums the 16 consecutive k 16j .. 16j + 15 of
+    // the stage (lane half h feeds 8h .. 8h + 7 of them), so a span of
+    // min(G, 64) k lies in one group. Each span's exact fp32 sum is scaled by
+    // its group's scale and added to the accumulator (one fmaf per output).
+    __device__ __forceinline__ void compute_grouped(const uint8_t* buf, f32x16* acc) const
+    {
+        const int i = lane & 31, h = lane >> 5;
+        constexpr int STEPS = 4 / C::SPANS;
+#pragma unroll
+        for (int sp = 0; sp < C::SPANS; ++sp) {
+            u32x4 b[C::FM][STEPS];
+#pragma unroll
+            for (int f = 0; f < C::FM; ++f) {
+                const int r = wm * (BM / WM) + 32 * f + i;
+#pragma unroll
+                for (int jj = 0; jj < STEPS; ++jj)
+                    b[f][jj] = *reinterpret_cast<const u32x4*>(buf + C::ABYTES + 128 * r +
+                                                               16 * ((2 * (sp * STEPS + jj) + h + (r >> 1)) & 7));
+            }
+            // one weight fragment at a time: a single span sum is live
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int r = wn * (BN / WN) + 32 * fn + i;
+                u32x4 a[STEPS];
+#pragma unroll
+                for (int jj = 0; jj < STEPS; ++jj) {
+                    const int j = sp * STEPS + jj;
+                    const u32x2 c8 = *reinterpret_cast<const u32x2*>(buf + 64 * r + 16 * ((j + (r >> 2)) & 3) + 8 * h);
+                    const u32x2 d0 = A::decode4(c8.x), d1 = A::decode4(c8.y);
+                    a[jj] = u32x4{d0.x, d0.y, d1.x, d1.y};
+                }
+                // accumulator 4q + e of the fragment is channel 32 fn + 8q + 4h + e
+                const float* sc =
+                    reinterpret_cast<const float*>(buf + C::SOFF) + sp * BN + wn * (BN / WN) + 32 * fn + 4 * h;
+                f32x4 s4[4];
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    s4[qq] = *reinterpret_cast<const f32x4*>(sc + 8 * qq);
+#pragma unroll
+                for (int fm = 0; fm < C::FM; ++fm) {
+                    f32x16 part = f32x16{0.0f};
+#pragma unroll
+                    for (int jj = 0; jj < STEPS; ++jj)
+                        part = mfma32<A>(a[jj], b[fm][jj], part);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[fn * C::FM + fm][e] = __builtin_fmaf(s4[e >> 2][e & 3], part[e], acc[fn * C::FM + fm][e]);
+                }
+            }
+        }
+    }
 };
 
 // Requires k % 256 == 0 (k / 64 stages, a multiple of the four-stage ring); x
@@ -155,7 +234,9 @@ struct BatchPipe {
 // grid.z > 1 splits k: workgroup row z owns k range [z * kc, (z + 1) * kc),
 // kc = k / gridDim.z (a multiple of 256), and writes fp32 sums to part
 // ([gridDim.z, m, n]) instead of y.
-template <typename A, int BN, int BM, int WN, int WM, int GM = 4>
+// G > 0: scale holds the group scales [n, k / G] and the epilogue adds only the
+// bias (no split).
+template <typename A, int BN, int BM, int WN, int WM, int G = 0, int GM = 4>
 __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* __restrict__ x,
                                                               const uint8_t* __restrict__ q,
                                                               const float* __restrict__ scale,
@@ -163,7 +244,7 @@ __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* _
                                                               uint16_t* __restrict__ y, int64_t m, int64_t n,
                                                               int64_t k, float* __restrict__ part)
 {
-    using P = BatchPipe<A, BN, BM, WN, WM>;
+    using P = BatchPipe<A, BN, BM, WN, WM, G>;
     using C = typename P::C;
     static_assert(BN <= C::W * kWave, "one epilogue operand per thread");
     __shared__ __attribute__((aligned(1024))) uint8_t b0[C::STAGE];
@@ -189,6 +270,9 @@ __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* _
     p.wn = p.wave % WN;
     p.wm = p.wave / WN;
     p.S = kc / 64;
+    p.gs = scale;
+    p.ng = G > 0 ? k / G : 0;
+    p.kz0 = (int64_t)blockIdx.z * kc;
     // the workgroups one XCD holds walk k in step; the XCDs start an eighth of k
     // apart (with a k split the XCD is taken within each slice of grid.z: the
     // tile order and the stagger are placement heuristics, the results do not
@@ -203,7 +287,7 @@ __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* _
     uint16_t r_bias = 0;
     if (tt < BN) {
         const int64_t c = p.n0 + tt < n ? p.n0 + tt : n - 1;
-        r_scale = scale[c];
+        r_scale = G > 0 ? 1.0f : scale[c];  // group scales were applied in the k loop
         r_bias = bias_bits(bias, c);
     }
 
@@ -270,13 +354,13 @@ __global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* _
     }
 }
 
-template <typename A, int BN, int BM, int WN, int WM>
+template <typename A, int BN, int BM, int WN, int WM, int G = 0>
 hipError_t launch_b(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
                     int64_t n, void* y, int splits, float* part, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM), (unsigned)splits);
     const dim3 block(WN * WM * kWave);
-    hipLaunchKernelGGL((batch_kernel<A, BN, BM, WN, WM>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
+    hipLaunchKernelGGL((batch_kernel<A, BN, BM, WN, WM, G>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
                        scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k,
                        splits > 1 ? part : nullptr);
     return hipGetLastError();
@@ -308,7 +392,11 @@ struct BatchPlan {
 //     bytes per ns.
 // Split counts divide k / 256 and leave at least 512 k per workgroup; without
 // workspace (allow_split false) every plan is single-pass. Ties go to the
-// larger tile.
+// larger tile. With group scales (group > 0) only the tiles whose grouped
+// kernel fits its registers without spills are planned: 64 x 64 and 64 x 32,
+// and 128 x 64 for groups of 64 and 128 (the span sums of groups of 32 push
+// it past the 256 registers an eight-wave tile has per lane; the larger tiles
+// spill at every group size).
 double batch_cost_us(const BatchTile& t, int64_t s, int64_t m, int64_t n, int64_t k)
 {
     const int64_t tn = (n + t.bn - 1) / t.bn, tm = (m + t.bm - 1) / t.bm, wgs = tn * tm * s;
@@ -323,12 +411,19 @@ double batch_cost_us(const BatchTile& t, int64_t s, int64_t m, int64_t n, int64_
     return (t_mem > t_mfma ? t_mem : t_mfma) + t_split;
 }
 
-BatchPlan batch_plan(int64_t m, int64_t n, int64_t k, bool allow_split)
+bool grouped_tile(const BatchTile& t, int64_t group)
+{
+    return t.bn == 64 || (t.bn == 128 && t.bm == 64 && group >= 64);
+}
+
+BatchPlan batch_plan(int64_t m, int64_t n, int64_t k, bool allow_split, int64_t group = 0)
 {
     BatchPlan best{kBatchTiles[0], 1};
     double best_cost = -1.0;
     const int64_t k256 = k / 256;
     for (const BatchTile& t : kBatchTiles) {
+        if (group > 0 && !grouped_tile(t, group))
+            continue;
         for (int64_t s = 1; s <= (allow_split ? k256 : 1); ++s) {
             if (k256 % s != 0 || (s > 1 && k / s < 512))
                 continue;
@@ -363,7 +458,59 @@ hipError_t launch_typed(const BatchPlan& p, const void* x, int64_t m, int64_t k,
     return launch_b<A, 32, 32, 1, 1>(x, m, k, q, scale, bias, n, y, s, part, stream);
 }
 
+template <typename A, int G>
+hipError_t launch_grouped_tile(const BatchTile& t, const void* x, int64_t m, int64_t k, const uint8_t* q,
+                               const float* gs, const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    if constexpr (G >= 64) {
+        if (t.bn == 128)
+            return launch_b<A, 128, 64, 4, 2, G>(x, m, k, q, gs, bias, n, y, 1, nullptr, stream);
+    }
+    if (t.bn != 64)
+        return hipErrorInvalidValue;  // not a grouped tile (batch_plan never picks one)
+    if (t.bm == 64)
+        return launch_b<A, 64, 64, 2, 2, G>(x, m, k, q, gs, bias, n, y, 1, nullptr, stream);
+    return launch_b<A, 64, 32, 2, 1, G>(x, m, k, q, gs, bias, n, y, 1, nullptr, stream);
+}
+
+template <typename A>
+hipError_t launch_grouped_typed(const BatchTile& t, int64_t group, const void* x, int64_t m, int64_t k,
+                                const uint8_t* q, const float* gs, const void* bias, int64_t n, void* y,
+                                hipStream_t stream)
+{
+    if (group == 32)
+        return launch_grouped_tile<A, 32>(t, x, m, k, q, gs, bias, n, y, stream);
+    if (group == 64)
+        return launch_grouped_tile<A, 64>(t, x, m, k, q, gs, bias, n, y, stream);
+    if (group == 128)
+        return launch_grouped_tile<A, 128>(t, x, m, k, q, gs, bias, n, y, stream);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_batch_grouped(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* gs,
+                                int64_t group, const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    if (m == 0 || n == 0)
+        return hipSuccess;
+    if (k % 256 != 0 || k == 0)
+        return hipErrorInvalidValue;
+    const BatchTile t = batch_plan(m, n, k, false, group).tile;
+    if (act == Act::BF16)
+        return launch_grouped_typed<Bf16>(t, group, x, m, k, q, gs, bias, n, y, stream);
+    if (act == Act::FP16)
+        return launch_grouped_typed<F16>(t, group, x, m, k, q, gs, bias, n, y, stream);
+    return hipErrorInvalidValue;
+}
+
+const char* batch_grouped_kernel_name(int64_t m, int64_t n, int64_t k, int64_t group)
+{
+    thread_local char name[96];
+    const BatchTile t = batch_plan(m, n, k, false, group).tile;
+    snprintf(name, sizeof name, "batch_grouped_kernel<BN=%d,BM=%d,W=%d>", t.bn, t.bm, t.wn * t.wm);
+    return name;
+}
 
 size_t batch_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {

@@ -82,13 +82,20 @@ hipError_t launch_quantize_groups(const void* w, Act w_type, int64_t n, int64_t 
 // The grouped linear. path 0: M = 1 GEMV (k % 256 == 0, x and q 16-byte
 // aligned); path 1: M <= 32 skinny ring where k allows it, else the generic
 // kernel; path 2: the generic kernel (any m, n, k % group == 0, x 2-byte and q
-// 1-byte aligned).
+// 1-byte aligned); path 3: the batch GEMM (launch_batch_grouped).
 hipError_t launch_linear_grouped(int path, const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
                                  const float* scale, int64_t group, const void* bias, int64_t n, void* y,
                                  hipStream_t stream);
 
+// The grouped linear above 32 tokens: the batch GEMM with group scales staged
+// beside the operands (k % 256 == 0, group 32 / 64 / 128, x and q 16-byte
+// aligned; single pass, no workspace).
+hipError_t launch_batch_grouped(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* gs,
+                                int64_t group, const void* bias, int64_t n, void* y, hipStream_t stream);
+const char* batch_grouped_kernel_name(int64_t m, int64_t n, int64_t k, int64_t group);
+
 // Name of the kernel launch_linear_grouped runs for this path and shape.
-const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k);
+const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k, int64_t group);
 
 // value(q) * scale[r, j / group] rounded to out_type.
 hipError_t launch_dequantize_grouped(const uint8_t* q, const float* scale, int64_t group, int64_t n, int64_t k,

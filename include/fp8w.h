@@ -195,23 +195,25 @@ FP8W_API fp8w_status_t fp8w_quantize_grouped(const void* w, fp8w_dtype_t w_dtype
    fp32 accumulation (each partial sum of exact products lies inside one
    group and is scaled before it is added), one rounding to act_dtype.
    Arguments as for fp8w_linear; no workspace. Dispatch as fp8w_linear_path
-   (m == 1: GEMV; m <= 32: skinny MFMA kernel; k % 256 == 0 and 16-byte
-   aligned x and q for both); everything else, and skinny shapes whose k the
-   ring cannot tile, runs a generic kernel (any m, n; x 2-byte aligned).
-   Asynchronous. */
+   (m == 1: GEMV; m <= 32: skinny MFMA kernel; m > 32: the batch GEMM, single
+   pass; k % 256 == 0 and 16-byte aligned x and q for all three); everything
+   else, and skinny shapes whose k the ring cannot tile, runs a generic kernel
+   (any m, n; x 2-byte aligned). Asynchronous. */
 FP8W_API fp8w_status_t fp8w_linear_grouped(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
                                            const uint8_t* q, const float* scale, int64_t group, const void* bias,
                                            int64_t n, void* y, hipStream_t stream);
 
 /* fp8w_linear_grouped with an explicit FP8W_PATH_* (same requirements as
-   fp8w_linear_with_path; FP8W_PATH_FALLBACK is the generic kernel). */
+   fp8w_linear_with_path, FP8W_PATH_BATCH included; FP8W_PATH_FALLBACK is the
+   generic kernel). */
 FP8W_API fp8w_status_t fp8w_linear_grouped_with_path(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
                                                      const uint8_t* q, const float* scale, int64_t group,
                                                      const void* bias, int64_t n, void* y, int path,
                                                      hipStream_t stream);
 
-/* Path fp8w_linear_grouped takes (FP8W_PATH_GEMV, _SKINNY or _FALLBACK; grouped
-   calls above 32 tokens take the generic kernel), -1 when the arguments are invalid. */
+/* Path fp8w_linear_grouped takes (FP8W_PATH_GEMV, _SKINNY, _BATCH or
+   _FALLBACK, by the rules of fp8w_linear_path), -1 when the arguments are
+   invalid. */
 FP8W_API int fp8w_linear_grouped_path(int64_t m, int64_t n, int64_t k, int64_t group, fp8w_dtype_t act_dtype,
                                       const void* x, const uint8_t* q);
 

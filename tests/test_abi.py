@@ -280,7 +280,9 @@ def test_grouped_paths_and_kernel_names():
     gp, gk, A = fw.fp8w_linear_grouped_path, fw.fp8w_linear_grouped_kernel, fw.PATH_AUTO
     assert gp(1, 4096, 4096, 32, fw.BF16, X, Q) == fw.PATH_GEMV
     assert gp(16, 4096, 4096, 64, fw.BF16, X, Q) == fw.PATH_SKINNY
-    assert gp(33, 4096, 4096, 128, fw.BF16, X, Q) == fw.PATH_FALLBACK
+    assert gp(33, 4096, 4096, 128, fw.BF16, X, Q) == fw.PATH_BATCH
+    assert gp(33, 4096, 4160, 64, fw.BF16, X, Q) == fw.PATH_FALLBACK     # k % 256 != 0
+    assert gp(33, 4096, 4096, 64, fw.BF16, X + 2, Q) == fw.PATH_FALLBACK  # x not 16-byte aligned
     assert gp(1, 4096, 4160, 32, fw.BF16, X, Q) == fw.PATH_FALLBACK      # k % 256 != 0
     assert gp(1, 4096, 4096, 48, fw.BF16, X, Q) == -1                    # group not 32/64/128
     assert gp(1, 4096, 4000, 64, fw.BF16, X, Q) == -1                    # group does not divide k
@@ -291,7 +293,12 @@ def test_grouped_paths_and_kernel_names():
     assert gk(A, 8, 4096, 4096, 64, fw.BF16, X, Q) == "pipe_grouped_kernel<XR=8,CT=1,KP=2,NS=4>"
     assert gk(A, 32, 4096, 4096, 64, fw.BF16, X, Q) == "pipe_grouped_kernel<XR=32,CT=1,KP=2,NS=2>"
     assert gk(A, 2, 4096, 768, 128, fw.BF16, X, Q) == "grouped_generic_kernel"      # ring cannot tile k
-    assert gk(A, 64, 4096, 4096, 32, fw.BF16, X, Q) == "grouped_generic_kernel"
+    assert gk(A, 64, 4096, 4096, 32, fw.BF16, X, Q) == "batch_grouped_kernel<BN=64,BM=32,W=2>"
+    assert gk(A, 128, 14336, 4096, 128, fw.BF16, X, Q) == "batch_grouped_kernel<BN=128,BM=64,W=8>"
+    assert gk(A, 128, 14336, 4096, 32, fw.BF16, X, Q).startswith("batch_grouped_kernel<BN=64,")  # no 128 x 64 for g 32
+    assert gk(fw.PATH_BATCH, 2, 4096, 4096, 64, fw.BF16, X, Q) == "batch_grouped_kernel<BN=64,BM=32,W=2>"
+    assert gk(fw.PATH_BATCH, 40, 4096, 4160, 64, fw.BF16, X, Q) is None    # k % 256 != 0
+    assert gk(A, 64, 4096, 4160, 64, fw.BF16, X, Q) == "grouped_generic_kernel"
     assert gk(fw.PATH_FALLBACK, 1, 4096, 4096, 32, fw.BF16, X, Q) == "grouped_generic_kernel"
     assert gk(fw.PATH_GEMV, 2, 4096, 4096, 32, fw.BF16, X, Q) is None
 
@@ -307,6 +314,9 @@ def test_grouped_rejects_invalid_arguments():
     assert _glin(k=4160, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
     assert _glin(y=Q) == fw.ERR_INVALID_VALUE                            # y overlaps q
     assert _glin(path=5) == fw.ERR_INVALID_VALUE
+    assert _glin(path=4) == fw.ERR_INVALID_VALUE
+    assert _glin(m=40, k=4160, path=fw.PATH_BATCH) == fw.ERR_INVALID_VALUE
+    assert _glin(m=40, x=X + 2, path=fw.PATH_BATCH) == fw.ERR_MISALIGNED
     assert _glin(m=0) == fw.SUCCESS
     assert _glin(n=0) == fw.SUCCESS
 

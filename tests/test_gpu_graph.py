@@ -4,7 +4,7 @@ Every path enqueues only kernel launches with the caller's buffers (no
 allocation, no memset, no host copy), so a captured sequence must replay to
 the eager results, bit for bit: each call is deterministic. The graph holds a
 GEMV, a single-pass and a split-k skinny call, a split and a single-pass call
-of the batch GEMM, a fallback call, grouped calls and a W8A8 layer. Between replays the outputs are overwritten with NaN and
+of the batch GEMM, a fallback call, grouped calls (skinny and batch) and a W8A8 layer. Between replays the outputs are overwritten with NaN and
 unrelated eager calls run on the same stream, so a replay that skipped a
 launch or read a stale buffer would show.
 """
@@ -27,6 +27,7 @@ CALLS = [
     ("linear", 300, 2048, 512, torch.bfloat16, "batch_kernel<BN=64,BM=32,W=2>"),
     ("grouped32", 1, 512, 1024, torch.bfloat16, None),
     ("grouped128", 16, 1024, 2048, torch.float16, None),
+    ("grouped64", 100, 1000, 1024, torch.bfloat16, None),  # the batch GEMM with group scales
     ("w8a8", 300, 512, 512, torch.bfloat16, None),
 ]
 

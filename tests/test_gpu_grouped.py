@@ -147,7 +147,7 @@ def test_grouped_skinny(m, n, k, g, dtype, bias, kernel):
 
 GENERIC = [
     # (m, n, k, g, dtype, bias, x_offset)
-    (33, 100, 512, 32, torch.bfloat16, True, 0),
+    (33, 100, 544, 32, torch.bfloat16, True, 0),    # k % 256 != 0 above 32 tokens
     (70, 45, 320, 64, torch.float16, False, 0),     # k % 256 != 0, ragged m and n
     (1, 77, 8320, 128, torch.bfloat16, True, 0),
     (5, 130, 1024, 32, torch.float16, True, 1),     # x not 16-byte aligned
@@ -170,14 +170,40 @@ def test_grouped_generic(m, n, k, g, dtype, bias, xoff):
     _run_and_check(w, x, b, g, fw.PATH_AUTO, "grouped_generic_kernel", x_offset=xoff)
 
 
-@pytest.mark.parametrize("m,k,g", [(1, 1024, 32), (4, 2048, 64), (24, 1024, 128)])
+BATCH = [
+    # (m, n, k, g, dtype, bias, kernel): the batch GEMM with group scales, every
+    # tile it plans for each group size, ragged channel and token tails, the
+    # shortest ring (k = 256) and k stagger over the XCDs
+    (33, 100, 512, 32, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
+    (40, 300, 1024, 128, torch.float16, False, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
+    (33, 4100, 768, 64, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
+    (96, 2000, 2048, 128, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
+    (100, 9000, 2048, 32, torch.float16, True, "batch_grouped_kernel<BN=64,BM=64,W=4>"),
+    (200, 10000, 512, 64, torch.bfloat16, False, "batch_grouped_kernel<BN=64,BM=64,W=4>"),
+    (300, 4096, 4096, 64, torch.float16, True, "batch_grouped_kernel<BN=128,BM=64,W=8>"),
+    (1000, 3000, 256, 128, torch.bfloat16, True, "batch_grouped_kernel<BN=128,BM=64,W=8>"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,g,dtype,bias,kernel", BATCH)
+def test_grouped_batch(m, n, k, g, dtype, bias, kernel):
+    print(f"grouped batch m={m} n={n} k={k} g={g} {kernel}", flush=True)
+    w, x, b = _case(m * 7 + n + k + g, m, n, k, g, dtype, bias)
+    _run_and_check(w, x, b, g, fw.PATH_AUTO, kernel)
+
+
+@pytest.mark.parametrize("m,k,g", [(1, 1024, 32), (4, 2048, 64), (24, 1024, 128), (32, 1024, 32),
+                                   (40, 1024, 64), (65, 2048, 32)])
 def test_grouped_paths_agree(m, k, g):
-    """Forced paths on the same covered shape each pass the gate."""
+    """Forced paths on the same covered shape each pass the gate and agree
+    within fp32 summation-order rounding."""
     n = 300
     w, x, b = _case(m + k + g, m, n, k, g, torch.bfloat16, True)
-    paths = [fw.PATH_SKINNY, fw.PATH_FALLBACK] + ([fw.PATH_GEMV] if m == 1 else [])
-    for p in paths:
-        _run_and_check(w, x, b, g, p)
+    paths = [fw.PATH_FALLBACK] + ([fw.PATH_SKINNY] if m <= 32 else []) + ([fw.PATH_GEMV] if m == 1 else []) + \
+        [fw.PATH_BATCH]
+    outs = [_run_and_check(w, x, b, g, p).double().cpu().numpy() for p in paths]
+    for o in outs[1:]:
+        assert np.allclose(o, outs[0], rtol=2e-2, atol=1e-2)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
@@ -199,7 +225,8 @@ def test_dequantize_grouped_bits(dtype):
 
 @pytest.mark.parametrize("shape,m,g", [((14336, 4096), 1, 128), ((4096, 14336), 1, 32),
                                        ((14336, 4096), 16, 32), ((14336, 4096), 32, 128),
-                                       ((4096, 4096), 16, 64)])
+                                       ((4096, 4096), 16, 64), ((14336, 4096), 128, 128),
+                                       ((4096, 14336), 64, 32)])
 def test_grouped_full_size(shape, m, g):
     """Decode- and sweep-sized layers: every output of the call against the oracle."""
     n, k = shape
