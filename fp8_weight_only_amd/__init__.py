@@ -32,6 +32,7 @@ __all__ = [
     "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes", "fp8w_linear_kernel",
     "fp8w_stream_read_probe", "fp8w_quantize_grouped", "fp8w_linear_grouped", "fp8w_linear_grouped_with_path",
     "fp8w_linear_grouped_path", "fp8w_linear_grouped_kernel", "fp8w_dequantize_grouped",
+    "fp8w_linear_grouped_with_workspace", "fp8w_linear_grouped_workspace_bytes", "grouped_workspace_bytes",
     "quantize_grouped", "linear_grouped", "dequantize_grouped", "fp8w_fnuz_to_ocp", "fnuz_to_ocp", "ocp_codes",
     "fp8w_quantize_activations", "fp8w_gemm_w8a8", "fp8w_linear_w8a8", "fp8w_linear_w8a8_workspace_bytes",
     "fp8w_linear_w8a8_kernel", "quantize_activations", "gemm_w8a8", "linear_w8a8",
@@ -65,6 +66,8 @@ EXPORTS = {
     "fp8w_quantize_grouped": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P]),
     "fp8w_linear_grouped": (_I, [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P]),
     "fp8w_linear_grouped_with_path": (_I, [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _I, _P]),
+    "fp8w_linear_grouped_with_workspace": (_I, [_P, _I, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _SZ, _I, _P]),
+    "fp8w_linear_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_linear_grouped_path": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_linear_grouped_kernel": (ctypes.c_char_p, [_I, _I64, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_dequantize_grouped": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P]),
@@ -157,6 +160,16 @@ def fp8w_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, stream)
 
 def fp8w_linear_grouped_with_path(x, act_dtype, m, k, q, scale, group, bias, n, y, path, stream) -> int:
     return load().fp8w_linear_grouped_with_path(x, act_dtype, m, k, q, scale, group, bias, n, y, path, stream)
+
+
+def fp8w_linear_grouped_with_workspace(x, act_dtype, m, k, q, scale, group, bias, n, y, workspace, workspace_bytes,
+                                       path, stream) -> int:
+    return load().fp8w_linear_grouped_with_workspace(x, act_dtype, m, k, q, scale, group, bias, n, y, workspace,
+                                                     workspace_bytes, path, stream)
+
+
+def fp8w_linear_grouped_workspace_bytes(m, n, k, group, act_dtype, x, q) -> int:
+    return load().fp8w_linear_grouped_workspace_bytes(m, n, k, group, act_dtype, x, q)
 
 
 def fp8w_linear_grouped_path(m, n, k, group, act_dtype, x, q) -> int:
@@ -338,10 +351,20 @@ def quantize_grouped(w: torch.Tensor, group: int):
     return q, scale
 
 
+def grouped_workspace_bytes(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor) -> int:
+    m, k = x.shape
+    group = k // scale.shape[1]
+    return fp8w_linear_grouped_workspace_bytes(m, q.shape[0], k, group, _dtype_code(x.dtype), x.data_ptr(),
+                                               q.data_ptr())
+
+
 def linear_grouped(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor = None,
-                   out: torch.Tensor = None, path: int = PATH_AUTO) -> torch.Tensor:
+                   out: torch.Tensor = None, path: int = PATH_AUTO, workspace: torch.Tensor = None) -> torch.Tensor:
     """y = sum_j scale[n, j] * sum_{k in group j} x[m,k] value(q[n,k]) + bias[n],
-    rounded once to x.dtype; scale is [n, k // group] (the group size follows)."""
+    rounded once to x.dtype; scale is [n, k // group] (the group size follows).
+    ``workspace``: used for a k split on some batch shapes (m > 32); when None
+    and the call's plan splits, one of fp8w_linear_grouped_workspace_bytes is
+    allocated here with torch; an empty tensor keeps the single-pass plan."""
     if x.dim() != 2 or q.dim() != 2 or q.dtype != torch.uint8 or scale.dtype != torch.float32 or scale.dim() != 2:
         raise ValueError("expected x [m,k], q uint8 [n,k], scale fp32 [n, k // group]")
     m, k = x.shape
@@ -356,10 +379,19 @@ def linear_grouped(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: 
         out = torch.empty((m, n), dtype=x.dtype, device=x.device)
     elif out.shape != (m, n) or out.dtype != x.dtype:
         raise ValueError("out must be [m, n] in the activation dtype")
-    st = fp8w_linear_grouped_with_path(_dev(x, "x") if x.numel() else 0, act, m, k,
-                                       _dev(q, "q") if q.numel() else 0, _dev(scale, "scale"), group,
-                                       _dev(bias, "bias") if bias is not None and n else 0, n,
-                                       _dev(out, "out") if out.numel() else 0, path, _stream(x.device))
+    xp = _dev(x, "x") if x.numel() else 0
+    qp = _dev(q, "q") if q.numel() else 0
+    need = 0
+    if path in (PATH_AUTO, PATH_BATCH) and fp8w_linear_grouped_path(m, n, k, group, act, xp, qp) == PATH_BATCH:
+        need = fp8w_linear_grouped_workspace_bytes(m, n, k, group, act, xp, qp)
+    if need and workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    wp = _dev(workspace, "workspace") if workspace is not None and workspace.numel() else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = fp8w_linear_grouped_with_workspace(xp, act, m, k, qp, _dev(scale, "scale"), group,
+                                            _dev(bias, "bias") if bias is not None and n else 0, n,
+                                            _dev(out, "out") if out.numel() else 0, wp, wb, path,
+                                            _stream(x.device))
     _check(st, "fp8w_linear_grouped")
     return out
 

@@ -213,8 +213,8 @@ size_t group_scale_bytes(int64_t n, int64_t k, int64_t group)
 }
 
 fp8w_status_t run_linear_grouped(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, const uint8_t* q,
-                                 const float* scale, int64_t group, const void* bias, int64_t n, void* y, int path,
-                                 hipStream_t stream)
+                                 const float* scale, int64_t group, const void* bias, int64_t n, void* y, void* ws,
+                                 size_t ws_bytes, int path, hipStream_t stream)
 {
     if (!valid_act(act) || !sizes_ok(m, n, k) || !valid_group(k, group))
         return FP8W_ERR_INVALID_VALUE;
@@ -243,7 +243,19 @@ fp8w_status_t run_linear_grouped(const void* x, fp8w_dtype_t act, int64_t m, int
         overlap(y, ybytes, scale, group_scale_bytes(n, k, group)) ||
         overlap(y, ybytes, bias, bias ? (size_t)n * 2 : 0))
         return FP8W_ERR_INVALID_VALUE;
-    return hip_status(fp8w::launch_linear_grouped(path, x, act_of(act), m, k, q, scale, group, bias, n, y, stream));
+    // the batch path splits k on plans that use it, when the caller's workspace is large enough
+    const size_t need = path == FP8W_PATH_BATCH ? fp8w::batch_grouped_workspace_bytes(m, n, k, group) : 0;
+    const bool use_ws = need > 0 && ws && ws_bytes >= need;
+    if (use_ws) {
+        if (!aligned(ws, 16))
+            return FP8W_ERR_MISALIGNED;
+        if (overlap(ws, need, y, ybytes) || overlap(ws, need, x, (size_t)m * (size_t)k * 2) ||
+            overlap(ws, need, q, (size_t)n * (size_t)k) || overlap(ws, need, scale, group_scale_bytes(n, k, group)) ||
+            overlap(ws, need, bias, bias ? (size_t)n * 2 : 0))
+            return FP8W_ERR_INVALID_VALUE;
+    }
+    return hip_status(fp8w::launch_linear_grouped(path, x, act_of(act), m, k, q, scale, group, bias, n, y,
+                                                  use_ws ? ws : nullptr, use_ws ? ws_bytes : 0, stream));
 }
 
 }  // namespace
@@ -288,14 +300,33 @@ fp8w_status_t fp8w_linear_grouped(const void* x, fp8w_dtype_t act_dtype, int64_t
                                   const float* scale, int64_t group, const void* bias, int64_t n, void* y,
                                   hipStream_t stream)
 {
-    return run_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, FP8W_PATH_AUTO, stream);
+    return run_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, nullptr, 0, FP8W_PATH_AUTO, stream);
 }
 
 fp8w_status_t fp8w_linear_grouped_with_path(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
                                             const uint8_t* q, const float* scale, int64_t group, const void* bias,
                                             int64_t n, void* y, int path, hipStream_t stream)
 {
-    return run_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, path, stream);
+    return run_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, nullptr, 0, path, stream);
+}
+
+fp8w_status_t fp8w_linear_grouped_with_workspace(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                                 const uint8_t* q, const float* scale, int64_t group,
+                                                 const void* bias, int64_t n, void* y, void* workspace,
+                                                 size_t workspace_bytes, int path, hipStream_t stream)
+{
+    return run_linear_grouped(x, act_dtype, m, k, q, scale, group, bias, n, y, workspace, workspace_bytes, path,
+                              stream);
+}
+
+size_t fp8w_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t group, fp8w_dtype_t act_dtype,
+                                           const void* x, const uint8_t* q)
+{
+    if (!valid_act(act_dtype) || !sizes_ok(m, n, k) || !valid_group(k, group))
+        return 0;
+    if (auto_path_grouped(m, k, x, q) != FP8W_PATH_BATCH)
+        return 0;
+    return fp8w::batch_grouped_workspace_bytes(m, n, k, group);
 }
 
 int fp8w_linear_grouped_path(int64_t m, int64_t n, int64_t k, int64_t group, fp8w_dtype_t act_dtype,
@@ -316,12 +347,12 @@ const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || k % 256 != 0 || k == 0)
             return nullptr;
-        return fp8w::grouped_kernel_name(path, m, n, k, group);
+        return fp8w::grouped_kernel_name(path, m, n, k, group, false);
     }
     if (path == FP8W_PATH_BATCH)
-        return m >= 1 && fast_k(k) ? fp8w::grouped_kernel_name(3, m, n, k, group) : nullptr;
+        return m >= 1 && fast_k(k) ? fp8w::grouped_kernel_name(3, m, n, k, group, auto_path_grouped(m, k, x, q) == FP8W_PATH_BATCH) : nullptr;
     if (path == FP8W_PATH_FALLBACK)
-        return fp8w::grouped_kernel_name(2, m, n, k, group);
+        return fp8w::grouped_kernel_name(2, m, n, k, group, false);
     return nullptr;
 }
 

@@ -237,7 +237,8 @@ struct BatchPipe {
 // G > 0: scale holds the group scales [n, k / G] and the epilogue adds only the
 // bias (no split).
 template <typename A, int BN, int BM, int WN, int WM, int G = 0, int GM = 4>
-__global__ __launch_bounds__(WN* WM * kWave) void batch_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(WN* WM * kWave) __attribute__((amdgpu_waves_per_eu(G > 0 && WN * WM < 8 ? 2 : 1)))
+void batch_kernel(const uint16_t* __restrict__ x,
                                                               const uint8_t* __restrict__ q,
                                                               const float* __restrict__ scale,
                                                               const uint16_t* __restrict__ bias,
@@ -459,56 +460,78 @@ hipError_t launch_typed(const BatchPlan& p, const void* x, int64_t m, int64_t k,
 }
 
 template <typename A, int G>
-hipError_t launch_grouped_tile(const BatchTile& t, const void* x, int64_t m, int64_t k, const uint8_t* q,
-                               const float* gs, const void* bias, int64_t n, void* y, hipStream_t stream)
+hipError_t launch_grouped_tile(const BatchTile& t, int splits, const void* x, int64_t m, int64_t k, const uint8_t* q,
+                               const float* gs, const void* bias, int64_t n, void* y, float* part,
+                               hipStream_t stream)
 {
     if constexpr (G >= 64) {
         if (t.bn == 128)
-            return launch_b<A, 128, 64, 4, 2, G>(x, m, k, q, gs, bias, n, y, 1, nullptr, stream);
+            return launch_b<A, 128, 64, 4, 2, G>(x, m, k, q, gs, bias, n, y, splits, part, stream);
     }
     if (t.bn != 64)
         return hipErrorInvalidValue;  // not a grouped tile (batch_plan never picks one)
     if (t.bm == 64)
-        return launch_b<A, 64, 64, 2, 2, G>(x, m, k, q, gs, bias, n, y, 1, nullptr, stream);
-    return launch_b<A, 64, 32, 2, 1, G>(x, m, k, q, gs, bias, n, y, 1, nullptr, stream);
+        return launch_b<A, 64, 64, 2, 2, G>(x, m, k, q, gs, bias, n, y, splits, part, stream);
+    return launch_b<A, 64, 32, 2, 1, G>(x, m, k, q, gs, bias, n, y, splits, part, stream);
 }
 
 template <typename A>
-hipError_t launch_grouped_typed(const BatchTile& t, int64_t group, const void* x, int64_t m, int64_t k,
+hipError_t launch_grouped_typed(const BatchPlan& p, int64_t group, const void* x, int64_t m, int64_t k,
                                 const uint8_t* q, const float* gs, const void* bias, int64_t n, void* y,
-                                hipStream_t stream)
+                                float* part, hipStream_t stream)
 {
     if (group == 32)
-        return launch_grouped_tile<A, 32>(t, x, m, k, q, gs, bias, n, y, stream);
+        return launch_grouped_tile<A, 32>(p.tile, p.splits, x, m, k, q, gs, bias, n, y, part, stream);
     if (group == 64)
-        return launch_grouped_tile<A, 64>(t, x, m, k, q, gs, bias, n, y, stream);
+        return launch_grouped_tile<A, 64>(p.tile, p.splits, x, m, k, q, gs, bias, n, y, part, stream);
     if (group == 128)
-        return launch_grouped_tile<A, 128>(t, x, m, k, q, gs, bias, n, y, stream);
+        return launch_grouped_tile<A, 128>(p.tile, p.splits, x, m, k, q, gs, bias, n, y, part, stream);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+size_t batch_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t group)
+{
+    if (m < 1 || n < 1 || k < 256 || k % 256 != 0)
+        return 0;
+    const BatchPlan p = batch_plan(m, n, k, true, group);
+    return p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
+// A k split writes partial sums that already hold the group scales; the reduce
+// adds them in split order and applies only the bias (unit scale).
 hipError_t launch_batch_grouped(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* gs,
-                                int64_t group, const void* bias, int64_t n, void* y, hipStream_t stream)
+                                int64_t group, const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes,
+                                hipStream_t stream)
 {
     if (m == 0 || n == 0)
         return hipSuccess;
     if (k % 256 != 0 || k == 0)
         return hipErrorInvalidValue;
-    const BatchTile t = batch_plan(m, n, k, false, group).tile;
+    const size_t need = batch_grouped_workspace_bytes(m, n, k, group);
+    const BatchPlan p = batch_plan(m, n, k, ws != nullptr && need > 0 && ws_bytes >= need, group);
+    float* part = static_cast<float*>(ws);
+    hipError_t e = hipErrorInvalidValue;
     if (act == Act::BF16)
-        return launch_grouped_typed<Bf16>(t, group, x, m, k, q, gs, bias, n, y, stream);
-    if (act == Act::FP16)
-        return launch_grouped_typed<F16>(t, group, x, m, k, q, gs, bias, n, y, stream);
-    return hipErrorInvalidValue;
+        e = launch_grouped_typed<Bf16>(p, group, x, m, k, q, gs, bias, n, y, part, stream);
+    else if (act == Act::FP16)
+        e = launch_grouped_typed<F16>(p, group, x, m, k, q, gs, bias, n, y, part, stream);
+    if (e != hipSuccess || p.splits <= 1)
+        return e;
+    return launch_splitk_reduce(part, p.splits, m, n, nullptr, bias, y, act, stream);
 }
 
-const char* batch_grouped_kernel_name(int64_t m, int64_t n, int64_t k, int64_t group)
+const char* batch_grouped_kernel_name(int64_t m, int64_t n, int64_t k, int64_t group, bool with_workspace)
 {
     thread_local char name[96];
-    const BatchTile t = batch_plan(m, n, k, false, group).tile;
-    snprintf(name, sizeof name, "batch_grouped_kernel<BN=%d,BM=%d,W=%d>", t.bn, t.bm, t.wn * t.wm);
+    const BatchPlan p = batch_plan(m, n, k, with_workspace, group);
+    const BatchTile& t = p.tile;
+    if (p.splits > 1)
+        snprintf(name, sizeof name, "batch_grouped_kernel<BN=%d,BM=%d,W=%d>x%d+splitk_reduce_kernel", t.bn, t.bm,
+                 t.wn * t.wm, p.splits);
+    else
+        snprintf(name, sizeof name, "batch_grouped_kernel<BN=%d,BM=%d,W=%d>", t.bn, t.bm, t.wn * t.wm);
     return name;
 }
 

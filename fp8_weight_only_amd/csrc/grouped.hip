@@ -620,15 +620,15 @@ hipError_t launch_grouped_typed(int path, const void* x, int64_t m, int64_t k, c
 }  // namespace
 
 hipError_t launch_linear_grouped(int path, const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
-                                 const float* scale, int64_t group, const void* bias, int64_t n, void* y,
-                                 hipStream_t stream)
+                                 const float* scale, int64_t group, const void* bias, int64_t n, void* y, void* ws,
+                                 size_t ws_bytes, hipStream_t stream)
 {
     if (m == 0 || n == 0)
         return hipSuccess;
     if (k == 0)
         path = 2;  // y = bias: the generic kernel's k loop is empty
     if (path == 3)
-        return launch_batch_grouped(x, act, m, k, q, scale, group, bias, n, y, stream);
+        return launch_batch_grouped(x, act, m, k, q, scale, group, bias, n, y, ws, ws_bytes, stream);
     const int lg = 63 - __builtin_clzll((unsigned long long)group);
     if (act == Act::BF16)
         return launch_grouped_typed<Bf16>(path, x, m, k, q, scale, lg, bias, n, y, stream);
@@ -637,14 +637,14 @@ hipError_t launch_linear_grouped(int path, const void* x, Act act, int64_t m, in
     return hipErrorInvalidValue;
 }
 
-const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k, int64_t group)
+const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k, int64_t group, bool with_workspace)
 {
     static thread_local char name[96];
     if (path == 0)
         return n * k >= ((int64_t)96 << 20) ? "gemv_grouped_kernel<R=4,U=2,NT=128>"
                                             : "gemv_grouped_kernel<R=2,U=2,NT=64,DB>";
     if (path == 3)
-        return batch_grouped_kernel_name(m, n, k, group);
+        return batch_grouped_kernel_name(m, n, k, group, with_workspace);
     if (path == 1) {
         const GroupedPlan p = plan_grouped(m, n, k);
         if (p.pipe) {

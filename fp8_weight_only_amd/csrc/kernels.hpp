@@ -82,20 +82,24 @@ hipError_t launch_quantize_groups(const void* w, Act w_type, int64_t n, int64_t 
 // The grouped linear. path 0: M = 1 GEMV (k % 256 == 0, x and q 16-byte
 // aligned); path 1: M <= 32 skinny ring where k allows it, else the generic
 // kernel; path 2: the generic kernel (any m, n, k % group == 0, x 2-byte and q
-// 1-byte aligned); path 3: the batch GEMM (launch_batch_grouped).
+// 1-byte aligned); path 3: the batch GEMM (launch_batch_grouped, which alone
+// uses ws).
 hipError_t launch_linear_grouped(int path, const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
-                                 const float* scale, int64_t group, const void* bias, int64_t n, void* y,
-                                 hipStream_t stream);
+                                 const float* scale, int64_t group, const void* bias, int64_t n, void* y, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
 
 // The grouped linear above 32 tokens: the batch GEMM with group scales staged
 // beside the operands (k % 256 == 0, group 32 / 64 / 128, x and q 16-byte
-// aligned; single pass, no workspace).
+// aligned). Splits k when the plan asks for it and ws holds
+// batch_grouped_workspace_bytes (16-byte aligned), else single pass.
+size_t batch_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t group);
 hipError_t launch_batch_grouped(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* gs,
-                                int64_t group, const void* bias, int64_t n, void* y, hipStream_t stream);
-const char* batch_grouped_kernel_name(int64_t m, int64_t n, int64_t k, int64_t group);
+                                int64_t group, const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+const char* batch_grouped_kernel_name(int64_t m, int64_t n, int64_t k, int64_t group, bool with_workspace);
 
 // Name of the kernel launch_linear_grouped runs for this path and shape.
-const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k, int64_t group);
+const char* grouped_kernel_name(int path, int64_t m, int64_t n, int64_t k, int64_t group, bool with_workspace);
 
 // value(q) * scale[r, j / group] rounded to out_type.
 hipError_t launch_dequantize_grouped(const uint8_t* q, const float* scale, int64_t group, int64_t n, int64_t k,

@@ -373,7 +373,8 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
 }
 
 // Sum of the split-k partial sums in split order, then the epilogue: one
-// output per thread.
+// output per thread. scale == nullptr: unit scale (the partial sums of the
+// grouped batch GEMM already hold their group scales).
 template <typename A>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int m,
                                                             int64_t n, const float* __restrict__ scale,
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     float sum = part[e];
     for (int s = 1; s < splits; ++s)
         sum += part[(int64_t)s * m * n + e];
-    y[e] = epilogue<A>(sum, scale[ch], bias_bits(bias, ch));
+    y[e] = epilogue<A>(sum, scale ? scale[ch] : 1.0f, bias_bits(bias, ch));
 }
 
 // ---------------------------------------------------------------- dispatch

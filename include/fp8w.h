@@ -194,9 +194,10 @@ FP8W_API fp8w_status_t fp8w_quantize_grouped(const void* w, fp8w_dtype_t w_dtype
 /* y[m,n] = sum_j scale[n,j] * sum_{i<group} x[m, j*group+i] * value(q[n, j*group+i]) + bias[n],
    fp32 accumulation (each partial sum of exact products lies inside one
    group and is scaled before it is added), one rounding to act_dtype.
-   Arguments as for fp8w_linear; no workspace. Dispatch as fp8w_linear_path
-   (m == 1: GEMV; m <= 32: skinny MFMA kernel; m > 32: the batch GEMM, single
-   pass; k % 256 == 0 and 16-byte aligned x and q for all three); everything
+   Arguments as for fp8w_linear; no workspace (see
+   fp8w_linear_grouped_with_workspace). Dispatch as fp8w_linear_path (m == 1:
+   GEMV; m <= 32: skinny MFMA kernel; m > 32: the batch GEMM, here its single
+   pass plan; k % 256 == 0 and 16-byte aligned x and q for all three); everything
    else, and skinny shapes whose k the ring cannot tile, runs a generic kernel
    (any m, n; x 2-byte aligned). Asynchronous. */
 FP8W_API fp8w_status_t fp8w_linear_grouped(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
@@ -211,13 +212,34 @@ FP8W_API fp8w_status_t fp8w_linear_grouped_with_path(const void* x, fp8w_dtype_t
                                                      const void* bias, int64_t n, void* y, int path,
                                                      hipStream_t stream);
 
+/* fp8w_linear_grouped with a workspace (and an explicit FP8W_PATH_*, or
+   FP8W_PATH_AUTO): on the batch path (m > 32) a plan that splits k over
+   workgroups uses fp8w_linear_grouped_workspace_bytes of it (16-byte aligned,
+   not overlapping any argument: FP8W_ERR_MISALIGNED / FP8W_ERR_INVALID_VALUE),
+   writing fp32 partial sums there and adding them in a second kernel;
+   without one (NULL, or fewer bytes) the same call runs its single-pass plan.
+   Other paths ignore the workspace. Asynchronous. */
+FP8W_API fp8w_status_t fp8w_linear_grouped_with_workspace(const void* x, fp8w_dtype_t act_dtype, int64_t m,
+                                                          int64_t k, const uint8_t* q, const float* scale,
+                                                          int64_t group, const void* bias, int64_t n, void* y,
+                                                          void* workspace, size_t workspace_bytes, int path,
+                                                          hipStream_t stream);
+
+/* Workspace bytes fp8w_linear_grouped_with_workspace uses on the path
+   FP8W_PATH_AUTO takes: splits * m * n * 4 on batch shapes whose plan splits
+   k, else 0 (also when invalid). */
+FP8W_API size_t fp8w_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t group,
+                                                    fp8w_dtype_t act_dtype, const void* x, const uint8_t* q);
+
 /* Path fp8w_linear_grouped takes (FP8W_PATH_GEMV, _SKINNY, _BATCH or
    _FALLBACK, by the rules of fp8w_linear_path), -1 when the arguments are
    invalid. */
 FP8W_API int fp8w_linear_grouped_path(int64_t m, int64_t n, int64_t k, int64_t group, fp8w_dtype_t act_dtype,
                                       const void* x, const uint8_t* q);
 
-/* Name of the kernel a grouped call takes (as fp8w_linear_kernel); NULL when invalid. */
+/* Name of the kernel a grouped call takes (as fp8w_linear_kernel: on the
+   batch path, given the workspace fp8w_linear_grouped_workspace_bytes
+   reports); NULL when invalid. */
 FP8W_API const char* fp8w_linear_grouped_kernel(int path, int64_t m, int64_t n, int64_t k, int64_t group,
                                                 fp8w_dtype_t act_dtype, const void* x, const uint8_t* q);
 

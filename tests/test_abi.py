@@ -30,7 +30,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fw.load()
     names = declared_symbols()
-    assert len(names) == 23
+    assert len(names) == 25
     for name in names:
         assert hasattr(lib, name), name
         assert name in fw.EXPORTS, name
@@ -293,7 +293,7 @@ def test_grouped_paths_and_kernel_names():
     assert gk(A, 8, 4096, 4096, 64, fw.BF16, X, Q) == "pipe_grouped_kernel<XR=8,CT=1,KP=2,NS=4>"
     assert gk(A, 32, 4096, 4096, 64, fw.BF16, X, Q) == "pipe_grouped_kernel<XR=32,CT=1,KP=2,NS=2>"
     assert gk(A, 2, 4096, 768, 128, fw.BF16, X, Q) == "grouped_generic_kernel"      # ring cannot tile k
-    assert gk(A, 64, 4096, 4096, 32, fw.BF16, X, Q) == "batch_grouped_kernel<BN=64,BM=32,W=2>"
+    assert gk(A, 64, 4096, 4096, 32, fw.BF16, X, Q) == "batch_grouped_kernel<BN=64,BM=64,W=4>x4+splitk_reduce_kernel"
     assert gk(A, 128, 14336, 4096, 128, fw.BF16, X, Q) == "batch_grouped_kernel<BN=128,BM=64,W=8>"
     assert gk(A, 128, 14336, 4096, 32, fw.BF16, X, Q).startswith("batch_grouped_kernel<BN=64,")  # no 128 x 64 for g 32
     assert gk(fw.PATH_BATCH, 2, 4096, 4096, 64, fw.BF16, X, Q) == "batch_grouped_kernel<BN=64,BM=32,W=2>"
@@ -301,6 +301,26 @@ def test_grouped_paths_and_kernel_names():
     assert gk(A, 64, 4096, 4160, 64, fw.BF16, X, Q) == "grouped_generic_kernel"
     assert gk(fw.PATH_FALLBACK, 1, 4096, 4096, 32, fw.BF16, X, Q) == "grouped_generic_kernel"
     assert gk(fw.PATH_GEMV, 2, 4096, 4096, 32, fw.BF16, X, Q) is None
+
+
+def test_grouped_workspace_bytes_and_validation():
+    wb = fw.fp8w_linear_grouped_workspace_bytes
+    assert wb(64, 4096, 4096, 32, fw.BF16, X, Q) == 4 * 64 * 4096 * 4              # x4 split
+    assert wb(300, 4096, 4096, 64, fw.BF16, X, Q) == 0                             # single pass
+    assert wb(16, 4096, 4096, 32, fw.BF16, X, Q) == 0                              # skinny path
+    assert wb(64, 4096, 4160, 64, fw.BF16, X, Q) == 0                              # generic kernel
+    assert wb(64, 4096, 4096, 48, fw.BF16, X, Q) == 0                              # invalid group
+
+    def g(ws, nbytes, **kw):
+        a = dict(x=X, act=fw.BF16, m=64, k=4096, q=Q, s=S, g=32, b=B, n=4096, y=Y, path=fw.PATH_AUTO)
+        a.update(kw)
+        return fw.fp8w_linear_grouped_with_workspace(a["x"], a["act"], a["m"], a["k"], a["q"], a["s"], a["g"],
+                                                     a["b"], a["n"], a["y"], ws, nbytes, a["path"], 0)
+    need = wb(64, 4096, 4096, 32, fw.BF16, X, Q)
+    assert g(WS + 8, need) == fw.ERR_MISALIGNED                                   # used, not 16-byte aligned
+    assert g(Y, need) == fw.ERR_INVALID_VALUE                                     # overlaps y
+    assert g(0, 0, m=0) == fw.SUCCESS
+    assert g(WS, need, path=4) == fw.ERR_INVALID_VALUE
 
 
 def test_grouped_rejects_invalid_arguments():

@@ -27,7 +27,8 @@ CALLS = [
     ("linear", 300, 2048, 512, torch.bfloat16, "batch_kernel<BN=64,BM=32,W=2>"),
     ("grouped32", 1, 512, 1024, torch.bfloat16, None),
     ("grouped128", 16, 1024, 2048, torch.float16, None),
-    ("grouped64", 100, 1000, 1024, torch.bfloat16, None),  # the batch GEMM with group scales
+    ("grouped64", 100, 1000, 1024, torch.bfloat16, None),  # the batch GEMM with group scales, k split
+    ("grouped128", 300, 2048, 512, torch.float16, None),  # and single pass
     ("w8a8", 300, 512, 512, torch.bfloat16, None),
 ]
 
@@ -43,10 +44,13 @@ class Recorded:
         self.bias = case.layer.bias.to(DEV)
         if kind.startswith("grouped"):
             self.q, self.scale = fw.quantize_grouped(w, int(kind[len("grouped"):]))
+            need = fw.grouped_workspace_bytes(self.x, self.q, self.scale)
+            self.ws = torch.empty((need,), dtype=torch.uint8, device=DEV)
         else:
             self.q, self.scale = fw.quantize(w)
         self.y = torch.empty((m, n), dtype=dtype, device=DEV)
-        self.ws = None
+        if not kind.startswith("grouped"):
+            self.ws = None
         if kind == "linear":
             need = fw.workspace_bytes(self.x, self.q, self.y)
             if kernel is not None:
@@ -64,7 +68,7 @@ class Recorded:
             fw.linear(self.x, self.q, self.scale, self.bias, out=out,
                       workspace=self.ws if self.ws is not None else torch.empty(0, dtype=torch.uint8, device=DEV))
         elif self.kind.startswith("grouped"):
-            fw.linear_grouped(self.x, self.q, self.scale, self.bias, out=out)
+            fw.linear_grouped(self.x, self.q, self.scale, self.bias, out=out, workspace=self.ws)
         else:
             fw.linear_w8a8(self.x, self.q, self.scale, self.bias, out=out, workspace=self.ws)
 

@@ -79,7 +79,7 @@ def _case(seed, m, n, k, g, dtype, bias):
     return w, x, b
 
 
-def _run_and_check(w, x, b, g, path, expect_kernel=None, x_offset=0):
+def _run_and_check(w, x, b, g, path, expect_kernel=None, x_offset=0, workspace=None):
     m, k = x.shape
     n = w.shape[0]
     q, s = fw.quantize_grouped(torch.from_numpy(w).to(DEV), g)
@@ -97,7 +97,7 @@ def _run_and_check(w, x, b, g, path, expect_kernel=None, x_offset=0):
         assert got == expect_kernel, got
     bd = None if b is None else b.to(DEV)
     y = nan_like((m, n), x.dtype, DEV)
-    fw.linear_grouped(xd, q, s, bd, out=y, path=path)
+    fw.linear_grouped(xd, q, s, bd, out=y, path=path, workspace=workspace)
     torch.cuda.synchronize()
     x64 = x.double().numpy()
     b64 = None if b is None else b.double().numpy()
@@ -175,13 +175,18 @@ BATCH = [
     # tile it plans for each group size, ragged channel and token tails, the
     # shortest ring (k = 256) and k stagger over the XCDs
     (33, 100, 512, 32, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
-    (40, 300, 1024, 128, torch.float16, False, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
+    (40, 300, 1024, 128, torch.float16, False, "batch_grouped_kernel<BN=64,BM=32,W=2>x2+splitk_reduce_kernel"),
     (33, 4100, 768, 64, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
-    (96, 2000, 2048, 128, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
+    (96, 2000, 2048, 128, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>x2+splitk_reduce_kernel"),
     (100, 9000, 2048, 32, torch.float16, True, "batch_grouped_kernel<BN=64,BM=64,W=4>"),
     (200, 10000, 512, 64, torch.bfloat16, False, "batch_grouped_kernel<BN=64,BM=64,W=4>"),
     (300, 4096, 4096, 64, torch.float16, True, "batch_grouped_kernel<BN=128,BM=64,W=8>"),
     (1000, 3000, 256, 128, torch.bfloat16, True, "batch_grouped_kernel<BN=128,BM=64,W=8>"),
+    # k split over workgroups (fp32 partial sums that hold the group scales)
+    (33, 1000, 3072, 32, torch.float16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>x6+splitk_reduce_kernel"),
+    (90, 1000, 1536, 128, torch.bfloat16, False, "batch_grouped_kernel<BN=64,BM=32,W=2>x3+splitk_reduce_kernel"),
+    (150, 1200, 4096, 64, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=64,W=4>x4+splitk_reduce_kernel"),
+    (128, 4096, 4096, 128, torch.float16, True, "batch_grouped_kernel<BN=128,BM=64,W=8>x4+splitk_reduce_kernel"),
 ]
 
 
@@ -189,7 +194,12 @@ BATCH = [
 def test_grouped_batch(m, n, k, g, dtype, bias, kernel):
     print(f"grouped batch m={m} n={n} k={k} g={g} {kernel}", flush=True)
     w, x, b = _case(m * 7 + n + k + g, m, n, k, g, dtype, bias)
-    _run_and_check(w, x, b, g, fw.PATH_AUTO, kernel)
+    y = _run_and_check(w, x, b, g, fw.PATH_AUTO, kernel)  # allocates the workspace a split plan asks for
+    if "splitk" in kernel:
+        # no workspace: the single-pass plan, within the gate and within fp32
+        # summation-order rounding of the split result
+        y1 = _run_and_check(w, x, b, g, fw.PATH_AUTO, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+        assert np.allclose(y1.double().cpu().numpy(), y.double().cpu().numpy(), rtol=2e-2, atol=1e-2)
 
 
 @pytest.mark.parametrize("m,k,g", [(1, 1024, 32), (4, 2048, 64), (24, 1024, 128), (32, 1024, 32),
