@@ -147,23 +147,30 @@ def grouped_bytes(m, n, k, g, bias):
 
 
 class GroupedCall:
+    """One grouped call per weight copy; a batch plan that splits k gets the
+    workspace it asks for (fp8w_linear_grouped_with_workspace)."""
+
     def __init__(self, layer, x, dev):
         self.layer, self.x = layer, x
         self.m = x.shape[0]
         self.y = torch.empty((self.m, layer.n), dtype=x.dtype, device=dev)
         act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
         self.act = act
+        need = fw.fp8w_linear_grouped_workspace_bytes(self.m, layer.n, layer.k, layer.group, act, x.data_ptr(),
+                                                      layer.qs[0][0].data_ptr())
+        self.ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
         self.args = [(x.data_ptr(), act, self.m, layer.k, q.data_ptr(), s.data_ptr(), layer.group,
-                      0 if layer.bias is None else layer.bias.data_ptr(), layer.n, self.y.data_ptr())
+                      0 if layer.bias is None else layer.bias.data_ptr(), layer.n, self.y.data_ptr(),
+                      self.ws.data_ptr() if need else 0, need, fw.PATH_AUTO)
                      for q, s in layer.qs]
         self.bytes = grouped_bytes(self.m, layer.n, layer.k, layer.group, layer.bias is not None)
         self.kernel = fw.fp8w_linear_grouped_kernel(fw.PATH_AUTO, self.m, layer.n, layer.k, layer.group, act,
                                                     x.data_ptr(), layer.qs[0][0].data_ptr())
 
     def launch(self, copy, stream):
-        r = fw.load().fp8w_linear_grouped(*self.args[copy % len(self.args)], stream)
+        r = fw.load().fp8w_linear_grouped_with_workspace(*self.args[copy % len(self.args)], stream)
         if r != 0:
-            raise fw.Fp8wError(r, "fp8w_linear_grouped")
+            raise fw.Fp8wError(r, "fp8w_linear_grouped_with_workspace")
 
 
 def grouped_report(call, st):
@@ -802,7 +809,7 @@ def _short_kernel_name(full):
     keys = {"pipe_kernel": ("XR", "CT", "KP", "NS"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
             "gemv_kernel": ("R", "U", "NT", "DB"), "wpipe_kernel": ("XR", "CT", "NS"), "w8a8_kernel": ("BN", "BM", "NS", "WN", "WM", "GM"),
             "gemv_grouped_kernel": ("R", "U", "NT", "DB"), "pipe_grouped_kernel": ("XR", "CT", "KP", "NS", "G"),
-            "batch_kernel": ("BN", "BM", "WN", "WM", "GM")}.get(name)
+            "batch_kernel": ("BN", "BM", "WN", "WM", "G", "GM")}.get(name)
     if keys and len(args) == len(keys) + 1:  # first argument is the activation type
         return f"{name}<" + ",".join(f"{kk}={v}" for kk, v in zip(keys, args[1:])) + ">"
     return name + targs
@@ -954,7 +961,8 @@ def extra_sections(dev, stream, reps=100, only=None):
 
     if "grouped" in want:
         # group scales along k: the decode layers at M = 1 (bf16) and the skinny
-        # layer at M = 2, 16, 32 (fp16), with g = 32 and g = 128
+        # layer at M = 2, 16, 32 (fp16), with g = 32 and g = 128; then the
+        # decode layers at the batched-decode sizes (the batch GEMM)
         gr = []
         for g in (32, 128):
             for i in range(3):
@@ -977,6 +985,20 @@ def extra_sections(dev, stream, reps=100, only=None):
                     f"[{c.kernel}]")
             del L
             torch.cuda.empty_cache()
+        for g in (32, 128):
+            for i in range(3):
+                lw = workloads.decode_layer(i)
+                n, k = lw.w.shape
+                L = GroupedLayer(lw, g, max(1, math.ceil(ROTATE_BYTES / grouped_bytes(max(workloads.BATCH_MS), n, k,
+                                                                                      g, True))), dev)
+                for m in workloads.BATCH_MS:
+                    c = GroupedCall(L, workloads.batch_x(i, m).to(dev), dev)
+                    gr.append(grouped_report(c, burst(c, reps, 10, stream)))
+                    log(f"  grouped g={g} {L.name} m={m}: {gr[-1]['us_per_call']:.2f} us "
+                        f"{gr[-1]['tflops']:.0f} TFLOP/s [{c.kernel}]")
+                    del c
+                del L
+                torch.cuda.empty_cache()
         ex["grouped"] = gr
 
     if "large" in want:
