@@ -187,6 +187,10 @@ BATCH = [
     (90, 1000, 1536, 128, torch.bfloat16, False, "batch_grouped_kernel<BN=64,BM=32,W=2>x3+splitk_reduce_kernel"),
     (150, 1200, 4096, 64, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=64,W=4>x4+splitk_reduce_kernel"),
     (128, 4096, 4096, 128, torch.float16, True, "batch_grouped_kernel<BN=128,BM=64,W=8>x4+splitk_reduce_kernel"),
+    # fewer channels than one tile (rows past n read the last row, never stored)
+    (33, 1, 256, 32, torch.bfloat16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
+    (257, 63, 512, 64, torch.float16, True, "batch_grouped_kernel<BN=64,BM=32,W=2>"),
+    (33, 5, 1024, 128, torch.bfloat16, False, "batch_grouped_kernel<BN=64,BM=32,W=2>x2+splitk_reduce_kernel"),
 ]
 
 
@@ -244,3 +248,18 @@ def test_grouped_full_size(shape, m, g):
     w = workloads.weight_normal(7, n // 1024 + k // 1024, n, k, 0.02)
     x = workloads.activations(7, m, m, k, torch.bfloat16)
     _run_and_check(w, x, None, g, fw.PATH_AUTO)
+
+
+def test_grouped_batch_zero_token_rows_give_bias():
+    """Token rows of zeros through the grouped batch GEMM give the bias exactly,
+    single pass and split."""
+    for (m, n, k, g) in [(70, 500, 512, 32), (40, 300, 2048, 128)]:
+        w, x, b = _case(m + n + k, m, n, k, g, torch.float16, True)
+        x[[0, 33, m - 1]] = 0.0
+        q, s = fw.quantize_grouped(torch.from_numpy(w).to(DEV), g)
+        xd = x.to(DEV)
+        assert fw.fp8w_linear_grouped_path(m, n, k, g, fw.FP16, xd.data_ptr(), q.data_ptr()) == fw.PATH_BATCH
+        y = fw.linear_grouped(xd, q, s, b.to(DEV))
+        torch.cuda.synchronize()
+        for r in (0, 33, m - 1):
+            assert torch.equal(y[r].cpu(), b)
