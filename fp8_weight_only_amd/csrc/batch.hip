@@ -33,6 +33,14 @@
 // so the 16 lanes of a ds_read_b128 phase (16 consecutive rows, one chunk)
 // hit distinct bank groups. Tiles are dealt XCD-aware and each XCD starts an
 // eighth of k later, as in the W8A8 kernel.
+//
+// Group scales along k (template G = 32 / 64 / 128; "FP8 weight-only
+// (precision: fp8_weights)" and the per-group reading of the quantization
+// pages: one scale per run of G weights of a row): each stage also stages its
+// channels' group scales in LDS, the MFMA steps take the standard k order so a
+// span of min(G, 64) k lies in one group, and every span's fp32 sum is scaled
+// and added to the accumulator; the scale is never folded into the decoded
+// weight. A k split writes partial sums that already hold the group scales.
 #include <stdio.h>
 
 #include <type_traits>
