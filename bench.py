@@ -1,64 +1,56 @@
 """Benchmark of the FP8 (e4m3) weight-only linear layer on one MI355X.
 
-One step = one pass of the per-call hot path over the decode GEMV workload:
-three fp8w_linear calls at M = 1 (bf16 activations) on the weight shapes
-[4096, 4096], [14336, 4096] and [4096, 14336]; each weight was quantized once
-at build time (that quantize is timed separately). Inputs are resident in HBM
-when the timed region starts, and every step reads a different copy of the
-weight codes and scales (rotating through >= 1 GiB) so the 256 MB Infinity
-Cache cannot serve repeats: the kernels stream from HBM.
+One step = one pass of the per-call hot path for M = 1..32 over the weight
+shapes the metric names:
+  * the decode GEMV workload, M = 1: three fp8w_linear calls with bf16
+    activations and a zero bf16 bias on the weights [4096, 4096],
+    [14336, 4096] and [4096, 14336] (N(0, 0.02^2) fp32, quantized once per
+    output channel); these run the M = 1 GEMV (gemv_kernel);
+  * the skinny sweep, M = 2, 4, 8, 16, 22, 32: six fp8w_linear calls with
+    fp16 activations and an N(0, 0.01^2) fp16 bias on [14336, 4096]
+    (0.02 * Student-t(3) weights); these run the matrix-core skinny GEMM
+    (pipe_kernel).
+Every weight was quantized once at build time (not timed here). Inputs are
+resident in HBM when the timed region starts, and every call reads a different
+copy of its weight codes and scales (each layer's copies rotate through
+>= 1 GiB), so the 256 MB Infinity Cache cannot serve repeats: the kernels
+stream from HBM.
 
-The timed region launches the calls eagerly through the C ABI (ctypes) on
-torch's current stream; host enqueue is faster than the kernels, so the GPU
-stays busy. The same steps replayed from a HIP graph are reported in "graph".
-The graph holds one pass over the rotated weight copies (one step per copy):
-on this ROCm each graph launch costs about 4.5 us, so a graph of a single step
-ran that much slower than eager launches, while a graph of eight steps runs
-within 1 % of them.
+The timed region launches the K steps eagerly through the C ABI (ctypes) on
+torch's current stream: first the K steps' M = 1 calls, then their M >= 2
+calls, with one HIP event at the start, one between the two phases and one at
+the end (synchronizes on both sides). The work is the K steps' work; the
+phase order only lets each kernel family's mean launch time be read from the
+events without a marker per step. If K steps take less than --min-ms, the
+region is timed again with enough steps to last that long; "steps" is the
+number of steps actually timed ("steps_requested" is K).
 
-value = algorithmic bytes of the timed steps / the timed region's duration
-(HIP events on the launch stream, around exactly --steps steps, with
-synchronizes on both sides). Algorithmic bytes per call = N*K (codes) + 4N
-(scales) + 2N (bias) + 2MK (x) + 2MN (y).
+value = algorithmic bytes of the timed steps / the timed region's duration, in
+GB/s. Algorithmic bytes per call = N*K (codes) + 4N (scales) + 2N (bias) +
+2MK (x) + 2MN (y).
 
-roofline: the dominant kernel is the M = 1 GEMV (it is every launch of the
-step): achieved = algorithmic bytes per launch / average launch duration, the
-duration being the timed region divided by its launches. Per-shape microseconds
-per call come from bursts of back-to-back launches of one shape between two
-events (the GPU overlaps consecutive dispatches, so a burst's average matches
-the profiler's kernel durations).
+roofline: for the kernel family that takes most of the step's time, achieved =
+its algorithmic bytes per launch / its mean launch duration (its phase of the
+timed region divided by its launches), against 8 TB/s; "kernels" gives the
+same for both families. traffic = HBM bytes per launch from the committed
+rocprofv3 --pmc summary (profiles/step_traffic.json), reported only while the
+family's sources hash to the value recorded there.
 
-Every timed region (the steps and each burst) is preceded by --spin-ms of the
-same work: the GPU raises its clocks only under sustained load, and the first
-~10 ms run up to 15 % slower than the steady state measured here.
+Every timed region is preceded by --spin-ms of the same work: the GPU raises
+its clocks only under sustained load, and the first ~10 ms run up to 15 %
+slower than the steady state measured here.
 
-Per-call lines give the burst mean and p10 / median / p90 over ten groups of
-the burst, warm (one cache-resident copy) numbers, and the host wall time of a
-single call ("host_latency": the ctypes enqueue, and enqueue plus a stream
-synchronize). Skinny lines also give the matrix-core work: padded M, issued and
-useful FLOPs as a share of the 2.5 PFLOP/s dense bf16/fp16 peak.
+stdout: ONE compact JSON line (the headline: the metric, the timed region, the
+roofline, per-call microseconds from back-to-back bursts of each call, the
+streaming-read reference, and the CPU oracle baseline). Progress goes to
+stderr, and the full record (per-call percentiles, warm numbers, host latency,
+the oracle timed on every workload and, with --extra, the other workloads) is
+written to --full-json (default gpurun_out/bench_full.json).
 
-Also reported ("extra"): latency-bound calls (the 1024 x 1024 GEMV and the
-x [22,1024] x [1024,4096] shape the pages time), the skinny sweep (M = 2..32,
-fp16), one decoder block at M = 16 (seven calls, and four with q/k/v and
-gate/up merged; eager and graph-replayed steps), the large shapes and their
-K = 8200 fallback, each with the same cache rotation; batched decode
-("batch": the decode weights at M = 64 / 128 / 256, the weight-only batch GEMM,
-against HBM and against the 2.5 PFLOP/s bf16 matrix-core peak); the W8A8 layer at
-prefill batches ("w8a8": M = 512 / 2048 / 4096 on the block's three distinct
-shapes, in TFLOP/s against the 5.0 PFLOP/s dense e4m3 matrix-core peak; the
-whole layer, its GEMM and its activation quantizer); the build-time quantize;
-a plain streaming-read reference ("read_ceiling": the library's
-fp8w_stream_read_probe over buffers of each decode weight's size, rotated the
-same way); and the CPU oracle ("cpu_baseline", all host threads and one),
-whose leg also checks this run's GPU results against the oracle results it
-produced.
-
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--spin-ms MS] [--quick]
-                       [--only tiny|skinny|block|large|batch|grouped|w8a8 ...] [--reps R]
-Profile helpers: --trace-summary CSV [--last N], --mfma-summary CSV N K,
---pmc-summary FETCH_CSV WRITE_CSV.
-Prints ONE JSON line on stdout; progress goes to stderr.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--min-ms MS] [--spin-ms MS]
+                       [--extra] [--only tiny|skinny|block|large|batch|grouped|w8a8 ...] [--reps R]
+Profiler helpers: --only-timed (the timed region alone), --trace-summary CSV [--last N],
+--mfma-summary CSV N K, --pmc-summary FETCH_CSV WRITE_CSV.
 """
 import argparse
 import hashlib
@@ -79,10 +71,18 @@ import fp8_weight_only_amd as fw  # noqa: E402
 import workloads  # noqa: E402
 
 METRIC = "fp8-weight linear achieved HBM GB/s (% of peak) + µs/call, M=1..32, K,N=4096..8192"
+DTYPE = "bf16/fp16 x e4m3 -> f32 acc"
 PEAK_HBM_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30
 SPIN_MS = 200.0  # sustained load before every timed region (clock ramp-up); --spin-ms
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode_traffic.json")
+MIN_TIMED_MS = 50.0  # shortest timed region; --min-ms
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_traffic.json")
+FULL_RECORD = os.path.join(ROOT, "gpurun_out", "bench_full.json")
+
+# the kernel families of the step and the sources that define each (kernel code
+# and tile choice): a change to any of them voids that family's recorded traffic
+FAMILIES = {"gemv_kernel": ("common.hpp", "gemv.hip"),
+            "pipe_kernel": ("common.hpp", "ring.hpp", "skinny.hip")}
 
 
 def log(*a):
@@ -93,15 +93,10 @@ def alg_bytes(m, n, k, bias=True):
     return n * k + 4 * n + (2 * n if bias else 0) + 2 * m * k + 2 * m * n
 
 
-# the sources that define the dominant kernel (the decode GEMV: its code and its
-# tile choice); a change to either voids the recorded traffic counters
-GEMV_SOURCES = ("common.hpp", "gemv.hip")
-
-
-def kernel_source_hash():
+def kernel_source_hash(family):
     h = hashlib.sha256()
     d = os.path.join(ROOT, "fp8_weight_only_amd", "csrc")
-    for f in GEMV_SOURCES:
+    for f in FAMILIES[family]:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -437,6 +432,61 @@ def timed_steps(calls, steps, warmup, copies, use_graph, dev):
     return e0.elapsed_time(e1)
 
 
+class Step:
+    """The timed workload: the three M = 1 decode calls and the six skinny-sweep
+    calls (M = 2..32) of one step, each layer with enough weight copies that a
+    copy is read again only after >= 1 GiB of other weights."""
+
+    def __init__(self, dev):
+        self.dec_lws = [workloads.decode_layer(i) for i in range(len(workloads.DECODE_SHAPES))]
+        dec_bytes = sum(lw.w.shape[0] * lw.w.shape[1] for lw in self.dec_lws)
+        self.dec_copies = max(1, math.ceil(ROTATE_BYTES / dec_bytes))
+        self.dec_layers = [Layer(lw, self.dec_copies, dev) for lw in self.dec_lws]
+        self.dec_xs = [workloads.decode_x(i) for i in range(len(self.dec_lws))]
+        self.dec_calls = [Call(L, x.to(dev), dev) for L, x in zip(self.dec_layers, self.dec_xs)]
+        self.sk_lw = workloads.skinny_layer()
+        n, k = self.sk_lw.w.shape
+        self.sk_copies = max(1, math.ceil(ROTATE_BYTES / (n * k)))
+        self.sk_layer = Layer(self.sk_lw, self.sk_copies, dev)
+        self.sk_xs = [workloads.skinny_x(m) for m in workloads.SKINNY_MS]
+        self.sk_calls = [Call(self.sk_layer, x.to(dev), dev) for x in self.sk_xs]
+        self.calls = self.dec_calls + self.sk_calls
+        self.dec_step_bytes = sum(c.bytes for c in self.dec_calls)
+        self.sk_step_bytes = sum(c.bytes for c in self.sk_calls)
+        self.step_bytes = self.dec_step_bytes + self.sk_step_bytes
+
+    def gemv_phase(self, i0, count, stream):
+        for i in range(i0, i0 + count):
+            for c in self.dec_calls:
+                c.launch(i, stream)
+
+    def skinny_phase(self, i0, count, stream):
+        per = len(self.sk_calls)
+        for i in range(i0, i0 + count):
+            for j, c in enumerate(self.sk_calls):
+                c.launch(i * per + j, stream)
+
+
+def timed_region(step, steps, warmup, dev, spin=True):
+    """(ms of the M = 1 phase, ms of the M >= 2 phase) of exactly `steps` steps:
+    events on the launch stream at the start, between the phases and at the end,
+    synchronizes on both sides."""
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if spin:
+        spin_up(lambda i: (step.gemv_phase(i, 1, stream), step.skinny_phase(i, 1, stream)), SPIN_MS)
+    step.gemv_phase(0, warmup, stream)
+    step.skinny_phase(0, warmup, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    step.gemv_phase(0, steps, stream)
+    ev[1].record()
+    step.skinny_phase(0, steps, stream)
+    ev[2].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+
+
 def read_ceiling(dev, sizes, reps=100):
     """The library's plain streaming-read kernel over the same byte counts,
     rotating through 1 GiB: the reference the GEMV's bandwidth is read against."""
@@ -479,25 +529,29 @@ def cpu_info():
     return os.cpu_count(), model
 
 
-def cpu_baseline(layers, lws, xs_cpu, calls, budget_s, with_configs=True):
+def cpu_baseline(step, budget_s):
     """The oracle (fp64 C, OpenMP over output channels) on the host cores, on the
-    same three decode calls, repeated until ~budget_s of CPU work; then once more
-    on one core. The oracle's results of this leg are also compared with the
-    GPU's: codes and scales bit for bit, and the GPU outputs of the same calls
-    against the output gate."""
+    same nine calls of one step, repeated until ~budget_s of CPU work; then the
+    three M = 1 calls on one core. The oracle's results of this leg are also
+    compared with the GPU's: codes and scales bit for bit, and the GPU outputs
+    of the same calls against the output gate."""
     import oracle
+    quant = {}
+    for lw in step.dec_lws + [step.sk_lw]:
+        q, s, st = oracle.quantize_rows(lw.w)
+        quant[lw.name] = (q, s, oracle.row_amax(lw.w), st)
     prepared = []
-    for lw, x in zip(lws, xs_cpu):
-        q, s, _ = oracle.quantize_rows(lw.w)
-        prepared.append((x.double().numpy(), q, s, None if lw.bias is None else lw.bias.double().numpy(),
-                         oracle.row_amax(lw.w)))
+    for c, lw, x in zip(step.calls, step.dec_lws + [step.sk_lw] * len(step.sk_calls), step.dec_xs + step.sk_xs):
+        q, s, amax, _ = quant[lw.name]
+        prepared.append((c, lw, x.double().numpy(), q, s, None if lw.bias is None else lw.bias.double().numpy(),
+                         amax))
 
-    def run(budget):
+    def run(items, budget):
         reps, byts, outs = 0, 0, []
         t0 = time.perf_counter()
         while True:
             outs = []
-            for (x64, q, s, b, _) in prepared:
+            for (_, _, x64, q, s, b, _) in items:
                 outs.append(oracle.linear_f64(x64, q, s, b))
                 byts += alg_bytes(x64.shape[0], q.shape[0], q.shape[1], b is not None)
             reps += 1
@@ -506,18 +560,21 @@ def cpu_baseline(layers, lws, xs_cpu, calls, budget_s, with_configs=True):
                 return reps, byts, el, outs
 
     threads = oracle.num_threads()
-    reps, byts, el, outs = run(budget_s)
+    reps, byts, el, outs = run(prepared, budget_s)
     oracle.set_num_threads(1)
     try:
-        reps1, byts1, el1, _ = run(min(budget_s, 3.0))
+        reps1, byts1, el1, _ = run(prepared[:len(step.dec_calls)], min(budget_s, 3.0))
     finally:
         oracle.set_num_threads(threads)
 
     # parity of this run's GPU results against the oracle's
     ok = True
-    for L, c, (x64, q, s, b, amax), y_ref in zip(layers, calls, prepared, outs):
+    for L in step.dec_layers + [step.sk_layer]:
+        q, s, _, st = quant[L.name]
+        ok &= st == 0
         ok &= bool(np.array_equal(L.qs[0][0].cpu().numpy(), q))
         ok &= bool(np.array_equal(L.qs[0][1].cpu().numpy().view(np.uint32), s.view(np.uint32)))
+    for (c, _, x64, _, _, _, amax), y_ref in zip(prepared, outs):
         c.y.fill_(float("nan"))
         c.launch(0, torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
@@ -525,16 +582,13 @@ def cpu_baseline(layers, lws, xs_cpu, calls, budget_s, with_configs=True):
         tol = 1e-2 * np.abs(y_ref) + 1e-3 * np.linalg.norm(x64, axis=1)[:, None] * amax[None, :]
         ok &= bool(np.all(np.isfinite(yv)) and np.all(np.abs(yv - y_ref) <= tol))
 
-    per_config = oracle_per_config() if with_configs else None
     nproc, model = cpu_info()
     return {"value": round(byts / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} passes over the 3 decode GEMV calls (M=1; 4096x4096, 14336x4096, 4096x14336) "
-                      f"through the fp64 oracle, {el:.1f} s",
+            "sample": f"{reps} passes over one step's 9 calls (3 decode GEMVs at M=1, the skinny sweep at "
+                      f"M=2..32) through the fp64 oracle, {el:.1f} s",
             "one_core": {"value": round(byts1 / el1 / 1e9, 3), "unit": "GB/s", "cores": 1,
-                         "sample": f"{reps1} passes, {el1:.1f} s"},
-            "gpu_parity_vs_this_oracle_run": ok,
-            "per_workload": per_config,
-            "host_cpus": nproc, "host_model": model}
+                         "sample": f"{reps1} passes over the 3 decode calls, {el1:.1f} s"},
+            "gpu_parity_vs_this_oracle_run": ok, "host_cpus": nproc, "host_model": model}
 
 
 def oracle_per_config():
@@ -595,36 +649,87 @@ def oracle_per_config():
     return {"threads": threads, "configs": out}
 
 
-def traffic_entry():
-    """HBM traffic per GEMV launch from the committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel sources; else None."""
+def traffic_entry(family):
+    """HBM bytes per launch of one kernel family of the step, from the committed
+    rocprofv3 --pmc summary, if it was taken on the family's current sources;
+    else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    fam = t.get("families", {}).get(family)
+    if not fam or fam.get("kernel_source_hash") != kernel_source_hash(family):
         return None
-    return t.get("bytes_per_launch")
+    return fam.get("bytes_per_launch")
+
+
+def family_row(name, launches_per_step, steps, phase_ms, alg_per_step):
+    """Roofline figures of one kernel family from its phase of the timed region."""
+    mean_us = phase_ms * 1e3 / (steps * launches_per_step)
+    alg = alg_per_step / launches_per_step
+    achieved = alg / (mean_us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_entry(name), "kernel": name,
+            "mean_launch_us": round(mean_us, 3), "alg_bytes_per_launch": round(alg, 1),
+            "launches": steps * launches_per_step}
+
+
+def headline(steps, steps_requested, warmup, gemv_ms, skinny_ms, step, per_call, ceiling, cpu, full_path):
+    """The compact result line (a few KB): everything the metric needs, nothing
+    that grows with the number of sections."""
+    ms = gemv_ms + skinny_ms
+    value = step["bytes"] * steps / (ms * 1e-3) / 1e9
+    fams = [family_row("gemv_kernel", step["gemv_launches"], steps, gemv_ms, step["gemv_bytes"]),
+            family_row("pipe_kernel", step["skinny_launches"], steps, skinny_ms, step["skinny_bytes"])]
+    dom = max(fams, key=lambda f: f["mean_launch_us"] * f["launches"])
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "steps_requested": steps_requested, "warmup": warmup, "ms_per_step": round(ms / steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
+        "pct_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "config": {"workload": "one step = the decode GEMV at M=1 (bf16 x, zero bias; e4m3 weights [4096,4096], "
+                               "[14336,4096], [4096,14336]) + the skinny sweep at M=2,4,8,16,22,32 (fp16 x, fp16 "
+                               "bias; e4m3 weight [14336,4096], Student-t(3) rows); per-channel scales; weight copies "
+                               "rotated through >= 1 GiB per layer",
+                   "m": [1] + list(workloads.SKINNY_MS), "bytes_per_step": step["bytes"],
+                   "calls_per_step": step["gemv_launches"] + step["skinny_launches"],
+                   "launch": "eager, C ABI on torch's current stream"},
+        "roofline": dom,
+        "kernels": [{k: f[k] for k in ("kernel", "mean_launch_us", "achieved", "frac", "traffic", "launches")}
+                    for f in fams],
+        "per_call": per_call,
+        "read_ceiling": ceiling,
+        "cpu_baseline": cpu,
+        "full_record": os.path.relpath(full_path, ROOT) if full_path else None,
+    }
+
+
+def compact_call(r):
+    return {"n": r["n"], "k": r["k"], "m": r["m"], "kernel": r["kernel"], "us": r["us_per_call"],
+            "pct_peak": r["pct_peak"]}
 
 
 def main():
     global SPIN_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--min-ms", type=float, default=MIN_TIMED_MS,
+                    help="shortest timed region: fewer steps than this lasts are replaced by enough steps")
     ap.add_argument("--spin-ms", type=float, default=SPIN_MS,
                     help="milliseconds of the same work run before each timed region (GPU clock ramp-up)")
-    ap.add_argument("--quick", action="store_true", help="decode workload only (no extra sections)")
+    ap.add_argument("--extra", action="store_true", help="also time the other workloads (full record only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-oracle-workloads", action="store_true",
-                    help="skip timing the oracle on every workload (part of the cpu_baseline leg)")
+                    help="skip timing the oracle on every workload (full record only)")
+    ap.add_argument("--full-json", default=FULL_RECORD, help="where the full record is written ('' for nowhere)")
     ap.add_argument("--only-timed", action="store_true",
-                    help="run only the timed region (for profiler runs: every GEMV launch is then a timed one)")
+                    help="run only the timed region (for profiler runs: the last 9*steps library launches are it)")
     ap.add_argument("--only", choices=SECTIONS, nargs="+",
-                    help="run only these extra sections (no decode workload) and print their JSON")
+                    help="run only these extra sections (no step) and print their JSON")
     ap.add_argument("--reps", type=int, default=100, help="launches per burst in the extra sections")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="print a markdown table of the library's kernels in a rocprofv3 kernel trace, then exit")
@@ -633,7 +738,7 @@ def main():
     ap.add_argument("--mfma-summary", nargs=3, metavar=("PMC_CSV", "N", "K"),
                     help="print a markdown table of the skinny kernels' matrix-core counters, then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/gemv_decode_traffic.json from two rocprofv3 --pmc runs, then exit")
+                    help="write profiles/step_traffic.json from two rocprofv3 --pmc runs of --only-timed, then exit")
     args = ap.parse_args()
     SPIN_MS = args.spin_ms
     if args.pmc_summary:
@@ -649,6 +754,9 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (each GPU would hold its own "
               "shard of the weight; the per-GPU kernel is what is measured here)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -666,89 +774,65 @@ def main():
         print(json.dumps(out), flush=True)
         return
 
-    # ---------------------------------------------------------------- decode workload (the metric)
-    per_step = sum(alg_bytes(1, n, k) for n, k in workloads.DECODE_SHAPES)
-    copies = max(1, math.ceil(ROTATE_BYTES / per_step))
-    log(f"decode workload: {per_step / 1e6:.2f} MB per step, {copies} rotated weight copies")
-    lws = [workloads.decode_layer(i) for i in range(3)]
-    layers = [Layer(lw, copies, dev) for lw in lws]
-    xs_cpu = [workloads.decode_x(i) for i in range(3)]
-    xs = [x.to(dev) for x in xs_cpu]
-    calls = [Call(L, x, dev) for L, x in zip(layers, xs)]
-    quant = [{"layer": L.name, "ms": round(L.quantize_ms, 4),
-              "gbps": round(5.0 * L.n * L.k / (L.quantize_ms * 1e-3) / 1e9, 1)} for L in layers]
+    # ---------------------------------------------------------------- the step (the metric)
+    step = Step(dev)
+    log(f"step: {step.step_bytes / 1e6:.2f} MB ({len(step.calls)} calls); rotated copies: decode "
+        f"{step.dec_copies}, skinny {step.sk_copies}")
+    shape = {"bytes": step.step_bytes, "gemv_launches": len(step.dec_calls),
+             "skinny_launches": len(step.sk_calls), "gemv_bytes": step.dec_step_bytes,
+             "skinny_bytes": step.sk_step_bytes}
 
     if args.only_timed:
-        ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
-        launches = args.steps * len(calls)
+        g_ms, s_ms = timed_region(step, args.steps, args.warmup, dev)
         calibration_copy(dev)
-        print(json.dumps({"steps": args.steps, "ms": ms, "us_per_step": ms * 1e3 / args.steps,
-                          "mean_launch_us": ms * 1e3 / launches,
-                          "gbps": per_step * args.steps / (ms * 1e-3) / 1e9}), flush=True)
+        line = headline(args.steps, args.steps, args.warmup, g_ms, s_ms, shape, None, None, None, None)
+        print(json.dumps({k: line[k] for k in ("value", "steps", "ms_per_step", "roofline", "kernels")}),
+              flush=True)
         return
 
-    per_call = []
-    for c in calls:
-        us = burst(c, 200, 20, stream)
-        per_call.append(call_report(c, us))
-        r = per_call[-1]
-        log(f"  {r['layer']}: {r['us_per_call']:.2f} us/call  {r['gbps']:.0f} GB/s ({r['pct_peak']:.1f}% of 8 TB/s)")
-    warm = [call_report(c, burst(c, 200, 20, stream, warm=True)) for c in calls]
-    host = [dict(layer=c.layer.name, **host_latency(c, stream)) for c in calls]
-    ceiling = read_ceiling(dev, [c.layer.n * c.layer.k for c in calls])
+    per_call, full_calls = [], []
+    for c in step.calls:
+        r = call_report(c, burst(c, 200, 20, stream))
+        full_calls.append(r)
+        per_call.append(compact_call(r))
+        log(f"  {r['layer']} m={r['m']}: {r['us_per_call']:.2f} us/call  {r['gbps']:.0f} GB/s "
+            f"({r['pct_peak']:.1f}% of 8 TB/s) [{r['kernel']}]")
+    ceiling = read_ceiling(dev, sorted({c.layer.n * c.layer.k for c in step.calls}))
 
-    ms = timed_steps(calls, args.steps, args.warmup, copies, False, dev)
-    graph_steps = copies * -(-max(200, args.steps // 10) // copies)
-    try:
-        graph_ms = timed_steps(calls, graph_steps, 20, copies, True, dev)
-    except Exception as e:  # noqa: BLE001
-        log(f"graph capture failed: {e}")
-        graph_ms = None
-    value = per_step * args.steps / (ms * 1e-3) / 1e9
-    ms_per_step = ms / args.steps
-    launches = args.steps * len(calls)
-    mean_launch_us = ms * 1e3 / launches
-    achieved = (per_step / len(calls)) / (mean_launch_us * 1e-6) / 1e9
-    log(f"timed region (eager): {ms_per_step * 1e3:.2f} us/step, {value:.0f} GB/s"
-        + (f"; graph replay {graph_ms * 1e3 / graph_steps:.2f} us/step" if graph_ms else ""))
+    steps = args.steps
+    g_ms, s_ms = timed_region(step, steps, args.warmup, dev)
+    if g_ms + s_ms < args.min_ms:
+        steps = max(steps, math.ceil(args.min_ms / ((g_ms + s_ms) / steps)))
+        log(f"  {args.steps} steps took {g_ms + s_ms:.2f} ms; timing {steps} steps")
+        g_ms, s_ms = timed_region(step, steps, args.warmup, dev, spin=False)
+    log(f"timed region: {steps} steps, {(g_ms + s_ms) * 1e3 / steps:.2f} us/step "
+        f"(M=1 phase {g_ms * 1e3 / steps:.2f}, M=2..32 phase {s_ms * 1e3 / steps:.2f})")
 
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "decode GEMV, M=1: three fp8w_linear calls per step on e4m3 weights [4096,4096], "
-                               "[14336,4096], [4096,14336] (N(0,0.02^2) fp32 -> per-channel scales), x bf16 N(0,1), "
-                               "zero bf16 bias; weight copies rotated through >= 1 GiB",
-                   "m": 1, "shapes_nk": workloads.DECODE_SHAPES, "act_dtype": "bf16", "weight_dtype": "e4m3fn",
-                   "accumulate": "f32", "rotated_copies": copies, "bytes_per_step": per_step,
-                   "launch": "eager, C ABI on torch's current stream"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_entry(),
-                     "kernel": "gemv_kernel (M=1 GEMV, every launch of the step)",
-                     "alg_bytes_per_launch": per_step / len(calls), "mean_launch_us": round(mean_launch_us, 3)},
-        "per_call": per_call,
-        "warm_per_call": warm,
-        "host_latency": host,
-        "graph": None if graph_ms is None else {
-            "steps": graph_steps, "us_per_step": round(graph_ms * 1e3 / graph_steps, 3),
-            "gbps": round(per_step * graph_steps / (graph_ms * 1e-3) / 1e9, 1)},
-        "quantize": quant,
-        "read_ceiling": ceiling,
-    }
+    full = {"per_call": full_calls,
+            "warm_per_call": [call_report(c, burst(c, 200, 20, stream, warm=True)) for c in step.calls],
+            "host_latency": [dict(layer=c.layer.name, m=c.m, **host_latency(c, stream)) for c in step.calls],
+            "read_ceiling": ceiling}
+    if args.extra:
+        full["extra"] = extra_sections(dev, stream, args.reps)
 
-    if not args.quick:
-        out["extra"] = extra_sections(dev, stream, args.reps)
-
-    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(layers, lws, xs_cpu, calls,
-                                                                          args.cpu_budget,
-                                                                          not args.no_oracle_workloads)
+    cpu = None
     if not args.no_cpu_baseline:
-        cb = out["cpu_baseline"]
-        log(f"cpu baseline: {cb['value']} GB/s on {cb['cores']} threads, {cb['one_core']['value']} GB/s on one; "
-            f"GPU results vs this oracle run: {'pass' if cb['gpu_parity_vs_this_oracle_run'] else 'FAIL'}")
+        cpu = cpu_baseline(step, args.cpu_budget)
+        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} threads, {cpu['one_core']['value']} GB/s on one; "
+            f"GPU results vs this oracle run: {'pass' if cpu['gpu_parity_vs_this_oracle_run'] else 'FAIL'}")
+        if not args.no_oracle_workloads:
+            full["oracle_per_workload"] = oracle_per_config()
 
     calibration_copy(dev)
-    print(json.dumps(out), flush=True)
+    line = headline(steps, args.steps, args.warmup, g_ms, s_ms, shape, per_call,
+                    [{"bytes": c["bytes"], "us": c["us"], "pct_peak": c["pct_peak"]} for c in ceiling], cpu,
+                    args.full_json or None)
+    full["headline"] = line
+    if args.full_json:
+        os.makedirs(os.path.dirname(os.path.abspath(args.full_json)), exist_ok=True)
+        with open(args.full_json, "w") as f:
+            json.dump(full, f, indent=1)
+    print(json.dumps(line), flush=True)
 
 
 COPY_BYTES = 256 << 20
@@ -771,27 +855,37 @@ def _pmc_rows(path, counter):
 
 def pmc_summary(fetch_csv, write_csv, out_path):
     """Turn two rocprofv3 --pmc runs of `bench.py --only-timed` (FETCH_SIZE, then
-    WRITE_SIZE, KiB per dispatch) into HBM bytes per GEMV launch, each counter
-    scaled by what it reads for the 256 MiB calibration copy."""
+    WRITE_SIZE, KiB per dispatch) into HBM bytes per launch of each kernel
+    family of the step, each counter scaled by what it reads for the 256 MiB
+    calibration copy at the end of the run."""
     res = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _pmc_rows(path, name)
-        gemv = [float(r["Counter_Value"]) for r in rows if "gemv_kernel" in r["Kernel_Name"]]
         # the calibration copy is the run's last and largest device copy (a blit
         # kernel or an elementwise copy, depending on how torch lowers it)
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"] or "direct_copy" in r["Kernel_Name"]]
         copy = float(max(copies, key=lambda r: int(r["Dispatch_Id"]))["Counter_Value"]) if copies else None
         factor = (COPY_BYTES / 1024.0) / copy if copy else None
-        res[name] = {"gemv_kib_mean": sum(gemv) / len(gemv), "gemv_dispatches": len(gemv),
-                     "copy_kib": copy, "scale": factor}
-    fetch = res["FETCH_SIZE"]["gemv_kib_mean"] * 1024 * res["FETCH_SIZE"]["scale"]
-    write = res["WRITE_SIZE"]["gemv_kib_mean"] * 1024 * res["WRITE_SIZE"]["scale"]
-    per_step = sum(alg_bytes(1, n, k) for n, k in workloads.DECODE_SHAPES)
-    out = {"kernel": "gemv_kernel (decode GEMV launches of bench.py --only-timed)",
-           "kernel_source_hash": kernel_source_hash(), "counters": res,
-           "bytes_per_launch": round(fetch + write, 1), "fetch_bytes_per_launch": round(fetch, 1),
-           "write_bytes_per_launch": round(write, 1),
-           "alg_bytes_per_launch": per_step / len(workloads.DECODE_SHAPES)}
+        res[name] = {"copy_kib": copy, "scale": factor, "families": {}}
+        for fam in FAMILIES:
+            vals = [float(r["Counter_Value"]) for r in rows if fam in r["Kernel_Name"] and "fp8w::" in r["Kernel_Name"]]
+            res[name]["families"][fam] = {"kib_mean": sum(vals) / len(vals) if vals else None,
+                                          "dispatches": len(vals)}
+    shapes = {"gemv_kernel": [(1, n, k, True) for n, k in workloads.DECODE_SHAPES],
+              "pipe_kernel": [(m, 14336, 4096, True) for m in workloads.SKINNY_MS]}
+    out = {"kernels": "the step's two kernel families, all their launches in a run of bench.py --only-timed",
+           "counters": res, "families": {}}
+    for fam in FAMILIES:
+        f = res["FETCH_SIZE"]["families"][fam]["kib_mean"]
+        w = res["WRITE_SIZE"]["families"][fam]["kib_mean"]
+        if f is None or w is None:
+            continue
+        fetch = f * 1024 * res["FETCH_SIZE"]["scale"]
+        write = w * 1024 * res["WRITE_SIZE"]["scale"]
+        alg = sum(alg_bytes(*s) for s in shapes[fam]) / len(shapes[fam])
+        out["families"][fam] = {"kernel_source_hash": kernel_source_hash(fam), "bytes_per_launch": round(fetch + write, 1),
+                                "fetch_bytes_per_launch": round(fetch, 1), "write_bytes_per_launch": round(write, 1),
+                                "alg_bytes_per_launch": alg, "traffic_over_alg": round((fetch + write) / alg, 4)}
     with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))

@@ -29,7 +29,8 @@ import torch
 
 __all__ = [
     "Fp8wError", "lib_path", "load", "fp8w_quantize", "fp8w_linear", "fp8w_linear_with_path",
-    "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes", "fp8w_linear_kernel",
+    "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes", "fp8w_linear_with_path_workspace_bytes",
+    "fp8w_linear_kernel",
     "fp8w_stream_read_probe", "fp8w_quantize_grouped", "fp8w_linear_grouped", "fp8w_linear_grouped_with_path",
     "fp8w_linear_grouped_path", "fp8w_linear_grouped_kernel", "fp8w_dequantize_grouped",
     "fp8w_linear_grouped_with_workspace", "fp8w_linear_grouped_workspace_bytes", "grouped_workspace_bytes",
@@ -61,6 +62,7 @@ EXPORTS = {
     "fp8w_dequantize_fallback": (_I, [_P, _P, _I64, _I64, _P, _I, _P]),
     "fp8w_linear_path": (_I, [_I64, _I64, _I64, _I, _P, _P, _P]),
     "fp8w_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _P, _P, _P]),
+    "fp8w_linear_with_path_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_linear_kernel": (ctypes.c_char_p, [_I, _I64, _I64, _I64, _I, _P, _P]),
     "fp8w_stream_read_probe": (_I, [_P, _SZ, _P, _P]),
     "fp8w_quantize_grouped": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P]),
@@ -138,6 +140,10 @@ def fp8w_linear_path(m, n, k, act_dtype, x, q, y) -> int:
 
 def fp8w_linear_workspace_bytes(m, n, k, act_dtype, x, q, y) -> int:
     return load().fp8w_linear_workspace_bytes(m, n, k, act_dtype, x, q, y)
+
+
+def fp8w_linear_with_path_workspace_bytes(path, m, n, k, act_dtype, x, q) -> int:
+    return load().fp8w_linear_with_path_workspace_bytes(path, m, n, k, act_dtype, x, q)
 
 
 def fp8w_linear_kernel(path, m, n, k, act_dtype, x, q):
@@ -303,14 +309,7 @@ def linear(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Te
     sp = _dev(scale, "scale") if n else 0
     bp = _dev(bias, "bias") if bias is not None and n else 0
     yp = _dev(out, "out") if out.numel() else 0
-    auto = fp8w_linear_path(m, n, k, act, xp, qp, yp)
-    eff = auto if path == PATH_AUTO else path
-    if eff == PATH_FALLBACK:
-        need = n * k * 2
-    elif eff in (PATH_SKINNY, PATH_BATCH) and eff == auto:
-        need = fp8w_linear_workspace_bytes(m, n, k, act, xp, qp, yp)
-    else:
-        need = 0
+    need = fp8w_linear_with_path_workspace_bytes(path, m, n, k, act, xp, qp)
     if need and workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
     wp = _dev(workspace, "workspace") if workspace is not None and workspace.numel() else 0

@@ -574,6 +574,23 @@ size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t
     return fallback_workspace(n, k, act_dtype);
 }
 
+size_t fp8w_linear_with_path_workspace_bytes(int path, int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype,
+                                             const void* x, const uint8_t* q)
+{
+    if (!valid_act(act_dtype) || !sizes_ok(m, n, k))
+        return 0;
+    const int autop = auto_path(m, k, x, q);
+    if (path == FP8W_PATH_AUTO)
+        path = autop;
+    if (path == FP8W_PATH_FALLBACK)
+        return fallback_workspace(n, k, act_dtype);
+    if (path == FP8W_PATH_SKINNY && autop == FP8W_PATH_SKINNY)
+        return fp8w::skinny_workspace_bytes(m, n, k);
+    if (path == FP8W_PATH_BATCH && autop == FP8W_PATH_BATCH)
+        return fp8w::batch_workspace_bytes(m, n, k);
+    return 0;
+}
+
 const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x,
                                const uint8_t* q)
 {

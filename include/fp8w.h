@@ -161,6 +161,17 @@ FP8W_API int fp8w_linear_path(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_
 FP8W_API size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t act_dtype, const void* x,
                                    const uint8_t* q, const void* y);
 
+/* Workspace bytes fp8w_linear_with_path uses for `path` (FP8W_PATH_AUTO or a
+   forced path) on these sizes and pointers, the amount fp8w_linear_kernel's
+   report assumes: FP8W_PATH_AUTO as fp8w_linear_workspace_bytes;
+   FP8W_PATH_FALLBACK n * k * element_size(act_dtype); FP8W_PATH_SKINNY and
+   FP8W_PATH_BATCH their k-split partial sums (splits * m * n * 4) only when that
+   path is also the one FP8W_PATH_AUTO takes, else 0 (a forced path runs its
+   single-pass plan); FP8W_PATH_GEMV 0. 0 when the arguments or the path are
+   invalid. */
+FP8W_API size_t fp8w_linear_with_path_workspace_bytes(int path, int64_t m, int64_t n, int64_t k,
+                                                      fp8w_dtype_t act_dtype, const void* x, const uint8_t* q);
+
 /*
  * Name of the kernel (and its tile parameters) that `path` (FP8W_PATH_AUTO or
  * a forced path) launches for these sizes and pointers, e.g.

@@ -230,8 +230,10 @@ def round_to_bf16(y) -> np.ndarray:
 
 
 def round_to_f16(y) -> np.ndarray:
-    """y -> fl32 -> fp16 (numpy's round-to-nearest-even cast), as float64."""
-    return round_to_f32(y).astype(np.float16).astype(np.float64)
+    """y -> fl32 -> fp16 (numpy's round-to-nearest-even cast), as float64; values
+    at or past the overflow midpoint become +-inf."""
+    with np.errstate(over="ignore"):
+        return round_to_f32(y).astype(np.float16).astype(np.float64)
 
 
 # ----------------------------------------------------------------- metrics

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fw.load()
     names = declared_symbols()
-    assert len(names) == 25
+    assert len(names) == 26
     for name in names:
         assert hasattr(lib, name), name
         assert name in fw.EXPORTS, name
@@ -138,6 +138,26 @@ def test_workspace_bytes():
     assert wb(32, 4096, 14336, fw.BF16, X, Q, Y) == 4 * 32 * 4096 * 4    # split k in four
     assert wb(16, 4096, 14336, fw.BF16, X, Q, Y) == 0
     assert wb(32, 8192, 1024, fw.BF16, X, Q, Y) == 0                      # k % 2048 != 0
+
+
+def test_workspace_bytes_per_path():
+    """The per-path query: auto equals fp8w_linear_workspace_bytes; a forced fallback
+    always needs the 16-bit weight; a forced skinny or batch path splits k (and uses
+    workspace) only where it is also the automatic path."""
+    pw = fw.fp8w_linear_with_path_workspace_bytes
+    wb = fw.fp8w_linear_workspace_bytes
+    for (m, n, k, act) in [(1, 4096, 4096, fw.BF16), (32, 4096, 14336, fw.BF16), (4, 28672, 8200, fw.BF16),
+                           (64, 14336, 4096, fw.BF16), (17, 11000, 4096, fw.FP16), (64, 100, 500, fw.FP16)]:
+        assert pw(fw.PATH_AUTO, m, n, k, act, X, Q) == wb(m, n, k, act, X, Q, Y)
+    assert pw(fw.PATH_FALLBACK, 1, 4096, 4096, fw.BF16, X, Q) == 4096 * 4096 * 2
+    assert pw(fw.PATH_FALLBACK, 32, 4096, 14336, fw.FP16, X, Q) == 4096 * 14336 * 2
+    assert pw(fw.PATH_SKINNY, 32, 4096, 14336, fw.BF16, X, Q) == 4 * 32 * 4096 * 4
+    assert pw(fw.PATH_BATCH, 32, 4096, 14336, fw.BF16, X, Q) == 0      # forced: single pass
+    assert pw(fw.PATH_SKINNY, 1, 4096, 4096, fw.BF16, X, Q) == 0
+    assert pw(fw.PATH_BATCH, 64, 14336, 4096, fw.BF16, X, Q) == 2 * 64 * 14336 * 4
+    assert pw(fw.PATH_GEMV, 1, 4096, 4096, fw.BF16, X, Q) == 0
+    assert pw(7, 1, 4096, 4096, fw.BF16, X, Q) == 0
+    assert pw(fw.PATH_FALLBACK, 1, 4096, 4096, fw.FP32, X, Q) == 0   # invalid activation dtype
 
 
 def _lin(x=X, act=fw.BF16, m=4, k=4096, q=Q, s=S, b=B, n=4096, y=Y, ws=0, wsb=0, path=fw.PATH_AUTO):

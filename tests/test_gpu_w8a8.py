@@ -105,7 +105,9 @@ def test_w8a8_zero_rows_and_scale_zero():
 @pytest.mark.parametrize("i", range(len(workloads.PREFILL_SHAPES)))
 def test_w8a8_prefill_workload(i):
     """The prefill workload at full size (M = 2048): activation codes and scales
-    bit-exact on every row; outputs of 48 seeded rows against the oracle."""
+    bit-exact on every row; outputs against the oracle on every row of the
+    [4096, 4096] layer (about 4 s of oracle time on 16 threads) and on 48 seeded
+    rows of the two 58.7 MB layers."""
     m = 2048
     lw = workloads.prefill_layer(i)
     n, k = lw.w.shape
@@ -125,10 +127,10 @@ def test_w8a8_prefill_workload(i):
     yv = y.double().cpu().numpy()
     assert np.all(np.isfinite(yv))
     q_ref, s_ref, _ = oracle.quantize_rows(lw.w)
-    rows = np.random.default_rng(700 + i).choice(m, size=48, replace=False)
+    rows = np.arange(m) if i == 0 else np.random.default_rng(700 + i).choice(m, size=48, replace=False)
     y_ref = oracle.linear_w8a8_f64(qx_ref[rows], sx_ref[rows], q_ref, s_ref, None)
     xd = oracle.decode(qx_ref[rows]) * sx_ref[rows].astype(np.float64)[:, None]
-    assert_gate(yv[rows], y_ref, xd, oracle.row_amax(lw.w), f"w8a8 prefill {lw.name} (sampled rows)")
+    assert_gate(yv[rows], y_ref, xd, oracle.row_amax(lw.w), f"w8a8 prefill {lw.name} ({rows.size} rows)")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])

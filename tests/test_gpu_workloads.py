@@ -26,7 +26,7 @@ import torch
 import fp8_weight_only_amd as fw
 import oracle
 import workloads
-from parity_util import assert_gate, assert_same_bits, gate_sampled, nan_like
+from parity_util import assert_gate, assert_same_bits, nan_like
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -79,7 +79,9 @@ def _quantize_checked(layer):
     return q, s, q_ref, s_ref
 
 
-def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path, full=True):
+def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path):
+    """Every output of the call against the oracle's fp64 value (the oracle does the
+    largest of these, [28672, 8192] at 32 tokens, in well under a second)."""
     m, k = x.shape
     n = layer.w.shape[0]
     xd = x.to(DEV)
@@ -91,22 +93,10 @@ def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path, full=True):
     yv = y.double().cpu().numpy()
     x64 = x.double().numpy()
     b64 = None if layer.bias is None else layer.bias.double().numpy()
-    if full:
-        y_ref = oracle.linear_f64(x64, q_ref, s_ref, b64)
-        assert_gate(yv, y_ref, x64, amax, f"{layer.name} m={m}")
-        _call_report(layer, m, yv, y_ref, x64, amax)
-        return yv, y_ref
-    # sampled: every row, 4096 seeded channels (including the first and last)
-    g = np.random.default_rng(m * 7 + n)
-    cols = np.unique(np.concatenate([[0, n - 1], g.choice(n, size=min(n, 4096), replace=False)]))
-    rows = np.repeat(np.arange(m), cols.size)
-    cc = np.tile(cols, m)
-    y_ref = oracle.linear_f64_sampled(x64, q_ref, s_ref, b64, rows, cc)
-    ok = gate_sampled(yv[rows, cc], y_ref, np.linalg.norm(x64, axis=1)[rows], amax[cc])
-    assert ok.all(), f"{layer.name} m={m}: {np.count_nonzero(~ok)} sampled outputs outside the gate"
-    assert np.all(np.isfinite(yv)), f"{layer.name} m={m}: non-finite outputs"
-    _call_report(layer, m, yv, None, x64, amax)
-    return yv, None
+    y_ref = oracle.linear_f64(x64, q_ref, s_ref, b64)
+    assert_gate(yv, y_ref, x64, amax, f"{layer.name} m={m}")
+    _call_report(layer, m, yv, y_ref, x64, amax)
+    return yv, y_ref
 
 
 def test_tiny_gemv():
@@ -169,4 +159,4 @@ def test_large(shape):
             path = fw.PATH_FALLBACK
         else:
             path = fw.PATH_GEMV if m == 1 else fw.PATH_SKINNY
-        _linear_checked(lay, q, s, q_ref, s_ref, workloads.large_x(shape, m), amax, path, full=(m <= 8))
+        _linear_checked(lay, q, s, q_ref, s_ref, workloads.large_x(shape, m), amax, path)

@@ -152,3 +152,33 @@ def test_bf16_rounding_matches_library_cast():
     # hand-derived ties: 1 + 2^-8 -> 1.0 (even) ; 1 + 3*2^-8 -> 1 + 2^-6 (even)
     assert oracle.round_to_bf16([1 + 2 ** -8])[0] == 1.0
     assert oracle.round_to_bf16([1 + 3 * 2 ** -8])[0] == 1 + 2 ** -6
+
+
+def test_f16_rounding_matches_library_cast():
+    """The oracle's value -> fp32 -> fp16 rounding equals torch's round-to-nearest-even
+    cast on random fp32 patterns, on exact fp16 ties (the 13 dropped bits equal to
+    0x1000) and their neighbours, in the subnormal range and at overflow."""
+    g = np.random.default_rng(4)
+    u = g.integers(0, 1 << 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    # patterns inside fp16's normal range whose low 13 bits are a tie
+    e = g.integers(113, 142, size=50000, dtype=np.uint64).astype(np.uint32)  # fp32 exponents 2^-14 .. 2^14
+    s = g.integers(0, 2, size=50000, dtype=np.uint64).astype(np.uint32) << np.uint32(31)
+    mant = g.integers(0, 1 << 10, size=50000, dtype=np.uint64).astype(np.uint32) << np.uint32(13)
+    ties = s | (e << np.uint32(23)) | mant | np.uint32(0x1000)
+    allu = np.concatenate([u, ties, ties + np.uint32(1), ties - np.uint32(1)])
+    f = allu.view(np.float32)
+    f = f[np.isfinite(f)]
+    f = np.concatenate([f, (g.standard_normal(20000) * 2.0 ** -20).astype(np.float32),
+                        np.array([65504.0, 65519.0, 65520.0, -65520.0, 7e4], dtype=np.float32)])
+    mine = oracle.round_to_f16(f)
+    ref = torch.from_numpy(f.copy()).to(torch.float16).double().numpy()
+    assert np.array_equal(mine, ref, equal_nan=True)
+    # hand-derived ties: 1 + 2^-11 -> 1.0 (even); 1 + 3*2^-11 -> 1 + 2^-9 (even);
+    # 2^-25 (half the smallest subnormal) -> +0; 3*2^-25 -> 2^-23 (even);
+    # 65520 (halfway between 65504 and 2^16) -> inf; 65519 -> 65504
+    assert oracle.round_to_f16([1 + 2 ** -11])[0] == 1.0
+    assert oracle.round_to_f16([1 + 3 * 2 ** -11])[0] == 1 + 2 ** -9
+    assert oracle.round_to_f16([2.0 ** -25])[0] == 0.0
+    assert oracle.round_to_f16([3 * 2.0 ** -25])[0] == 2.0 ** -23
+    assert oracle.round_to_f16([65520.0])[0] == np.inf
+    assert oracle.round_to_f16([65519.0])[0] == 65504.0

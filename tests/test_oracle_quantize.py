@@ -130,3 +130,54 @@ def test_gaussian_rows_error_is_a_few_percent():
     rep = oracle.weight_error(w, q, scale)
     assert 0.015 < rep["rel_l2"] < 0.035
     assert rep["underflow"] < 1e-3
+
+
+def test_row_amax_hand_rows():
+    """max_k |W[n,k]| per output row ("The contract": the scale's amax is taken over
+    one output channel's row). Hand-written rows whose answers are read off by eye:
+    the extreme is negative in one row, a row is all zeros (signed zeros included),
+    one row holds a 50x outlier, and the matrix is not square, so a transposed
+    index (max over a column) or a dropped absolute value gives a different answer."""
+    w = np.array([[0.25, -3.5, 1.0, 2.0, -0.5],
+                  [0.0, -0.0, 0.0, -0.0, 0.0],
+                  [0.02, -0.01, 0.015, 1.0, -0.03],
+                  [-1e-30, 2e-30, -4e-30, 0.0, 3e-30]], dtype=np.float32)
+    got = oracle.row_amax(w)
+    assert got.shape == (4,)
+    assert got[0] == 3.5
+    assert got[1] == 0.0 and not np.signbit(got[1])
+    assert got[2] == 1.0
+    assert got[3] == float(np.float32(4e-30))
+    # the column maxima (what a transposed index would return) differ
+    assert not np.array_equal(got[:4], np.abs(w).max(axis=0)[:4])
+    # one element per row: |w|
+    single = np.array([[-7.0], [0.125], [-0.0]], dtype=np.float32)
+    assert list(oracle.row_amax(single)) == [7.0, 0.125, 0.0]
+
+
+def test_row_amax_matches_numpy_on_outlier_rows():
+    """Against numpy's own reduction on rows shaped like the decoder-block workload:
+    Gaussian rows, some scaled 50x, some all zero, and rows whose extreme is negative."""
+    g = np.random.default_rng(21)
+    w = (g.standard_normal((300, 1000)) * 0.02).astype(np.float32)
+    w[::17] *= 50.0
+    w[5::29] = 0.0
+    w[7, 11] = -abs(w[7]).max() * 3.0
+    ref = np.abs(w.astype(np.float64)).max(axis=1)
+    assert np.array_equal(oracle.row_amax(w), ref)
+
+
+def test_row_amax_is_448_scale_within_one_ulp():
+    """scale = fl32(amax / 448) is correctly rounded, so 448 * scale lies within one
+    fp32 ulp of amax for every row with a normal scale, and amax is 0 exactly when
+    the scale is 0."""
+    g = np.random.default_rng(23)
+    w = (g.standard_normal((400, 700)) * g.uniform(1e-20, 1e20, (400, 1))).astype(np.float32)
+    w[3] = 0.0
+    _, scale, st = oracle.quantize_rows(w)
+    assert st == 0
+    amax = oracle.row_amax(w)
+    assert (amax == 0.0).tolist() == (scale == 0.0).tolist()
+    nz = scale != 0
+    ulp = np.spacing(amax[nz].astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(448.0 * scale[nz].astype(np.float64) - amax[nz]) <= ulp)
