@@ -49,7 +49,8 @@ written to --full-json (default gpurun_out/bench_full.json).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--min-ms MS] [--spin-ms MS]
                        [--extra] [--only tiny|skinny|block|large|batch|grouped|w8a8 ...] [--reps R]
-Profiler helpers: --only-timed (the timed region alone), --trace-summary CSV [--last N],
+Profiler helpers: --only-timed (the timed region alone), --shape N K M [--act fp16] (one call
+shape alone), --trace-summary CSV [--last N],
 --mfma-summary CSV N K, --pmc-summary FETCH_CSV WRITE_CSV.
 """
 import argparse
@@ -731,6 +732,10 @@ def main():
     ap.add_argument("--only", choices=SECTIONS, nargs="+",
                     help="run only these extra sections (no step) and print their JSON")
     ap.add_argument("--reps", type=int, default=100, help="launches per burst in the extra sections")
+    ap.add_argument("--shape", nargs=3, type=int, metavar=("N", "K", "M"),
+                    help="time one fp8w_linear shape alone (N(0,0.02^2) weights, no bias, weight copies rotated "
+                         "through >= 1 GiB): --steps back-to-back launches, then print its JSON (profiler runs)")
+    ap.add_argument("--act", choices=("bf16", "fp16"), default="bf16", help="activation dtype of --shape")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="print a markdown table of the library's kernels in a rocprofv3 kernel trace, then exit")
     ap.add_argument("--last", type=int, default=None,
@@ -772,6 +777,17 @@ def main():
         out = extra_sections(dev, stream, args.reps, args.only)
         calibration_copy(dev)
         print(json.dumps(out), flush=True)
+        return
+
+    if args.shape:
+        n, k, m = args.shape
+        case = workloads.random_case(7, m, n, k, torch.bfloat16 if args.act == "bf16" else torch.float16,
+                                     with_bias=False)
+        L = Layer(case.layer, max(1, math.ceil(ROTATE_BYTES / (n * k))), dev)
+        c = Call(L, case.x.to(dev), dev)
+        r = call_report(c, burst(c, args.steps, args.warmup, stream))
+        calibration_copy(dev)
+        print(json.dumps(r), flush=True)
         return
 
     # ---------------------------------------------------------------- the step (the metric)
