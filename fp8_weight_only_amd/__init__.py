@@ -28,7 +28,7 @@ import os
 import torch
 
 __all__ = [
-    "Fp8wError", "lib_path", "load", "fp8w_quantize", "fp8w_linear", "fp8w_linear_with_path",
+    "Fp8wError", "lib_path", "load", "fp8w_quantize", "fp8w_linear", "fp8w_linear_with_path", "fp8w_linear_noalloc", "linear_noalloc", "SCRATCH_BYTES",
     "fp8w_dequantize_fallback", "fp8w_linear_path", "fp8w_linear_workspace_bytes", "fp8w_linear_with_path_workspace_bytes",
     "fp8w_linear_kernel",
     "fp8w_stream_read_probe", "fp8w_quantize_grouped", "fp8w_linear_grouped", "fp8w_linear_grouped_with_path",
@@ -43,6 +43,7 @@ __all__ = [
 ]
 
 BF16, FP16, FP32 = 0, 1, 2
+SCRATCH_BYTES = 32 << 20  # FP8W_SCRATCH_BYTES: the static scratch of fp8w_linear_noalloc, per GPU
 PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_FALLBACK, PATH_BATCH = -1, 0, 1, 2, 3
 SUCCESS, ERR_INVALID_VALUE, ERR_MISALIGNED, ERR_NONFINITE, ERR_WORKSPACE, ERR_HIP = range(6)
 
@@ -59,6 +60,7 @@ EXPORTS = {
     "fp8w_quantize": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "fp8w_linear": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "fp8w_linear_with_path": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _I, _P]),
+    "fp8w_linear_noalloc": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
     "fp8w_dequantize_fallback": (_I, [_P, _P, _I64, _I64, _P, _I, _P]),
     "fp8w_linear_path": (_I, [_I64, _I64, _I64, _I, _P, _P, _P]),
     "fp8w_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _P, _P, _P]),
@@ -140,6 +142,10 @@ def fp8w_linear_path(m, n, k, act_dtype, x, q, y) -> int:
 
 def fp8w_linear_workspace_bytes(m, n, k, act_dtype, x, q, y) -> int:
     return load().fp8w_linear_workspace_bytes(m, n, k, act_dtype, x, q, y)
+
+
+def fp8w_linear_noalloc(x, act_dtype, m, k, q, scale, bias, n, y, stream) -> int:
+    return load().fp8w_linear_noalloc(x, act_dtype, m, k, q, scale, bias, n, y, stream)
 
 
 def fp8w_linear_with_path_workspace_bytes(path, m, n, k, act_dtype, x, q) -> int:
@@ -316,6 +322,31 @@ def linear(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Te
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = fp8w_linear_with_path(xp, act, m, k, qp, sp, bp, n, yp, wp, wb, path, _stream(x.device))
     _check(st, "fp8w_linear")
+    return out
+
+
+def linear_noalloc(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor = None,
+                   out: torch.Tensor = None) -> torch.Tensor:
+    """``linear`` through fp8w_linear_noalloc: any workspace the call uses is the
+    library's static per-GPU scratch, so with ``out`` given nothing is allocated.
+    Calls that may overlap on one GPU must not be made (they share the scratch)."""
+    if x.dim() != 2 or q.dim() != 2 or q.dtype != torch.uint8 or scale.dtype != torch.float32:
+        raise ValueError("expected x [m,k], q uint8 [n,k], scale fp32 [n]")
+    m, k = x.shape
+    n = q.shape[0]
+    if q.shape[1] != k or scale.shape != (n,):
+        raise ValueError("shape mismatch between x, q and scale")
+    if bias is not None and (bias.shape != (n,) or bias.dtype != x.dtype):
+        raise ValueError("bias must be [n] in the activation dtype")
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    elif out.shape != (m, n) or out.dtype != x.dtype:
+        raise ValueError("out must be [m, n] in the activation dtype")
+    st = fp8w_linear_noalloc(_dev(x, "x") if x.numel() else 0, _dtype_code(x.dtype), m, k,
+                             _dev(q, "q") if q.numel() else 0, _dev(scale, "scale") if n else 0,
+                             _dev(bias, "bias") if bias is not None and n else 0, n,
+                             _dev(out, "out") if out.numel() else 0, _stream(x.device))
+    _check(st, "fp8w_linear_noalloc")
     return out
 
 

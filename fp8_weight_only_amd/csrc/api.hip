@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/fp8w.h"
@@ -258,9 +260,84 @@ fp8w_status_t run_linear_grouped(const void* x, fp8w_dtype_t act, int64_t m, int
                                                   use_ws ? ws : nullptr, use_ws ? ws_bytes : 0, stream));
 }
 
+// ---- scratch of the no-allocation entry point (fp8w_linear_noalloc)
+// Every GPU the library runs on holds its own copy of this array, at its own
+// address, until the process ends. In host code `scratch` names only a
+// host-side handle, not a device address: the address is looked up once per
+// device with hipGetSymbolAddress (that device current) and kept, and only that
+// pointer is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[FP8W_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the scratch array on the GPU that `stream` runs on.
+fp8w_status_t scratch_for(hipStream_t stream, void** out)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return FP8W_ERR_INVALID_VALUE;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = 0;
+            e = hipGetDevice(&cur);
+            if (e != hipSuccess)
+                return hip_status(e);
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+                return hip_status(e);
+            void* addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+            if (e != hipSuccess)
+                return hip_status(e);
+            if (back != hipSuccess)
+                return hip_status(back);
+            if (!addr)
+                return hip_status(hipErrorInvalidSymbol);
+            p = addr;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return FP8W_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+fp8w_status_t fp8w_linear_noalloc(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k, const uint8_t* q,
+                                  const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    fp8w_status_t st = check_linear(x, act_dtype, m, k, q, scale, bias, n, y);
+    if (st != FP8W_SUCCESS || m == 0 || n == 0)
+        return st;
+    const int path = auto_path(m, k, x, q);
+    size_t need = 0;
+    if (path == FP8W_PATH_FALLBACK) {
+        need = fallback_workspace(n, k, act_dtype);
+        if (need > FP8W_SCRATCH_BYTES)  // the 16-bit weight would not fit: rejected before anything runs
+            return FP8W_ERR_WORKSPACE;
+    } else if (path == FP8W_PATH_SKINNY) {
+        need = fp8w::skinny_workspace_bytes(m, n, k);
+    } else if (path == FP8W_PATH_BATCH) {
+        need = fp8w::batch_workspace_bytes(m, n, k);
+    }
+    void* ws = nullptr;
+    if (need > 0 && (st = scratch_for(stream, &ws)) != FP8W_SUCCESS)
+        return st;
+    // a k split whose partial sums would not fit takes its single-pass plan, as
+    // fp8w_linear does when given fewer bytes
+    return run_linear(x, act_dtype, m, k, q, scale, bias, n, y, ws, ws ? (size_t)FP8W_SCRATCH_BYTES : 0,
+                      FP8W_PATH_AUTO, stream);
+}
 
 fp8w_status_t fp8w_quantize_grouped(const void* w, fp8w_dtype_t w_dtype, int64_t n, int64_t k, int64_t group,
                                     uint8_t* q, float* scale, hipStream_t stream)
@@ -623,7 +700,8 @@ const char* fp8w_status_string(fp8w_status_t status)
     case FP8W_ERR_NONFINITE:
         return "non-finite weight (NaN or infinity)";
     case FP8W_ERR_WORKSPACE:
-        return "workspace missing or too small for the fallback path";
+        return "workspace missing or too small for the fallback path (fp8w_linear_noalloc: the call needs more "
+               "than the library's static scratch buffer holds)";
     case FP8W_ERR_HIP:
         return "HIP runtime error";
     }

@@ -21,7 +21,9 @@
  *   - Tensors are dense and row-major: W, q and a dequantised weight are
  *     [n, k] (n output channels, k input features), x is [m, k], y is [m, n].
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
- *     never allocates device memory and keeps no state between calls.
+ *     never allocates device memory. Its only state is fp8w_linear_noalloc's
+ *     static scratch array (part of the loaded code object) and the cached
+ *     device address of it per GPU.
  *   - Work is enqueued on `stream` (0 = the null stream) in stream order.
  *     Only fp8w_quantize synchronizes (on `stream`), to report non-finite
  *     weights. The other calls are asynchronous.
@@ -30,7 +32,9 @@
  *   - Sizes: 0 <= n, k <= 2^31 - 1; 0 <= m <= 1048560; n*k <= 2^62.
  *     A zero-sized call is valid and enqueues nothing, except that k == 0
  *     writes y = bias (or zeros).
- *   - Thread-safe: there is no global mutable state.
+ *   - Thread-safe: the scratch address cache is filled once per GPU under a
+ *     lock; nothing else is shared between calls (but see fp8w_linear_noalloc
+ *     on overlapping calls).
  */
 #ifndef FP8W_H
 #define FP8W_H
@@ -131,6 +135,34 @@ FP8W_API fp8w_status_t fp8w_linear_with_path(const void* x, fp8w_dtype_t act_dty
                                     const uint8_t* q, const float* scale, const void* bias, int64_t n,
                                     void* y, void* workspace, size_t workspace_bytes, int path,
                                     hipStream_t stream);
+
+/* Size of the static device scratch buffer of fp8w_linear_noalloc, per GPU. */
+#define FP8W_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * fp8w_linear for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments (minus the workspace), dispatch, kernels and results as
+ * fp8w_linear given a workspace of FP8W_SCRATCH_BYTES: the workspace is a
+ * static device array inside the library (32 MiB on every GPU the library runs
+ * on, held until the process ends), so nothing is allocated, by the call or by
+ * the caller; the call makes no hipMalloc, hipFree or other allocating call.
+ *   - A k split whose fp32 partial sums need more than FP8W_SCRATCH_BYTES runs
+ *     its single-pass plan instead (as fp8w_linear does with a short workspace).
+ *   - The fallback path needs n * k * 2 bytes for the 16-bit weight; a call
+ *     that needs more than FP8W_SCRATCH_BYTES returns FP8W_ERR_WORKSPACE before
+ *     anything is enqueued.
+ *   - Every call on one GPU shares that GPU's buffer. Each call writes the part
+ *     it reads before reading it, so nothing carries over between calls, but
+ *     calls that may run at the same time on one GPU (streams not ordered with
+ *     each other) race on the buffer and must not be made.
+ *   - The first call that needs the buffer on a device looks up its address
+ *     there (with that device current; the caller's current device is restored).
+ * Asynchronous, like fp8w_linear.
+ */
+FP8W_API fp8w_status_t fp8w_linear_noalloc(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,
+                                           const uint8_t* q, const float* scale, const void* bias, int64_t n,
+                                           void* y, hipStream_t stream);
 
 /*
  * The dequantised weight ("The contract", item "Fallback": q.float() * scale[:, None]).

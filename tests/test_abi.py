@@ -30,7 +30,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fw.load()
     names = declared_symbols()
-    assert len(names) == 26
+    assert len(names) == 27
     for name in names:
         assert hasattr(lib, name), name
         assert name in fw.EXPORTS, name
@@ -413,3 +413,19 @@ def test_w8a8_validation():
     assert fw.fp8w_linear_w8a8_kernel(100, 200, 256) == "w8a8_kernel<BN=128,BM=64,NS=4,W=4>"
     assert fw.fp8w_linear_w8a8_kernel(512, 14336, 4096) == "w8a8_kernel<BN=256,BM=128,NS=4,W=8>"
     assert fw.fp8w_linear_w8a8_kernel(512, 4096, 4000) is None
+
+
+def test_noalloc_rejects_before_touching_the_gpu():
+    """fp8w_linear_noalloc validates like fp8w_linear, and a fallback call whose
+    16-bit weight would not fit the static scratch is refused before any HIP call
+    (so these run without a GPU)."""
+    na = fw.fp8w_linear_noalloc
+    assert fw.SCRATCH_BYTES == 32 << 20
+    # k % 256 != 0: the fallback; 28672 x 8200 x 2 bytes > 32 MiB
+    assert na(X, fw.BF16, 4, 8200, Q, S, 0, 28672, Y, 0) == fw.ERR_WORKSPACE
+    # misaligned x: the fallback too, 4096 x 4096 x 2 = exactly 32 MiB would fit, 4097 rows do not
+    assert na(X + 2, fw.BF16, 4, 4096, Q, S, 0, 4097, Y, 0) == fw.ERR_WORKSPACE
+    assert na(X, fw.FP32, 4, 4096, Q, S, 0, 4096, Y, 0) == fw.ERR_INVALID_VALUE
+    assert na(X, fw.BF16, 4, 4096, Q, 0, 0, 4096, Y, 0) == fw.ERR_INVALID_VALUE      # no scale
+    assert na(X, fw.BF16, 4, 4096, Q, S, 0, 4096, X, 0) == fw.ERR_INVALID_VALUE      # y overlaps x
+    assert na(X, fw.BF16, 0, 4096, Q, S, 0, 4096, Y, 0) == fw.SUCCESS                # empty: nothing runs
