@@ -38,6 +38,18 @@ size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 // thread-local string; for tests and measurement reports).
 const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace);
 
+// The skinny kernel for layers of fewer than 8192 channels (narrow_kernel):
+// activation fragments in VGPRs, codes alone in per-wave LDS rings. plan_narrow
+// says whether it takes a shape (ok) and with which tile.
+struct NarrowPlan {
+    bool ok;
+    int mt, w, ns;  // 16-token MFMA tiles, waves, ring stages
+};
+NarrowPlan plan_narrow(int64_t m, int64_t n, int64_t k);
+hipError_t launch_narrow(const NarrowPlan& p, const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
+                         const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream);
+const char* narrow_kernel_name(const NarrowPlan& p);
+
 // Sum of fp32 partial sums part[splits, m, n] in split order, then the
 // scale/bias epilogue into y (act_type).
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t m, int64_t n, const float* scale,

@@ -534,6 +534,10 @@ hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, c
                         const void* bias, int64_t n, void* y, float* part, size_t part_bytes, hipStream_t stream)
 {
     const int mi = (int)m;
+    const NarrowPlan np = plan_narrow(m, n, k);
+    if (np.ok)
+        return launch_narrow(np, x, std::is_same<A, Bf16>::value ? Act::BF16 : Act::FP16, m, k, q, scale, bias, n, y,
+                             stream);
     const size_t need = skinny_workspace_bytes(m, n, k);
     const SkinnyPlan p = plan_skinny(m, n, k, part != nullptr && need > 0 && part_bytes >= need);
     if (p.pipe) {
@@ -559,7 +563,7 @@ hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, c
 
 size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {
-    if (m < 1 || m > 32 || n < 1 || k < 256 || k % 256 != 0)
+    if (m < 1 || m > 32 || n < 1 || k < 256 || k % 256 != 0 || plan_narrow(m, n, k).ok)
         return 0;
     const SkinnyPlan p = plan_skinny(m, n, k, true);
     return p.pipe && p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
@@ -603,6 +607,9 @@ hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uin
 const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace)
 {
     thread_local char name[96];
+    const NarrowPlan np = plan_narrow(m, n, k);
+    if (np.ok)
+        return narrow_kernel_name(np);
     const SkinnyPlan p = plan_skinny(m, n, k, with_workspace);
     if (p.pipe && p.splits > 1)
         snprintf(name, sizeof name, "pipe_kernel<XR=%d,CT=%d,KP=%d,NS=%d>x%d+splitk_reduce_kernel", p.xr, p.ct,

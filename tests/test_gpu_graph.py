@@ -21,7 +21,8 @@ DEV = torch.device("cuda:0")
 CALLS = [
     ("linear", 1, 1000, 1024, torch.bfloat16, "gemv_kernel<R=2,U=2,NT=64,DB>"),
     ("linear", 8, 2048, 1024, torch.float16, None),
-    ("linear", 20, 4100, 2048, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    ("linear", 20, 4100, 10240, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    ("linear", 12, 2000, 4096, torch.float16, "narrow_kernel<MT=1,W=4,NS=4>"),
     ("linear", 3, 300, 1000, torch.bfloat16, None),  # k % 256 != 0: fallback through the workspace
     ("linear", 70, 640, 1024, torch.float16, "batch_kernel<BN=32,BM=32,W=1>x2+splitk_reduce_kernel"),
     ("linear", 300, 2048, 512, torch.bfloat16, "batch_kernel<BN=64,BM=32,W=2>"),

@@ -103,8 +103,8 @@ PIPE = [
     (12, 14400, 1024, torch.float16, "pipe_kernel<XR=12,CT=4,KP=1,NS=4>"),
     (20, 8200, 2048, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
     (32, 8192, 4096, torch.float16, "pipe_kernel<XR=32,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
-    (17, 4100, 2048, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
-    (24, 5000, 4096, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"),
+    (17, 4100, 10240, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    (24, 5000, 12288, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"),
     (32, 4096, 6144, torch.bfloat16, "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
 ]
 
@@ -118,7 +118,33 @@ def test_pipe_kernel_parity(m, n, k, dtype, kernel):
     _check(case, expect_path=fw.PATH_SKINNY)
 
 
-@pytest.mark.parametrize("m,n,k,splits", [(24, 8256, 4096, 2), (20, 4160, 8192, 4)])
+NARROW = [
+    # (m, n, k, dtype, kernel the dispatcher must pick): every instance of the
+    # narrow-layer kernel, ragged channel tails, rings that run their main loop
+    # (more stages than the ring holds) and rings that do not, every token tile
+    (2, 4096, 4096, torch.bfloat16, "narrow_kernel<MT=1,W=4,NS=4>"),
+    (5, 1000, 4096, torch.float16, "narrow_kernel<MT=1,W=4,NS=4>"),
+    (9, 4100, 8192, torch.bfloat16, "narrow_kernel<MT=1,W=4,NS=4>"),
+    (16, 33, 4096, torch.float16, "narrow_kernel<MT=1,W=4,NS=4>"),
+    (16, 4096, 4096, torch.bfloat16, "narrow_kernel<MT=1,W=4,NS=4>"),
+    (12, 4096, 7168, torch.bfloat16, "narrow_kernel<MT=1,W=7,NS=4>"),
+    (3, 500, 14336, torch.float16, "narrow_kernel<MT=1,W=7,NS=4>"),
+    (17, 4096, 2048, torch.bfloat16, "narrow_kernel<MT=2,W=4,NS=2>"),
+    (24, 300, 8192, torch.float16, "narrow_kernel<MT=2,W=4,NS=2>"),
+    (20, 4100, 6144, torch.bfloat16, "narrow_kernel<MT=2,W=4,NS=2>"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,dtype,kernel", NARROW)
+def test_narrow_kernel_parity(m, n, k, dtype, kernel):
+    print(f"narrow m={m} n={n} k={k} {dtype} {kernel}", flush=True)
+    assert fw.fp8w_linear_kernel(fw.PATH_AUTO, m, n, k, fw.BF16 if dtype == torch.bfloat16 else fw.FP16,
+                                 0, 0) == kernel
+    case = workloads.random_case(17 * m + n + k, m, n, k, dtype, with_bias=(m % 2 == 0))
+    _check(case, expect_path=fw.PATH_SKINNY)
+
+
+@pytest.mark.parametrize("m,n,k,splits", [(24, 8256, 4096, 2), (20, 4160, 10240, 4)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 def test_split_k_matches_single_pass(m, n, k, splits, dtype):
     """A shape that splits k when given workspace: with it (workgroup rows of

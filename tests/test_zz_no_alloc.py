@@ -50,11 +50,11 @@ def _noalloc(x, q, s, b):
 
 
 # consecutive calls, each smaller than the one before, on every path that uses
-# the scratch: skinny k split in four, then in two / four on smaller layers;
+# the scratch: skinny k split in four, then in two, on smaller layers;
 # batch k split; the fallback's 16-bit weight; and the GEMV (no scratch)
 SEQUENCES = [
-    [(32, 4096, 14336, torch.bfloat16, False), (20, 4096, 4096, torch.float16, True)],
-    [(24, 8192, 4096, torch.bfloat16, True), (17, 4096, 2048, torch.bfloat16, False)],
+    [(32, 4096, 14336, torch.bfloat16, False), (20, 4096, 10240, torch.float16, True)],
+    [(24, 8192, 4096, torch.bfloat16, True), (17, 8192, 2048, torch.bfloat16, False)],
     [(64, 14336, 4096, torch.bfloat16, False), (40, 2048, 1024, torch.float16, True)],
     [(8, 3000, 1000, torch.bfloat16, True), (3, 700, 520, torch.float16, False)],
     [(1, 4096, 4096, torch.bfloat16, True), (1, 1024, 1024, torch.float16, False)],
