@@ -410,6 +410,10 @@ template <typename A, int XR, int CT, int KP, int NS>
 hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
                        int64_t n, void* y, hipStream_t stream, int splits = 1, float* part = nullptr)
 {
+    // the ring issues only stages that exist when each split's k is a whole,
+    // positive number of NS-stage groups
+    if (splits < 1 || k % ((int64_t)splits * KP * 256 * NS) != 0)
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)((n + 16 * CT - 1) / (16 * CT)), (unsigned)splits), block(CT * KP * kWave);
     hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
                        q, scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k,
