@@ -249,34 +249,93 @@ struct Pipe {
         }
     }
 
-    // MFMA pair j of this wave's 256 k: lane (i, g) takes codes 64g + 16j .. +15 of
-    // channel i (16 contiguous k, two MFMAs) and the matching activations of
-    // token i (+ 16 mt).
-    __device__ __forceinline__ void compute(const uint8_t* buf, f32x4* acc) const
+    // Which k each wave multiplies. Sliced (CT dividing 4, a ring of more than
+    // two stages): the 256 k of a k-part are four groups of 64, and wave (ct,
+    // kp) takes groups ct, ct + CT, .. of every channel tile of the k-part, so
+    // each activation fragment is read from LDS once and serves all CT tiles.
+    // At 32 tokens this cuts the LDS reads per stage from 80 to 32 KB; measured
+    // on MI355X, [14336 x 4096] went from 14.8 to 13.5 us at 22 tokens and from
+    // 15.5 to 14.7 at 32. With two stages it measured slower (18.9 against 20.6
+    // us on [4096 x 14336] at 22 tokens, split four ways), so there, as for
+    // CT = 3, wave (ct, kp) takes all of k-part kp for its own tile.
+    static constexpr bool kSliced = 4 % CT == 0 && NS > 2;
+    static constexpr int NACC = kSliced ? CT : 1;  // channel tiles a wave accumulates
+
+    // 16 contiguous codes of row i (two MFMAs' A fragments) and the matching
+    // activations of token i (+ 16 mt): lane (i, g) of group j takes chunk
+    // 4 j + g (sliced) or 4 g + j; rows sit rotated in LDS as issue() put them.
+    __device__ __forceinline__ void mfma_pair(const uint8_t* cb, const u32x4* b0, const u32x4* b1, int c,
+                                              f32x4* acc) const
     {
-        const int i = lane & 15, g = lane >> 4;
-        const uint8_t* cb = buf + wave * C::CODE;
-        const uint8_t* xb = buf + C::W * C::CODE + kp * C::XPART;
+        const int i = lane & 15;
+        const u32x4 c16 = *reinterpret_cast<const u32x4*>(cb + 16 * (16 * i + ((c + i) & 15)));
+        const u32x2 d0 = A::decode4(c16.x), d1 = A::decode4(c16.y);
+        const u32x2 d2 = A::decode4(c16.z), d3 = A::decode4(c16.w);
+        const u32x4 a0 = {d0.x, d0.y, d1.x, d1.y};
+        const u32x4 a1 = {d2.x, d2.y, d3.x, d3.y};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x4 c16 = *reinterpret_cast<const u32x4*>(cb + 16 * (16 * i + ((4 * g + j + i) & 15)));
-            const u32x2 d0 = A::decode4(c16.x), d1 = A::decode4(c16.y);
-            const u32x2 d2 = A::decode4(c16.z), d3 = A::decode4(c16.w);
-            const u32x4 a0 = {d0.x, d0.y, d1.x, d1.y};
-            const u32x4 a1 = {d2.x, d2.y, d3.x, d3.y};
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int t = (i + 16 * mt) < XR ? (i + 16 * mt) : XR - 1;
-                const uint8_t* xr = xb + 16 * (32 * t);
-                const u32x4 b0 = *reinterpret_cast<const u32x4*>(xr + 16 * ((8 * g + 2 * j + t) & 31));
-                const u32x4 b1 = *reinterpret_cast<const u32x4*>(xr + 16 * ((8 * g + 2 * j + 1 + t) & 31));
-                acc[mt] = A::mfma(a0, b0, acc[mt]);
-                acc[mt] = A::mfma(a1, b1, acc[mt]);
-            }
+        for (int mt = 0; mt < MT; ++mt) {
+            acc[mt] = A::mfma(a0, b0[mt], acc[mt]);
+            acc[mt] = A::mfma(a1, b1[mt], acc[mt]);
         }
     }
 
+    __device__ __forceinline__ void x_frag(const uint8_t* xb, int c, u32x4* b0, u32x4* b1) const
+    {
+        const int i = lane & 15;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int t = (i + 16 * mt) < XR ? (i + 16 * mt) : XR - 1;
+            const uint8_t* xr = xb + 16 * (32 * t);
+            b0[mt] = *reinterpret_cast<const u32x4*>(xr + 16 * ((2 * c + t) & 31));
+            b1[mt] = *reinterpret_cast<const u32x4*>(xr + 16 * ((2 * c + 1 + t) & 31));
+        }
+    }
+
+    __device__ __forceinline__ void compute(const uint8_t* buf, f32x4 (*acc)[MT]) const
+    {
+        const int g = lane >> 4;
+        const uint8_t* xb = buf + C::W * C::CODE + kp * C::XPART;
+        u32x4 b0[MT], b1[MT];
+        if constexpr (kSliced) {
+#pragma unroll
+            for (int jj = 0; jj < 4 / CT; ++jj) {
+                const int c = 4 * (ct + CT * jj) + g;
+                x_frag(xb, c, b0, b1);
+#pragma unroll
+                for (int t = 0; t < CT; ++t)
+                    mfma_pair(buf + (t + CT * kp) * C::CODE, b0, b1, c, acc[t]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x_frag(xb, 4 * g + j, b0, b1);
+                mfma_pair(buf + wave * C::CODE, b0, b1, 4 * g + j, acc[0]);
+            }
+        }
+    }
 };
+
+// Sum for tile ct of the partial sums in part[w][t][lane], over the waves in
+// index order: with NACC == CT (sliced) every wave w contributes part[w][ct];
+// with NACC == 1 the waves of tile ct are ct, ct + CT, .. (one per k-part).
+template <int NACC, int W, int CT>
+__device__ __forceinline__ f32x4 kSlicedSum(f32x4 (*part)[NACC][kWave], int ct, int lane)
+{
+    if constexpr (NACC == CT && CT > 1) {
+        f32x4 sum = part[0][ct][lane];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            sum += part[w][ct][lane];
+        return sum;
+    } else {
+        f32x4 sum = part[ct][0][lane];
+#pragma unroll
+        for (int w = ct + CT; w < W; w += CT)
+            sum += part[w][0][lane];
+        return sum;
+    }
+}
 
 // Requires (k / splits) % (KP * 256 * NS) == 0; the ring is run_ring's.
 template <typename A, int XR, int CT, int KP, int NS>
@@ -307,10 +366,13 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     p.kp = p.wave / CT;
     p.n0 = (int64_t)blockIdx.x * (16 * CT);
 
-    f32x4 acc[MT];
+    constexpr int NACC = P::NACC;
+    f32x4 acc[NACC][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NACC; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[t][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // epilogue operands of this lane's four channels, fetched before the ring
     // starts (extra loads ahead of the ring only make its waits stricter)
@@ -331,27 +393,25 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     p.rot = (int64_t)(blockIdx.x / 8) % S;
     run_ring<NS, C::LOADS>(p, S, b0, b1, b2, b3, acc);
 
-    // k-part partial sums meet in stage buffer 0, then wave (ct, 0) adds them in
-    // k order and applies the epilogue; D[4g + r][i] is channel 4g + r, token i.
-    static_assert(C::STAGE >= C::W * MT * kWave * 16, "reduction fits in a stage buffer");
-    f32x4(*part)[MT][kWave] = reinterpret_cast<f32x4(*)[MT][kWave]>(b0);
-    __syncthreads();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        part[p.wave][mt][p.lane] = acc[mt];
-    __syncthreads();
-    if (p.kp != 0)
-        return;
+    // The waves' partial sums meet in stage buffer 0, one token tile at a
+    // time: wave w's sums for tile t at part[w][t]. Wave (ct, 0) adds those of
+    // tile ct over the waves in index order and applies the epilogue;
+    // D[4g + r][i] is channel 4g + r, token i.
+    static_assert(C::STAGE >= C::W * NACC * kWave * 16, "reduction fits in a stage buffer");
+    f32x4(*part)[NACC][kWave] = reinterpret_cast<f32x4(*)[NACC][kWave]>(b0);
     const int i = p.lane & 15, g = p.lane >> 4;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        f32x4 sum = part[p.ct][mt][p.lane];
+        __syncthreads();
 #pragma unroll
-        for (int kp = 1; kp < KP; ++kp)
-            sum += part[kp * CT + p.ct][mt][p.lane];
+        for (int t = 0; t < NACC; ++t)
+            part[p.wave][t][p.lane] = acc[t][mt];
+        __syncthreads();
         const int tok = i + 16 * mt;
-        if (tok >= m)
+        if (p.kp != 0 || tok >= m)
             continue;
+        // sliced: every wave holds a share of every tile; else wave (ct, kp) holds tile ct of k-part kp
+        f32x4 sum = kSlicedSum<NACC, C::W, CT>(part, p.ct, p.lane);
         const float v[4] = {sum.x, sum.y, sum.z, sum.w};
         if (part_out) {  // split k: fp32 partial sums, reduced by splitk_reduce_kernel
             float* o = part_out + ((int64_t)blockIdx.y * m + tok) * n;
