@@ -46,7 +46,9 @@ __device__ __forceinline__ void stage_barrier()
 // Runs stages 0 .. S-1 through the ring (S % NS == 0, S >= NS). P provides
 // issue(s, buf) (exactly LOADS load instructions per wave) and compute(buf, acc).
 // The last group of NS stages issues only its first load, then drains.
-template <int NS, int LOADS, typename P, typename Acc>
+// PIN keeps the compiler from moving any of a step's compute ahead of that
+// step's loads, so the next stage is requested as soon as the barrier opens.
+template <int NS, int LOADS, bool PIN = false, typename P, typename Acc>
 __device__ __forceinline__ void run_ring(const P& p, int64_t S, uint8_t* b0, uint8_t* b1, uint8_t* b2, uint8_t* b3,
                                          Acc* acc)
 {
@@ -56,6 +58,8 @@ __device__ __forceinline__ void run_ring(const P& p, int64_t S, uint8_t* b0, uin
         wait_loads_at_most<LOADS*(NS - 2)>();
         stage_barrier();
         p.issue(s + NS - 1, nxt);
+        if constexpr (PIN)
+            __builtin_amdgcn_sched_barrier(0);
         p.compute(cur, acc);
     };
     p.issue(0, b0);

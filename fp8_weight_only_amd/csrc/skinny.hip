@@ -391,7 +391,10 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     // workgroups are dealt to the eight XCDs in turn: consecutive workgroups of
     // one XCD get consecutive start stages
     p.rot = (int64_t)(blockIdx.x / 8) % S;
-    run_ring<NS, C::LOADS>(p, S, b0, b1, b2, b3, acc);
+    // with the sliced compute, the loads pinned ahead of each step's compute
+    // measured 0.2-0.4 us faster at 16-22 tokens on [14336 x 4096]; for CT = 3
+    // they were 0.2-0.6 us slower
+    run_ring<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
 
     // The waves' partial sums meet in stage buffer 0, one token tile at a
     // time: wave w's sums for tile t at part[w][t]. Wave (ct, 0) adds those of
