@@ -187,18 +187,22 @@ def grouped_report(call, st):
 
 
 class Call:
-    """Argument tuples of one fp8w_linear call for every weight copy."""
+    """Argument tuples of one fp8w_linear call for every weight copy (path:
+    fp8w_linear_with_path's forced path instead of the dispatch's)."""
 
-    def __init__(self, layer, x, dev, ws=None):
+    def __init__(self, layer, x, dev, ws=None, path=None):
         self.layer, self.x = layer, x
         self.m = x.shape[0]
+        self.req_path = fw.PATH_AUTO if path is None else path
         self.y = torch.empty((self.m, layer.n), dtype=x.dtype, device=dev)
+        act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
         if ws is None:  # the workspace the library asks for (fallback, or a k split), allocated once
-            wsb = fw.workspace_bytes(x, layer.qs[0][0])
+            wsb = fw.fp8w_linear_with_path_workspace_bytes(self.req_path, self.m, layer.n, layer.k, act,
+                                                           x.data_ptr(), layer.qs[0][0].data_ptr())
             ws = torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None
         self.ws = ws
-        act = fw.BF16 if x.dtype == torch.bfloat16 else fw.FP16
-        self.path = ["gemv", "skinny", "fallback", "batch"][fw.linear_path(x, layer.qs[0][0])]
+        self.path = ["gemv", "skinny", "fallback", "batch"][
+            fw.linear_path(x, layer.qs[0][0]) if path is None else path]
         self.args = [(x.data_ptr(), act, self.m, layer.k, q.data_ptr(), s.data_ptr(),
                       0 if layer.bias is None else layer.bias.data_ptr(), layer.n, self.y.data_ptr(),
                       0 if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel())
@@ -206,7 +210,10 @@ class Call:
         self.bytes = alg_bytes(self.m, layer.n, layer.k, layer.bias is not None)
 
     def launch(self, copy, stream):
-        r = fw.load().fp8w_linear(*self.args[copy % len(self.args)], stream)
+        if self.req_path == fw.PATH_AUTO:
+            r = fw.load().fp8w_linear(*self.args[copy % len(self.args)], stream)
+        else:
+            r = fw.load().fp8w_linear_with_path(*self.args[copy % len(self.args)], self.req_path, stream)
         if r != 0:
             raise fw.Fp8wError(r, "fp8w_linear")
 
@@ -342,12 +349,16 @@ def mfma_issued_flops(kernel, m, n, k):
     segments per instruction of which one is kept, so tokens count as
     MP*MT*SEG. None for other kernels."""
     import re
-    mm = re.match(r"pipe(?:_grouped)?_kernel<XR=(\d+),CT=(\d+),KP=\d+,NS=\d+>", kernel or "")
+    mm = re.match(r"pipe(?:_grouped)?_kernel<XR=(\d+),CT=(\d+),KP=\d+,NS=\d+(,CB=4)?>", kernel or "")
     if mm:
         xr, ct = int(mm.group(1)), int(mm.group(2))
         mt = 2 if xr > 16 else 1
         chans = 16 * ct * math.ceil(n / (16 * ct))
-        return 2.0 * k * chans * 16 * mt, 16 * mt
+        kr = k
+        if mm.group(3):  # the 4-byte path: the ring's columns (an even number of stages); the tail is fp32
+            kr = k - k % 256
+            kr -= 256 if (kr // 256) % 2 else 0
+        return 2.0 * kr * chans * 16 * mt, 16 * mt
     mm = re.match(r"seg_kernel<SEG=(\d+),T=(\d+),W=\d+,U=\d+,MT=(\d+)>", kernel or "")
     if mm:
         seg, t, mt = int(mm.group(1)), int(mm.group(2)), int(mm.group(3))
@@ -363,8 +374,8 @@ def call_report(call, us):
     us = st["mean"] if st else us
     gbps = call.bytes / (us * 1e-6) / 1e9
     act = fw.BF16 if call.x.dtype == torch.bfloat16 else fw.FP16
-    kernel = fw.fp8w_linear_kernel(fw.PATH_AUTO, call.m, call.layer.n, call.layer.k, act, call.x.data_ptr(),
-                                   call.layer.qs[0][0].data_ptr())
+    kernel = fw.fp8w_linear_kernel(getattr(call, "req_path", fw.PATH_AUTO), call.m, call.layer.n, call.layer.k,
+                                   act, call.x.data_ptr(), call.layer.qs[0][0].data_ptr())
     if call.path in ("skinny", "batch") and call.ws is None and "splitk" in kernel:
         kernel = "single pass (no workspace)"
     useful = 2.0 * call.m * call.layer.n * call.layer.k
@@ -1123,6 +1134,11 @@ def extra_sections(dev, stream, reps=100, only=None):
                 lg.append(call_report(c, burst(c, max(20, reps // 2), 5, stream)))
                 log(f"  large {shape} m={m} [{lg[-1]['kernel']}]: {lg[-1]['us_per_call']:.2f} us "
                     f"{lg[-1]['pct_peak']:.1f}% of peak")
+                if shape == workloads.LARGE_FALLBACK_SHAPE:  # the dequantizing fallback, forced, for comparison
+                    c = Call(L, x, dev, path=fw.PATH_FALLBACK)
+                    lg.append(dict(call_report(c, burst(c, max(20, reps // 2), 5, stream)), forced=True))
+                    log(f"  large {shape} m={m} forced [{lg[-1]['kernel']}]: {lg[-1]['us_per_call']:.2f} us "
+                        f"{lg[-1]['pct_peak']:.1f}% of peak")
             lg.append({"layer": L.name, "quantize_ms": round(L.quantize_ms, 3)})
             del L
             torch.cuda.empty_cache()

@@ -83,19 +83,37 @@ bool fast_pointers(const void* x, const uint8_t* q)
     return aligned(x, 16) && aligned(q, 16);
 }
 
+// The skinny kernel's 4-byte path: 1..32 tokens whose codes the 16-byte
+// kernels cannot load (k not a multiple of 256, or q not 16-byte aligned),
+// with k % 8 == 0, k >= 512, q 4-byte and x 16-byte aligned.
+bool ring4_shape(int64_t m, int64_t k, const void* x, const uint8_t* q)
+{
+    if (m < 1 || m > 32 || k < 512 || k % 8 != 0 || !aligned(x, 16) || !aligned(q, 4))
+        return false;
+    return !(fast_k(k) && fast_pointers(x, q));
+}
+
 // The per-channel linear: GEMV, skinny MFMA, the batch GEMM above 32 tokens,
 // or the fallback.
 int auto_path(int64_t m, int64_t k, const void* x, const uint8_t* q)
+{
+    if (m >= 1 && fast_k(k) && fast_pointers(x, q))
+        return m == 1 ? FP8W_PATH_GEMV : m <= 32 ? FP8W_PATH_SKINNY : FP8W_PATH_BATCH;
+    return ring4_shape(m, k, x, q) ? FP8W_PATH_SKINNY : FP8W_PATH_FALLBACK;
+}
+
+// The grouped linear: the same split by tokens, without the 4-byte path.
+int auto_path_grouped(int64_t m, int64_t k, const void* x, const uint8_t* q)
 {
     if (!fast_k(k) || !fast_pointers(x, q) || m < 1)
         return FP8W_PATH_FALLBACK;
     return m == 1 ? FP8W_PATH_GEMV : m <= 32 ? FP8W_PATH_SKINNY : FP8W_PATH_BATCH;
 }
 
-// The grouped linear: the same split by tokens as the per-channel one.
-int auto_path_grouped(int64_t m, int64_t k, const void* x, const uint8_t* q)
+// Workspace bytes the skinny path uses for this call (the 4-byte path: none).
+size_t skinny_workspace(int64_t m, int64_t n, int64_t k, const void* x, const uint8_t* q)
 {
-    return auto_path(m, k, x, q);
+    return ring4_shape(m, k, x, q) ? 0 : fp8w::skinny_workspace_bytes(m, n, k);
 }
 
 size_t fallback_workspace(int64_t n, int64_t k, fp8w_dtype_t act)
@@ -140,13 +158,24 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
         return st;
     if (path == FP8W_PATH_AUTO)
         path = auto_path(m, k, x, q);
-    if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
-        if (path == FP8W_PATH_GEMV && m != 1 && m != 0)
+    if (path == FP8W_PATH_GEMV) {
+        if (m != 1 && m != 0)
             return FP8W_ERR_INVALID_VALUE;
-        if (m > 32 || !fast_k(k))
+        if (!fast_k(k))
             return FP8W_ERR_INVALID_VALUE;
         if (!fast_pointers(x, q))
             return FP8W_ERR_MISALIGNED;
+    } else if (path == FP8W_PATH_SKINNY) {
+        // the 16-byte kernels (k % 256 == 0, x and q 16-byte aligned) or the
+        // 4-byte path (k % 8 == 0, k >= 512, x 16-byte and q 4-byte aligned)
+        if (m > 32)
+            return FP8W_ERR_INVALID_VALUE;
+        if (!(fast_k(k) && fast_pointers(x, q))) {
+            if (k < 512 || k % 8 != 0)
+                return fast_k(k) ? FP8W_ERR_MISALIGNED : FP8W_ERR_INVALID_VALUE;
+            if (!aligned(x, 16) || !aligned(q, 4))
+                return FP8W_ERR_MISALIGNED;
+        }
     } else if (path == FP8W_PATH_BATCH) {
         if (!fast_k(k))
             return FP8W_ERR_INVALID_VALUE;
@@ -176,7 +205,7 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
     }
     if (path == FP8W_PATH_SKINNY) {
         // split k on shapes that use it, when the caller's workspace is large enough
-        const size_t need = fp8w::skinny_workspace_bytes(m, n, k);
+        const size_t need = skinny_workspace(m, n, k, x, q);
         const bool use_ws = need > 0 && ws && ws_bytes >= need;
         if (use_ws) {
             if (!aligned(ws, 16))
@@ -326,7 +355,7 @@ fp8w_status_t fp8w_linear_noalloc(const void* x, fp8w_dtype_t act_dtype, int64_t
         if (need > FP8W_SCRATCH_BYTES)  // the 16-bit weight would not fit: rejected before anything runs
             return FP8W_ERR_WORKSPACE;
     } else if (path == FP8W_PATH_SKINNY) {
-        need = fp8w::skinny_workspace_bytes(m, n, k);
+        need = skinny_workspace(m, n, k, x, q);
     } else if (path == FP8W_PATH_BATCH) {
         need = fp8w::batch_workspace_bytes(m, n, k);
     }
@@ -643,7 +672,7 @@ size_t fp8w_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, fp8w_dtype_t
 {
     const int p = fp8w_linear_path(m, n, k, act_dtype, x, q, y);
     if (p == FP8W_PATH_SKINNY)
-        return fp8w::skinny_workspace_bytes(m, n, k);
+        return skinny_workspace(m, n, k, x, q);
     if (p == FP8W_PATH_BATCH)
         return fp8w::batch_workspace_bytes(m, n, k);
     if (p != FP8W_PATH_FALLBACK)
@@ -662,7 +691,7 @@ size_t fp8w_linear_with_path_workspace_bytes(int path, int64_t m, int64_t n, int
     if (path == FP8W_PATH_FALLBACK)
         return fallback_workspace(n, k, act_dtype);
     if (path == FP8W_PATH_SKINNY && autop == FP8W_PATH_SKINNY)
-        return fp8w::skinny_workspace_bytes(m, n, k);
+        return skinny_workspace(m, n, k, x, q);
     if (path == FP8W_PATH_BATCH && autop == FP8W_PATH_BATCH)
         return fp8w::batch_workspace_bytes(m, n, k);
     return 0;
@@ -675,6 +704,8 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
         return nullptr;
     if (path == FP8W_PATH_AUTO)
         path = auto_path(m, k, x, q);
+    if (path == FP8W_PATH_SKINNY && ring4_shape(m, k, x, q))
+        return fp8w::skinny_kernel_name(m, n, k, false, true);
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || !fast_k(k))
             return nullptr;

@@ -24,19 +24,30 @@ hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, cons
 // Name of the GEMV instance launch_gemv picks for this shape.
 const char* gemv_kernel_name(int64_t n, int64_t k);
 
-// M = 1..32 MFMA skinny GEMM; k % 256 == 0, x and q 16-byte aligned. Shapes
-// that split k use ws (fp32 partial sums, 16-byte aligned, not overlapping any
-// operand) when ws_bytes >= skinny_workspace_bytes(m, n, k); otherwise they take
-// the single-pass plan.
+// M = 1..32 MFMA skinny GEMM; x 16-byte aligned; either k % 256 == 0 and q
+// 16-byte aligned, or (the 4-byte path, plan_ring4) k % 8 == 0, k >= 512 and q
+// 4-byte aligned. Shapes that split k use ws (fp32 partial sums, 16-byte
+// aligned, not overlapping any operand) when ws_bytes >= skinny_workspace_bytes
+// (m, n, k); otherwise they take the single-pass plan. The 4-byte path never
+// splits.
 hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
                          const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
-// Workspace bytes the skinny path uses for split k on this shape (0: none).
+// Workspace bytes the 16-byte skinny path uses for split k on this shape (0: none).
 size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 // Name of the kernel and tile launch_skinny picks for this shape (a
-// thread-local string; for tests and measurement reports).
-const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace);
+// thread-local string; for tests and measurement reports); ring4: the 4-byte path.
+const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace, bool ring4 = false);
+
+// The 4-byte path's plan: ok when it takes the shape (1..32 tokens, k % 8 == 0,
+// k >= 512); the ring covers kr columns, the rest is the fp32 tail.
+struct Ring4Plan {
+    bool ok;
+    int xr, ct, kp, ns;
+    int64_t kr;
+};
+Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k);
 
 // The skinny kernel for layers of fewer than 8192 channels (narrow_kernel):
 // activation fragments in VGPRs, codes alone in per-wave LDS rings. plan_narrow

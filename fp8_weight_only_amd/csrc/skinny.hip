@@ -182,8 +182,11 @@ __global__ __launch_bounds__(W* kWave) void seg_kernel(
 // XR activation rows are fetched (m <= XR; MFMA columns past XR read row XR - 1
 // and are discarded); CT channel tiles of 16 and KP k-parts make the
 // workgroup's CT * KP waves; NS stage buffers; one stage is 256 k per wave.
-template <int XR, int CT, int KP, int NS>
+// CB is the bytes of codes one lane loads per instruction: 16, or 4 for rows
+// that are only 4-byte aligned (k not a multiple of 16, or an unaligned q).
+template <int XR, int CT, int KP, int NS, int CB = 16>
 struct PipeCfg {
+    static_assert(CB == 16 || CB == 4, "code load width");
     static_assert(XR % 2 == 0 && XR >= 2 && XR <= 32, "activation rows");
     static_assert(NS >= 2 && NS <= 4, "stages");
     static constexpr int MT = XR > 16 ? 2 : 1;      // 16-token MFMA tiles
@@ -193,13 +196,14 @@ struct PipeCfg {
     static constexpr int STAGE = W * CODE + KP * XPART;
     static constexpr int XLOADS = (XR / 2) * KP;    // 1 KB activation loads per stage
     static constexpr int XPW = (XLOADS + W - 1) / W;  // per wave; duplicates fill the last round
-    static constexpr int LOADS = 4 + XPW;           // load instructions per wave and stage
+    static constexpr int CLOADS = CODE / (kWave * CB);  // code load instructions per wave and stage
+    static constexpr int LOADS = CLOADS + XPW;      // load instructions per wave and stage
     static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
 };
 
-template <typename A, int XR, int CT, int KP, int NS>
+template <typename A, int XR, int CT, int KP, int NS, int CB = 16>
 struct Pipe {
-    using C = PipeCfg<XR, CT, KP, NS>;
+    using C = PipeCfg<XR, CT, KP, NS, CB>;
     static constexpr int MT = C::MT;
 
     const uint16_t* x;
@@ -225,15 +229,29 @@ struct Pipe {
         int64_t sr = s + rot;  // s < S and rot < S
         sr = sr < S ? sr : sr - S;
         const int64_t kb = sr * (KP * 256);
+        if constexpr (CB == 16) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * j + (lane >> 4);
-            const int chunk = ((lane & 15) - r) & 15;
-            int64_t row = n0 + 16 * ct + r;
-            row = row < n ? row : n - 1;
-            const uint8_t* src = q + row * k + kb + kp * 256 + chunk * 16;
-            __builtin_amdgcn_global_load_lds((const void*)src, FP8W_LDS(buf + wave * C::CODE + j * 1024), 16, 0,
-                                             2 /* non-temporal */);
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * j + (lane >> 4);
+                const int chunk = ((lane & 15) - r) & 15;
+                int64_t row = n0 + 16 * ct + r;
+                row = row < n ? row : n - 1;
+                const uint8_t* src = q + row * k + kb + kp * 256 + chunk * 16;
+                __builtin_amdgcn_global_load_lds((const void*)src, FP8W_LDS(buf + wave * C::CODE + j * 1024), 16,
+                                                 0, 2 /* non-temporal */);
+            }
+        } else {
+            // 4-byte loads, the same LDS image: instruction r fills row r, lane
+            // l the word l % 4 of slot l / 4, which holds chunk (slot - r) mod 16
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int chunk = ((lane >> 2) - r) & 15;
+                int64_t row = n0 + 16 * ct + r;
+                row = row < n ? row : n - 1;
+                const uint8_t* src = q + row * k + kb + kp * 256 + chunk * 16 + 4 * (lane & 3);
+                __builtin_amdgcn_global_load_lds((const void*)src, FP8W_LDS(buf + wave * C::CODE + r * 256), 4, 0,
+                                                 2 /* non-temporal */);
+            }
         }
 #pragma unroll
         for (int u = 0; u < C::XPW; ++u) {
@@ -337,14 +355,47 @@ __device__ __forceinline__ f32x4 kSlicedSum(f32x4 (*part)[NACC][kWave], int ct, 
     }
 }
 
-// Requires (k / splits) % (KP * 256 * NS) == 0; the ring is run_ring's.
-template <typename A, int XR, int CT, int KP, int NS>
+// Eight codes as two 4-byte loads (rows of the 4-byte path are 4-byte aligned).
+__device__ __forceinline__ u32x2 load_codes8(const uint8_t* p)
+{
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+    return u32x2{w[0], w[1]};
+}
+
+// Sum over 8 tail columns for four channels: tx holds one token's 8
+// activations, tq[r] channel r's 8 codes; exact decode, fp32 FMAs.
+template <typename A>
+__device__ __forceinline__ void tail8(u32x4 tx, const u32x2* tq, float* t)
+{
+    const uint32_t xw[4] = {tx.x, tx.y, tx.z, tx.w};
+    float xf[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        xf[2 * e] = A::lo_f32(xw[e]);
+        xf[2 * e + 1] = A::hi_f32(xw[e]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float w[8];
+        decode4_f32(tq[r].x, w[0], w[1], w[2], w[3]);
+        decode4_f32(tq[r].y, w[4], w[5], w[6], w[7]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            t[r] = __builtin_fmaf(xf[e], w[e], t[r]);
+    }
+}
+
+// The ring covers k columns 0 .. kr - 1 (kr / splits a multiple of KP * 256 *
+// NS); k is the row stride. Columns kr .. k - 1 (a multiple of 8, only without
+// a split) are added in fp32 by the waves that apply the epilogue, their first
+// eight fetched before the ring starts.
+template <typename A, int XR, int CT, int KP, int NS, int CB>
 __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k, int64_t kr,
     float* __restrict__ part_out)
 {
-    using P = Pipe<A, XR, CT, KP, NS>;
+    using P = Pipe<A, XR, CT, KP, NS, CB>;
     using C = typename P::C;
     constexpr int MT = C::MT;
     __shared__ __attribute__((aligned(1024))) uint8_t b0[C::STAGE];
@@ -353,7 +404,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t b3[NS > 3 ? C::STAGE : 16];
 
     // split k: workgroup row blockIdx.y owns k range [y * kc, (y + 1) * kc)
-    const int64_t kc = k / gridDim.y;
+    const int64_t kc = kr / gridDim.y;
     P p;
     p.x = x + (int64_t)blockIdx.y * kc;
     p.q = q + (int64_t)blockIdx.y * kc;
@@ -385,6 +436,23 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
         sc[r] = scale[ch];
         bi[r] = bias_bits(bias, ch);
     }
+    // the tail's first 8 columns, for the same channels and this lane's tokens
+    const bool tail = k > kr && p.kp == 0;
+    u32x2 tq[4];
+    u32x4 tx[MT];
+    if (tail) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int64_t ch = p.n0 + 16 * p.ct + 4 * (p.lane >> 4) + r;
+            ch = ch < n ? ch : n - 1;
+            tq[r] = load_codes8(q + ch * k + kr);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int t = (p.lane & 15) + 16 * mt;
+            tx[mt] = load16(x + (int64_t)(t < m ? t : m - 1) * k + kr);
+        }
+    }
 
     const int64_t S = kc / (KP * 256);
     p.S = S;
@@ -415,7 +483,24 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
             continue;
         // sliced: every wave holds a share of every tile; else wave (ct, kp) holds tile ct of k-part kp
         f32x4 sum = kSlicedSum<NACC, C::W, CT>(part, p.ct, p.lane);
-        const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+        float v[4] = {sum.x, sum.y, sum.z, sum.w};
+        if (tail) {
+            float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            tail8<A>(tx[mt], tq, t4);
+            for (int64_t c = kr + 8; c < k; c += 8) {  // longer tails, eight columns at a time
+                u32x2 cq[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
+                    ch = ch < n ? ch : n - 1;
+                    cq[r] = load_codes8(q + ch * k + c);
+                }
+                tail8<A>(load16(x + (int64_t)tok * k + c), cq, t4);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v[r] += t4[r];
+        }
         if (part_out) {  // split k: fp32 partial sums, reduced by splitk_reduce_kernel
             float* o = part_out + ((int64_t)blockIdx.y * m + tok) * n;
 #pragma unroll
@@ -469,18 +554,25 @@ hipError_t launch_seg(const void* x, int m, int64_t k, const uint8_t* q, const f
 
 // splits > 1: k is split over `splits` workgroup rows whose fp32 partial sums
 // go to part (splits * m * n floats), then a second kernel reduces them.
-template <typename A, int XR, int CT, int KP, int NS>
+// kr (default k): the columns the ring covers; the rest is the fp32 tail.
+template <typename A, int XR, int CT, int KP, int NS, int CB = 16>
 hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
-                       int64_t n, void* y, hipStream_t stream, int splits = 1, float* part = nullptr)
+                       int64_t n, void* y, hipStream_t stream, int splits = 1, float* part = nullptr,
+                       int64_t kr = -1)
 {
+    if (kr < 0)
+        kr = k;
     // the ring issues only stages that exist when each split's k is a whole,
     // positive number of NS-stage groups
-    if (splits < 1 || k % ((int64_t)splits * KP * 256 * NS) != 0)
+    if (splits < 1 || kr <= 0 || kr > k || kr % ((int64_t)splits * KP * 256 * NS) != 0)
+        return hipErrorInvalidValue;
+    // a tail only without a split, in whole 8-column blocks; rows as wide as the loads
+    if ((kr != k && (splits != 1 || (k - kr) % 8 != 0)) || k % 8 != 0 || (CB == 16 && k % 16 != 0))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)((n + 16 * CT - 1) / (16 * CT)), (unsigned)splits), block(CT * KP * kWave);
-    hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
-                       q, scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k,
-                       splits > 1 ? part : nullptr);
+    hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS, CB>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias),
+                       static_cast<uint16_t*>(y), m, n, k, kr, splits > 1 ? part : nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits <= 1)
         return e;
@@ -596,6 +688,50 @@ hipError_t launch_pipe_xr(const SkinnyPlan& p, const void* x, int m, int64_t k, 
     }
 }
 
+template <typename A, int XR>
+hipError_t launch_ring4_xr(const Ring4Plan& p, const void* x, int m, int64_t k, const uint8_t* q,
+                           const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    const int key = p.ct * 100 + p.kp * 10 + p.ns;
+    const int64_t kr = p.kr;
+    switch (key) {
+    case 412: return launch_pipe<A, XR, 4, 1, 2, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 414: return launch_pipe<A, XR, 4, 1, 4, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 212: return launch_pipe<A, XR, 2, 1, 2, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 214: return launch_pipe<A, XR, 2, 1, 4, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 122: return launch_pipe<A, XR, 1, 2, 2, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 124:
+        if constexpr (XR <= 16)  // 32 rows: 16 activation loads per wave, too many for four stages
+            return launch_pipe<A, XR, 1, 2, 4, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+        return hipErrorInvalidValue;
+    case 222:
+    case 224:
+        if constexpr (XR <= 16) {
+            if (key == 222)
+                return launch_pipe<A, XR, 2, 2, 2, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+            return launch_pipe<A, XR, 2, 2, 4, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+        }
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename A>
+hipError_t launch_ring4(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
+                        int64_t n, void* y, hipStream_t stream)
+{
+    const Ring4Plan p = plan_ring4(m, n, k);
+    if (!p.ok)
+        return hipErrorInvalidValue;
+    const int mi = (int)m;
+    switch (p.xr) {
+    case 4: return launch_ring4_xr<A, 4>(p, x, mi, k, q, scale, bias, n, y, stream);
+    case 8: return launch_ring4_xr<A, 8>(p, x, mi, k, q, scale, bias, n, y, stream);
+    case 16: return launch_ring4_xr<A, 16>(p, x, mi, k, q, scale, bias, n, y, stream);
+    default: return launch_ring4_xr<A, 32>(p, x, mi, k, q, scale, bias, n, y, stream);
+    }
+}
+
 template <typename A>
 hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale,
                         const void* bias, int64_t n, void* y, float* part, size_t part_bytes, hipStream_t stream)
@@ -627,6 +763,50 @@ hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, c
 }
 
 }  // namespace
+
+// The 4-byte path: codes whose rows are only 4-byte aligned (k a multiple of 8
+// but not of 256, or q not 16-byte aligned; k >= 512), 1..32 tokens.
+// pipe_kernel with 4-byte code loads (measured on MI355X as fast as 16-byte
+// ones for the same ring: 9.98 against 9.84 us over [14336, 4096], 36.6
+// against 35.9 over [28672, 8192]) covers kr = k rounded down to an even
+// number of 256-column stages; the remaining columns (fewer than 512, a
+// multiple of 8) are the fp32 tail. Channel tiles and k-parts follow
+// plan_skinny for kr without a split; where that picks seg_kernel or three
+// tiles, two tiles. Activation rows 4, 8, 16 or 32.
+Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k)
+{
+    Ring4Plan r{};
+    if (m < 1 || m > 32 || n < 1 || k < 512 || k % 8 != 0)
+        return r;
+    int64_t kr = k - k % 256;
+    if ((kr / 256) % 2 != 0)
+        kr -= 256;
+    const SkinnyPlan p = plan_skinny(m < 2 ? 2 : m, n, kr, false);
+    int ct = p.pipe && p.ct != 3 ? p.ct : 2, kp = p.pipe && p.ct != 3 ? p.kp : 1;
+    if (ct == 2 && kp == 2 && m > 16)
+        kp = 1;
+    const int xr = m <= 4 ? 4 : m <= 8 ? 8 : m <= 16 ? 16 : 32;
+    // four stages unless plan_skinny runs two (the widest layers, for two
+    // workgroups per CU), the k-parts do not divide them, or the wait counter
+    // cannot hold them (one tile, two k-parts, 32 rows: 16 activation loads
+    // per wave)
+    const bool deep = !(p.pipe && p.ns == 2);
+    const bool four = deep && !(ct == 1 && kp == 2 && xr == 32);
+    int ns = four && kr % ((int64_t)kp * 256 * 4) == 0 ? 4 : kr % ((int64_t)kp * 256 * 2) == 0 ? 2 : 0;
+    if (ns == 0) {  // one k-part: kr / 256 is even, so two stages always fit
+        if (ct == 1)
+            ct = 2;
+        kp = 1;
+        ns = deep && kr % 1024 == 0 ? 4 : 2;
+    }
+    r.ok = true;
+    r.xr = xr;
+    r.ct = ct;
+    r.kp = kp;
+    r.ns = ns;
+    r.kr = kr;
+    return r;
+}
 
 size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {
@@ -661,8 +841,17 @@ hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uin
 {
     if (n == 0 || m == 0)
         return hipSuccess;
-    if (m > 32 || k % 256 != 0)
+    if (m > 32)
         return hipErrorInvalidValue;
+    if (k % 256 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0) {  // rows only 4-byte aligned
+        if (reinterpret_cast<uintptr_t>(q) % 4 != 0 || reinterpret_cast<uintptr_t>(x) % 16 != 0)
+            return hipErrorInvalidValue;
+        if (act == Act::BF16)
+            return launch_ring4<Bf16>(x, m, k, q, scale, bias, n, y, stream);
+        if (act == Act::FP16)
+            return launch_ring4<F16>(x, m, k, q, scale, bias, n, y, stream);
+        return hipErrorInvalidValue;
+    }
     float* part = static_cast<float*>(ws);
     if (act == Act::BF16)
         return launch_typed<Bf16>(x, m, k, q, scale, bias, n, y, part, ws_bytes, stream);
@@ -671,9 +860,16 @@ hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uin
     return hipErrorInvalidValue;
 }
 
-const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace)
+const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace, bool ring4)
 {
     thread_local char name[96];
+    if (ring4) {
+        const Ring4Plan p = plan_ring4(m, n, k);
+        if (!p.ok)
+            return nullptr;
+        snprintf(name, sizeof name, "pipe_kernel<XR=%d,CT=%d,KP=%d,NS=%d,CB=4>", p.xr, p.ct, p.kp, p.ns);
+        return name;
+    }
     const NarrowPlan np = plan_narrow(m, n, k);
     if (np.ok)
         return narrow_kernel_name(np);

@@ -61,12 +61,20 @@ def test_path_selection():
     assert p(33, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_BATCH
     assert p(4096, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_BATCH
     assert p(64, 4096, 4100, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK      # k % 256 != 0
-    assert p(64, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_FALLBACK  # q not 16-B aligned
-    assert p(1, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK      # k % 256 != 0
+    assert p(64, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_FALLBACK  # q not 16-B aligned, m > 32
+    assert p(1, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_SKINNY        # 4-byte path: k % 8 == 0, k >= 512
+    assert p(32, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_SKINNY
+    assert p(33, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK     # 4-byte path: m <= 32 only
+    assert p(4, 100, 520, fw.BF16, X, Q, Y) == fw.PATH_SKINNY
+    assert p(4, 100, 504, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # 4-byte path: k >= 512
+    assert p(4, 100, 4100, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK        # 4-byte path: k % 8 == 0
+    assert p(4, 100, 4096, fw.BF16, X, Q + 4, Y) == fw.PATH_SKINNY      # q 4-byte aligned
+    assert p(4, 100, 4096, fw.BF16, X, Q + 2, Y) == fw.PATH_FALLBACK    # q 2-byte aligned
+    assert p(4, 100, 8200, fw.BF16, X + 8, Q, Y) == fw.PATH_FALLBACK    # 4-byte path: x 16-byte aligned
     assert p(1, 100, 128, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # k < 256
     assert p(1, 100, 0, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK           # k == 0
     assert p(1, 4096, 4096, fw.BF16, X + 2, Q, Y) == fw.PATH_FALLBACK   # x not 16-B aligned
-    assert p(4, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_FALLBACK   # q not 16-B aligned
+    assert p(4, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_SKINNY     # q not 16-B aligned: 4-byte path
     assert p(1, 4096, 4096, fw.BF16, 0, 0, 0) == fw.PATH_GEMV           # NULL = aligned
     assert p(1, 4096, 4096, fw.FP32, X, Q, Y) == -1                     # fp32 activations
     assert p(-1, 4096, 4096, fw.BF16, X, Q, Y) == -1
@@ -106,7 +114,14 @@ def test_kernel_names():
     assert kn(A, 20, 12300, 512, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=2>"
     assert kn(A, 16, 12288, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=3,KP=1,NS=4>"
     assert kn(fw.PATH_SKINNY, 1, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"
-    assert kn(A, 4, 28672, 8200, fw.BF16, X, Q) == "dequantize_kernel+wpipe_kernel<XR=4,CT=4,NS=4>"
+    assert kn(A, 4, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
+    assert kn(A, 1, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
+    assert kn(A, 32, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2,CB=4>"
+    assert kn(A, 16, 14336, 4104, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4,CB=4>"
+    assert kn(A, 16, 4096, 4096, fw.BF16, X, Q + 4) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=4>"
+    assert kn(A, 9, 100, 776, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=2,CB=4>"   # 768 = 3 stages: 512
+    assert kn(A, 32, 2048, 4096 + 8, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=4>"
+    assert kn(fw.PATH_FALLBACK, 4, 28672, 8200, fw.BF16, X, Q) == "dequantize_kernel+wpipe_kernel<XR=4,CT=4,NS=4>"
     assert kn(A, 40, 300, 1000, fw.FP16, X, Q) == "dequantize_kernel+wpipe_kernel<XR=32,CT=4,NS=4>"
     assert kn(A, 5, 31, 37, fw.BF16, X, Q) == "dequantize_kernel+fallback_gemm_kernel"       # k % 8 != 0
     assert kn(A, 4, 128, 200, fw.BF16, X, Q) == "dequantize_kernel+fallback_gemm_kernel"     # k < 256
@@ -130,7 +145,9 @@ def test_workspace_bytes():
     wb = fw.fp8w_linear_workspace_bytes
     assert wb(1, 4096, 4096, fw.BF16, X, Q, Y) == 0
     assert wb(16, 4096, 4096, fw.BF16, X, Q, Y) == 0
-    assert wb(4, 28672, 8200, fw.BF16, X, Q, Y) == 28672 * 8200 * 2
+    assert wb(4, 28672, 8200, fw.BF16, X, Q, Y) == 0                     # 4-byte skinny path
+    assert wb(4, 28672, 8196, fw.BF16, X, Q, Y) == 28672 * 8196 * 2      # k % 8 != 0: fallback
+    assert wb(32, 4096, 14336, fw.BF16, X, Q + 4, Y) == 0                 # 4-byte path: no split
     assert wb(64, 100, 500, fw.FP16, X, Q, Y) == 100 * 500 * 2           # k % 256 != 0: fallback
     assert wb(64, 100, 512, fw.FP16, X, Q, Y) == 0                       # batch kernel, single pass
     assert wb(64, 14336, 4096, fw.BF16, X, Q, Y) == 2 * 64 * 14336 * 4    # batch kernel, k in two
@@ -188,7 +205,11 @@ def test_linear_rejects_invalid_arguments():
     # forced paths the shape cannot take
     assert _lin(m=2, path=fw.PATH_GEMV) == fw.ERR_INVALID_VALUE
     assert _lin(m=33, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
-    assert _lin(k=4000, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
+    assert _lin(k=4004, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE     # k % 8 != 0
+    assert _lin(k=504, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE      # 4-byte path: k >= 512
+    assert _lin(k=4104, x=X + 8, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED  # 4-byte path: x 16-byte aligned
+    assert _lin(q=Q + 2, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED      # codes at least 4-byte aligned
+    assert _lin(k=256, q=Q + 4, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED  # 4-byte path needs k >= 512
     assert _lin(m=1, x=X + 2, path=fw.PATH_GEMV) == fw.ERR_MISALIGNED
     assert _lin(m=64, k=4000, path=fw.PATH_BATCH) == fw.ERR_INVALID_VALUE
     assert _lin(m=64, k=128, path=fw.PATH_BATCH) == fw.ERR_INVALID_VALUE
@@ -219,10 +240,11 @@ def test_batch_split_workspace_is_validated():
 
 
 def test_linear_fallback_needs_workspace():
-    assert _lin(k=8200) == fw.ERR_WORKSPACE
-    assert _lin(k=8200, ws=WS, wsb=4096 * 8200 * 2 - 1) == fw.ERR_WORKSPACE
-    assert _lin(k=8200, ws=WS + 1, wsb=4096 * 8200 * 2) == fw.ERR_MISALIGNED
-    assert _lin(k=8200, ws=X, wsb=4096 * 8200 * 2) == fw.ERR_INVALID_VALUE  # overlaps x
+    assert _lin(k=8200, path=fw.PATH_FALLBACK) == fw.ERR_WORKSPACE
+    assert _lin(k=8196) == fw.ERR_WORKSPACE                               # k % 8 != 0: the fallback
+    assert _lin(k=8200, ws=WS, wsb=4096 * 8200 * 2 - 1, path=fw.PATH_FALLBACK) == fw.ERR_WORKSPACE
+    assert _lin(k=8196, ws=WS + 1, wsb=4096 * 8196 * 2) == fw.ERR_MISALIGNED
+    assert _lin(k=8196, ws=X, wsb=4096 * 8196 * 2) == fw.ERR_INVALID_VALUE  # overlaps x
     assert _lin(m=64, path=fw.PATH_FALLBACK) == fw.ERR_WORKSPACE
 
 
@@ -426,8 +448,8 @@ def test_noalloc_rejects_before_touching_the_gpu():
     (so these run without a GPU)."""
     na = fw.fp8w_linear_noalloc
     assert fw.SCRATCH_BYTES == 32 << 20
-    # k % 256 != 0: the fallback; 28672 x 8200 x 2 bytes > 32 MiB
-    assert na(X, fw.BF16, 4, 8200, Q, S, 0, 28672, Y, 0) == fw.ERR_WORKSPACE
+    # k % 8 != 0: the fallback; 28672 x 8196 x 2 bytes > 32 MiB
+    assert na(X, fw.BF16, 4, 8196, Q, S, 0, 28672, Y, 0) == fw.ERR_WORKSPACE
     # misaligned x: the fallback too, 4096 x 4096 x 2 = exactly 32 MiB would fit, 4097 rows do not
     assert na(X + 2, fw.BF16, 4, 4096, Q, S, 0, 4097, Y, 0) == fw.ERR_WORKSPACE
     assert na(X, fw.FP32, 4, 4096, Q, S, 0, 4096, Y, 0) == fw.ERR_INVALID_VALUE

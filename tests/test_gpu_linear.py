@@ -63,12 +63,13 @@ SMALL = [
     (33, 64, 512, torch.bfloat16, True, fw.PATH_BATCH),
     (300, 200, 768, torch.float16, False, fw.PATH_BATCH),
     (70, 40, 300, torch.float16, True, fw.PATH_FALLBACK),
-    (1, 77, 8200, torch.bfloat16, True, fw.PATH_FALLBACK),
+    (1, 77, 8200, torch.bfloat16, True, fw.PATH_SKINNY),       # 4-byte path: k % 256 != 0, 8-value tail
     (3, 50, 1, torch.bfloat16, True, fw.PATH_FALLBACK),
     (5, 31, 37, torch.float16, False, fw.PATH_FALLBACK),
     (4, 128, 200, torch.bfloat16, True, fw.PATH_FALLBACK),
     (40, 300, 1000, torch.float16, True, fw.PATH_FALLBACK),    # 2 token tiles, 488-value k tail
-    (7, 16500, 776, torch.bfloat16, False, fw.PATH_FALLBACK),  # wide layer, 264-value tail
+    (7, 16500, 776, torch.bfloat16, False, fw.PATH_SKINNY),    # 4-byte path, wide layer, 264-value tail
+    (7, 16500, 504, torch.bfloat16, False, fw.PATH_FALLBACK),  # k < 512: the fallback's ring, 248-value tail
     (12, 70, 264, torch.bfloat16, True, fw.PATH_FALLBACK),     # shortest ring (2 stages), 8-value tail
 ]
 
@@ -116,6 +117,49 @@ def test_pipe_kernel_parity(m, n, k, dtype, kernel):
                                  0, 0) == kernel
     case = workloads.random_case(31 * m + n + k, m, n, k, dtype, with_bias=(m % 2 == 1))
     _check(case, expect_path=fw.PATH_SKINNY)
+
+
+RING4 = [
+    # (m, n, k, dtype, bias, byte offset of q, kernel the dispatcher must pick):
+    # the skinny kernel's 4-byte path, every ring shape it uses, tails of 8,
+    # 248, 264 and 504 columns, codes 4-, 8- and 12-byte aligned, ragged channels
+    (1, 77, 8200, torch.bfloat16, True, 0, "pipe_kernel<XR=4,CT=2,KP=1,NS=4,CB=4>"),
+    (2, 16500, 1032, torch.bfloat16, False, 0, "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"),
+    (4, 12300, 4344, torch.float16, True, 0, "pipe_kernel<XR=4,CT=4,KP=1,NS=4,CB=4>"),
+    (6, 12288, 2056, torch.bfloat16, True, 0, "pipe_kernel<XR=8,CT=2,KP=1,NS=4,CB=4>"),
+    (8, 8200, 2056, torch.float16, False, 0, "pipe_kernel<XR=8,CT=2,KP=2,NS=4,CB=4>"),
+    (16, 9000, 1288, torch.bfloat16, True, 0, "pipe_kernel<XR=16,CT=2,KP=1,NS=4,CB=4>"),
+    (17, 8300, 1544, torch.float16, True, 0, "pipe_kernel<XR=32,CT=2,KP=1,NS=2,CB=4>"),
+    (9, 300, 776, torch.bfloat16, False, 0, "pipe_kernel<XR=16,CT=2,KP=1,NS=2,CB=4>"),
+    (12, 1000, 4104, torch.float16, True, 0, "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=4>"),
+    (32, 300, 2056, torch.bfloat16, True, 0, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=4>"),
+    (24, 5000, 1528, torch.bfloat16, False, 0, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=4>"),
+    (5, 28672, 1032, torch.bfloat16, True, 0, "pipe_kernel<XR=8,CT=4,KP=1,NS=2,CB=4>"),
+    (16, 4096, 4096, torch.bfloat16, True, 4, "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=4>"),
+    (3, 14336, 4096, torch.float16, True, 8, "pipe_kernel<XR=4,CT=4,KP=1,NS=4,CB=4>"),
+    (32, 14336, 4096, torch.bfloat16, False, 12, "pipe_kernel<XR=32,CT=4,KP=1,NS=4,CB=4>"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,dtype,bias,qoff,kernel", RING4)
+def test_ring4_parity(m, n, k, dtype, bias, qoff, kernel):
+    """Codes whose rows are only 4-byte aligned: every output against the oracle."""
+    print(f"ring4 m={m} n={n} k={k} {dtype} bias={bias} qoff={qoff} {kernel}", flush=True)
+    case = workloads.random_case(17 * m + n + k, m, n, k, dtype, with_bias=bias)
+    q0, s, x, b = _prepare(case)
+    qbuf = torch.zeros(n * k + 16, dtype=torch.uint8, device=DEV)
+    q = qbuf[qoff:qoff + n * k].view(n, k)
+    q.copy_(q0)
+    act = fw.BF16 if dtype == torch.bfloat16 else fw.FP16
+    assert fw.fp8w_linear_kernel(fw.PATH_AUTO, m, n, k, act, x.data_ptr(), q.data_ptr()) == kernel
+    assert fw.linear_path(x, q) == fw.PATH_SKINNY
+    assert fw.workspace_bytes(x, q) == 0
+    q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
+    assert_same_bits(q.cpu().numpy(), q_ref, "codes")
+    y = nan_like((m, n), dtype, DEV)
+    fw.linear(x, q, s, b, out=y)
+    torch.cuda.synchronize()
+    assert_gate(y.double().cpu().numpy(), y_ref, x64, amax, f"ring4 m={m} n={n} k={k} qoff={qoff}")
 
 
 NARROW = [

@@ -79,9 +79,10 @@ def _quantize_checked(layer):
     return q, s, q_ref, s_ref
 
 
-def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path):
+def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path, also_paths=()):
     """Every output of the call against the oracle's fp64 value (the oracle does the
-    largest of these, [28672, 8192] at 32 tokens, in well under a second)."""
+    largest of these, [28672, 8192] at 32 tokens, in well under a second); then
+    the same call forced onto each of also_paths, against the same values."""
     m, k = x.shape
     n = layer.w.shape[0]
     xd = x.to(DEV)
@@ -96,6 +97,11 @@ def _linear_checked(layer, q, s, q_ref, s_ref, x, amax, expect_path):
     y_ref = oracle.linear_f64(x64, q_ref, s_ref, b64)
     assert_gate(yv, y_ref, x64, amax, f"{layer.name} m={m}")
     _call_report(layer, m, yv, y_ref, x64, amax)
+    for path in also_paths:
+        yp = nan_like((m, n), x.dtype, DEV)
+        fw.linear(xd, q, s, bd, out=yp, path=path)
+        torch.cuda.synchronize()
+        assert_gate(yp.double().cpu().numpy(), y_ref, x64, amax, f"{layer.name} m={m} path={path}")
     return yv, y_ref
 
 
@@ -156,7 +162,10 @@ def test_large(shape):
     for m in workloads.LARGE_MS:
         print(f"  m={m}", flush=True)
         if shape == workloads.LARGE_FALLBACK_SHAPE:
-            path = fw.PATH_FALLBACK
+            # k = 8200: the skinny kernel's 4-byte path (any m <= 32), and the
+            # dequantizing fallback forced, each on every output
+            _linear_checked(lay, q, s, q_ref, s_ref, workloads.large_x(shape, m), amax, fw.PATH_SKINNY,
+                            also_paths=(fw.PATH_FALLBACK,))
         else:
             path = fw.PATH_GEMV if m == 1 else fw.PATH_SKINNY
-        _linear_checked(lay, q, s, q_ref, s_ref, workloads.large_x(shape, m), amax, path)
+            _linear_checked(lay, q, s, q_ref, s_ref, workloads.large_x(shape, m), amax, path)

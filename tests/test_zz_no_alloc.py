@@ -51,13 +51,15 @@ def _noalloc(x, q, s, b):
 
 # consecutive calls, each smaller than the one before, on every path that uses
 # the scratch: skinny k split in four, then in two, on smaller layers;
-# batch k split; the fallback's 16-bit weight; and the GEMV (no scratch)
+# batch k split; the fallback's 16-bit weight (k % 8 != 0); and the GEMV and
+# the skinny kernel's 4-byte path (no scratch)
 SEQUENCES = [
     [(32, 4096, 14336, torch.bfloat16, False), (20, 4096, 10240, torch.float16, True)],
     [(24, 8192, 4096, torch.bfloat16, True), (17, 8192, 2048, torch.bfloat16, False)],
     [(64, 14336, 4096, torch.bfloat16, False), (40, 2048, 1024, torch.float16, True)],
-    [(8, 3000, 1000, torch.bfloat16, True), (3, 700, 520, torch.float16, False)],
+    [(8, 3000, 1004, torch.bfloat16, True), (3, 700, 524, torch.float16, False)],
     [(1, 4096, 4096, torch.bfloat16, True), (1, 1024, 1024, torch.float16, False)],
+    [(16, 2000, 2056, torch.bfloat16, True), (2, 500, 776, torch.float16, False)],
 ]
 
 
@@ -83,7 +85,7 @@ def test_noalloc_matches_linear_on_consecutive_calls(seq):
 
 
 def test_noalloc_refuses_a_fallback_weight_larger_than_the_scratch():
-    case, q, s, b = _prepare(590, 4, 4097, 4104, torch.bfloat16, False)  # k % 256 != 0: the fallback
+    case, q, s, b = _prepare(590, 4, 4097, 4100, torch.bfloat16, False)  # k % 8 != 0: the fallback
     x = case.x.to(DEV)
     assert fw.linear_path(x, q) == fw.PATH_FALLBACK and fw.workspace_bytes(x, q) > fw.SCRATCH_BYTES
     y = nan_like((4, 4097), torch.bfloat16, DEV)
