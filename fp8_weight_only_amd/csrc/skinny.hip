@@ -437,20 +437,23 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
         bi[r] = bias_bits(bias, ch);
     }
     // the tail's first 8 columns, for the same channels and this lane's tokens
-    const bool tail = k > kr && p.kp == 0;
+    // (only the 4-byte path has a tail: the 16-byte one needs k % 256 == 0)
+    const bool tail = CB == 4 && k > kr && p.kp == 0;
     u32x2 tq[4];
     u32x4 tx[MT];
-    if (tail) {
+    if constexpr (CB == 4) {
+        if (tail) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int64_t ch = p.n0 + 16 * p.ct + 4 * (p.lane >> 4) + r;
-            ch = ch < n ? ch : n - 1;
-            tq[r] = load_codes8(q + ch * k + kr);
-        }
+            for (int r = 0; r < 4; ++r) {
+                int64_t ch = p.n0 + 16 * p.ct + 4 * (p.lane >> 4) + r;
+                ch = ch < n ? ch : n - 1;
+                tq[r] = load_codes8(q + ch * k + kr);
+            }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int t = (p.lane & 15) + 16 * mt;
-            tx[mt] = load16(x + (int64_t)(t < m ? t : m - 1) * k + kr);
+            for (int mt = 0; mt < MT; ++mt) {
+                const int t = (p.lane & 15) + 16 * mt;
+                tx[mt] = load16(x + (int64_t)(t < m ? t : m - 1) * k + kr);
+            }
         }
     }
 
@@ -484,22 +487,24 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
         // sliced: every wave holds a share of every tile; else wave (ct, kp) holds tile ct of k-part kp
         f32x4 sum = kSlicedSum<NACC, C::W, CT>(part, p.ct, p.lane);
         float v[4] = {sum.x, sum.y, sum.z, sum.w};
-        if (tail) {
-            float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            tail8<A>(tx[mt], tq, t4);
-            for (int64_t c = kr + 8; c < k; c += 8) {  // longer tails, eight columns at a time
-                u32x2 cq[4];
+        if constexpr (CB == 4) {
+            if (tail) {
+                float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                tail8<A>(tx[mt], tq, t4);
+                for (int64_t c = kr + 8; c < k; c += 8) {  // longer tails, eight columns at a time
+                    u32x2 cq[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
-                    ch = ch < n ? ch : n - 1;
-                    cq[r] = load_codes8(q + ch * k + c);
+                    for (int r = 0; r < 4; ++r) {
+                        int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
+                        ch = ch < n ? ch : n - 1;
+                        cq[r] = load_codes8(q + ch * k + c);
+                    }
+                    tail8<A>(load16(x + (int64_t)tok * k + c), cq, t4);
                 }
-                tail8<A>(load16(x + (int64_t)tok * k + c), cq, t4);
-            }
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                v[r] += t4[r];
+                for (int r = 0; r < 4; ++r)
+                    v[r] += t4[r];
+            }
         }
         if (part_out) {  // split k: fp32 partial sums, reduced by splitk_reduce_kernel
             float* o = part_out + ((int64_t)blockIdx.y * m + tok) * n;
