@@ -51,7 +51,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--min-ms MS] [--spin
                        [--extra] [--only tiny|skinny|block|large|batch|grouped|w8a8 ...] [--reps R]
 Profiler helpers: --only-timed (the timed region alone), --shape N K M [--act fp16] (one call
 shape alone), --trace-summary CSV [--last N],
---mfma-summary CSV N K, --pmc-summary FETCH_CSV WRITE_CSV.
+--mfma-summary CSV N K, --pmc-summary FETCH_CSV WRITE_CSV, --counter-summary KERNEL CSV [CSV ...].
 """
 import argparse
 import hashlib
@@ -755,8 +755,14 @@ def main():
                     help="print a markdown table of the skinny kernels' matrix-core counters, then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/step_traffic.json from two rocprofv3 --pmc runs of --only-timed, then exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar="ARG",
+                    help="KERNEL CSV [CSV ...]: mean per dispatch of every counter in rocprofv3 --pmc CSVs for the "
+                         "library kernels whose name contains KERNEL, then exit")
     args = ap.parse_args()
     SPIN_MS = args.spin_ms
+    if args.counter_summary:
+        counter_summary(args.counter_summary[0], args.counter_summary[1:])
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_FILE)
         return
@@ -880,6 +886,34 @@ def _pmc_rows(path, counter):
         return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
 
 
+def counter_summary(kernel, csvs):
+    """Markdown table: for the library dispatches whose name contains `kernel`,
+    the mean per dispatch of every counter in the given rocprofv3 --pmc CSVs
+    (one counter set per run). FETCH_SIZE and WRITE_SIZE (KiB) are also given
+    in bytes, scaled by what the same run's last device copy (bench.py's 256 MiB
+    calibration) reads for them."""
+    import csv
+    print("| Counter | Mean per dispatch | Dispatches | Bytes (calibrated) |")
+    print("|---|---|---|---|")
+    for path in csvs:
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        for name in sorted({r["Counter_Name"] for r in rows}):
+            vals = [float(r["Counter_Value"]) for r in rows
+                    if r["Counter_Name"] == name and kernel in r["Kernel_Name"] and "fp8w::" in r["Kernel_Name"]]
+            if not vals:
+                continue
+            mean = sum(vals) / len(vals)
+            cal = ""
+            if name in ("FETCH_SIZE", "WRITE_SIZE"):
+                copies = [r for r in rows if r["Counter_Name"] == name and
+                          ("copyBuffer" in r["Kernel_Name"] or "direct_copy" in r["Kernel_Name"])]
+                if copies:
+                    copy = float(max(copies, key=lambda r: int(r["Dispatch_Id"]))["Counter_Value"])
+                    cal = f"{mean * COPY_BYTES / copy / 1e6:.2f} MB"
+            print(f"| {name} | {mean:,.1f} | {len(vals)} | {cal} |")
+
+
 def pmc_summary(fetch_csv, write_csv, out_path):
     """Turn two rocprofv3 --pmc runs of `bench.py --only-timed` (FETCH_SIZE, then
     WRITE_SIZE, KiB per dispatch) into HBM bytes per launch of each kernel
@@ -927,12 +961,13 @@ def _short_kernel_name(full):
         return full[:60]
     name, targs = m.group(1), (m.group(2) or "")
     args = [a.strip() for a in targs[1:-1].split(",")] if targs else []
-    keys = {"pipe_kernel": ("XR", "CT", "KP", "NS"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
+    keys = {"pipe_kernel": ("XR", "CT", "KP", "NS", "CB"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
             "gemv_kernel": ("R", "U", "NT", "DB"), "wpipe_kernel": ("XR", "CT", "NS"), "w8a8_kernel": ("BN", "BM", "NS", "WN", "WM", "GM"),
             "gemv_grouped_kernel": ("R", "U", "NT", "DB"), "pipe_grouped_kernel": ("XR", "CT", "KP", "NS", "G"),
             "batch_kernel": ("BN", "BM", "WN", "WM", "G", "GM")}.get(name)
     if keys and len(args) == len(keys) + 1:  # first argument is the activation type
-        return f"{name}<" + ",".join(f"{kk}={v}" for kk, v in zip(keys, args[1:])) + ">"
+        short = f"{name}<" + ",".join(f"{kk}={v}" for kk, v in zip(keys, args[1:])) + ">"
+        return short.replace(",CB=16>", ">")  # the library's names give the load width only when it is 4
     return name + targs
 
 
