@@ -201,6 +201,13 @@ struct PipeCfg {
     static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
 };
 
+// Eight codes as two 4-byte loads (rows of the 4-byte path are 4-byte aligned).
+__device__ __forceinline__ u32x2 load_codes8(const uint8_t* p)
+{
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+    return u32x2{w[0], w[1]};
+}
+
 template <typename A, int XR, int CT, int KP, int NS, int CB = 16>
 struct Pipe {
     using C = PipeCfg<XR, CT, KP, NS, CB>;
@@ -310,6 +317,49 @@ struct Pipe {
         }
     }
 
+    // k tail block b: columns kr + 32 b .. + 31; lane (i, g) takes the eight
+    // at + 8 g, as the A (codes of row i of each tile it holds) and B (token i)
+    // operands of one MFMA. Groups at or past k load nothing and stay zero in
+    // both operands.
+    template <int NT>
+    __device__ __forceinline__ void tail_load(int64_t kr, int b, u32x2 (&code)[NT], u32x4 (&xv)[MT]) const
+    {
+        const int i = lane & 15, g = lane >> 4;
+        const int64_t c = kr + 32 * b + 8 * g;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            code[t] = u32x2{0u, 0u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            xv[mt] = u32x4{0u, 0u, 0u, 0u};
+        if (c < k) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                int64_t ch = n0 + 16 * (NT == 1 ? ct : t) + i;
+                ch = ch < n ? ch : n - 1;
+                code[t] = load_codes8(q + ch * k + c);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int tok = i + 16 * mt < m ? i + 16 * mt : m - 1;
+                xv[mt] = load16(x + (int64_t)tok * k + c);
+            }
+        }
+    }
+
+    template <int NT>
+    __device__ __forceinline__ void tail_use(const u32x2 (&code)[NT], const u32x4 (&xv)[MT], f32x4 (*acc)[MT]) const
+    {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const u32x2 d0 = A::decode4(code[t].x), d1 = A::decode4(code[t].y);
+            const u32x4 a = {d0.x, d0.y, d1.x, d1.y};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[t][mt] = A::mfma(a, xv[mt], acc[t][mt]);
+        }
+    }
+
     __device__ __forceinline__ void compute(const uint8_t* buf, f32x4 (*acc)[MT]) const
     {
         const int g = lane >> 4;
@@ -355,40 +405,11 @@ __device__ __forceinline__ f32x4 kSlicedSum(f32x4 (*part)[NACC][kWave], int ct, 
     }
 }
 
-// Eight codes as two 4-byte loads (rows of the 4-byte path are 4-byte aligned).
-__device__ __forceinline__ u32x2 load_codes8(const uint8_t* p)
-{
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
-    return u32x2{w[0], w[1]};
-}
-
-// Sum over 8 tail columns for four channels: tx holds one token's 8
-// activations, tq[r] channel r's 8 codes; exact decode, fp32 FMAs.
-template <typename A>
-__device__ __forceinline__ void tail8(u32x4 tx, const u32x2* tq, float* t)
-{
-    const uint32_t xw[4] = {tx.x, tx.y, tx.z, tx.w};
-    float xf[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        xf[2 * e] = A::lo_f32(xw[e]);
-        xf[2 * e + 1] = A::hi_f32(xw[e]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float w[8];
-        decode4_f32(tq[r].x, w[0], w[1], w[2], w[3]);
-        decode4_f32(tq[r].y, w[4], w[5], w[6], w[7]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            t[r] = __builtin_fmaf(xf[e], w[e], t[r]);
-    }
-}
-
 // The ring covers k columns 0 .. kr - 1 (kr / splits a multiple of KP * 256 *
-// NS); k is the row stride. Columns kr .. k - 1 (a multiple of 8, only without
-// a split) are added in fp32 by the waves that apply the epilogue, their first
-// eight fetched before the ring starts.
+// NS); k is the row stride. Columns kr .. k - 1 (the 4-byte path only, a
+// multiple of 8 below 512, no split) are further MFMAs on operands loaded
+// straight into registers (Pipe::tail_load), 32 columns each, dealt to the
+// waves in turn; each wave fetches its first before the ring starts.
 template <typename A, int XR, int CT, int KP, int NS, int CB>
 __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
@@ -436,25 +457,18 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
         sc[r] = scale[ch];
         bi[r] = bias_bits(bias, ch);
     }
-    // the tail's first 8 columns, for the same channels and this lane's tokens
-    // (only the 4-byte path has a tail: the 16-byte one needs k % 256 == 0)
-    const bool tail = CB == 4 && k > kr && p.kp == 0;
-    u32x2 tq[4];
-    u32x4 tx[MT];
+    // the k tail's blocks this wave multiplies (sliced: all its tiles, blocks
+    // wave, wave + W, ..; else its own tile, blocks kp, kp + KP, ..), the first
+    // fetched now
+    constexpr int NT = P::NACC;
+    const int bstep = P::kSliced ? C::W : KP;
+    const int tb0 = P::kSliced ? p.wave : p.kp;
+    const int nblk = CB == 4 ? (int)((k - kr + 31) / 32) : 0;
+    u32x2 tcode[NT];
+    u32x4 txv[MT];
     if constexpr (CB == 4) {
-        if (tail) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                int64_t ch = p.n0 + 16 * p.ct + 4 * (p.lane >> 4) + r;
-                ch = ch < n ? ch : n - 1;
-                tq[r] = load_codes8(q + ch * k + kr);
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int t = (p.lane & 15) + 16 * mt;
-                tx[mt] = load16(x + (int64_t)(t < m ? t : m - 1) * k + kr);
-            }
-        }
+        if (tb0 < nblk)
+            p.tail_load(kr, tb0, tcode, txv);
     }
 
     const int64_t S = kc / (KP * 256);
@@ -466,6 +480,22 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     // measured 0.2-0.4 us faster at 16-22 tokens on [14336 x 4096]; for CT = 3
     // they were 0.2-0.6 us slower
     run_ring<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
+    if constexpr (CB == 4) {
+        if (tb0 < nblk) {
+            p.tail_use(tcode, txv, acc);
+            for (int b = tb0 + bstep; b < nblk; b += 2 * bstep) {  // two blocks' loads in flight at a time
+                u32x2 c1[NT], c2[NT];
+                u32x4 x1[MT], x2[MT];
+                const bool two = b + bstep < nblk;
+                p.tail_load(kr, b, c1, x1);
+                if (two)
+                    p.tail_load(kr, b + bstep, c2, x2);
+                p.tail_use(c1, x1, acc);
+                if (two)
+                    p.tail_use(c2, x2, acc);
+            }
+        }
+    }
 
     // The waves' partial sums meet in stage buffer 0, one token tile at a
     // time: wave w's sums for tile t at part[w][t]. Wave (ct, 0) adds those of
@@ -486,26 +516,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
             continue;
         // sliced: every wave holds a share of every tile; else wave (ct, kp) holds tile ct of k-part kp
         f32x4 sum = kSlicedSum<NACC, C::W, CT>(part, p.ct, p.lane);
-        float v[4] = {sum.x, sum.y, sum.z, sum.w};
-        if constexpr (CB == 4) {
-            if (tail) {
-                float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                tail8<A>(tx[mt], tq, t4);
-                for (int64_t c = kr + 8; c < k; c += 8) {  // longer tails, eight columns at a time
-                    u32x2 cq[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
-                        ch = ch < n ? ch : n - 1;
-                        cq[r] = load_codes8(q + ch * k + c);
-                    }
-                    tail8<A>(load16(x + (int64_t)tok * k + c), cq, t4);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    v[r] += t4[r];
-            }
-        }
+        const float v[4] = {sum.x, sum.y, sum.z, sum.w};
         if (part_out) {  // split k: fp32 partial sums, reduced by splitk_reduce_kernel
             float* o = part_out + ((int64_t)blockIdx.y * m + tok) * n;
 #pragma unroll
@@ -559,7 +570,7 @@ hipError_t launch_seg(const void* x, int m, int64_t k, const uint8_t* q, const f
 
 // splits > 1: k is split over `splits` workgroup rows whose fp32 partial sums
 // go to part (splits * m * n floats), then a second kernel reduces them.
-// kr (default k): the columns the ring covers; the rest is the fp32 tail.
+// kr (default k): the columns the ring covers; the rest is the k tail.
 template <typename A, int XR, int CT, int KP, int NS, int CB = 16>
 hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
                        int64_t n, void* y, hipStream_t stream, int splits = 1, float* part = nullptr,
@@ -775,9 +786,9 @@ hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, c
 // ones for the same ring: 9.98 against 9.84 us over [14336, 4096], 36.6
 // against 35.9 over [28672, 8192]) covers kr = k rounded down to an even
 // number of 256-column stages; the remaining columns (fewer than 512, a
-// multiple of 8) are the fp32 tail. Channel tiles and k-parts follow
-// plan_skinny for kr without a split; where that picks seg_kernel or three
-// tiles, two tiles. Activation rows 4, 8, 16 or 32.
+// multiple of 8) are the k tail, further MFMAs on register operands. Channel
+// tiles and k-parts follow plan_skinny for kr without a split; where that
+// picks seg_kernel or three tiles, two tiles. Activation rows 4, 8, 16 or 32.
 Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k)
 {
     Ring4Plan r{};
