@@ -320,7 +320,8 @@ struct Pipe {
     // k tail block b: columns kr + 32 b .. + 31; lane (i, g) takes the eight
     // at + 8 g, as the A (codes of row i of each tile it holds) and B (token i)
     // operands of one MFMA. Groups at or past k load nothing and stay zero in
-    // both operands.
+    // both operands. (A tail exists only without a k split, so q and x here are
+    // the rows' starts.)
     template <int NT>
     __device__ __forceinline__ void tail_load(int64_t kr, int b, u32x2 (&code)[NT], u32x4 (&xv)[MT]) const
     {
