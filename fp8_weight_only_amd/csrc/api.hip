@@ -93,12 +93,23 @@ bool ring4_shape(int64_t m, int64_t k, const void* x, const uint8_t* q)
     return !(fast_k(k) && fast_pointers(x, q));
 }
 
+// The GEMV's 8-code chunks: one token whose codes the 16-byte loads cannot
+// take, with k % 8 == 0, k >= 256, q 8-byte and x 16-byte aligned.
+bool gemv8_shape(int64_t m, int64_t k, const void* x, const uint8_t* q)
+{
+    if (m != 1 || k < 256 || k % 8 != 0 || !aligned(x, 16) || !aligned(q, 8))
+        return false;
+    return !(fast_k(k) && fast_pointers(x, q));
+}
+
 // The per-channel linear: GEMV, skinny MFMA, the batch GEMM above 32 tokens,
 // or the fallback.
 int auto_path(int64_t m, int64_t k, const void* x, const uint8_t* q)
 {
     if (m >= 1 && fast_k(k) && fast_pointers(x, q))
         return m == 1 ? FP8W_PATH_GEMV : m <= 32 ? FP8W_PATH_SKINNY : FP8W_PATH_BATCH;
+    if (gemv8_shape(m, k, x, q))
+        return FP8W_PATH_GEMV;
     return ring4_shape(m, k, x, q) ? FP8W_PATH_SKINNY : FP8W_PATH_FALLBACK;
 }
 
@@ -161,10 +172,14 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
     if (path == FP8W_PATH_GEMV) {
         if (m != 1 && m != 0)
             return FP8W_ERR_INVALID_VALUE;
-        if (!fast_k(k))
-            return FP8W_ERR_INVALID_VALUE;
-        if (!fast_pointers(x, q))
-            return FP8W_ERR_MISALIGNED;
+        // 16-code chunks (k % 256 == 0, x and q 16-byte aligned) or 8-code
+        // chunks (k % 8 == 0, x 16-byte and q 8-byte aligned)
+        if (!(fast_k(k) && fast_pointers(x, q))) {
+            if (k < 256 || k % 8 != 0)
+                return FP8W_ERR_INVALID_VALUE;
+            if (!aligned(x, 16) || !aligned(q, 8))
+                return FP8W_ERR_MISALIGNED;
+        }
     } else if (path == FP8W_PATH_SKINNY) {
         // the 16-byte kernels (k % 256 == 0, x and q 16-byte aligned) or the
         // 4-byte path (k % 8 == 0, k >= 512, x 16-byte and q 4-byte aligned)
@@ -706,6 +721,8 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
         path = auto_path(m, k, x, q);
     if (path == FP8W_PATH_SKINNY && ring4_shape(m, k, x, q))
         return fp8w::skinny_kernel_name(m, n, k, false, true);
+    if (path == FP8W_PATH_GEMV && gemv8_shape(m, k, x, q))
+        return fp8w::gemv_kernel_name(n, k, true);
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || !fast_k(k))
             return nullptr;

@@ -29,23 +29,45 @@
 namespace fp8w {
 namespace {
 
-template <typename A, int R>
-__device__ __forceinline__ void accum_chunk(const u32x4* code, u32x4 x0, u32x4 x1, float* acc)
+// A chunk is CH consecutive codes of a row (one load: 16 bytes, or 8 where
+// rows are only 8-byte aligned) and the CH activations they multiply.
+template <int CH>
+struct Chunk {
+    static_assert(CH == 16 || CH == 8, "chunk width");
+    static constexpr int CW = CH / 4;  // code words
+    static constexpr int XV = CH / 8;  // 16-byte activation loads
+    typedef uint32_t Words[CW];
+    __device__ __forceinline__ static void load_codes(const uint8_t* p, uint32_t* w)
+    {
+        if constexpr (CH == 16) {
+            const u32x4 v = load_stream16(p);
+            w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
+        } else {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+            w[0] = v.x, w[1] = v.y;
+        }
+    }
+};
+
+template <typename A, int R, int CH>
+__device__ __forceinline__ void accum_chunk(const uint32_t (*code)[CH / 4], const u32x4* xv, float* acc)
 {
-    float xf[16];
-    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float xf[CH];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        xf[2 * e + 0] = A::lo_f32(xw[e]);
-        xf[2 * e + 1] = A::hi_f32(xw[e]);
+    for (int v = 0; v < CH / 8; ++v) {
+        const uint32_t xw[4] = {xv[v].x, xv[v].y, xv[v].z, xv[v].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xf[8 * v + 2 * e + 0] = A::lo_f32(xw[e]);
+            xf[8 * v + 2 * e + 1] = A::hi_f32(xw[e]);
+        }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const uint32_t cw[4] = {code[r].x, code[r].y, code[r].z, code[r].w};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < CH / 4; ++d) {
             float w0, w1, w2, w3;
-            decode4_f32(cw[d], w0, w1, w2, w3);
+            decode4_f32(code[r][d], w0, w1, w2, w3);
             acc[r] = __builtin_fmaf(xf[4 * d + 0], w0, acc[r]);
             acc[r] = __builtin_fmaf(xf[4 * d + 1], w1, acc[r]);
             acc[r] = __builtin_fmaf(xf[4 * d + 2], w2, acc[r]);
@@ -57,20 +79,21 @@ __device__ __forceinline__ void accum_chunk(const u32x4* code, u32x4 x0, u32x4 x
 // U passes of a thread's chunks for R rows, and the activation chunks they
 // share. load() issues every load of the group back to back (the scheduling
 // barrier keeps the compiler from trading loads in flight for registers).
-template <int R, int U>
+template <int R, int U, int CH>
 struct Group {
-    u32x4 code[U][R];
-    u32x4 xv[U][2];
+    uint32_t code[U][R][CH / 4];
+    u32x4 xv[U][CH / 8];
     __device__ __forceinline__ void load(const uint8_t* const* qr, const uint16_t* xp, int64_t c0, int nt)
     {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t off = (c0 + (int64_t)nt * u) * 16;
+            const int64_t off = (c0 + (int64_t)nt * u) * CH;
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                code[u][r] = load_stream16(qr[r] + off);
-            xv[u][0] = load16(xp + off);
-            xv[u][1] = load16(xp + off + 8);
+                Chunk<CH>::load_codes(qr[r] + off, code[u][r]);
+#pragma unroll
+            for (int v = 0; v < CH / 8; ++v)
+                xv[u][v] = load16(xp + off + 8 * v);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -79,11 +102,11 @@ struct Group {
     {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            accum_chunk<A, R>(code[u], xv[u][0], xv[u][1], acc);
+            accum_chunk<A, R, CH>(code[u], xv[u], acc);
     }
 };
 
-template <typename A, int R, int U, int NT, bool DB>
+template <typename A, int R, int U, int NT, bool DB, int CH>
 __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
                                                   const float* __restrict__ scale,
                                                   const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -95,13 +118,13 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
     const int lane = t & (kWave - 1);
     const int wave = t >> 6;
     const int64_t row0 = (int64_t)blockIdx.x * R;
-    const int64_t nch = k >> 4;  // 16-code chunks per row
+    const int64_t nch = k / CH;  // chunks per row
 
     const uint8_t* qr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        qr[r] = q + (row0 + r < n ? row0 + r : n - 1) * k + (int64_t)t * 16;
-    const uint16_t* xp = x + (int64_t)t * 16;
+        qr[r] = q + (row0 + r < n ? row0 + r : n - 1) * k + (int64_t)t * CH;
+    const uint16_t* xp = x + (int64_t)t * CH;
 
     // epilogue operands of this workgroup's rows, fetched up front (threads
     // t < R use them; the others read a valid row and discard it)
@@ -119,7 +142,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
     // requests in flight instead of draining it at every group
     constexpr int64_t GS = (int64_t)NT * U;
     const int64_t G = nch / GS;
-    Group<R, U> ga, gb;
+    Group<R, U, CH> ga, gb;
     if constexpr (DB) {
         int64_t g = 0;
         if (G > 0) {
@@ -147,12 +170,16 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
     int64_t c0 = G * GS;
     for (; c0 < nch; c0 += NT) {  // tail passes: only threads whose chunk exists
         if (c0 + t < nch) {
-            const int64_t off = c0 * 16;
-            u32x4 code[R];
+            const int64_t off = c0 * CH;
+            uint32_t code[R][CH / 4];
+            u32x4 xv[CH / 8];
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                code[r] = load_stream16(qr[r] + off);
-            accum_chunk<A, R>(code, load16(xp + off), load16(xp + off + 8), acc);
+                Chunk<CH>::load_codes(qr[r] + off, code[r]);
+#pragma unroll
+            for (int v = 0; v < CH / 8; ++v)
+                xv[v] = load16(xp + off + 8 * v);
+            accum_chunk<A, R, CH>(code, xv, acc);
         }
     }
 
@@ -186,13 +213,13 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
     }
 }
 
-template <typename A, int R, int U, int NT, bool DB>
+template <typename A, int R, int U, int NT, bool DB, int CH = 16>
 hipError_t launch_cfg(const void* x, int64_t k, const uint8_t* q, const float* scale, const void* bias, int64_t n,
                       void* y, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + R - 1) / R)), block(NT);
-    hipLaunchKernelGGL((gemv_kernel<A, R, U, NT, DB>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
-                       scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), n, k);
+    hipLaunchKernelGGL((gemv_kernel<A, R, U, NT, DB, CH>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
+                       q, scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), n, k);
     return hipGetLastError();
 }
 
@@ -214,6 +241,11 @@ template <typename A>
 hipError_t launch_typed(const void* x, int64_t k, const uint8_t* q, const float* scale, const void* bias,
                         int64_t n, void* y, hipStream_t stream)
 {
+    if (k % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0) {  // rows only 8-byte aligned: 8-code chunks
+        if (n * k >= kLargeWeight)
+            return launch_cfg<A, 4, 2, 128, false, 8>(x, k, q, scale, bias, n, y, stream);
+        return launch_cfg<A, 2, 2, 64, true, 8>(x, k, q, scale, bias, n, y, stream);
+    }
     if (n * k >= kLargeWeight)
         return launch_cfg<A, 4, 2, 128, false>(x, k, q, scale, bias, n, y, stream);
     return launch_cfg<A, 2, 2, 64, true>(x, k, q, scale, bias, n, y, stream);
@@ -221,8 +253,10 @@ hipError_t launch_typed(const void* x, int64_t k, const uint8_t* q, const float*
 
 }  // namespace
 
-const char* gemv_kernel_name(int64_t n, int64_t k)
+const char* gemv_kernel_name(int64_t n, int64_t k, bool ch8)
 {
+    if (ch8)
+        return n * k >= kLargeWeight ? "gemv_kernel<R=4,U=2,NT=128,CH=8>" : "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>";
     return n * k >= kLargeWeight ? "gemv_kernel<R=4,U=2,NT=128>" : "gemv_kernel<R=2,U=2,NT=64,DB>";
 }
 

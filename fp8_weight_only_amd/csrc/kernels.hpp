@@ -17,12 +17,13 @@ enum class Act { BF16 = 0, FP16 = 1, FP32 = 2 };
 hipError_t launch_quantize(const void* w, Act w_type, int64_t n, int64_t k, uint8_t* q, float* scale,
                            hipStream_t stream);
 
-// M = 1 streaming GEMV; k % 256 == 0, x and q 16-byte aligned.
+// M = 1 streaming GEMV; x 16-byte aligned; k % 16 == 0 and q 16-byte aligned
+// (16-code chunks), or k % 8 == 0 and q 8-byte aligned (8-code chunks).
 hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,
                        const void* bias, int64_t n, void* y, hipStream_t stream);
 
-// Name of the GEMV instance launch_gemv picks for this shape.
-const char* gemv_kernel_name(int64_t n, int64_t k);
+// Name of the GEMV instance launch_gemv picks for this shape (ch8: 8-code chunks).
+const char* gemv_kernel_name(int64_t n, int64_t k, bool ch8 = false);
 
 // M = 1..32 MFMA skinny GEMM; x 16-byte aligned; either k % 256 == 0 and q
 // 16-byte aligned, or (the 4-byte path, plan_ring4) k % 8 == 0, k >= 512 and q

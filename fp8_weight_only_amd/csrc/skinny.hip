@@ -788,8 +788,9 @@ hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, c
 // against 35.9 over [28672, 8192]) covers kr = k rounded down to an even
 // number of 256-column stages; the remaining columns (fewer than 512, a
 // multiple of 8) are the k tail, further MFMAs on register operands. Channel
-// tiles and k-parts follow plan_skinny for kr without a split; where that
-// picks seg_kernel or three tiles, two tiles. Activation rows 4, 8, 16 or 32.
+// tiles and k-parts follow plan_skinny for kr without a split (with the
+// exceptions below). Activation rows 4, 8, 16 or 32. One token with 8-byte
+// aligned codes takes the GEMV's 8-code chunks instead (fp8w_linear's dispatch).
 Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k)
 {
     Ring4Plan r{};
@@ -799,7 +800,11 @@ Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k)
     if ((kr / 256) % 2 != 0)
         kr -= 256;
     const SkinnyPlan p = plan_skinny(m < 2 ? 2 : m, n, kr, false);
-    int ct = p.pipe && p.ct != 3 ? p.ct : 2, kp = p.pipe && p.ct != 3 ? p.kp : 1;
+    // where plan_skinny picks seg_kernel (under 8192 channels, up to 8 tokens):
+    // one tile and two k-parts, so that a 4096-channel layer still has 256
+    // workgroups (two tiles left half the CUs idle: [4096, 14344] at one
+    // token 36.7 us); where it picks three tiles, two
+    int ct = p.pipe ? (p.ct != 3 ? p.ct : 2) : 1, kp = p.pipe ? (p.ct != 3 ? p.kp : 1) : 2;
     if (ct == 2 && kp == 2 && m > 16)
         kp = 1;
     const int xr = m <= 4 ? 4 : m <= 8 ? 8 : m <= 16 ? 16 : 32;

@@ -62,7 +62,11 @@ def test_path_selection():
     assert p(4096, 4096, 4096, fw.BF16, X, Q, Y) == fw.PATH_BATCH
     assert p(64, 4096, 4100, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK      # k % 256 != 0
     assert p(64, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_FALLBACK  # q not 16-B aligned, m > 32
-    assert p(1, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_SKINNY        # 4-byte path: k % 8 == 0, k >= 512
+    assert p(1, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_GEMV          # 8-code GEMV: k % 8 == 0, q 8-byte aligned
+    assert p(1, 28672, 8200, fw.BF16, X, Q + 4, Y) == fw.PATH_SKINNY    # q 4-byte aligned: 4-byte skinny path
+    assert p(1, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_GEMV
+    assert p(1, 300, 264, fw.BF16, X, Q, Y) == fw.PATH_GEMV             # 8-code GEMV from k = 256
+    assert p(2, 300, 264, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # 4-byte skinny path from k = 512
     assert p(32, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_SKINNY
     assert p(33, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK     # 4-byte path: m <= 32 only
     assert p(4, 100, 520, fw.BF16, X, Q, Y) == fw.PATH_SKINNY
@@ -115,7 +119,10 @@ def test_kernel_names():
     assert kn(A, 16, 12288, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=3,KP=1,NS=4>"
     assert kn(fw.PATH_SKINNY, 1, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"
     assert kn(A, 4, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
-    assert kn(A, 1, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
+    assert kn(A, 1, 28672, 8200, fw.BF16, X, Q) == "gemv_kernel<R=4,U=2,NT=128,CH=8>"
+    assert kn(A, 1, 4096, 4104, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"
+    assert kn(A, 1, 28672, 8200, fw.BF16, X, Q + 4) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
+    assert kn(A, 4, 4096, 14344, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=4>"
     assert kn(A, 32, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2,CB=4>"
     assert kn(A, 16, 14336, 4104, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4,CB=4>"
     assert kn(A, 16, 4096, 4096, fw.BF16, X, Q + 4) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=4>"
@@ -210,6 +217,9 @@ def test_linear_rejects_invalid_arguments():
     assert _lin(k=4104, x=X + 8, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED  # 4-byte path: x 16-byte aligned
     assert _lin(q=Q + 2, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED      # codes at least 4-byte aligned
     assert _lin(k=256, q=Q + 4, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED  # 4-byte path needs k >= 512
+    assert _lin(m=1, k=4100, path=fw.PATH_GEMV) == fw.ERR_INVALID_VALUE     # k % 8 != 0
+    assert _lin(m=1, k=4104, q=Q + 4, path=fw.PATH_GEMV) == fw.ERR_MISALIGNED  # 8-code chunks: q 8-byte aligned
+    assert _lin(m=1, k=4104, x=X + 8, path=fw.PATH_GEMV) == fw.ERR_MISALIGNED  # x 16-byte aligned
     assert _lin(m=1, x=X + 2, path=fw.PATH_GEMV) == fw.ERR_MISALIGNED
     assert _lin(m=64, k=4000, path=fw.PATH_BATCH) == fw.ERR_INVALID_VALUE
     assert _lin(m=64, k=128, path=fw.PATH_BATCH) == fw.ERR_INVALID_VALUE

@@ -63,7 +63,7 @@ SMALL = [
     (33, 64, 512, torch.bfloat16, True, fw.PATH_BATCH),
     (300, 200, 768, torch.float16, False, fw.PATH_BATCH),
     (70, 40, 300, torch.float16, True, fw.PATH_FALLBACK),
-    (1, 77, 8200, torch.bfloat16, True, fw.PATH_SKINNY),       # 4-byte path: k % 256 != 0, 8-value tail
+    (1, 77, 8200, torch.bfloat16, True, fw.PATH_GEMV),         # 8-code GEMV: k % 256 != 0
     (3, 50, 1, torch.bfloat16, True, fw.PATH_FALLBACK),
     (5, 31, 37, torch.float16, False, fw.PATH_FALLBACK),
     (4, 128, 200, torch.bfloat16, True, fw.PATH_FALLBACK),
@@ -123,7 +123,8 @@ RING4 = [
     # (m, n, k, dtype, bias, byte offset of q, kernel the dispatcher must pick):
     # the skinny kernel's 4-byte path, every ring shape it uses, tails of 8,
     # 248, 264 and 504 columns, codes 4-, 8- and 12-byte aligned, ragged channels
-    (1, 77, 8200, torch.bfloat16, True, 0, "pipe_kernel<XR=4,CT=2,KP=1,NS=4,CB=4>"),
+    (1, 77, 8200, torch.bfloat16, True, 4, "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=4>"),
+    (4, 4096, 14344, torch.float16, True, 0, "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=4>"),
     (2, 16500, 1032, torch.bfloat16, False, 0, "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"),
     (4, 12300, 4344, torch.float16, True, 0, "pipe_kernel<XR=4,CT=4,KP=1,NS=4,CB=4>"),
     (6, 12288, 2056, torch.bfloat16, True, 0, "pipe_kernel<XR=8,CT=2,KP=1,NS=4,CB=4>"),
@@ -160,6 +161,37 @@ def test_ring4_parity(m, n, k, dtype, bias, qoff, kernel):
     fw.linear(x, q, s, b, out=y)
     torch.cuda.synchronize()
     assert_gate(y.double().cpu().numpy(), y_ref, x64, amax, f"ring4 m={m} n={n} k={k} qoff={qoff}")
+
+
+GEMV8 = [
+    # (m, n, k, dtype, bias, byte offset of q, kernel): one token on codes whose
+    # rows are only 8-byte aligned, both GEMV instances, pass tails
+    (1, 77, 8200, torch.bfloat16, True, 0, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
+    (1, 4096, 4104, torch.float16, False, 0, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
+    (1, 300, 264, torch.bfloat16, True, 0, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
+    (1, 4096, 4096, torch.bfloat16, True, 8, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
+    (1, 12300, 8200, torch.float16, True, 0, "gemv_kernel<R=4,U=2,NT=128,CH=8>"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,dtype,bias,qoff,kernel", GEMV8)
+def test_gemv8_parity(m, n, k, dtype, bias, qoff, kernel):
+    """One token, codes whose rows are only 8-byte aligned: every output against the oracle."""
+    print(f"gemv8 n={n} k={k} {dtype} bias={bias} qoff={qoff} {kernel}", flush=True)
+    case = workloads.random_case(23 * n + k, m, n, k, dtype, with_bias=bias)
+    q0, s, x, b = _prepare(case)
+    qbuf = torch.zeros(n * k + 16, dtype=torch.uint8, device=DEV)
+    q = qbuf[qoff:qoff + n * k].view(n, k)
+    q.copy_(q0)
+    act = fw.BF16 if dtype == torch.bfloat16 else fw.FP16
+    assert fw.fp8w_linear_kernel(fw.PATH_AUTO, m, n, k, act, x.data_ptr(), q.data_ptr()) == kernel
+    assert fw.linear_path(x, q) == fw.PATH_GEMV
+    assert fw.workspace_bytes(x, q) == 0
+    q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
+    y = nan_like((m, n), dtype, DEV)
+    fw.linear(x, q, s, b, out=y)
+    torch.cuda.synchronize()
+    assert_gate(y.double().cpu().numpy(), y_ref, x64, amax, f"gemv8 n={n} k={k} qoff={qoff}")
 
 
 NARROW = [
