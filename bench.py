@@ -962,12 +962,13 @@ def _short_kernel_name(full):
     name, targs = m.group(1), (m.group(2) or "")
     args = [a.strip() for a in targs[1:-1].split(",")] if targs else []
     keys = {"pipe_kernel": ("XR", "CT", "KP", "NS", "CB"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
-            "gemv_kernel": ("R", "U", "NT", "DB"), "wpipe_kernel": ("XR", "CT", "NS"), "w8a8_kernel": ("BN", "BM", "NS", "WN", "WM", "GM"),
+            "gemv_kernel": ("R", "U", "NT", "DB", "CH"), "wpipe_kernel": ("XR", "CT", "NS"), "w8a8_kernel": ("BN", "BM", "NS", "WN", "WM", "GM"),
             "gemv_grouped_kernel": ("R", "U", "NT", "DB"), "pipe_grouped_kernel": ("XR", "CT", "KP", "NS", "G"),
             "batch_kernel": ("BN", "BM", "WN", "WM", "G", "GM")}.get(name)
     if keys and len(args) == len(keys) + 1:  # first argument is the activation type
         short = f"{name}<" + ",".join(f"{kk}={v}" for kk, v in zip(keys, args[1:])) + ">"
-        return short.replace(",CB=16>", ">")  # the library's names give the load width only when it is 4
+        # the library's names give the load width only where it is not 16 bytes
+        return short.replace(",CB=16>", ">").replace(",CH=16>", ">")
     return name + targs
 
 
