@@ -121,6 +121,7 @@ def test_kernel_names():
     assert kn(A, 4, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
     assert kn(A, 1, 28672, 8200, fw.BF16, X, Q) == "gemv_kernel<R=4,U=2,NT=128,CH=8>"
     assert kn(A, 1, 4096, 4104, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"
+    assert kn(A, 1, 4096, 4112, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"   # k % 16 == 0: 16-code chunks
     assert kn(A, 1, 28672, 8200, fw.BF16, X, Q + 4) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
     assert kn(A, 4, 4096, 14344, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=4>"
     assert kn(A, 32, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2,CB=4>"

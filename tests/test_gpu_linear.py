@@ -171,6 +171,7 @@ GEMV8 = [
     (1, 300, 264, torch.bfloat16, True, 0, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
     (1, 4096, 4096, torch.bfloat16, True, 8, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
     (1, 12300, 8200, torch.float16, True, 0, "gemv_kernel<R=4,U=2,NT=128,CH=8>"),
+    (1, 1000, 4112, torch.bfloat16, True, 0, "gemv_kernel<R=2,U=2,NT=64,DB>"),  # k % 16 == 0: 16-code chunks, pass tail
 ]
 
 
