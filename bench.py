@@ -34,7 +34,8 @@ its algorithmic bytes per launch / its mean launch duration (its phase of the
 timed region divided by its launches), against 8 TB/s; "kernels" gives the
 same for both families. traffic = HBM bytes per launch from the committed
 rocprofv3 --pmc summary (profiles/step_traffic.json), reported only while the
-family's sources hash to the value recorded there.
+family's sources and the library's compile flags hash to the value recorded
+there.
 
 Every timed region is preceded by --spin-ms of the same work: the GPU raises
 its clocks only under sustained load, and the first ~10 ms run up to 15 %
@@ -81,7 +82,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_traffic.json")
 FULL_RECORD = os.path.join(ROOT, "gpurun_out", "bench_full.json")
 
 # the kernel families of the step and the sources that define each (kernel code
-# and tile choice): a change to any of them voids that family's recorded traffic
+# and tile choice): a change to any of them, or to the compile flags, voids that
+# family's recorded traffic
 FAMILIES = {"gemv_kernel": ("common.hpp", "gemv.hip"),
             "pipe_kernel": ("common.hpp", "ring.hpp", "skinny.hip")}
 
@@ -95,7 +97,9 @@ def alg_bytes(m, n, k, bias=True):
 
 
 def kernel_source_hash(family):
-    h = hashlib.sha256()
+    from fp8_weight_only_amd import _build
+    flags = [f for f in _build.CFLAGS if not f.startswith("--offload-arch") and not os.path.isabs(f) and f != "-I"]
+    h = hashlib.sha256(" ".join(flags).encode())  # the compile flags shape the code too (paths left out)
     d = os.path.join(ROOT, "fp8_weight_only_amd", "csrc")
     for f in FAMILIES[family]:
         with open(os.path.join(d, f), "rb") as fh:
