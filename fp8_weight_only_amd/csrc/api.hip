@@ -721,12 +721,14 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
         path = auto_path(m, k, x, q);
     if (path == FP8W_PATH_SKINNY && ring4_shape(m, k, x, q))
         return fp8w::skinny_kernel_name(m, n, k, false, true);
-    if (path == FP8W_PATH_GEMV && gemv8_shape(m, k, x, q))  // 16-code chunks still where k and q allow
-        return fp8w::gemv_kernel_name(n, k, k % 16 != 0 || !aligned(q, 16));
+    if (path == FP8W_PATH_GEMV && gemv8_shape(m, k, x, q))  // the chunking follows k and q's alignment
+        return fp8w::gemv_kernel_name(n, k, q);
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {
         if ((path == FP8W_PATH_GEMV && m != 1) || m < 1 || m > 32 || !fast_k(k))
             return nullptr;
-        return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(n, k) : fp8w::skinny_kernel_name(m, n, k, true);
+        // 16-code chunks: a call here needs 16-byte aligned codes
+        return path == FP8W_PATH_GEMV ? fp8w::gemv_kernel_name(n, k, nullptr)
+                                      : fp8w::skinny_kernel_name(m, n, k, true);
     }
     if (path == FP8W_PATH_BATCH)  // the workspace fp8w_linear_workspace_bytes reports exists only on the batch path
         return m >= 1 && fast_k(k) ? fp8w::batch_kernel_name(m, n, k, auto_path(m, k, x, q) == FP8W_PATH_BATCH)

@@ -23,6 +23,17 @@
 // Many small workgroups (R rows each) keep every CU streaming until the end
 // of the matrix; measured on MI355X, this shape runs within a few percent of a
 // plain streaming-read kernel of the same bytes for matrices of 58 MB and up.
+//
+// Rows that are not all 16-byte aligned (k % 8 == 0, q 8-byte aligned):
+// - k % 16 == 8: consecutive rows alternate between two alignments mod 16,
+//   and rows two apart always share one (2k % 16 == 0). gemv_shift_kernel
+//   gives each workgroup R rows of one parity and starts its 16-code chunks at
+//   the first 16-byte boundary of those rows (a shift of 0 or 8 columns, the
+//   same for the activation chunks); the columns before the shift and after
+//   the last whole chunk (fewer than 16 each) are one lane's work each.
+// - k % 16 == 0 with q 8 bytes off a 16-byte boundary: every row is off by 8;
+//   gemv_kernel runs on 8-code chunks (8-byte loads), which measured faster
+//   here than the shifted 16-code chunks.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -106,17 +117,129 @@ struct Group {
     }
 };
 
+// The same group of U passes for the shifted kernel, whose last group may be
+// partial: a chunk index past `last` loads chunk `last` (in bounds) and its
+// codes and activations are then zeroed, so that it adds exactly 0.
+template <int R, int U>
+struct ClampedGroup {
+    uint32_t code[U][R][4];
+    u32x4 xv[U][2];
+    // c0: this lane's chunk index in the group's first pass
+    __device__ __forceinline__ void load(const uint8_t* const* qr, const uint16_t* xp, int64_t c0, int nt,
+                                         int64_t last)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + (int64_t)nt * u;
+            const int64_t off = (c < last ? c : last) * 16;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const u32x4 v = load_stream16(qr[r] + off);
+                code[u][r][0] = v.x, code[u][r][1] = v.y, code[u][r][2] = v.z, code[u][r][3] = v.w;
+            }
+            xv[u][0] = load16(xp + off);
+            xv[u][1] = load16(xp + off + 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c0 + (int64_t)nt * u > last) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    code[u][r][0] = code[u][r][1] = code[u][r][2] = code[u][r][3] = 0u;
+                xv[u][0] = xv[u][1] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    template <typename A>
+    __device__ __forceinline__ void use(float* acc) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            accum_chunk<A, R, 16>(code[u], xv[u], acc);
+    }
+};
+
+// Groups 0..G-1, loaded by load(group, g) and consumed in order by
+// group.use(acc). With DB the next group's loads are issued before the current
+// group is consumed, so each wave keeps a continuous stream of requests in
+// flight instead of draining it at every group.
+template <typename A, bool DB, typename Grp, typename Load>
+__device__ __forceinline__ void stream_groups(int64_t G, Grp& ga, Grp& gb, Load load, float* acc)
+{
+    if constexpr (DB) {
+        if (G <= 0)
+            return;
+        int64_t g = 0;
+        load(ga, 0);
+        for (; g + 2 < G; g += 2) {
+            load(gb, g + 1);
+            ga.template use<A>(acc);
+            load(ga, g + 2);
+            gb.template use<A>(acc);
+        }
+        if (g + 1 < G) {
+            load(gb, g + 1);
+            ga.template use<A>(acc);
+            gb.template use<A>(acc);
+        } else {
+            ga.template use<A>(acc);
+        }
+    } else {
+        for (int64_t g = 0; g < G; ++g) {
+            load(ga, g);
+            ga.template use<A>(acc);
+        }
+    }
+}
+
+// Per-thread sums of R rows to the R outputs: one wave reduces in registers
+// and lane r stores output r; several waves meet in LDS in wave order. row(r)
+// is output r's channel; rows at or past n are not stored.
+template <typename A, int R, int NT, typename Row>
+__device__ __forceinline__ void finish_rows(const float* acc, float (*red)[R], float sc, uint16_t bi, Row row,
+                                            int64_t n, uint16_t* __restrict__ y)
+{
+    constexpr int NW = NT / kWave;
+    const int t = threadIdx.x;
+    if constexpr (NW == 1) {
+        // after the butterfly every lane holds every row's sum (no LDS, no barrier)
+        float tot = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float s = wave_sum(acc[r]);
+            if (t == r)
+                tot = s;
+        }
+        if (t < R && row(t) < n)
+            y[row(t)] = epilogue<A>(tot, sc, bi);
+        return;
+    }
+    const int lane = t & (kWave - 1), wave = t >> 6;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float s = wave_sum(acc[r]);
+        if (lane == 0)
+            red[wave][r] = s;
+    }
+    __syncthreads();
+    if (t < R && row(t) < n) {
+        float s = red[0][t];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            s += red[w][t];
+        y[row(t)] = epilogue<A>(s, sc, bi);
+    }
+}
+
 template <typename A, int R, int U, int NT, bool DB, int CH>
 __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
                                                   const float* __restrict__ scale,
                                                   const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
                                                   int64_t n, int64_t k)
 {
-    constexpr int NW = NT / kWave;
-    __shared__ float red[NW][R];
+    __shared__ float red[NT / kWave][R];
     const int t = threadIdx.x;
-    const int lane = t & (kWave - 1);
-    const int wave = t >> 6;
     const int64_t row0 = (int64_t)blockIdx.x * R;
     const int64_t nch = k / CH;  // chunks per row
 
@@ -137,38 +260,12 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
     for (int r = 0; r < R; ++r)
         acc[r] = 0.0f;
 
-    // groups of U passes; with DB the next group's loads are issued before the
-    // current group is consumed, so each wave keeps a continuous stream of
-    // requests in flight instead of draining it at every group
+    // whole groups of U passes, then predicated tail passes: only threads whose chunk exists
     constexpr int64_t GS = (int64_t)NT * U;
-    const int64_t G = nch / GS;
     Group<R, U, CH> ga, gb;
-    if constexpr (DB) {
-        int64_t g = 0;
-        if (G > 0) {
-            ga.load(qr, xp, 0, NT);
-            for (; g + 2 < G; g += 2) {
-                gb.load(qr, xp, (g + 1) * GS, NT);
-                ga.template use<A>(acc);
-                ga.load(qr, xp, (g + 2) * GS, NT);
-                gb.template use<A>(acc);
-            }
-            if (g + 1 < G) {
-                gb.load(qr, xp, (g + 1) * GS, NT);
-                ga.template use<A>(acc);
-                gb.template use<A>(acc);
-            } else {
-                ga.template use<A>(acc);
-            }
-        }
-    } else {
-        for (int64_t g = 0; g < G; ++g) {
-            ga.load(qr, xp, g * GS, NT);
-            ga.template use<A>(acc);
-        }
-    }
-    int64_t c0 = G * GS;
-    for (; c0 < nch; c0 += NT) {  // tail passes: only threads whose chunk exists
+    stream_groups<A, DB>(
+        nch / GS, ga, gb, [&](Group<R, U, CH>& grp, int64_t g) { grp.load(qr, xp, g * GS, NT); }, acc);
+    for (int64_t c0 = nch / GS * GS; c0 < nch; c0 += NT) {
         if (c0 + t < nch) {
             const int64_t off = c0 * CH;
             uint32_t code[R][CH / 4];
@@ -182,35 +279,66 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const uint16_t* __restrict__ x
             accum_chunk<A, R, CH>(code, xv, acc);
         }
     }
+    finish_rows<A, R, NT>(acc, red, sc, bi, [&](int r) { return row0 + r; }, n, y);
+}
 
-    if constexpr (NW == 1) {
-        // one wave: after the butterfly every lane holds every row's sum, and
-        // lane r stores row r (no LDS, no barrier)
-        float tot = 0.0f;
+// Rows only 8-byte aligned with k % 16 == 8 (see the top of this file).
+// Workgroups 2j and 2j + 1 take rows 2Rj .. 2Rj + 2R - 1, the even ones and
+// the odd ones: R rows two apart, which share their alignment mod 16.
+template <typename A, int R, int U, int NT, bool DB>
+__global__ __launch_bounds__(NT) void gemv_shift_kernel(const uint16_t* __restrict__ x,
+                                                        const uint8_t* __restrict__ q,
+                                                        const float* __restrict__ scale,
+                                                        const uint16_t* __restrict__ bias,
+                                                        uint16_t* __restrict__ y, int64_t n, int64_t k)
+{
+    constexpr int CH = 16;
+    __shared__ float red[NT / kWave][R];
+    const int t = threadIdx.x;
+    const int64_t base = (int64_t)(blockIdx.x >> 1) * 2 * R + (blockIdx.x & 1);
+    if (base >= n)
+        return;
+    int64_t row[R];  // rows past n: row `base`, read and discarded
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        row[r] = base + 2 * r < n ? base + 2 * r : base;
+    // columns to the first 16-byte boundary of these rows: 0 or 8
+    const int s = (int)((16 - (reinterpret_cast<uintptr_t>(q + base * k) & 15)) & 15);
+    const int64_t nch = (k - s) / CH;  // whole chunks from column s
+    const uint8_t* qr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        qr[r] = q + row[r] * k + s;
+    const uint16_t* xp = x + s;
+
+    const int64_t er = row[t % R];
+    const float sc = scale[er];
+    const uint16_t bi = bias_bits(bias, er);
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = 0.0f;
+
+    // groups of U passes, the last one possibly partial
+    constexpr int64_t GS = (int64_t)NT * U;
+    ClampedGroup<R, U> ga, gb;
+    stream_groups<A, DB>(
+        (nch + GS - 1) / GS, ga, gb,
+        [&](ClampedGroup<R, U>& grp, int64_t g) { grp.load(qr, xp, g * GS + t, NT, nch - 1); }, acc);
+
+    // columns before s and after the last whole chunk: one lane per column
+    const int64_t tail0 = s + CH * nch;
+    const int64_t c = t < s ? t : tail0 + (t - s);
+    if (t < s || c < k) {
+        const float xf = A::to_f32(x[c]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float s = wave_sum(acc[r]);
-            if (t == r)
-                tot = s;
+            float w0, w1, w2, w3;
+            decode4_f32((uint32_t)q[row[r] * k + c], w0, w1, w2, w3);
+            acc[r] = __builtin_fmaf(xf, w0, acc[r]);
         }
-        if (t < R && row0 + t < n)
-            y[row0 + t] = epilogue<A>(tot, sc, bi);
-        return;
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const float s = wave_sum(acc[r]);
-        if (lane == 0)
-            red[wave][r] = s;
-    }
-    __syncthreads();
-    if (t < R && row0 + t < n) {
-        float s = red[0][t];
-#pragma unroll
-        for (int w = 1; w < NW; ++w)
-            s += red[w][t];
-        y[row0 + t] = epilogue<A>(s, sc, bi);
-    }
+    finish_rows<A, R, NT>(acc, red, sc, bi, [&](int r) { return base + 2 * (int64_t)r; }, n, y);
 }
 
 template <typename A, int R, int U, int NT, bool DB, int CH = 16>
@@ -237,27 +365,59 @@ hipError_t launch_cfg(const void* x, int64_t k, const uint8_t* q, const float* s
 // of each CU's instruction cache.
 constexpr int64_t kLargeWeight = (int64_t)96 << 20;
 
+template <typename A, int R, int U, int NT, bool DB>
+hipError_t launch_shift(const void* x, int64_t k, const uint8_t* q, const float* scale, const void* bias, int64_t n,
+                        void* y, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(2 * ((n + 2 * R - 1) / (2 * R)))), block(NT);
+    hipLaunchKernelGGL((gemv_shift_kernel<A, R, U, NT, DB>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias),
+                       static_cast<uint16_t*>(y), n, k);
+    return hipGetLastError();
+}
+
+// Which chunking the rows allow (x is 16-byte aligned, k % 8 == 0 and q
+// 8-byte aligned on every path here).
+enum class Rows { ALIGNED, ALTERNATE, OFF8 };
+
+Rows rows_of(int64_t k, const uint8_t* q)
+{
+    if (k % 16 != 0)
+        return Rows::ALTERNATE;  // rows 2 apart share an alignment, neighbours differ by 8
+    return reinterpret_cast<uintptr_t>(q) % 16 == 0 ? Rows::ALIGNED : Rows::OFF8;
+}
+
 template <typename A>
 hipError_t launch_typed(const void* x, int64_t k, const uint8_t* q, const float* scale, const void* bias,
                         int64_t n, void* y, hipStream_t stream)
 {
-    if (k % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0) {  // rows only 8-byte aligned: 8-code chunks
-        if (n * k >= kLargeWeight)
-            return launch_cfg<A, 4, 2, 128, false, 8>(x, k, q, scale, bias, n, y, stream);
-        return launch_cfg<A, 2, 2, 64, true, 8>(x, k, q, scale, bias, n, y, stream);
+    const bool large = n * k >= kLargeWeight;
+    switch (rows_of(k, q)) {
+    case Rows::ALTERNATE:  // [28672, 8200]: 43.6 us on 8-code chunks, 39.7 shifted; [4096, 14344]: 12.7 -> 12.1
+        return large ? launch_shift<A, 4, 2, 128, false>(x, k, q, scale, bias, n, y, stream)
+                     : launch_shift<A, 2, 2, 64, true>(x, k, q, scale, bias, n, y, stream);
+    case Rows::OFF8:  // [4096, 4096] with q 8 bytes off: 5.3 us on 8-code chunks, 5.8 shifted
+        return large ? launch_cfg<A, 4, 2, 128, false, 8>(x, k, q, scale, bias, n, y, stream)
+                     : launch_cfg<A, 2, 2, 64, true, 8>(x, k, q, scale, bias, n, y, stream);
+    default:
+        return large ? launch_cfg<A, 4, 2, 128, false>(x, k, q, scale, bias, n, y, stream)
+                     : launch_cfg<A, 2, 2, 64, true>(x, k, q, scale, bias, n, y, stream);
     }
-    if (n * k >= kLargeWeight)
-        return launch_cfg<A, 4, 2, 128, false>(x, k, q, scale, bias, n, y, stream);
-    return launch_cfg<A, 2, 2, 64, true>(x, k, q, scale, bias, n, y, stream);
 }
 
 }  // namespace
 
-const char* gemv_kernel_name(int64_t n, int64_t k, bool ch8)
+const char* gemv_kernel_name(int64_t n, int64_t k, const uint8_t* q)
 {
-    if (ch8)
-        return n * k >= kLargeWeight ? "gemv_kernel<R=4,U=2,NT=128,CH=8>" : "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>";
-    return n * k >= kLargeWeight ? "gemv_kernel<R=4,U=2,NT=128>" : "gemv_kernel<R=2,U=2,NT=64,DB>";
+    const bool large = n * k >= kLargeWeight;
+    switch (rows_of(k, q)) {
+    case Rows::ALTERNATE:
+        return large ? "gemv_shift_kernel<R=4,U=2,NT=128>" : "gemv_shift_kernel<R=2,U=2,NT=64,DB>";
+    case Rows::OFF8:
+        return large ? "gemv_kernel<R=4,U=2,NT=128,CH=8>" : "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>";
+    default:
+        return large ? "gemv_kernel<R=4,U=2,NT=128>" : "gemv_kernel<R=2,U=2,NT=64,DB>";
+    }
 }
 
 hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,

@@ -18,12 +18,14 @@ hipError_t launch_quantize(const void* w, Act w_type, int64_t n, int64_t k, uint
                            hipStream_t stream);
 
 // M = 1 streaming GEMV; x 16-byte aligned; k % 16 == 0 and q 16-byte aligned
-// (16-code chunks), or k % 8 == 0 and q 8-byte aligned (8-code chunks).
+// (16-code chunks), or k % 8 == 0 and q 8-byte aligned (k % 16 == 8: 16-code
+// chunks from each row's first 16-byte boundary; else 8-code chunks).
 hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, const float* scale,
                        const void* bias, int64_t n, void* y, hipStream_t stream);
 
-// Name of the GEMV instance launch_gemv picks for this shape (ch8: 8-code chunks).
-const char* gemv_kernel_name(int64_t n, int64_t k, bool ch8 = false);
+// Name of the GEMV instance launch_gemv picks for this shape and code address
+// (16-code chunks; rows of alternating alignment; 8-code chunks).
+const char* gemv_kernel_name(int64_t n, int64_t k, const uint8_t* q);
 
 // M = 1..32 MFMA skinny GEMM; x 16-byte aligned; either k % 256 == 0 and q
 // 16-byte aligned, or (the 4-byte path, plan_ring4) k % 8 == 0, k >= 512 and q

@@ -119,8 +119,10 @@ def test_kernel_names():
     assert kn(A, 16, 12288, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=3,KP=1,NS=4>"
     assert kn(fw.PATH_SKINNY, 1, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"
     assert kn(A, 4, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
-    assert kn(A, 1, 28672, 8200, fw.BF16, X, Q) == "gemv_kernel<R=4,U=2,NT=128,CH=8>"
-    assert kn(A, 1, 4096, 4104, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"
+    assert kn(A, 1, 28672, 8200, fw.BF16, X, Q) == "gemv_shift_kernel<R=4,U=2,NT=128>"  # k % 16 == 8
+    assert kn(A, 1, 4096, 4104, fw.BF16, X, Q) == "gemv_shift_kernel<R=2,U=2,NT=64,DB>"
+    assert kn(A, 1, 4096, 4096, fw.BF16, X, Q + 8) == "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"  # every row 8 bytes off
+    assert kn(A, 1, 28672, 8192, fw.BF16, X, Q + 8) == "gemv_kernel<R=4,U=2,NT=128,CH=8>"
     assert kn(A, 1, 4096, 4112, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"   # k % 16 == 0: 16-code chunks
     assert kn(A, 1, 28672, 8200, fw.BF16, X, Q + 4) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
     assert kn(A, 4, 4096, 14344, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=4>"

@@ -165,12 +165,18 @@ def test_ring4_parity(m, n, k, dtype, bias, qoff, kernel):
 
 GEMV8 = [
     # (m, n, k, dtype, bias, byte offset of q, kernel): one token on codes whose
-    # rows are only 8-byte aligned, both GEMV instances, pass tails
-    (1, 77, 8200, torch.bfloat16, True, 0, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
-    (1, 4096, 4104, torch.float16, False, 0, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
-    (1, 300, 264, torch.bfloat16, True, 0, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
-    (1, 4096, 4096, torch.bfloat16, True, 8, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),
-    (1, 12300, 8200, torch.float16, True, 0, "gemv_kernel<R=4,U=2,NT=128,CH=8>"),
+    # rows are only 8-byte aligned, every GEMV instance, pass tails
+    (1, 77, 8200, torch.bfloat16, True, 0, "gemv_shift_kernel<R=2,U=2,NT=64,DB>"),   # k % 16 == 8: rows alternate
+    (1, 77, 8200, torch.bfloat16, True, 8, "gemv_shift_kernel<R=2,U=2,NT=64,DB>"),   # row 0 the shifted one
+    (1, 4096, 4104, torch.float16, False, 0, "gemv_shift_kernel<R=2,U=2,NT=64,DB>"),
+    (1, 300, 264, torch.bfloat16, True, 0, "gemv_shift_kernel<R=2,U=2,NT=64,DB>"),   # 16 chunks: one partial group
+    (1, 1, 1032, torch.float16, True, 8, "gemv_shift_kernel<R=2,U=2,NT=64,DB>"),     # one row: odd workgroup idle
+    (1, 5, 4360, torch.bfloat16, False, 0, "gemv_shift_kernel<R=2,U=2,NT=64,DB>"),   # odd n: a row pair short
+    (1, 12300, 8200, torch.float16, True, 0, "gemv_shift_kernel<R=4,U=2,NT=128>"),
+    (1, 12301, 8200, torch.bfloat16, False, 8, "gemv_shift_kernel<R=4,U=2,NT=128>"),
+    (1, 4096, 4096, torch.bfloat16, True, 8, "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"),  # every row 8 bytes off
+    (1, 300, 280, torch.float16, True, 8, "gemv_shift_kernel<R=2,U=2,NT=64,DB>"),
+    (1, 12300, 8192, torch.float16, True, 8, "gemv_kernel<R=4,U=2,NT=128,CH=8>"),
     (1, 1000, 4112, torch.bfloat16, True, 0, "gemv_kernel<R=2,U=2,NT=64,DB>"),  # k % 16 == 0: 16-code chunks, pass tail
 ]
 
