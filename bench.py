@@ -353,16 +353,22 @@ def mfma_issued_flops(kernel, m, n, k):
     segments per instruction of which one is kept, so tokens count as
     MP*MT*SEG. None for other kernels."""
     import re
-    mm = re.match(r"pipe(?:_grouped)?_kernel<XR=(\d+),CT=(\d+),KP=\d+,NS=\d+(,CB=4)?>", kernel or "")
+    mm = re.match(r"pipe(?:_grouped)?_kernel<XR=(\d+),CT=(\d+),KP=\d+,NS=\d+(?:,CB=(\d+))?>", kernel or "")
     if mm:
         xr, ct = int(mm.group(1)), int(mm.group(2))
+        cb = int(mm.group(3) or 16)
         mt = 2 if xr > 16 else 1
         chans = 16 * ct * math.ceil(n / (16 * ct))
-        kr = k
-        if mm.group(3):  # the 4-byte path: the ring's columns (an even number of stages); the tail is fp32
-            kr = k - k % 256
+        cols = k
+        if cb != 16:  # the ring's columns (an even number of stages), then 32-column MFMA blocks for the rest
+            room = k - 8 if cb == 8 and k % 16 == 8 else k
+            kr = room - room % 256
             kr -= 256 if (kr // 256) % 2 else 0
-        return 2.0 * kr * chans * 16 * mt, 16 * mt
+            cols = kr + 32 * math.ceil((k - kr) / 32)
+            if cb == 8:  # workgroups of one row parity, a pair per 32 * CT channels; an odd one past n exits
+                pairs = math.ceil(n / (32 * ct))
+                chans = 16 * ct * (2 * pairs - (1 if 32 * ct * (pairs - 1) + 1 >= n else 0))
+        return 2.0 * cols * chans * 16 * mt, 16 * mt
     mm = re.match(r"seg_kernel<SEG=(\d+),T=(\d+),W=\d+,U=\d+,MT=(\d+)>", kernel or "")
     if mm:
         seg, t, mt = int(mm.group(1)), int(mm.group(2)), int(mm.group(3))

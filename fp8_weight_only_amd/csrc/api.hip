@@ -83,7 +83,7 @@ bool fast_pointers(const void* x, const uint8_t* q)
     return aligned(x, 16) && aligned(q, 16);
 }
 
-// The skinny kernel's 4-byte path: 1..32 tokens whose codes the 16-byte
+// The skinny kernel's unaligned-code path: 1..32 tokens whose codes the 16-byte
 // kernels cannot load (k not a multiple of 256, or q not 16-byte aligned),
 // with k % 8 == 0, k >= 512, q 4-byte and x 16-byte aligned.
 bool ring4_shape(int64_t m, int64_t k, const void* x, const uint8_t* q)
@@ -113,7 +113,7 @@ int auto_path(int64_t m, int64_t k, const void* x, const uint8_t* q)
     return ring4_shape(m, k, x, q) ? FP8W_PATH_SKINNY : FP8W_PATH_FALLBACK;
 }
 
-// The grouped linear: the same split by tokens, without the 4-byte path.
+// The grouped linear: the same split by tokens, without the unaligned-code path.
 int auto_path_grouped(int64_t m, int64_t k, const void* x, const uint8_t* q)
 {
     if (!fast_k(k) || !fast_pointers(x, q) || m < 1)
@@ -121,7 +121,7 @@ int auto_path_grouped(int64_t m, int64_t k, const void* x, const uint8_t* q)
     return m == 1 ? FP8W_PATH_GEMV : m <= 32 ? FP8W_PATH_SKINNY : FP8W_PATH_BATCH;
 }
 
-// Workspace bytes the skinny path uses for this call (the 4-byte path: none).
+// Workspace bytes the skinny path uses for this call (the unaligned-code path: none).
 size_t skinny_workspace(int64_t m, int64_t n, int64_t k, const void* x, const uint8_t* q)
 {
     return ring4_shape(m, k, x, q) ? 0 : fp8w::skinny_workspace_bytes(m, n, k);
@@ -182,7 +182,7 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
         }
     } else if (path == FP8W_PATH_SKINNY) {
         // the 16-byte kernels (k % 256 == 0, x and q 16-byte aligned) or the
-        // 4-byte path (k % 8 == 0, k >= 512, x 16-byte and q 4-byte aligned)
+        // unaligned-code path (k % 8 == 0, k >= 512, x 16-byte and q 4-byte aligned)
         if (m > 32)
             return FP8W_ERR_INVALID_VALUE;
         if (!(fast_k(k) && fast_pointers(x, q))) {
@@ -720,7 +720,7 @@ const char* fp8w_linear_kernel(int path, int64_t m, int64_t n, int64_t k, fp8w_d
     if (path == FP8W_PATH_AUTO)
         path = auto_path(m, k, x, q);
     if (path == FP8W_PATH_SKINNY && ring4_shape(m, k, x, q))
-        return fp8w::skinny_kernel_name(m, n, k, false, true);
+        return fp8w::skinny_kernel_name(m, n, k, false, true, q);
     if (path == FP8W_PATH_GEMV && gemv8_shape(m, k, x, q))  // the chunking follows k and q's alignment
         return fp8w::gemv_kernel_name(n, k, q);
     if (path == FP8W_PATH_GEMV || path == FP8W_PATH_SKINNY) {

@@ -28,10 +28,9 @@ hipError_t launch_gemv(const void* x, Act act, int64_t k, const uint8_t* q, cons
 const char* gemv_kernel_name(int64_t n, int64_t k, const uint8_t* q);
 
 // M = 1..32 MFMA skinny GEMM; x 16-byte aligned; either k % 256 == 0 and q
-// 16-byte aligned, or (the 4-byte path, plan_ring4) k % 8 == 0, k >= 512 and q
-// 4-byte aligned. Shapes that split k use ws (fp32 partial sums, 16-byte
+// 16-byte aligned, or (plan_ring4) k % 8 == 0, k >= 512 and q 4-byte aligned. Shapes that split k use ws (fp32 partial sums, 16-byte
 // aligned, not overlapping any operand) when ws_bytes >= skinny_workspace_bytes
-// (m, n, k); otherwise they take the single-pass plan. The 4-byte path never
+// (m, n, k); otherwise they take the single-pass plan. The unaligned-code path never
 // splits.
 hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uint8_t* q, const float* scale,
                          const void* bias, int64_t n, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -40,17 +39,22 @@ hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uin
 size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 // Name of the kernel and tile launch_skinny picks for this shape (a
-// thread-local string; for tests and measurement reports); ring4: the 4-byte path.
-const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace, bool ring4 = false);
+// thread-local string; for tests and measurement reports); ring4: the path for
+// codes the 16-byte kernels cannot load, at address q.
+const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace, bool ring4 = false,
+                               const uint8_t* q = nullptr);
 
-// The 4-byte path's plan: ok when it takes the shape (1..32 tokens, k % 8 == 0,
-// k >= 512); the ring covers kr columns, the rest is the fp32 tail.
+// The plan for codes the 16-byte kernels cannot load: ok when it takes the
+// shape (1..32 tokens, k % 8 == 0, k >= 512); the ring covers kr columns, the
+// other k - kr are register-operand MFMAs; cb is the rows' alignment the
+// kernel is built for (8: 16-byte loads from a shift of 0 or 8 columns; 4:
+// 4-byte loads).
 struct Ring4Plan {
     bool ok;
-    int xr, ct, kp, ns;
+    int xr, ct, kp, ns, cb;
     int64_t kr;
 };
-Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k);
+Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k, const uint8_t* q);
 
 // The skinny kernel for layers of fewer than 8192 channels (narrow_kernel):
 // activation fragments in VGPRs, codes alone in per-wave LDS rings. plan_narrow

@@ -182,11 +182,12 @@ __global__ __launch_bounds__(W* kWave) void seg_kernel(
 // XR activation rows are fetched (m <= XR; MFMA columns past XR read row XR - 1
 // and are discarded); CT channel tiles of 16 and KP k-parts make the
 // workgroup's CT * KP waves; NS stage buffers; one stage is 256 k per wave.
-// CB is the bytes of codes one lane loads per instruction: 16, or 4 for rows
-// that are only 4-byte aligned (k not a multiple of 16, or an unaligned q).
+// CB is the alignment of the code rows the kernel is built for: 16 (16-byte
+// loads), 8 (rows 8-byte aligned: 16-byte loads from each row's first 16-byte
+// boundary, a workgroup's rows all of one parity) or 4 (4-byte loads).
 template <int XR, int CT, int KP, int NS, int CB = 16>
 struct PipeCfg {
-    static_assert(CB == 16 || CB == 4, "code load width");
+    static_assert(CB == 16 || CB == 8 || CB == 4, "code row alignment");
     static_assert(XR % 2 == 0 && XR >= 2 && XR <= 32, "activation rows");
     static_assert(NS >= 2 && NS <= 4, "stages");
     static constexpr int MT = XR > 16 ? 2 : 1;      // 16-token MFMA tiles
@@ -196,12 +197,12 @@ struct PipeCfg {
     static constexpr int STAGE = W * CODE + KP * XPART;
     static constexpr int XLOADS = (XR / 2) * KP;    // 1 KB activation loads per stage
     static constexpr int XPW = (XLOADS + W - 1) / W;  // per wave; duplicates fill the last round
-    static constexpr int CLOADS = CODE / (kWave * CB);  // code load instructions per wave and stage
+    static constexpr int CLOADS = CODE / (kWave * (CB == 4 ? 4 : 16));  // code loads per wave and stage
     static constexpr int LOADS = CLOADS + XPW;      // load instructions per wave and stage
     static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
 };
 
-// Eight codes as two 4-byte loads (rows of the 4-byte path are 4-byte aligned).
+// Eight codes as two 4-byte loads (the rows these blocks read may be only 4-byte aligned).
 __device__ __forceinline__ u32x2 load_codes8(const uint8_t* p)
 {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
@@ -212,13 +213,25 @@ template <typename A, int XR, int CT, int KP, int NS, int CB = 16>
 struct Pipe {
     using C = PipeCfg<XR, CT, KP, NS, CB>;
     static constexpr int MT = C::MT;
+    // CB == 8: the workgroup's channels are n0, n0 + 2, .. (one parity), which
+    // share their alignment mod 16 (2k % 16 == 0)
+    static constexpr int RS = CB == 8 ? 2 : 1;
 
-    const uint16_t* x;
+    const uint16_t* x;  // CB == 8: both advanced by the workgroup's shift sh
     const uint8_t* q;
     int m;
     int64_t n, k, n0;
     int64_t S, rot;  // stages; this workgroup's first stage
+    int64_t T, sh;   // columns outside the ring (k - kr); columns before the ring (0, or 8 for CB == 8)
     int lane, wave, ct, kp;
+
+    // channel c of the workgroup (16 ct + r), clamped to a real row of the
+    // same alignment; results of clamped rows are never stored
+    __device__ __forceinline__ int64_t chan(int c) const
+    {
+        const int64_t ch = n0 + (int64_t)RS * c;
+        return ch < n ? ch : (CB == 8 ? n0 : n - 1);
+    }
 
     // Stage s into buf. Workgroups start at different stages (rot) and wrap
     // around, so that the workgroups resident on one XCD at a time read all
@@ -236,13 +249,12 @@ struct Pipe {
         int64_t sr = s + rot;  // s < S and rot < S
         sr = sr < S ? sr : sr - S;
         const int64_t kb = sr * (KP * 256);
-        if constexpr (CB == 16) {
+        if constexpr (CB != 4) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * j + (lane >> 4);
                 const int chunk = ((lane & 15) - r) & 15;
-                int64_t row = n0 + 16 * ct + r;
-                row = row < n ? row : n - 1;
+                const int64_t row = chan(16 * ct + r);
                 const uint8_t* src = q + row * k + kb + kp * 256 + chunk * 16;
                 __builtin_amdgcn_global_load_lds((const void*)src, FP8W_LDS(buf + wave * C::CODE + j * 1024), 16,
                                                  0, 2 /* non-temporal */);
@@ -253,8 +265,7 @@ struct Pipe {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int chunk = ((lane >> 2) - r) & 15;
-                int64_t row = n0 + 16 * ct + r;
-                row = row < n ? row : n - 1;
+                const int64_t row = chan(16 * ct + r);
                 const uint8_t* src = q + row * k + kb + kp * 256 + chunk * 16 + 4 * (lane & 3);
                 __builtin_amdgcn_global_load_lds((const void*)src, FP8W_LDS(buf + wave * C::CODE + r * 256), 4, 0,
                                                  2 /* non-temporal */);
@@ -317,27 +328,29 @@ struct Pipe {
         }
     }
 
-    // k tail block b: columns kr + 32 b .. + 31; lane (i, g) takes the eight
-    // at + 8 g, as the A (codes of row i of each tile it holds) and B (token i)
-    // operands of one MFMA. Groups at or past k load nothing and stay zero in
-    // both operands. (A tail exists only without a k split, so q and x here are
-    // the rows' starts.)
+    // Block b of the columns outside the ring (the T = k - kr columns before
+    // and after it, in that order: the sh before, then kr + sh .. k - 1): 32
+    // of them; lane (i, g) takes the eight at 32 b + 8 g, as the A (codes of
+    // row i of each tile it holds) and B (token i) operands of one MFMA.
+    // Groups at or past T load nothing and stay zero in both operands. (These
+    // columns exist only without a k split; q and x point at column sh of the
+    // rows, so column c sits at offset c - sh.)
     template <int NT>
     __device__ __forceinline__ void tail_load(int64_t kr, int b, u32x2 (&code)[NT], u32x4 (&xv)[MT]) const
     {
         const int i = lane & 15, g = lane >> 4;
-        const int64_t c = kr + 32 * b + 8 * g;
+        const int64_t v = 32 * b + 8 * g;
+        const int64_t c = (v < sh ? v : kr + v) - sh;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             code[t] = u32x2{0u, 0u};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             xv[mt] = u32x4{0u, 0u, 0u, 0u};
-        if (c < k) {
+        if (v < T) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                int64_t ch = n0 + 16 * (NT == 1 ? ct : t) + i;
-                ch = ch < n ? ch : n - 1;
+                const int64_t ch = chan(16 * (NT == 1 ? ct : t) + i);
                 code[t] = load_codes8(q + ch * k + c);
             }
 #pragma unroll
@@ -406,11 +419,14 @@ __device__ __forceinline__ f32x4 kSlicedSum(f32x4 (*part)[NACC][kWave], int ct, 
     }
 }
 
-// The ring covers k columns 0 .. kr - 1 (kr / splits a multiple of KP * 256 *
-// NS); k is the row stride. Columns kr .. k - 1 (the 4-byte path only, a
-// multiple of 8 below 512, no split) are further MFMAs on operands loaded
-// straight into registers (Pipe::tail_load), 32 columns each, dealt to the
-// waves in turn; each wave fetches its first before the ring starts.
+// The ring covers kr columns (kr / splits a multiple of KP * 256 * NS) from
+// column sh: 0, or for CB == 8 the columns to the first 16-byte boundary of
+// the workgroup's rows (0 or 8); k is the row stride. The other k - kr columns
+// (CB 8 and 4 only, a multiple of 8 below 512, no split) are further MFMAs on
+// operands loaded straight into registers (Pipe::tail_load), 32 columns each,
+// dealt to the waves in turn; each wave fetches its first before the ring
+// starts. CB == 8: workgroups 2j and 2j + 1 own the even and the odd channels
+// of 32 CT.
 template <typename A, int XR, int CT, int KP, int NS, int CB>
 __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
@@ -437,7 +453,17 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     p.wave = threadIdx.x / kWave;
     p.ct = p.wave % CT;
     p.kp = p.wave / CT;
-    p.n0 = (int64_t)blockIdx.x * (16 * CT);
+    p.n0 = CB == 8 ? (int64_t)(blockIdx.x >> 1) * (32 * CT) + (blockIdx.x & 1) : (int64_t)blockIdx.x * (16 * CT);
+    p.T = k - kr;
+    p.sh = 0;
+    if constexpr (CB == 8) {
+        if (p.n0 >= n)  // the odd workgroup of the last pair when n is short
+            return;
+        // columns to the first 16-byte boundary of the workgroup's rows
+        p.sh = (int64_t)((16 - (reinterpret_cast<uintptr_t>(q + p.n0 * k) & 15)) & 15);
+        p.x += p.sh;
+        p.q += p.sh;
+    }
 
     constexpr int NACC = P::NACC;
     f32x4 acc[NACC][MT];
@@ -453,8 +479,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     uint16_t bi[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        int64_t ch = p.n0 + 16 * p.ct + 4 * (p.lane >> 4) + r;
-        ch = ch < n ? ch : n - 1;
+        const int64_t ch = p.chan(16 * p.ct + 4 * (p.lane >> 4) + r);
         sc[r] = scale[ch];
         bi[r] = bias_bits(bias, ch);
     }
@@ -464,10 +489,10 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     constexpr int NT = P::NACC;
     const int bstep = P::kSliced ? C::W : KP;
     const int tb0 = P::kSliced ? p.wave : p.kp;
-    const int nblk = CB == 4 ? (int)((k - kr + 31) / 32) : 0;
+    const int nblk = CB != 16 ? (int)((p.T + 31) / 32) : 0;
     u32x2 tcode[NT];
     u32x4 txv[MT];
-    if constexpr (CB == 4) {
+    if constexpr (CB != 16) {
         if (tb0 < nblk)
             p.tail_load(kr, tb0, tcode, txv);
     }
@@ -481,7 +506,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     // measured 0.2-0.4 us faster at 16-22 tokens on [14336 x 4096]; for CT = 3
     // they were 0.2-0.6 us slower
     run_ring<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
-    if constexpr (CB == 4) {
+    if constexpr (CB != 16) {
         if (tb0 < nblk) {
             p.tail_use(tcode, txv, acc);
             for (int b = tb0 + bstep; b < nblk; b += 2 * bstep) {  // two blocks' loads in flight at a time
@@ -522,7 +547,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
             float* o = part_out + ((int64_t)blockIdx.y * m + tok) * n;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
+                const int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;  // a split runs only with CB == 16
                 if (ch < n)
                     o[ch] = v[r];
             }
@@ -530,7 +555,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t ch = p.n0 + 16 * p.ct + 4 * g + r;
+            const int64_t ch = p.n0 + (int64_t)P::RS * (16 * p.ct + 4 * g + r);
             if (ch < n)
                 y[(int64_t)tok * n + ch] = epilogue<A>(v[r], sc[r], bi[r]);
         }
@@ -583,10 +608,13 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
     // positive number of NS-stage groups
     if (splits < 1 || kr <= 0 || kr > k || kr % ((int64_t)splits * KP * 256 * NS) != 0)
         return hipErrorInvalidValue;
-    // a tail only without a split, in whole 8-column blocks; rows as wide as the loads
-    if ((kr != k && (splits != 1 || (k - kr) % 8 != 0)) || k % 8 != 0 || (CB == 16 && k % 16 != 0))
+    // a tail only without a split, in whole 8-column blocks; rows as wide as the
+    // loads; CB == 8: room for a shift of 8 columns before the ring
+    if ((kr != k && (splits != 1 || (k - kr) % 8 != 0)) || k % 8 != 0 || (CB == 16 && k % 16 != 0) ||
+        (CB == 8 && (splits != 1 || kr > k - 8 || reinterpret_cast<uintptr_t>(q) % 8 != 0)))
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((n + 16 * CT - 1) / (16 * CT)), (unsigned)splits), block(CT * KP * kWave);
+    const unsigned gx = CB == 8 ? (unsigned)(2 * ((n + 32 * CT - 1) / (32 * CT))) : (unsigned)((n + 16 * CT - 1) / (16 * CT));
+    const dim3 grid(gx, (unsigned)splits), block(CT * KP * kWave);
     hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS, CB>), grid, block, 0, stream,
                        static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias),
                        static_cast<uint16_t*>(y), m, n, k, kr, splits > 1 ? part : nullptr);
@@ -705,31 +733,43 @@ hipError_t launch_pipe_xr(const SkinnyPlan& p, const void* x, int m, int64_t k, 
     }
 }
 
-template <typename A, int XR>
+template <typename A, int XR, int CB>
 hipError_t launch_ring4_xr(const Ring4Plan& p, const void* x, int m, int64_t k, const uint8_t* q,
                            const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
 {
     const int key = p.ct * 100 + p.kp * 10 + p.ns;
     const int64_t kr = p.kr;
     switch (key) {
-    case 412: return launch_pipe<A, XR, 4, 1, 2, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
-    case 414: return launch_pipe<A, XR, 4, 1, 4, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
-    case 212: return launch_pipe<A, XR, 2, 1, 2, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
-    case 214: return launch_pipe<A, XR, 2, 1, 4, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
-    case 122: return launch_pipe<A, XR, 1, 2, 2, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 412: return launch_pipe<A, XR, 4, 1, 2, CB>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 414: return launch_pipe<A, XR, 4, 1, 4, CB>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 212: return launch_pipe<A, XR, 2, 1, 2, CB>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 214: return launch_pipe<A, XR, 2, 1, 4, CB>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+    case 122: return launch_pipe<A, XR, 1, 2, 2, CB>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
     case 124:
         if constexpr (XR <= 16)  // 32 rows: 16 activation loads per wave, too many for four stages
-            return launch_pipe<A, XR, 1, 2, 4, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+            return launch_pipe<A, XR, 1, 2, 4, CB>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
         return hipErrorInvalidValue;
     case 222:
     case 224:
         if constexpr (XR <= 16) {
             if (key == 222)
-                return launch_pipe<A, XR, 2, 2, 2, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
-            return launch_pipe<A, XR, 2, 2, 4, 4>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+                return launch_pipe<A, XR, 2, 2, 2, CB>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
+            return launch_pipe<A, XR, 2, 2, 4, CB>(x, m, k, q, scale, bias, n, y, stream, 1, nullptr, kr);
         }
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename A, int CB>
+hipError_t launch_ring4_cb(const Ring4Plan& p, const void* x, int m, int64_t k, const uint8_t* q,
+                           const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
+{
+    switch (p.xr) {
+    case 4: return launch_ring4_xr<A, 4, CB>(p, x, m, k, q, scale, bias, n, y, stream);
+    case 8: return launch_ring4_xr<A, 8, CB>(p, x, m, k, q, scale, bias, n, y, stream);
+    case 16: return launch_ring4_xr<A, 16, CB>(p, x, m, k, q, scale, bias, n, y, stream);
+    default: return launch_ring4_xr<A, 32, CB>(p, x, m, k, q, scale, bias, n, y, stream);
     }
 }
 
@@ -737,16 +777,12 @@ template <typename A>
 hipError_t launch_ring4(const void* x, int64_t m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
                         int64_t n, void* y, hipStream_t stream)
 {
-    const Ring4Plan p = plan_ring4(m, n, k);
+    const Ring4Plan p = plan_ring4(m, n, k, q);
     if (!p.ok)
         return hipErrorInvalidValue;
-    const int mi = (int)m;
-    switch (p.xr) {
-    case 4: return launch_ring4_xr<A, 4>(p, x, mi, k, q, scale, bias, n, y, stream);
-    case 8: return launch_ring4_xr<A, 8>(p, x, mi, k, q, scale, bias, n, y, stream);
-    case 16: return launch_ring4_xr<A, 16>(p, x, mi, k, q, scale, bias, n, y, stream);
-    default: return launch_ring4_xr<A, 32>(p, x, mi, k, q, scale, bias, n, y, stream);
-    }
+    if (p.cb == 8)
+        return launch_ring4_cb<A, 8>(p, x, (int)m, k, q, scale, bias, n, y, stream);
+    return launch_ring4_cb<A, 4>(p, x, (int)m, k, q, scale, bias, n, y, stream);
 }
 
 template <typename A>
@@ -781,24 +817,20 @@ hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, c
 
 }  // namespace
 
-// The 4-byte path: codes whose rows are only 4-byte aligned (k a multiple of 8
-// but not of 256, or q not 16-byte aligned; k >= 512), 1..32 tokens.
-// pipe_kernel with 4-byte code loads (measured on MI355X as fast as 16-byte
-// ones for the same ring: 9.98 against 9.84 us over [14336, 4096], 36.6
-// against 35.9 over [28672, 8192]) covers kr = k rounded down to an even
-// number of 256-column stages; the remaining columns (fewer than 512, a
-// multiple of 8) are the k tail, further MFMAs on register operands. Channel
-// tiles and k-parts follow plan_skinny for kr without a split (with the
-// exceptions below). Activation rows 4, 8, 16 or 32. One token with 8-byte
-// aligned codes takes the GEMV's 8-code chunks instead (fp8w_linear's dispatch).
-Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k)
+namespace {
+
+// The ring's columns and tile for 1..32 tokens when the ring may cover at most
+// `room` columns of each row (k, or k - 8 to leave room for a shift).
+Ring4Plan plan_ring4_within(int64_t m, int64_t n, int64_t k, int64_t room)
 {
     Ring4Plan r{};
     if (m < 1 || m > 32 || n < 1 || k < 512 || k % 8 != 0)
         return r;
-    int64_t kr = k - k % 256;
+    int64_t kr = room - room % 256;
     if ((kr / 256) % 2 != 0)
         kr -= 256;
+    if (kr <= 0)
+        return r;
     const SkinnyPlan p = plan_skinny(m < 2 ? 2 : m, n, kr, false);
     // where plan_skinny picks seg_kernel (under 8192 channels, up to 8 tokens):
     // one tile and two k-parts, so that a 4096-channel layer still has 256
@@ -827,6 +859,42 @@ Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k)
     r.kp = kp;
     r.ns = ns;
     r.kr = kr;
+    return r;
+}
+
+}  // namespace
+
+// The skinny path for codes the 16-byte kernels cannot load (k a multiple of
+// 8 but not of 256, or q not 16-byte aligned; k >= 512), 1..32 tokens:
+// pipe_kernel over kr columns, an even number of 256-column stages; the other
+// columns (at most 512, a multiple of 8) are further MFMAs on register
+// operands. cb = 8 (rows 16-byte aligned, or k % 16 == 8 with q 8-byte
+// aligned, so that neighbouring rows alternate between two alignments):
+// 16-byte loads from the first 16-byte boundary of each workgroup's rows (with
+// k % 16 == 8 the ring leaves room for a shift of 8 columns). Measured on
+// MI355X against 4-byte loads: [28672, 8200] at 4 / 8 / 32 tokens 46.4 / 47.2
+// / 54.4 us against 50.3 / 49.3 / 79.2, [4096, 14344] at 4 tokens 13.3 against
+// 22.3, [12288, 2056] at 24 tokens 15.3 against 21.2. Otherwise (cb = 4)
+// 4-byte loads: with every row 8 bytes off a 16-byte boundary the shift would
+// leave up to 512 columns to the register operands ([4096, 4096] with q 8
+// bytes off at 8 tokens: 15.7 us shifted, 9.7 with 4-byte loads). 4-byte loads
+// measured as fast as 16-byte ones on aligned rows (9.98 against 9.84 us over
+// [14336, 4096]) but touch three 128-byte lines per 256-byte segment of a row
+// that is not 16-byte aligned instead of two. Channel tiles and k-parts follow
+// plan_skinny for kr without a split (with the exceptions in
+// plan_ring4_within). Activation rows 4, 8, 16 or 32. One token with 8-byte
+// aligned codes takes the GEMV instead (fp8w_linear's dispatch).
+Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k, const uint8_t* q)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(q);
+    if (a % 8 == 0 && (k % 16 == 8 || a % 16 == 0)) {
+        Ring4Plan r = plan_ring4_within(m, n, k, k % 16 == 8 ? k - 8 : k);
+        r.cb = 8;
+        if (r.ok)
+            return r;
+    }
+    Ring4Plan r = plan_ring4_within(m, n, k, k);
+    r.cb = 4;
     return r;
 }
 
@@ -865,7 +933,7 @@ hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uin
         return hipSuccess;
     if (m > 32)
         return hipErrorInvalidValue;
-    if (k % 256 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0) {  // rows only 4-byte aligned
+    if (k % 256 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0) {  // codes the 16-byte kernels cannot load
         if (reinterpret_cast<uintptr_t>(q) % 4 != 0 || reinterpret_cast<uintptr_t>(x) % 16 != 0)
             return hipErrorInvalidValue;
         if (act == Act::BF16)
@@ -882,14 +950,14 @@ hipError_t launch_skinny(const void* x, Act act, int64_t m, int64_t k, const uin
     return hipErrorInvalidValue;
 }
 
-const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace, bool ring4)
+const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_workspace, bool ring4, const uint8_t* q)
 {
     thread_local char name[96];
     if (ring4) {
-        const Ring4Plan p = plan_ring4(m, n, k);
+        const Ring4Plan p = plan_ring4(m, n, k, q);
         if (!p.ok)
             return nullptr;
-        snprintf(name, sizeof name, "pipe_kernel<XR=%d,CT=%d,KP=%d,NS=%d,CB=4>", p.xr, p.ct, p.kp, p.ns);
+        snprintf(name, sizeof name, "pipe_kernel<XR=%d,CT=%d,KP=%d,NS=%d,CB=%d>", p.xr, p.ct, p.kp, p.ns, p.cb);
         return name;
     }
     const NarrowPlan np = plan_narrow(m, n, k);

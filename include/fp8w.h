@@ -115,11 +115,14 @@ FP8W_API fp8w_status_t fp8w_quantize(const void* w, fp8w_dtype_t w_dtype, int64_
  * Dispatch (fp8w_linear_path): the fast kernels take k % 256 == 0 with x, q
  * 16-byte aligned: m == 1 the GEMV, 2 <= m <= 32 the skinny MFMA kernel, m > 32
  * the batch GEMM (which decodes the codes in its main loop, no workspace).
- * Where the codes' rows are only 8- or 4-byte aligned (k % 256 != 0 or q not
- * 16-byte aligned), with k % 8 == 0 and x 16-byte aligned: m == 1 takes the
- * GEMV with 8-code loads when k >= 256 and q is 8-byte aligned; otherwise
+ * Where the fast kernels cannot load the codes (k % 256 != 0 or q not 16-byte
+ * aligned), with k % 8 == 0 and x 16-byte aligned: m == 1 takes the GEMV when
+ * k >= 256 and q is 8-byte aligned (16-code chunks from each row's first
+ * 16-byte boundary when k % 16 == 8, else 8-code chunks); otherwise
  * 1 <= m <= 32 takes the skinny kernel when k >= 512 and q is 4-byte aligned
- * (4-byte code loads; the columns past a multiple of 512 as extra MFMAs; no
+ * (16-byte loads from the first 16-byte boundary of each workgroup's rows
+ * where q is 8-byte aligned and the rows are 16-byte aligned or alternate,
+ * else 4-byte loads; the columns outside its ring as extra MFMAs; no
  * workspace). Everything else takes the fallback. Results of different paths and plans agree to
  * within fp32 summation-order rounding; a given call is deterministic.
  * Asynchronous; a failed launch returns FP8W_ERR_HIP.
@@ -135,8 +138,8 @@ FP8W_API fp8w_status_t fp8w_linear(const void* x, fp8w_dtype_t act_dtype, int64_
  * k % 256 == 0 (FP8W_ERR_INVALID_VALUE otherwise) and 16-byte aligned x and q
  * (FP8W_ERR_MISALIGNED otherwise); FP8W_PATH_GEMV also takes k % 8 == 0,
  * k >= 256 with x 16-byte and q 8-byte aligned, and FP8W_PATH_SKINNY
- * k % 8 == 0, k >= 512 with x 16-byte and q 4-byte aligned (the 8- and 4-byte
- * shapes of fp8w_linear's dispatch). FP8W_PATH_FALLBACK takes any shape and needs
+ * k % 8 == 0, k >= 512 with x 16-byte and q 4-byte aligned (the shapes
+ * fp8w_linear's dispatch sends there when the fast kernels cannot load the codes). FP8W_PATH_FALLBACK takes any shape and needs
  * n * k * element_size(act_dtype) bytes of workspace.
  */
 FP8W_API fp8w_status_t fp8w_linear_with_path(const void* x, fp8w_dtype_t act_dtype, int64_t m, int64_t k,

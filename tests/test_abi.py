@@ -68,17 +68,17 @@ def test_path_selection():
     assert p(1, 300, 264, fw.BF16, X, Q, Y) == fw.PATH_GEMV             # 8-code GEMV from k = 256
     assert p(2, 300, 264, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # 4-byte skinny path from k = 512
     assert p(32, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_SKINNY
-    assert p(33, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK     # 4-byte path: m <= 32 only
+    assert p(33, 28672, 8200, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK     # unaligned-code path: m <= 32 only
     assert p(4, 100, 520, fw.BF16, X, Q, Y) == fw.PATH_SKINNY
-    assert p(4, 100, 504, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # 4-byte path: k >= 512
-    assert p(4, 100, 4100, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK        # 4-byte path: k % 8 == 0
+    assert p(4, 100, 504, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # unaligned-code path: k >= 512
+    assert p(4, 100, 4100, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK        # unaligned-code path: k % 8 == 0
     assert p(4, 100, 4096, fw.BF16, X, Q + 4, Y) == fw.PATH_SKINNY      # q 4-byte aligned
     assert p(4, 100, 4096, fw.BF16, X, Q + 2, Y) == fw.PATH_FALLBACK    # q 2-byte aligned
-    assert p(4, 100, 8200, fw.BF16, X + 8, Q, Y) == fw.PATH_FALLBACK    # 4-byte path: x 16-byte aligned
+    assert p(4, 100, 8200, fw.BF16, X + 8, Q, Y) == fw.PATH_FALLBACK    # unaligned-code path: x 16-byte aligned
     assert p(1, 100, 128, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK         # k < 256
     assert p(1, 100, 0, fw.BF16, X, Q, Y) == fw.PATH_FALLBACK           # k == 0
     assert p(1, 4096, 4096, fw.BF16, X + 2, Q, Y) == fw.PATH_FALLBACK   # x not 16-B aligned
-    assert p(4, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_SKINNY     # q not 16-B aligned: 4-byte path
+    assert p(4, 4096, 4096, fw.BF16, X, Q + 8, Y) == fw.PATH_SKINNY     # q not 16-B aligned: unaligned-code path
     assert p(1, 4096, 4096, fw.BF16, 0, 0, 0) == fw.PATH_GEMV           # NULL = aligned
     assert p(1, 4096, 4096, fw.FP32, X, Q, Y) == -1                     # fp32 activations
     assert p(-1, 4096, 4096, fw.BF16, X, Q, Y) == -1
@@ -118,19 +118,22 @@ def test_kernel_names():
     assert kn(A, 20, 12300, 512, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=2>"
     assert kn(A, 16, 12288, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=3,KP=1,NS=4>"
     assert kn(fw.PATH_SKINNY, 1, 4096, 4096, fw.BF16, X, Q) == "seg_kernel<SEG=4,T=4,W=4,U=2,MT=1>"
-    assert kn(A, 4, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
+    assert kn(A, 4, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=8>"
     assert kn(A, 1, 28672, 8200, fw.BF16, X, Q) == "gemv_shift_kernel<R=4,U=2,NT=128>"  # k % 16 == 8
     assert kn(A, 1, 4096, 4104, fw.BF16, X, Q) == "gemv_shift_kernel<R=2,U=2,NT=64,DB>"
     assert kn(A, 1, 4096, 4096, fw.BF16, X, Q + 8) == "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>"  # every row 8 bytes off
     assert kn(A, 1, 28672, 8192, fw.BF16, X, Q + 8) == "gemv_kernel<R=4,U=2,NT=128,CH=8>"
     assert kn(A, 1, 4096, 4112, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"   # k % 16 == 0: 16-code chunks
     assert kn(A, 1, 28672, 8200, fw.BF16, X, Q + 4) == "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"
-    assert kn(A, 4, 4096, 14344, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=4>"
-    assert kn(A, 32, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2,CB=4>"
-    assert kn(A, 16, 14336, 4104, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4,CB=4>"
+    assert kn(A, 4, 4096, 14344, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=8>"
+    assert kn(A, 32, 28672, 8200, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2,CB=8>"
+    assert kn(A, 16, 14336, 4104, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4,CB=8>"
     assert kn(A, 16, 4096, 4096, fw.BF16, X, Q + 4) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=4>"
-    assert kn(A, 9, 100, 776, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=2,CB=4>"   # 768 = 3 stages: 512
-    assert kn(A, 32, 2048, 4096 + 8, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=4>"
+    assert kn(A, 9, 100, 776, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=2,CB=8>"   # 768 = 3 stages: 512
+    assert kn(A, 32, 2048, 4096 + 8, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=8>"
+    # every row 8 bytes off a 16-byte boundary (k % 16 == 0, q 8 bytes off): 4-byte loads
+    assert kn(A, 8, 4096, 4096, fw.BF16, X, Q + 8) == "pipe_kernel<XR=8,CT=1,KP=2,NS=4,CB=4>"
+    assert kn(A, 16, 8192, 4112, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=2,NS=4,CB=8>"  # aligned rows
     assert kn(fw.PATH_FALLBACK, 4, 28672, 8200, fw.BF16, X, Q) == "dequantize_kernel+wpipe_kernel<XR=4,CT=4,NS=4>"
     assert kn(A, 40, 300, 1000, fw.FP16, X, Q) == "dequantize_kernel+wpipe_kernel<XR=32,CT=4,NS=4>"
     assert kn(A, 5, 31, 37, fw.BF16, X, Q) == "dequantize_kernel+fallback_gemm_kernel"       # k % 8 != 0
@@ -157,7 +160,7 @@ def test_workspace_bytes():
     assert wb(16, 4096, 4096, fw.BF16, X, Q, Y) == 0
     assert wb(4, 28672, 8200, fw.BF16, X, Q, Y) == 0                     # 4-byte skinny path
     assert wb(4, 28672, 8196, fw.BF16, X, Q, Y) == 28672 * 8196 * 2      # k % 8 != 0: fallback
-    assert wb(32, 4096, 14336, fw.BF16, X, Q + 4, Y) == 0                 # 4-byte path: no split
+    assert wb(32, 4096, 14336, fw.BF16, X, Q + 4, Y) == 0                 # unaligned-code path: no split
     assert wb(64, 100, 500, fw.FP16, X, Q, Y) == 100 * 500 * 2           # k % 256 != 0: fallback
     assert wb(64, 100, 512, fw.FP16, X, Q, Y) == 0                       # batch kernel, single pass
     assert wb(64, 14336, 4096, fw.BF16, X, Q, Y) == 2 * 64 * 14336 * 4    # batch kernel, k in two
@@ -216,10 +219,10 @@ def test_linear_rejects_invalid_arguments():
     assert _lin(m=2, path=fw.PATH_GEMV) == fw.ERR_INVALID_VALUE
     assert _lin(m=33, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE
     assert _lin(k=4004, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE     # k % 8 != 0
-    assert _lin(k=504, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE      # 4-byte path: k >= 512
-    assert _lin(k=4104, x=X + 8, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED  # 4-byte path: x 16-byte aligned
+    assert _lin(k=504, path=fw.PATH_SKINNY) == fw.ERR_INVALID_VALUE      # unaligned-code path: k >= 512
+    assert _lin(k=4104, x=X + 8, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED  # unaligned-code path: x 16-byte aligned
     assert _lin(q=Q + 2, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED      # codes at least 4-byte aligned
-    assert _lin(k=256, q=Q + 4, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED  # 4-byte path needs k >= 512
+    assert _lin(k=256, q=Q + 4, path=fw.PATH_SKINNY) == fw.ERR_MISALIGNED  # unaligned-code path needs k >= 512
     assert _lin(m=1, k=4100, path=fw.PATH_GEMV) == fw.ERR_INVALID_VALUE     # k % 8 != 0
     assert _lin(m=1, k=4104, q=Q + 4, path=fw.PATH_GEMV) == fw.ERR_MISALIGNED  # 8-code chunks: q 8-byte aligned
     assert _lin(m=1, k=4104, x=X + 8, path=fw.PATH_GEMV) == fw.ERR_MISALIGNED  # x 16-byte aligned

@@ -68,7 +68,7 @@ SMALL = [
     (5, 31, 37, torch.float16, False, fw.PATH_FALLBACK),
     (4, 128, 200, torch.bfloat16, True, fw.PATH_FALLBACK),
     (40, 300, 1000, torch.float16, True, fw.PATH_FALLBACK),    # 2 token tiles, 488-value k tail
-    (7, 16500, 776, torch.bfloat16, False, fw.PATH_SKINNY),    # 4-byte path, wide layer, 264-value tail
+    (7, 16500, 776, torch.bfloat16, False, fw.PATH_SKINNY),    # unaligned-code path, wide layer, 264-value tail
     (7, 16500, 504, torch.bfloat16, False, fw.PATH_FALLBACK),  # k < 512: the fallback's ring, 248-value tail
     (12, 70, 264, torch.bfloat16, True, fw.PATH_FALLBACK),     # shortest ring (2 stages), 8-value tail
 ]
@@ -121,24 +121,35 @@ def test_pipe_kernel_parity(m, n, k, dtype, kernel):
 
 RING4 = [
     # (m, n, k, dtype, bias, byte offset of q, kernel the dispatcher must pick):
-    # the skinny kernel's 4-byte path, every ring shape it uses, tails of 8,
-    # 248, 264 and 504 columns, codes 4-, 8- and 12-byte aligned, ragged channels
+    # codes the 16-byte kernels cannot load. CB=8: rows 8-byte aligned that
+    # are 16-byte aligned or alternate (k % 16 == 8), 16-byte loads from each
+    # workgroup's first 16-byte boundary, workgroups of one row parity; CB=4:
+    # 4-byte loads (q 4 bytes off, or every row 8 bytes off). Every ring shape
+    # either uses, columns outside the ring of 8 to 504, ragged channels.
     (1, 77, 8200, torch.bfloat16, True, 4, "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=4>"),
-    (4, 4096, 14344, torch.float16, True, 0, "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=4>"),
-    (2, 16500, 1032, torch.bfloat16, False, 0, "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=4>"),
-    (4, 12300, 4344, torch.float16, True, 0, "pipe_kernel<XR=4,CT=4,KP=1,NS=4,CB=4>"),
-    (6, 12288, 2056, torch.bfloat16, True, 0, "pipe_kernel<XR=8,CT=2,KP=1,NS=4,CB=4>"),
-    (8, 8200, 2056, torch.float16, False, 0, "pipe_kernel<XR=8,CT=2,KP=2,NS=4,CB=4>"),
-    (16, 9000, 1288, torch.bfloat16, True, 0, "pipe_kernel<XR=16,CT=2,KP=1,NS=4,CB=4>"),
-    (17, 8300, 1544, torch.float16, True, 0, "pipe_kernel<XR=32,CT=2,KP=1,NS=2,CB=4>"),
-    (9, 300, 776, torch.bfloat16, False, 0, "pipe_kernel<XR=16,CT=2,KP=1,NS=2,CB=4>"),
-    (12, 1000, 4104, torch.float16, True, 0, "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=4>"),
-    (32, 300, 2056, torch.bfloat16, True, 0, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=4>"),
-    (24, 5000, 1528, torch.bfloat16, False, 0, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=4>"),
-    (5, 28672, 1032, torch.bfloat16, True, 0, "pipe_kernel<XR=8,CT=4,KP=1,NS=2,CB=4>"),
+    (4, 4096, 14344, torch.float16, True, 0, "pipe_kernel<XR=4,CT=1,KP=2,NS=4,CB=8>"),
+    (2, 16500, 1032, torch.bfloat16, False, 0, "pipe_kernel<XR=4,CT=4,KP=1,NS=2,CB=8>"),
+    (4, 12300, 4344, torch.float16, True, 0, "pipe_kernel<XR=4,CT=4,KP=1,NS=4,CB=8>"),
+    (6, 12288, 2056, torch.bfloat16, True, 0, "pipe_kernel<XR=8,CT=2,KP=1,NS=4,CB=8>"),
+    (8, 8200, 2056, torch.float16, False, 0, "pipe_kernel<XR=8,CT=2,KP=2,NS=4,CB=8>"),
+    (16, 9000, 1288, torch.bfloat16, True, 0, "pipe_kernel<XR=16,CT=2,KP=1,NS=4,CB=8>"),
+    (17, 8300, 1544, torch.float16, True, 0, "pipe_kernel<XR=32,CT=2,KP=1,NS=2,CB=8>"),
+    (9, 300, 776, torch.bfloat16, False, 0, "pipe_kernel<XR=16,CT=2,KP=1,NS=2,CB=8>"),
+    (12, 1000, 4104, torch.float16, True, 0, "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=8>"),
+    (32, 300, 2056, torch.bfloat16, True, 0, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=8>"),
+    (24, 5000, 1528, torch.bfloat16, False, 0, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=8>"),
+    (5, 28672, 1032, torch.bfloat16, True, 0, "pipe_kernel<XR=8,CT=4,KP=1,NS=2,CB=8>"),
     (16, 4096, 4096, torch.bfloat16, True, 4, "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=4>"),
     (3, 14336, 4096, torch.float16, True, 8, "pipe_kernel<XR=4,CT=4,KP=1,NS=4,CB=4>"),
     (32, 14336, 4096, torch.bfloat16, False, 12, "pipe_kernel<XR=32,CT=4,KP=1,NS=4,CB=4>"),
+    (3, 100, 520, torch.float16, True, 8, "pipe_kernel<XR=4,CT=2,KP=1,NS=2,CB=8>"),     # row 0 the shifted one
+    (7, 33, 1032, torch.bfloat16, True, 8, "pipe_kernel<XR=8,CT=1,KP=2,NS=2,CB=8>"),    # odd n: last odd workgroup idle
+    (13, 65, 2312, torch.float16, False, 8, "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=8>"),
+    (10, 333, 4480, torch.bfloat16, True, 0, "pipe_kernel<XR=16,CT=1,KP=2,NS=4,CB=8>"),  # aligned rows, 384 left over
+    (20, 4100, 4112, torch.float16, True, 0, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=8>"),
+    (32, 129, 8200, torch.bfloat16, True, 8, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=8>"),
+    (22, 70, 8200, torch.float16, False, 0, "pipe_kernel<XR=32,CT=1,KP=2,NS=2,CB=8>"),
+    (2, 8200, 2056, torch.bfloat16, True, 0, "pipe_kernel<XR=4,CT=2,KP=2,NS=4,CB=8>"),
 ]
 
 

@@ -163,7 +163,7 @@ def test_large(shape):
         print(f"  m={m}", flush=True)
         if shape == workloads.LARGE_FALLBACK_SHAPE:
             # k = 8200: the GEMV's 8-code chunks (one token) or the skinny
-            # kernel's 4-byte path, and the dequantizing fallback forced, each
+            # kernel's unaligned-code path, and the dequantizing fallback forced, each
             # on every output
             _linear_checked(lay, q, s, q_ref, s_ref, workloads.large_x(shape, m), amax,
                             fw.PATH_GEMV if m == 1 else fw.PATH_SKINNY, also_paths=(fw.PATH_FALLBACK,))

@@ -52,7 +52,7 @@ def _noalloc(x, q, s, b):
 # consecutive calls, each smaller than the one before, on every path that uses
 # the scratch: skinny k split in four, then in two, on smaller layers;
 # batch k split; the fallback's 16-bit weight (k % 8 != 0); and the GEMV and
-# the skinny kernel's 4-byte path (no scratch)
+# the skinny kernel's unaligned-code path (no scratch)
 SEQUENCES = [
     [(32, 4096, 14336, torch.bfloat16, False), (20, 4096, 10240, torch.float16, True)],
     [(24, 8192, 4096, torch.bfloat16, True), (17, 8192, 2048, torch.bfloat16, False)],
