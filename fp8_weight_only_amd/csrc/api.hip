@@ -93,8 +93,9 @@ bool ring4_shape(int64_t m, int64_t k, const void* x, const uint8_t* q)
     return !(fast_k(k) && fast_pointers(x, q));
 }
 
-// The GEMV's 8-code chunks: one token whose codes the 16-byte loads cannot
-// take, with k % 8 == 0, k >= 256, q 8-byte and x 16-byte aligned.
+// The GEMV on rows only 8-byte aligned: one token whose codes the 16-byte
+// kernels cannot load at their row starts, with k % 8 == 0, k >= 256, q
+// 8-byte and x 16-byte aligned.
 bool gemv8_shape(int64_t m, int64_t k, const void* x, const uint8_t* q)
 {
     if (m != 1 || k < 256 || k % 8 != 0 || !aligned(x, 16) || !aligned(q, 8))
@@ -172,8 +173,8 @@ fp8w_status_t run_linear(const void* x, fp8w_dtype_t act, int64_t m, int64_t k, 
     if (path == FP8W_PATH_GEMV) {
         if (m != 1 && m != 0)
             return FP8W_ERR_INVALID_VALUE;
-        // 16-code chunks (k % 256 == 0, x and q 16-byte aligned) or 8-code
-        // chunks (k % 8 == 0, x 16-byte and q 8-byte aligned)
+        // k % 256 == 0 with x and q 16-byte aligned, or rows 8-byte aligned
+        // (k % 8 == 0, x 16-byte and q 8-byte aligned: launch_gemv picks the chunking)
         if (!(fast_k(k) && fast_pointers(x, q))) {
             if (k < 256 || k % 8 != 0)
                 return FP8W_ERR_INVALID_VALUE;
