@@ -1,5 +1,5 @@
-"""Seeded random shapes through every dispatch path of fp8w_linear and
-fp8w_linear_grouped, against the oracle.
+"""Seeded random shapes through every dispatch path of fp8w_linear,
+fp8w_linear_grouped and fp8w_linear_w8a8, against the oracle.
 
 Each case draws the number of tokens m, the channels n, the reduction length k
 (a multiple of 256, of 16, of 8, of 2, or odd), the activation dtype, a bias or
@@ -203,3 +203,51 @@ def test_random_grouped_parity(case):
     x64 = c.x.double().numpy()
     y_ref = oracle.linear_f64_groups(x64, q_ref, s_ref, g, None if c.layer.bias is None else c.layer.bias.double().numpy())
     assert_gate(y.double().cpu().numpy(), y_ref, x64, oracle.row_amax(w), f"grouped sweep {_gids(case)} path={NAMES[path]}")
+
+
+def _draw_w8a8(i):
+    r = np.random.default_rng([20261204, i])
+    k = 256 * int(r.integers(1, 13))
+    m = int(r.choice([int(r.integers(1, 33)), int(r.integers(33, 257)), int(r.integers(257, 700))], p=[0.3, 0.4, 0.3]))
+    n = int(r.integers(1, 1500))
+    n = max(1, min(n, int(6e7) // (m * k)))
+    dtype = torch.bfloat16 if r.random() < 0.5 else torch.float16
+    bias = bool(r.random() < 0.7)
+    return (i, m, n, k, dtype, bias)
+
+
+W8A8 = [_draw_w8a8(i) for i in range(64)]
+
+
+def _wids(c):
+    i, m, n, k, dtype, bias = c
+    return f"{i}-m{m}-n{n}-k{k}-{'bf16' if dtype == torch.bfloat16 else 'fp16'}" + ("-bias" if bias else "")
+
+
+@pytest.mark.parametrize("case", W8A8, ids=[_wids(c) for c in W8A8])
+def test_random_w8a8_parity(case):
+    """W8A8 ("Skill: Write an FP8 Kernel", "Required reasoning process" steps 2,
+    4 and 5): the activation codes and scales bit for bit, every output within
+    the gate against the oracle's fp64 layer on the same codes, nothing
+    written outside y."""
+    i, m, n, k, dtype, bias = case
+    print(f"w8a8 sweep {_wids(case)}", flush=True)
+    c = workloads.random_case(9000 + i, m, n, k, dtype, with_bias=bias)
+    q, s = fw.quantize(torch.from_numpy(c.layer.w).to(DEV))
+    x = c.x.to(DEV)
+    qx, sx = fw.quantize_activations(x)
+    qx_ref, sx_ref, st = oracle.quantize_activations(c.x.float().numpy())
+    assert st == 0
+    assert_same_bits(sx.cpu().numpy(), sx_ref, "activation scales")
+    assert_same_bits(qx.cpu().numpy(), qx_ref, "activation codes")
+    b = None if c.layer.bias is None else c.layer.bias.to(DEV)
+    ybuf = torch.full((m * n + GUARD,), float("nan"), dtype=dtype, device=DEV)
+    y = ybuf[:m * n].view(m, n)
+    fw.linear_w8a8(x, q, s, b, out=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(ybuf[m * n:].float()).all()), "write outside y"
+    q_ref, s_ref, _ = oracle.quantize_rows(c.layer.w)
+    b64 = None if c.layer.bias is None else c.layer.bias.double().numpy()
+    xd = oracle.decode(qx_ref) * sx_ref.astype(np.float64)[:, None]
+    y_ref = oracle.linear_w8a8_f64(qx_ref, sx_ref, q_ref, s_ref, b64)
+    assert_gate(y.double().cpu().numpy(), y_ref, xd, oracle.row_amax(c.layer.w), f"w8a8 sweep {_wids(case)}")
