@@ -132,10 +132,12 @@ struct Narrow {
 };
 
 // Requires k % (W * 256 * NS) == 0 and m <= 16 * MT. One workgroup per 16 channels.
+// The output pointer comes last, so that the sizes lie in the 56 bytes of
+// arguments the wave finds preloaded in SGPRs.
 template <typename A, int MT_, int W, int NS>
 __global__ __launch_bounds__(W* kWave) void narrow_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k)
+    const uint16_t* __restrict__ bias, int m, int64_t n, int64_t k, uint16_t* __restrict__ y)
 {
     using P = Narrow<A, MT_, W, NS>;
     using C = typename P::C;
@@ -253,7 +255,7 @@ hipError_t launch_narrow_cfg(const void* x, int m, int64_t k, const uint8_t* q, 
 {
     const dim3 grid((unsigned)((n + 15) / 16)), block(W * kWave);
     hipLaunchKernelGGL((narrow_kernel<A, MT, W, NS>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
-                       scale, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), m, n, k);
+                       scale, static_cast<const uint16_t*>(bias), m, n, k, static_cast<uint16_t*>(y));
     return hipGetLastError();
 }
 

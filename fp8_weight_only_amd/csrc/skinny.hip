@@ -48,10 +48,12 @@ namespace fp8w {
 namespace {
 
 // ---------------------------------------------------------------- seg_kernel
+// The output pointer comes last, so that the sizes lie in the 56 bytes of
+// arguments the wave finds preloaded in SGPRs.
 template <typename A, int SEG, int T, int W, int U, int MT>
 __global__ __launch_bounds__(W* kWave) void seg_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k)
+    const uint16_t* __restrict__ bias, int m, int64_t n, int64_t k, uint16_t* __restrict__ y)
 {
     constexpr int MP = 16 / SEG;     // channels (and tokens) per MFMA
     constexpr int SPAN = 64 * SEG;   // k covered by one MFMA pair
@@ -427,10 +429,17 @@ __device__ __forceinline__ f32x4 kSlicedSum(f32x4 (*part)[NACC][kWave], int ct, 
 // dealt to the waves in turn; each wave fetches its first before the ring
 // starts. CB == 8: workgroups 2j and 2j + 1 own the even and the odd channels
 // of 32 CT.
+//
+// Arguments: what the ring needs from its first instruction (the operands,
+// the sizes, kc = kr / splits and the stages per split S, each under 2^31)
+// lie in the first 56 bytes, which the wave finds preloaded in SGPRs (the
+// build preloads 14); the output pointers, needed only at the end, follow.
+// Measured on MI355X: 0.2-0.3 us per launch against sizes fetched with a
+// scalar load (and a 64-bit division by the grid's height) before the ring.
 template <typename A, int XR, int CT, int KP, int NS, int CB>
 __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int m, int64_t n, int64_t k, int64_t kr,
+    const uint16_t* __restrict__ bias, int n, int k, int kr, int kc, int m, int S, uint16_t* __restrict__ y,
     float* __restrict__ part_out)
 {
     using P = Pipe<A, XR, CT, KP, NS, CB>;
@@ -442,7 +451,6 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t b3[NS > 3 ? C::STAGE : 16];
 
     // split k: workgroup row blockIdx.y owns k range [y * kc, (y + 1) * kc)
-    const int64_t kc = kr / gridDim.y;
     P p;
     p.x = x + (int64_t)blockIdx.y * kc;
     p.q = q + (int64_t)blockIdx.y * kc;
@@ -497,11 +505,10 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
             p.tail_load(kr, tb0, tcode, txv);
     }
 
-    const int64_t S = kc / (KP * 256);
     p.S = S;
     // workgroups are dealt to the eight XCDs in turn: consecutive workgroups of
     // one XCD get consecutive start stages
-    p.rot = (int64_t)(blockIdx.x / 8) % S;
+    p.rot = (int64_t)((blockIdx.x / 8) % (unsigned)S);
     // with the sliced compute, the loads pinned ahead of each step's compute
     // measured 0.2-0.4 us faster at 16-22 tokens on [14336 x 4096]; for CT = 3
     // they were 0.2-0.6 us slower
@@ -589,8 +596,8 @@ hipError_t launch_seg(const void* x, int m, int64_t k, const uint8_t* q, const f
     constexpr int C = (16 / SEG) * T;  // channels per workgroup
     const dim3 grid((unsigned)((n + C - 1) / C)), block(W * kWave);
     hipLaunchKernelGGL((seg_kernel<A, SEG, T, W, U, MT>), grid, block, 0, stream,
-                       static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias),
-                       static_cast<uint16_t*>(y), m, n, k);
+                       static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias), m, n, k,
+                       static_cast<uint16_t*>(y));
     return hipGetLastError();
 }
 
@@ -613,11 +620,15 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
     if ((kr != k && (splits != 1 || (k - kr) % 8 != 0)) || k % 8 != 0 || (CB == 16 && k % 16 != 0) ||
         (CB == 8 && (splits != 1 || kr > k - 8 || reinterpret_cast<uintptr_t>(q) % 8 != 0)))
         return hipErrorInvalidValue;
+    if (n > INT32_MAX || k > INT32_MAX)  // the kernel takes its sizes as 32-bit values
+        return hipErrorInvalidValue;
     const unsigned gx = CB == 8 ? (unsigned)(2 * ((n + 32 * CT - 1) / (32 * CT))) : (unsigned)((n + 16 * CT - 1) / (16 * CT));
     const dim3 grid(gx, (unsigned)splits), block(CT * KP * kWave);
+    const int64_t kc = kr / splits;  // each split's columns: a whole number of NS-stage groups
     hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS, CB>), grid, block, 0, stream,
-                       static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias),
-                       static_cast<uint16_t*>(y), m, n, k, kr, splits > 1 ? part : nullptr);
+                       static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias), (int)n, (int)k,
+                       (int)kr, (int)kc, m, (int)(kc / (KP * 256)), static_cast<uint16_t*>(y),
+                       splits > 1 ? part : nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits <= 1)
         return e;
