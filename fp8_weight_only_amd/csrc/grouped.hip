@@ -99,13 +99,15 @@ struct GGroup {
     }
 };
 
+// The output pointer comes last, so that the sizes lie in the 56 bytes of
+// arguments the wave finds preloaded in SGPRs.
 template <typename A, int R, int U, int NT, bool DB>
 __global__ __launch_bounds__(NT) void gemv_grouped_kernel(const uint16_t* __restrict__ x,
                                                           const uint8_t* __restrict__ q,
                                                           const float* __restrict__ scale,
-                                                          const uint16_t* __restrict__ bias,
-                                                          uint16_t* __restrict__ y, int64_t n, int64_t k,
-                                                          int lg_chunks)  // log2(G / 16)
+                                                          const uint16_t* __restrict__ bias, int64_t n, int64_t k,
+                                                          int lg_chunks,  // log2(G / 16)
+                                                          uint16_t* __restrict__ y)
 {
     constexpr int NW = NT / kWave;
     __shared__ float red[NW][R];
@@ -592,11 +594,11 @@ hipError_t launch_grouped_typed(int path, const void* x, int64_t m, int64_t k, c
         if (n * k >= ((int64_t)96 << 20)) {
             hipLaunchKernelGGL((gemv_grouped_kernel<A, 4, 2, 128, false>), dim3((unsigned)((n + 3) / 4)), dim3(128), 0,
                                stream, static_cast<const uint16_t*>(x), q, scale,
-                               static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), n, k, lg - 4);
+                               static_cast<const uint16_t*>(bias), n, k, lg - 4, static_cast<uint16_t*>(y));
         } else {
             hipLaunchKernelGGL((gemv_grouped_kernel<A, 2, 2, 64, true>), dim3((unsigned)((n + 1) / 2)), dim3(64), 0,
                                stream, static_cast<const uint16_t*>(x), q, scale,
-                               static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), n, k, lg - 4);
+                               static_cast<const uint16_t*>(bias), n, k, lg - 4, static_cast<uint16_t*>(y));
         }
         return hipGetLastError();
     }
