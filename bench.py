@@ -972,7 +972,8 @@ def _short_kernel_name(full):
     name, targs = m.group(1), (m.group(2) or "")
     args = [a.strip() for a in targs[1:-1].split(",")] if targs else []
     keys = {"pipe_kernel": ("XR", "CT", "KP", "NS", "CB"), "seg_kernel": ("SEG", "T", "W", "U", "MT"),
-            "gemv_kernel": ("R", "U", "NT", "DB", "CH"), "wpipe_kernel": ("XR", "CT", "NS"), "w8a8_kernel": ("BN", "BM", "NS", "WN", "WM", "GM"),
+            "gemv_kernel": ("R", "U", "NT", "DB", "CH"), "gemv_shift_kernel": ("R", "U", "NT", "DB"),
+            "narrow_kernel": ("MT", "W", "NS"), "wpipe_kernel": ("XR", "CT", "NS"), "w8a8_kernel": ("BN", "BM", "NS", "WN", "WM", "GM"),
             "gemv_grouped_kernel": ("R", "U", "NT", "DB"), "pipe_grouped_kernel": ("XR", "CT", "KP", "NS", "G"),
             "batch_kernel": ("BN", "BM", "WN", "WM", "G", "GM")}.get(name)
     if keys and len(args) == len(keys) + 1:  # first argument is the activation type
