@@ -245,7 +245,8 @@ def test_split_k_matches_single_pass(m, n, k, splits, dtype):
     fp32 partial sums, then the reduce kernel) and without it (single pass) both
     pass the gate, and agree to fp32 summation-order rounding."""
     act = fw.BF16 if dtype == torch.bfloat16 else fw.FP16
-    assert fw.fp8w_linear_workspace_bytes(m, n, k, act, 0, 0, 0) == splits * m * n * 4
+    need = splits * m * n * 4
+    assert fw.fp8w_linear_workspace_bytes(m, n, k, act, 0, 0, 0) == need
     case = workloads.random_case(4242, m, n, k, dtype, with_bias=True)
     q, s, x, b = _prepare(case)
     q_ref, s_ref, x64, y_ref, amax = oracle_case(case.layer.w, case.x, case.layer.bias)
@@ -258,13 +259,15 @@ def test_split_k_matches_single_pass(m, n, k, splits, dtype):
         assert_gate(yv, y_ref, x64, amax, f"split={ws is None}")
         outs.append(yv)
     assert np.allclose(outs[0], outs[1], rtol=2e-2, atol=1e-2)
-    # a second call reuses the workspace contents without clearing: same bits
-    y2 = nan_like((m, n), dtype, DEV)
-    ws = torch.full((splits * m * n * 4,), 0x7F, dtype=torch.uint8, device=DEV)
-    fw.linear(x, q, s, b, out=y2, workspace=ws)
-    fw.linear(x, q, s, b, out=y2, workspace=ws)
-    torch.cuda.synchronize()
-    assert np.array_equal(y2.double().cpu().numpy(), outs[0])
+    # whatever the workspace holds when a call starts, and when calls reuse it
+    # without clearing: the same bits
+    for fill in (0x7F, 0x00, 0xFF):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        for _ in range(3):
+            y2 = nan_like((m, n), dtype, DEV)
+            fw.linear(x, q, s, b, out=y2, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(y2.double().cpu().numpy(), outs[0]), f"workspace filled with {fill:#x}"
 
 
 @pytest.mark.parametrize("m,k", [(1, 256), (1, 4096), (2, 1024), (16, 768), (17, 512), (32, 2048)])
