@@ -62,6 +62,7 @@ Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k, const uint8_t* q);
 struct NarrowPlan {
     bool ok;
     int mt, w, ns;  // 16-token MFMA tiles, waves, ring stages
+    bool ql;        // activation parts loaded by neighbouring lanes, moved by ds_bpermute
 };
 NarrowPlan plan_narrow(int64_t m, int64_t n, int64_t k);
 hipError_t launch_narrow(const NarrowPlan& p, const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,

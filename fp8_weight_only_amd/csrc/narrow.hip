@@ -30,8 +30,13 @@
 //     s mod NS;
 //   * loads, per 16-token tile, eight 16-byte activation fragments into
 //     registers: for MFMA pair j (0..3) and half h, lane (i, g) takes token i's
-//     elements 16 (4j + g) + 8h .. + 7, so the four lanes of a token read 64
-//     contiguous bytes;
+//     elements 16 (4j + g) + 8h .. + 7, so the lanes of a token cover one
+//     128-byte line with the two halves. Those lanes are 16 apart, so a
+//     quarter-wave (four neighbouring lanes, four tokens) touches four lines
+//     per instruction. With QL the same fragments are loaded by lane 4i + g
+//     instead (a quarter-wave reads one token's line) and moved to lane i + 16g
+//     with ds_bpermute just before their MFMA: four LDS-crossbar moves per
+//     fragment, paid back from 10 tokens on;
 //   * reads chunk 4j + g of code row i from LDS for pair j, decodes it to two
 //     8-element operands and issues two MFMAs per token tile. MFMA (j, h)
 //     pairs k slot 8g + e with k = 64j + 16g + 8h + e in both operands.
@@ -74,13 +79,19 @@ struct NarrowCfg {
     static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
 };
 
-template <typename A, int MT_, int W, int NS>
+// QL: each token's activation fragments are loaded by four neighbouring lanes
+// (lane 4 t + g takes token t's part g), so each quarter of a load instruction
+// reads one 128-byte line instead of four; before each MFMA the parts move to
+// the operand layout's lanes (t + 16 g) with ds_bpermute. Lanes of tokens past
+// m load nothing (their columns of D are never stored).
+template <typename A, int MT_, int W, int NS, bool QL>
 struct Narrow {
     using C = NarrowCfg<MT_, W, NS>;
     static constexpr int MT = C::MT;
 
     const uint8_t* q;     // row n0 of the codes
-    const uint16_t* xrow[MT];  // this lane's token rows
+    const uint16_t* xrow[MT];  // this lane's token rows (QL: the loading lane's)
+    bool xon[MT];         // QL: this lane loads for a token below m
     int64_t n, k, n0;
     int64_t S, rot;       // stages per wave; this workgroup's first stage
     int lane, wave;
@@ -101,19 +112,35 @@ struct Narrow {
             __builtin_amdgcn_global_load_lds((const void*)src, FP8W_LDS(buf + wave * C::CODE + j * 1024), 16, 0,
                                              2 /* non-temporal */);
         }
-        const int g = lane >> 4;
+        const int g = QL ? (lane & 3) : (lane >> 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    xv[j][h][mt] = load16(xrow[mt] + kb + 64 * j + 16 * g + 8 * h);
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (!QL || xon[mt])
+                        xv[j][h][mt] = load16(xrow[mt] + kb + 64 * j + 16 * g + 8 * h);
+                }
+    }
+
+    // QL: lane t + 16 g takes the part its token's loading lane 4 t + g holds
+    __device__ __forceinline__ static u32x4 to_operand(const u32x4 v, int src)
+    {
+        if constexpr (!QL)
+            return v;
+        u32x4 r;
+        r.x = __builtin_amdgcn_ds_bpermute(src, (int)v.x);
+        r.y = __builtin_amdgcn_ds_bpermute(src, (int)v.y);
+        r.z = __builtin_amdgcn_ds_bpermute(src, (int)v.z);
+        r.w = __builtin_amdgcn_ds_bpermute(src, (int)v.w);
+        return r;
     }
 
     __device__ __forceinline__ void compute(const uint8_t* buf, const u32x4 (&xv)[4][2][MT], f32x4* acc) const
     {
         const int i = lane & 15, g = lane >> 4;
+        const int src = (4 * i + g) << 2;  // QL: byte address of lane 4 i + g
         const uint8_t* cb = buf + wave * C::CODE + 256 * i;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -124,8 +151,8 @@ struct Narrow {
             const u32x4 a1 = {d2.x, d2.y, d3.x, d3.y};
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                acc[mt] = A::mfma(a0, xv[j][0][mt], acc[mt]);
-                acc[mt] = A::mfma(a1, xv[j][1][mt], acc[mt]);
+                acc[mt] = A::mfma(a0, to_operand(xv[j][0][mt], src), acc[mt]);
+                acc[mt] = A::mfma(a1, to_operand(xv[j][1][mt], src), acc[mt]);
             }
         }
     }
@@ -134,12 +161,12 @@ struct Narrow {
 // Requires k % (W * 256 * NS) == 0 and m <= 16 * MT. One workgroup per 16 channels.
 // The output pointer comes last, so that the sizes lie in the 56 bytes of
 // arguments the wave finds preloaded in SGPRs.
-template <typename A, int MT_, int W, int NS>
+template <typename A, int MT_, int W, int NS, bool QL>
 __global__ __launch_bounds__(W* kWave) void narrow_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
     const uint16_t* __restrict__ bias, int m, int64_t n, int64_t k, uint16_t* __restrict__ y)
 {
-    using P = Narrow<A, MT_, W, NS>;
+    using P = Narrow<A, MT_, W, NS, QL>;
     using C = typename P::C;
     constexpr int MT = C::MT;
     constexpr int LOADS = C::LOADS;
@@ -166,7 +193,8 @@ __global__ __launch_bounds__(W* kWave) void narrow_kernel(
     const int i = p.lane & 15, g = p.lane >> 4;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int t = i + 16 * mt;
+        const int t = (QL ? (p.lane >> 2) : i) + 16 * mt;
+        p.xon[mt] = t < m;
         p.xrow[mt] = x + (int64_t)(t < m ? t : m - 1) * k;  // rows past m: a real row, results discarded
     }
     const int64_t S = k / (W * 256);
@@ -249,12 +277,12 @@ __global__ __launch_bounds__(W* kWave) void narrow_kernel(
     }
 }
 
-template <typename A, int MT, int W, int NS>
+template <typename A, int MT, int W, int NS, bool QL>
 hipError_t launch_narrow_cfg(const void* x, int m, int64_t k, const uint8_t* q, const float* scale,
                              const void* bias, int64_t n, void* y, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + 15) / 16)), block(W * kWave);
-    hipLaunchKernelGGL((narrow_kernel<A, MT, W, NS>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
+    hipLaunchKernelGGL((narrow_kernel<A, MT, W, NS, QL>), grid, block, 0, stream, static_cast<const uint16_t*>(x), q,
                        scale, static_cast<const uint16_t*>(bias), m, n, k, static_cast<uint16_t*>(y));
     return hipGetLastError();
 }
@@ -263,27 +291,33 @@ hipError_t launch_narrow_cfg(const void* x, int m, int64_t k, const uint8_t* q, 
 
 // Where it runs, from A/B sweeps against pipe_kernel / seg_kernel / the k split
 // on MI355X (weights rotated through 1 GiB): layers under 8192 channels with
-//   * k a multiple of 4096, 2..16 tokens: four waves, four-stage rings (the
+//   * k a multiple of 4096, 2..9 tokens: four waves, four-stage rings (the
 //     whole k = 4096 in flight); 0.1-1.1 us faster on 1024- to 4096-channel
 //     layers, e.g. [4096, 4096] at 4 tokens 6.7 -> 5.7 us, at 9: 7.2 -> 6.3;
-//   * k a multiple of 7168 (the 14336-wide down projection), 2..12 tokens:
-//     seven waves; [4096, 14336] at 9 tokens 16.7 -> 14.6 us (at 16 tokens
-//     the ring of pipe_kernel stays faster, 17.8 against 18.9);
+//   * k a multiple of 4096, 10..16 tokens: eight waves, two-stage rings, QL
+//     loads; [4096, 4096] at 16 tokens 7.2 -> 6.5 us, [4096, 8192] 11.5 ->
+//     10.1, [2048, 4096] 6.9 -> 5.9 (the activation loads of four tokens'
+//     lanes each touched four 128-byte lines per quarter-wave);
+//   * k a multiple of 7168 (the 14336-wide down projection), 2..5 tokens:
+//     seven waves, four-stage rings; [4096, 14336] at 4 tokens 12.3 us;
+//   * k a multiple of 7168, 6..16 tokens: seven waves, two-stage rings, QL
+//     loads; [4096, 14336] at 8 / 12 / 16 tokens 13.8 / 16.2 / 17.5 (the
+//     last on pipe_kernel) -> 13.0 / 14.6 / 16.2 us;
 //   * 17..24 tokens, k <= 8192 a multiple of 2048: two token tiles, four
 //     waves, two stages; [4096, 4096] at 17 tokens 9.7 (k split) -> 8.4 us,
 //     [2048, 8192] at 22 tokens 16.7 -> 14.7 (at 32 tokens and on long k the
-//     k split stays faster).
+//     k split stays faster; QL loads measured 0.6-1 us slower here).
 NarrowPlan plan_narrow(int64_t m, int64_t n, int64_t k)
 {
     NarrowPlan p{};
     if (m < 2 || m > 24 || n < 1 || n >= 8192 || k < 256 || k % 256 != 0)
         return p;
     if (m <= 16 && k % 4096 == 0) {
-        p = NarrowPlan{true, 1, 4, 4};
-    } else if (m <= 12 && k % 7168 == 0) {
-        p = NarrowPlan{true, 1, 7, 4};
+        p = m >= 10 ? NarrowPlan{true, 1, 8, 2, true} : NarrowPlan{true, 1, 4, 4, false};
+    } else if (m <= 16 && k % 7168 == 0) {
+        p = m >= 6 ? NarrowPlan{true, 1, 7, 2, true} : NarrowPlan{true, 1, 7, 4, false};
     } else if (m >= 17 && k % 2048 == 0 && k <= 8192) {
-        p = NarrowPlan{true, 2, 4, 2};
+        p = NarrowPlan{true, 2, 4, 2, false};
     }
     return p;
 }
@@ -292,11 +326,13 @@ template <typename A>
 static hipError_t launch_narrow_typed(const NarrowPlan& p, const void* x, int m, int64_t k, const uint8_t* q,
                                       const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream)
 {
-    const int key = p.mt * 100 + p.w * 10 + p.ns;
+    const int key = (p.ql ? 1000 : 0) + p.mt * 100 + p.w * 10 + p.ns;
     switch (key) {
-    case 144: return launch_narrow_cfg<A, 1, 4, 4>(x, m, k, q, scale, bias, n, y, stream);
-    case 174: return launch_narrow_cfg<A, 1, 7, 4>(x, m, k, q, scale, bias, n, y, stream);
-    case 242: return launch_narrow_cfg<A, 2, 4, 2>(x, m, k, q, scale, bias, n, y, stream);
+    case 144: return launch_narrow_cfg<A, 1, 4, 4, false>(x, m, k, q, scale, bias, n, y, stream);
+    case 174: return launch_narrow_cfg<A, 1, 7, 4, false>(x, m, k, q, scale, bias, n, y, stream);
+    case 242: return launch_narrow_cfg<A, 2, 4, 2, false>(x, m, k, q, scale, bias, n, y, stream);
+    case 1182: return launch_narrow_cfg<A, 1, 8, 2, true>(x, m, k, q, scale, bias, n, y, stream);
+    case 1172: return launch_narrow_cfg<A, 1, 7, 2, true>(x, m, k, q, scale, bias, n, y, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -318,7 +354,7 @@ hipError_t launch_narrow(const NarrowPlan& p, const void* x, Act act, int64_t m,
 const char* narrow_kernel_name(const NarrowPlan& p)
 {
     thread_local char name[64];
-    snprintf(name, sizeof name, "narrow_kernel<MT=%d,W=%d,NS=%d>", p.mt, p.w, p.ns);
+    snprintf(name, sizeof name, "narrow_kernel<MT=%d,W=%d,NS=%d%s>", p.mt, p.w, p.ns, p.ql ? ",QL" : "");
     return name;
 }
 

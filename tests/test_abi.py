@@ -97,14 +97,19 @@ def test_kernel_names():
     assert kn(A, 22, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"
     assert kn(A, 8, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=8,CT=2,KP=2,NS=4>"
     assert kn(A, 16, 8192, 3072, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"       # k % 2048 != 0
-    assert kn(A, 16, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=4,NS=4>"
+    assert kn(A, 16, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=8,NS=2,QL>"
+    assert kn(A, 9, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=4,NS=4>"
+    assert kn(A, 10, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=8,NS=2,QL>"
     assert kn(A, 16, 4100, 2048, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"     # k % 4096 != 0
-    assert kn(A, 16, 4096, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"
+    assert kn(A, 16, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
+    assert kn(A, 16, 4100, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
+    assert kn(A, 5, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=4>"
     assert kn(A, 32, 4096, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"
     assert kn(A, 22, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=2,W=4,NS=2>"
     assert kn(A, 22, 4096, 12288, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"
     assert kn(A, 17, 6000, 10240, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"
-    assert kn(A, 12, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=4>"
+    assert kn(A, 12, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
+    assert kn(A, 6, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
     assert kn(A, 25, 4096, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"
     assert kn(A, 32, 2048, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=1,KP=2,NS=4>"      # n < 4096
     assert kn(A, 32, 4096, 4608, fw.BF16, X, Q) == "seg_kernel<SEG=1,T=2,W=4,U=1,MT=2>"     # k % 2048 != 0

@@ -219,9 +219,16 @@ NARROW = [
     (2, 4096, 4096, torch.bfloat16, "narrow_kernel<MT=1,W=4,NS=4>"),
     (5, 1000, 4096, torch.float16, "narrow_kernel<MT=1,W=4,NS=4>"),
     (9, 4100, 8192, torch.bfloat16, "narrow_kernel<MT=1,W=4,NS=4>"),
-    (16, 33, 4096, torch.float16, "narrow_kernel<MT=1,W=4,NS=4>"),
-    (16, 4096, 4096, torch.bfloat16, "narrow_kernel<MT=1,W=4,NS=4>"),
-    (12, 4096, 7168, torch.bfloat16, "narrow_kernel<MT=1,W=7,NS=4>"),
+    (16, 33, 4096, torch.float16, "narrow_kernel<MT=1,W=8,NS=2,QL>"),
+    (16, 4096, 4096, torch.bfloat16, "narrow_kernel<MT=1,W=8,NS=2,QL>"),
+    (10, 4100, 4096, torch.float16, "narrow_kernel<MT=1,W=8,NS=2,QL>"),
+    (11, 2000, 4096, torch.float16, "narrow_kernel<MT=1,W=8,NS=2,QL>"),
+    (13, 1000, 8192, torch.bfloat16, "narrow_kernel<MT=1,W=8,NS=2,QL>"),
+    (12, 4096, 7168, torch.bfloat16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
+    (16, 4096, 14336, torch.bfloat16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
+    (6, 500, 14336, torch.float16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
+    (15, 4100, 21504, torch.float16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
+    (5, 500, 7168, torch.float16, "narrow_kernel<MT=1,W=7,NS=4>"),
     (3, 500, 14336, torch.float16, "narrow_kernel<MT=1,W=7,NS=4>"),
     (17, 4096, 2048, torch.bfloat16, "narrow_kernel<MT=2,W=4,NS=2>"),
     (24, 300, 8192, torch.float16, "narrow_kernel<MT=2,W=4,NS=2>"),
