@@ -88,6 +88,10 @@ template <typename A, int MT_, int W, int NS, bool QL>
 struct Narrow {
     using C = NarrowCfg<MT_, W, NS>;
     static constexpr int MT = C::MT;
+    // The waits count every load instruction of a stage, so no instruction may
+    // be skipped by a whole wave: with one token tile, token 0's lanes always
+    // load (m >= 1). A second tile's QL loads could all be masked off.
+    static_assert(!QL || MT == 1, "QL loads with one token tile");
 
     const uint8_t* q;     // row n0 of the codes
     const uint16_t* xrow[MT];  // this lane's token rows (QL: the loading lane's)
