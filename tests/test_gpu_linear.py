@@ -245,6 +245,36 @@ def test_narrow_kernel_parity(m, n, k, dtype, kernel):
     _check(case, expect_path=fw.PATH_SKINNY)
 
 
+def _ql_draw(i):
+    r = np.random.default_rng([5574, i])
+    if r.random() < 0.5:
+        k = 4096 * int(r.integers(1, 4))
+        m = int(r.integers(10, 17))
+    else:
+        k = 7168 * int(r.integers(1, 4))
+        m = int(r.integers(6, 17))
+    n = int(r.integers(1, 8192))
+    n = max(1, min(n, int(3e7) // k))
+    dtype = torch.bfloat16 if r.random() < 0.5 else torch.float16
+    return (i, m, n, k, dtype, bool(r.random() < 0.6))
+
+
+@pytest.mark.parametrize("case", [_ql_draw(i) for i in range(24)],
+                         ids=lambda c: f"{c[0]}-m{c[1]}-n{c[2]}-k{c[3]}")
+def test_narrow_ql_random_shapes(case):
+    """Seeded shapes that take the QL narrow kernels (each token's activation
+    parts loaded by neighbouring lanes, moved by ds_bpermute): every token count
+    they take, ragged channel counts, one to three 4096- or 7168-column ring
+    lengths, both activation types, with and without bias."""
+    i, m, n, k, dtype, bias = case
+    act = fw.BF16 if dtype == torch.bfloat16 else fw.FP16
+    name = fw.fp8w_linear_kernel(fw.PATH_AUTO, m, n, k, act, 0, 0)
+    print(f"ql sweep {i} m={m} n={n} k={k} {dtype} {name}", flush=True)
+    assert name.startswith("narrow_kernel<") and name.endswith(",QL>")
+    case = workloads.random_case(7300 + i, m, n, k, dtype, with_bias=bias)
+    _check(case, expect_path=fw.PATH_SKINNY)
+
+
 @pytest.mark.parametrize("m,n,k,splits", [(24, 8256, 4096, 2), (20, 4160, 10240, 4)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 def test_split_k_matches_single_pass(m, n, k, splits, dtype):
