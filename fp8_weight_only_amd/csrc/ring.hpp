@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 #define FP8W_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -108,6 +110,85 @@ __device__ __forceinline__ void run_ring(const P& p, int64_t S, uint8_t* b0, uin
         stage_barrier();
         p.compute(b3, acc);
     }
+}
+
+// f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void ring_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        ring_for<B + 1, E>(f);
+    }
+}
+
+// s_waitcnt for at most g stages of LOADS loads still outstanding, g uniform
+// in 0 .. GMAX (the count must be an immediate, so each value is its own wait).
+template <int LOADS, int GMAX>
+__device__ __forceinline__ void wait_stages_at_most(int64_t g)
+{
+    static_assert(GMAX >= 0 && GMAX <= 2, "stages in flight");
+    if constexpr (GMAX >= 2) {
+        if (g >= 2) {
+            wait_loads_at_most<2 * LOADS>();
+            return;
+        }
+    }
+    if constexpr (GMAX >= 1) {
+        if (g >= 1) {
+            wait_loads_at_most<LOADS>();
+            return;
+        }
+    }
+    wait_loads_at_most<0>();
+}
+
+// run_ring for any number of stages S >= NS (S need not be a multiple of NS).
+// Step s waits for stage s, opens the barrier, issues stage s + NS - 1 into
+// the buffer stage s - 1 used (while that stage exists) and computes stage s
+// from buffer s mod NS. Whole groups of NS steps that all issue run as in
+// run_ring; the last steps (fewer than 2 NS - 1) check at run time whether
+// they issue, and each waits with the stages issued after its own,
+// min(NS - 2, S - 1 - s), still allowed in flight (loads complete in order).
+template <int NS, int LOADS, bool PIN = false, typename P, typename Acc>
+__device__ __forceinline__ void run_ring_any(const P& p, int64_t S, uint8_t* b0, uint8_t* b1, uint8_t* b2,
+                                             uint8_t* b3, Acc* acc)
+{
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
+    uint8_t* const bufs[4] = {b0, b1, b2, b3};
+    p.issue(0, b0);
+    if constexpr (NS > 2)
+        p.issue(1, b1);
+    if constexpr (NS > 3)
+        p.issue(2, b2);
+    int64_t s0 = 0;
+    for (; s0 + 2 * NS - 2 < S; s0 += NS) {
+        ring_for<0, NS>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            wait_loads_at_most<LOADS*(NS - 2)>();
+            stage_barrier();
+            p.issue(s0 + u + NS - 1, bufs[(u + NS - 1) % NS]);
+            if constexpr (PIN)
+                __builtin_amdgcn_sched_barrier(0);
+            p.compute(bufs[u], acc);
+        });
+    }
+    ring_for<0, 2 * NS - 1>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int64_t s = s0 + u;
+        if (s < S) {
+            const int64_t after = S - 1 - s < NS - 2 ? S - 1 - s : NS - 2;
+            wait_stages_at_most<LOADS, NS - 2>(after);
+            stage_barrier();
+            if (s + NS - 1 < S) {
+                p.issue(s + NS - 1, bufs[(u + NS - 1) % NS]);
+                if constexpr (PIN)
+                    __builtin_amdgcn_sched_barrier(0);
+            }
+            p.compute(bufs[u % NS], acc);
+        }
+    });
 }
 
 // Tile (tn, tm) of workgroup (blockIdx.x, blockIdx.y). Workgroups are dealt

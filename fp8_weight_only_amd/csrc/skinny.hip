@@ -512,7 +512,10 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     // with the sliced compute, the loads pinned ahead of each step's compute
     // measured 0.2-0.4 us faster at 16-22 tokens on [14336 x 4096]; for CT = 3
     // they were 0.2-0.6 us slower
-    run_ring<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
+    if constexpr (NS == 3)  // three stages: any S >= 3, not only multiples of three
+        run_ring_any<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
+    else
+        run_ring<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
     if constexpr (CB != 16) {
         if (tb0 < nblk) {
             p.tail_use(tcode, txv, acc);
@@ -612,8 +615,12 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
     if (kr < 0)
         kr = k;
     // the ring issues only stages that exist when each split's k is a whole,
-    // positive number of NS-stage groups
-    if (splits < 1 || kr <= 0 || kr > k || kr % ((int64_t)splits * KP * 256 * NS) != 0)
+    // positive number of NS-stage groups (three-stage rings: any whole number
+    // of stages, at least three)
+    if (splits < 1 || kr <= 0 || kr > k)
+        return hipErrorInvalidValue;
+    if (NS == 3 ? (kr % ((int64_t)splits * KP * 256) != 0 || kr / ((int64_t)splits * KP * 256) < NS)
+                : kr % ((int64_t)splits * KP * 256 * NS) != 0)
         return hipErrorInvalidValue;
     // a tail only without a split, in whole 8-column blocks; rows as wide as the
     // loads; CB == 8: room for a shift of 8 columns before the ring
@@ -656,6 +663,13 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
 // the CUs idle (10.9 against 11.7 us at 16 tokens on [12288 x 4096], 14.7
 // against 15.3 at 32). seg_kernel covers small batches on narrow layers, where
 // it measured faster, and the shapes the ring cannot tile.
+// Layers of 16384+ channels with k >= 8192 take eight channel tiles and a
+// three-stage ring from 13 tokens on (224 workgroups of eight waves on 28672
+// channels, 144 KB of LDS at 32 tokens): half the activation bytes per code
+// byte of the four-tile plan. [28672 x 8192] at 16 / 22 / 32 tokens 37.5 /
+// 41.1 / 45.8 -> 36.8 / 40.0 / 41.4 us, [28672 x 12288] 57.9 / 62.8 / 69.7 ->
+// 54.4 / 59.0 / 60.7; at k = 4096, and below 13 tokens, the ring is too short
+// or the activations too few for it to pay (up to 2.7 us slower).
 struct SkinnyPlan {
     bool pipe;
     int xr, ct, kp, ns, splits;  // pipe_kernel
@@ -667,7 +681,10 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
     SkinnyPlan p{};
     int ct = 0, kp = 1, ns = 4, splits = 1;
     if (m >= 2) {
-        if (n >= 16384) {
+        if (n >= 16384 && m >= 13 && k >= 8192) {
+            ct = 8;  // eight tiles, three stages (the stage count need not divide by three)
+            ns = 3;
+        } else if (n >= 16384) {
             ct = 4;
             ns = 2;
         } else if (n >= 12288) {
@@ -692,9 +709,11 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
     }
     if (ct != 0) {
         const int64_t kc = k / splits;
-        if (kc % (kp * 256 * ns) != 0)
+        if (ns == 3 && (kc % 256 != 0 || kc / 256 < 3))
+            ct = 4, ns = 2;
+        if (ns != 3 && kc % (kp * 256 * ns) != 0)
             ns = 2;
-        if (kc % (kp * 256 * ns) == 0) {
+        if (ns == 3 || kc % (kp * 256 * ns) == 0) {
             p.pipe = true;
             p.xr = m <= 4 ? 4 : m <= 8 ? 8 : m <= 12 ? 12 : m <= 16 ? 16 : m <= 24 ? 24 : 32;
             p.ct = ct;
@@ -724,6 +743,10 @@ hipError_t launch_pipe_xr(const SkinnyPlan& p, const void* x, int m, int64_t k, 
     const int key = p.ct * 100 + p.kp * 10 + p.ns;
     const int sp = p.splits;
     switch (key) {
+    case 813:
+        if constexpr (XR >= 16)  // the plan takes eight tiles from 13 tokens on
+            return launch_pipe<A, XR, 8, 1, 3>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+        return hipErrorInvalidValue;
     case 412: return launch_pipe<A, XR, 4, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
     case 414: return launch_pipe<A, XR, 4, 1, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
     case 312: return launch_pipe<A, XR, 3, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
@@ -842,7 +865,11 @@ Ring4Plan plan_ring4_within(int64_t m, int64_t n, int64_t k, int64_t room)
         kr -= 256;
     if (kr <= 0)
         return r;
-    const SkinnyPlan p = plan_skinny(m < 2 ? 2 : m, n, kr, false);
+    SkinnyPlan p = plan_skinny(m < 2 ? 2 : m, n, kr, false);
+    if (p.pipe && p.ct == 8) {  // this ring keeps the widest layers' four tiles and two stages
+        p.ct = 4;
+        p.ns = 2;
+    }
     // where plan_skinny picks seg_kernel (under 8192 channels, up to 8 tokens):
     // one tile and two k-parts, so that a 4096-channel layer still has 256
     // workgroups (two tiles left half the CUs idle: [4096, 14344] at one

@@ -93,7 +93,10 @@ def test_kernel_names():
     assert kn(A, 1, 4096, 14336, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"
     assert kn(A, 1, 28672, 8192, fw.BF16, X, Q) == "gemv_kernel<R=4,U=2,NT=128>"
     assert kn(A, 16, 14336, 4096, fw.FP16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4>"
-    assert kn(A, 32, 28672, 8192, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>"
+    assert kn(A, 32, 28672, 8192, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=8,KP=1,NS=3>"
+    assert kn(A, 13, 28672, 8192, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=8,KP=1,NS=3>"
+    assert kn(A, 12, 28672, 8192, fw.BF16, X, Q) == "pipe_kernel<XR=12,CT=4,KP=1,NS=2>"
+    assert kn(A, 32, 28672, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>"     # k < 8192
     assert kn(A, 22, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"
     assert kn(A, 8, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=8,CT=2,KP=2,NS=4>"
     assert kn(A, 16, 8192, 3072, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"       # k % 2048 != 0

@@ -107,6 +107,11 @@ PIPE = [
     (17, 4100, 10240, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
     (24, 5000, 12288, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"),
     (32, 4096, 6144, torch.bfloat16, "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    # eight tiles on three-stage rings, stage counts 32, 33 and 34 (every
+    # remainder mod 3), ragged channel tail
+    (13, 16400, 8192, torch.float16, "pipe_kernel<XR=16,CT=8,KP=1,NS=3>"),
+    (22, 16400, 8448, torch.bfloat16, "pipe_kernel<XR=24,CT=8,KP=1,NS=3>"),
+    (32, 16400, 8704, torch.float16, "pipe_kernel<XR=32,CT=8,KP=1,NS=3>"),
 ]
 
 
