@@ -670,6 +670,10 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
 // 41.1 / 45.8 -> 36.8 / 40.0 / 41.4 us, [28672 x 12288] 57.9 / 62.8 / 69.7 ->
 // 54.4 / 59.0 / 60.7; at k = 4096, and below 13 tokens, the ring is too short
 // or the activations too few for it to pay (up to 2.7 us slower).
+// On 8192-channel layers the k split starts at 12 tokens where k >= 20480:
+// [8192 x 28672] at 12 / 14 / 16 tokens 39.7 / 41.3 / 42.4 -> 38.2 / 38.6 /
+// 39.0 us; with k = 14336 the two plans are within 0.5 us, with k = 8192 the
+// split is 2-3 us slower.
 struct SkinnyPlan {
     bool pipe;
     int xr, ct, kp, ns, splits;  // pipe_kernel
@@ -690,7 +694,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
         } else if (n >= 12288) {
             ct = n <= 256 * 48 ? 3 : 4;
         } else if (n >= 8192) {
-            if (m > 16 && allow_split && k % (2 * 1024) == 0) {
+            if ((m > 16 || (m >= 12 && k >= 20480)) && allow_split && k % (2 * 1024) == 0) {
                 ct = 4;
                 splits = 2;
             } else if (m <= 16 && k % 2048 == 0) {

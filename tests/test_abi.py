@@ -99,6 +99,9 @@ def test_kernel_names():
     assert kn(A, 32, 28672, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>"     # k < 8192
     assert kn(A, 22, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"
     assert kn(A, 8, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=8,CT=2,KP=2,NS=4>"
+    assert kn(A, 12, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=12,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"
+    assert kn(A, 11, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=12,CT=2,KP=2,NS=4>"
+    assert kn(A, 16, 8192, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=2,NS=4>"      # k < 20480
     assert kn(A, 16, 8192, 3072, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"       # k % 2048 != 0
     assert kn(A, 16, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=8,NS=2,QL>"
     assert kn(A, 9, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=4,NS=4>"
@@ -177,7 +180,9 @@ def test_workspace_bytes():
     assert wb(1, 4096, 4096, fw.FP32, X, Q, Y) == 0
     assert wb(32, 8192, 28672, fw.BF16, X, Q, Y) == 2 * 32 * 8192 * 4     # split k
     assert wb(17, 11000, 4096, fw.FP16, X, Q, Y) == 2 * 17 * 11000 * 4
-    assert wb(16, 8192, 28672, fw.BF16, X, Q, Y) == 0
+    assert wb(16, 8192, 28672, fw.BF16, X, Q, Y) == 2 * 16 * 8192 * 4     # split k from 12 tokens on long rows
+    assert wb(11, 8192, 28672, fw.BF16, X, Q, Y) == 0
+    assert wb(16, 8192, 14336, fw.BF16, X, Q, Y) == 0
     assert wb(32, 4096, 14336, fw.BF16, X, Q, Y) == 4 * 32 * 4096 * 4    # split k in four
     assert wb(16, 4096, 14336, fw.BF16, X, Q, Y) == 0
     assert wb(32, 8192, 1024, fw.BF16, X, Q, Y) == 0                      # k % 2048 != 0

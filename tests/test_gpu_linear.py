@@ -112,6 +112,8 @@ PIPE = [
     (13, 16400, 8192, torch.float16, "pipe_kernel<XR=16,CT=8,KP=1,NS=3>"),
     (22, 16400, 8448, torch.bfloat16, "pipe_kernel<XR=24,CT=8,KP=1,NS=3>"),
     (32, 16400, 8704, torch.float16, "pipe_kernel<XR=32,CT=8,KP=1,NS=3>"),
+    # k split from 12 tokens on long rows of 8192-channel layers
+    (12, 8200, 20480, torch.bfloat16, "pipe_kernel<XR=12,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
 ]
 
 
