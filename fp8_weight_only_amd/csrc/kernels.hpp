@@ -64,7 +64,9 @@ struct NarrowPlan {
     int mt, w, ns;  // 16-token MFMA tiles, waves, ring stages
     bool ql;        // activation parts loaded by neighbouring lanes, moved by ds_bpermute
 };
-NarrowPlan plan_narrow(int64_t m, int64_t n, int64_t k);
+// split_ok: the caller gives workspace for a k split, which the skinny kernel
+// then prefers on the shapes where it measured faster (see plan_narrow).
+NarrowPlan plan_narrow(int64_t m, int64_t n, int64_t k, bool split_ok = false);
 hipError_t launch_narrow(const NarrowPlan& p, const void* x, Act act, int64_t m, int64_t k, const uint8_t* q,
                          const float* scale, const void* bias, int64_t n, void* y, hipStream_t stream);
 const char* narrow_kernel_name(const NarrowPlan& p);

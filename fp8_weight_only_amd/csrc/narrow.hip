@@ -311,10 +311,16 @@ hipError_t launch_narrow_cfg(const void* x, int m, int64_t k, const uint8_t* q, 
 //     waves, two stages; [4096, 4096] at 17 tokens 9.7 (k split) -> 8.4 us,
 //     [2048, 8192] at 22 tokens 16.7 -> 14.7 (at 32 tokens and on long k the
 //     k split stays faster; QL loads measured 0.6-1 us slower here).
-NarrowPlan plan_narrow(int64_t m, int64_t n, int64_t k)
+NarrowPlan plan_narrow(int64_t m, int64_t n, int64_t k, bool split_ok)
 {
     NarrowPlan p{};
     if (m < 2 || m > 24 || n < 1 || n >= 8192 || k < 256 || k % 256 != 0)
+        return p;
+    // with workspace, 12..16 tokens on layers of 4096+ channels with k % 7168 == 0,
+    // k % 2048 == 0 and k % 4096 != 0 (the 14336-wide down projection) take
+    // the skinny kernel's four-way k split (13.9 / 14.3 us at 12 / 16 tokens
+    // on [4096, 14336], against 14.6 / 16.2 here)
+    if (split_ok && m >= 12 && m <= 16 && n >= 4096 && k % 7168 == 0 && k % 2048 == 0 && k % 4096 != 0)
         return p;
     if (m <= 16 && k % 4096 == 0) {
         p = m >= 10 ? NarrowPlan{true, 1, 8, 2, true} : NarrowPlan{true, 1, 4, 4, false};

@@ -436,7 +436,7 @@ __device__ __forceinline__ f32x4 kSlicedSum(f32x4 (*part)[NACC][kWave], int ct, 
 // build preloads 14); the output pointers, needed only at the end, follow.
 // Measured on MI355X: 0.2-0.3 us per launch against sizes fetched with a
 // scalar load (and a 64-bit division by the grid's height) before the ring.
-template <typename A, int XR, int CT, int KP, int NS, int CB>
+template <typename A, int XR, int CT, int KP, int NS, int CB, bool ANY>
 __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
     const uint16_t* __restrict__ bias, int n, int k, int kr, int kc, int m, int S, uint16_t* __restrict__ y,
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     // with the sliced compute, the loads pinned ahead of each step's compute
     // measured 0.2-0.4 us faster at 16-22 tokens on [14336 x 4096]; for CT = 3
     // they were 0.2-0.6 us slower
-    if constexpr (NS == 3)  // three stages: any S >= 3, not only multiples of three
+    if constexpr (ANY)  // any S >= NS, not only multiples of NS
         run_ring_any<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
     else
         run_ring<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
@@ -607,7 +607,8 @@ hipError_t launch_seg(const void* x, int m, int64_t k, const uint8_t* q, const f
 // splits > 1: k is split over `splits` workgroup rows whose fp32 partial sums
 // go to part (splits * m * n floats), then a second kernel reduces them.
 // kr (default k): the columns the ring covers; the rest is the k tail.
-template <typename A, int XR, int CT, int KP, int NS, int CB = 16>
+// ANY (always with NS = 3): the ring takes any whole number of stages >= NS.
+template <typename A, int XR, int CT, int KP, int NS, int CB = 16, bool ANY = (NS == 3)>
 hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const float* scale, const void* bias,
                        int64_t n, void* y, hipStream_t stream, int splits = 1, float* part = nullptr,
                        int64_t kr = -1)
@@ -619,7 +620,8 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
     // of stages, at least three)
     if (splits < 1 || kr <= 0 || kr > k)
         return hipErrorInvalidValue;
-    if (NS == 3 ? (kr % ((int64_t)splits * KP * 256) != 0 || kr / ((int64_t)splits * KP * 256) < NS)
+    static_assert(ANY || NS != 3, "three-stage rings take any stage count");
+    if (ANY ? (kr % ((int64_t)splits * KP * 256) != 0 || kr / ((int64_t)splits * KP * 256) < NS)
                 : kr % ((int64_t)splits * KP * 256 * NS) != 0)
         return hipErrorInvalidValue;
     // a tail only without a split, in whole 8-column blocks; rows as wide as the
@@ -632,7 +634,7 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
     const unsigned gx = CB == 8 ? (unsigned)(2 * ((n + 32 * CT - 1) / (32 * CT))) : (unsigned)((n + 16 * CT - 1) / (16 * CT));
     const dim3 grid(gx, (unsigned)splits), block(CT * KP * kWave);
     const int64_t kc = kr / splits;  // each split's columns: a whole number of NS-stage groups
-    hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS, CB>), grid, block, 0, stream,
+    hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS, CB, ANY>), grid, block, 0, stream,
                        static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias), (int)n, (int)k,
                        (int)kr, (int)kc, m, (int)(kc / (KP * 256)), static_cast<uint16_t*>(y),
                        splits > 1 ? part : nullptr);
@@ -670,6 +672,13 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
 // 41.1 / 45.8 -> 36.8 / 40.0 / 41.4 us, [28672 x 12288] 57.9 / 62.8 / 69.7 ->
 // 54.4 / 59.0 / 60.7; at k = 4096, and below 13 tokens, the ring is too short
 // or the activations too few for it to pay (up to 2.7 us slower).
+// Splits whose stages are not a multiple of four take three-stage rings (any
+// stage count) instead of two: [4096 x 14336] split four ways at 17 / 22 / 32
+// tokens 18.2 / 18.4 / 19.1 -> 15.0 / 15.6 / 16.6 us; [4096 x 10240] at 16 /
+// 32 tokens 14.1 / 15.4 -> 13.2 / 14.8. On 4096-8191-channel layers with
+// k % 7168 == 0 and k % 4096 != 0 (the 14336-wide down projection) that split
+// also runs from 12 tokens when the caller gives workspace, ahead of
+// narrow_kernel: 14.6 / 16.2 -> 13.9 / 14.3 us at 12 / 16 tokens.
 // On 8192-channel layers the k split starts at 12 tokens where k >= 20480:
 // [8192 x 28672] at 12 / 14 / 16 tokens 39.7 / 41.3 / 42.4 -> 38.2 / 38.6 /
 // 39.0 us; with k = 14336 the two plans are within 0.5 us, with k = 8192 the
@@ -703,7 +712,8 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
             } else {
                 ct = 2;
             }
-        } else if (m > 16 && n >= 4096 && allow_split && k % (4 * 512) == 0) {
+        } else if ((m > 16 || (m >= 12 && k % 7168 == 0 && k % 4096 != 0)) && n >= 4096 && allow_split &&
+                   k % (4 * 512) == 0) {
             ct = 4;
             splits = 4;
         } else if (m > 8) {
@@ -715,8 +725,8 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
         const int64_t kc = k / splits;
         if (ns == 3 && (kc % 256 != 0 || kc / 256 < 3))
             ct = 4, ns = 2;
-        if (ns != 3 && kc % (kp * 256 * ns) != 0)
-            ns = 2;
+        if (ns != 3 && kc % (kp * 256 * ns) != 0)  // a split's stages not a multiple of four: three
+            ns = splits > 1 && kp == 1 && kc % 256 == 0 && kc / 256 >= 3 ? 3 : 2;
         if (ns == 3 || kc % (kp * 256 * ns) == 0) {
             p.pipe = true;
             p.xr = m <= 4 ? 4 : m <= 8 ? 8 : m <= 12 ? 12 : m <= 16 ? 16 : m <= 24 ? 24 : 32;
@@ -750,6 +760,10 @@ hipError_t launch_pipe_xr(const SkinnyPlan& p, const void* x, int m, int64_t k, 
     case 813:
         if constexpr (XR >= 16)  // the plan takes eight tiles from 13 tokens on
             return launch_pipe<A, XR, 8, 1, 3>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+        return hipErrorInvalidValue;
+    case 413:
+        if constexpr (XR >= 12)  // k splits, from 12 tokens on
+            return launch_pipe<A, XR, 4, 1, 3>(x, m, k, q, scale, bias, n, y, stream, sp, part);
         return hipErrorInvalidValue;
     case 412: return launch_pipe<A, XR, 4, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
     case 414: return launch_pipe<A, XR, 4, 1, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);
@@ -828,12 +842,13 @@ hipError_t launch_typed(const void* x, int64_t m, int64_t k, const uint8_t* q, c
                         const void* bias, int64_t n, void* y, float* part, size_t part_bytes, hipStream_t stream)
 {
     const int mi = (int)m;
-    const NarrowPlan np = plan_narrow(m, n, k);
+    const size_t need = skinny_workspace_bytes(m, n, k);
+    const bool ws_ok = part != nullptr && need > 0 && part_bytes >= need;
+    const NarrowPlan np = plan_narrow(m, n, k, ws_ok);
     if (np.ok)
         return launch_narrow(np, x, std::is_same<A, Bf16>::value ? Act::BF16 : Act::FP16, m, k, q, scale, bias, n, y,
                              stream);
-    const size_t need = skinny_workspace_bytes(m, n, k);
-    const SkinnyPlan p = plan_skinny(m, n, k, part != nullptr && need > 0 && part_bytes >= need);
+    const SkinnyPlan p = plan_skinny(m, n, k, ws_ok);
     if (p.pipe) {
         switch (p.xr) {
         case 4: return launch_pipe_xr<A, 4>(p, x, mi, k, q, scale, bias, n, y, part, stream);
@@ -942,7 +957,7 @@ Ring4Plan plan_ring4(int64_t m, int64_t n, int64_t k, const uint8_t* q)
 
 size_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {
-    if (m < 1 || m > 32 || n < 1 || k < 256 || k % 256 != 0 || plan_narrow(m, n, k).ok)
+    if (m < 1 || m > 32 || n < 1 || k < 256 || k % 256 != 0 || plan_narrow(m, n, k, true).ok)
         return 0;
     const SkinnyPlan p = plan_skinny(m, n, k, true);
     return p.pipe && p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
@@ -1002,7 +1017,7 @@ const char* skinny_kernel_name(int64_t m, int64_t n, int64_t k, bool with_worksp
         snprintf(name, sizeof name, "pipe_kernel<XR=%d,CT=%d,KP=%d,NS=%d,CB=%d>", p.xr, p.ct, p.kp, p.ns, p.cb);
         return name;
     }
-    const NarrowPlan np = plan_narrow(m, n, k);
+    const NarrowPlan np = plan_narrow(m, n, k, with_workspace);
     if (np.ok)
         return narrow_kernel_name(np);
     const SkinnyPlan p = plan_skinny(m, n, k, with_workspace);

@@ -107,14 +107,17 @@ def test_kernel_names():
     assert kn(A, 9, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=4,NS=4>"
     assert kn(A, 10, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=8,NS=2,QL>"
     assert kn(A, 16, 4100, 2048, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=1,KP=2,NS=4>"     # k % 4096 != 0
-    assert kn(A, 16, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
-    assert kn(A, 16, 4100, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
+    assert kn(A, 16, 4096, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"
+    assert kn(A, 16, 4100, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"
+    assert kn(A, 11, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
+    assert kn(A, 16, 4096, 28672, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=8,NS=2,QL>"
     assert kn(A, 5, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=4>"
-    assert kn(A, 32, 4096, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"
+    assert kn(A, 32, 4096, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"
+    assert kn(A, 28, 4100, 2048, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"  # 2 stages a split
     assert kn(A, 22, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=2,W=4,NS=2>"
     assert kn(A, 22, 4096, 12288, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"
-    assert kn(A, 17, 6000, 10240, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"
-    assert kn(A, 12, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
+    assert kn(A, 17, 6000, 10240, fw.BF16, X, Q) == "pipe_kernel<XR=24,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"
+    assert kn(A, 12, 4096, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=12,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"
     assert kn(A, 6, 4096, 14336, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=7,NS=2,QL>"
     assert kn(A, 25, 4096, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"
     assert kn(A, 32, 2048, 4096, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=1,KP=2,NS=4>"      # n < 4096
@@ -184,7 +187,8 @@ def test_workspace_bytes():
     assert wb(11, 8192, 28672, fw.BF16, X, Q, Y) == 0
     assert wb(16, 8192, 14336, fw.BF16, X, Q, Y) == 0
     assert wb(32, 4096, 14336, fw.BF16, X, Q, Y) == 4 * 32 * 4096 * 4    # split k in four
-    assert wb(16, 4096, 14336, fw.BF16, X, Q, Y) == 0
+    assert wb(16, 4096, 14336, fw.BF16, X, Q, Y) == 4 * 16 * 4096 * 4    # split k in four from 12 tokens
+    assert wb(11, 4096, 14336, fw.BF16, X, Q, Y) == 0
     assert wb(32, 8192, 1024, fw.BF16, X, Q, Y) == 0                      # k % 2048 != 0
 
 

@@ -21,7 +21,7 @@ DEV = torch.device("cuda:0")
 CALLS = [
     ("linear", 1, 1000, 1024, torch.bfloat16, "gemv_kernel<R=2,U=2,NT=64,DB>"),
     ("linear", 8, 2048, 1024, torch.float16, None),
-    ("linear", 20, 4100, 10240, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    ("linear", 20, 4100, 10240, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"),
     ("linear", 12, 2000, 4096, torch.float16, "narrow_kernel<MT=1,W=8,NS=2,QL>"),
     ("linear", 3, 300, 1004, torch.bfloat16, None),  # k % 8 != 0: fallback through the workspace
     ("linear", 5, 700, 2056, torch.float16, "pipe_kernel<XR=8,CT=1,KP=2,NS=4,CB=8>"),  # shifted rows, k tail

@@ -104,9 +104,12 @@ PIPE = [
     (12, 14400, 1024, torch.float16, "pipe_kernel<XR=12,CT=4,KP=1,NS=4>"),
     (20, 8200, 2048, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
     (32, 8192, 4096, torch.float16, "pipe_kernel<XR=32,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
-    (17, 4100, 10240, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    (17, 4100, 10240, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"),
+    (28, 4100, 2048, torch.bfloat16, "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    (16, 4096, 14336, torch.bfloat16, "pipe_kernel<XR=16,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"),
+    (12, 4100, 14336, torch.float16, "pipe_kernel<XR=12,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"),
     (24, 5000, 12288, torch.bfloat16, "pipe_kernel<XR=24,CT=4,KP=1,NS=4>x4+splitk_reduce_kernel"),
-    (32, 4096, 6144, torch.bfloat16, "pipe_kernel<XR=32,CT=4,KP=1,NS=2>x4+splitk_reduce_kernel"),
+    (32, 4096, 6144, torch.bfloat16, "pipe_kernel<XR=32,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"),
     # eight tiles on three-stage rings, stage counts 32, 33 and 34 (every
     # remainder mod 3), ragged channel tail
     (13, 16400, 8192, torch.float16, "pipe_kernel<XR=16,CT=8,KP=1,NS=3>"),
@@ -232,7 +235,7 @@ NARROW = [
     (11, 2000, 4096, torch.float16, "narrow_kernel<MT=1,W=8,NS=2,QL>"),
     (13, 1000, 8192, torch.bfloat16, "narrow_kernel<MT=1,W=8,NS=2,QL>"),
     (12, 4096, 7168, torch.bfloat16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
-    (16, 4096, 14336, torch.bfloat16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
+    (11, 4096, 14336, torch.bfloat16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
     (6, 500, 14336, torch.float16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
     (15, 4100, 21504, torch.float16, "narrow_kernel<MT=1,W=7,NS=2,QL>"),
     (5, 500, 7168, torch.float16, "narrow_kernel<MT=1,W=7,NS=4>"),
