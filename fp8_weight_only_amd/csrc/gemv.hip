@@ -353,17 +353,26 @@ hipError_t launch_cfg(const void* x, int64_t k, const uint8_t* q, const float* s
 
 // Tile choice, from sweeps on MI355X (kernel durations, weights rotated
 // through 1 GiB). Weights under 96 MB: one-wave workgroups of two rows,
-// two-pass groups, double-buffered; four-row, 128-thread workgroups with
+// double-buffered groups of two passes; four-row, 128-thread workgroups with
 // single-buffered two-pass groups above. On the long rows of the
 // [4096, 14336] down projection the double-buffered one-wave tile took 11.1-11.5
 // us against 12.3 for the single-buffered 128-thread one (a plain read of the
 // same bytes: 10.1-10.3); on [4096, 4096] and [14336, 4096] the two were
 // within 0.3 us of each other. Double buffering did not help the large
-// weights' four-row tile. A single instance for all the decode-sized layers
-// also means consecutive layers of different shapes run the same code: in a
-// decode step, switching to a second kernel binary cost about 1 us, the refill
-// of each CU's instruction cache.
+// weights' four-row tile.
 constexpr int64_t kLargeWeight = (int64_t)96 << 20;
+
+// Groups of one pass (each wave two passes ahead instead of its whole share at
+// once) on long rows of 4096-8191-channel layers: [4096, 14336] 11.10 -> 10.73
+// us, [5120, 13824] 14.50 -> 13.97, [4096, 8192] 7.42 -> 7.24, [4096, 6144]
+// 6.03 -> 5.85; not on [2048, 8192] (+0.5 us), [1024, 16384] (+1.5), [8192,
+// 10240] (+0.15) or k % 512 != 0 ([4096, 11008]: +0.6). In the decode step
+// the down projection's second kernel binary cost no measurable time beside
+// the other layers' (the GEMV family's mean launch 9.07 -> 8.82 us).
+bool one_pass_groups(int64_t n, int64_t k)
+{
+    return n >= 4096 && n < 8192 && k >= 6144 && k % 512 == 0;
+}
 
 template <typename A, int R, int U, int NT, bool DB>
 hipError_t launch_shift(const void* x, int64_t k, const uint8_t* q, const float* scale, const void* bias, int64_t n,
@@ -400,8 +409,10 @@ hipError_t launch_typed(const void* x, int64_t k, const uint8_t* q, const float*
         return large ? launch_cfg<A, 4, 2, 128, false, 8>(x, k, q, scale, bias, n, y, stream)
                      : launch_cfg<A, 2, 2, 64, true, 8>(x, k, q, scale, bias, n, y, stream);
     default:
-        return large ? launch_cfg<A, 4, 2, 128, false>(x, k, q, scale, bias, n, y, stream)
-                     : launch_cfg<A, 2, 2, 64, true>(x, k, q, scale, bias, n, y, stream);
+        if (large)
+            return launch_cfg<A, 4, 2, 128, false>(x, k, q, scale, bias, n, y, stream);
+        return one_pass_groups(n, k) ? launch_cfg<A, 2, 1, 64, true>(x, k, q, scale, bias, n, y, stream)
+                                     : launch_cfg<A, 2, 2, 64, true>(x, k, q, scale, bias, n, y, stream);
     }
 }
 
@@ -416,7 +427,9 @@ const char* gemv_kernel_name(int64_t n, int64_t k, const uint8_t* q)
     case Rows::OFF8:
         return large ? "gemv_kernel<R=4,U=2,NT=128,CH=8>" : "gemv_kernel<R=2,U=2,NT=64,DB,CH=8>";
     default:
-        return large ? "gemv_kernel<R=4,U=2,NT=128>" : "gemv_kernel<R=2,U=2,NT=64,DB>";
+        return large                     ? "gemv_kernel<R=4,U=2,NT=128>"
+               : one_pass_groups(n, k) ? "gemv_kernel<R=2,U=1,NT=64,DB>"
+                                       : "gemv_kernel<R=2,U=2,NT=64,DB>";
     }
 }
 

@@ -90,7 +90,9 @@ def test_kernel_names():
     kn = fw.fp8w_linear_kernel
     A = fw.PATH_AUTO
     assert kn(A, 1, 4096, 4096, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"
-    assert kn(A, 1, 4096, 14336, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"
+    assert kn(A, 1, 4096, 14336, fw.BF16, X, Q) == "gemv_kernel<R=2,U=1,NT=64,DB>"     # one-pass groups
+    assert kn(A, 1, 4096, 11008, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"     # k % 512 != 0
+    assert kn(A, 1, 8192, 8192, fw.BF16, X, Q) == "gemv_kernel<R=2,U=2,NT=64,DB>"
     assert kn(A, 1, 28672, 8192, fw.BF16, X, Q) == "gemv_kernel<R=4,U=2,NT=128>"
     assert kn(A, 16, 14336, 4096, fw.FP16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=4>"
     assert kn(A, 32, 28672, 8192, fw.BF16, X, Q) == "pipe_kernel<XR=32,CT=8,KP=1,NS=3>"

@@ -199,6 +199,8 @@ GEMV8 = [
     (1, 300, 280, torch.float16, True, 8, "gemv_shift_kernel<R=2,U=2,NT=64,DB>"),
     (1, 12300, 8192, torch.float16, True, 8, "gemv_kernel<R=4,U=2,NT=128,CH=8>"),
     (1, 1000, 4112, torch.bfloat16, True, 0, "gemv_kernel<R=2,U=2,NT=64,DB>"),  # k % 16 == 0: 16-code chunks, pass tail
+    (1, 4100, 6656, torch.float16, True, 0, "gemv_kernel<R=2,U=1,NT=64,DB>"),   # one-pass groups, odd group count, pass tail
+    (1, 5000, 14336, torch.bfloat16, False, 0, "gemv_kernel<R=2,U=1,NT=64,DB>"),  # fourteen one-pass groups
 ]
 
 
