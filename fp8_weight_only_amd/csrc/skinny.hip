@@ -450,10 +450,23 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t b2[NS > 2 ? C::STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t b3[NS > 3 ? C::STAGE : 16];
 
-    // split k: workgroup row blockIdx.y owns k range [y * kc, (y + 1) * kc)
+    // split k: workgroup row blockIdx.y owns k range [y * kc, (y + 1) * kc);
+    // ANY rings with a split: S is the stage count of all splits together, and
+    // row y owns stages [y S / splits, (y + 1) S / splits) (splits may differ
+    // by one stage)
+    int Sy = S;
+    int64_t k0 = (int64_t)blockIdx.y * kc;
+    if constexpr (ANY) {
+        if (gridDim.y > 1) {
+            const unsigned sp = gridDim.y, y0 = blockIdx.y;
+            const int sb = (int)((y0 * (unsigned)S) / sp), se = (int)(((y0 + 1) * (unsigned)S) / sp);
+            Sy = se - sb;
+            k0 = (int64_t)sb * (KP * 256);
+        }
+    }
     P p;
-    p.x = x + (int64_t)blockIdx.y * kc;
-    p.q = q + (int64_t)blockIdx.y * kc;
+    p.x = x + k0;
+    p.q = q + k0;
     p.m = m;
     p.n = n;
     p.k = k;
@@ -505,17 +518,17 @@ __global__ __launch_bounds__(CT* KP * kWave) void pipe_kernel(
             p.tail_load(kr, tb0, tcode, txv);
     }
 
-    p.S = S;
+    p.S = Sy;
     // workgroups are dealt to the eight XCDs in turn: consecutive workgroups of
     // one XCD get consecutive start stages
-    p.rot = (int64_t)((blockIdx.x / 8) % (unsigned)S);
+    p.rot = (int64_t)((blockIdx.x / 8) % (unsigned)Sy);
     // with the sliced compute, the loads pinned ahead of each step's compute
     // measured 0.2-0.4 us faster at 16-22 tokens on [14336 x 4096]; for CT = 3
     // they were 0.2-0.6 us slower
     if constexpr (ANY)  // any S >= NS, not only multiples of NS
-        run_ring_any<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
+        run_ring_any<NS, C::LOADS, P::kSliced>(p, Sy, b0, b1, b2, b3, acc);
     else
-        run_ring<NS, C::LOADS, P::kSliced>(p, S, b0, b1, b2, b3, acc);
+        run_ring<NS, C::LOADS, P::kSliced>(p, Sy, b0, b1, b2, b3, acc);
     if constexpr (CB != 16) {
         if (tb0 < nblk) {
             p.tail_use(tcode, txv, acc);
@@ -621,8 +634,9 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
     if (splits < 1 || kr <= 0 || kr > k)
         return hipErrorInvalidValue;
     static_assert(ANY || NS != 3, "three-stage rings take any stage count");
-    if (ANY ? (kr % ((int64_t)splits * KP * 256) != 0 || kr / ((int64_t)splits * KP * 256) < NS)
-                : kr % ((int64_t)splits * KP * 256 * NS) != 0)
+    // ANY: whole stages, at least NS in the smallest split (splits may differ by one stage)
+    if (ANY ? (kr % ((int64_t)KP * 256) != 0 || kr / ((int64_t)KP * 256) / splits < NS)
+            : kr % ((int64_t)splits * KP * 256 * NS) != 0)
         return hipErrorInvalidValue;
     // a tail only without a split, in whole 8-column blocks; rows as wide as the
     // loads; CB == 8: room for a shift of 8 columns before the ring
@@ -633,11 +647,13 @@ hipError_t launch_pipe(const void* x, int m, int64_t k, const uint8_t* q, const 
         return hipErrorInvalidValue;
     const unsigned gx = CB == 8 ? (unsigned)(2 * ((n + 32 * CT - 1) / (32 * CT))) : (unsigned)((n + 16 * CT - 1) / (16 * CT));
     const dim3 grid(gx, (unsigned)splits), block(CT * KP * kWave);
-    const int64_t kc = kr / splits;  // each split's columns: a whole number of NS-stage groups
+    // each split's columns (equal splits; an ANY ring with a split gets the
+    // stage count of all splits and divides it itself)
+    const int64_t kc = kr / splits;
+    const int64_t stages = ANY && splits > 1 ? kr / (KP * 256) : kc / (KP * 256);
     hipLaunchKernelGGL((pipe_kernel<A, XR, CT, KP, NS, CB, ANY>), grid, block, 0, stream,
                        static_cast<const uint16_t*>(x), q, scale, static_cast<const uint16_t*>(bias), (int)n, (int)k,
-                       (int)kr, (int)kc, m, (int)(kc / (KP * 256)), static_cast<uint16_t*>(y),
-                       splits > 1 ? part : nullptr);
+                       (int)kr, (int)kc, m, (int)stages, static_cast<uint16_t*>(y), splits > 1 ? part : nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits <= 1)
         return e;
@@ -693,6 +709,20 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
 {
     SkinnyPlan p{};
     int ct = 0, kp = 1, ns = 4, splits = 1;
+    // an odd number of 256-column stages on a 2048-8191-channel layer: no
+    // single-pass ring shape divides it; splits of whole stages (uneven by at
+    // most one) on three-stage rings, as many as keep the grid near one
+    // workgroup per CU ([4096, 11008] at 12 / 16 / 32 tokens 32.2 / 32.8 /
+    // 36.8 -> 13.0 / 13.5 / 15.0 us; [5120, 13824] at 2 / 16 / 32 tokens 19.7 /
+    // 40.9 / 45.4 -> 15.7 / 17.6 / 19.8; [2048, 5632] at 16 / 32 tokens 17.1 /
+    // 19.7 -> 8.7 / 10.1; below 9 tokens seg_kernel stays unless each split
+    // has 16+ stages on 4096+ channels: [4096, 11008] split four ways 12.7 us
+    // at 2 tokens against 12.4; short rows stay on the single pass)
+    const int oct = n >= 4096 ? 4 : 2;
+    const int64_t otiles = (n + 16 * oct - 1) / (16 * oct);
+    const int64_t osp = 256 / otiles < 2 ? 2 : 256 / otiles > 4 ? 4 : 256 / otiles;
+    const bool odd_split = n >= 2048 && n < 8192 && k % 2048 != 0 && k % 256 == 0 && k >= 5120 &&
+                           k / 256 / osp >= 3 && (m >= 9 || (n >= 4096 && k / 256 / osp >= 16)) && allow_split;
     if (m >= 2) {
         if (n >= 16384 && m >= 13 && k >= 8192) {
             ct = 8;  // eight tiles, three stages (the stage count need not divide by three)
@@ -716,6 +746,10 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
                    k % (4 * 512) == 0) {
             ct = 4;
             splits = 4;
+        } else if (odd_split) {
+            ct = oct;
+            splits = (int)osp;
+            ns = 3;
         } else if (m > 8) {
             ct = 1;
             kp = 2;
@@ -723,7 +757,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, bool allow_split)
     }
     if (ct != 0) {
         const int64_t kc = k / splits;
-        if (ns == 3 && (kc % 256 != 0 || kc / 256 < 3))
+        if (ns == 3 && splits == 1 && (kc % 256 != 0 || kc / 256 < 3))
             ct = 4, ns = 2;
         if (ns != 3 && kc % (kp * 256 * ns) != 0)  // a split's stages not a multiple of four: three
             ns = splits > 1 && kp == 1 && kc % 256 == 0 && kc / 256 >= 3 ? 3 : 2;
@@ -761,9 +795,10 @@ hipError_t launch_pipe_xr(const SkinnyPlan& p, const void* x, int m, int64_t k, 
         if constexpr (XR >= 16)  // the plan takes eight tiles from 13 tokens on
             return launch_pipe<A, XR, 8, 1, 3>(x, m, k, q, scale, bias, n, y, stream, sp, part);
         return hipErrorInvalidValue;
-    case 413:
-        if constexpr (XR >= 12)  // k splits, from 12 tokens on
-            return launch_pipe<A, XR, 4, 1, 3>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 413: return launch_pipe<A, XR, 4, 1, 3>(x, m, k, q, scale, bias, n, y, stream, sp, part);
+    case 213:
+        if constexpr (XR >= 12)  // splits of 2048-4095-channel layers, from 9 tokens on
+            return launch_pipe<A, XR, 2, 1, 3>(x, m, k, q, scale, bias, n, y, stream, sp, part);
         return hipErrorInvalidValue;
     case 412: return launch_pipe<A, XR, 4, 1, 2>(x, m, k, q, scale, bias, n, y, stream, sp, part);
     case 414: return launch_pipe<A, XR, 4, 1, 4>(x, m, k, q, scale, bias, n, y, stream, sp, part);

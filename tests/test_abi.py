@@ -104,6 +104,10 @@ def test_kernel_names():
     assert kn(A, 12, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=12,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"
     assert kn(A, 11, 8192, 28672, fw.BF16, X, Q) == "pipe_kernel<XR=12,CT=2,KP=2,NS=4>"
     assert kn(A, 16, 8192, 14336, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=2,NS=4>"      # k < 20480
+    assert kn(A, 16, 4096, 11008, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"
+    assert kn(A, 8, 4096, 11008, fw.BF16, X, Q) == "seg_kernel<SEG=2,T=2,W=8,U=2,MT=1>"     # splits under 16 stages
+    assert kn(A, 4, 5120, 13824, fw.BF16, X, Q) == "pipe_kernel<XR=4,CT=4,KP=1,NS=3>x3+splitk_reduce_kernel"
+    assert kn(A, 8, 2048, 5632, fw.BF16, X, Q) == "seg_kernel<SEG=2,T=2,W=8,U=2,MT=1>"
     assert kn(A, 16, 8192, 3072, fw.BF16, X, Q) == "pipe_kernel<XR=16,CT=2,KP=1,NS=4>"       # k % 2048 != 0
     assert kn(A, 16, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=8,NS=2,QL>"
     assert kn(A, 9, 4096, 4096, fw.BF16, X, Q) == "narrow_kernel<MT=1,W=4,NS=4>"
@@ -191,6 +195,8 @@ def test_workspace_bytes():
     assert wb(32, 4096, 14336, fw.BF16, X, Q, Y) == 4 * 32 * 4096 * 4    # split k in four
     assert wb(16, 4096, 14336, fw.BF16, X, Q, Y) == 4 * 16 * 4096 * 4    # split k in four from 12 tokens
     assert wb(11, 4096, 14336, fw.BF16, X, Q, Y) == 0
+    assert wb(16, 4096, 11008, fw.BF16, X, Q, Y) == 4 * 16 * 4096 * 4    # odd stage count: uneven split in four
+    assert wb(8, 4096, 11008, fw.BF16, X, Q, Y) == 0
     assert wb(32, 8192, 1024, fw.BF16, X, Q, Y) == 0                      # k % 2048 != 0
 
 

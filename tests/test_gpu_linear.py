@@ -115,6 +115,16 @@ PIPE = [
     (13, 16400, 8192, torch.float16, "pipe_kernel<XR=16,CT=8,KP=1,NS=3>"),
     (22, 16400, 8448, torch.bfloat16, "pipe_kernel<XR=24,CT=8,KP=1,NS=3>"),
     (32, 16400, 8704, torch.float16, "pipe_kernel<XR=32,CT=8,KP=1,NS=3>"),
+    # an odd number of 256-column stages: splits of whole stages, uneven by at
+    # most one (43 stages in four, 29 in three, 22 in four), three-stage rings,
+    # four- and two-tile workgroups, ragged channel counts, one split plan
+    # below 9 tokens
+    (12, 4096, 11008, torch.bfloat16, "pipe_kernel<XR=12,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"),
+    (32, 5120, 13824, torch.float16, "pipe_kernel<XR=32,CT=4,KP=1,NS=3>x3+splitk_reduce_kernel"),
+    (3, 4100, 13824, torch.bfloat16, "pipe_kernel<XR=4,CT=4,KP=1,NS=3>x3+splitk_reduce_kernel"),
+    (20, 2048, 5632, torch.float16, "pipe_kernel<XR=24,CT=2,KP=1,NS=3>x4+splitk_reduce_kernel"),
+    (9, 2100, 7424, torch.bfloat16, "pipe_kernel<XR=12,CT=2,KP=1,NS=3>x3+splitk_reduce_kernel"),
+    (17, 4096, 7168, torch.float16, "pipe_kernel<XR=24,CT=4,KP=1,NS=3>x4+splitk_reduce_kernel"),
     # k split from 12 tokens on long rows of 8192-channel layers
     (12, 8200, 20480, torch.bfloat16, "pipe_kernel<XR=12,CT=4,KP=1,NS=4>x2+splitk_reduce_kernel"),
 ]
