@@ -52,7 +52,8 @@ def _noalloc(x, q, s, b):
 # consecutive calls, each smaller than the one before, on every path that uses
 # the scratch: skinny k split in four, then in two, on smaller layers;
 # batch k split; the fallback's 16-bit weight (k % 8 != 0); and the GEMV and
-# the skinny kernel's unaligned-code path (no scratch)
+# the skinny kernel's unaligned-code path (no scratch); then four-way splits
+# of an odd stage count (uneven splits, three-stage rings)
 SEQUENCES = [
     [(32, 4096, 14336, torch.bfloat16, False), (20, 4096, 10240, torch.float16, True)],
     [(24, 8192, 4096, torch.bfloat16, True), (17, 8192, 2048, torch.bfloat16, False)],
@@ -60,6 +61,7 @@ SEQUENCES = [
     [(8, 3000, 1004, torch.bfloat16, True), (3, 700, 524, torch.float16, False)],
     [(1, 4096, 4096, torch.bfloat16, True), (1, 1024, 1024, torch.float16, False)],
     [(16, 2000, 2056, torch.bfloat16, True), (2, 500, 776, torch.float16, False)],
+    [(16, 4096, 11008, torch.bfloat16, True), (12, 4096, 7424, torch.float16, False)],
 ]
 
 
