@@ -46,7 +46,7 @@ roofline, per-call microseconds from back-to-back bursts of each call, the
 streaming-read reference, and the CPU oracle baseline). Progress goes to
 stderr, and the full record (per-call percentiles, warm numbers, host latency,
 the oracle timed on every workload and, with --extra, the other workloads) is
-written to --full-json (default gpurun_out/bench_full.json).
+written to --full-json (default results/bench_full.json).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--min-ms MS] [--spin-ms MS]
                        [--extra] [--only tiny|skinny|block|large|batch|grouped|w8a8 ...] [--reps R]
@@ -79,7 +79,7 @@ ROTATE_BYTES = 1 << 30
 SPIN_MS = 200.0  # sustained load before every timed region (clock ramp-up); --spin-ms
 MIN_TIMED_MS = 50.0  # shortest timed region; --min-ms
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_traffic.json")
-FULL_RECORD = os.path.join(ROOT, "gpurun_out", "bench_full.json")
+FULL_RECORD = os.path.join(ROOT, "results", "bench_full.json")
 
 # the kernel families of the step and the sources that define each (kernel code
 # and tile choice): a change to any of them, or to the compile flags, voids that

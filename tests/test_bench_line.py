@@ -25,7 +25,7 @@ def _line(steps=480, requested=20):
            "one_core": {"value": 2.49, "unit": "GB/s", "cores": 1, "sample": "y" * 60},
            "gpu_parity_vs_this_oracle_run": True, "host_cpus": 128, "host_model": "AMD EPYC 9575F 64-Core Processor"}
     return bench.headline(steps, requested, 5, 12.0, 38.0, shape, per_call, ceiling, cpu,
-                          os.path.join(ROOT, "gpurun_out", "bench_full.json"))
+                          os.path.join(ROOT, "results", "bench_full.json"))
 
 
 def test_headline_is_compact_and_complete():
