@@ -122,41 +122,58 @@ __device__ __forceinline__ void ring_for(F&& f)
     }
 }
 
-// s_waitcnt for at most g stages of LOADS loads still outstanding, g uniform
-// in 0 .. GMAX (the count must be an immediate, so each value is its own wait).
-template <int LOADS, int GMAX>
-__device__ __forceinline__ void wait_stages_at_most(int64_t g)
+// Stage buffer I of four, chosen at compile time (no array of pointers, so
+// every LDS access keeps its own __shared__ object).
+template <int I>
+__device__ __forceinline__ uint8_t* ring_buf(uint8_t* b0, uint8_t* b1, uint8_t* b2, uint8_t* b3)
 {
-    static_assert(GMAX >= 0 && GMAX <= 2, "stages in flight");
-    if constexpr (GMAX >= 2) {
-        if (g >= 2) {
-            wait_loads_at_most<2 * LOADS>();
-            return;
+    if constexpr (I == 0)
+        return b0;
+    else if constexpr (I == 1)
+        return b1;
+    else if constexpr (I == 2)
+        return b2;
+    else
+        return b3;
+}
+
+// The last R steps of run_ring_any (NS - 1 <= R <= 2 NS - 2), from stage s0
+// (a multiple of NS) on, all known at compile time: step u issues stage
+// s0 + u + NS - 1 while it exists and waits with the stages issued after its
+// own, min(NS - 2, R - 1 - u), still allowed in flight (loads complete in
+// order). Straight-line code, so the compiler's wait-count pass still tells
+// the stage buffers apart; a run-time test around each issue made it drain
+// every outstanding load before each step's compute.
+template <int NS, int LOADS, bool PIN, int R, typename P, typename Acc>
+__device__ __forceinline__ void ring_tail(const P& p, int64_t s0, uint8_t* b0, uint8_t* b1, uint8_t* b2, uint8_t* b3,
+                                          Acc* acc)
+{
+    ring_for<0, R>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int after = R - 1 - u < NS - 2 ? R - 1 - u : NS - 2;
+        wait_loads_at_most<LOADS * after>();
+        stage_barrier();
+        if constexpr (u + NS - 1 < R) {
+            p.issue(s0 + u + NS - 1, ring_buf<(u + NS - 1) % NS>(b0, b1, b2, b3));
+            if constexpr (PIN)
+                __builtin_amdgcn_sched_barrier(0);
         }
-    }
-    if constexpr (GMAX >= 1) {
-        if (g >= 1) {
-            wait_loads_at_most<LOADS>();
-            return;
-        }
-    }
-    wait_loads_at_most<0>();
+        p.compute(ring_buf<u % NS>(b0, b1, b2, b3), acc);
+    });
 }
 
 // run_ring for any number of stages S >= NS (S need not be a multiple of NS).
 // Step s waits for stage s, opens the barrier, issues stage s + NS - 1 into
 // the buffer stage s - 1 used (while that stage exists) and computes stage s
-// from buffer s mod NS. Whole groups of NS steps that all issue run as in
-// run_ring; the last steps (fewer than 2 NS - 1) check at run time whether
-// they issue, and each waits with the stages issued after its own,
-// min(NS - 2, S - 1 - s), still allowed in flight (loads complete in order).
+// from buffer s mod NS. Whole groups of NS steps run as in run_ring while at
+// least 2 NS - 1 steps remain; the last R steps (NS - 1 <= R <= 2 NS - 2) run
+// as one of NS straight-line tails, chosen by R.
 template <int NS, int LOADS, bool PIN = false, typename P, typename Acc>
 __device__ __forceinline__ void run_ring_any(const P& p, int64_t S, uint8_t* b0, uint8_t* b1, uint8_t* b2,
                                              uint8_t* b3, Acc* acc)
 {
     static_assert(NS >= 2 && NS <= 4, "stages");
     static_assert(LOADS * (NS - 2) < 64, "vmcnt range");
-    uint8_t* const bufs[4] = {b0, b1, b2, b3};
     p.issue(0, b0);
     if constexpr (NS > 2)
         p.issue(1, b1);
@@ -168,26 +185,17 @@ __device__ __forceinline__ void run_ring_any(const P& p, int64_t S, uint8_t* b0,
             constexpr int u = decltype(uc)::value;
             wait_loads_at_most<LOADS*(NS - 2)>();
             stage_barrier();
-            p.issue(s0 + u + NS - 1, bufs[(u + NS - 1) % NS]);
+            p.issue(s0 + u + NS - 1, ring_buf<(u + NS - 1) % NS>(b0, b1, b2, b3));
             if constexpr (PIN)
                 __builtin_amdgcn_sched_barrier(0);
-            p.compute(bufs[u], acc);
+            p.compute(ring_buf<u>(b0, b1, b2, b3), acc);
         });
     }
-    ring_for<0, 2 * NS - 1>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        const int64_t s = s0 + u;
-        if (s < S) {
-            const int64_t after = S - 1 - s < NS - 2 ? S - 1 - s : NS - 2;
-            wait_stages_at_most<LOADS, NS - 2>(after);
-            stage_barrier();
-            if (s + NS - 1 < S) {
-                p.issue(s + NS - 1, bufs[(u + NS - 1) % NS]);
-                if constexpr (PIN)
-                    __builtin_amdgcn_sched_barrier(0);
-            }
-            p.compute(bufs[u % NS], acc);
-        }
+    const int64_t rest = S - s0;
+    ring_for<NS - 1, 2 * NS - 1>([&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        if (rest == R)
+            ring_tail<NS, LOADS, PIN, R>(p, s0, b0, b1, b2, b3, acc);
     });
 }
 
